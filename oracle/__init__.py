@@ -1,0 +1,247 @@
+"""ctypes wrapper of the plain C oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product package.  It shares no
+code with the HIP library.
+
+Parity status of each function (what pins it, in tests/test_oracle_*.py):
+  oracle_init / value tables  -- pinned: every bf16 and e4m3 code against
+                                 torch's own decoders.
+  e4m3_encode                 -- pinned: torch's float8_e4m3fn cast at every
+                                 representable value, midpoint and
+                                 midpoint +- 1 ulp; saturation by the format
+                                 definition.
+  quant_row / quant_rows_bf16 -- pinned: closed-form cases (zero row, exact
+                                 448 row, power-of-two rows) and torch's cast.
+  route                       -- pinned: brute-force stable sort, invariants,
+                                 exhaustive tiny cases.
+  forward_f64/f32/bf16        -- pinned: dense fp64 torch matmul references
+                                 (k=1, k=E mean, scattered gate matrix),
+                                 structural invariants.
+  forward_fp8                 -- pinned: dense torch reference applying
+                                 torch's e4m3 cast; exactness of the fp8 dot
+                                 products against integer arithmetic.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP, no fast-math, no contraction)."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+           "-shared", "-fPIC", "-Wall", SRC_PATH, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        L.oracle_init.restype = None
+        L.oracle_bf16_value.restype = ctypes.c_double
+        L.oracle_bf16_value.argtypes = [i]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_e4m3_value.argtypes = [i]
+        L.oracle_e4m3_encode.restype = i
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_quant_row.restype = None
+        L.oracle_quant_row.argtypes = [P, i, P, P]
+        L.oracle_quant_rows_bf16.restype = None
+        L.oracle_quant_rows_bf16.argtypes = [P, i, i, P, P]
+        L.oracle_route.restype = i
+        L.oracle_route.argtypes = [P, i, i, i, P, P, P, P, i, P, P]
+        for name in ("oracle_forward_f64", "oracle_forward_f32", "oracle_forward_bf16"):
+            f = getattr(L, name)
+            f.restype = None
+            f.argtypes = [P, P, P, P, P, i, i, i, i, i, P, i, P]
+        L.oracle_forward_fp8.restype = None
+        L.oracle_forward_fp8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P, P, P, P, P]
+        L.oracle_num_threads.restype = i
+        L.oracle_init()
+        _lib = L
+    return _lib
+
+
+def _np(a, dtype):
+    """Contiguous numpy view/copy of a tensor or array with the given dtype."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().contiguous()
+            if a.dtype == torch.bfloat16:
+                a = a.view(torch.int16)
+            elif a.dtype == torch.float8_e4m3fn:
+                a = a.view(torch.uint8)
+            a = a.numpy()
+    except ImportError:
+        pass
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        if dtype in (np.uint16, np.uint8) and a.dtype.itemsize == np.dtype(dtype).itemsize:
+            a = a.view(dtype)
+        else:
+            a = a.astype(dtype)
+    return a
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def bf16_value(code: int) -> float:
+    return lib().oracle_bf16_value(int(code))
+
+
+def e4m3_value(code: int) -> float:
+    return lib().oracle_e4m3_value(int(code))
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().oracle_e4m3_encode(float(v))
+
+
+def e4m3_encode_array(v) -> np.ndarray:
+    v = _np(v, np.float32).reshape(-1)
+    L = lib()
+    return np.array([L.oracle_e4m3_encode(float(x)) for x in v], dtype=np.uint8)
+
+
+def quant_row(v):
+    """Per-row e4m3 quantisation of fp32 values -> (codes uint8[n], scale float)."""
+    v = _np(v, np.float32).reshape(-1)
+    codes = np.zeros(v.size, dtype=np.uint8)
+    scale = np.zeros(1, dtype=np.float32)
+    lib().oracle_quant_row(_p(v), v.size, _p(codes), _p(scale))
+    return codes, float(scale[0])
+
+
+def quant_rows_bf16(x):
+    """Per-token quantisation of bf16 x [T][H] -> (codes uint8[T][H], scales fp32[T])."""
+    xa = _np(x, np.uint16)
+    T, H = xa.shape
+    codes = np.zeros((T, H), dtype=np.uint8)
+    scales = np.zeros(T, dtype=np.float32)
+    lib().oracle_quant_rows_bf16(_p(xa), T, H, _p(codes), _p(scales))
+    return codes, scales
+
+
+def max_tasks(P: int, E: int, BM: int) -> int:
+    return P // BM + min(E, P)
+
+
+def route(ids, E: int, BM: int):
+    """Routing & index build.  Returns a dict of numpy int32 arrays:
+    offsets[E+1], sorted[P], pos[P], tasks[num_tasks][4], num_tasks, num_dropped."""
+    ida = _np(ids, np.int32).reshape(-1)
+    P = ida.size
+    mt = max_tasks(P, E, BM)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    srt = np.zeros(max(P, 1), dtype=np.int32)
+    pos = np.zeros(max(P, 1), dtype=np.int32)
+    tasks = np.zeros((max(mt, 1), 4), dtype=np.int32)
+    nt = np.zeros(1, dtype=np.int32)
+    nd = np.zeros(1, dtype=np.int32)
+    rc = lib().oracle_route(_p(ida), P, E, BM, _p(offsets), _p(srt), _p(pos), _p(tasks), mt,
+                            _p(nt), _p(nd))
+    if rc != 0:
+        raise RuntimeError("oracle_route: task list overflow")
+    n = int(nt[0])
+    return {"offsets": offsets, "sorted": srt[:P], "pos": pos[:P], "tasks": tasks[:n].copy(),
+            "num_tasks": n, "num_dropped": int(nd[0])}
+
+
+def _rows_arg(rows, T):
+    if rows is None:
+        return None, T
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1))
+    if r.size and (r.min() < 0 or r.max() >= T):
+        raise ValueError("row index out of range")
+    return r, r.size
+
+
+def _forward_plain(fname, x, topk_w, ids, W1, W2, dt, rows):
+    xa = _np(x, dt)
+    T, H = xa.shape
+    ida = _np(ids, np.int32)
+    k = ida.shape[1] if ida.ndim == 2 else 1
+    wa = _np(topk_w, np.float32)
+    W1a = _np(W1, dt)
+    W2a = _np(W2, dt)
+    E, I2, H1 = W1a.shape
+    I = I2 // 2
+    assert H1 == H and W2a.shape == (E, H, I)
+    r, n = _rows_arg(rows, T)
+    out = np.zeros((n, H), dtype=np.float64)
+    getattr(lib(), fname)(_p(xa), _p(wa), _p(ida), _p(W1a), _p(W2a), T, k, E, H, I,
+                          _p(r) if r is not None else None, n, _p(out))
+    return out
+
+
+def forward_f64(x, topk_w, ids, W1, W2, rows=None):
+    """Layer output in fp64 from fp64 inputs; rows = token subset (default all)."""
+    return _forward_plain("oracle_forward_f64", x, topk_w, ids, W1, W2, np.float64, rows)
+
+
+def forward_f32(x, topk_w, ids, W1, W2, rows=None):
+    return _forward_plain("oracle_forward_f32", x, topk_w, ids, W1, W2, np.float32, rows)
+
+
+def forward_bf16(x, topk_w, ids, W1, W2, rows=None):
+    """Layer output in fp64 from bf16 x/W1/W2 (torch bf16 tensors or uint16 codes)."""
+    return _forward_plain("oracle_forward_bf16", x, topk_w, ids, W1, W2, np.uint16, rows)
+
+
+def forward_fp8(x, topk_w, ids, W1, s1, W2, s2, rows=None, want_quant=False):
+    """fp8 w8a8 layer output in fp64.  x bf16 [T][H]; W1/W2 e4m3 codes; s1 [E][2I],
+    s2 [E][H] fp32.  With want_quant also returns (xq, sx, hq, sh) of the rows."""
+    xa = _np(x, np.uint16)
+    T, H = xa.shape
+    ida = _np(ids, np.int32)
+    k = ida.shape[1]
+    wa = _np(topk_w, np.float32)
+    W1a = _np(W1, np.uint8)
+    W2a = _np(W2, np.uint8)
+    s1a = _np(s1, np.float32)
+    s2a = _np(s2, np.float32)
+    E, I2, _ = W1a.shape
+    I = I2 // 2
+    r, n = _rows_arg(rows, T)
+    out = np.zeros((n, H), dtype=np.float64)
+    xq = sx = hq = sh = None
+    if want_quant:
+        xq = np.zeros((n, H), dtype=np.uint8)
+        sx = np.zeros(n, dtype=np.float32)
+        hq = np.zeros((n, k, I), dtype=np.uint8)
+        sh = np.zeros((n, k), dtype=np.float32)
+    lib().oracle_forward_fp8(_p(xa), _p(wa), _p(ida), _p(W1a), _p(s1a), _p(W2a), _p(s2a),
+                             T, k, E, H, I, _p(r) if r is not None else None, n, _p(out),
+                             _p(xq) if want_quant else None, _p(sx) if want_quant else None,
+                             _p(hq) if want_quant else None, _p(sh) if want_quant else None)
+    if want_quant:
+        return out, (xq, sx, hq, sh)
+    return out

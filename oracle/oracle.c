@@ -1,0 +1,401 @@
+/*
+ * Plain CPU oracle of the fused Mixture-of-Experts layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file or the library built from it; only the tests, the smoke
+ * check and the benchmark's CPU-baseline leg use it.  It shares no code,
+ * header, table or constant generator with the HIP library.
+ *
+ * What it computes (HPC-Ops x SGLang blog, section "MoE: reducing overhead
+ * around small expert GEMMs"): the routed SwiGLU mixture
+ *
+ *     out[t] = sum_j w[t][j] * W2[e_j] * ( SiLU(W1g[e_j] x[t]) * (W1u[e_j] x[t]) )
+ *
+ * The fused pipeline of that section (routing and index build, gate-up
+ * through the route index, SiLU-and-mul with FP8 requant, down GEMM, top-k
+ * weighted reduction back to token order) changes the data flow, not the
+ * result, so this oracle is the plain definition: a loop over tokens, and
+ * for each token a loop over its k experts in ascending j, in fp64.
+ *
+ * Readings of points the pages leave open (each also listed in the design
+ * notes of the repository):
+ *  - W1[e] is [2I][H]: rows [0,I) gate, rows [I,2I) up (the SGLang guide,
+ *    section 4.1, stacks gate and up into 2*I rows and halves N after
+ *    silu_and_mul).  W2[e] is [H][I].
+ *  - SiLU(g) = g * sigmoid(g) = g / (1 + exp(-g)).
+ *  - The routing weight multiplies the down projection's output of that
+ *    pair, in the top-k weighted reduction.
+ *  - An expert id outside [0, E) marks a dropped pair: it belongs to no
+ *    expert and adds nothing to the output.  Duplicate ids of one token are
+ *    separate pairs and both count.
+ *  - Within an expert's contiguous range of the routing, pairs are in
+ *    ascending pair index p = t*k + j (a stable counting sort).
+ *  - The per-tile task map is a flat expert-major list of row tiles of
+ *    height BM; a partial last tile carries its row count.
+ *  - FP8 is OCP E4M3 ("e4m3fn": bias 7, max finite 448, no infinities,
+ *    NaN = S.1111.111).  Per-row activation quantisation: amax = max|v|,
+ *    scale = fp32(amax/448), inv = fp32(448/amax) (both divisions in fp64,
+ *    then rounded to fp32), code = e4m3_rne_satfinite(fp32(v * inv)); an
+ *    all-zero row gets scale 1 and all codes 0.  x is quantised per token;
+ *    the intermediate is quantised per (token, expert) row.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off (no -ffast-math), so every fp64
+ * sum keeps the order written here.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double BF16_VALUE[65536];
+static double E4M3_VALUE[256];
+static int tables_ready = 0;
+
+/* Value tables built from the two format definitions (sign, biased
+ * exponent, mantissa), not from any bit reinterpretation. */
+void oracle_init(void)
+{
+    if (tables_ready)
+        return;
+    for (int c = 0; c < 65536; c++) {
+        int s = c >> 15, ex = (c >> 7) & 0xFF, m = c & 0x7F;
+        double v;
+        if (ex == 0xFF)
+            v = m ? NAN : INFINITY;
+        else if (ex == 0)
+            v = ldexp((double)m, -126 - 7);          /* 0.m * 2^-126 */
+        else
+            v = ldexp(128.0 + m, ex - 127 - 7);      /* 1.m * 2^(ex-127) */
+        BF16_VALUE[c] = s ? -v : v;
+    }
+    for (int c = 0; c < 256; c++) {
+        int s = c >> 7, ex = (c >> 3) & 0xF, m = c & 7;
+        double v;
+        if (ex == 15 && m == 7)
+            v = NAN;
+        else if (ex == 0)
+            v = ldexp((double)m, -6 - 3);            /* 0.m * 2^-6 */
+        else
+            v = ldexp(8.0 + m, ex - 7 - 3);          /* 1.m * 2^(ex-7) */
+        E4M3_VALUE[c] = s ? -v : v;
+    }
+    tables_ready = 1;
+}
+
+double oracle_bf16_value(int code) { oracle_init(); return BF16_VALUE[code & 0xFFFF]; }
+double oracle_e4m3_value(int code) { oracle_init(); return E4M3_VALUE[code & 0xFF]; }
+
+/* Nearest E4M3 value to v, ties to the even mantissa (code LSB 0),
+ * saturating to +-448.  Codes 0..126 are the non-negative finite values in
+ * ascending order, so the two neighbours of |v| are found by bisection. */
+int oracle_e4m3_encode(float v)
+{
+    oracle_init();
+    if (isnan(v))
+        return 0x7F;
+    int sign = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    int lo = 0, hi = 126;                 /* invariant: E4M3_VALUE[lo] <= a */
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (E4M3_VALUE[mid] <= a)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    int c = lo;
+    if (lo < 126) {
+        double below = a - E4M3_VALUE[lo];
+        double above = E4M3_VALUE[lo + 1] - a;
+        if (above < below || (above == below && (lo & 1)))
+            c = lo + 1;
+    }
+    return sign | c;
+}
+
+/* Per-row activation quantisation rule (see header).  v holds fp32 values. */
+void oracle_quant_row(const float *v, int n, uint8_t *codes, float *scale)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; i++) {
+        float a = fabsf(v[i]);
+        if (a > amax)
+            amax = a;
+    }
+    if (amax == 0.0f) {
+        *scale = 1.0f;
+        memset(codes, 0, (size_t)n);
+        return;
+    }
+    float s = (float)((double)amax / 448.0);
+    float inv = (float)(448.0 / (double)amax);
+    for (int i = 0; i < n; i++) {
+        float prod = v[i] * inv;          /* one fp32 multiply */
+        codes[i] = (uint8_t)oracle_e4m3_encode(prod);
+    }
+    *scale = s;
+}
+
+/* Per-token quantisation of bf16 rows x[T][H] (the fp8 path's first step). */
+void oracle_quant_rows_bf16(const uint16_t *x, int T, int H, uint8_t *codes, float *scales)
+{
+    oracle_init();
+    float *row = (float *)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
+    for (int t = 0; t < T; t++) {
+        for (int h = 0; h < H; h++)
+            row[h] = (float)BF16_VALUE[x[(size_t)t * H + h]];
+        oracle_quant_row(row, H, codes + (size_t)t * H, scales + t);
+    }
+    free(row);
+}
+
+/* ------------------------------------------------------------------------
+ * Routing and index build (blog section "MoE", routing & index build):
+ * a counting pass over the top-k expert ids that gives every expert a
+ * contiguous output range, the route index (sorted position -> pair and
+ * its inverse) and a per-tile task map.
+ *
+ *   ids[P]      expert id of pair p = t*k + j
+ *   offsets[E+1] start of each expert's range; offsets[E] = valid pairs
+ *   sorted[P]   pair index at each sorted position; dropped pairs fill
+ *               [offsets[E], P) in ascending p
+ *   pos[P]      inverse of sorted
+ *   tasks[4*n]  {expert, row_begin, rows, 0} row tiles of height BM,
+ *               expert-major; experts without pairs emit none
+ * Returns 0, or -1 if max_tasks is too small.
+ * ---------------------------------------------------------------------- */
+int oracle_route(const int32_t *ids, int P, int E, int BM,
+                 int32_t *offsets, int32_t *sorted, int32_t *pos,
+                 int32_t *tasks, int max_tasks, int32_t *num_tasks, int32_t *num_dropped)
+{
+    int32_t *count = (int32_t *)calloc((size_t)E + 1, sizeof(int32_t));
+    int32_t *cursor = (int32_t *)calloc((size_t)E + 1, sizeof(int32_t));
+    for (int p = 0; p < P; p++) {
+        int e = ids[p];
+        if (e >= 0 && e < E)
+            count[e]++;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; e++)
+        offsets[e + 1] = offsets[e] + count[e];
+    for (int e = 0; e < E; e++)
+        cursor[e] = offsets[e];
+    int dropped_cursor = offsets[E];
+    for (int p = 0; p < P; p++) {
+        int e = ids[p];
+        int r;
+        if (e >= 0 && e < E)
+            r = cursor[e]++;
+        else
+            r = dropped_cursor++;
+        sorted[r] = p;
+        pos[p] = r;
+    }
+    *num_dropped = P - offsets[E];
+    int n = 0, rc = 0;
+    for (int e = 0; e < E; e++) {
+        for (int m0 = 0; m0 < count[e]; m0 += BM) {
+            if (n >= max_tasks) {
+                rc = -1;
+                continue;
+            }
+            int rows = count[e] - m0 < BM ? count[e] - m0 : BM;
+            tasks[4 * n + 0] = e;
+            tasks[4 * n + 1] = offsets[e] + m0;
+            tasks[4 * n + 2] = rows;
+            tasks[4 * n + 3] = 0;
+            n++;
+        }
+    }
+    *num_tasks = n;
+    free(count);
+    free(cursor);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * Forward pass.  Matrices are viewed through a tag so one plain loop serves
+ * fp64, fp32, bf16-code and e4m3-code storage; a row is decoded to fp64
+ * before use.
+ * ---------------------------------------------------------------------- */
+enum { K_F64 = 0, K_F32 = 1, K_BF16 = 2, K_E4M3 = 3 };
+
+static void load_row(int kind, const void *base, size_t off, int n, double *dst)
+{
+    switch (kind) {
+    case K_F64: { const double *p = (const double *)base + off; for (int i = 0; i < n; i++) dst[i] = p[i]; break; }
+    case K_F32: { const float *p = (const float *)base + off; for (int i = 0; i < n; i++) dst[i] = (double)p[i]; break; }
+    case K_BF16: { const uint16_t *p = (const uint16_t *)base + off; for (int i = 0; i < n; i++) dst[i] = BF16_VALUE[p[i]]; break; }
+    case K_E4M3: { const uint8_t *p = (const uint8_t *)base + off; for (int i = 0; i < n; i++) dst[i] = E4M3_VALUE[p[i]]; break; }
+    }
+}
+
+static double dot(const double *a, const double *b, int n)
+{
+    double s = 0.0;
+    for (int i = 0; i < n; i++)
+        s += a[i] * b[i];
+    return s;
+}
+
+static double silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* One token of the unquantised layer (x, W1, W2 of any kind). */
+static void token_plain(int xkind, const void *x, int wkind, const void *W1, const void *W2,
+                        const float *topk_w, const int32_t *ids, int t, int k, int E, int H, int I,
+                        double *acc)
+{
+    double *xr = (double *)malloc(sizeof(double) * (size_t)H);
+    double *wr = (double *)malloc(sizeof(double) * (size_t)(H > I ? H : I));
+    double *a = (double *)malloc(sizeof(double) * (size_t)I);
+    load_row(xkind, x, (size_t)t * H, H, xr);
+    for (int m = 0; m < H; m++)
+        acc[m] = 0.0;
+    for (int j = 0; j < k; j++) {
+        int p = t * k + j;
+        int e = ids[p];
+        if (e < 0 || e >= E)
+            continue;
+        double w = (double)topk_w[p];
+        for (int n = 0; n < I; n++) {
+            load_row(wkind, W1, ((size_t)e * 2 * I + n) * H, H, wr);
+            double g = dot(wr, xr, H);
+            load_row(wkind, W1, ((size_t)e * 2 * I + I + n) * H, H, wr);
+            double u = dot(wr, xr, H);
+            a[n] = silu(g) * u;
+        }
+        for (int m = 0; m < H; m++) {
+            load_row(wkind, W2, ((size_t)e * H + m) * I, I, wr);
+            double y = dot(wr, a, I);
+            acc[m] += w * y;
+        }
+    }
+    free(xr);
+    free(wr);
+    free(a);
+}
+
+/* rows[0..nrows) are the tokens to evaluate (NULL: all T, nrows = T);
+ * out is [nrows][H] fp64. */
+static void forward_plain(int xkind, const void *x, int wkind, const void *W1, const void *W2,
+                          const float *topk_w, const int32_t *ids, int T, int k, int E, int H, int I,
+                          const int32_t *rows, int nrows, double *out)
+{
+    oracle_init();
+    if (!rows)
+        nrows = T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; r++) {
+        int t = rows ? rows[r] : r;
+        token_plain(xkind, x, wkind, W1, W2, topk_w, ids, t, k, E, H, I, out + (size_t)r * H);
+    }
+}
+
+void oracle_forward_f64(const double *x, const float *topk_w, const int32_t *ids,
+                        const double *W1, const double *W2, int T, int k, int E, int H, int I,
+                        const int32_t *rows, int nrows, double *out)
+{
+    forward_plain(K_F64, x, K_F64, W1, W2, topk_w, ids, T, k, E, H, I, rows, nrows, out);
+}
+
+void oracle_forward_f32(const float *x, const float *topk_w, const int32_t *ids,
+                        const float *W1, const float *W2, int T, int k, int E, int H, int I,
+                        const int32_t *rows, int nrows, double *out)
+{
+    forward_plain(K_F32, x, K_F32, W1, W2, topk_w, ids, T, k, E, H, I, rows, nrows, out);
+}
+
+void oracle_forward_bf16(const uint16_t *x, const float *topk_w, const int32_t *ids,
+                         const uint16_t *W1, const uint16_t *W2, int T, int k, int E, int H, int I,
+                         const int32_t *rows, int nrows, double *out)
+{
+    forward_plain(K_BF16, x, K_BF16, W1, W2, topk_w, ids, T, k, E, H, I, rows, nrows, out);
+}
+
+/* One token of the fp8 w8a8 layer.  x is bf16; W1/W2 are e4m3 codes with
+ * one fp32 scale per output channel (s1[e][2I], s2[e][H]). */
+static void token_fp8(const uint16_t *x, const float *topk_w, const int32_t *ids,
+                      const uint8_t *W1, const float *s1, const uint8_t *W2, const float *s2,
+                      int t, int k, int E, int H, int I, double *acc,
+                      uint8_t *xq_out, float *sx_out, uint8_t *hq_out, float *sh_out)
+{
+    float *xf = (float *)malloc(sizeof(float) * (size_t)H);
+    uint8_t *xq = (uint8_t *)malloc((size_t)H);
+    double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+    double *wr = (double *)malloc(sizeof(double) * (size_t)(H > I ? H : I));
+    float *af = (float *)malloc(sizeof(float) * (size_t)I);
+    uint8_t *hq = (uint8_t *)malloc((size_t)I);
+    double *hd = (double *)malloc(sizeof(double) * (size_t)I);
+    float sx;
+
+    for (int h = 0; h < H; h++)
+        xf[h] = (float)BF16_VALUE[x[(size_t)t * H + h]];
+    oracle_quant_row(xf, H, xq, &sx);
+    if (xq_out) {
+        memcpy(xq_out, xq, (size_t)H);
+        *sx_out = sx;
+    }
+    load_row(K_E4M3, xq, 0, H, xd);
+    for (int m = 0; m < H; m++)
+        acc[m] = 0.0;
+    for (int j = 0; j < k; j++) {
+        int p = t * k + j;
+        int e = ids[p];
+        if (e < 0 || e >= E)
+            continue;
+        double w = (double)topk_w[p];
+        for (int n = 0; n < I; n++) {
+            load_row(K_E4M3, W1, ((size_t)e * 2 * I + n) * H, H, wr);
+            double g = (double)sx * (double)s1[(size_t)e * 2 * I + n] * dot(wr, xd, H);
+            load_row(K_E4M3, W1, ((size_t)e * 2 * I + I + n) * H, H, wr);
+            double u = (double)sx * (double)s1[(size_t)e * 2 * I + I + n] * dot(wr, xd, H);
+            af[n] = (float)(silu(g) * u);
+        }
+        float sh;
+        oracle_quant_row(af, I, hq, &sh);
+        if (hq_out) {
+            memcpy(hq_out + (size_t)j * I, hq, (size_t)I);
+            sh_out[j] = sh;
+        }
+        load_row(K_E4M3, hq, 0, I, hd);
+        for (int m = 0; m < H; m++) {
+            load_row(K_E4M3, W2, ((size_t)e * H + m) * I, I, wr);
+            double y = (double)sh * (double)s2[(size_t)e * H + m] * dot(wr, hd, I);
+            acc[m] += w * y;
+        }
+    }
+    free(xf); free(xq); free(xd); free(wr); free(af); free(hq); free(hd);
+}
+
+/* fp8 w8a8 forward.  Optional outputs (may be NULL): xq_out [nrows][H] and
+ * sx_out [nrows] (the token's quantised activations), hq_out [nrows][k][I]
+ * and sh_out [nrows][k] (each pair's quantised intermediate; rows of
+ * dropped pairs are left untouched). */
+void oracle_forward_fp8(const uint16_t *x, const float *topk_w, const int32_t *ids,
+                        const uint8_t *W1, const float *s1, const uint8_t *W2, const float *s2,
+                        int T, int k, int E, int H, int I, const int32_t *rows, int nrows,
+                        double *out, uint8_t *xq_out, float *sx_out, uint8_t *hq_out, float *sh_out)
+{
+    oracle_init();
+    if (!rows)
+        nrows = T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; r++) {
+        int t = rows ? rows[r] : r;
+        token_fp8(x, topk_w, ids, W1, s1, W2, s2, t, k, E, H, I, out + (size_t)r * H,
+                  xq_out ? xq_out + (size_t)r * H : NULL, sx_out ? sx_out + r : NULL,
+                  hq_out ? hq_out + (size_t)r * k * I : NULL, sh_out ? sh_out + (size_t)r * k : NULL);
+    }
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
