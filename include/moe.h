@@ -1,0 +1,199 @@
+/*
+ * moe.h -- C ABI of the fused Mixture-of-Experts layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer (HPC-Ops x SGLang blog, section "MoE: reducing overhead around
+ * small expert GEMMs") computes, for every token t with top-k expert ids
+ * e_j and routing weights w[t][j],
+ *
+ *     out[t] = sum_j w[t][j] * W2[e_j] ( SiLU(W1g[e_j] x[t]) * (W1u[e_j] x[t]) )
+ *
+ * as a pipeline of hand-written HIP kernels: a routing/index build that
+ * counting-sorts token-expert pairs in LDS into contiguous per-expert
+ * ranges plus a per-tile task map; a grouped gate-up GEMM on MFMA that
+ * reads tokens through the route index (no gather buffer); one fused
+ * kernel for SiLU-and-mul and, on the fp8 path, the per-row FP8
+ * requantisation; a grouped down GEMM; and a top-k weighted reduction back
+ * to token order.
+ *
+ * Conventions for every entry point
+ *  - Pointers marked (device) are device memory on the current HIP device;
+ *    (host) are host memory.  The caller owns every buffer: the library
+ *    never allocates or frees memory and keeps no per-call state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every device-side step is enqueued asynchronously on it; no call
+ *    synchronises, allocates or reads device memory from the host, so the
+ *    calls can be captured into a HIP graph.  Grids depend only on the
+ *    host-side sizes, so one capture serves any routing at those sizes.
+ *  - Shapes: T tokens (0 <= T, T*k <= 65536), k experts per token
+ *    (1..16), E experts (1..256), hidden size H and expert intermediate
+ *    size I (positive multiples of 64, at most 65536).
+ *  - Layouts (row-major, last index contiguous):
+ *      x        [T][H]      bf16 hidden states
+ *      topk_ids [T][k]      int32 expert ids; an id outside [0, E) marks a
+ *                           dropped pair (it adds nothing to the output);
+ *                           duplicate ids of one token are separate pairs
+ *      topk_w   [T][k]      fp32 routing weights
+ *      W1       [E][2I][H]  gate rows [0, I), up rows [I, 2I)
+ *      W2       [E][H][I]
+ *      out      [T][H]      bf16
+ *    bf16 is IEEE binary16-brain (1/8/7); fp8 is OCP E4M3 ("e4m3fn",
+ *    max finite 448).
+ *  - Stage order: [fp8: quantise x] -> gate-up GEMM -> SiLU-and-mul
+ *    [+ fp8 requant] -> down GEMM -> top-k weighted reduction, all on
+ *    `stream`.
+ *  - Return value: MOE_OK (0) or a negative moe_status_t.  Argument errors
+ *    are detected on the host before anything is enqueued; nothing is
+ *    launched when a call fails.  T == 0 returns MOE_OK with no launch.
+ *    No C++ exception crosses this interface.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,        /* null pointer, bad count, misaligned buffer */
+    MOE_ERR_UNSUPPORTED_SHAPE = -2,  /* H or I not a multiple of 64, T*k > 65536, ... */
+    MOE_ERR_BUFFER_TOO_SMALL = -3,   /* routing buffer or workspace smaller than required */
+    MOE_ERR_HIP = -4                 /* a HIP runtime call or kernel launch failed */
+} moe_status_t;
+
+typedef enum {
+    MOE_DTYPE_BF16 = 0,      /* bf16 activations and weights, fp32 accumulation */
+    MOE_DTYPE_FP8_W8A8 = 1   /* e4m3 weights (per-output-channel fp32 scales) and
+                                e4m3 activations (per-row fp32 scales) */
+} moe_dtype_t;
+
+/* One row tile of the task map: rows [row_begin, row_begin + rows) of the
+ * expert-sorted order, all routed to `expert`; rows <= block_m. */
+typedef struct {
+    int32_t expert;
+    int32_t row_begin;
+    int32_t rows;
+    int32_t reserved;   /* 0 */
+} moe_task_t;
+
+/* First 64 bytes of a routing buffer, written by moe_build_routing_*. */
+typedef struct {
+    int32_t num_tasks;     /* valid entries of the task map */
+    int32_t num_dropped;   /* pairs whose id is outside [0, E) */
+    int32_t block_m;       /* tile height the task map was cut with */
+    int32_t num_pairs;     /* P = T * k */
+    int32_t num_experts;   /* E */
+    int32_t max_tasks;     /* capacity of the task map */
+    int32_t reserved[10];
+} moe_routing_header_t;
+
+/* Byte offsets of the parts of a routing buffer (all 16-byte aligned). */
+typedef struct {
+    size_t header;           /* moe_routing_header_t */
+    size_t expert_offsets;   /* int32 [E+1]: expert e owns sorted rows
+                                [expert_offsets[e], expert_offsets[e+1]);
+                                expert_offsets[E] = number of valid pairs */
+    size_t sorted_pairs;     /* int32 [P]: pair index p = t*k + j at each sorted
+                                row; valid pairs ascending in p within each
+                                expert, then dropped pairs ascending in p */
+    size_t pair_pos;         /* int32 [P]: sorted row of pair p (inverse) */
+    size_t tasks;            /* moe_task_t [max_tasks]: expert-major row tiles */
+    size_t total_bytes;      /* minimum size of the routing buffer */
+    int32_t block_m;         /* tile height chosen for these sizes and dtype */
+    int32_t max_tasks;       /* P / block_m + min(E, P) */
+} moe_routing_layout_t;
+
+/* Byte offsets of the parts of a forward workspace (all 256-byte aligned);
+ * an offset of (size_t)-1 marks a part the dtype does not use.  The two
+ * GEMMs may split their reduction into split_k1 / split_k2 slices whose
+ * fp32 partial sums are added, in ascending slice order, by the kernel
+ * that consumes them. */
+typedef struct {
+    size_t xq;          /* fp8: uint8 [T][H]   per-token e4m3 codes of x */
+    size_t x_scale;     /* fp8: fp32  [T]      per-token scales of x */
+    size_t g;           /* fp32 [split_k1][P][2I] gate-up partial sums (scaled on fp8) */
+    size_t h;           /* bf16 [P][I] SiLU(gate)*up (bf16), or uint8 e4m3 codes [P][I] (fp8) */
+    size_t h_scale;     /* fp8: fp32  [P]      per-row scales of h */
+    size_t y;           /* fp32 [split_k2][P][H] unweighted down-projection partial sums */
+    size_t total_bytes; /* minimum size of the workspace */
+    int32_t split_k1;   /* slices of the gate-up reduction over H */
+    int32_t split_k2;   /* slices of the down reduction over I */
+} moe_workspace_layout_t;
+
+/* Human-readable name of a status code (static string). */
+const char *moe_status_string(int status);
+
+/* Layout of the routing buffer for these sizes (host-only computation).
+ * dtype is a moe_dtype_t; `out` is a host pointer.  The tile height is a
+ * fixed function of (dtype, T, k, E, H, I), shared by the routing build and
+ * the forward pass. */
+int moe_routing_layout(int T, int k, int E, int H, int I, int dtype,
+                       moe_routing_layout_t *out /* host */);
+
+/* Layout of the forward workspace for these sizes (host-only). */
+int moe_workspace_layout(int T, int k, int E, int H, int I, int dtype,
+                         moe_workspace_layout_t *out /* host */);
+
+/* Routing & index build (blog section "MoE", routing & index build): one
+ * workgroup counting-sorts the P = T*k pairs by expert id in LDS, writing
+ * the header, expert offsets, route index (sorted_pairs, pair_pos) and the
+ * per-tile task map into `routing` (device, 16-byte aligned, at least
+ * moe_routing_layout().total_bytes).  The order is deterministic: stable in
+ * the pair index.  topk_ids (device) is [T][k] int32.  The _bf16 and _fp8
+ * variants differ only in the tile height they cut the task map with,
+ * which must match the forward call of the same dtype. */
+int moe_build_routing_bf16(const int32_t *topk_ids, int T, int k, int E, int H, int I,
+                           void *routing, size_t routing_bytes, void *stream);
+int moe_build_routing_fp8(const int32_t *topk_ids, int T, int k, int E, int H, int I,
+                          void *routing, size_t routing_bytes, void *stream);
+
+/* bf16 forward (blog section "MoE", gate-up & activation, PDL chaining;
+ * operator table: BF16 hidden states).  x (device) bf16 [T][H]; topk_w
+ * (device) fp32 [T][k]; routing (device) built by moe_build_routing_bf16
+ * with the same sizes; w1 (device) bf16 [E][2I][H]; w2 (device) bf16
+ * [E][H][I]; workspace (device, 256-byte aligned, at least
+ * moe_workspace_layout().total_bytes); out (device) bf16 [T][H].
+ * Experts that receive no pair are never read.  Accumulation is fp32; the
+ * intermediate SiLU(gate)*up and the per-pair down rows are stored as bf16;
+ * the top-k reduction adds the pairs of a token in ascending j in fp32. */
+int moe_forward_bf16(const void *x, const float *topk_w, const void *routing,
+                     const void *w1, const void *w2,
+                     int T, int k, int E, int H, int I,
+                     void *workspace, size_t workspace_bytes, void *out, void *stream);
+
+/* fp8 w8a8 forward (operator table: FP8 E4M3 expert weights; gate-up &
+ * activation: FP8 requant before the down GEMM).  As moe_forward_bf16,
+ * except: w1/w2 (device) are e4m3 codes, w1_scale (device) fp32 [E][2I] and
+ * w2_scale (device) fp32 [E][H] are per-output-channel scales.  x is
+ * quantised per token and SiLU(gate)*up per (token, expert) row with the
+ * rule scale = fp32(amax/448), code = e4m3_rne_satfinite(fp32(v *
+ * fp32(448/amax))) (an all-zero row gets scale 1); the e4m3 codes and
+ * scales are left in the workspace (see moe_workspace_layout_t). */
+int moe_forward_fp8(const void *x, const float *topk_w, const void *routing,
+                    const uint8_t *w1, const float *w1_scale,
+                    const uint8_t *w2, const float *w2_scale,
+                    int T, int k, int E, int H, int I,
+                    void *workspace, size_t workspace_bytes, void *out, void *stream);
+
+/* Measurement hook.  When `events` is non-NULL (n >= 10 hipEvent_t
+ * handles, host array), every later forward call records events[2*s]
+ * before and events[2*s+1] after stage s on its stream, for the stages it
+ * runs: 0 activation quantisation (fp8), 1 gate-up GEMM, 2 requantisation
+ * (fp8), 3 down GEMM, 4 top-k reduction.  NULL switches it off.  The
+ * setting is process-wide and not thread-safe; do not enable it while a
+ * forward call is being captured into a graph. */
+int moe_set_stage_events(void *const *events, int n);
+
+/* Number of compute units of the current device as cached by the library
+ * (queried once per device), or a negative status. */
+int moe_device_cu_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

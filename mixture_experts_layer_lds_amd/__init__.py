@@ -1,0 +1,241 @@
+"""Python binding of libmoe.so, the MI355X fused Mixture-of-Experts layer.
+
+The binding only marshals arguments: every step of the layer runs in the
+HIP kernels of libmoe.so (see include/moe.h).  PyTorch provides device
+memory and streams.  There is no fallback path: if the library is missing
+or cannot be loaded, importing this module raises.
+
+Functions carry the C names:
+
+    moe_routing_layout(T, k, E, H, I, dtype)            -> dict (host only)
+    moe_workspace_layout(T, k, E, H, I, dtype)          -> dict (host only)
+    moe_build_routing_bf16(topk_ids, E, H, I, routing)  -> None
+    moe_build_routing_fp8(topk_ids, E, H, I, routing)   -> None
+    moe_forward_bf16(x, topk_w, routing, w1, w2, workspace, out) -> out
+    moe_forward_fp8(x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, out) -> out
+
+plus allocation helpers (alloc_routing, alloc_workspace) and a convenience
+moe_layer() that runs routing + forward with freshly allocated buffers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime that libmoe.so binds to
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_DTYPE_BF16 = 0
+MOE_DTYPE_FP8_W8A8 = 1
+DTYPES = {"bf16": MOE_DTYPE_BF16, "fp8": MOE_DTYPE_FP8_W8A8}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, name, status):
+        self.status = status
+        super().__init__(f"{name} failed: {status} ({status_string(status)})")
+
+
+class RoutingLayout(ctypes.Structure):
+    _fields_ = [("header", ctypes.c_size_t), ("expert_offsets", ctypes.c_size_t),
+                ("sorted_pairs", ctypes.c_size_t), ("pair_pos", ctypes.c_size_t),
+                ("tasks", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t),
+                ("block_m", ctypes.c_int32), ("max_tasks", ctypes.c_int32)]
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [("xq", ctypes.c_size_t), ("x_scale", ctypes.c_size_t), ("g", ctypes.c_size_t),
+                ("h", ctypes.c_size_t), ("h_scale", ctypes.c_size_t), ("y", ctypes.c_size_t),
+                ("total_bytes", ctypes.c_size_t), ("split_k1", ctypes.c_int32),
+                ("split_k2", ctypes.c_int32)]
+
+
+EXPORTS = ("moe_status_string", "moe_routing_layout", "moe_workspace_layout",
+           "moe_build_routing_bf16", "moe_build_routing_fp8", "moe_forward_bf16",
+           "moe_forward_fp8", "moe_set_stage_events", "moe_device_cu_count")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m mixture_experts_layer_lds_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i, P, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_status_string.argtypes = [i]
+    L.moe_routing_layout.restype = i
+    L.moe_routing_layout.argtypes = [i, i, i, i, i, i, ctypes.POINTER(RoutingLayout)]
+    L.moe_workspace_layout.restype = i
+    L.moe_workspace_layout.argtypes = [i, i, i, i, i, i, ctypes.POINTER(WorkspaceLayout)]
+    for n in ("moe_build_routing_bf16", "moe_build_routing_fp8"):
+        f = getattr(L, n)
+        f.restype = i
+        f.argtypes = [P, i, i, i, i, i, P, sz, P]
+    L.moe_forward_bf16.restype = i
+    L.moe_forward_bf16.argtypes = [P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
+    L.moe_forward_fp8.restype = i
+    L.moe_forward_fp8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
+    L.moe_set_stage_events.restype = i
+    L.moe_set_stage_events.argtypes = [ctypes.POINTER(P), i]
+    L.moe_device_cu_count.restype = i
+    L.moe_device_cu_count.argtypes = []
+    return L
+
+
+_lib = _load()
+
+
+def status_string(status: int) -> str:
+    return _lib.moe_status_string(int(status)).decode()
+
+
+def _check(name, rc):
+    if rc != 0:
+        raise MoeError(name, rc)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def moe_routing_layout(T, k, E, H, I, dtype="bf16") -> dict:
+    L = RoutingLayout()
+    _check("moe_routing_layout", _lib.moe_routing_layout(T, k, E, H, I, DTYPES[dtype], ctypes.byref(L)))
+    return {f: getattr(L, f) for f, _ in RoutingLayout._fields_}
+
+
+def moe_workspace_layout(T, k, E, H, I, dtype="bf16") -> dict:
+    W = WorkspaceLayout()
+    _check("moe_workspace_layout", _lib.moe_workspace_layout(T, k, E, H, I, DTYPES[dtype], ctypes.byref(W)))
+    return {f: getattr(W, f) for f, _ in WorkspaceLayout._fields_}
+
+
+def alloc_routing(T, k, E, H, I, dtype="bf16", device="cuda"):
+    n = moe_routing_layout(T, k, E, H, I, dtype)["total_bytes"]
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def alloc_workspace(T, k, E, H, I, dtype="bf16", device="cuda"):
+    n = moe_workspace_layout(T, k, E, H, I, dtype)["total_bytes"]
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _shape_tk(topk_ids):
+    if topk_ids.dim() != 2 or topk_ids.dtype != torch.int32 or not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be a contiguous int32 [T][k] tensor")
+    return topk_ids.shape
+
+
+def _build_routing(fn, name, topk_ids, E, H, I, routing, stream):
+    T, k = _shape_tk(topk_ids)
+    _check(name, fn(_ptr(topk_ids), T, k, E, H, I, _ptr(routing), routing.numel(), _stream(stream)))
+
+
+def moe_build_routing_bf16(topk_ids, E, H, I, routing, stream=None):
+    _build_routing(_lib.moe_build_routing_bf16, "moe_build_routing_bf16", topk_ids, E, H, I, routing, stream)
+
+
+def moe_build_routing_fp8(topk_ids, E, H, I, routing, stream=None):
+    _build_routing(_lib.moe_build_routing_fp8, "moe_build_routing_fp8", topk_ids, E, H, I, routing, stream)
+
+
+def _check_tensor(name, t, dtype, shape):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
+def moe_forward_bf16(x, topk_w, routing, w1, w2, workspace, out, stream=None):
+    T, H = x.shape
+    k = topk_w.shape[1]
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    _check_tensor("x", x, torch.bfloat16, (T, H))
+    _check_tensor("topk_w", topk_w, torch.float32, (T, k))
+    _check_tensor("w1", w1, torch.bfloat16, (E, 2 * I, H))
+    _check_tensor("w2", w2, torch.bfloat16, (E, H, I))
+    _check_tensor("out", out, torch.bfloat16, (T, H))
+    _check("moe_forward_bf16", _lib.moe_forward_bf16(
+        _ptr(x), _ptr(topk_w), _ptr(routing), _ptr(w1), _ptr(w2), T, k, E, H, I,
+        _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_forward_fp8(x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, out, stream=None):
+    T, H = x.shape
+    k = topk_w.shape[1]
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    _check_tensor("x", x, torch.bfloat16, (T, H))
+    _check_tensor("topk_w", topk_w, torch.float32, (T, k))
+    _check_tensor("w1", w1, torch.uint8, (E, 2 * I, H))
+    _check_tensor("w1_scale", w1_scale, torch.float32, (E, 2 * I))
+    _check_tensor("w2", w2, torch.uint8, (E, H, I))
+    _check_tensor("w2_scale", w2_scale, torch.float32, (E, H))
+    _check_tensor("out", out, torch.bfloat16, (T, H))
+    _check("moe_forward_fp8", _lib.moe_forward_fp8(
+        _ptr(x), _ptr(topk_w), _ptr(routing), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale),
+        T, k, E, H, I, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_set_stage_events(events):
+    """events: list of 10 torch.cuda.Event(enable_timing=True) (already recorded once), or None."""
+    if events is None:
+        _check("moe_set_stage_events", _lib.moe_set_stage_events(None, 0))
+        return
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _check("moe_set_stage_events", _lib.moe_set_stage_events(arr, len(events)))
+
+
+def moe_device_cu_count() -> int:
+    n = _lib.moe_device_cu_count()
+    if n < 0:
+        raise MoeError("moe_device_cu_count", n)
+    return n
+
+
+def moe_layer(x, topk_ids, topk_w, weights, dtype="bf16", out=None, stream=None):
+    """Routing + forward with freshly allocated routing buffer and workspace.
+
+    weights: {"w1", "w2"} (bf16) or {"w1", "w1_scale", "w2", "w2_scale"} (fp8).
+    Returns (out, routing, workspace)."""
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    E, I2, _ = weights["w1"].shape
+    I = I2 // 2
+    routing = alloc_routing(T, k, E, H, I, dtype, x.device)
+    ws = alloc_workspace(T, k, E, H, I, dtype, x.device)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    if dtype == "bf16":
+        moe_build_routing_bf16(topk_ids, E, H, I, routing, stream)
+        moe_forward_bf16(x, topk_w, routing, weights["w1"], weights["w2"], ws, out, stream)
+    else:
+        moe_build_routing_fp8(topk_ids, E, H, I, routing, stream)
+        moe_forward_fp8(x, topk_w, routing, weights["w1"], weights["w1_scale"], weights["w2"],
+                        weights["w2_scale"], ws, out, stream)
+    return out, routing, ws
+
+
+def read_routing(routing, T, k, E, H, I, dtype="bf16") -> dict:
+    """Copy a routing buffer's parts to host int32 tensors (for tests and tools)."""
+    L = moe_routing_layout(T, k, E, H, I, dtype)
+    b = routing.cpu()
+    P = T * k
+
+    def part(off, n):
+        return b[off:off + 4 * n].view(torch.int32).clone()
+
+    hdr = part(L["header"], 16)
+    nt = int(hdr[0])
+    return {"header": hdr, "num_tasks": nt, "num_dropped": int(hdr[1]), "block_m": int(hdr[2]),
+            "offsets": part(L["expert_offsets"], E + 1), "sorted": part(L["sorted_pairs"], P),
+            "pos": part(L["pair_pos"], P), "tasks": part(L["tasks"], 4 * nt).view(nt, 4),
+            "layout": L}

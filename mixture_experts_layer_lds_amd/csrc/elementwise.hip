@@ -1,0 +1,177 @@
+// Row-wise stages of the fused MoE layer: per-token FP8 quantisation of the
+// hidden states, SiLU-and-mul (+ FP8 requantisation) of the gate-up
+// output, and the top-k weighted reduction back to token order
+// (HPC-Ops x SGLang blog, section "MoE": gate-up & activation; PDL chaining
+// paragraph for the final reduction).
+//
+// All three are HBM-bound streaming kernels: 16-byte vector loads along the
+// contiguous dimension, one workgroup per row, no LDS beyond a 4-wave
+// max-reduction.
+#include "moe_common.h"
+
+namespace moe {
+
+constexpr int kRowThreads = 256;
+
+__device__ __forceinline__ float block_max_256(float v, float* s_red) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  float r = __builtin_fmaxf(__builtin_fmaxf(s_red[0], s_red[1]), __builtin_fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+  return r;
+}
+
+// x[T][H] bf16 -> xq[T][H] e4m3 + scale[T]; H % 8 == 0.
+__global__ void __launch_bounds__(kRowThreads)
+quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restrict__ xq,
+                       float* __restrict__ scale) {
+  __shared__ float s_red[4];
+  const int t = blockIdx.x;
+  const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
+  const int nvec = H / 8;
+  float amax = 0.0f;
+  for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
+    const u32x4 v = row[i];
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_bits_to_f32(v[w] & 0xffffu)));
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_bits_to_f32(v[w] >> 16)));
+    }
+  }
+  amax = block_max_256(amax, s_red);
+  float sc, inv;
+  e4m3_row_scales(amax, &sc, &inv);
+  u32x2* out = reinterpret_cast<u32x2*>(xq + (size_t)t * H);
+  for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
+    const u32x4 v = row[i];
+    float f[8];
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      f[2 * w] = __fmul_rn(bf16_bits_to_f32(v[w] & 0xffffu), inv);
+      f[2 * w + 1] = __fmul_rn(bf16_bits_to_f32(v[w] >> 16), inv);
+    }
+    u32x2 q;
+    q.x = f32x4_to_e4m3x4_sat(f[0], f[1], f[2], f[3]);
+    q.y = f32x4_to_e4m3x4_sat(f[4], f[5], f[6], f[7]);
+    out[i] = q;
+  }
+  if (threadIdx.x == 0) scale[t] = sc;
+}
+
+// h[r][n] = SiLU(sum_s g[s][r][n]) * sum_s g[s][r][I + n] for the valid sorted
+// rows r < expert_offsets[E].  FP8 = false: bf16 h.  FP8 = true: the row is
+// computed twice, first for its amax, then quantised with the per-row rule.
+template <bool FP8>
+__global__ void __launch_bounds__(kRowThreads)
+act_kernel(const float* __restrict__ g, int S, int P, int I,
+           const int32_t* __restrict__ expert_offsets, int E, void* __restrict__ h,
+           float* __restrict__ h_scale) {
+  __shared__ float s_red[4];
+  const int r = blockIdx.x;
+  if (r >= expert_offsets[E]) return;   // block-uniform
+  const size_t slice = (size_t)P * 2 * I;
+  const float* grow = g + (size_t)r * 2 * I;
+  const int nvec = I / 4;
+  auto load_h4 = [&](int i) {
+    f32x4 gs = *reinterpret_cast<const f32x4*>(grow + 4 * i);
+    f32x4 us = *reinterpret_cast<const f32x4*>(grow + I + 4 * i);
+    for (int s = 1; s < S; s++) {
+      gs += *reinterpret_cast<const f32x4*>(grow + s * slice + 4 * i);
+      us += *reinterpret_cast<const f32x4*>(grow + s * slice + I + 4 * i);
+    }
+    f32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; w++) o[w] = silu_f32(gs[w]) * us[w];
+    return o;
+  };
+  if (!FP8) {
+    uint16_t* hrow = static_cast<uint16_t*>(h) + (size_t)r * I;
+    for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
+      const f32x4 o = load_h4(i);
+      u32x2 packed;
+      packed.x = (uint32_t)f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16);
+      packed.y = (uint32_t)f32_to_bf16_bits(o[2]) | ((uint32_t)f32_to_bf16_bits(o[3]) << 16);
+      *reinterpret_cast<u32x2*>(hrow + 4 * i) = packed;
+    }
+    return;
+  }
+  float amax = 0.0f;
+  for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
+    const f32x4 o = load_h4(i);
+#pragma unroll
+    for (int w = 0; w < 4; w++) amax = __builtin_fmaxf(amax, __builtin_fabsf(o[w]));
+  }
+  amax = block_max_256(amax, s_red);
+  float sc, inv;
+  e4m3_row_scales(amax, &sc, &inv);
+  uint32_t* qrow = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(h) + (size_t)r * I);
+  for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
+    const f32x4 o = load_h4(i);
+    qrow[i] = f32x4_to_e4m3x4_sat(__fmul_rn(o[0], inv), __fmul_rn(o[1], inv),
+                                  __fmul_rn(o[2], inv), __fmul_rn(o[3], inv));
+  }
+  if (threadIdx.x == 0) h_scale[r] = sc;
+}
+
+// out[t][:] = bf16( sum_{j ascending, pair valid} w[t][j] * sum_s y[s][pos][:] ).
+__global__ void __launch_bounds__(kRowThreads)
+reduce_kernel(const float* __restrict__ y, int S, int P, const float* __restrict__ topk_w,
+              const int32_t* __restrict__ pair_pos, const int32_t* __restrict__ expert_offsets,
+              int E, int k, int H, uint16_t* __restrict__ out) {
+  const int t = blockIdx.x;
+  const int valid = expert_offsets[E];
+  const size_t slice = (size_t)P * H;
+  const int nvec = H / 4;
+  for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < k; j++) {
+      const int p = t * k + j;
+      const int r = pair_pos[p];
+      if (r >= valid) continue;   // dropped pair
+      const float* yrow = y + (size_t)r * H + 4 * i;
+      f32x4 v = *reinterpret_cast<const f32x4*>(yrow);
+      for (int s = 1; s < S; s++) v += *reinterpret_cast<const f32x4*>(yrow + s * slice);
+      const float w = topk_w[p];
+#pragma unroll
+      for (int q = 0; q < 4; q++) acc[q] = __fadd_rn(acc[q], __fmul_rn(w, v[q]));
+    }
+    u32x2 packed;
+    packed.x = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
+    packed.y = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+    *reinterpret_cast<u32x2*>(out + (size_t)t * H + 4 * i) = packed;
+  }
+}
+
+}  // namespace moe
+
+namespace moe_host {
+
+hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* scale,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(moe::quant_rows_bf16_kernel, dim3(T), dim3(moe::kRowThreads), 0, s, x, H,
+                     xq, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_act(const float* g, int S, int P, int I, const int32_t* expert_offsets, int E,
+                      bool fp8, void* h, float* h_scale, hipStream_t s) {
+  if (fp8)
+    hipLaunchKernelGGL(moe::act_kernel<true>, dim3(P), dim3(moe::kRowThreads), 0, s, g, S, P, I,
+                       expert_offsets, E, h, h_scale);
+  else
+    hipLaunchKernelGGL(moe::act_kernel<false>, dim3(P), dim3(moe::kRowThreads), 0, s, g, S, P,
+                       I, expert_offsets, E, h, h_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const float* y, int S, int P, const float* topk_w,
+                         const int32_t* pair_pos, const int32_t* expert_offsets, int E, int T,
+                         int k, int H, uint16_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(moe::reduce_kernel, dim3(T), dim3(moe::kRowThreads), 0, s, y, S, P, topk_w,
+                     pair_pos, expert_offsets, E, k, H, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe_host

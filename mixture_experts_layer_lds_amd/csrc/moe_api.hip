@@ -1,0 +1,363 @@
+// C ABI of the fused MoE layer: argument checks, buffer layouts, the tile
+// plan and the launch sequence.  See include/moe.h for the contract.
+//
+// The launch path is plain C++ over the HIP runtime with native-type
+// arguments and a per-device cache of the compute-unit count, so no Python
+// sits between the caller and the kernels (the FlagOS C++ launch wrapper
+// article makes the same point about interpreter overhead on the launch
+// path).
+#include <mutex>
+
+#include "moe_common.h"
+
+namespace {
+
+using moe_host::GemmArgs;
+using moe_host::GemmPlan;
+
+constexpr size_t kNone = ~(size_t)0;
+constexpr long kTargetItems = 2048;   // work items that fill 256 CUs x 8 waves
+
+struct Plan {
+  int block_m = 16;
+  int mb = 1;
+  int max_tasks = 0;
+  int split1 = 1, unroll1 = 1;   // gate-up: K = H
+  int split2 = 1, unroll2 = 1;   // down:    K = I
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_shape(int T, int k, int E, int H, int I) {
+  if (T < 0 || k < 1 || k > moe::kMaxTopK || E < 1 || E > moe::kMaxExperts || H <= 0 || I <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (H % 64 || I % 64 || H > 65536 || I > 65536) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if ((long)T * k > moe::kMaxPairs) return MOE_ERR_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
+int choose_unroll(int nsteps, int mb) {
+  const int maxu = mb >= 2 ? 2 : 4;
+  for (int u = maxu; u > 1; u >>= 1)
+    if (nsteps % u == 0) return u;
+  return 1;
+}
+
+// Largest power-of-two K split (<= 16) that keeps >= 2 pipeline groups per
+// slice and stops once the estimated work items reach the target.
+int choose_split(int nsteps, int unroll, long items) {
+  const int groups = nsteps / unroll;
+  int s = 1;
+  while (s < 16 && items * s < kTargetItems && groups % (2 * s) == 0 && groups / (2 * s) >= 2)
+    s *= 2;
+  return s;
+}
+
+// Tile plan: a fixed function of the shape and dtype, shared by the routing
+// build, the workspace layout and the forward pass.
+Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
+  Plan p;
+  const long P = (long)T * k;
+  const long active = P < E ? P : E;
+  const long avg = active > 0 ? (P + active - 1) / active : 1;
+  p.block_m = avg <= 16 ? 16 : (avg <= 32 ? 32 : 64);
+  p.mb = p.block_m / 16;
+  p.max_tasks = (int)(P / p.block_m + (P < E ? P : E));
+  long est_tasks = (P + p.block_m - 1) / p.block_m;
+  if (est_tasks < active) est_tasks = active;
+  const int esz = dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2;
+  const int nsteps1 = H * esz / 64, nsteps2 = I * esz / 64;
+  p.unroll1 = choose_unroll(nsteps1, p.mb);
+  p.unroll2 = choose_unroll(nsteps2, p.mb);
+  p.split1 = choose_split(nsteps1, p.unroll1, est_tasks * (2L * I / 16));
+  p.split2 = choose_split(nsteps2, p.unroll2, est_tasks * ((long)H / 16));
+  return p;
+}
+
+void routing_layout(int T, int k, int E, const Plan& p, moe_routing_layout_t* L) {
+  const size_t P = (size_t)T * k;
+  size_t off = 0;
+  L->header = off;
+  off += 64;
+  L->expert_offsets = off;
+  off = align_up(off + 4 * ((size_t)E + 1), 16);
+  L->sorted_pairs = off;
+  off = align_up(off + 4 * P, 16);
+  L->pair_pos = off;
+  off = align_up(off + 4 * P, 16);
+  L->tasks = off;
+  off = align_up(off + sizeof(moe_task_t) * (size_t)p.max_tasks, 16);
+  L->total_bytes = off;
+  L->block_m = p.block_m;
+  L->max_tasks = p.max_tasks;
+}
+
+void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
+                      moe_workspace_layout_t* W) {
+  const size_t P = (size_t)T * k;
+  const bool fp8 = dtype == MOE_DTYPE_FP8_W8A8;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  W->xq = fp8 ? take((size_t)T * H) : kNone;
+  W->x_scale = fp8 ? take(4 * (size_t)T) : kNone;
+  W->g = take(4 * (size_t)p.split1 * P * 2 * I);
+  W->h = take(P * I * (fp8 ? 1 : 2));
+  W->h_scale = fp8 ? take(4 * P) : kNone;
+  W->y = take(4 * (size_t)p.split2 * P * H);
+  W->total_bytes = off;
+  W->split_k1 = p.split1;
+  W->split_k2 = p.split2;
+}
+
+// Compute-unit count per device, queried once.
+int cu_count(int* out) {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return MOE_ERR_HIP;
+    cache[dev] = n;
+  }
+  *out = cache[dev];
+  return MOE_OK;
+}
+
+int gemm_grid(long max_items, int cus) {
+  long waves = (long)cus * 8;
+  if (max_items < waves) waves = max_items;
+  if (waves < 1) waves = 1;
+  return (int)((waves + 3) / 4);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Stage-event hook (measurement only).
+void* g_events[10];
+bool g_events_on = false;
+
+struct StageScope {
+  hipStream_t s;
+  int stage;
+  StageScope(hipStream_t s_, int st) : s(s_), stage(st) {
+    if (g_events_on) (void)hipEventRecord(static_cast<hipEvent_t>(g_events[2 * stage]), s);
+  }
+  ~StageScope() {
+    if (g_events_on) (void)hipEventRecord(static_cast<hipEvent_t>(g_events[2 * stage + 1]), s);
+  }
+};
+
+int build_routing(int dtype, const int32_t* ids, int T, int k, int E, int H, int I,
+                  void* routing, size_t routing_bytes, void* stream) {
+  int rc = check_shape(T, k, E, H, I);
+  if (rc != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!ids || !routing) return MOE_ERR_INVALID_ARG;
+  if (!aligned(ids, 4) || !aligned(routing, 16)) return MOE_ERR_INVALID_ARG;
+  const Plan p = make_plan(dtype, T, k, E, H, I);
+  moe_routing_layout_t L;
+  routing_layout(T, k, E, p, &L);
+  if (routing_bytes < L.total_bytes) return MOE_ERR_BUFFER_TOO_SMALL;
+  const hipError_t e = moe_host::launch_route(ids, T * k, E, p.block_m, p.max_tasks, routing, L,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+struct RoutingView {
+  const int32_t* header;
+  const int32_t* expert_offsets;
+  const int32_t* sorted_pairs;
+  const int32_t* pair_pos;
+  const moe_task_t* tasks;
+};
+
+RoutingView view_routing(const void* routing, const moe_routing_layout_t& L) {
+  const char* b = static_cast<const char*>(routing);
+  return RoutingView{reinterpret_cast<const int32_t*>(b + L.header),
+                     reinterpret_cast<const int32_t*>(b + L.expert_offsets),
+                     reinterpret_cast<const int32_t*>(b + L.sorted_pairs),
+                     reinterpret_cast<const int32_t*>(b + L.pair_pos),
+                     reinterpret_cast<const moe_task_t*>(b + L.tasks)};
+}
+
+int forward(int dtype, const void* x, const float* topk_w, const void* routing, const void* w1,
+            const float* w1_scale, const void* w2, const float* w2_scale, int T, int k, int E,
+            int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  int rc = check_shape(T, k, E, H, I);
+  if (rc != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  const bool fp8 = dtype == MOE_DTYPE_FP8_W8A8;
+  if (!x || !topk_w || !routing || !w1 || !w2 || !workspace || !out) return MOE_ERR_INVALID_ARG;
+  if (fp8 && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16) ||
+      !aligned(topk_w, 4) || !aligned(routing, 16) || !aligned(workspace, 256))
+    return MOE_ERR_INVALID_ARG;
+  if (fp8 && (!aligned(w1_scale, 4) || !aligned(w2_scale, 4))) return MOE_ERR_INVALID_ARG;
+
+  const Plan p = make_plan(dtype, T, k, E, H, I);
+  moe_routing_layout_t L;
+  routing_layout(T, k, E, p, &L);
+  moe_workspace_layout_t W;
+  workspace_layout(dtype, T, k, H, I, p, &W);
+  if (workspace_bytes < W.total_bytes) return MOE_ERR_BUFFER_TOO_SMALL;
+  int cus = 0;
+  if ((rc = cu_count(&cus)) != MOE_OK) return rc;
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const RoutingView R = view_routing(routing, L);
+  char* ws = static_cast<char*>(workspace);
+  const int P = T * k;
+  float* g = reinterpret_cast<float*>(ws + W.g);
+  float* y = reinterpret_cast<float*>(ws + W.y);
+  void* h = ws + W.h;
+  float* h_scale = fp8 ? reinterpret_cast<float*>(ws + W.h_scale) : nullptr;
+  uint8_t* xq = fp8 ? reinterpret_cast<uint8_t*>(ws + W.xq) : nullptr;
+  float* x_scale = fp8 ? reinterpret_cast<float*>(ws + W.x_scale) : nullptr;
+  hipError_t e = hipSuccess;
+
+  if (fp8) {
+    StageScope st(s, 0);
+    e = moe_host::launch_quant_rows_bf16(static_cast<const uint16_t*>(x), T, H, xq, x_scale, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 1);
+    GemmArgs a{};
+    a.a = fp8 ? static_cast<const void*>(xq) : x;
+    a.a_scale = x_scale;
+    a.b = w1;
+    a.b_scale = w1_scale;
+    a.sorted_pairs = R.sorted_pairs;
+    a.header = R.header;
+    a.tasks = R.tasks;
+    a.c = g;
+    a.K = H;
+    a.N = 2 * I;
+    a.P = P;
+    a.topk = k;
+    a.max_tasks = p.max_tasks;
+    a.split = p.split1;
+    GemmPlan gp{p.mb, 1, p.unroll1, gemm_grid((long)p.max_tasks * (2L * I / 16) * p.split1, cus)};
+    e = moe_host::launch_grouped_gemm(a, true, fp8, gp, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 2);
+    e = moe_host::launch_act(g, p.split1, P, I, R.expert_offsets, E, fp8, h, h_scale, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 3);
+    GemmArgs a{};
+    a.a = h;
+    a.a_scale = h_scale;
+    a.b = w2;
+    a.b_scale = w2_scale;
+    a.sorted_pairs = R.sorted_pairs;
+    a.header = R.header;
+    a.tasks = R.tasks;
+    a.c = y;
+    a.K = I;
+    a.N = H;
+    a.P = P;
+    a.topk = k;
+    a.max_tasks = p.max_tasks;
+    a.split = p.split2;
+    GemmPlan gp{p.mb, 1, p.unroll2, gemm_grid((long)p.max_tasks * (H / 16) * p.split2, cus)};
+    e = moe_host::launch_grouped_gemm(a, false, fp8, gp, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 4);
+    e = moe_host::launch_reduce(y, p.split2, P, topk_w, R.pair_pos, R.expert_offsets, E, T, k, H,
+                                static_cast<uint16_t*>(out), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case MOE_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int moe_routing_layout(int T, int k, int E, int H, int I, int dtype, moe_routing_layout_t* out) {
+  if (!out || (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_W8A8)) return MOE_ERR_INVALID_ARG;
+  const int rc = check_shape(T, k, E, H, I);
+  if (rc != MOE_OK) return rc;
+  routing_layout(T, k, E, make_plan(dtype, T, k, E, H, I), out);
+  return MOE_OK;
+}
+
+int moe_workspace_layout(int T, int k, int E, int H, int I, int dtype, moe_workspace_layout_t* out) {
+  if (!out || (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_W8A8)) return MOE_ERR_INVALID_ARG;
+  const int rc = check_shape(T, k, E, H, I);
+  if (rc != MOE_OK) return rc;
+  workspace_layout(dtype, T, k, H, I, make_plan(dtype, T, k, E, H, I), out);
+  return MOE_OK;
+}
+
+int moe_build_routing_bf16(const int32_t* topk_ids, int T, int k, int E, int H, int I,
+                           void* routing, size_t routing_bytes, void* stream) {
+  return build_routing(MOE_DTYPE_BF16, topk_ids, T, k, E, H, I, routing, routing_bytes, stream);
+}
+
+int moe_build_routing_fp8(const int32_t* topk_ids, int T, int k, int E, int H, int I,
+                          void* routing, size_t routing_bytes, void* stream) {
+  return build_routing(MOE_DTYPE_FP8_W8A8, topk_ids, T, k, E, H, I, routing, routing_bytes,
+                       stream);
+}
+
+int moe_forward_bf16(const void* x, const float* topk_w, const void* routing, const void* w1,
+                     const void* w2, int T, int k, int E, int H, int I, void* workspace,
+                     size_t workspace_bytes, void* out, void* stream) {
+  return forward(MOE_DTYPE_BF16, x, topk_w, routing, w1, nullptr, w2, nullptr, T, k, E, H, I,
+                 workspace, workspace_bytes, out, stream);
+}
+
+int moe_forward_fp8(const void* x, const float* topk_w, const void* routing, const uint8_t* w1,
+                    const float* w1_scale, const uint8_t* w2, const float* w2_scale, int T, int k,
+                    int E, int H, int I, void* workspace, size_t workspace_bytes, void* out,
+                    void* stream) {
+  return forward(MOE_DTYPE_FP8_W8A8, x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H,
+                 I, workspace, workspace_bytes, out, stream);
+}
+
+int moe_set_stage_events(void* const* events, int n) {
+  if (!events) {
+    g_events_on = false;
+    return MOE_OK;
+  }
+  if (n < 10) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < 10; i++) {
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+    g_events[i] = events[i];
+  }
+  g_events_on = true;
+  return MOE_OK;
+}
+
+int moe_device_cu_count(void) {
+  int n = 0;
+  const int rc = cu_count(&n);
+  return rc == MOE_OK ? n : rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// Shared device/host definitions of the MI355X fused-MoE library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kMaxPairs = 65536;
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 16;
+
+// Routing-buffer header fields (int32 index into the 64-byte header).
+constexpr int kHdrNumTasks = 0;
+constexpr int kHdrNumDropped = 1;
+constexpr int kHdrBlockM = 2;
+constexpr int kHdrNumPairs = 3;
+constexpr int kHdrNumExperts = 4;
+constexpr int kHdrMaxTasks = 5;
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __builtin_bit_cast(float, b << 16);
+}
+
+// fp32 -> OCP e4m3 code, round to nearest even, saturating to +-448.  The
+// hardware conversion rounds to nearest even but turns magnitudes above the
+// largest finite value into NaN, so the input is clamped first.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float v) {
+  v = __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xffu;
+}
+
+// Four fp32 -> four e4m3 codes packed little-endian in one word.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3x4_sat(float a, float b, float c, float d) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+  b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+  c = __builtin_fminf(__builtin_fmaxf(c, -448.0f), 448.0f);
+  d = __builtin_fminf(__builtin_fmaxf(d, -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// Scale pair of the per-row activation quantisation: scale = fp32(amax/448),
+// inv = fp32(448/amax), both divisions in fp64; an all-zero row gets 1 and 1.
+__device__ __forceinline__ void e4m3_row_scales(float amax, float* scale, float* inv) {
+  if (amax > 0.0f) {
+    *scale = (float)((double)amax / 448.0);
+    *inv = (float)(448.0 / (double)amax);
+  } else {
+    *scale = 1.0f;
+    *inv = 1.0f;
+  }
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace moe
+
+// Host-side launch helpers implemented by the kernel translation units.
+namespace moe_host {
+
+hipError_t launch_route(const int32_t* ids, int P, int E, int block_m, int max_tasks,
+                        void* routing, const moe_routing_layout_t& L, hipStream_t s);
+
+// Per-token e4m3 quantisation of bf16 rows x[T][H].
+hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* scale,
+                                  hipStream_t s);
+
+// SiLU-and-mul of the gate-up partial sums g[S][P][2I] for the valid sorted
+// rows; writes bf16 h[P][I] (fp8 = false) or e4m3 codes h[P][I] + scales.
+hipError_t launch_act(const float* g, int S, int P, int I, const int32_t* expert_offsets, int E,
+                      bool fp8, void* h, float* h_scale, hipStream_t s);
+
+// out[t] = bf16(sum_j w[t][j] * sum_s y[s][pos[t*k+j]]) over valid pairs.
+hipError_t launch_reduce(const float* y, int S, int P, const float* topk_w,
+                         const int32_t* pair_pos, const int32_t* expert_offsets, int E, int T,
+                         int k, int H, uint16_t* out, hipStream_t s);
+
+struct GemmArgs {
+  const void* a;            // gathered: x / xq [T][K]; contiguous: h / hq [P][K]
+  const float* a_scale;     // fp8: per-row scales of a ([T] gathered, [P] contiguous)
+  const void* b;            // per-expert weights [E][N][K]
+  const float* b_scale;     // fp8: per-output-channel scales [E][N]
+  const int32_t* sorted_pairs;  // gathered: pair index of each sorted row
+  const int32_t* header;        // routing header (num_tasks at index 0)
+  const moe_task_t* tasks;
+  float* c;                 // fp32 partial sums [S][P][N]
+  int K;                    // reduction length (elements)
+  int N;                    // output columns
+  int P;                    // rows of each partial slice (T*k)
+  int topk;                 // k: a pair index divided by k is its token
+  int max_tasks;
+  int split;                // S: slices of the reduction
+};
+
+struct GemmPlan {
+  int mb;                   // 16-row MFMA blocks per task tile (block_m / 16)
+  int nsub;                 // 16-column MFMA blocks per work item
+  int unroll;               // 64-byte K steps per pipeline stage
+  int grid;                 // workgroups of the persistent launch (4 waves each)
+};
+
+hipError_t launch_grouped_gemm(const GemmArgs& a, bool gather, bool fp8, const GemmPlan& plan,
+                               hipStream_t s);
+
+}  // namespace moe_host

@@ -1,0 +1,74 @@
+"""Helpers shared by the GPU parity tests: run the HIP layer, run the oracle
+on the same bytes, compare with the stated tolerances."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from moe_inputs import make_tokens, make_weights
+
+BF16_REL, BF16_ABS = 1e-2, 1e-3      # max|err| <= 1e-2*max|ref| + 1e-3
+FP8_REL = 4e-2                        # max|err| <= 4e-2*max|ref|
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def device_weights(wl, device="cuda"):
+    """Weights of a workload for the GPU path: bf16 (tiny f32 data is rounded
+    to bf16) or e4m3 codes + scales."""
+    W = make_weights(wl, device=device)
+    if wl.dtype == "f32":
+        W = {"w1": W["w1"].bfloat16().contiguous(), "w2": W["w2"].bfloat16().contiguous()}
+    return W
+
+
+def path_dtype(wl):
+    return "fp8" if wl.dtype == "fp8" else "bf16"
+
+
+def run_gpu(lib, x, ids, w, W, dtype):
+    x = x.cuda().bfloat16().contiguous()
+    ids = ids.cuda().contiguous()
+    w = w.cuda().float().contiguous()
+    out, routing, ws = lib.moe_layer(x, ids, w, W, dtype=dtype)
+    torch.cuda.synchronize()
+    return out, routing, ws
+
+
+def oracle_rows(x, ids, w, W, dtype, rows=None, want_quant=False):
+    """Oracle output rows (fp64) on the exact bytes the GPU saw."""
+    xb = x.detach().cpu().bfloat16().contiguous()
+    idc = ids.detach().cpu().contiguous()
+    wc = w.detach().cpu().float().contiguous()
+    if dtype == "bf16":
+        return oracle.forward_bf16(xb, wc, idc, W["w1"].cpu(), W["w2"].cpu(), rows=rows)
+    return oracle.forward_fp8(xb, wc, idc, W["w1"].cpu(), W["w1_scale"].cpu(), W["w2"].cpu(),
+                              W["w2_scale"].cpu(), rows=rows, want_quant=want_quant)
+
+
+def check_tol(got, ref, dtype, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    bound = BF16_REL * scale + BF16_ABS if dtype == "bf16" else FP8_REL * scale
+    cos = float(np.dot(got.ravel(), ref.ravel()) /
+                max(np.linalg.norm(got) * np.linalg.norm(ref), 1e-300)) if got.size else 1.0
+    log(f"  {what} max|err|={err:.3e} max|ref|={scale:.3e} bound={bound:.3e} cos={cos:.6f}")
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert err <= bound, f"{what}: max|err| {err} > bound {bound}"
+    return err, bound, cos
+
+
+def sample_rows(T, n, seed=0):
+    if T <= n:
+        return list(range(T))
+    g = np.random.default_rng(seed)
+    mid = sorted(g.choice(np.arange(1, T - 1), size=n - 2, replace=False).tolist())
+    return [0] + mid + [T - 1]

@@ -1,0 +1,196 @@
+"""GPU parity of the forward pass against the oracle.
+
+bf16: max|err| <= 1e-2*max|ref| + 1e-3.  fp8 w8a8: max|err| <= 4e-2*max|ref|
+against the oracle applying the same quantisation, and the per-token e4m3
+codes and scales of x bit-exact.  Small shapes are compared on every
+output; the five workloads at full size are compared on sampled tokens
+(always including the first and last), in the launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_inputs import WORKLOADS, custom_workload, make_tokens, random_ids, random_weights_w
+from moe_testlib import check_tol, device_weights, log, oracle_rows, path_dtype, run_gpu, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import mixture_experts_layer_lds_amd as m
+    return m
+
+
+def out64(out):
+    return out.float().cpu().double().numpy()
+
+
+SMALL = [
+    # E, H, I, k, T, p_drop
+    (8, 128, 64, 2, 4, 0.0),
+    (16, 256, 192, 4, 37, 0.1),
+    (4, 512, 128, 1, 50, 0.0),
+    (64, 256, 320, 8, 129, 0.05),
+    (3, 64, 64, 3, 200, 0.0),
+    (256, 192, 128, 8, 9, 0.0),
+]
+
+
+@pytest.mark.parametrize("E,H,I,k,T,p_drop", SMALL)
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_small_shapes_all_outputs(lib, E, H, I, k, T, p_drop, dtype):
+    log(f"small {dtype} E={E} H={H} I={I} k={k} T={T}")
+    wl = custom_workload(E, H, I, k, dtype=dtype, seed=E + H + I)
+    W = device_weights(wl)
+    x, _, _ = make_tokens(wl, T, seed=T + 5)
+    ids = random_ids(T, k, E, seed=T + 6, p_drop=p_drop)
+    w = random_weights_w(T, k, seed=T + 7)
+    out, routing, ws = run_gpu(lib, x, ids, w, W, dtype)
+    if dtype == "bf16":
+        ref = oracle_rows(x, ids, w, W, dtype)
+    else:
+        ref, (xq, sx, hq, sh) = oracle_rows(x, ids, w, W, dtype, want_quant=True)
+        L = lib.moe_workspace_layout(T, k, E, H, I, "fp8")
+        wsc = ws.cpu()
+        gxq = wsc[L["xq"]:L["xq"] + T * H].view(T, H).numpy()
+        gsx = wsc[L["x_scale"]:L["x_scale"] + 4 * T].view(torch.float32).numpy()
+        assert np.array_equal(gxq, xq), "x e4m3 codes"
+        assert np.array_equal(gsx, sx), "x scales"
+    check_tol(out64(out), ref, dtype, "out")
+
+
+def test_tiny_workload(lib):
+    wl = WORKLOADS["tiny"]
+    W = device_weights(wl)
+    x, ids, w = make_tokens(wl, 4)
+    out, _, _ = run_gpu(lib, x, ids, w, W, "bf16")
+    ref = oracle_rows(x, ids, w, W, "bf16")
+    check_tol(out64(out), ref, "bf16", "tiny vs bf16-rounded oracle")
+    # and against the fp32 originals (rounding of x and W to bf16 included)
+    W32 = __import__("moe_inputs").make_weights(wl)
+    ref32 = oracle.forward_f32(x, w, ids, W32["w1"], W32["w2"])
+    err = np.max(np.abs(out64(out) - ref32)) / np.max(np.abs(ref32))
+    log(f"  tiny vs fp32 oracle rel err {err:.3e}")
+    assert err < 3e-2
+
+
+_weights_cache = {}
+
+
+def workload_weights(name):
+    if name not in _weights_cache:
+        _weights_cache.clear()
+        torch.cuda.empty_cache()
+        wl = WORKLOADS[name]
+        W = device_weights(wl)
+        Wc = {k: v.cpu() for k, v in W.items()}
+        _weights_cache[name] = (W, Wc)
+    return _weights_cache[name]
+
+
+FULL = [(name, T) for name in ("mixtral", "qwen3", "qwen2", "dsv3") for T in WORKLOADS[name].Ts]
+
+
+@pytest.mark.parametrize("name,T", FULL)
+def test_full_size_sampled(lib, name, T):
+    wl = WORKLOADS[name]
+    dtype = path_dtype(wl)
+    log(f"full {name} T={T} {dtype}")
+    W, Wc = workload_weights(name)
+    x, ids, w = make_tokens(wl, T)
+    out, _, ws = run_gpu(lib, x, ids, w, W, dtype)
+    rows = sample_rows(T, 6 if wl.I * wl.H > 2 ** 25 else 12, seed=T)
+    ref = oracle_rows(x, ids, w, Wc, dtype, rows=rows)
+    check_tol(out64(out)[rows], ref, dtype, f"{name} T={T} rows={len(rows)}")
+    o = out.float()
+    assert torch.isfinite(o).all()
+
+
+def test_deterministic_and_permutation_equivariant(lib):
+    wl = custom_workload(32, 512, 256, 4, seed=3)
+    W = device_weights(wl)
+    T = 300
+    x, _, _ = make_tokens(wl, T, seed=4)
+    ids = random_ids(T, 4, 32, seed=5, p_drop=0.05)
+    w = random_weights_w(T, 4, seed=6)
+    a, _, _ = run_gpu(lib, x, ids, w, W, "bf16")
+    b, _, _ = run_gpu(lib, x, ids, w, W, "bf16")
+    assert torch.equal(a, b)
+    perm = torch.randperm(T, generator=torch.Generator().manual_seed(1))
+    c, _, _ = run_gpu(lib, x[perm], ids[perm], w[perm], W, "bf16")
+    assert torch.equal(a[perm.cuda()], c)
+
+
+def test_idle_experts_never_read_and_zero_weight(lib):
+    wl = custom_workload(16, 256, 128, 2, seed=7)
+    W = device_weights(wl)
+    T = 20
+    x, _, _ = make_tokens(wl, T, seed=8)
+    ids = random_ids(T, 2, 8, seed=9)          # experts 8..15 stay idle
+    w = random_weights_w(T, 2, seed=10)
+    a, _, _ = run_gpu(lib, x, ids, w, W, "bf16")
+    Wn = {"w1": W["w1"].clone(), "w2": W["w2"].clone()}
+    Wn["w1"][8:] = float("nan")
+    Wn["w2"][8:] = float("nan")
+    b, _, _ = run_gpu(lib, x, ids, w, Wn, "bf16")
+    assert torch.isfinite(b.float()).all() and torch.equal(a, b)
+    # a zero weight removes the pair exactly like a dropped id
+    w0 = w.clone()
+    w0[3, 1] = 0.0
+    ids_d = ids.clone()
+    ids_d[3, 1] = -1
+    c, _, _ = run_gpu(lib, x, ids, w0, W, "bf16")
+    d, _, _ = run_gpu(lib, x, ids_d, w0, W, "bf16")
+    assert torch.equal(c, d)
+
+
+def test_empty_batch_is_a_no_op(lib):
+    wl = custom_workload(8, 128, 64, 2, seed=1)
+    W = device_weights(wl)
+    x = torch.zeros(0, 128, dtype=torch.bfloat16, device="cuda")
+    ids = torch.zeros(0, 2, dtype=torch.int32, device="cuda")
+    w = torch.zeros(0, 2, dtype=torch.float32, device="cuda")
+    out, _, _ = lib.moe_layer(x, ids, w, W)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 128)
+
+
+def test_graph_capture_replays_match_eager(lib):
+    wl = custom_workload(16, 256, 192, 4, seed=12)
+    W = device_weights(wl)
+    T, k, E, H, I = 33, 4, 16, 256, 192
+    x, _, _ = make_tokens(wl, T, seed=13)
+    x = x.cuda()
+    ids = random_ids(T, k, E, seed=14).cuda()
+    w = random_weights_w(T, k, seed=15).cuda()
+    routing = lib.alloc_routing(T, k, E, H, I)
+    ws = lib.alloc_workspace(T, k, E, H, I)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        lib.moe_build_routing_bf16(ids, E, H, I, routing)
+        lib.moe_forward_bf16(x, w, routing, W["w1"], W["w2"], ws, out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib.moe_build_routing_bf16(ids, E, H, I, routing)
+        lib.moe_forward_bf16(x, w, routing, W["w1"], W["w2"], ws, out)
+    # new routing between replays: the captured grids serve any routing
+    ids2 = random_ids(T, k, E, seed=16).cuda()
+    for rep in range(4):
+        out.zero_()
+        ws.fill_(0x7F)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
+    ids.copy_(ids2)
+    g.replay()
+    torch.cuda.synchronize()
+    ref2, _, _ = run_gpu(lib, x, ids2, w, W, "bf16")
+    assert torch.equal(out, ref2)

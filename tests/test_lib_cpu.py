@@ -1,0 +1,132 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every function include/moe.h declares, and
+reject bad arguments on the host with the documented status codes before
+enqueueing any work.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import mixture_experts_layer_lds_amd as mod
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_all_exported(m):
+    names = declared_functions()
+    assert len(names) >= 9
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moe.h but not exported"
+    assert set(names) == set(m.EXPORTS)
+
+
+def test_status_strings(m):
+    assert m.status_string(0) == "ok"
+    assert m.status_string(-3) == "buffer too small"
+
+
+def test_routing_layout_sizes(m):
+    L = m.moe_routing_layout(4, 2, 8, 128, 64, "bf16")
+    assert L["header"] == 0 and L["expert_offsets"] == 64
+    assert L["block_m"] in (16, 32, 64)
+    assert L["max_tasks"] == 8 // L["block_m"] + min(8, 8)
+    for key in ("expert_offsets", "sorted_pairs", "pair_pos", "tasks", "total_bytes"):
+        assert L[key] % 16 == 0
+    assert L["tasks"] + 16 * L["max_tasks"] <= L["total_bytes"]
+    big = m.moe_routing_layout(4096, 8, 64, 3584, 640, "bf16")
+    assert big["sorted_pairs"] + 4 * 32768 <= big["pair_pos"]
+
+
+def test_workspace_layout(m):
+    W = m.moe_workspace_layout(16, 8, 256, 7168, 2048, "fp8")
+    P = 128
+    assert W["xq"] == 0 and W["x_scale"] >= 16 * 7168
+    assert W["g"] >= W["x_scale"] + 4 * 16
+    assert W["h"] >= W["g"] + 4 * W["split_k1"] * P * 4096
+    assert W["y"] + 4 * W["split_k2"] * P * 7168 <= W["total_bytes"]
+    for key in ("xq", "x_scale", "g", "h", "h_scale", "y"):
+        assert W[key] % 256 == 0
+    Wb = m.moe_workspace_layout(16, 8, 256, 7168, 2048, "bf16")
+    assert Wb["xq"] == 2 ** 64 - 1 and Wb["h_scale"] == 2 ** 64 - 1
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 2, 8, 128, 64), -1), ((4, 0, 8, 128, 64), -1), ((4, 17, 8, 128, 64), -1),
+    ((4, 2, 0, 128, 64), -1), ((4, 2, 257, 128, 64), -1), ((4, 2, 8, 0, 64), -1),
+    ((4, 2, 8, 96, 64), -2), ((4, 2, 8, 128, 100), -2), ((8193, 8, 8, 128, 64), -2),
+    ((4, 2, 8, 128 * 1024, 64), -2),
+])
+def test_layout_rejects_bad_shapes(m, args, code):
+    lib = m._lib
+    L = m.RoutingLayout()
+    assert lib.moe_routing_layout(*args, 0, ctypes.byref(L)) == code
+    W = m.WorkspaceLayout()
+    assert lib.moe_workspace_layout(*args, 0, ctypes.byref(W)) == code
+    assert lib.moe_routing_layout(4, 2, 8, 128, 64, 7, ctypes.byref(L)) == -1
+
+
+def test_calls_reject_bad_arguments_without_launching(m):
+    lib = m._lib
+    fake = ctypes.c_void_p(4096)            # never dereferenced: every call fails its checks
+    odd = ctypes.c_void_p(4097)
+    L = m.moe_routing_layout(4, 2, 8, 128, 64, "bf16")
+    n = L["total_bytes"]
+    # null ids / routing
+    assert lib.moe_build_routing_bf16(None, 4, 2, 8, 128, 64, fake, n, None) == -1
+    assert lib.moe_build_routing_fp8(fake, 4, 2, 8, 128, 64, None, n, None) == -1
+    # routing buffer too small
+    assert lib.moe_build_routing_bf16(fake, 4, 2, 8, 128, 64, fake, n - 1, None) == -3
+    # misaligned routing buffer
+    assert lib.moe_build_routing_bf16(fake, 4, 2, 8, 128, 64, odd, n, None) == -1
+    # bad shape wins over everything
+    assert lib.moe_build_routing_bf16(fake, 4, 2, 8, 100, 64, fake, n, None) == -2
+    # T == 0 is a no-op success, even with null pointers
+    assert lib.moe_build_routing_bf16(None, 0, 2, 8, 128, 64, None, 0, None) == 0
+    assert lib.moe_forward_bf16(None, None, None, None, None, 0, 2, 8, 128, 64, None, 0, None, None) == 0
+    W = m.moe_workspace_layout(4, 2, 8, 128, 64, "bf16")["total_bytes"]
+    args = [fake, fake, fake, fake, fake, 4, 2, 8, 128, 64, fake, W, fake, None]
+    a = list(args)
+    a[0] = None
+    assert lib.moe_forward_bf16(*a) == -1                 # null x
+    a = list(args)
+    a[11] = W - 1
+    assert lib.moe_forward_bf16(*a) == -3                 # workspace too small
+    a = list(args)
+    a[10] = ctypes.c_void_p(4096 + 16)
+    assert lib.moe_forward_bf16(*a) == -1                 # workspace not 256-byte aligned
+    a = list(args)
+    a[3] = odd
+    assert lib.moe_forward_bf16(*a) == -1                 # misaligned w1
+    Wf = m.moe_workspace_layout(4, 2, 8, 128, 64, "fp8")["total_bytes"]
+    fargs = [fake, fake, fake, fake, fake, fake, fake, 4, 2, 8, 128, 64, fake, Wf, fake, None]
+    a = list(fargs)
+    a[4] = None
+    assert lib.moe_forward_fp8(*a) == -1                  # null w1_scale
+    a = list(fargs)
+    a[13] = Wf - 1
+    assert lib.moe_forward_fp8(*a) == -3
+
+
+def test_stage_event_hook_argument_checks(m):
+    lib = m._lib
+    assert lib.moe_set_stage_events(None, 0) == 0
+    arr = (ctypes.c_void_p * 4)(*[1, 2, 3, 4])
+    assert lib.moe_set_stage_events(arr, 4) == -1
+    arr = (ctypes.c_void_p * 10)(*([1] * 9 + [0]))
+    assert lib.moe_set_stage_events(arr, 10) == -1
+    assert lib.moe_set_stage_events(None, 0) == 0
