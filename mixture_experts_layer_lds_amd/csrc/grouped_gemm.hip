@@ -31,12 +31,11 @@ namespace moe {
 template <bool FP8>
 __device__ __forceinline__ void mfma_step(f32x4& acc, const u32x4& a, const u32x4& b) {
   if constexpr (FP8) {
-    const long a0 = __builtin_bit_cast(long, a.xy);
-    const long a1 = __builtin_bit_cast(long, a.zw);
-    const long b0 = __builtin_bit_cast(long, b.xy);
-    const long b1 = __builtin_bit_cast(long, b.zw);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a0, b0, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a1, b1, acc, 0, 0, 0);
+    // bytes 0..7 and 8..15 of the fragment feed two consecutive MFMAs
+    const i64x2 a2 = __builtin_bit_cast(i64x2, a);
+    const i64x2 b2 = __builtin_bit_cast(i64x2, b);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[0], b2[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[1], b2[1], acc, 0, 0, 0);
   } else {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
