@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch: the routing/index
+build and the forward pass (gate-up GEMM, SiLU-and-mul [+ fp8 requant],
+down GEMM, top-k weighted reduction), launched through the C ABI on
+torch's current stream with every input already resident in HBM.
+
+Default workload: a Mixtral-8x7B-shaped layer (bf16, E=8, H=4096, I=14336,
+top-2, uniform softmax routing) at T=16 tokens, with seeded synthetic
+weights and tokens.  `value` is the layer's essential HBM bytes (weights of
+the experts that receive tokens + x + out + ids + weights) divided by the
+measured time per layer, in GB/s.
+
+Printed: one JSON line (rank 0, N=1 only) with the timed-region figures,
+the dominant kernel's roofline (HIP events recorded around each stage on the
+launch stream inside the timed region), per-stage times, a T sweep timed by
+HIP-graph replay, and the CPU oracle timed on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "us per MoE layer + achieved HBM GB/s (% of peak), T=1..4096 tokens, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+STAGES = ("quant_x", "gate_up", "act", "down", "reduce")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def layer_bytes_and_flops(wl, ids, T):
+    """Essential HBM bytes of one layer call and its algorithmic flops."""
+    import torch
+    E, H, I = wl.E, wl.H, wl.I
+    flat = ids.reshape(-1).to(torch.int64).cpu()
+    valid = flat[(flat >= 0) & (flat < E)]
+    active = int(torch.unique(valid).numel())
+    bw = 1 if wl.dtype == "fp8" else 2
+    per_expert = 3 * H * I * bw + ((2 * I + H) * 4 if wl.dtype == "fp8" else 0)
+    P = flat.numel()
+    nbytes = active * per_expert + T * H * 2 + T * H * 2 + P * 8
+    flops = 6.0 * valid.numel() * H * I
+    return nbytes, flops, active, int(valid.numel())
+
+
+def stage_bytes(wl, active, P_valid, T):
+    """Algorithmic bytes each stage must move (its own inputs and outputs)."""
+    E, H, I = wl.E, wl.H, wl.I
+    fp8 = wl.dtype == "fp8"
+    bw = 1 if fp8 else 2
+    bx = 1 if fp8 else 2
+    return {
+        "quant_x": T * H * 2 + T * H + T * 4 if fp8 else 0,
+        "gate_up": active * (2 * I * H * bw + (2 * I * 4 if fp8 else 0)) + T * H * bx
+                   + P_valid * 2 * I * 4,
+        "act": P_valid * 2 * I * 4 + P_valid * I * (1 if fp8 else 2),
+        "down": active * (H * I * bw + (H * 4 if fp8 else 0)) + P_valid * I * (1 if fp8 else 2)
+                + P_valid * H * 4,
+        "reduce": P_valid * H * 4 + T * H * 2,
+    }
+
+
+class Layer:
+    """Buffers and launch of one layer at one token count."""
+
+    def __init__(self, moe, wl, W, T, dtype, device="cuda"):
+        import torch
+        from moe_inputs import make_tokens
+        self.moe, self.wl, self.W, self.T, self.dtype = moe, wl, W, T, dtype
+        x, ids, w = make_tokens(wl, T, device=device)
+        self.x, self.ids, self.w = x.contiguous(), ids.contiguous(), w.contiguous()
+        E, H, I, k = wl.E, wl.H, wl.I, wl.k
+        self.routing = moe.alloc_routing(T, k, E, H, I, dtype)
+        self.ws = moe.alloc_workspace(T, k, E, H, I, dtype)
+        self.out = torch.empty(T, H, dtype=torch.bfloat16, device=device)
+
+    def run(self, W=None):
+        m, wl, W = self.moe, self.wl, (W or self.W)
+        if self.dtype == "bf16":
+            m.moe_build_routing_bf16(self.ids, wl.E, wl.H, wl.I, self.routing)
+            m.moe_forward_bf16(self.x, self.w, self.routing, W["w1"], W["w2"], self.ws, self.out)
+        else:
+            m.moe_build_routing_fp8(self.ids, wl.E, wl.H, wl.I, self.routing)
+            m.moe_forward_fp8(self.x, self.w, self.routing, W["w1"], W["w1_scale"], W["w2"],
+                              W["w2_scale"], self.ws, self.out)
+
+
+def timed_steps(layer, steps, warmup):
+    """Eager steps; per-stage HIP events recorded by the library's stage hook."""
+    import torch
+    moe = layer.moe
+    for _ in range(warmup):
+        layer.run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(steps)]
+    rt = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for step_ev in ev:          # materialise the events before handing them over
+        for e in step_ev:
+            e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        moe.moe_set_stage_events(ev[i])
+        rt[i][0].record()
+        layer.run()
+        rt[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    moe.moe_set_stage_events(None)
+    stage_ms = {s: [] for s in STAGES}
+    for i in range(steps):
+        for si, s in enumerate(STAGES):
+            if layer.dtype != "fp8" and s == "quant_x":
+                continue
+            stage_ms[s].append(ev[i][2 * si].elapsed_time(ev[i][2 * si + 1]))
+    step_ms = [a.elapsed_time(b) for a, b in rt]
+    return wall, step_ms, stage_ms
+
+
+def graph_time_us(layer, weight_sets, reps=50, warmup=10):
+    """Median per-layer time by HIP-graph replay, rotating weight copies so
+    no replay finds the previous one's weights in the caches."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for W in weight_sets:
+            layer.run(W)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graphs = []
+    for W in weight_sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.run(W)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    times = []
+    for i in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        graphs[i % len(graphs)].replay()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1000.0)
+    return statistics.median(times), min(times)
+
+
+def cpu_baseline(wl, layer, W_host, dtype, reps=3):
+    import oracle
+    x = layer.x.cpu()
+    ids = layer.ids.cpu()
+    w = layer.w.cpu()
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        if dtype == "bf16":
+            oracle.forward_bf16(x, w, ids, W_host["w1"], W_host["w2"])
+        else:
+            oracle.forward_fp8(x, w, ids, W_host["w1"], W_host["w1_scale"], W_host["w2"],
+                               W_host["w2_scale"])
+        times.append(time.perf_counter() - t0)
+    return statistics.median(times), oracle.num_threads()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixtral",
+                    choices=["tiny", "mixtral", "qwen3", "qwen2", "dsv3"])
+    ap.add_argument("--tokens", type=int, default=16)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the graph-replay T sweep")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--once", action="store_true",
+                    help="one untimed step only (for counter collection under a profiler)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the layer runs on a single MI355X and this build "
+              "has no multi-GPU path (see the sharding design notes); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixture_experts_layer_lds_amd as moe
+    from moe_inputs import WORKLOADS, make_weights
+
+    torch.cuda.set_device(0)
+    wl = WORKLOADS[args.workload]
+    dtype = "fp8" if wl.dtype == "fp8" else "bf16"
+    T = args.tokens
+    log(f"[bench] workload={wl.name} T={T} dtype={dtype}: generating weights")
+    W = make_weights(wl, device="cuda")
+    if wl.dtype == "f32":
+        W = {k: v.bfloat16().contiguous() for k, v in W.items()}
+    layer = Layer(moe, wl, W, T, dtype)
+
+    if args.once:
+        layer.run()
+        torch.cuda.synchronize()
+        log("[bench] one step done")
+        return
+
+    nbytes, flops, active, P_valid = layer_bytes_and_flops(wl, layer.ids, T)
+    log(f"[bench] timed region: {args.warmup} warmup + {args.steps} steps")
+    wall, step_ms, stage_ms = timed_steps(layer, args.steps, args.warmup)
+    ms_per_step = wall * 1000.0 / args.steps
+    us_layer = statistics.median(step_ms) * 1000.0
+    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+    sb = stage_bytes(wl, active, P_valid, T)
+    stages = {}
+    for s, v in stage_ms.items():
+        if v:
+            avg = sum(v) / len(v)
+            stages[s] = {"avg_us": round(avg * 1000.0, 2),
+                         "algorithmic_GBs": round(sb[s] / (avg * 1e-3) / 1e9, 1) if sb[s] else None}
+    dom = max(("gate_up", "down"), key=lambda s: stages[s]["avg_us"])
+    dom_us = stages[dom]["avg_us"]
+    dom_bytes = sb[dom]
+    dom_flops = 2.0 * P_valid * H_I(wl, dom)
+    intensity = dom_flops / max(dom_bytes, 1)
+    ridge = MFMA_PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
+        roof = {"kernel": f"grouped_gemm ({dom})", "bound": "hbm",
+                "achieved": round(dom_bytes / (dom_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"kernel": f"grouped_gemm ({dom})", "bound": "mfma",
+                "achieved": round(dom_flops / (dom_us * 1e-6) / 1e12, 1),
+                "peak": MFMA_PEAK_TFLOPS[dtype], "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["algorithmic_bytes"] = dom_bytes
+    roof["avg_launch_us"] = dom_us
+
+    sweep = []
+    if not args.no_sweep:
+        for Ts in wl.Ts:
+            lay = Layer(moe, wl, W, Ts, dtype)
+            nb, fl, act_e, pv = layer_bytes_and_flops(wl, lay.ids, Ts)
+            copies = 1
+            if nb < 1e9:
+                per_copy = sum(v.numel() * v.element_size() for v in W.values())
+                copies = max(1, min(8, math.ceil(1e9 / nb), int(40e9 // per_copy)))
+            sets = [W] + [{k: v.clone() for k, v in W.items()} for _ in range(copies - 1)]
+            med, best = graph_time_us(lay, sets)
+            sweep.append({"T": Ts, "us_per_layer": round(med, 2), "best_us": round(best, 2),
+                          "active_experts": act_e, "essential_MB": round(nb / 1e6, 2),
+                          "GBs": round(nb / (med * 1e-6) / 1e9, 1),
+                          "hbm_frac": round(nb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "mfma_frac": round(fl / (med * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS[dtype], 4),
+                          "weight_copies": copies})
+            del sets, lay
+            torch.cuda.empty_cache()
+            log(f"[bench] sweep T={Ts}: {sweep[-1]['us_per_layer']} us, {sweep[-1]['GBs']} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on the host)")
+        W_host = {k: v.cpu() for k, v in W.items()}
+        sec, cores = cpu_baseline(wl, layer, W_host, dtype)
+        cpu = {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": cores,
+               "kind": "oracle", "us_per_layer": round(sec * 1e6, 1),
+               "sample": f"the full {wl.name} layer at T={T} ({T * wl.k} pairs), fp64 C oracle, "
+                         f"OpenMP over tokens, median of 3 runs"}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,1/sqrt(fan_in)) weights, N(0,1) tokens and router logits)",
+        "config": {"workload": wl.label, "E": wl.E, "H": wl.H, "I": wl.I, "k": wl.k, "T": T,
+                   "routing": wl.routing, "parallelism": "none (one GPU)"},
+        "us_per_layer": round(us_layer, 2),
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "essential_bytes": nbytes,
+        "active_experts": active,
+        "stages": stages,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def H_I(wl, stage):
+    """Inner-product length x output width of one pair's GEMM in a stage."""
+    return (2 * wl.I * wl.H) if stage == "gate_up" else (wl.H * wl.I)
+
+
+if __name__ == "__main__":
+    main()

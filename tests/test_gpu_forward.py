@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from moe_inputs import WORKLOADS, custom_workload, make_tokens, random_ids, random_weights_w
+from moe_inputs import WORKLOADS, custom_workload, make_tokens, make_weights, random_ids, random_weights_w
 from moe_testlib import check_tol, device_weights, log, oracle_rows, path_dtype, run_gpu, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -64,13 +64,13 @@ def test_small_shapes_all_outputs(lib, E, H, I, k, T, p_drop, dtype):
 
 def test_tiny_workload(lib):
     wl = WORKLOADS["tiny"]
-    W = device_weights(wl)
+    W32 = make_weights(wl)                    # fp32 data, drawn on the host
+    W = {k: v.bfloat16().cuda().contiguous() for k, v in W32.items()}
     x, ids, w = make_tokens(wl, 4)
     out, _, _ = run_gpu(lib, x, ids, w, W, "bf16")
     ref = oracle_rows(x, ids, w, W, "bf16")
     check_tol(out64(out), ref, "bf16", "tiny vs bf16-rounded oracle")
     # and against the fp32 originals (rounding of x and W to bf16 included)
-    W32 = __import__("moe_inputs").make_weights(wl)
     ref32 = oracle.forward_f32(x, w, ids, W32["w1"], W32["w2"])
     err = np.max(np.abs(out64(out) - ref32)) / np.max(np.abs(ref32))
     log(f"  tiny vs fp32 oracle rel err {err:.3e}")
