@@ -37,6 +37,8 @@
  *      W1       [E][2I][H]  gate rows [0, I), up rows [I, 2I)
  *      W2       [E][H][I]
  *      out      [T][H]      bf16
+ *    The forward calls take W1 and W2 pre-packed by moe_pack_weights (same
+ *    byte size, MFMA-fragment order); everything else is row-major.
  *    bf16 is IEEE binary16-brain (1/8/7); fp8 is OCP E4M3 ("e4m3fn",
  *    max finite 448).
  *  - Stage order: [fp8: quantise x] -> gate-up GEMM -> SiLU-and-mul
@@ -138,6 +140,20 @@ int moe_routing_layout(int T, int k, int E, int H, int I, int dtype,
 int moe_workspace_layout(int T, int k, int E, int H, int I, int dtype,
                          moe_workspace_layout_t *out /* host */);
 
+/* One-time weight pre-pack (done when weights are loaded, like the blog's
+ * router weights that are preprocessed once and reused across requests and
+ * graph replays).  w (device) is a row-major [E][rows][cols] tensor of
+ * dtype elements (bf16, or e4m3 codes for MOE_DTYPE_FP8_W8A8); packed
+ * (device, same byte size, must not overlap w) receives it cut into blocks
+ * of 16 rows x 64 bytes, each stored as one contiguous 1 KiB chunk whose
+ * 16-byte piece l holds row (l % 16), bytes 16*(l / 16).. of the block;
+ * chunks are ordered (expert, 16-row block, 64-byte step).  Pack W1 with
+ * rows = 2I, cols = H and W2 with rows = H, cols = I.  Requires rows % 16
+ * == 0 and cols * element size % 64 == 0; both pointers 16-byte aligned.
+ * Scales are not packed. */
+int moe_pack_weights(const void *w, int E, int rows, int cols, int dtype, void *packed,
+                     void *stream);
+
 /* Routing & index build (blog section "MoE", routing & index build): one
  * workgroup counting-sorts the P = T*k pairs by expert id in LDS, writing
  * the header, expert offsets, route index (sorted_pairs, pair_pos) and the
@@ -154,8 +170,8 @@ int moe_build_routing_fp8(const int32_t *topk_ids, int T, int k, int E, int H, i
 /* bf16 forward (blog section "MoE", gate-up & activation, PDL chaining;
  * operator table: BF16 hidden states).  x (device) bf16 [T][H]; topk_w
  * (device) fp32 [T][k]; routing (device) built by moe_build_routing_bf16
- * with the same sizes; w1 (device) bf16 [E][2I][H]; w2 (device) bf16
- * [E][H][I]; workspace (device, 256-byte aligned, at least
+ * with the same sizes; w1 (device) bf16 [E][2I][H] and w2 (device) bf16
+ * [E][H][I], both packed by moe_pack_weights; workspace (device, 256-byte aligned, at least
  * moe_workspace_layout().total_bytes); out (device) bf16 [T][H].
  * Experts that receive no pair are never read.  Accumulation is fp32; the
  * intermediate SiLU(gate)*up and the per-pair down rows are stored as bf16;
@@ -167,7 +183,8 @@ int moe_forward_bf16(const void *x, const float *topk_w, const void *routing,
 
 /* fp8 w8a8 forward (operator table: FP8 E4M3 expert weights; gate-up &
  * activation: FP8 requant before the down GEMM).  As moe_forward_bf16,
- * except: w1/w2 (device) are e4m3 codes, w1_scale (device) fp32 [E][2I] and
+ * except: w1/w2 (device) are e4m3 codes (packed by moe_pack_weights with
+ * dtype MOE_DTYPE_FP8_W8A8), w1_scale (device) fp32 [E][2I] and
  * w2_scale (device) fp32 [E][H] are per-output-channel scales.  x is
  * quantised per token and SiLU(gate)*up per (token, expert) row with the
  * rule scale = fp32(amax/448), code = e4m3_rne_satfinite(fp32(v *

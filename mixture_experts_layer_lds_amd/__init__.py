@@ -7,6 +7,7 @@ or cannot be loaded, importing this module raises.
 
 Functions carry the C names:
 
+    moe_pack_weights(w, dtype)                          -> packed copy (one-time)
     moe_routing_layout(T, k, E, H, I, dtype)            -> dict (host only)
     moe_workspace_layout(T, k, E, H, I, dtype)          -> dict (host only)
     moe_build_routing_bf16(topk_ids, E, H, I, routing)  -> None
@@ -14,8 +15,10 @@ Functions carry the C names:
     moe_forward_bf16(x, topk_w, routing, w1, w2, workspace, out) -> out
     moe_forward_fp8(x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, out) -> out
 
-plus allocation helpers (alloc_routing, alloc_workspace) and a convenience
-moe_layer() that runs routing + forward with freshly allocated buffers.
+plus allocation helpers (alloc_routing, alloc_workspace), pack_weights() for a
+whole weight dict, and a convenience moe_layer() that runs routing + forward
+with freshly allocated buffers.  The forward calls take W1/W2 packed by
+moe_pack_weights (a one-time byte permutation into MFMA-fragment order).
 """
 from __future__ import annotations
 
@@ -52,7 +55,7 @@ class WorkspaceLayout(ctypes.Structure):
                 ("split_k2", ctypes.c_int32)]
 
 
-EXPORTS = ("moe_status_string", "moe_routing_layout", "moe_workspace_layout",
+EXPORTS = ("moe_status_string", "moe_pack_weights", "moe_routing_layout", "moe_workspace_layout",
            "moe_build_routing_bf16", "moe_build_routing_fp8", "moe_forward_bf16",
            "moe_forward_fp8", "moe_set_stage_events", "moe_device_cu_count")
 
@@ -64,6 +67,8 @@ def _load():
     i, P, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [i]
+    L.moe_pack_weights.restype = i
+    L.moe_pack_weights.argtypes = [P, i, i, i, i, P, P]
     L.moe_routing_layout.restype = i
     L.moe_routing_layout.argtypes = [i, i, i, i, i, i, ctypes.POINTER(RoutingLayout)]
     L.moe_workspace_layout.restype = i
@@ -103,6 +108,28 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def moe_pack_weights(w, dtype="bf16", out=None, stream=None):
+    """Packed copy of a row-major [E][rows][cols] weight tensor (bf16, or uint8
+    e4m3 codes for dtype "fp8")."""
+    want = torch.bfloat16 if dtype == "bf16" else torch.uint8
+    if w.dtype != want or w.dim() != 3 or not w.is_contiguous():
+        raise ValueError(f"moe_pack_weights: expected contiguous {want} [E][rows][cols]")
+    E, rows, cols = w.shape
+    if out is None:
+        out = torch.empty_like(w)
+    _check("moe_pack_weights", _lib.moe_pack_weights(_ptr(w), E, rows, cols, DTYPES[dtype],
+                                                     _ptr(out), _stream(stream)))
+    return out
+
+
+def pack_weights(weights, dtype="bf16", stream=None):
+    """Weight dict with w1/w2 packed for the forward calls (scales copied by reference)."""
+    out = dict(weights)
+    out["w1"] = moe_pack_weights(weights["w1"], dtype, stream=stream)
+    out["w2"] = moe_pack_weights(weights["w2"], dtype, stream=stream)
+    return out
 
 
 def moe_routing_layout(T, k, E, H, I, dtype="bf16") -> dict:
@@ -204,8 +231,8 @@ def moe_device_cu_count() -> int:
 def moe_layer(x, topk_ids, topk_w, weights, dtype="bf16", out=None, stream=None):
     """Routing + forward with freshly allocated routing buffer and workspace.
 
-    weights: {"w1", "w2"} (bf16) or {"w1", "w1_scale", "w2", "w2_scale"} (fp8).
-    Returns (out, routing, workspace)."""
+    weights: {"w1", "w2"} (bf16) or {"w1", "w1_scale", "w2", "w2_scale"} (fp8),
+    with w1/w2 already packed (pack_weights).  Returns (out, routing, workspace)."""
     T, H = x.shape
     k = topk_ids.shape[1]
     E, I2, _ = weights["w1"].shape

@@ -61,87 +61,103 @@ quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restric
 }
 
 // h[r][n] = SiLU(sum_s g[s][r][n]) * sum_s g[s][r][I + n] for the valid sorted
-// rows r < expert_offsets[E].  FP8 = false: bf16 h.  FP8 = true: the row is
-// computed twice, first for its amax, then quantised with the per-row rule.
-template <bool FP8>
+// rows r < expert_offsets[E].
+__device__ __forceinline__ f32x4 silu_mul4(const float* __restrict__ grow, size_t slice, int S,
+                                           int I, int i) {
+  f32x4 gs = *reinterpret_cast<const f32x4*>(grow + 4 * i);
+  f32x4 us = *reinterpret_cast<const f32x4*>(grow + I + 4 * i);
+  for (int s = 1; s < S; s++) {
+    gs += *reinterpret_cast<const f32x4*>(grow + s * slice + 4 * i);
+    us += *reinterpret_cast<const f32x4*>(grow + s * slice + I + 4 * i);
+  }
+  f32x4 o;
+#pragma unroll
+  for (int w = 0; w < 4; w++) o[w] = silu_f32(gs[w]) * us[w];
+  return o;
+}
+
+// bf16 path: grid (row, column chunk of kActCols); writes bf16 h.
+constexpr int kActCols = 2048;
+
 __global__ void __launch_bounds__(kRowThreads)
-act_kernel(const float* __restrict__ g, int S, int P, int I,
-           const int32_t* __restrict__ expert_offsets, int E, void* __restrict__ h,
-           float* __restrict__ h_scale) {
+act_bf16_kernel(const float* __restrict__ g, int S, int P, int I,
+                const int32_t* __restrict__ expert_offsets, int E, uint16_t* __restrict__ h) {
+  const int r = blockIdx.x;
+  if (r >= expert_offsets[E]) return;
+  const size_t slice = (size_t)P * 2 * I;
+  const float* grow = g + (size_t)r * 2 * I;
+  uint16_t* hrow = h + (size_t)r * I;
+  const int v0 = blockIdx.y * (kActCols / 4);
+  const int v1 = min(I / 4, v0 + kActCols / 4);
+#pragma unroll 2
+  for (int i = v0 + threadIdx.x; i < v1; i += kRowThreads) {
+    const f32x4 o = silu_mul4(grow, slice, S, I, i);
+    u32x2 packed;
+    packed.x = (uint32_t)f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16);
+    packed.y = (uint32_t)f32_to_bf16_bits(o[2]) | ((uint32_t)f32_to_bf16_bits(o[3]) << 16);
+    *reinterpret_cast<u32x2*>(hrow + 4 * i) = packed;
+  }
+}
+
+// fp8 path: one workgroup per row; the row is computed twice, first for its
+// amax, then quantised with the per-row rule (e4m3 codes + fp32 scale).
+__global__ void __launch_bounds__(kRowThreads)
+act_fp8_kernel(const float* __restrict__ g, int S, int P, int I,
+               const int32_t* __restrict__ expert_offsets, int E, uint8_t* __restrict__ hq,
+               float* __restrict__ h_scale) {
   __shared__ float s_red[4];
   const int r = blockIdx.x;
   if (r >= expert_offsets[E]) return;   // block-uniform
   const size_t slice = (size_t)P * 2 * I;
   const float* grow = g + (size_t)r * 2 * I;
   const int nvec = I / 4;
-  auto load_h4 = [&](int i) {
-    f32x4 gs = *reinterpret_cast<const f32x4*>(grow + 4 * i);
-    f32x4 us = *reinterpret_cast<const f32x4*>(grow + I + 4 * i);
-    for (int s = 1; s < S; s++) {
-      gs += *reinterpret_cast<const f32x4*>(grow + s * slice + 4 * i);
-      us += *reinterpret_cast<const f32x4*>(grow + s * slice + I + 4 * i);
-    }
-    f32x4 o;
-#pragma unroll
-    for (int w = 0; w < 4; w++) o[w] = silu_f32(gs[w]) * us[w];
-    return o;
-  };
-  if (!FP8) {
-    uint16_t* hrow = static_cast<uint16_t*>(h) + (size_t)r * I;
-    for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
-      const f32x4 o = load_h4(i);
-      u32x2 packed;
-      packed.x = (uint32_t)f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16);
-      packed.y = (uint32_t)f32_to_bf16_bits(o[2]) | ((uint32_t)f32_to_bf16_bits(o[3]) << 16);
-      *reinterpret_cast<u32x2*>(hrow + 4 * i) = packed;
-    }
-    return;
-  }
   float amax = 0.0f;
+#pragma unroll 4
   for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
-    const f32x4 o = load_h4(i);
+    const f32x4 o = silu_mul4(grow, slice, S, I, i);
 #pragma unroll
     for (int w = 0; w < 4; w++) amax = __builtin_fmaxf(amax, __builtin_fabsf(o[w]));
   }
   amax = block_max_256(amax, s_red);
   float sc, inv;
   e4m3_row_scales(amax, &sc, &inv);
-  uint32_t* qrow = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(h) + (size_t)r * I);
+  uint32_t* qrow = reinterpret_cast<uint32_t*>(hq + (size_t)r * I);
+#pragma unroll 4
   for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
-    const f32x4 o = load_h4(i);
+    const f32x4 o = silu_mul4(grow, slice, S, I, i);
     qrow[i] = f32x4_to_e4m3x4_sat(__fmul_rn(o[0], inv), __fmul_rn(o[1], inv),
                                   __fmul_rn(o[2], inv), __fmul_rn(o[3], inv));
   }
   if (threadIdx.x == 0) h_scale[r] = sc;
 }
 
-// out[t][:] = bf16( sum_{j ascending, pair valid} w[t][j] * sum_s y[s][pos][:] ).
+// out[t][:] = bf16( sum_{j ascending, pair valid} w[t][j] * sum_s y[s][pos][:] );
+// grid (token, column chunk of kRowThreads*4).
 __global__ void __launch_bounds__(kRowThreads)
 reduce_kernel(const float* __restrict__ y, int S, int P, const float* __restrict__ topk_w,
               const int32_t* __restrict__ pair_pos, const int32_t* __restrict__ expert_offsets,
               int E, int k, int H, uint16_t* __restrict__ out) {
   const int t = blockIdx.x;
+  const int i = blockIdx.y * kRowThreads + threadIdx.x;   // vec4 column index
+  if (4 * i >= H) return;
   const int valid = expert_offsets[E];
   const size_t slice = (size_t)P * H;
-  const int nvec = H / 4;
-  for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j = 0; j < k; j++) {
-      const int p = t * k + j;
-      const int r = pair_pos[p];
-      if (r >= valid) continue;   // dropped pair
-      const float* yrow = y + (size_t)r * H + 4 * i;
-      f32x4 v = *reinterpret_cast<const f32x4*>(yrow);
-      for (int s = 1; s < S; s++) v += *reinterpret_cast<const f32x4*>(yrow + s * slice);
-      const float w = topk_w[p];
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < k; j++) {
+    const int p = t * k + j;
+    const int r = pair_pos[p];
+    if (r >= valid) continue;   // dropped pair
+    const float* yrow = y + (size_t)r * H + 4 * i;
+    f32x4 v = *reinterpret_cast<const f32x4*>(yrow);
+    for (int s = 1; s < S; s++) v += *reinterpret_cast<const f32x4*>(yrow + s * slice);
+    const float w = topk_w[p];
 #pragma unroll
-      for (int q = 0; q < 4; q++) acc[q] = __fadd_rn(acc[q], __fmul_rn(w, v[q]));
-    }
-    u32x2 packed;
-    packed.x = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
-    packed.y = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
-    *reinterpret_cast<u32x2*>(out + (size_t)t * H + 4 * i) = packed;
+    for (int q = 0; q < 4; q++) acc[q] = __fadd_rn(acc[q], __fmul_rn(w, v[q]));
   }
+  u32x2 packed;
+  packed.x = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
+  packed.y = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+  *reinterpret_cast<u32x2*>(out + (size_t)t * H + 4 * i) = packed;
 }
 
 }  // namespace moe
@@ -157,19 +173,22 @@ hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, 
 
 hipError_t launch_act(const float* g, int S, int P, int I, const int32_t* expert_offsets, int E,
                       bool fp8, void* h, float* h_scale, hipStream_t s) {
-  if (fp8)
-    hipLaunchKernelGGL(moe::act_kernel<true>, dim3(P), dim3(moe::kRowThreads), 0, s, g, S, P, I,
-                       expert_offsets, E, h, h_scale);
-  else
-    hipLaunchKernelGGL(moe::act_kernel<false>, dim3(P), dim3(moe::kRowThreads), 0, s, g, S, P,
-                       I, expert_offsets, E, h, h_scale);
+  if (fp8) {
+    hipLaunchKernelGGL(moe::act_fp8_kernel, dim3(P), dim3(moe::kRowThreads), 0, s, g, S, P, I,
+                       expert_offsets, E, static_cast<uint8_t*>(h), h_scale);
+  } else {
+    const dim3 grid(P, (I + moe::kActCols - 1) / moe::kActCols);
+    hipLaunchKernelGGL(moe::act_bf16_kernel, grid, dim3(moe::kRowThreads), 0, s, g, S, P, I,
+                       expert_offsets, E, static_cast<uint16_t*>(h));
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_reduce(const float* y, int S, int P, const float* topk_w,
                          const int32_t* pair_pos, const int32_t* expert_offsets, int E, int T,
                          int k, int H, uint16_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(moe::reduce_kernel, dim3(T), dim3(moe::kRowThreads), 0, s, y, S, P, topk_w,
+  const dim3 grid(T, (H / 4 + moe::kRowThreads - 1) / moe::kRowThreads);
+  hipLaunchKernelGGL(moe::reduce_kernel, grid, dim3(moe::kRowThreads), 0, s, y, S, P, topk_w,
                      pair_pos, expert_offsets, E, k, H, out);
   return hipGetLastError();
 }

@@ -4,21 +4,27 @@
 // consumes the per-tile task map and spreads small, ragged expert tiles
 // over the compute units; one group of lanes both loads and multiplies).
 //
-// Work item = (task tile, 16*NSUB output columns, K slice).  Each wave of
-// the persistent grid takes items round-robin until the device-side task
-// count is exhausted, so one launch size serves every routing.
+// Work item = (16*NSUB output columns, task tile, K slice), n-tile major so
+// that the row tiles of one expert that share a weight block run side by
+// side and meet its bytes in L2.  Each wave of the persistent grid takes
+// items round-robin until the device-side task count is exhausted, so one
+// launch size serves every routing.
 //
 // A wave computes a (16*MB) x (16*NSUB) block of C with
 // v_mfma_f32_16x16x32_bf16 (bf16) or two v_mfma_f32_16x16x32_fp8_fp8 per
-// 64-byte step (fp8).  Both operands are streamed from global memory
-// straight into registers with 16-byte loads: lane l holds row (l % 16) of
-// its 16-row block and the 16 bytes at offset 16*(l / 16) of each 64-byte
-// K step, so every row is read as 64 contiguous bytes per instruction and
-// every weight byte is fetched exactly once per K slice.  At decode sizes
-// the weights are read once in total, which is the HBM roofline of the
-// layer; the token rows are tiny and come from L2.  Two register stages of
-// UNROLL steps each keep a K step of loads in flight while the previous one
-// is multiplied.
+// 64-byte step (fp8).  Lane l holds row (l % 16) of its 16-row block and
+// the 16 bytes at offset 16*(l / 16) of each 64-byte K step.
+//
+// Weights arrive pre-packed (moe_pack_weights): every 16-row x 64-byte
+// block is one contiguous 1 KiB chunk in exactly that lane order, and the
+// chunks of a 16-row block follow each other along K.  A wave's weight
+// loads are therefore whole 1 KiB lines, and a work item streams one
+// contiguous run of its expert's weights with non-temporal loads (read
+// once, kept out of the caches' way).  Token rows are read through the
+// route index (gate-up) or contiguously (down) with ordinary loads; they
+// are small and shared by many items through L2.  Two register stages of
+// UNROLL steps keep the next loads in flight while the previous ones are
+// multiplied.
 //
 // The K dimension may be split into S slices (split-K) to put enough loads
 // in flight when there are few tasks (decode); slice s writes its fp32
@@ -60,14 +66,16 @@ grouped_gemm_kernel(moe_host::GemmArgs g) {
   const char* __restrict__ A = static_cast<const char*>(g.a);
   const char* __restrict__ B = static_cast<const char*>(g.b);
 
+  const int nsteps = (int)(row_bytes / 64);
   for (int item = wave; item < total; item += nwaves) {
     const int s = item % S;
-    const int tn = item / S;
-    const int ti = tn / n_tiles;
-    const int nt = tn - ti * n_tiles;
+    const int rest = item / S;
+    const int ti = rest % num_tasks;
+    const int nt = rest / num_tasks;
     const moe_task_t task = g.tasks[ti];
     const int n0 = nt * 16 * NSUB;
-    const size_t k_off = (size_t)s * steps_per_slice * 64 + 16 * lgrp;
+    const int step0 = s * steps_per_slice;
+    const size_t k_off = (size_t)step0 * 64 + 16 * lgrp;
 
     const char* ap[MB];
     bool aok[MB];
@@ -79,10 +87,12 @@ grouped_gemm_kernel(moe_host::GemmArgs g) {
       if (aok[b]) arow = GATHER ? g.sorted_pairs[task.row_begin + rr] / g.topk : task.row_begin + rr;
       ap[b] = A + (size_t)arow * row_bytes + k_off;
     }
+    // packed weights: chunk (expert, 16-row block, step) of 1 KiB, lane-ordered
     const char* bp[NSUB];
 #pragma unroll
     for (int q = 0; q < NSUB; q++)
-      bp[q] = B + ((size_t)task.expert * g.N + n0 + 16 * q + lrow) * row_bytes + k_off;
+      bp[q] = B + (((size_t)task.expert * (g.N / 16) + n0 / 16 + q) * nsteps + step0) * 1024 +
+              16 * lane;
 
     f32x4 acc[MB][NSUB];
 #pragma unroll
@@ -96,9 +106,12 @@ grouped_gemm_kernel(moe_host::GemmArgs g) {
     auto load = [&](u32x4(&fa)[UNROLL][MB], u32x4(&fb)[UNROLL][NSUB], int grp) {
 #pragma unroll
       for (int u = 0; u < UNROLL; u++) {
-        const size_t off = (size_t)(grp * UNROLL + u) * 64;
+        const int step = grp * UNROLL + u;
+        const size_t off = (size_t)step * 64;
 #pragma unroll
-        for (int q = 0; q < NSUB; q++) fb[u][q] = *reinterpret_cast<const u32x4*>(bp[q] + off);
+        for (int q = 0; q < NSUB; q++)
+          fb[u][q] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(bp[q] + (size_t)step * 1024));
 #pragma unroll
         for (int b = 0; b < MB; b++)
           fa[u][b] = aok[b] ? *reinterpret_cast<const u32x4*>(ap[b] + off) : u32x4{0u, 0u, 0u, 0u};

@@ -60,7 +60,9 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   const long P = (long)T * k;
   const long active = P < E ? P : E;
   const long avg = active > 0 ? (P + active - 1) / active : 1;
-  p.block_m = avg <= 16 ? 16 : (avg <= 32 ? 32 : 64);
+  // tile height ~2x the mean rows per active expert, so that the usual
+  // spread of a uniform routing still fits one tile per expert
+  p.block_m = avg <= 8 ? 16 : (avg <= 16 ? 32 : 64);
   p.mb = p.block_m / 16;
   p.max_tasks = (int)(P / p.block_m + (P < E ? P : E));
   long est_tasks = (P + p.block_m - 1) / p.block_m;
@@ -312,6 +314,23 @@ int moe_workspace_layout(int T, int k, int E, int H, int I, int dtype, moe_works
   if (rc != MOE_OK) return rc;
   workspace_layout(dtype, T, k, H, I, make_plan(dtype, T, k, E, H, I), out);
   return MOE_OK;
+}
+
+int moe_pack_weights(const void* w, int E, int rows, int cols, int dtype, void* packed,
+                     void* stream) {
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_W8A8) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || rows < 1 || cols < 1) return MOE_ERR_INVALID_ARG;
+  const long row_bytes = (long)cols * (dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2);
+  if (rows % 16 || row_bytes % 64 || rows > 2 * 65536 || cols > 65536)
+    return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (!w || !packed || !aligned(w, 16) || !aligned(packed, 16)) return MOE_ERR_INVALID_ARG;
+  const size_t total = (size_t)E * rows * row_bytes;
+  const char* a = static_cast<const char*>(w);
+  const char* b = static_cast<const char*>(packed);
+  if (a < b + total && b < a + total) return MOE_ERR_INVALID_ARG;   // overlap
+  const hipError_t e = moe_host::launch_pack(w, E, rows, (int)row_bytes, packed,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int moe_build_routing_bf16(const int32_t* topk_ids, int T, int k, int E, int H, int I,

@@ -104,7 +104,7 @@ hipError_t launch_reduce(const float* y, int S, int P, const float* topk_w,
 struct GemmArgs {
   const void* a;            // gathered: x / xq [T][K]; contiguous: h / hq [P][K]
   const float* a_scale;     // fp8: per-row scales of a ([T] gathered, [P] contiguous)
-  const void* b;            // per-expert weights [E][N][K]
+  const void* b;            // per-expert weights [E][N][K], packed by launch_pack
   const float* b_scale;     // fp8: per-output-channel scales [E][N]
   const int32_t* sorted_pairs;  // gathered: pair index of each sorted row
   const int32_t* header;        // routing header (num_tasks at index 0)
@@ -124,6 +124,10 @@ struct GemmPlan {
   int unroll;               // 64-byte K steps per pipeline stage
   int grid;                 // workgroups of the persistent launch (4 waves each)
 };
+
+// Byte permutation of W[E][rows][row_bytes] into 1 KiB MFMA-fragment chunks.
+hipError_t launch_pack(const void* w, int E, int rows, int row_bytes, void* packed,
+                       hipStream_t s);
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, bool gather, bool fp8, const GemmPlan& plan,
                                hipStream_t s);

@@ -32,7 +32,11 @@ def path_dtype(wl):
     return "fp8" if wl.dtype == "fp8" else "bf16"
 
 
-def run_gpu(lib, x, ids, w, W, dtype):
+def run_gpu(lib, x, ids, w, W, dtype, packed=None):
+    """Run routing + forward; W is row-major (packed here) unless `packed` is given."""
+    if packed is None:
+        packed = lib.pack_weights(W, dtype)
+    W = packed
     x = x.cuda().bfloat16().contiguous()
     ids = ids.cuda().contiguous()
     w = w.cuda().float().contiguous()

@@ -87,7 +87,9 @@ def workload_weights(name):
         wl = WORKLOADS[name]
         W = device_weights(wl)
         Wc = {k: v.cpu() for k, v in W.items()}
-        _weights_cache[name] = (W, Wc)
+        Wp = __import__("mixture_experts_layer_lds_amd").pack_weights(W, path_dtype(wl))
+        del W
+        _weights_cache[name] = (Wp, Wc)
     return _weights_cache[name]
 
 
@@ -99,9 +101,9 @@ def test_full_size_sampled(lib, name, T):
     wl = WORKLOADS[name]
     dtype = path_dtype(wl)
     log(f"full {name} T={T} {dtype}")
-    W, Wc = workload_weights(name)
+    Wp, Wc = workload_weights(name)
     x, ids, w = make_tokens(wl, T)
-    out, _, ws = run_gpu(lib, x, ids, w, W, dtype)
+    out, _, ws = run_gpu(lib, x, ids, w, None, dtype, packed=Wp)
     rows = sample_rows(T, 6 if wl.I * wl.H > 2 ** 25 else 12, seed=T)
     ref = oracle_rows(x, ids, w, Wc, dtype, rows=rows)
     check_tol(out64(out)[rows], ref, dtype, f"{name} T={T} rows={len(rows)}")
@@ -153,7 +155,7 @@ def test_empty_batch_is_a_no_op(lib):
     x = torch.zeros(0, 128, dtype=torch.bfloat16, device="cuda")
     ids = torch.zeros(0, 2, dtype=torch.int32, device="cuda")
     w = torch.zeros(0, 2, dtype=torch.float32, device="cuda")
-    out, _, _ = lib.moe_layer(x, ids, w, W)
+    out, _, _ = lib.moe_layer(x, ids, w, lib.pack_weights(W))
     torch.cuda.synchronize()
     assert out.shape == (0, 128)
 
@@ -169,6 +171,8 @@ def test_graph_capture_replays_match_eager(lib):
     routing = lib.alloc_routing(T, k, E, H, I)
     ws = lib.alloc_workspace(T, k, E, H, I)
     out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    Wr = W
+    W = lib.pack_weights(Wr)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -192,5 +196,34 @@ def test_graph_capture_replays_match_eager(lib):
     ids.copy_(ids2)
     g.replay()
     torch.cuda.synchronize()
-    ref2, _, _ = run_gpu(lib, x, ids2, w, W, "bf16")
+    ref2, _, _ = run_gpu(lib, x, ids2, w, Wr, "bf16")
     assert torch.equal(out, ref2)
+
+
+@pytest.mark.parametrize("dtype,E,rows,cols", [("bf16", 3, 32, 64), ("bf16", 2, 48, 160),
+                                                ("fp8", 3, 16, 128), ("fp8", 1, 64, 192)])
+def test_pack_weights_is_the_documented_permutation(lib, dtype, E, rows, cols):
+    g = torch.Generator().manual_seed(rows + cols)
+    if dtype == "bf16":
+        w = torch.randn(E, rows, cols, generator=g).bfloat16()
+        raw = w.view(torch.uint8).view(E, rows, cols * 2)
+    else:
+        w = torch.randint(0, 256, (E, rows, cols), generator=g, dtype=torch.uint8)
+        raw = w
+    packed = lib.moe_pack_weights(w.cuda(), dtype)
+    torch.cuda.synchronize()
+    got = packed.cpu().contiguous().view(torch.uint8).reshape(-1).numpy()
+    # reference: chunk (e, row block, 64-byte step) of 1 KiB; piece l = row l%16, bytes 16*(l//16)
+    rb = raw.numpy()
+    nb = rb.shape[2]
+    ref = np.empty(E * rows * nb, dtype=np.uint8)
+    o = 0
+    for e in range(E):
+        for blk in range(rows // 16):
+            for step in range(nb // 64):
+                for l in range(64):
+                    r = blk * 16 + l % 16
+                    c0 = step * 64 + 16 * (l // 16)
+                    ref[o:o + 16] = rb[e, r, c0:c0 + 16]
+                    o += 16
+    assert np.array_equal(got, ref)
