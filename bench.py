@@ -65,7 +65,9 @@ def stage_bytes(wl, active, P_valid, T):
     fp8 = wl.dtype == "fp8"
     bw = 1 if fp8 else 2
     bx = 1 if fp8 else 2
+    P = T * wl.k
     return {
+        "routing": P * 4 + P * 12,
         "quant_x": T * H * 2 + T * H + T * 4 if fp8 else 0,
         "gate_up": active * (2 * I * H * bw + (2 * I * 4 if fp8 else 0)) + T * H * bx
                    + P_valid * 2 * I * 4,
@@ -90,15 +92,22 @@ class Layer:
         self.ws = moe.alloc_workspace(T, k, E, H, I, dtype)
         self.out = torch.empty(T, H, dtype=torch.bfloat16, device=device)
 
-    def run(self, W=None):
-        m, wl, W = self.moe, self.wl, (W or self.W)
+    def run_routing(self):
+        m, wl = self.moe, self.wl
+        build = m.moe_build_routing_bf16 if self.dtype == "bf16" else m.moe_build_routing_fp8
+        build(self.ids, wl.E, wl.H, wl.I, self.routing)
+
+    def run_forward(self, W=None):
+        m, W = self.moe, (W or self.W)
         if self.dtype == "bf16":
-            m.moe_build_routing_bf16(self.ids, wl.E, wl.H, wl.I, self.routing)
             m.moe_forward_bf16(self.x, self.w, self.routing, W["w1"], W["w2"], self.ws, self.out)
         else:
-            m.moe_build_routing_fp8(self.ids, wl.E, wl.H, wl.I, self.routing)
             m.moe_forward_fp8(self.x, self.w, self.routing, W["w1"], W["w1_scale"], W["w2"],
                               W["w2_scale"], self.ws, self.out)
+
+    def run(self, W=None):
+        self.run_routing()
+        self.run_forward(W)
 
 
 def timed_steps(layer, steps, warmup):
@@ -111,6 +120,7 @@ def timed_steps(layer, steps, warmup):
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(steps)]
     rt = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
+    rr = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for step_ev in ev:          # materialise the events before handing them over
         for e in step_ev:
             e.record()
@@ -119,12 +129,15 @@ def timed_steps(layer, steps, warmup):
     for i in range(steps):
         moe.moe_set_stage_events(ev[i])
         rt[i][0].record()
-        layer.run()
+        layer.run_routing()
+        rr[i].record()
+        layer.run_forward()
         rt[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     moe.moe_set_stage_events(None)
     stage_ms = {s: [] for s in STAGES}
+    stage_ms["routing"] = [rt[i][0].elapsed_time(rr[i]) for i in range(steps)]
     for i in range(steps):
         for si, s in enumerate(STAGES):
             if layer.dtype != "fp8" and s == "quant_x":

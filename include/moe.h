@@ -110,20 +110,27 @@ typedef struct {
 } moe_routing_layout_t;
 
 /* Byte offsets of the parts of a forward workspace (all 256-byte aligned);
- * an offset of (size_t)-1 marks a part the dtype does not use.  The two
- * GEMMs may split their reduction into split_k1 / split_k2 slices whose
- * fp32 partial sums are added, in ascending slice order, by the kernel
- * that consumes them. */
+ * an offset of (size_t)-1 marks a part these sizes do not use.  Two tilings
+ * exist, chosen by a fixed function of the sizes (large_tiles):
+ *  - register streaming (few rows per expert, e.g. decode): the GEMMs may
+ *    split their reduction into split_k1 / split_k2 slices whose fp32 partial
+ *    sums the next kernel adds in ascending slice order;
+ *  - 128-row LDS tiles (many rows per expert): no split; SiLU(gate)*up is
+ *    formed in the gate-up GEMM's epilogue and the down rows are bf16. */
 typedef struct {
     size_t xq;          /* fp8: uint8 [T][H]   per-token e4m3 codes of x */
     size_t x_scale;     /* fp8: fp32  [T]      per-token scales of x */
-    size_t g;           /* fp32 [split_k1][P][2I] gate-up partial sums (scaled on fp8) */
+    size_t g;           /* streaming: fp32 [split_k1][P][2I] gate-up partial sums
+                           (scaled on fp8); LDS tiles + fp8: fp32 [P][I]
+                           SiLU(gate)*up before requantisation */
     size_t h;           /* bf16 [P][I] SiLU(gate)*up (bf16), or uint8 e4m3 codes [P][I] (fp8) */
     size_t h_scale;     /* fp8: fp32  [P]      per-row scales of h */
-    size_t y;           /* fp32 [split_k2][P][H] unweighted down-projection partial sums */
+    size_t y;           /* streaming: fp32 [split_k2][P][H] unweighted down partial sums;
+                           LDS tiles: bf16 [P][H] unweighted down rows */
     size_t total_bytes; /* minimum size of the workspace */
     int32_t split_k1;   /* slices of the gate-up reduction over H */
     int32_t split_k2;   /* slices of the down reduction over I */
+    int32_t large_tiles;/* 1: 128-row LDS tiles; 0: register streaming */
 } moe_workspace_layout_t;
 
 /* Human-readable name of a status code (static string). */

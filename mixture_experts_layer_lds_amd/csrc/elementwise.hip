@@ -26,9 +26,10 @@ __device__ __forceinline__ float block_max_256(float v, float* s_red) {
 // x[T][H] bf16 -> xq[T][H] e4m3 + scale[T]; H % 8 == 0.
 __global__ void __launch_bounds__(kRowThreads)
 quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restrict__ xq,
-                       float* __restrict__ scale) {
+                       float* __restrict__ scale, float* __restrict__ zero_rows, int zk) {
   __shared__ float s_red[4];
   const int t = blockIdx.x;
+  if (zero_rows && threadIdx.x < zk) zero_rows[(size_t)t * zk + threadIdx.x] = 0.0f;
   const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
   const int nvec = H / 8;
   float amax = 0.0f;
@@ -132,9 +133,11 @@ act_fp8_kernel(const float* __restrict__ g, int S, int P, int I,
 }
 
 // out[t][:] = bf16( sum_{j ascending, pair valid} w[t][j] * sum_s y[s][pos][:] );
-// grid (token, column chunk of kRowThreads*4).
+// grid (token, column chunk of kRowThreads*4).  y is fp32 [S][P][H], or bf16
+// [P][H] when Y_BF16.
+template <bool Y_BF16>
 __global__ void __launch_bounds__(kRowThreads)
-reduce_kernel(const float* __restrict__ y, int S, int P, const float* __restrict__ topk_w,
+reduce_kernel(const void* __restrict__ yv, int S, int P, const float* __restrict__ topk_w,
               const int32_t* __restrict__ pair_pos, const int32_t* __restrict__ expert_offsets,
               int E, int k, int H, uint16_t* __restrict__ out) {
   const int t = blockIdx.x;
@@ -147,9 +150,16 @@ reduce_kernel(const float* __restrict__ y, int S, int P, const float* __restrict
     const int p = t * k + j;
     const int r = pair_pos[p];
     if (r >= valid) continue;   // dropped pair
-    const float* yrow = y + (size_t)r * H + 4 * i;
-    f32x4 v = *reinterpret_cast<const f32x4*>(yrow);
-    for (int s = 1; s < S; s++) v += *reinterpret_cast<const f32x4*>(yrow + s * slice);
+    f32x4 v;
+    if constexpr (Y_BF16) {
+      const u32x2 b = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(yv) + (size_t)r * H + 4 * i);
+      v = f32x4{bf16_bits_to_f32(b.x & 0xffffu), bf16_bits_to_f32(b.x >> 16),
+                bf16_bits_to_f32(b.y & 0xffffu), bf16_bits_to_f32(b.y >> 16)};
+    } else {
+      const float* yrow = static_cast<const float*>(yv) + (size_t)r * H + 4 * i;
+      v = *reinterpret_cast<const f32x4*>(yrow);
+      for (int s = 1; s < S; s++) v += *reinterpret_cast<const f32x4*>(yrow + s * slice);
+    }
     const float w = topk_w[p];
 #pragma unroll
     for (int q = 0; q < 4; q++) acc[q] = __fadd_rn(acc[q], __fmul_rn(w, v[q]));
@@ -165,9 +175,9 @@ reduce_kernel(const float* __restrict__ y, int S, int P, const float* __restrict
 namespace moe_host {
 
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* scale,
-                                  hipStream_t s) {
+                                  float* zero_rows, int zk, hipStream_t s) {
   hipLaunchKernelGGL(moe::quant_rows_bf16_kernel, dim3(T), dim3(moe::kRowThreads), 0, s, x, H,
-                     xq, scale);
+                     xq, scale, zero_rows, zk);
   return hipGetLastError();
 }
 
@@ -184,12 +194,16 @@ hipError_t launch_act(const float* g, int S, int P, int I, const int32_t* expert
   return hipGetLastError();
 }
 
-hipError_t launch_reduce(const float* y, int S, int P, const float* topk_w,
+hipError_t launch_reduce(const void* y, bool y_bf16, int S, int P, const float* topk_w,
                          const int32_t* pair_pos, const int32_t* expert_offsets, int E, int T,
                          int k, int H, uint16_t* out, hipStream_t s) {
   const dim3 grid(T, (H / 4 + moe::kRowThreads - 1) / moe::kRowThreads);
-  hipLaunchKernelGGL(moe::reduce_kernel, grid, dim3(moe::kRowThreads), 0, s, y, S, P, topk_w,
-                     pair_pos, expert_offsets, E, k, H, out);
+  if (y_bf16)
+    hipLaunchKernelGGL(moe::reduce_kernel<true>, grid, dim3(moe::kRowThreads), 0, s, y, S, P,
+                       topk_w, pair_pos, expert_offsets, E, k, H, out);
+  else
+    hipLaunchKernelGGL(moe::reduce_kernel<false>, grid, dim3(moe::kRowThreads), 0, s, y, S, P,
+                       topk_w, pair_pos, expert_offsets, E, k, H, out);
   return hipGetLastError();
 }
 

@@ -22,8 +22,10 @@ struct Plan {
   int block_m = 16;
   int mb = 1;
   int max_tasks = 0;
-  int split1 = 1, unroll1 = 1;   // gate-up: K = H
-  int split2 = 1, unroll2 = 1;   // down:    K = I
+  bool tiled = false;            // LDS-tiled GEMMs (large T) instead of register streaming
+  int bn1 = 128, bn2 = 128;      // tiled: N tile of gate-up / down
+  int split1 = 1, unroll1 = 1;   // streaming gate-up: K = H
+  int split2 = 1, unroll2 = 1;   // streaming down:    K = I
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -60,19 +62,25 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   const long P = (long)T * k;
   const long active = P < E ? P : E;
   const long avg = active > 0 ? (P + active - 1) / active : 1;
-  // tile height ~2x the mean rows per active expert, so that the usual
-  // spread of a uniform routing still fits one tile per expert
-  p.block_m = avg <= 8 ? 16 : (avg <= 16 ? 32 : 64);
+  // Many rows per expert: 128-row LDS tiles.  Otherwise register-streaming
+  // tiles about twice the mean rows per active expert, so that the usual
+  // spread of a uniform routing still fits one tile per expert.
+  p.tiled = avg > 48;
+  p.block_m = p.tiled ? 128 : (avg <= 8 ? 16 : (avg <= 16 ? 32 : 64));
   p.mb = p.block_m / 16;
   p.max_tasks = (int)(P / p.block_m + (P < E ? P : E));
+  p.bn1 = 128;                           // 64 output columns of h per tile: I % 64 == 0
+  p.bn2 = (H % 128 == 0) ? 128 : 64;
   long est_tasks = (P + p.block_m - 1) / p.block_m;
   if (est_tasks < active) est_tasks = active;
   const int esz = dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2;
   const int nsteps1 = H * esz / 64, nsteps2 = I * esz / 64;
-  p.unroll1 = choose_unroll(nsteps1, p.mb);
-  p.unroll2 = choose_unroll(nsteps2, p.mb);
-  p.split1 = choose_split(nsteps1, p.unroll1, est_tasks * (2L * I / 16));
-  p.split2 = choose_split(nsteps2, p.unroll2, est_tasks * ((long)H / 16));
+  if (!p.tiled) {
+    p.unroll1 = choose_unroll(nsteps1, p.mb);
+    p.unroll2 = choose_unroll(nsteps2, p.mb);
+    p.split1 = choose_split(nsteps1, p.unroll1, est_tasks * (2L * I / 16));
+    p.split2 = choose_split(nsteps2, p.unroll2, est_tasks * ((long)H / 16));
+  }
   return p;
 }
 
@@ -106,13 +114,17 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
   };
   W->xq = fp8 ? take((size_t)T * H) : kNone;
   W->x_scale = fp8 ? take(4 * (size_t)T) : kNone;
-  W->g = take(4 * (size_t)p.split1 * P * 2 * I);
+  if (p.tiled)
+    W->g = fp8 ? take(4 * P * I) : kNone;               // fp32 SiLU(gate)*up before requant
+  else
+    W->g = take(4 * (size_t)p.split1 * P * 2 * I);      // fp32 gate-up partial sums
   W->h = take(P * I * (fp8 ? 1 : 2));
   W->h_scale = fp8 ? take(4 * P) : kNone;
-  W->y = take(4 * (size_t)p.split2 * P * H);
+  W->y = p.tiled ? take(2 * P * H) : take(4 * (size_t)p.split2 * P * H);
   W->total_bytes = off;
   W->split_k1 = p.split1;
   W->split_k2 = p.split2;
+  W->large_tiles = p.tiled ? 1 : 0;
 }
 
 // Compute-unit count per device, queried once.
@@ -216,8 +228,6 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
   const RoutingView R = view_routing(routing, L);
   char* ws = static_cast<char*>(workspace);
   const int P = T * k;
-  float* g = reinterpret_cast<float*>(ws + W.g);
-  float* y = reinterpret_cast<float*>(ws + W.y);
   void* h = ws + W.h;
   float* h_scale = fp8 ? reinterpret_cast<float*>(ws + W.h_scale) : nullptr;
   uint8_t* xq = fp8 ? reinterpret_cast<uint8_t*>(ws + W.xq) : nullptr;
@@ -226,9 +236,71 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
 
   if (fp8) {
     StageScope st(s, 0);
-    e = moe_host::launch_quant_rows_bf16(static_cast<const uint16_t*>(x), T, H, xq, x_scale, s);
+    e = moe_host::launch_quant_rows_bf16(static_cast<const uint16_t*>(x), T, H, xq, x_scale,
+                                         p.tiled ? h_scale : nullptr, k, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
+  if (p.tiled) {
+    const int grid = cus * 2;
+    float* h32 = fp8 ? reinterpret_cast<float*>(ws + W.g) : nullptr;
+    {
+      StageScope st(s, 1);
+      moe_host::TiledArgs a{};
+      a.a = fp8 ? static_cast<const void*>(xq) : x;
+      a.a_scale = x_scale;
+      a.b = w1;
+      a.b_scale = w1_scale;
+      a.sorted_pairs = R.sorted_pairs;
+      a.header = R.header;
+      a.tasks = R.tasks;
+      a.c = fp8 ? static_cast<void*>(h32) : h;
+      a.row_amax = h_scale;
+      a.K = H;
+      a.N_out = I;
+      a.w_rows = 2 * I;
+      a.topk = k;
+      a.max_tasks = p.max_tasks;
+      e = moe_host::launch_tiled_gemm(a, true, fp8, p.bn1, grid, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 2);
+      if (fp8) {
+        e = moe_host::launch_requant_rows(h32, P, I, R.expert_offsets, E,
+                                          static_cast<uint8_t*>(h), h_scale, s);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+      }
+    }
+    {
+      StageScope st(s, 3);
+      moe_host::TiledArgs a{};
+      a.a = h;
+      a.a_scale = h_scale;
+      a.b = w2;
+      a.b_scale = w2_scale;
+      a.sorted_pairs = R.sorted_pairs;
+      a.header = R.header;
+      a.tasks = R.tasks;
+      a.c = ws + W.y;
+      a.K = I;
+      a.N_out = H;
+      a.w_rows = H;
+      a.topk = k;
+      a.max_tasks = p.max_tasks;
+      e = moe_host::launch_tiled_gemm(a, false, fp8, p.bn2, grid, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 4);
+      e = moe_host::launch_reduce(ws + W.y, true, 1, P, topk_w, R.pair_pos, R.expert_offsets, E,
+                                  T, k, H, static_cast<uint16_t*>(out), s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+  }
+
+  float* g = reinterpret_cast<float*>(ws + W.g);
+  float* y = reinterpret_cast<float*>(ws + W.y);
   {
     StageScope st(s, 1);
     GemmArgs a{};
@@ -278,8 +350,8 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
   }
   {
     StageScope st(s, 4);
-    e = moe_host::launch_reduce(y, p.split2, P, topk_w, R.pair_pos, R.expert_offsets, E, T, k, H,
-                                static_cast<uint16_t*>(out), s);
+    e = moe_host::launch_reduce(y, false, p.split2, P, topk_w, R.pair_pos, R.expert_offsets, E, T,
+                                k, H, static_cast<uint16_t*>(out), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;

@@ -87,17 +87,19 @@ namespace moe_host {
 hipError_t launch_route(const int32_t* ids, int P, int E, int block_m, int max_tasks,
                         void* routing, const moe_routing_layout_t& L, hipStream_t s);
 
-// Per-token e4m3 quantisation of bf16 rows x[T][H].
+// Per-token e4m3 quantisation of bf16 rows x[T][H]; when zero_rows is not
+// null the same launch also clears zero_rows[0 .. T*zk) (row amax slots).
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* scale,
-                                  hipStream_t s);
+                                  float* zero_rows, int zk, hipStream_t s);
 
 // SiLU-and-mul of the gate-up partial sums g[S][P][2I] for the valid sorted
 // rows; writes bf16 h[P][I] (fp8 = false) or e4m3 codes h[P][I] + scales.
 hipError_t launch_act(const float* g, int S, int P, int I, const int32_t* expert_offsets, int E,
                       bool fp8, void* h, float* h_scale, hipStream_t s);
 
-// out[t] = bf16(sum_j w[t][j] * sum_s y[s][pos[t*k+j]]) over valid pairs.
-hipError_t launch_reduce(const float* y, int S, int P, const float* topk_w,
+// out[t] = bf16(sum_j w[t][j] * sum_s y[s][pos[t*k+j]]) over valid pairs;
+// y is fp32 [S][P][H] (y_bf16 = false) or bf16 [P][H] (S = 1).
+hipError_t launch_reduce(const void* y, bool y_bf16, int S, int P, const float* topk_w,
                          const int32_t* pair_pos, const int32_t* expert_offsets, int E, int T,
                          int k, int H, uint16_t* out, hipStream_t s);
 
@@ -131,5 +133,32 @@ hipError_t launch_pack(const void* w, int E, int rows, int row_bytes, void* pack
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, bool gather, bool fp8, const GemmPlan& plan,
                                hipStream_t s);
+
+// LDS-tiled grouped GEMM (128-row task tiles).  Gate-up mode writes
+// SiLU(gate)*up (bf16, or fp32 + row amax on the fp8 path); down mode writes
+// bf16 rows.
+struct TiledArgs {
+  const void* a;                // gate-up: x / xq [T][K] (gathered); down: h / hq [P][K]
+  const float* a_scale;         // fp8: x scales [T] / h scales [P]
+  const void* b;                // packed weights, w_rows rows per expert
+  const float* b_scale;         // fp8: [E][w_rows]
+  const int32_t* sorted_pairs;
+  const int32_t* header;
+  const moe_task_t* tasks;
+  void* c;                      // gate-up: h [P][N_out]; down: y [P][N_out] bf16
+  float* row_amax;              // fp8 gate-up: [P] atomic-max slots (pre-cleared)
+  int K;                        // reduction length (elements)
+  int N_out;                    // output columns (I for gate-up, H for down)
+  int w_rows;                   // weight rows per expert (2I or H)
+  int topk;
+  int max_tasks;
+};
+
+hipError_t launch_tiled_gemm(const TiledArgs& a, bool gateup, bool fp8, int bn, int grid,
+                             hipStream_t s);
+
+// fp32 rows -> e4m3 codes with the row amax held in h_scale (replaced by the scale).
+hipError_t launch_requant_rows(const float* h32, int P, int I, const int32_t* expert_offsets,
+                               int E, uint8_t* hq, float* h_scale, hipStream_t s);
 
 }  // namespace moe_host

@@ -1,0 +1,320 @@
+// LDS-tiled grouped expert GEMM for large token counts (many rows per
+// expert), where the layer turns from HBM-bound to MFMA-bound.
+//
+// Same pipeline role as grouped_gemm.hip (HPC-Ops x SGLang blog, section
+// "MoE": gate-up reads tokens through the route index, persistent grid over
+// the task map), but each workgroup owns a BM x BN output tile of one task
+// and stages its operands through LDS, so every A row and weight column is
+// fetched once per tile and reused by several waves.
+//
+//  * 256 threads = 2 x 2 waves; each wave computes (BM/2) x (BN/2) with
+//    v_mfma_f32_16x16x32_bf16 (or two fp8 MFMAs per 64-byte step).
+//  * One K iteration covers 128 bytes of every row (two 64-byte steps).
+//    LDS holds the A and B tiles of an iteration in 1 KiB chunks laid out
+//    in MFMA lane order (piece l of a chunk = row l % 16, bytes 16*(l/16)),
+//    the same order the weights are packed in, so weight chunks are copied
+//    verbatim and every fragment read is a conflict-free, lane-contiguous
+//    128-bit LDS read.  Two LDS stages: the next iteration's global loads
+//    are in flight while the current one is multiplied.
+//  * Gate-up mode pairs gate and up column blocks inside each wave (wave
+//    column half c holds gate blocks and the matching up blocks), so
+//    SiLU(gate)*up is formed in registers in the epilogue and the fp32 gate/
+//    up sums never reach memory.  The bf16 path stores h in bf16; the fp8
+//    path stores h in fp32 and folds each row's amax into h_scale with an
+//    atomic max on the (non-negative) float bits, which is order-independent;
+//    a small kernel then requantises the rows.
+//  * Down mode stores the unweighted rows y in bf16 for the top-k reduction.
+//  * Work items (task, n-tile) are handed out XCD-aware: consecutive items
+//    go to workgroups of the same XCD, so the A rows of a task and the
+//    weight block of an expert are shared through one L2.
+#include "moe_common.h"
+
+namespace moe {
+
+constexpr int kTileThreads = 256;
+constexpr int kIterSteps = 2;   // 64-byte K steps per K iteration
+
+template <int BM, int BN>
+struct TileShape {
+  static constexpr int kWM = BM / 2, kWN = BN / 2;
+  static constexpr int kMB = kWM / 16, kNB = kWN / 16;
+  static constexpr int kAChunks = BM / 16 * kIterSteps;
+  static constexpr int kBChunks = BN / 16 * kIterSteps;
+  static constexpr int kAPieces = kAChunks * 64 / kTileThreads;
+  static constexpr int kBPieces = kBChunks * 64 / kTileThreads;
+  static constexpr int kStageBytes = (kAChunks + kBChunks) * 1024;
+};
+
+template <bool FP8>
+__device__ __forceinline__ void mfma_step_t(f32x4& acc, const u32x4& a, const u32x4& b) {
+  if constexpr (FP8) {
+    const i64x2 a2 = __builtin_bit_cast(i64x2, a);
+    const i64x2 b2 = __builtin_bit_cast(i64x2, b);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[0], b2[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[1], b2[1], acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+}
+
+// Max of v over the 16 lanes that share (lane >> 4).
+__device__ __forceinline__ float max16(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+template <int BM, int BN, bool GATEUP, bool FP8>
+__global__ void __launch_bounds__(kTileThreads, 2)
+tiled_gemm_kernel(moe_host::TiledArgs g) {
+  using S = TileShape<BM, BN>;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
+  // gate-up: each tile covers BN/2 output columns of h (BN/2 gate + BN/2 up rows of W1)
+  const int out_cols = GATEUP ? BN / 2 : BN;
+  const int n_tiles = g.N_out / out_cols;
+  const int total = num_tasks * n_tiles;
+  const size_t row_bytes = (size_t)g.K * (FP8 ? 1 : 2);
+  const int nsteps = (int)(row_bytes / 64);
+  const int nk = (nsteps + kIterSteps - 1) / kIterSteps;
+  const int w_blocks = g.w_rows / 16;   // 16-row blocks per expert in the packed weights
+  const char* __restrict__ A = static_cast<const char*>(g.a);
+  const char* __restrict__ B = static_cast<const char*>(g.b);
+
+  // XCD-aware order: workgroups are dispatched round-robin over 8 XCDs, so
+  // renumber them to give each XCD a contiguous run of items.
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per_xcd = G / 8, extra = G % 8;
+  const int vid = (xcd < extra ? xcd * (per_xcd + 1) : extra * (per_xcd + 1) + (xcd - extra) * per_xcd) + slot;
+
+  for (int item = vid; item < total; item += G) {
+    const int ti = item / n_tiles;
+    const int nt = item - ti * n_tiles;
+    const moe_task_t task = g.tasks[ti];
+
+    // --- per-thread global sources of its A and B pieces
+    const char* asrc[S::kAPieces];
+    bool aok[S::kAPieces];
+    int ast[S::kAPieces];
+#pragma unroll
+    for (int i = 0; i < S::kAPieces; i++) {
+      const int p = tid + kTileThreads * i;
+      const int c = p >> 6, l = p & 63;
+      const int rb = c / kIterSteps;
+      ast[i] = c % kIterSteps;
+      const int rr = rb * 16 + (l & 15);
+      aok[i] = rr < task.rows;
+      int arow = 0;
+      if (aok[i]) arow = GATEUP ? g.sorted_pairs[task.row_begin + rr] / g.topk : task.row_begin + rr;
+      asrc[i] = A + (size_t)arow * row_bytes + ast[i] * 64 + 16 * (l >> 4);
+    }
+    const char* bsrc[S::kBPieces];
+    int bst[S::kBPieces];
+#pragma unroll
+    for (int i = 0; i < S::kBPieces; i++) {
+      const int p = tid + kTileThreads * i;
+      const int c = p >> 6, l = p & 63;
+      const int j = c / kIterSteps;   // 16-row block of the tile's weight rows
+      bst[i] = c % kIterSteps;
+      int wrb;
+      if (GATEUP) {
+        const int half = BN / 32;
+        wrb = (j < half) ? (nt * half + j) : (g.N_out / 16 + nt * half + (j - half));
+      } else {
+        wrb = nt * (BN / 16) + j;
+      }
+      bsrc[i] = B + (((size_t)task.expert * w_blocks + wrb) * nsteps + bst[i]) * 1024 + 16 * l;
+    }
+
+    u32x4 ra[S::kAPieces], rb_[S::kBPieces];
+    auto gload = [&](int kt) {
+#pragma unroll
+      for (int i = 0; i < S::kAPieces; i++) {
+        const bool ok = aok[i] && (kt * kIterSteps + ast[i] < nsteps);
+        ra[i] = ok ? *reinterpret_cast<const u32x4*>(asrc[i] + (size_t)kt * 128) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < S::kBPieces; i++) {
+        const bool ok = kt * kIterSteps + bst[i] < nsteps;
+        rb_[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                          bsrc[i] + (size_t)kt * kIterSteps * 1024))
+                    : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    auto lstore = [&](int stage) {
+      char* base = lds + stage * S::kStageBytes;
+#pragma unroll
+      for (int i = 0; i < S::kAPieces; i++)
+        *reinterpret_cast<u32x4*>(base + (size_t)(tid + kTileThreads * i) * 16) = ra[i];
+#pragma unroll
+      for (int i = 0; i < S::kBPieces; i++)
+        *reinterpret_cast<u32x4*>(base + S::kAChunks * 1024 + (size_t)(tid + kTileThreads * i) * 16) = rb_[i];
+    };
+
+    f32x4 acc[S::kMB][S::kNB];
+#pragma unroll
+    for (int m = 0; m < S::kMB; m++)
+#pragma unroll
+      for (int q = 0; q < S::kNB; q++) acc[m][q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // LDS chunk index of this wave's q-th weight block
+    auto bblock = [&](int q) {
+      if (GATEUP) {
+        const int half = S::kNB / 2;
+        return q < half ? (wn * half + q) : (BN / 32 + wn * half + (q - half));
+      }
+      return wn * S::kNB + q;
+    };
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt++) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) gload(kt + 1);
+      const char* base = lds + cur * S::kStageBytes;
+#pragma unroll
+      for (int st = 0; st < kIterSteps; st++) {
+        u32x4 fa[S::kMB], fb[S::kNB];
+#pragma unroll
+        for (int m = 0; m < S::kMB; m++)
+          fa[m] = *reinterpret_cast<const u32x4*>(base + ((wm * S::kMB + m) * kIterSteps + st) * 1024 + 16 * lane);
+#pragma unroll
+        for (int q = 0; q < S::kNB; q++)
+          fb[q] = *reinterpret_cast<const u32x4*>(base + S::kAChunks * 1024 +
+                                                  (bblock(q) * kIterSteps + st) * 1024 + 16 * lane);
+#pragma unroll
+        for (int m = 0; m < S::kMB; m++)
+#pragma unroll
+          for (int q = 0; q < S::kNB; q++) mfma_step_t<FP8>(acc[m][q], fa[m], fb[q]);
+      }
+      if (kt + 1 < nk) lstore(cur ^ 1);
+      __syncthreads();
+    }
+
+    // --- epilogue: lane holds column (lane % 16) and rows 4*(lane/16)+i of each block
+    const int lrow = lane & 15, lgrp = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < S::kMB; m++) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int rr = wm * S::kWM + m * 16 + 4 * lgrp + i;
+        const bool ok = rr < task.rows;
+        const int r = task.row_begin + (ok ? rr : 0);
+        if constexpr (GATEUP) {
+          constexpr int half = S::kNB / 2;
+          float sx = 1.0f;
+          if constexpr (FP8) sx = ok ? g.a_scale[g.sorted_pairs[r] / g.topk] : 0.0f;
+          float rmax = 0.0f;
+#pragma unroll
+          for (int q = 0; q < half; q++) {
+            const int col = nt * (BN / 2) + wn * half * 16 + q * 16 + lrow;
+            float gv = acc[m][q][i], uv = acc[m][q + half][i];
+            if constexpr (FP8) {
+              gv = (gv * sx) * g.b_scale[(size_t)task.expert * g.w_rows + col];
+              uv = (uv * sx) * g.b_scale[(size_t)task.expert * g.w_rows + g.N_out + col];
+            }
+            const float hv = silu_f32(gv) * uv;
+            if (ok) {
+              if constexpr (FP8) {
+                static_cast<float*>(g.c)[(size_t)r * g.N_out + col] = hv;
+              } else {
+                static_cast<uint16_t*>(g.c)[(size_t)r * g.N_out + col] = f32_to_bf16_bits(hv);
+              }
+            }
+            rmax = __builtin_fmaxf(rmax, __builtin_fabsf(hv));
+          }
+          if constexpr (FP8) {
+            rmax = max16(rmax);
+            if (ok && lrow == 0)
+              atomicMax(reinterpret_cast<unsigned int*>(g.row_amax) + r, __float_as_uint(rmax));
+          }
+        } else {
+          float sa = 1.0f;
+          if constexpr (FP8) sa = ok ? g.a_scale[r] : 0.0f;
+#pragma unroll
+          for (int q = 0; q < S::kNB; q++) {
+            const int col = nt * BN + wn * S::kWN + q * 16 + lrow;
+            float v = acc[m][q][i];
+            if constexpr (FP8) v = (v * sa) * g.b_scale[(size_t)task.expert * g.w_rows + col];
+            if (ok) static_cast<uint16_t*>(g.c)[(size_t)r * g.N_out + col] = f32_to_bf16_bits(v);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, bool GATEUP, bool FP8>
+static hipError_t launch_tiled_t(const moe_host::TiledArgs& a, int grid, hipStream_t s) {
+  constexpr int lds_bytes = 2 * TileShape<BM, BN>::kStageBytes;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&tiled_gemm_kernel<BM, BN, GATEUP, FP8>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((tiled_gemm_kernel<BM, BN, GATEUP, FP8>), dim3(grid), dim3(kTileThreads),
+                     lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+// requantise fp32 rows h32[r][0..I) of the valid sorted rows with the
+// row amax accumulated in h_scale[r] (replaced by the row scale).
+__global__ void __launch_bounds__(256)
+requant_rows_kernel(const float* __restrict__ h32, int I, const int32_t* __restrict__ expert_offsets,
+                    int E, uint8_t* __restrict__ hq, float* __restrict__ h_scale) {
+  const int r = blockIdx.x;
+  if (r >= expert_offsets[E]) return;
+  const float amax = h_scale[r];
+  __syncthreads();   // every thread has read the amax before it is replaced
+  float sc, inv;
+  e4m3_row_scales(amax, &sc, &inv);
+  const f32x4* row = reinterpret_cast<const f32x4*>(h32 + (size_t)r * I);
+  uint32_t* q = reinterpret_cast<uint32_t*>(hq + (size_t)r * I);
+  for (int i = threadIdx.x; i < I / 4; i += 256) {
+    const f32x4 v = row[i];
+    q[i] = f32x4_to_e4m3x4_sat(__fmul_rn(v[0], inv), __fmul_rn(v[1], inv), __fmul_rn(v[2], inv),
+                               __fmul_rn(v[3], inv));
+  }
+  if (threadIdx.x == 0) h_scale[r] = sc;
+}
+
+}  // namespace moe
+
+namespace moe_host {
+
+hipError_t launch_tiled_gemm(const TiledArgs& a, bool gateup, bool fp8, int bn, int grid,
+                             hipStream_t s) {
+  if (bn == 128) {
+    if (gateup) return fp8 ? moe::launch_tiled_t<128, 128, true, true>(a, grid, s)
+                           : moe::launch_tiled_t<128, 128, true, false>(a, grid, s);
+    return fp8 ? moe::launch_tiled_t<128, 128, false, true>(a, grid, s)
+               : moe::launch_tiled_t<128, 128, false, false>(a, grid, s);
+  }
+  if (bn == 64) {
+    if (gateup) return fp8 ? moe::launch_tiled_t<128, 64, true, true>(a, grid, s)
+                           : moe::launch_tiled_t<128, 64, true, false>(a, grid, s);
+    return fp8 ? moe::launch_tiled_t<128, 64, false, true>(a, grid, s)
+               : moe::launch_tiled_t<128, 64, false, false>(a, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_requant_rows(const float* h32, int P, int I, const int32_t* expert_offsets,
+                               int E, uint8_t* hq, float* h_scale, hipStream_t s) {
+  hipLaunchKernelGGL(moe::requant_rows_kernel, dim3(P), dim3(256), 0, s, h32, I, expert_offsets,
+                     E, hq, h_scale);
+  return hipGetLastError();
+}
+
+}  // namespace moe_host

@@ -36,6 +36,10 @@ SMALL = [
     (64, 256, 320, 8, 129, 0.05),
     (3, 64, 64, 3, 200, 0.0),
     (256, 192, 128, 8, 9, 0.0),
+    # many rows per expert: 128-row LDS tiles (ragged last tiles, dropped pairs)
+    (8, 256, 192, 2, 700, 0.05),
+    (8, 192, 320, 2, 700, 0.0),       # H % 128 != 0; fp8 rows of 192 / 320 bytes
+    (16, 512, 256, 4, 1500, 0.02),
 ]
 
 
