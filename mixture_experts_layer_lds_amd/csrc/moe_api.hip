@@ -69,8 +69,14 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   p.block_m = p.tiled ? 128 : (avg <= 8 ? 16 : (avg <= 16 ? 32 : 64));
   p.mb = p.block_m / 16;
   p.max_tasks = (int)(P / p.block_m + (P < E ? P : E));
-  p.bn1 = 128;                           // 64 output columns of h per tile: I % 64 == 0
-  p.bn2 = (H % 128 == 0) ? 128 : 64;
+  // LDS tiles: the direct-to-LDS 128x256 ring where the shape allows it
+  // (128-byte K iterations, >= 2 of them, 128 h columns / 256 y columns per
+  // tile), else the register-staged 128x128 / 128x64 tiles.
+  const int esz_t = dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2;
+  const bool dma1 = (H * esz_t) % 128 == 0 && H * esz_t >= 256 && I % 128 == 0;
+  const bool dma2 = (I * esz_t) % 128 == 0 && I * esz_t >= 256 && H % 256 == 0;
+  p.bn1 = dma1 ? 256 : 128;              // 128 (or 64) output columns of h per tile
+  p.bn2 = dma2 ? 256 : ((H % 128 == 0) ? 128 : 64);
   long est_tasks = (P + p.block_m - 1) / p.block_m;
   if (est_tasks < active) est_tasks = active;
   const int esz = dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2;
@@ -241,7 +247,8 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (p.tiled) {
-    const int grid = cus * 2;
+    const int grid1 = p.bn1 == 256 ? cus : cus * 2;   // the 144 KiB LDS ring fits once per CU
+    const int grid2 = p.bn2 == 256 ? cus : cus * 2;
     float* h32 = fp8 ? reinterpret_cast<float*>(ws + W.g) : nullptr;
     {
       StageScope st(s, 1);
@@ -260,7 +267,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
       a.w_rows = 2 * I;
       a.topk = k;
       a.max_tasks = p.max_tasks;
-      e = moe_host::launch_tiled_gemm(a, true, fp8, p.bn1, grid, s);
+      e = moe_host::launch_tiled_gemm(a, true, fp8, p.bn1, grid1, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
     {
@@ -287,7 +294,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
       a.w_rows = H;
       a.topk = k;
       a.max_tasks = p.max_tasks;
-      e = moe_host::launch_tiled_gemm(a, false, fp8, p.bn2, grid, s);
+      e = moe_host::launch_tiled_gemm(a, false, fp8, p.bn2, grid2, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
     {
