@@ -132,42 +132,54 @@ act_fp8_kernel(const float* __restrict__ g, int S, int P, int I,
   if (threadIdx.x == 0) h_scale[r] = sc;
 }
 
-// out[t][:] = bf16( sum_{j ascending, pair valid} w[t][j] * sum_s y[s][pos][:] );
-// grid (token, column chunk of kRowThreads*4).  y is fp32 [S][P][H], or bf16
-// [P][H] when Y_BF16.
+// out[t][:] = bf16( sum_{j ascending, pair valid} w[t][j] * sum_s y[s][pos][:] ).
+// y is fp32 [S][P][H] (4 columns per thread, 16-byte loads), or bf16 [P][H]
+// when Y_BF16 (8 columns per thread, 16-byte loads).  Grid (token, column
+// chunk of kRowThreads * columns-per-thread).
 template <bool Y_BF16>
 __global__ void __launch_bounds__(kRowThreads)
 reduce_kernel(const void* __restrict__ yv, int S, int P, const float* __restrict__ topk_w,
               const int32_t* __restrict__ pair_pos, const int32_t* __restrict__ expert_offsets,
               int E, int k, int H, uint16_t* __restrict__ out) {
+  constexpr int C = Y_BF16 ? 8 : 4;
   const int t = blockIdx.x;
-  const int i = blockIdx.y * kRowThreads + threadIdx.x;   // vec4 column index
-  if (4 * i >= H) return;
+  const int c0 = (blockIdx.y * kRowThreads + threadIdx.x) * C;   // first column
+  if (c0 >= H) return;
   const int valid = expert_offsets[E];
   const size_t slice = (size_t)P * H;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[C];
+#pragma unroll
+  for (int q = 0; q < C; q++) acc[q] = 0.0f;
   for (int j = 0; j < k; j++) {
     const int p = t * k + j;
     const int r = pair_pos[p];
     if (r >= valid) continue;   // dropped pair
-    f32x4 v;
+    float v[C];
     if constexpr (Y_BF16) {
-      const u32x2 b = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(yv) + (size_t)r * H + 4 * i);
-      v = f32x4{bf16_bits_to_f32(b.x & 0xffffu), bf16_bits_to_f32(b.x >> 16),
-                bf16_bits_to_f32(b.y & 0xffffu), bf16_bits_to_f32(b.y >> 16)};
+      const u32x4 b = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(yv) + (size_t)r * H + c0);
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        v[2 * q] = bf16_bits_to_f32(b[q] & 0xffffu);
+        v[2 * q + 1] = bf16_bits_to_f32(b[q] >> 16);
+      }
     } else {
-      const float* yrow = static_cast<const float*>(yv) + (size_t)r * H + 4 * i;
-      v = *reinterpret_cast<const f32x4*>(yrow);
-      for (int s = 1; s < S; s++) v += *reinterpret_cast<const f32x4*>(yrow + s * slice);
+      const float* yrow = static_cast<const float*>(yv) + (size_t)r * H + c0;
+      f32x4 a = *reinterpret_cast<const f32x4*>(yrow);
+      for (int s = 1; s < S; s++) a += *reinterpret_cast<const f32x4*>(yrow + s * slice);
+#pragma unroll
+      for (int q = 0; q < 4; q++) v[q] = a[q];
     }
     const float w = topk_w[p];
 #pragma unroll
-    for (int q = 0; q < 4; q++) acc[q] = __fadd_rn(acc[q], __fmul_rn(w, v[q]));
+    for (int q = 0; q < C; q++) acc[q] = __fadd_rn(acc[q], __fmul_rn(w, v[q]));
   }
-  u32x2 packed;
-  packed.x = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
-  packed.y = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
-  *reinterpret_cast<u32x2*>(out + (size_t)t * H + 4 * i) = packed;
+  uint32_t packed[C / 2];
+#pragma unroll
+  for (int q = 0; q < C / 2; q++)
+    packed[q] = (uint32_t)f32_to_bf16_bits(acc[2 * q]) | ((uint32_t)f32_to_bf16_bits(acc[2 * q + 1]) << 16);
+  uint16_t* o = out + (size_t)t * H + c0;
+  if constexpr (Y_BF16) *reinterpret_cast<u32x4*>(o) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+  else *reinterpret_cast<u32x2*>(o) = u32x2{packed[0], packed[1]};
 }
 
 }  // namespace moe
@@ -197,7 +209,8 @@ hipError_t launch_act(const float* g, int S, int P, int I, const int32_t* expert
 hipError_t launch_reduce(const void* y, bool y_bf16, int S, int P, const float* topk_w,
                          const int32_t* pair_pos, const int32_t* expert_offsets, int E, int T,
                          int k, int H, uint16_t* out, hipStream_t s) {
-  const dim3 grid(T, (H / 4 + moe::kRowThreads - 1) / moe::kRowThreads);
+  const int cols = y_bf16 ? 8 : 4;
+  const dim3 grid(T, (H / cols + moe::kRowThreads - 1) / moe::kRowThreads);
   if (y_bf16)
     hipLaunchKernelGGL(moe::reduce_kernel<true>, grid, dim3(moe::kRowThreads), 0, s, y, S, P,
                        topk_w, pair_pos, expert_offsets, E, k, H, out);

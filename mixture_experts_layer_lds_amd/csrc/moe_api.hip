@@ -23,6 +23,7 @@ struct Plan {
   int mb = 1;
   int max_tasks = 0;
   bool tiled = false;            // LDS-tiled GEMMs (large T) instead of register streaming
+  int bm_t = 128;                // tiled: rows per tile (128 or 256)
   int bn1 = 128, bn2 = 128;      // tiled: N tile of gate-up / down
   int split1 = 1, unroll1 = 1;   // streaming gate-up: K = H
   int split2 = 1, unroll2 = 1;   // streaming down:    K = I
@@ -62,21 +63,25 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   const long P = (long)T * k;
   const long active = P < E ? P : E;
   const long avg = active > 0 ? (P + active - 1) / active : 1;
-  // Many rows per expert: 128-row LDS tiles.  Otherwise register-streaming
-  // tiles about twice the mean rows per active expert, so that the usual
-  // spread of a uniform routing still fits one tile per expert.
+  // Many rows per expert: LDS tiles.  Otherwise register-streaming tiles
+  // about twice the mean rows per active expert, so that the usual spread
+  // of a uniform routing still fits one tile per expert.
   p.tiled = avg > 48;
-  p.block_m = p.tiled ? 128 : (avg <= 8 ? 16 : (avg <= 16 ? 32 : 64));
+  const int esz_t = dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2;
+  const int rb1 = H * esz_t, rb2 = I * esz_t;   // row bytes of the two reductions
+  // 256 x 256 direct-to-LDS tiles (4-stage ring, 64-byte K steps) when the
+  // experts hold enough rows to fill them; else 128-row tiles: the 128 x 256
+  // direct-to-LDS ring (128-byte K steps) where the shape allows it, or the
+  // register-staged 128 x 128 / 128 x 64 tiles.
+  const bool big = avg >= 96 && I % 128 == 0 && H % 256 == 0 && rb1 >= 192 && rb2 >= 192;
+  p.bm_t = big ? 256 : 128;
+  const bool dma1 = rb1 % 128 == 0 && rb1 >= 256 && I % 128 == 0;
+  const bool dma2 = rb2 % 128 == 0 && rb2 >= 256 && H % 256 == 0;
+  p.bn1 = big || dma1 ? 256 : 128;       // 128 (or 64) output columns of h per tile
+  p.bn2 = big || dma2 ? 256 : ((H % 128 == 0) ? 128 : 64);
+  p.block_m = p.tiled ? p.bm_t : (avg <= 8 ? 16 : (avg <= 16 ? 32 : 64));
   p.mb = p.block_m / 16;
   p.max_tasks = (int)(P / p.block_m + (P < E ? P : E));
-  // LDS tiles: the direct-to-LDS 128x256 ring where the shape allows it
-  // (128-byte K iterations, >= 2 of them, 128 h columns / 256 y columns per
-  // tile), else the register-staged 128x128 / 128x64 tiles.
-  const int esz_t = dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2;
-  const bool dma1 = (H * esz_t) % 128 == 0 && H * esz_t >= 256 && I % 128 == 0;
-  const bool dma2 = (I * esz_t) % 128 == 0 && I * esz_t >= 256 && H % 256 == 0;
-  p.bn1 = dma1 ? 256 : 128;              // 128 (or 64) output columns of h per tile
-  p.bn2 = dma2 ? 256 : ((H % 128 == 0) ? 128 : 64);
   long est_tasks = (P + p.block_m - 1) / p.block_m;
   if (est_tasks < active) est_tasks = active;
   const int esz = dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2;
@@ -247,7 +252,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (p.tiled) {
-    const int grid1 = p.bn1 == 256 ? cus : cus * 2;   // the 144 KiB LDS ring fits once per CU
+    const int grid1 = p.bn1 == 256 ? cus : cus * 2;   // a direct-to-LDS ring fits once per CU
     const int grid2 = p.bn2 == 256 ? cus : cus * 2;
     float* h32 = fp8 ? reinterpret_cast<float*>(ws + W.g) : nullptr;
     {
@@ -267,7 +272,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
       a.w_rows = 2 * I;
       a.topk = k;
       a.max_tasks = p.max_tasks;
-      e = moe_host::launch_tiled_gemm(a, true, fp8, p.bn1, grid1, s);
+      e = moe_host::launch_tiled_gemm(a, true, fp8, p.bm_t, p.bn1, grid1, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
     {
@@ -294,7 +299,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
       a.w_rows = H;
       a.topk = k;
       a.max_tasks = p.max_tasks;
-      e = moe_host::launch_tiled_gemm(a, false, fp8, p.bn2, grid2, s);
+      e = moe_host::launch_tiled_gemm(a, false, fp8, p.bm_t, p.bn2, grid2, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
     {

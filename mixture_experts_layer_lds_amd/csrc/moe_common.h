@@ -154,7 +154,7 @@ struct TiledArgs {
   int max_tasks;
 };
 
-hipError_t launch_tiled_gemm(const TiledArgs& a, bool gateup, bool fp8, int bn, int grid,
+hipError_t launch_tiled_gemm(const TiledArgs& a, bool gateup, bool fp8, int bm, int bn, int grid,
                              hipStream_t s);
 
 // fp32 rows -> e4m3 codes with the row amax held in h_scale (replaced by the scale).

@@ -5,20 +5,23 @@
 // grouped GEMMs.
 //
 // One workgroup of 1024 threads does the whole build in LDS; global memory
-// sees only the id reads and one write per output word (no global
-// atomics).  The order inside an expert's range is the ascending pair
-// index, which makes the result a deterministic function of the ids:
+// sees only the id reads and the output writes (no global atomics).  The
+// order inside an expert's range is the ascending pair index, which makes
+// the result a deterministic function of the ids:
 //
-//  1. histogram of keys (expert id, or E for a dropped pair) with LDS atomics
-//     -- counts are order independent;
-//  2. exclusive scan of the counts -> the start row of every key;
-//  3. rounds of 1024 consecutive pairs: inside a wave, the rank of a pair
-//     among the earlier lanes holding the same key comes from nine ballots
-//     over the key bits and a popcount; per-(wave, key) counts in LDS are
-//     turned into per-wave base rows by one thread per key, in wave order,
-//     so pair p lands at base[wave][key] + rank, after every earlier pair of
-//     its key;
-//  4. per-expert tile counts ceil(c_e / block_m), scanned to task offsets;
+//  A. each of the 16 waves owns one contiguous segment of pairs and walks
+//     it 64 pairs at a time; the rank of a pair among the earlier lanes
+//     holding the same key (expert id, or E for a dropped pair) comes from
+//     nine ballots over the key bits and a popcount, and the wave's own LDS
+//     counter row for that key (read by every lane of the key group, then
+//     advanced by its first lane) turns it into the pair's rank inside the
+//     segment.  No barrier is needed: a wave only touches its own row;
+//  B. one thread per key turns the 16 segment counts into segment bases
+//     (a prefix over waves) and the key total; one wave scans the totals
+//     into the start row of every key;
+//  C. every wave re-walks its segment: row = start[key] + base[wave][key] +
+//     rank, so pair p lands after every earlier pair of its key;
+//  D. per-expert tile counts ceil(c_e / block_m), scanned to task offsets;
 //     one thread per expert writes its tiles.
 #include "moe_common.h"
 
@@ -27,6 +30,7 @@ namespace moe {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kKeys = kMaxExperts + 1;   // expert ids plus the dropped bucket
+constexpr int kBatch = 8;                // 64-pair steps whose loads are issued together
 
 // Exclusive prefix sum of in[0..n) into out[0..n) by one wave (n <= 64*64);
 // in and out may alias.  Returns the total to every lane.
@@ -51,6 +55,18 @@ __device__ int wave_exclusive_scan(const int* in, int* out, int n, int lane) {
   return __shfl(incl, kWave - 1, kWave);
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its global stores (a fenced __syncthreads() would wait
+// out the store latency at every phase).  Global memory is never used to
+// pass data between threads of this kernel: each thread reads back only its
+// own writes.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 __global__ void __launch_bounds__(kRouteThreads)
 route_kernel(const int32_t* __restrict__ ids, int P, int E, int block_m, int max_tasks,
              int32_t* __restrict__ header, int32_t* __restrict__ expert_offsets,
@@ -58,9 +74,7 @@ route_kernel(const int32_t* __restrict__ ids, int P, int E, int block_m, int max
              moe_task_t* __restrict__ tasks) {
   __shared__ int s_count[kKeys];
   __shared__ int s_start[kKeys + 1];
-  __shared__ int s_cursor[kKeys];
   __shared__ int s_wcount[kRouteWaves][kKeys];
-  __shared__ int s_wbase[kRouteWaves][kKeys];
   __shared__ int s_task0[kKeys];
   __shared__ int s_total_tasks;
 
@@ -69,75 +83,105 @@ route_kernel(const int32_t* __restrict__ ids, int P, int E, int block_m, int max
   const int wave = tid >> 6;
   const int nkeys = E + 1;
 
-  for (int i = tid; i < kKeys; i += kRouteThreads) s_count[i] = 0;
   for (int i = tid; i < kRouteWaves * kKeys; i += kRouteThreads) (&s_wcount[0][0])[i] = 0;
-  __syncthreads();
+  lds_barrier();
 
-  // 1. histogram
-  for (int p = tid; p < P; p += kRouteThreads) {
-    const int e = ids[p];
-    const int key = (e >= 0 && e < E) ? e : E;
-    atomicAdd(&s_count[key], 1);
-  }
-  __syncthreads();
+  // segment of this wave: a multiple of 64 pairs
+  const int seg = ((P + kRouteWaves - 1) / kRouteWaves + kWave - 1) / kWave * kWave;
+  const int p0 = min(P, wave * seg), p1 = min(P, p0 + seg);
+  const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int* wrow = s_wcount[wave];
 
-  // 2. start row of every key
-  if (wave == 0) {
-    wave_exclusive_scan(s_count, s_start, nkeys, lane);
+  // A. ranks inside the segment (kept in pair_pos until phase C).  The ids
+  // of kBatch consecutive 64-pair steps are loaded together, so one memory
+  // latency covers kBatch steps.
+  for (int b0 = p0; b0 < p1; b0 += kWave * kBatch) {
+    // unconditional loads of a clamped index: a load under a branch gets its
+    // own wait, which would serialise the batch
+    int raw[kBatch], keys[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) raw[u] = ids[min(b0 + u * kWave + lane, p1 - 1)];
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) {
+      const int p = b0 + u * kWave + lane;
+      const int e = raw[u];
+      keys[u] = p < p1 ? ((e >= 0 && e < E) ? e : E) : -1;   // -1: beyond the segment
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) {
+      const int p = b0 + u * kWave + lane;
+      const int key = keys[u];
+      const bool have = key >= 0;
+      uint64_t same = __ballot(have);
+#pragma unroll
+      for (int bit = 0; bit < 9; bit++) {   // keys < 512
+        const bool set = (key >> bit) & 1;
+        const uint64_t m = __ballot(have && set);
+        same &= set ? m : ~m;
+      }
+      const int below = __popcll(same & lanes_below);
+      int before = 0;
+      if (have) before = wrow[key];
+      __builtin_amdgcn_wave_barrier();      // every lane has read the counter ...
+      if (have && below == 0) wrow[key] = before + __popcll(same);   // ... before its first lane advances it
+      __builtin_amdgcn_wave_barrier();
+      if (have) pair_pos[p] = before + below;
+    }
   }
-  __syncthreads();
+  lds_barrier();
+
+  // B. per-key totals and per-wave segment bases
+  for (int kk = tid; kk < nkeys; kk += kRouteThreads) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kRouteWaves; w++) {
+      const int c = s_wcount[w][kk];
+      s_wcount[w][kk] = run;
+      run += c;
+    }
+    s_count[kk] = run;
+  }
+  lds_barrier();
+  if (wave == 0) wave_exclusive_scan(s_count, s_start, nkeys, lane);
+  lds_barrier();
   for (int i = tid; i < nkeys; i += kRouteThreads) {
-    s_cursor[i] = s_start[i];
     if (i < E) s_task0[i] = (s_count[i] + block_m - 1) / block_m;
     expert_offsets[i] = s_start[i];   // key E: number of valid pairs
   }
-  __syncthreads();
 
-  // 3. stable scatter, 1024 pairs per round
-  const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int base = 0; base < P; base += kRouteThreads) {
-    const int p = base + tid;
-    const bool have = p < P;
-    int key = 0;
-    if (have) {
-      const int e = ids[p];
-      key = (e >= 0 && e < E) ? e : E;
-    }
-    uint64_t same = __ballot(have);
+  // C. scatter (ids and in-segment ranks of kBatch steps loaded together)
+  for (int b0 = p0; b0 < p1; b0 += kWave * kBatch) {
+    int raw[kBatch], keys[kBatch], ranks[kBatch];
 #pragma unroll
-    for (int bit = 0; bit < 9; bit++) {   // keys < 512
-      const bool set = (key >> bit) & 1;
-      const uint64_t m = __ballot(have && set);
-      same &= set ? m : ~m;
+    for (int u = 0; u < kBatch; u++) {
+      const int pc = min(b0 + u * kWave + lane, p1 - 1);
+      raw[u] = ids[pc];
+      ranks[u] = pair_pos[pc];
     }
-    const int rank = __popcll(same & lanes_below);
-    if (have && rank == 0) s_wcount[wave][key] = __popcll(same);
-    __syncthreads();
-    for (int kk = tid; kk < nkeys; kk += kRouteThreads) {
-      int run = s_cursor[kk];
 #pragma unroll
-      for (int w = 0; w < kRouteWaves; w++) {
-        const int c = s_wcount[w][kk];
-        s_wbase[w][kk] = run;
-        s_wcount[w][kk] = 0;
-        run += c;
+    for (int u = 0; u < kBatch; u++) {
+      const int p = b0 + u * kWave + lane;
+      const int e = raw[u];
+      keys[u] = p < p1 ? ((e >= 0 && e < E) ? e : E) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) {
+      const int p = b0 + u * kWave + lane;
+      if (keys[u] >= 0) {
+        const int r = s_start[keys[u]] + wrow[keys[u]] + ranks[u];
+        sorted_pairs[r] = p;
+        pair_pos[p] = r;
       }
-      s_cursor[kk] = run;
-    }
-    __syncthreads();
-    if (have) {
-      const int r = s_wbase[wave][key] + rank;
-      sorted_pairs[r] = p;
-      pair_pos[p] = r;
     }
   }
+  lds_barrier();
 
-  // 4. task map
+  // D. task map
   if (wave == 0) {
     const int total = wave_exclusive_scan(s_task0, s_task0, E, lane);
     if (lane == 0) s_total_tasks = total;
   }
-  __syncthreads();
+  lds_barrier();
   for (int e = tid; e < E; e += kRouteThreads) {
     const int c = s_count[e];
     int t = s_task0[e];

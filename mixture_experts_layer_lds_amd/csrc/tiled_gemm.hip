@@ -269,27 +269,23 @@ static hipError_t launch_tiled_t(const moe_host::TiledArgs& a, int grid, hipStre
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant: 128 x 256 tiles, 8 waves of 64 x 64 (two per
-// SIMD, so one wave's MFMAs cover the other's waits), one workgroup per CU.  Operand chunks go from global memory straight into LDS
-// with global_load_lds_dwordx4 (each wave instruction fills one 1 KiB chunk,
-// lane l writing bytes 16*l..16*l+15), through a ring of three 48 KiB
-// stages.  A stage is issued two K iterations before it is multiplied, so
-// two full compute phases cover the load latency; the ring runs straight
-// across work-item boundaries (the next tile's first stages load while the
-// current tile finishes), which matters for the short-K down GEMM.  Waits
-// are explicit vmcnt counts plus a plain s_barrier (a fenced
-// __syncthreads() would drain the whole ring).  Requires row_bytes % 128
-// == 0, at least two K iterations, and N_out % 128 (gate-up) / % 256 (down).
-constexpr int kDmaBM = 128, kDmaBN = 256, kDmaStages = 3;
-constexpr int kDmaWaves = 8, kDmaThreads = kDmaWaves * 64;   // 2 (M) x 4 (N) waves of 64 x 64
-constexpr int kDmaAChunks = kDmaBM / 16 * kIterSteps;        // 16
-constexpr int kDmaBChunks = kDmaBN / 16 * kIterSteps;        // 32
-constexpr int kDmaStageBytes = (kDmaAChunks + kDmaBChunks) * 1024;   // 48 KiB
-constexpr int kDmaAPerWave = kDmaAChunks / kDmaWaves;                 // 2
-constexpr int kDmaBPerWave = kDmaBChunks / kDmaWaves;                 // 4
-constexpr int kDmaPerWave = kDmaAPerWave + kDmaBPerWave;              // 6 loads / wave / stage
-constexpr int kDmaLdsBytes = kDmaStages * kDmaStageBytes;             // 144 KiB
-
+// Direct-to-LDS variant: BM x BN tiles computed by 8 waves (two per SIMD, so
+// one wave's MFMAs cover the other's waits), one workgroup per CU.
+// Operand chunks go from global memory straight into LDS with
+// global_load_lds_dwordx4 (each wave instruction fills one 1 KiB chunk,
+// lane l writing bytes 16*l..16*l+15), through a ring of NST stages of KS
+// 64-byte K steps each.  Stage f+NST-1 is issued while stage f is being
+// multiplied, so NST-1 compute phases cover the load latency; the ring runs
+// straight across work-item boundaries (the next tile's first stages load
+// while the current tile finishes), which matters for the short-K down
+// GEMM.  Waits are explicit vmcnt counts plus a plain s_barrier (a fenced
+// __syncthreads() would drain the whole ring).
+//
+// Shapes used: 128 x 256, two steps per stage, three stages (48 KiB
+// stages), and 256 x 256, one step per stage, four stages (32 KiB stages;
+// two thirds of the operand bytes per flop of the former).  Requires
+// row_bytes % (64*KS) == 0, at least KS*(NST-1) K steps and N_out a multiple
+// of the tile's output columns.
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void dma16(const void* src, char* lds_dst) {
@@ -305,11 +301,28 @@ __device__ __forceinline__ void barrier_nofence() {
   __asm__ volatile("" ::: "memory");
 }
 
-// wait until at most N of this wave's vector-memory loads are outstanding
+// wait until at most N of this wave's vector-memory operations are outstanding
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
+
+template <int BM_, int BN_, int KS_, int NST_, int WM_, int WN_>
+struct DmaShape {
+  static constexpr int BM = BM_, BN = BN_, KS = KS_, NST = NST_, WM = WM_, WN = WN_;
+  static constexpr int kWaves = WM * WN, kThreads = kWaves * 64;
+  static constexpr int MB = BM / WM / 16, NB = BN / WN / 16;   // 16x16 blocks per wave
+  static constexpr int kAChunks = BM / 16 * KS, kBChunks = BN / 16 * KS;
+  static constexpr int kAPerWave = kAChunks / kWaves, kBPerWave = kBChunks / kWaves;
+  static constexpr int kPerWave = kAPerWave + kBPerWave;   // DMA ops per wave per stage
+  static constexpr int kStageBytes = (kAChunks + kBChunks) * 1024;
+  static constexpr int kLdsBytes = NST * kStageBytes;
+  static constexpr int kAhead = NST - 1;                      // stages in flight ahead
+  static_assert(kAChunks % kWaves == 0 && kBChunks % kWaves == 0, "chunk split");
+  static_assert(kWaves % KS == 0, "a wave's chunks share one K step");
+};
+using DmaWide = DmaShape<128, 256, 2, 3, 2, 4>;   // 48 KiB stages x 3
+using DmaBig = DmaShape<256, 256, 1, 4, 4, 2>;    // 32 KiB stages x 4
 
 // Scalar (constant-cache) load of a wave-uniform 16-byte task record.  Its
 // wait is on lgkmcnt, so it does not drain the in-flight direct-to-LDS loads
@@ -326,28 +339,29 @@ __device__ __forceinline__ moe_task_t load_task_scalar(const moe_task_t* p) {
   return t;
 }
 
+template <class Sh>
 struct DmaItem {
   int expert, row_begin, rows, nt;
-  const char* a[kDmaAPerWave];   // this lane's A sources (step and lane offsets applied)
-  const char* b;                 // this lane's packed-B source for weight block 0
+  const char* a[Sh::kAPerWave];   // this lane's A sources (step and lane offsets applied)
+  const char* b;                  // this lane's packed-B source for weight block 0
 };
 
-template <bool GATEUP, bool FP8>
-__device__ __forceinline__ DmaItem dma_item(const moe_host::TiledArgs& g, int item, int n_tiles,
-                                            size_t row_bytes, int nsteps, int w_blocks,
-                                            int wave, int lane) {
-  DmaItem it;
+template <class Sh, bool GATEUP>
+__device__ __forceinline__ DmaItem<Sh> dma_item(const moe_host::TiledArgs& g, int item, int n_tiles,
+                                                size_t row_bytes, int nsteps, int w_blocks,
+                                                int wave, int lane) {
+  DmaItem<Sh> it;
   const int ti = item / n_tiles;
   it.nt = item - ti * n_tiles;
   const moe_task_t task = load_task_scalar(g.tasks + ti);
   it.expert = task.expert;
   it.row_begin = task.row_begin;
   it.rows = task.rows;
-  // wave w loads chunks w + 8*i: row block (w >> 1) + 4*i, 64-byte step w & 1
-  const int st = wave & 1, rbo = wave >> 1;
+  // wave w loads chunks w + kWaves*i: 16-row block (w + kWaves*i) / KS, step w % KS
+  const int st = wave % Sh::KS;
 #pragma unroll
-  for (int i = 0; i < kDmaAPerWave; i++) {
-    int rr = (rbo + 4 * i) * 16 + (lane & 15);
+  for (int i = 0; i < Sh::kAPerWave; i++) {
+    int rr = ((wave + Sh::kWaves * i) / Sh::KS) * 16 + (lane & 15);
     if (rr >= task.rows) rr = 0;    // a valid row; its products are never stored
     const int arow = GATEUP ? g.sorted_pairs[task.row_begin + rr] / g.topk : task.row_begin + rr;
     it.a[i] = static_cast<const char*>(g.a) + (size_t)arow * row_bytes + st * 64 + 16 * (lane >> 4);
@@ -356,24 +370,24 @@ __device__ __forceinline__ DmaItem dma_item(const moe_host::TiledArgs& g, int it
   return it;
 }
 
-template <bool GATEUP, bool FP8>
-__global__ void __launch_bounds__(kDmaThreads, 1)
+template <class Sh, bool GATEUP, bool FP8>
+__global__ void __launch_bounds__(Sh::kThreads, 1)
 tiled_dma_kernel(moe_host::TiledArgs g) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
+  constexpr int MB = Sh::MB, NB = Sh::NB, KS = Sh::KS, NST = Sh::NST, AHEAD = Sh::kAhead;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;   // 2 x 4 waves
-  const int st_w = wave & 1, rbo = wave >> 1;
-  constexpr int MB = 4, NB = 4;              // 16x16 blocks per wave (64 x 64)
+  const int wm = wave / Sh::WN, wn = wave % Sh::WN;
+  const int st_w = wave % KS;
 
   const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
-  const int out_cols = GATEUP ? kDmaBN / 2 : kDmaBN;
+  const int out_cols = GATEUP ? Sh::BN / 2 : Sh::BN;
   const int n_tiles = g.N_out / out_cols;
   const int total = num_tasks * n_tiles;
   const size_t row_bytes = (size_t)g.K * (FP8 ? 1 : 2);
   const int nsteps = (int)(row_bytes / 64);
-  const int nk = nsteps / kIterSteps;
+  const int nk = nsteps / KS;
   const int w_blocks = g.w_rows / 16;
 
   const int G = gridDim.x;
@@ -387,34 +401,43 @@ tiled_dma_kernel(moe_host::TiledArgs g) {
   // weight 16-row block of the tile's j-th B block
   auto wrb = [&](int nt, int j) {
     if (GATEUP) {
-      constexpr int half = kDmaBN / 32;   // 8 gate blocks, then 8 up blocks
+      constexpr int half = Sh::BN / 32;   // gate blocks, then the matching up blocks
       return j < half ? nt * half + j : g.N_out / 16 + nt * half + (j - half);
     }
-    return nt * (kDmaBN / 16) + j;
+    return nt * (Sh::BN / 16) + j;
   };
 
   // Sources of the current and the next item, kept in registers.
-  DmaItem cur = dma_item<GATEUP, FP8>(g, vid, n_tiles, row_bytes, nsteps, w_blocks, wave, lane);
-  DmaItem nxt = cur;
+  DmaItem<Sh> cur = dma_item<Sh, GATEUP>(g, vid, n_tiles, row_bytes, nsteps, w_blocks, wave, lane);
+  DmaItem<Sh> nxt = cur;
   if (n_items > 1)
-    nxt = dma_item<GATEUP, FP8>(g, vid + G, n_tiles, row_bytes, nsteps, w_blocks, wave, lane);
+    nxt = dma_item<Sh, GATEUP>(g, vid + G, n_tiles, row_bytes, nsteps, w_blocks, wave, lane);
 
-  auto issue = [&](const DmaItem& it, int kt, int slot) {
-    char* sb = lds + slot * kDmaStageBytes;
+  auto issue = [&](const DmaItem<Sh>& it, int kt, int slot_) {
+    char* sb = lds + slot_ * Sh::kStageBytes;
 #pragma unroll
-    for (int i = 0; i < kDmaAPerWave; i++)
-      dma16(it.a[i] + (size_t)kt * 128, sb + ((rbo + 4 * i) * kIterSteps + st_w) * 1024);
+    for (int i = 0; i < Sh::kAPerWave; i++)
+      dma16(it.a[i] + (size_t)kt * KS * 64, sb + (wave + Sh::kWaves * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < kDmaBPerWave; i++) {
-      const int j = rbo + 4 * i;
-      dma16(it.b + ((size_t)wrb(it.nt, j) * nsteps + (size_t)kt * kIterSteps) * 1024,
-            sb + (kDmaAChunks + j * kIterSteps + st_w) * 1024);
+    for (int i = 0; i < Sh::kBPerWave; i++) {
+      const int c = wave + Sh::kWaves * i;
+      dma16(it.b + ((size_t)wrb(it.nt, c / KS) * nsteps + (size_t)kt * KS) * 1024,
+            sb + (Sh::kAChunks + c) * 1024);
     }
   };
+  // flat stage index fi -> (item relative to the current one, K iteration)
+  auto issue_flat = [&](int fi, int ii) {
+    const int item_rel = fi / nk - ii;
+    const int kt = fi % nk;
+    if (item_rel == 0) issue(cur, kt, fi % NST);
+    else issue(nxt, kt, fi % NST);
+  };
 
-  issue(cur, 0, 0);
-  issue(cur, 1, 1);   // nk >= 2
-  int f = 0;          // flat stage index over all items of this workgroup
+#pragma unroll
+  for (int d = 0; d < AHEAD; d++)
+    if (d < F) issue_flat(d, 0);   // nk >= AHEAD: all in item 0
+
+  int f = 0;   // flat stage index over all items of this workgroup
   for (int ii = 0; ii < n_items; ii++) {
     f32x4 acc[MB][NB];
 #pragma unroll
@@ -423,43 +446,47 @@ tiled_dma_kernel(moe_host::TiledArgs g) {
       for (int q = 0; q < NB; q++) acc[m][q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     for (int kt = 0; kt < nk; kt++, f++) {
-      // stage f landed (only stage f+1 may still be in flight), in every wave
-      if (f + 1 < F) wait_vm<kDmaPerWave>(); else wait_vm<0>();
+      // stage f landed (only the stages issued after it may still be in
+      // flight), in every wave
+      const int later = min(AHEAD - 1, F - 1 - f);
+      if (later >= 3) wait_vm<3 * Sh::kPerWave>();
+      else if (later == 2) wait_vm<2 * Sh::kPerWave>();
+      else if (later == 1) wait_vm<Sh::kPerWave>();
+      else wait_vm<0>();
       barrier_nofence();
-      const char* base = lds + (f % kDmaStages) * kDmaStageBytes;
+      const char* base = lds + (f % NST) * Sh::kStageBytes;
 #pragma unroll
-      for (int st = 0; st < kIterSteps; st++) {
+      for (int st = 0; st < KS; st++) {
         u32x4 fa[MB], fb[NB];
 #pragma unroll
         for (int m = 0; m < MB; m++)
-          fa[m] = *reinterpret_cast<const u32x4*>(base + ((wm * MB + m) * kIterSteps + st) * 1024 + 16 * lane);
+          fa[m] = *reinterpret_cast<const u32x4*>(base + ((wm * MB + m) * KS + st) * 1024 + 16 * lane);
 #pragma unroll
         for (int q = 0; q < NB; q++) {
           int j;
-          if (GATEUP) j = q < NB / 2 ? wn * (NB / 2) + q : kDmaBN / 32 + wn * (NB / 2) + (q - NB / 2);
+          if (GATEUP) j = q < NB / 2 ? wn * (NB / 2) + q : Sh::BN / 32 + wn * (NB / 2) + (q - NB / 2);
           else j = wn * NB + q;
-          fb[q] = *reinterpret_cast<const u32x4*>(base + (kDmaAChunks + j * kIterSteps + st) * 1024 + 16 * lane);
+          fb[q] = *reinterpret_cast<const u32x4*>(base + (Sh::kAChunks + j * KS + st) * 1024 + 16 * lane);
         }
 #pragma unroll
         for (int m = 0; m < MB; m++)
 #pragma unroll
           for (int q = 0; q < NB; q++) mfma_step_t<FP8>(acc[m][q], fa[m], fb[q]);
       }
-      // Stage f+2 goes into the slot of stage f-1, which every wave finished
-      // reading before the barrier above.  Issued after this stage's MFMAs
-      // (which run on asynchronously) so the two overlap.
-      const int slot2 = (f + 2) % kDmaStages;
-      if (kt + 2 < nk) issue(cur, kt + 2, slot2);
-      else if (ii + 1 < n_items) issue(nxt, kt + 2 - nk, slot2);
+      // Stage f+AHEAD goes into the slot of stage f-1, which every wave
+      // finished reading before the barrier above.  Issued after this
+      // stage's MFMAs (which run on asynchronously) so the two overlap.
+      if (f + AHEAD < F) issue_flat(f + AHEAD, ii);
     }
 
     // ---- epilogue of this item
     const int lrow = lane & 15, lgrp = lane >> 4;
+    constexpr int WROWS = Sh::BM / Sh::WM;
 #pragma unroll
     for (int m = 0; m < MB; m++) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const int rr = wm * 64 + m * 16 + 4 * lgrp + i;
+        const int rr = wm * WROWS + m * 16 + 4 * lgrp + i;
         const bool ok = rr < cur.rows;
         const int r = cur.row_begin + (ok ? rr : 0);
         if constexpr (GATEUP) {
@@ -468,7 +495,7 @@ tiled_dma_kernel(moe_host::TiledArgs g) {
           float rmax = 0.0f;
 #pragma unroll
           for (int q = 0; q < NB / 2; q++) {
-            const int col = cur.nt * (kDmaBN / 2) + wn * (NB / 2) * 16 + q * 16 + lrow;   // 32 h columns per wave
+            const int col = cur.nt * (Sh::BN / 2) + wn * (NB / 2) * 16 + q * 16 + lrow;
             float gv = acc[m][q][i], uv = acc[m][q + NB / 2][i];
             if constexpr (FP8) {
               gv = (gv * sx) * g.b_scale[(size_t)cur.expert * g.w_rows + col];
@@ -491,7 +518,7 @@ tiled_dma_kernel(moe_host::TiledArgs g) {
           if constexpr (FP8) sa = g.a_scale[r];
 #pragma unroll
           for (int q = 0; q < NB; q++) {
-            const int col = cur.nt * kDmaBN + wn * (NB * 16) + q * 16 + lrow;
+            const int col = cur.nt * Sh::BN + wn * (NB * 16) + q * 16 + lrow;
             float v = acc[m][q][i];
             if constexpr (FP8) v = (v * sa) * g.b_scale[(size_t)cur.expert * g.w_rows + col];
             if (ok) static_cast<uint16_t*>(g.c)[(size_t)r * g.N_out + col] = f32_to_bf16_bits(v);
@@ -501,24 +528,30 @@ tiled_dma_kernel(moe_host::TiledArgs g) {
     }
     cur = nxt;
     if (ii + 2 < n_items)
-      nxt = dma_item<GATEUP, FP8>(g, vid + (ii + 2) * G, n_tiles, row_bytes, nsteps, w_blocks,
-                                  wave, lane);
+      nxt = dma_item<Sh, GATEUP>(g, vid + (ii + 2) * G, n_tiles, row_bytes, nsteps, w_blocks, wave, lane);
   }
 }
 
-template <bool GATEUP, bool FP8>
+template <class Sh, bool GATEUP, bool FP8>
 static hipError_t launch_dma_t(const moe_host::TiledArgs& a, int grid, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&tiled_dma_kernel<GATEUP, FP8>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, kDmaLdsBytes);
+        reinterpret_cast<const void*>(&tiled_dma_kernel<Sh, GATEUP, FP8>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((tiled_dma_kernel<GATEUP, FP8>), dim3(grid), dim3(kDmaThreads),
-                     kDmaLdsBytes, s, a);
+  hipLaunchKernelGGL((tiled_dma_kernel<Sh, GATEUP, FP8>), dim3(grid), dim3(Sh::kThreads),
+                     Sh::kLdsBytes, s, a);
   return hipGetLastError();
+}
+
+template <class Sh>
+static hipError_t launch_dma_shape(const moe_host::TiledArgs& a, bool gateup, bool fp8, int grid,
+                                   hipStream_t s) {
+  if (gateup) return fp8 ? launch_dma_t<Sh, true, true>(a, grid, s) : launch_dma_t<Sh, true, false>(a, grid, s);
+  return fp8 ? launch_dma_t<Sh, false, true>(a, grid, s) : launch_dma_t<Sh, false, false>(a, grid, s);
 }
 
 // requantise fp32 rows h32[r][0..I) of the valid sorted rows with the
@@ -546,14 +579,11 @@ requant_rows_kernel(const float* __restrict__ h32, int I, const int32_t* __restr
 
 namespace moe_host {
 
-hipError_t launch_tiled_gemm(const TiledArgs& a, bool gateup, bool fp8, int bn, int grid,
+hipError_t launch_tiled_gemm(const TiledArgs& a, bool gateup, bool fp8, int bm, int bn, int grid,
                              hipStream_t s) {
-  if (bn == 256) {   // direct-to-LDS ring, one workgroup per CU
-    if (gateup) return fp8 ? moe::launch_dma_t<true, true>(a, grid, s)
-                           : moe::launch_dma_t<true, false>(a, grid, s);
-    return fp8 ? moe::launch_dma_t<false, true>(a, grid, s)
-               : moe::launch_dma_t<false, false>(a, grid, s);
-  }
+  if (bm == 256 && bn == 256) return moe::launch_dma_shape<moe::DmaBig>(a, gateup, fp8, grid, s);
+  if (bm != 128) return hipErrorInvalidValue;
+  if (bn == 256) return moe::launch_dma_shape<moe::DmaWide>(a, gateup, fp8, grid, s);
   if (bn == 128) {
     if (gateup) return fp8 ? moe::launch_tiled_t<128, 128, true, true>(a, grid, s)
                            : moe::launch_tiled_t<128, 128, true, false>(a, grid, s);

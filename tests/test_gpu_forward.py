@@ -40,6 +40,7 @@ SMALL = [
     (8, 256, 192, 2, 700, 0.05),
     (8, 192, 320, 2, 700, 0.0),       # H % 128 != 0; fp8 rows of 192 / 320 bytes
     (16, 512, 256, 4, 1500, 0.02),
+    (32, 256, 128, 8, 500, 0.0),      # 256-row tiles about half full
 ]
 
 
