@@ -73,7 +73,7 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   // experts hold enough rows to fill them; else 128-row tiles: the 128 x 256
   // direct-to-LDS ring (128-byte K steps) where the shape allows it, or the
   // register-staged 128 x 128 / 128 x 64 tiles.
-  const bool big = avg >= 96 && I % 128 == 0 && H % 256 == 0 && rb1 >= 192 && rb2 >= 192;
+  const bool big = avg >= 192 && I % 128 == 0 && H % 256 == 0 && rb1 >= 192 && rb2 >= 192;
   p.bm_t = big ? 256 : 128;
   const bool dma1 = rb1 % 128 == 0 && rb1 >= 256 && I % 128 == 0;
   const bool dma2 = rb2 % 128 == 0 && rb2 >= 256 && H % 256 == 0;

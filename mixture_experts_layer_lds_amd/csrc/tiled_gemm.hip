@@ -322,7 +322,7 @@ struct DmaShape {
   static_assert(kWaves % KS == 0, "a wave's chunks share one K step");
 };
 using DmaWide = DmaShape<128, 256, 2, 3, 2, 4>;   // 48 KiB stages x 3
-using DmaBig = DmaShape<256, 256, 1, 4, 4, 2>;    // 32 KiB stages x 4
+using DmaBig = DmaShape<256, 256, 1, 5, 4, 2>;    // 32 KiB stages x 5 (all of LDS)
 
 // Scalar (constant-cache) load of a wave-uniform 16-byte task record.  Its
 // wait is on lgkmcnt, so it does not drain the in-flight direct-to-LDS loads
@@ -449,7 +449,8 @@ tiled_dma_kernel(moe_host::TiledArgs g) {
       // stage f landed (only the stages issued after it may still be in
       // flight), in every wave
       const int later = min(AHEAD - 1, F - 1 - f);
-      if (later >= 3) wait_vm<3 * Sh::kPerWave>();
+      if (later >= 4) wait_vm<4 * Sh::kPerWave>();
+      else if (later == 3) wait_vm<3 * Sh::kPerWave>();
       else if (later == 2) wait_vm<2 * Sh::kPerWave>();
       else if (later == 1) wait_vm<Sh::kPerWave>();
       else wait_vm<0>();
