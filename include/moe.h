@@ -104,6 +104,8 @@ typedef struct {
                                 expert, then dropped pairs ascending in p */
     size_t pair_pos;         /* int32 [P]: sorted row of pair p (inverse) */
     size_t tasks;            /* moe_task_t [max_tasks]: expert-major row tiles */
+    size_t scratch;          /* work area of the routing build (large P only;
+                                contents unspecified afterwards) */
     size_t total_bytes;      /* minimum size of the routing buffer */
     int32_t block_m;         /* tile height chosen for these sizes and dtype */
     int32_t max_tasks;       /* P / block_m + min(E, P) */

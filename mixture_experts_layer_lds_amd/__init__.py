@@ -44,7 +44,8 @@ class MoeError(RuntimeError):
 class RoutingLayout(ctypes.Structure):
     _fields_ = [("header", ctypes.c_size_t), ("expert_offsets", ctypes.c_size_t),
                 ("sorted_pairs", ctypes.c_size_t), ("pair_pos", ctypes.c_size_t),
-                ("tasks", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t),
+                ("tasks", ctypes.c_size_t), ("scratch", ctypes.c_size_t),
+                ("total_bytes", ctypes.c_size_t),
                 ("block_m", ctypes.c_int32), ("max_tasks", ctypes.c_int32)]
 
 

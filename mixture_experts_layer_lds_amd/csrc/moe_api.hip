@@ -108,6 +108,8 @@ void routing_layout(int T, int k, int E, const Plan& p, moe_routing_layout_t* L)
   off = align_up(off + 4 * P, 16);
   L->tasks = off;
   off = align_up(off + sizeof(moe_task_t) * (size_t)p.max_tasks, 16);
+  L->scratch = off;
+  off = align_up(off + moe_host::route_scratch_bytes((int)P), 16);
   L->total_bytes = off;
   L->block_m = p.block_m;
   L->max_tasks = p.max_tasks;

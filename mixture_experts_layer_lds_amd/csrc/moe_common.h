@@ -86,6 +86,8 @@ namespace moe_host {
 
 hipError_t launch_route(const int32_t* ids, int P, int E, int block_m, int max_tasks,
                         void* routing, const moe_routing_layout_t& L, hipStream_t s);
+// Bytes of the routing work area (per-segment key counts) for P pairs.
+size_t route_scratch_bytes(int P);
 
 // Per-token e4m3 quantisation of bf16 rows x[T][H]; when zero_rows is not
 // null the same launch also clears zero_rows[0 .. T*zk) (row amax slots).

@@ -206,6 +206,187 @@ route_kernel(const int32_t* __restrict__ ids, int P, int E, int block_m, int max
   }
 }
 
+// ---------------------------------------------------------------------------
+// Many pairs (P > kOneGroupPairs): the same stable counting sort spread over
+// many workgroups in three launches, so that the scattered writes of the
+// route index are not funnelled through one compute unit.
+//   count:   one 4-wave workgroup per segment of kSegPairs consecutive pairs:
+//            in-wave ranks as in phase A above, then per-wave bases inside the
+//            segment; writes each pair's rank inside its segment (into
+//            pair_pos) and the segment's per-key counts;
+//   scan:    one workgroup: per key, a prefix over segments (segment bases)
+//            and the key totals; expert offsets, task map and header as in
+//            phases B and D above;
+//   scatter: one workgroup per segment: row = base[segment][key] + rank.
+constexpr int kOneGroupPairs = 4096;
+constexpr int kSegThreads = 256;
+constexpr int kSegWaves = kSegThreads / kWave;                 // 4
+constexpr int kSegPairs = kSegWaves * kWave * kBatch;          // 2048: one batch per wave
+constexpr int kMaxSegs = kMaxPairs / kSegPairs;                // 32
+
+__global__ void __launch_bounds__(kSegThreads)
+route_count_kernel(const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ seg_counts,
+                   int32_t* __restrict__ pair_pos) {
+  __shared__ int s_w[kSegWaves][kKeys];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int nkeys = E + 1;
+  for (int i = tid; i < kSegWaves * kKeys; i += kSegThreads) (&s_w[0][0])[i] = 0;
+  lds_barrier();
+  const int p0 = blockIdx.x * kSegPairs + wave * kWave * kBatch;
+  const int pend = min(P, (int)(blockIdx.x + 1) * kSegPairs);
+  const int p1 = min(pend, p0 + kWave * kBatch);
+  const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int* wrow = s_w[wave];
+  int keys[kBatch], ranks[kBatch];
+  if (p0 < p1) {
+    int raw[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) raw[u] = ids[min(p0 + u * kWave + lane, p1 - 1)];
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) {
+      const int p = p0 + u * kWave + lane;
+      const int e = raw[u];
+      keys[u] = p < p1 ? ((e >= 0 && e < E) ? e : E) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) {
+      const int key = keys[u];
+      const bool have = key >= 0;
+      uint64_t same = __ballot(have);
+#pragma unroll
+      for (int bit = 0; bit < 9; bit++) {
+        const bool set = (key >> bit) & 1;
+        const uint64_t m = __ballot(have && set);
+        same &= set ? m : ~m;
+      }
+      const int below = __popcll(same & lanes_below);
+      int before = 0;
+      if (have) before = wrow[key];
+      __builtin_amdgcn_wave_barrier();
+      if (have && below == 0) wrow[key] = before + __popcll(same);
+      __builtin_amdgcn_wave_barrier();
+      ranks[u] = before + below;
+    }
+  }
+  lds_barrier();
+  // per-wave bases inside the segment, segment counts
+  for (int kk = tid; kk < nkeys; kk += kSegThreads) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kSegWaves; w++) {
+      const int c = s_w[w][kk];
+      s_w[w][kk] = run;
+      run += c;
+    }
+    seg_counts[blockIdx.x * kKeys + kk] = run;
+  }
+  lds_barrier();
+  if (p0 < p1) {
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) {
+      const int p = p0 + u * kWave + lane;
+      if (keys[u] >= 0) pair_pos[p] = wrow[keys[u]] + ranks[u];
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kRouteThreads)
+route_scan_kernel(int P, int E, int block_m, int max_tasks, int32_t* __restrict__ seg_counts,
+                  int32_t* __restrict__ header, int32_t* __restrict__ expert_offsets,
+                  moe_task_t* __restrict__ tasks) {
+  __shared__ int s_count[kKeys];
+  __shared__ int s_start[kKeys + 1];
+  __shared__ int s_task0[kKeys];
+  __shared__ int s_total_tasks;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int nkeys = E + 1;
+  const int nseg = (P + kSegPairs - 1) / kSegPairs;
+  int bases[kMaxSegs];
+  if (tid < nkeys) {
+    int c[kMaxSegs];
+#pragma unroll
+    for (int sgi = 0; sgi < kMaxSegs; sgi++) c[sgi] = seg_counts[min(sgi, nseg - 1) * kKeys + tid];
+    int run = 0;
+#pragma unroll
+    for (int sgi = 0; sgi < kMaxSegs; sgi++) {
+      bases[sgi] = run;
+      if (sgi < nseg) run += c[sgi];
+    }
+    s_count[tid] = run;
+  }
+  lds_barrier();
+  if (wave == 0) wave_exclusive_scan(s_count, s_start, nkeys, lane);
+  lds_barrier();
+  if (tid < nkeys) {
+    const int st = s_start[tid];
+#pragma unroll
+    for (int sgi = 0; sgi < kMaxSegs; sgi++)
+      if (sgi < nseg) seg_counts[sgi * kKeys + tid] = st + bases[sgi];
+    if (tid < E) s_task0[tid] = (s_count[tid] + block_m - 1) / block_m;
+    expert_offsets[tid] = st;
+  }
+  lds_barrier();
+  if (wave == 0) {
+    const int total = wave_exclusive_scan(s_task0, s_task0, E, lane);
+    if (lane == 0) s_total_tasks = total;
+  }
+  lds_barrier();
+  for (int e = tid; e < E; e += kRouteThreads) {
+    const int c = s_count[e];
+    int t = s_task0[e];
+    for (int m0 = 0; m0 < c && t < max_tasks; m0 += block_m, t++) {
+      moe_task_t task;
+      task.expert = e;
+      task.row_begin = s_start[e] + m0;
+      task.rows = min(block_m, c - m0);
+      task.reserved = 0;
+      tasks[t] = task;
+    }
+  }
+  if (tid < 16) {
+    int v = 0;
+    if (tid == kHdrNumTasks) v = min(s_total_tasks, max_tasks);
+    else if (tid == kHdrNumDropped) v = P - s_start[E];
+    else if (tid == kHdrBlockM) v = block_m;
+    else if (tid == kHdrNumPairs) v = P;
+    else if (tid == kHdrNumExperts) v = E;
+    else if (tid == kHdrMaxTasks) v = max_tasks;
+    header[tid] = v;
+  }
+}
+
+__global__ void __launch_bounds__(kSegThreads)
+route_scatter_kernel(const int32_t* __restrict__ ids, int P, int E,
+                     const int32_t* __restrict__ seg_base, int32_t* __restrict__ sorted_pairs,
+                     int32_t* __restrict__ pair_pos) {
+  const int tid = threadIdx.x;
+  const int p0 = blockIdx.x * kSegPairs;
+  const int p1 = min(P, p0 + kSegPairs);
+  int raw[kBatch], rk[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; u++) {
+    const int pc = min(p0 + u * kSegThreads + tid, p1 - 1);
+    raw[u] = ids[pc];
+    rk[u] = pair_pos[pc];
+  }
+  int keys[kBatch], base[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; u++) {
+    const int e = raw[u];
+    keys[u] = (e >= 0 && e < E) ? e : E;
+    base[u] = seg_base[blockIdx.x * kKeys + keys[u]];
+  }
+#pragma unroll
+  for (int u = 0; u < kBatch; u++) {
+    const int p = p0 + u * kSegThreads + tid;
+    if (p < p1) {
+      const int r = base[u] + rk[u];
+      sorted_pairs[r] = p;
+      pair_pos[p] = r;
+    }
+  }
+}
+
 }  // namespace moe
 
 namespace moe_host {
@@ -213,13 +394,34 @@ namespace moe_host {
 hipError_t launch_route(const int32_t* ids, int P, int E, int block_m, int max_tasks,
                         void* routing, const moe_routing_layout_t& L, hipStream_t s) {
   char* base = static_cast<char*>(routing);
-  hipLaunchKernelGGL(moe::route_kernel, dim3(1), dim3(moe::kRouteThreads), 0, s, ids, P, E,
-                     block_m, max_tasks, reinterpret_cast<int32_t*>(base + L.header),
-                     reinterpret_cast<int32_t*>(base + L.expert_offsets),
-                     reinterpret_cast<int32_t*>(base + L.sorted_pairs),
-                     reinterpret_cast<int32_t*>(base + L.pair_pos),
-                     reinterpret_cast<moe_task_t*>(base + L.tasks));
+  int32_t* header = reinterpret_cast<int32_t*>(base + L.header);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.expert_offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted_pairs);
+  int32_t* pos = reinterpret_cast<int32_t*>(base + L.pair_pos);
+  moe_task_t* tasks = reinterpret_cast<moe_task_t*>(base + L.tasks);
+  if (P <= moe::kOneGroupPairs) {
+    hipLaunchKernelGGL(moe::route_kernel, dim3(1), dim3(moe::kRouteThreads), 0, s, ids, P, E,
+                       block_m, max_tasks, header, offsets, sorted, pos, tasks);
+    return hipGetLastError();
+  }
+  int32_t* seg = reinterpret_cast<int32_t*>(base + L.scratch);
+  const int nseg = (P + moe::kSegPairs - 1) / moe::kSegPairs;
+  hipLaunchKernelGGL(moe::route_count_kernel, dim3(nseg), dim3(moe::kSegThreads), 0, s, ids, P, E,
+                     seg, pos);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(moe::route_scan_kernel, dim3(1), dim3(moe::kRouteThreads), 0, s, P, E, block_m,
+                     max_tasks, seg, header, offsets, tasks);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(moe::route_scatter_kernel, dim3(nseg), dim3(moe::kSegThreads), 0, s, ids, P, E,
+                     seg, sorted, pos);
   return hipGetLastError();
+}
+
+size_t route_scratch_bytes(int P) {
+  return P <= moe::kOneGroupPairs ? 0
+                                  : (size_t)((P + moe::kSegPairs - 1) / moe::kSegPairs) * moe::kKeys * 4;
 }
 
 }  // namespace moe_host
