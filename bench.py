@@ -208,6 +208,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--once", action="store_true",
                     help="one untimed step only (for counter collection under a profiler)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (3 times); under rocprofv3 "
+                         "--pmc it gives the FETCH_SIZE/WRITE_SIZE a copy of known size reads")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -222,6 +225,14 @@ def main():
     from moe_inputs import WORKLOADS, make_weights
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 1 GiB device copies done")
+        return
     wl = WORKLOADS[args.workload]
     dtype = "fp8" if wl.dtype == "fp8" else "bf16"
     T = args.tokens
@@ -270,7 +281,7 @@ def main():
                 "achieved": round(dom_flops / (dom_us * 1e-6) / 1e12, 1),
                 "peak": MFMA_PEAK_TFLOPS[dtype], "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = counted_traffic(dom, wl.name, T)
     roof["algorithmic_bytes"] = dom_bytes
     roof["avg_launch_us"] = dom_us
 
@@ -330,6 +341,30 @@ def main():
         "sweep": sweep,
     }
     print(json.dumps(rec), flush=True)
+
+
+def counted_traffic(stage, workload, T):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary (copy-calibrated), or None when no summary
+    covers this kernel and workload or the kernel source changed since."""
+    import glob
+    import hashlib
+    import re
+    for path in glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md")):
+        m = re.search(r"```json\s*(\{.*?\})\s*```", open(path).read(), re.S)
+        if not m:
+            continue
+        rec = json.loads(m.group(1))
+        if rec.get("kernel") != f"grouped_gemm ({stage})" or rec.get("workload") != workload \
+                or rec.get("T") != T:
+            continue
+        src = os.path.join(ROOT, rec["source"])
+        if not os.path.exists(src):
+            continue
+        if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != rec["source_sha256_16"]:
+            return None
+        return rec["traffic_bytes"]
+    return None
 
 
 def H_I(wl, stage):
