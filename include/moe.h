@@ -112,27 +112,33 @@ typedef struct {
 } moe_routing_layout_t;
 
 /* Byte offsets of the parts of a forward workspace (all 256-byte aligned);
- * an offset of (size_t)-1 marks a part these sizes do not use.  Two tilings
- * exist, chosen by a fixed function of the sizes (large_tiles):
- *  - register streaming (few rows per expert, e.g. decode): the GEMMs may
- *    split their reduction into split_k1 / split_k2 slices whose fp32 partial
- *    sums the next kernel adds in ascending slice order;
- *  - 128-row LDS tiles (many rows per expert): no split; SiLU(gate)*up is
- *    formed in the gate-up GEMM's epilogue and the down rows are bf16. */
+ * an offset of (size_t)-1 marks a part these sizes do not use.  Three tilings
+ * exist, chosen by a fixed function of the sizes and dtype (`tiling`):
+ *  0 register streaming (few rows per expert, e.g. decode) and
+ *  2 strips (token rows staged in LDS, weights streamed to registers; a few
+ *    dozen to ~80 rows per expert): the GEMMs may split their reduction into
+ *    split_k1 / split_k2 slices whose fp32 partial sums the next kernel adds
+ *    in ascending slice order; strips with split_k2 == 1 write bf16 down rows;
+ *  1 LDS tiles of both operands (many rows per expert): no split;
+ *    SiLU(gate)*up is formed in the gate-up GEMM's epilogue and the down rows
+ *    are bf16. */
 typedef struct {
     size_t xq;          /* fp8: uint8 [T][H]   per-token e4m3 codes of x */
     size_t x_scale;     /* fp8: fp32  [T]      per-token scales of x */
-    size_t g;           /* streaming: fp32 [split_k1][P][2I] gate-up partial sums
-                           (scaled on fp8); LDS tiles + fp8: fp32 [P][I]
+    size_t g;           /* tilings 0, 2: fp32 [split_k1][P][2I] gate-up partial
+                           sums (fp8: tiling 0 fully scaled, tiling 2 weight
+                           scales only); tiling 1 + fp8: fp32 [P][I]
                            SiLU(gate)*up before requantisation */
     size_t h;           /* bf16 [P][I] SiLU(gate)*up (bf16), or uint8 e4m3 codes [P][I] (fp8) */
     size_t h_scale;     /* fp8: fp32  [P]      per-row scales of h */
-    size_t y;           /* streaming: fp32 [split_k2][P][H] unweighted down partial sums;
-                           LDS tiles: bf16 [P][H] unweighted down rows */
+    size_t y;           /* tiling 0, or 2 with split_k2 > 1: fp32 [split_k2][P][H]
+                           unweighted down partial sums; tiling 1, or 2 with
+                           split_k2 == 1: bf16 [P][H] unweighted down rows
+                           (fp8, tiling 2: weight scales only) */
     size_t total_bytes; /* minimum size of the workspace */
     int32_t split_k1;   /* slices of the gate-up reduction over H */
     int32_t split_k2;   /* slices of the down reduction over I */
-    int32_t large_tiles;/* 1: 128-row LDS tiles; 0: register streaming */
+    int32_t tiling;     /* 0 register streaming, 1 LDS tiles, 2 strips */
 } moe_workspace_layout_t;
 
 /* Human-readable name of a status code (static string). */

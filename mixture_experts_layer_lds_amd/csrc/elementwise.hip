@@ -61,16 +61,19 @@ quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restric
   if (threadIdx.x == 0) scale[t] = sc;
 }
 
-// h[r][n] = SiLU(sum_s g[s][r][n]) * sum_s g[s][r][I + n] for the valid sorted
-// rows r < expert_offsets[E].
+// h[r][n] = SiLU(rs * sum_s g[s][r][n]) * (rs * sum_s g[s][r][I + n]) for the
+// valid sorted rows r < expert_offsets[E]; rs is the row's activation scale
+// when the partial sums carry only the weight scales, else 1.
 __device__ __forceinline__ f32x4 silu_mul4(const float* __restrict__ grow, size_t slice, int S,
-                                           int I, int i) {
+                                           int I, int i, float rs) {
   f32x4 gs = *reinterpret_cast<const f32x4*>(grow + 4 * i);
   f32x4 us = *reinterpret_cast<const f32x4*>(grow + I + 4 * i);
   for (int s = 1; s < S; s++) {
     gs += *reinterpret_cast<const f32x4*>(grow + s * slice + 4 * i);
     us += *reinterpret_cast<const f32x4*>(grow + s * slice + I + 4 * i);
   }
+  gs *= rs;
+  us *= rs;
   f32x4 o;
 #pragma unroll
   for (int w = 0; w < 4; w++) o[w] = silu_f32(gs[w]) * us[w];
@@ -92,7 +95,7 @@ act_bf16_kernel(const float* __restrict__ g, int S, int P, int I,
   const int v1 = min(I / 4, v0 + kActCols / 4);
 #pragma unroll 2
   for (int i = v0 + threadIdx.x; i < v1; i += kRowThreads) {
-    const f32x4 o = silu_mul4(grow, slice, S, I, i);
+    const f32x4 o = silu_mul4(grow, slice, S, I, i, 1.0f);
     u32x2 packed;
     packed.x = (uint32_t)f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16);
     packed.y = (uint32_t)f32_to_bf16_bits(o[2]) | ((uint32_t)f32_to_bf16_bits(o[3]) << 16);
@@ -104,18 +107,20 @@ act_bf16_kernel(const float* __restrict__ g, int S, int P, int I,
 // amax, then quantised with the per-row rule (e4m3 codes + fp32 scale).
 __global__ void __launch_bounds__(kRowThreads)
 act_fp8_kernel(const float* __restrict__ g, int S, int P, int I,
-               const int32_t* __restrict__ expert_offsets, int E, uint8_t* __restrict__ hq,
-               float* __restrict__ h_scale) {
+               const int32_t* __restrict__ expert_offsets, int E,
+               const float* __restrict__ x_scale, const int32_t* __restrict__ sorted_pairs, int k,
+               uint8_t* __restrict__ hq, float* __restrict__ h_scale) {
   __shared__ float s_red[4];
   const int r = blockIdx.x;
   if (r >= expert_offsets[E]) return;   // block-uniform
+  const float rs = x_scale ? x_scale[sorted_pairs[r] / k] : 1.0f;
   const size_t slice = (size_t)P * 2 * I;
   const float* grow = g + (size_t)r * 2 * I;
   const int nvec = I / 4;
   float amax = 0.0f;
 #pragma unroll 4
   for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
-    const f32x4 o = silu_mul4(grow, slice, S, I, i);
+    const f32x4 o = silu_mul4(grow, slice, S, I, i, rs);
 #pragma unroll
     for (int w = 0; w < 4; w++) amax = __builtin_fmaxf(amax, __builtin_fabsf(o[w]));
   }
@@ -125,14 +130,16 @@ act_fp8_kernel(const float* __restrict__ g, int S, int P, int I,
   uint32_t* qrow = reinterpret_cast<uint32_t*>(hq + (size_t)r * I);
 #pragma unroll 4
   for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
-    const f32x4 o = silu_mul4(grow, slice, S, I, i);
+    const f32x4 o = silu_mul4(grow, slice, S, I, i, rs);
     qrow[i] = f32x4_to_e4m3x4_sat(__fmul_rn(o[0], inv), __fmul_rn(o[1], inv),
                                   __fmul_rn(o[2], inv), __fmul_rn(o[3], inv));
   }
   if (threadIdx.x == 0) h_scale[r] = sc;
 }
 
-// out[t][:] = bf16( sum_{j ascending, pair valid} w[t][j] * sum_s y[s][pos][:] ).
+// out[t][:] = bf16( sum_{j ascending, pair valid} w[t][j] * rs[pos] * sum_s y[s][pos][:] ),
+// rs = row_scale (the fp8 activation scale of the row when y carries only
+// the weight scales) or 1.
 // y is fp32 [S][P][H] (4 columns per thread, 16-byte loads), or bf16 [P][H]
 // when Y_BF16 (8 columns per thread, 16-byte loads).  Grid (token, column
 // chunk of kRowThreads * columns-per-thread).
@@ -140,7 +147,8 @@ template <bool Y_BF16>
 __global__ void __launch_bounds__(kRowThreads)
 reduce_kernel(const void* __restrict__ yv, int S, int P, const float* __restrict__ topk_w,
               const int32_t* __restrict__ pair_pos, const int32_t* __restrict__ expert_offsets,
-              int E, int k, int H, uint16_t* __restrict__ out) {
+              const float* __restrict__ row_scale, int E, int k, int H,
+              uint16_t* __restrict__ out) {
   constexpr int C = Y_BF16 ? 8 : 4;
   const int t = blockIdx.x;
   const int c0 = (blockIdx.y * kRowThreads + threadIdx.x) * C;   // first column
@@ -169,6 +177,11 @@ reduce_kernel(const void* __restrict__ yv, int S, int P, const float* __restrict
 #pragma unroll
       for (int q = 0; q < 4; q++) v[q] = a[q];
     }
+    if (row_scale) {
+      const float rs = row_scale[r];
+#pragma unroll
+      for (int q = 0; q < C; q++) v[q] = __fmul_rn(v[q], rs);
+    }
     const float w = topk_w[p];
 #pragma unroll
     for (int q = 0; q < C; q++) acc[q] = __fadd_rn(acc[q], __fmul_rn(w, v[q]));
@@ -194,10 +207,12 @@ hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, 
 }
 
 hipError_t launch_act(const float* g, int S, int P, int I, const int32_t* expert_offsets, int E,
-                      bool fp8, void* h, float* h_scale, hipStream_t s) {
+                      bool fp8, const float* x_scale, const int32_t* sorted_pairs, int k, void* h,
+                      float* h_scale, hipStream_t s) {
   if (fp8) {
     hipLaunchKernelGGL(moe::act_fp8_kernel, dim3(P), dim3(moe::kRowThreads), 0, s, g, S, P, I,
-                       expert_offsets, E, static_cast<uint8_t*>(h), h_scale);
+                       expert_offsets, E, x_scale, sorted_pairs, k, static_cast<uint8_t*>(h),
+                       h_scale);
   } else {
     const dim3 grid(P, (I + moe::kActCols - 1) / moe::kActCols);
     hipLaunchKernelGGL(moe::act_bf16_kernel, grid, dim3(moe::kRowThreads), 0, s, g, S, P, I,
@@ -207,16 +222,16 @@ hipError_t launch_act(const float* g, int S, int P, int I, const int32_t* expert
 }
 
 hipError_t launch_reduce(const void* y, bool y_bf16, int S, int P, const float* topk_w,
-                         const int32_t* pair_pos, const int32_t* expert_offsets, int E, int T,
-                         int k, int H, uint16_t* out, hipStream_t s) {
+                         const int32_t* pair_pos, const int32_t* expert_offsets, const float* row_scale,
+                         int E, int T, int k, int H, uint16_t* out, hipStream_t s) {
   const int cols = y_bf16 ? 8 : 4;
   const dim3 grid(T, (H / cols + moe::kRowThreads - 1) / moe::kRowThreads);
   if (y_bf16)
     hipLaunchKernelGGL(moe::reduce_kernel<true>, grid, dim3(moe::kRowThreads), 0, s, y, S, P,
-                       topk_w, pair_pos, expert_offsets, E, k, H, out);
+                       topk_w, pair_pos, expert_offsets, row_scale, E, k, H, out);
   else
     hipLaunchKernelGGL(moe::reduce_kernel<false>, grid, dim3(moe::kRowThreads), 0, s, y, S, P,
-                       topk_w, pair_pos, expert_offsets, E, k, H, out);
+                       topk_w, pair_pos, expert_offsets, row_scale, E, k, H, out);
   return hipGetLastError();
 }
 

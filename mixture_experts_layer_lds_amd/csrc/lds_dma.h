@@ -1,0 +1,68 @@
+// Device helpers shared by the LDS-staged GEMM kernels: direct global->LDS
+// copies, explicit vector-memory waits, a barrier without a memory fence,
+// and scalar (constant-cache) loads of wave-uniform records.
+#pragma once
+
+#include "moe_common.h"
+
+namespace moe {
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+
+// global_load_lds_dwordx4: each lane copies 16 bytes from src into LDS; one
+// wave instruction fills 1 KiB at lds_dst (lane l writes bytes 16l..16l+15).
+// Completion is tracked by vmcnt like any vector load.
+__device__ __forceinline__ void dma16(const void* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
+}
+
+// Workgroup barrier without a memory fence (a fence would drain every
+// in-flight load); the empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void barrier_nofence() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (loads complete in issue order, so every older one is done).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Scalar load of a wave-uniform 16-byte task record.  Its wait is on
+// lgkmcnt, so it does not drain in-flight vector loads as a vector load's
+// vmcnt wait would.
+__device__ __forceinline__ moe_task_t load_task_scalar(const moe_task_t* p) {
+  i32x4_t v;
+  __asm__ volatile("s_load_dwordx4 %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  moe_task_t t;
+  t.expert = v[0];
+  t.row_begin = v[1];
+  t.rows = v[2];
+  t.reserved = v[3];
+  return t;
+}
+
+// Scalar load of 16 consecutive wave-uniform dwords (64 bytes, 4-byte aligned).
+__device__ __forceinline__ i32x16_t load16_scalar(const void* p) {
+  i32x16_t v;
+  __asm__ volatile("s_load_dwordx16 %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+// Lane l receives v[l % 16].
+__device__ __forceinline__ int spread16(const i32x16_t& v, int lane) {
+  const int j = lane & 15;
+  int r = v[0];
+#pragma unroll
+  for (int i = 1; i < 16; i++) r = (j == i) ? v[i] : r;
+  return r;
+}
+
+}  // namespace moe

@@ -17,16 +17,25 @@ using moe_host::GemmPlan;
 
 constexpr size_t kNone = ~(size_t)0;
 constexpr long kTargetItems = 2048;   // work items that fill 256 CUs x 8 waves
+// The plan is a fixed function of the sizes (the layout queries run without
+// a device), so it balances work for MI355X's compute-unit count; launches
+// use the device's actual count.
+constexpr long kPlanCUs = 256;
+constexpr int kStripCols = 256;       // output columns per strip work item
+
+enum Tiling { kStreaming = 0, kLdsTiles = 1, kStrips = 2 };
 
 struct Plan {
   int block_m = 16;
   int mb = 1;
   int max_tasks = 0;
-  bool tiled = false;            // LDS-tiled GEMMs (large T) instead of register streaming
-  int bm_t = 128;                // tiled: rows per tile (128 or 256)
-  int bn1 = 128, bn2 = 128;      // tiled: N tile of gate-up / down
-  int split1 = 1, unroll1 = 1;   // streaming gate-up: K = H
-  int split2 = 1, unroll2 = 1;   // streaming down:    K = I
+  int tiling = kStreaming;
+  int bm_t = 128;                // LDS tiles: rows per tile (128 or 256)
+  int bn1 = 128, bn2 = 128;      // LDS tiles: N tile of gate-up / down
+  int split1 = 1, unroll1 = 1;   // streaming / strips gate-up: K = H
+  int split2 = 1, unroll2 = 1;   // streaming / strips down:    K = I
+  int ks1 = 4, nbuf1 = 4;        // strips: K steps per stage, stages in flight (gate-up)
+  int ks2 = 4, nbuf2 = 4;        // (down)
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -56,6 +65,38 @@ int choose_split(int nsteps, int unroll, long items) {
   return s;
 }
 
+// Strip GEMM configuration for a reduction of nsteps 64-byte steps and
+// `items` work items per K slice: the (K steps per stage, stages in flight)
+// pairs the kernel is built for, in order of preference, and the smallest
+// power-of-two K split whose items spread evenly (>= 80%) over the CUs, else
+// the best-spread one.  Returns false if no configuration divides the
+// reduction.
+bool choose_strip(int nsteps, int mb, bool fp8, long items, int* split, int* ks, int* nbuf) {
+  // about 12-24 KiB of weights in flight per wave first
+  static const int kCfg[8][2] = {{2, 4}, {4, 3}, {4, 4}, {2, 3}, {4, 2}, {1, 4}, {2, 2}, {1, 2}};
+  double best_eff = -1.0;
+  for (int S = 1; S <= 8; S *= 2) {
+    for (const auto& c : kCfg) {
+      if (!moe_host::strip_config_supported(mb, c[0], c[1], fp8)) continue;
+      if (nsteps % (c[0] * S)) continue;
+      const int nk = nsteps / (c[0] * S);
+      if (nk < c[1] || nk % c[1]) continue;
+      const long n = items * S;
+      const long rounds = (n + kPlanCUs - 1) / kPlanCUs;
+      const double eff = (double)n / (double)(rounds * kPlanCUs);
+      if (eff > best_eff + 1e-9) {
+        best_eff = eff;
+        *split = S;
+        *ks = c[0];
+        *nbuf = c[1];
+      }
+      break;   // first supported configuration for this split
+    }
+    if (best_eff >= 0.8) break;
+  }
+  return best_eff >= 0.0;
+}
+
 // Tile plan: a fixed function of the shape and dtype, shared by the routing
 // build, the workspace layout and the forward pass.
 Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
@@ -63,11 +104,31 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   const long P = (long)T * k;
   const long active = P < E ? P : E;
   const long avg = active > 0 ? (P + active - 1) / active : 1;
-  // Many rows per expert: LDS tiles.  Otherwise register-streaming tiles
-  // about twice the mean rows per active expert, so that the usual spread
-  // of a uniform routing still fits one tile per expert.
-  p.tiled = avg > 48;
   const int esz_t = dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2;
+  const int nsteps1 = H * esz_t / 64, nsteps2 = I * esz_t / 64;
+  // Few rows per expert (decode): register streaming, tiles of 16 rows.
+  // A few dozen to ~80 rows: strips (token rows in LDS, weights streamed),
+  // tiles of about twice the mean rows per active expert so that the usual
+  // spread of a uniform routing still fits one tile per expert.  More rows:
+  // LDS tiles of both operands.
+  if (avg > 8 && avg <= 80 && (2 * I) % kStripCols == 0 && H % kStripCols == 0) {
+    // tile height about twice the mean rows per expert
+    const int mb = avg <= 16 ? 2 : (avg <= 40 ? 4 : 8);
+    long tasks = (P + 16 * mb - 1) / (16 * mb);
+    if (tasks < active) tasks = active;
+    Plan q = p;
+    const bool fp8 = dtype == MOE_DTYPE_FP8_W8A8;
+    if (choose_strip(nsteps1, mb, fp8, tasks * (2L * I / kStripCols), &q.split1, &q.ks1, &q.nbuf1) &&
+        choose_strip(nsteps2, mb, fp8, tasks * ((long)H / kStripCols), &q.split2, &q.ks2, &q.nbuf2)) {
+      q.tiling = kStrips;
+      q.mb = mb;
+      q.block_m = 16 * mb;
+      q.max_tasks = (int)(P / q.block_m + (P < E ? P : E));
+      return q;
+    }
+  }
+  const bool tiled = avg > 48;
+  p.tiling = tiled ? kLdsTiles : kStreaming;
   const int rb1 = H * esz_t, rb2 = I * esz_t;   // row bytes of the two reductions
   // 256 x 256 direct-to-LDS tiles (4-stage ring, 64-byte K steps) when the
   // experts hold enough rows to fill them; else 128-row tiles: the 128 x 256
@@ -79,14 +140,12 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   const bool dma2 = rb2 % 128 == 0 && rb2 >= 256 && H % 256 == 0;
   p.bn1 = big || dma1 ? 256 : 128;       // 128 (or 64) output columns of h per tile
   p.bn2 = big || dma2 ? 256 : ((H % 128 == 0) ? 128 : 64);
-  p.block_m = p.tiled ? p.bm_t : (avg <= 8 ? 16 : (avg <= 16 ? 32 : 64));
+  p.block_m = tiled ? p.bm_t : (avg <= 8 ? 16 : (avg <= 16 ? 32 : 64));
   p.mb = p.block_m / 16;
   p.max_tasks = (int)(P / p.block_m + (P < E ? P : E));
   long est_tasks = (P + p.block_m - 1) / p.block_m;
   if (est_tasks < active) est_tasks = active;
-  const int esz = dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2;
-  const int nsteps1 = H * esz / 64, nsteps2 = I * esz / 64;
-  if (!p.tiled) {
+  if (!tiled) {
     p.unroll1 = choose_unroll(nsteps1, p.mb);
     p.unroll2 = choose_unroll(nsteps2, p.mb);
     p.split1 = choose_split(nsteps1, p.unroll1, est_tasks * (2L * I / 16));
@@ -110,7 +169,9 @@ void routing_layout(int T, int k, int E, const Plan& p, moe_routing_layout_t* L)
   off = align_up(off + sizeof(moe_task_t) * (size_t)p.max_tasks, 16);
   L->scratch = off;
   off = align_up(off + moe_host::route_scratch_bytes((int)P), 16);
-  L->total_bytes = off;
+  // tail: the strip GEMM reads the token indices of a row tile as one
+  // 64-byte scalar load, which may run up to 60 bytes past the last row
+  L->total_bytes = off + 64;
   L->block_m = p.block_m;
   L->max_tasks = p.max_tasks;
 }
@@ -127,17 +188,18 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
   };
   W->xq = fp8 ? take((size_t)T * H) : kNone;
   W->x_scale = fp8 ? take(4 * (size_t)T) : kNone;
-  if (p.tiled)
+  if (p.tiling == kLdsTiles)
     W->g = fp8 ? take(4 * P * I) : kNone;               // fp32 SiLU(gate)*up before requant
   else
     W->g = take(4 * (size_t)p.split1 * P * 2 * I);      // fp32 gate-up partial sums
   W->h = take(P * I * (fp8 ? 1 : 2));
   W->h_scale = fp8 ? take(4 * P) : kNone;
-  W->y = p.tiled ? take(2 * P * H) : take(4 * (size_t)p.split2 * P * H);
+  const bool y_bf16 = p.tiling == kLdsTiles || (p.tiling == kStrips && p.split2 == 1);
+  W->y = y_bf16 ? take(2 * P * H) : take(4 * (size_t)p.split2 * P * H);
   W->total_bytes = off;
-  W->split_k1 = p.split1;
-  W->split_k2 = p.split2;
-  W->large_tiles = p.tiled ? 1 : 0;
+  W->split_k1 = p.tiling == kLdsTiles ? 1 : p.split1;
+  W->split_k2 = p.tiling == kLdsTiles ? 1 : p.split2;
+  W->tiling = p.tiling;
 }
 
 // Compute-unit count per device, queried once.
@@ -250,10 +312,68 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
   if (fp8) {
     StageScope st(s, 0);
     e = moe_host::launch_quant_rows_bf16(static_cast<const uint16_t*>(x), T, H, xq, x_scale,
-                                         p.tiled ? h_scale : nullptr, k, s);
+                                         p.tiling == kLdsTiles ? h_scale : nullptr, k, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
-  if (p.tiled) {
+  if (p.tiling == kStrips) {
+    float* g = reinterpret_cast<float*>(ws + W.g);
+    const bool y_bf16 = p.split2 == 1;
+    {
+      StageScope st(s, 1);
+      moe_host::StripArgs a{};
+      a.a = fp8 ? static_cast<const void*>(xq) : x;
+      a.b = w1;
+      a.b_scale = w1_scale;
+      a.sorted_pairs = R.sorted_pairs;
+      a.header = R.header;
+      a.tasks = R.tasks;
+      a.c = g;
+      a.K = H;
+      a.N = 2 * I;
+      a.P = P;
+      a.topk = k;
+      a.max_tasks = p.max_tasks;
+      a.split = p.split1;
+      a.out_bf16 = 0;
+      e = moe_host::launch_strip_gemm(a, true, fp8, p.mb, p.ks1, p.nbuf1, cus, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 2);
+      e = moe_host::launch_act(g, p.split1, P, I, R.expert_offsets, E, fp8, x_scale,
+                               R.sorted_pairs, k, h, h_scale, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 3);
+      moe_host::StripArgs a{};
+      a.a = h;
+      a.b = w2;
+      a.b_scale = w2_scale;
+      a.sorted_pairs = R.sorted_pairs;
+      a.header = R.header;
+      a.tasks = R.tasks;
+      a.c = ws + W.y;
+      a.K = I;
+      a.N = H;
+      a.P = P;
+      a.topk = k;
+      a.max_tasks = p.max_tasks;
+      a.split = p.split2;
+      a.out_bf16 = y_bf16 ? 1 : 0;
+      e = moe_host::launch_strip_gemm(a, false, fp8, p.mb, p.ks2, p.nbuf2, cus, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 4);
+      e = moe_host::launch_reduce(ws + W.y, y_bf16, p.split2, P, topk_w, R.pair_pos,
+                                  R.expert_offsets, h_scale, E, T, k, H,
+                                  static_cast<uint16_t*>(out), s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+  }
+  if (p.tiling == kLdsTiles) {
     const int grid1 = p.bn1 == 256 ? cus : cus * 2;   // a direct-to-LDS ring fits once per CU
     const int grid2 = p.bn2 == 256 ? cus : cus * 2;
     float* h32 = fp8 ? reinterpret_cast<float*>(ws + W.g) : nullptr;
@@ -306,8 +426,8 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     }
     {
       StageScope st(s, 4);
-      e = moe_host::launch_reduce(ws + W.y, true, 1, P, topk_w, R.pair_pos, R.expert_offsets, E,
-                                  T, k, H, static_cast<uint16_t*>(out), s);
+      e = moe_host::launch_reduce(ws + W.y, true, 1, P, topk_w, R.pair_pos, R.expert_offsets,
+                                  nullptr, E, T, k, H, static_cast<uint16_t*>(out), s);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
     return MOE_OK;
@@ -338,7 +458,8 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
   }
   {
     StageScope st(s, 2);
-    e = moe_host::launch_act(g, p.split1, P, I, R.expert_offsets, E, fp8, h, h_scale, s);
+    e = moe_host::launch_act(g, p.split1, P, I, R.expert_offsets, E, fp8, nullptr, nullptr, k, h,
+                             h_scale, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
@@ -364,8 +485,8 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
   }
   {
     StageScope st(s, 4);
-    e = moe_host::launch_reduce(y, false, p.split2, P, topk_w, R.pair_pos, R.expert_offsets, E, T,
-                                k, H, static_cast<uint16_t*>(out), s);
+    e = moe_host::launch_reduce(y, false, p.split2, P, topk_w, R.pair_pos, R.expert_offsets,
+                                nullptr, E, T, k, H, static_cast<uint16_t*>(out), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;

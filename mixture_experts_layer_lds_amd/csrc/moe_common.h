@@ -71,6 +71,23 @@ __device__ __forceinline__ void e4m3_row_scales(float amax, float* scale, float*
   }
 }
 
+// acc += A * B^T over 128 bytes of K of e4m3 data, on the full-rate gfx950
+// instruction (v_mfma_scale_f32_16x16x128_f8f6f4, both block scales 2^0).
+// (a0, a1) and (b0, b1) are the lane's 16-byte fragments of two consecutive
+// 64-byte K steps in the packed lane order (lane l: row/column l % 16,
+// bytes 16*(l/16) of each step).  The instruction reads a lane's 32 bytes
+// as one run of K; A and B lanes of the same group l/16 supply the same K
+// positions, so the sum runs over exactly the 128 products of the two steps.
+__device__ __forceinline__ void mfma_fp8_k128(f32x4& acc, const u32x4& a0, const u32x4& a1,
+                                              const u32x4& b0, const u32x4& b1) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                   (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+}
+
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -96,14 +113,18 @@ hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, 
 
 // SiLU-and-mul of the gate-up partial sums g[S][P][2I] for the valid sorted
 // rows; writes bf16 h[P][I] (fp8 = false) or e4m3 codes h[P][I] + scales.
+// With x_scale (fp8 strips), the slice sums of row r are first multiplied
+// by x_scale[sorted_pairs[r] / k].
 hipError_t launch_act(const float* g, int S, int P, int I, const int32_t* expert_offsets, int E,
-                      bool fp8, void* h, float* h_scale, hipStream_t s);
+                      bool fp8, const float* x_scale, const int32_t* sorted_pairs, int k, void* h,
+                      float* h_scale, hipStream_t s);
 
-// out[t] = bf16(sum_j w[t][j] * sum_s y[s][pos[t*k+j]]) over valid pairs;
-// y is fp32 [S][P][H] (y_bf16 = false) or bf16 [P][H] (S = 1).
+// out[t] = bf16(sum_j w[t][j] * row_scale[r] * sum_s y[s][r]) over valid
+// pairs, r = pos[t*k+j]; y is fp32 [S][P][H] (y_bf16 = false) or bf16
+// [P][H] (S = 1); row_scale null means 1.
 hipError_t launch_reduce(const void* y, bool y_bf16, int S, int P, const float* topk_w,
-                         const int32_t* pair_pos, const int32_t* expert_offsets, int E, int T,
-                         int k, int H, uint16_t* out, hipStream_t s);
+                         const int32_t* pair_pos, const int32_t* expert_offsets, const float* row_scale,
+                         int E, int T, int k, int H, uint16_t* out, hipStream_t s);
 
 struct GemmArgs {
   const void* a;            // gathered: x / xq [T][K]; contiguous: h / hq [P][K]
@@ -158,6 +179,32 @@ struct TiledArgs {
 
 hipError_t launch_tiled_gemm(const TiledArgs& a, bool gateup, bool fp8, int bm, int bn, int grid,
                              hipStream_t s);
+
+// Strip GEMM (A in an LDS ring shared by 8 waves, weights streamed to
+// registers): work items of 256 output columns of one task tile and one K
+// slice.  On fp8 only the weight column scale is applied; the consumer
+// applies the row scale.
+struct StripArgs {
+  const void* a;                // gathered: x / xq [T][K]; contiguous: h / hq [P][K]
+  const void* b;                // packed weights [E][N][K]
+  const float* b_scale;         // fp8: [E][N]
+  const int32_t* sorted_pairs;  // gathered: pair index of each sorted row
+  const int32_t* header;
+  const moe_task_t* tasks;
+  void* c;                      // fp32 [split][P][N], or bf16 [P][N] when out_bf16
+  int K;                        // reduction length (elements)
+  int N;                        // output columns, a multiple of 256
+  int P;
+  int topk;
+  int max_tasks;
+  int split;                    // K slices
+  int out_bf16;                 // 1: bf16 rows (split == 1)
+};
+
+// (mb, ks, nbuf) = 16-row blocks per tile, 64-byte K steps per stage, stages in flight.
+bool strip_config_supported(int mb, int ks, int nbuf, bool fp8);
+hipError_t launch_strip_gemm(const StripArgs& a, bool gather, bool fp8, int mb, int ks, int nbuf,
+                             int grid, hipStream_t s);
 
 // fp32 rows -> e4m3 codes with the row amax held in h_scale (replaced by the scale).
 hipError_t launch_requant_rows(const float* h32, int P, int I, const int32_t* expert_offsets,

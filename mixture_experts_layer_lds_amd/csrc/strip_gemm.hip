@@ -1,0 +1,316 @@
+// Grouped expert GEMM for a few dozen to a few hundred rows per expert:
+// the layer is still bound by streaming the expert weights from HBM, but a
+// task tile holds too many token rows for register streaming, which would
+// re-read every row of the tile from L2 once per 16 weight columns.
+//
+// Same pipeline role as grouped_gemm.hip (HPC-Ops x SGLang blog, section
+// "MoE": gate-up reads tokens through the route index with no separate
+// gather; a persistent grid consumes the per-tile task map).
+//
+//  * One workgroup of 8 waves per CU.  Work item = (task tile of 16*MB
+//    rows, strip of 256 output columns, K slice).
+//  * The tile's token rows go through LDS: a ring of NBUF+1 stages, each
+//    holding KS 64-byte K steps of all 16*MB rows as 1 KiB chunks in MFMA
+//    lane order, filled by direct global->LDS copies spread over the waves.
+//  * Each wave owns 32 columns of the strip and streams their packed
+//    weights (1 KiB chunks, non-temporal) straight into registers NBUF
+//    stages ahead, so a CU keeps 8 x NBUF x KS x 2 KiB of weights in flight
+//    without passing them through LDS.  A weight fragment in registers
+//    meets all 16*MB rows of the tile; a token fragment read from LDS meets
+//    both of the wave's 16-column blocks.
+//  * The ring runs straight across work items: the next item's first stages
+//    are in flight while the current one finishes and stores its results.
+//  * Per-item metadata (the task record, the tile's token indices, fp8
+//    column scales) comes from scalar loads, whose waits are on lgkmcnt, so
+//    the vector-memory queue holds only the ring's loads and the epilogue's
+//    stores, and the explicit vmcnt waits below count exactly those.
+//
+// Output: fp32 partial sums c[s][P][N], or bf16 rows c[P][N] (one slice,
+// out_bf16).  On fp8 the per-column weight scale is applied here and the
+// per-row activation scale by the consumer (SiLU-and-mul, or the top-k
+// reduction).
+#include "lds_dma.h"
+
+namespace moe {
+
+constexpr int kStripWaves = 8;
+constexpr int kStripThreads = kStripWaves * 64;
+
+template <int MB, int KS, int NSUB>
+struct StripItem {
+  static constexpr int NA = MB * KS / kStripWaves;   // token chunks this wave copies per stage
+  int row_begin, rows, s;
+  int col;                     // first output column of this wave
+  const char* a[NA];           // this lane's token sources (K step and lane offsets applied)
+  const char* b;               // this lane's packed-weight source of column block 0
+  float bs[NSUB];              // fp8: weight scale of this lane's column in each block
+};
+
+template <int MB, int KS, int NSUB, bool GATHER, bool FP8>
+__device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::StripArgs& g, int item,
+                                                              int n_strips, int nk, size_t row_bytes,
+                                                              int nsteps, int wave, int lane) {
+  constexpr int kCols = kStripWaves * NSUB * 16;
+  StripItem<MB, KS, NSUB> it;
+  const int s = item % g.split;
+  const int rest = item / g.split;
+  // the strips of one tile side by side: they meet its token rows in L2
+  const int nt = rest % n_strips;
+  const int ti = rest / n_strips;
+  const moe_task_t task = load_task_scalar(g.tasks + ti);
+  it.row_begin = task.row_begin;
+  it.rows = task.rows;
+  it.s = s;
+  it.col = nt * kCols + wave * (NSUB * 16);
+  const int step0 = s * nk * KS;
+  const int lrow = lane & 15;
+#pragma unroll
+  for (int i = 0; i < StripItem<MB, KS, NSUB>::NA; i++) {
+    // chunk c = 16-row block c / KS, K step c % KS of every stage
+    const int c = wave + kStripWaves * i;
+    const int rb = c / KS, st = c % KS;
+    // row blocks past the tile, and rows past it inside the last block,
+    // re-read the tile's first row: always a valid address, never stored
+    const int rb_ld = rb * 16 < task.rows ? rb : 0;
+    const bool in_tile = rb_ld * 16 + lrow < task.rows;
+    int arow;
+    if constexpr (GATHER) {
+      const i32x16_t sp = load16_scalar(g.sorted_pairs + task.row_begin + rb_ld * 16);
+      const int p = in_tile ? spread16(sp, lane) : sp[0];
+      arow = p / g.topk;
+    } else {
+      arow = task.row_begin + (in_tile ? rb_ld * 16 + lrow : 0);
+    }
+    it.a[i] = static_cast<const char*>(g.a) + (size_t)arow * row_bytes + (size_t)(step0 + st) * 64 +
+              16 * (lane >> 4);
+  }
+  it.b = static_cast<const char*>(g.b) +
+         (((size_t)task.expert * (g.N / 16) + it.col / 16) * nsteps + step0) * 1024 + 16 * lane;
+#pragma unroll
+  for (int q = 0; q < NSUB; q++) {
+    it.bs[q] = 1.0f;
+    if constexpr (FP8) {
+      const i32x16_t v = load16_scalar(g.b_scale + (size_t)task.expert * g.N + it.col + 16 * q);
+      it.bs[q] = __int_as_float(spread16(v, lane));
+    }
+  }
+  return it;
+}
+
+template <bool FP8>
+__device__ __forceinline__ void strip_mfma(f32x4& acc, const u32x4& a, const u32x4& b) {
+  if constexpr (FP8) {
+    const i64x2 a2 = __builtin_bit_cast(i64x2, a);
+    const i64x2 b2 = __builtin_bit_cast(i64x2, b);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[0], b2[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[1], b2[1], acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+}
+
+template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8>
+__global__ void __launch_bounds__(kStripThreads, 1)
+strip_gemm_kernel(moe_host::StripArgs g) {
+  using It = StripItem<MB, KS, NSUB>;
+  constexpr int NA = It::NA;
+  constexpr int PER = NA + KS * NSUB;   // vector-memory operations per wave per stage
+  constexpr int NST = NBUF + 1;         // LDS ring slots
+  constexpr int SLOT = MB * KS * 1024;
+  static_assert(NA >= 1 && NA * kStripWaves == MB * KS, "token chunks split evenly over waves");
+  static_assert(NBUF >= 2, "ring depth");
+  static_assert((NBUF - 1) * PER < 64, "vmcnt range");
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int lane = threadIdx.x & 63;
+  // wave-uniform, and known to be so: the scalar loads address with it
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
+  const int n_strips = g.N / (kStripWaves * NSUB * 16);
+  const int total = num_tasks * n_strips * g.split;
+  const size_t row_bytes = (size_t)g.K * (FP8 ? 1 : 2);
+  const int nsteps = (int)(row_bytes / 64);
+  const int nk = nsteps / (KS * g.split);   // stages per item: a multiple of NBUF, >= NBUF
+
+  // XCD-aware numbering: workgroups are dispatched round-robin over the 8
+  // XCDs; give each XCD a contiguous run of items, so the strips of one task
+  // tile share its token rows through one L2.
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per_xcd = G / 8, extra = G % 8;
+  const int vid = (xcd < extra ? xcd * (per_xcd + 1) : extra * (per_xcd + 1) + (xcd - extra) * per_xcd) + slot;
+  if (vid >= total) return;
+  const int n_items = (total - vid + G - 1) / G;
+
+  It cur = strip_item<MB, KS, NSUB, GATHER, FP8>(g, vid, n_strips, nk, row_bytes, nsteps, wave,
+                                                 lane);
+  It nxt = cur;
+  if (n_items > 1)
+    nxt = strip_item<MB, KS, NSUB, GATHER, FP8>(g, vid + G, n_strips, nk, row_bytes, nsteps, wave,
+                                                lane);
+
+  // Every stage issues exactly PER vector-memory operations per wave: the
+  // NBUF stages past the last one re-load the last item's first stages
+  // (valid addresses, never used), so the wait before each stage is the
+  // same count and the compiler's own waits for the weight registers see
+  // the same queue on every path.
+  u32x4 bb[NBUF][KS][NSUB];
+  auto issue = [&](bool in_cur, int kt, int fslot, u32x4 (&b)[KS][NSUB]) {
+    char* sb = lds + fslot * SLOT;
+#pragma unroll
+    for (int i = 0; i < NA; i++)
+      dma16((in_cur ? cur.a[i] : nxt.a[i]) + (size_t)kt * KS * 64,
+            sb + (wave + kStripWaves * i) * 1024);
+    const char* bsrc = in_cur ? cur.b : nxt.b;
+#pragma unroll
+    for (int u = 0; u < KS; u++)
+#pragma unroll
+      for (int q = 0; q < NSUB; q++)
+        b[u][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            bsrc + ((size_t)q * nsteps + (size_t)kt * KS + u) * 1024));
+  };
+
+  // The empty asm statements keep each stage's operations together in
+  // issue order (the barriers do so inside the loop), which the vmcnt
+  // counts rely on.
+#pragma unroll
+  for (int d = 0; d < NBUF; d++) {
+    issue(true, d, d, bb[d]);
+    __asm__ volatile("" ::: "memory");
+  }
+
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  int f = 0;   // flat stage index over all items of this workgroup
+  for (int ii = 0; ii < n_items; ii++) {
+    f32x4 acc[MB][NSUB];
+#pragma unroll
+    for (int m = 0; m < MB; m++)
+#pragma unroll
+      for (int q = 0; q < NSUB; q++) acc[m][q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int kt0 = 0; kt0 < nk; kt0 += NBUF, f += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; u++) {
+        const int fc = f + u;
+        // stage fc has landed in this wave (NBUF-1 later stages, and any
+        // epilogue stores, may still be in flight), then in every wave
+        wait_vm<(NBUF - 1) * PER>();
+        barrier_nofence();
+        const char* sb = lds + (fc % NST) * SLOT;
+        if constexpr (FP8 && KS % 2 == 0) {
+          // two K steps per full-rate fp8 instruction
+#pragma unroll
+          for (int st = 0; st < KS; st += 2) {
+#pragma unroll
+            for (int m = 0; m < MB; m++) {
+              const u32x4 a0 = *reinterpret_cast<const u32x4*>(sb + (m * KS + st) * 1024 + 16 * lane);
+              const u32x4 a1 = *reinterpret_cast<const u32x4*>(sb + (m * KS + st + 1) * 1024 + 16 * lane);
+#pragma unroll
+              for (int q = 0; q < NSUB; q++)
+                mfma_fp8_k128(acc[m][q], a0, a1, bb[u][st][q], bb[u][st + 1][q]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int st = 0; st < KS; st++) {
+#pragma unroll
+            for (int m = 0; m < MB; m++) {
+              const u32x4 a = *reinterpret_cast<const u32x4*>(sb + (m * KS + st) * 1024 + 16 * lane);
+#pragma unroll
+              for (int q = 0; q < NSUB; q++) strip_mfma<FP8>(acc[m][q], a, bb[u][st][q]);
+            }
+          }
+        }
+        // Stage fc+NBUF reuses this stage's registers and the ring slot of
+        // stage fc-1, which every wave finished reading before the barrier.
+        const int ktn = kt0 + u + NBUF;
+        const bool in_cur = ktn < nk;
+        issue(in_cur, in_cur ? ktn : ktn - nk, (fc + NBUF) % NST, bb[u]);
+      }
+    }
+
+    // Epilogue: lane holds column (lane % 16) and rows 4*(lane / 16) + i of
+    // each 16 x 16 block.
+#pragma unroll
+    for (int m = 0; m < MB; m++) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int rr = 16 * m + 4 * lgrp + i;
+        if (rr < cur.rows) {
+          const size_t r = (size_t)(cur.row_begin + rr);
+#pragma unroll
+          for (int q = 0; q < NSUB; q++) {
+            const int col = cur.col + 16 * q + lrow;
+            float v = acc[m][q][i];
+            if constexpr (FP8) v = v * cur.bs[q];
+            if (g.out_bf16)
+              static_cast<uint16_t*>(g.c)[r * g.N + col] = f32_to_bf16_bits(v);
+            else
+              static_cast<float*>(g.c)[((size_t)cur.s * g.P + r) * g.N + col] = v;
+          }
+        }
+      }
+    }
+    cur = nxt;
+    if (ii + 2 < n_items)
+      nxt = strip_item<MB, KS, NSUB, GATHER, FP8>(g, vid + (ii + 2) * G, n_strips, nk, row_bytes,
+                                                  nsteps, wave, lane);
+  }
+  // the trailing re-loads still write this workgroup's LDS: let them land
+  wait_vm<0>();
+}
+
+template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8>
+static hipError_t launch_strip_t(const moe_host::StripArgs& a, int grid, hipStream_t s) {
+  constexpr int lds_bytes = (NBUF + 1) * MB * KS * 1024;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8>), dim3(grid),
+                     dim3(kStripThreads), lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+template <int MB, int KS, int NBUF, int NSUB>
+static hipError_t launch_strip_cfg(const moe_host::StripArgs& a, bool gather, bool fp8, int grid,
+                                   hipStream_t s) {
+  if (gather) return fp8 ? launch_strip_t<MB, KS, NBUF, NSUB, true, true>(a, grid, s)
+                         : launch_strip_t<MB, KS, NBUF, NSUB, true, false>(a, grid, s);
+  return fp8 ? launch_strip_t<MB, KS, NBUF, NSUB, false, true>(a, grid, s)
+             : launch_strip_t<MB, KS, NBUF, NSUB, false, false>(a, grid, s);
+}
+
+}  // namespace moe
+
+namespace moe_host {
+
+// (16-row blocks per tile, K steps per stage, stages in flight) built here.
+#define MOE_STRIP_CONFIGS(X) \
+  X(2, 4, 4) X(2, 4, 3) X(2, 4, 2)                       \
+  X(4, 2, 4) X(4, 4, 3) X(4, 4, 4) X(4, 2, 3) X(4, 4, 2) X(4, 2, 2) \
+  X(8, 2, 4) X(8, 2, 3) X(8, 1, 4) X(8, 2, 2)
+
+bool strip_config_supported(int mb, int ks, int nbuf, bool fp8) {
+  (void)fp8;   // every configuration is built for both data types
+#define MOE_STRIP_CASE(M, K, N) if (mb == M && ks == K && nbuf == N) return true;
+  MOE_STRIP_CONFIGS(MOE_STRIP_CASE)
+#undef MOE_STRIP_CASE
+  return false;
+}
+
+hipError_t launch_strip_gemm(const StripArgs& a, bool gather, bool fp8, int mb, int ks, int nbuf,
+                             int grid, hipStream_t s) {
+#define MOE_STRIP_CASE(M, K, N) \
+  if (mb == M && ks == K && nbuf == N) return moe::launch_strip_cfg<M, K, N, 2>(a, gather, fp8, grid, s);
+  MOE_STRIP_CONFIGS(MOE_STRIP_CASE)
+#undef MOE_STRIP_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe_host

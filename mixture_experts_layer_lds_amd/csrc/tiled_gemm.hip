@@ -27,7 +27,7 @@
 //  * Work items (task, n-tile) are handed out XCD-aware: consecutive items
 //    go to workgroups of the same XCD, so the A rows of a task and the
 //    weight block of an expert are shared through one L2.
-#include "moe_common.h"
+#include "lds_dma.h"
 
 namespace moe {
 
@@ -180,20 +180,41 @@ tiled_gemm_kernel(moe_host::TiledArgs g) {
       const int cur = kt & 1;
       if (kt + 1 < nk) gload(kt + 1);
       const char* base = lds + cur * S::kStageBytes;
+      if constexpr (FP8) {
+        // both K steps of the iteration in one full-rate fp8 instruction
+        static_assert(kIterSteps == 2, "fp8 pairs the two steps of an iteration");
+        u32x4 fa[S::kMB][2], fb[S::kNB][2];
 #pragma unroll
-      for (int st = 0; st < kIterSteps; st++) {
-        u32x4 fa[S::kMB], fb[S::kNB];
+        for (int st = 0; st < 2; st++) {
+#pragma unroll
+          for (int m = 0; m < S::kMB; m++)
+            fa[m][st] = *reinterpret_cast<const u32x4*>(base + ((wm * S::kMB + m) * kIterSteps + st) * 1024 + 16 * lane);
+#pragma unroll
+          for (int q = 0; q < S::kNB; q++)
+            fb[q][st] = *reinterpret_cast<const u32x4*>(base + S::kAChunks * 1024 +
+                                                        (bblock(q) * kIterSteps + st) * 1024 + 16 * lane);
+        }
 #pragma unroll
         for (int m = 0; m < S::kMB; m++)
-          fa[m] = *reinterpret_cast<const u32x4*>(base + ((wm * S::kMB + m) * kIterSteps + st) * 1024 + 16 * lane);
 #pragma unroll
-        for (int q = 0; q < S::kNB; q++)
-          fb[q] = *reinterpret_cast<const u32x4*>(base + S::kAChunks * 1024 +
-                                                  (bblock(q) * kIterSteps + st) * 1024 + 16 * lane);
+          for (int q = 0; q < S::kNB; q++)
+            mfma_fp8_k128(acc[m][q], fa[m][0], fa[m][1], fb[q][0], fb[q][1]);
+      } else {
 #pragma unroll
-        for (int m = 0; m < S::kMB; m++)
+        for (int st = 0; st < kIterSteps; st++) {
+          u32x4 fa[S::kMB], fb[S::kNB];
 #pragma unroll
-          for (int q = 0; q < S::kNB; q++) mfma_step_t<FP8>(acc[m][q], fa[m], fb[q]);
+          for (int m = 0; m < S::kMB; m++)
+            fa[m] = *reinterpret_cast<const u32x4*>(base + ((wm * S::kMB + m) * kIterSteps + st) * 1024 + 16 * lane);
+#pragma unroll
+          for (int q = 0; q < S::kNB; q++)
+            fb[q] = *reinterpret_cast<const u32x4*>(base + S::kAChunks * 1024 +
+                                                    (bblock(q) * kIterSteps + st) * 1024 + 16 * lane);
+#pragma unroll
+          for (int m = 0; m < S::kMB; m++)
+#pragma unroll
+            for (int q = 0; q < S::kNB; q++) mfma_step_t<FP8>(acc[m][q], fa[m], fb[q]);
+        }
       }
       if (kt + 1 < nk) lstore(cur ^ 1);
       __syncthreads();
@@ -282,31 +303,10 @@ static hipError_t launch_tiled_t(const moe_host::TiledArgs& a, int grid, hipStre
 // __syncthreads() would drain the whole ring).
 //
 // Shapes used: 128 x 256, two steps per stage, three stages (48 KiB
-// stages), and 256 x 256, one step per stage, four stages (32 KiB stages;
+// stages), and 256 x 256, one step per stage, five stages (32 KiB stages;
 // two thirds of the operand bytes per flop of the former).  Requires
 // row_bytes % (64*KS) == 0, at least KS*(NST-1) K steps and N_out a multiple
 // of the tile's output columns.
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void dma16(const void* src, char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
-}
-
-// Workgroup barrier without a memory fence (a fence would drain every
-// in-flight load); the empty asm statements keep the compiler from moving
-// memory accesses across it.
-__device__ __forceinline__ void barrier_nofence() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
-// wait until at most N of this wave's vector-memory operations are outstanding
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
 template <int BM_, int BN_, int KS_, int NST_, int WM_, int WN_>
 struct DmaShape {
   static constexpr int BM = BM_, BN = BN_, KS = KS_, NST = NST_, WM = WM_, WN = WN_;
@@ -323,21 +323,6 @@ struct DmaShape {
 };
 using DmaWide = DmaShape<128, 256, 2, 3, 2, 4>;   // 48 KiB stages x 3
 using DmaBig = DmaShape<256, 256, 1, 5, 4, 2>;    // 32 KiB stages x 5 (all of LDS)
-
-// Scalar (constant-cache) load of a wave-uniform 16-byte task record.  Its
-// wait is on lgkmcnt, so it does not drain the in-flight direct-to-LDS loads
-// that a vector load's vmcnt wait would.
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ moe_task_t load_task_scalar(const moe_task_t* p) {
-  i32x4_t v;
-  __asm__ volatile("s_load_dwordx4 %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
-  moe_task_t t;
-  t.expert = v[0];
-  t.row_begin = v[1];
-  t.rows = v[2];
-  t.reserved = v[3];
-  return t;
-}
 
 template <class Sh>
 struct DmaItem {
@@ -379,7 +364,6 @@ tiled_dma_kernel(moe_host::TiledArgs g) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / Sh::WN, wn = wave % Sh::WN;
-  const int st_w = wave % KS;
 
   const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
   const int out_cols = GATEUP ? Sh::BN / 2 : Sh::BN;
@@ -456,23 +440,44 @@ tiled_dma_kernel(moe_host::TiledArgs g) {
       else wait_vm<0>();
       barrier_nofence();
       const char* base = lds + (f % NST) * Sh::kStageBytes;
+      auto bchunk = [&](int q) {
+        if (GATEUP) return q < NB / 2 ? wn * (NB / 2) + q : Sh::BN / 32 + wn * (NB / 2) + (q - NB / 2);
+        return wn * NB + q;
+      };
+      if constexpr (FP8 && KS % 2 == 0) {
+        // two K steps per full-rate fp8 instruction
 #pragma unroll
-      for (int st = 0; st < KS; st++) {
-        u32x4 fa[MB], fb[NB];
+        for (int st = 0; st < KS; st += 2) {
+          u32x4 fa[MB][2], fb[NB][2];
 #pragma unroll
-        for (int m = 0; m < MB; m++)
-          fa[m] = *reinterpret_cast<const u32x4*>(base + ((wm * MB + m) * KS + st) * 1024 + 16 * lane);
+          for (int h = 0; h < 2; h++) {
 #pragma unroll
-        for (int q = 0; q < NB; q++) {
-          int j;
-          if (GATEUP) j = q < NB / 2 ? wn * (NB / 2) + q : Sh::BN / 32 + wn * (NB / 2) + (q - NB / 2);
-          else j = wn * NB + q;
-          fb[q] = *reinterpret_cast<const u32x4*>(base + (Sh::kAChunks + j * KS + st) * 1024 + 16 * lane);
+            for (int m = 0; m < MB; m++)
+              fa[m][h] = *reinterpret_cast<const u32x4*>(base + ((wm * MB + m) * KS + st + h) * 1024 + 16 * lane);
+#pragma unroll
+            for (int q = 0; q < NB; q++)
+              fb[q][h] = *reinterpret_cast<const u32x4*>(base + (Sh::kAChunks + bchunk(q) * KS + st + h) * 1024 + 16 * lane);
+          }
+#pragma unroll
+          for (int m = 0; m < MB; m++)
+#pragma unroll
+            for (int q = 0; q < NB; q++) mfma_fp8_k128(acc[m][q], fa[m][0], fa[m][1], fb[q][0], fb[q][1]);
         }
+      } else {
 #pragma unroll
-        for (int m = 0; m < MB; m++)
+        for (int st = 0; st < KS; st++) {
+          u32x4 fa[MB], fb[NB];
 #pragma unroll
-          for (int q = 0; q < NB; q++) mfma_step_t<FP8>(acc[m][q], fa[m], fb[q]);
+          for (int m = 0; m < MB; m++)
+            fa[m] = *reinterpret_cast<const u32x4*>(base + ((wm * MB + m) * KS + st) * 1024 + 16 * lane);
+#pragma unroll
+          for (int q = 0; q < NB; q++)
+            fb[q] = *reinterpret_cast<const u32x4*>(base + (Sh::kAChunks + bchunk(q) * KS + st) * 1024 + 16 * lane);
+#pragma unroll
+          for (int m = 0; m < MB; m++)
+#pragma unroll
+            for (int q = 0; q < NB; q++) mfma_step_t<FP8>(acc[m][q], fa[m], fb[q]);
+        }
       }
       // Stage f+AHEAD goes into the slot of stage f-1, which every wave
       // finished reading before the barrier above.  Issued after this

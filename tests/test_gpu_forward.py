@@ -40,7 +40,7 @@ SMALL = [
     (8, 256, 192, 2, 700, 0.05),
     (8, 192, 320, 2, 700, 0.0),       # H % 128 != 0; fp8 rows of 192 / 320 bytes
     (16, 512, 256, 4, 1500, 0.02),
-    (32, 256, 128, 8, 500, 0.0),      # 256-row tiles about half full
+    (32, 256, 128, 8, 500, 0.0),      # 128-row tiles about full
 ]
 
 
@@ -64,6 +64,56 @@ def test_small_shapes_all_outputs(lib, E, H, I, k, T, p_drop, dtype):
         gsx = wsc[L["x_scale"]:L["x_scale"] + 4 * T].view(torch.float32).numpy()
         assert np.array_equal(gxq, xq), "x e4m3 codes"
         assert np.array_equal(gsx, sx), "x scales"
+    check_tol(out64(out), ref, dtype, "out")
+
+
+# A few dozen to ~80 rows per expert: strips (token rows staged in LDS,
+# weights streamed to registers), with split reductions, ragged last tiles,
+# dropped pairs and more work items than compute units.
+STRIP = [
+    # E, H, I, k, T, p_drop
+    (16, 512, 256, 4, 48, 0.05),      # 32-row tiles
+    (8, 1024, 512, 2, 128, 0.0),      # 64-row tiles, deep K splits
+    (8, 512, 256, 2, 300, 0.02),      # 128-row tiles
+    (64, 1024, 640, 8, 256, 0.02),    # 5 strips of 2I, 20-step down reduction
+    (64, 2048, 512, 4, 512, 0.0),     # more work items than CUs
+]
+
+
+@pytest.mark.parametrize("E,H,I,k,T,p_drop", STRIP)
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_strip_shapes_all_outputs(lib, E, H, I, k, T, p_drop, dtype):
+    L = lib.moe_workspace_layout(T, k, E, H, I, dtype)
+    log(f"strip {dtype} E={E} H={H} I={I} k={k} T={T} tiling={L['tiling']} "
+        f"splits={L['split_k1']},{L['split_k2']}")
+    if dtype == "bf16":
+        assert L["tiling"] == 2
+    wl = custom_workload(E, H, I, k, dtype=dtype, seed=E + H + I + 1)
+    W = device_weights(wl)
+    x, _, _ = make_tokens(wl, T, seed=T + 15)
+    ids = random_ids(T, k, E, seed=T + 16, p_drop=p_drop)
+    w = random_weights_w(T, k, seed=T + 17)
+    out, _, _ = run_gpu(lib, x, ids, w, W, dtype)
+    ref = oracle_rows(x, ids, w, W, dtype)
+    check_tol(out64(out), ref, dtype, "out")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_strip_hot_expert_many_tiles(lib, dtype):
+    # expert 0 in every token's first slot: several row tiles of one expert
+    # share each weight strip
+    E, H, I, k, T = 32, 512, 256, 4, 256
+    assert lib.moe_workspace_layout(T, k, E, H, I, dtype)["tiling"] == 2
+    log(f"strip hot expert {dtype}")
+    wl = custom_workload(E, H, I, k, dtype=dtype, seed=21)
+    W = device_weights(wl)
+    x, _, _ = make_tokens(wl, T, seed=22)
+    ids = random_ids(T, k, E, seed=23)
+    ids[:, 0] = 0
+    w = random_weights_w(T, k, seed=24)
+    out, routing, _ = run_gpu(lib, x, ids, w, W, dtype)
+    assert lib.read_routing(routing, T, k, E, H, I, dtype)["num_tasks"] > E
+    ref = oracle_rows(x, ids, w, W, dtype)
     check_tol(out64(out), ref, dtype, "out")
 
 
