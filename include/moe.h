@@ -214,10 +214,13 @@ int moe_forward_fp8(const void *x, const float *topk_w, const void *routing,
 /* Measurement hook.  When `events` is non-NULL (n >= 10 hipEvent_t
  * handles, host array), every later forward call records events[2*s]
  * before and events[2*s+1] after stage s on its stream, for the stages it
- * runs: 0 activation quantisation (fp8), 1 gate-up GEMM, 2 requantisation
- * (fp8), 3 down GEMM, 4 top-k reduction.  NULL switches it off.  The
- * setting is process-wide and not thread-safe; do not enable it while a
- * forward call is being captured into a graph. */
+ * runs: 0 activation quantisation (fp8), 1 gate-up GEMM, 2 SiLU-and-mul /
+ * requantisation, 3 down GEMM, 4 top-k reduction.  A stage whose two
+ * entries are both NULL is not recorded (each record costs a few
+ * microseconds of stream time); a pair with one NULL entry, or no
+ * non-NULL pair, is an invalid argument.  NULL `events` switches the hook
+ * off.  The setting is process-wide and not thread-safe; do not enable it
+ * while a forward call is being captured into a graph. */
 int moe_set_stage_events(void *const *events, int n);
 
 /* Number of compute units of the current device as cached by the library

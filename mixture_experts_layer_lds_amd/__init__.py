@@ -214,11 +214,14 @@ def moe_forward_fp8(x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, o
 
 
 def moe_set_stage_events(events):
-    """events: list of 10 torch.cuda.Event(enable_timing=True) (already recorded once), or None."""
+    """events: list of 10 entries, each a torch.cuda.Event(enable_timing=True)
+    (already recorded once) or None (stage s is recorded when entries 2s and
+    2s+1 are events), or None to switch the hook off."""
     if events is None:
         _check("moe_set_stage_events", _lib.moe_set_stage_events(None, 0))
         return
-    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event if e is not None else None
+                                             for e in events])
     _check("moe_set_stage_events", _lib.moe_set_stage_events(arr, len(events)))
 
 

@@ -170,6 +170,12 @@ static hipError_t launch_mb(const moe_host::GemmArgs& a, const moe_host::GemmPla
     case 1: hipLaunchKernelGGL((grouped_gemm_kernel<MB, 1, 1, GATHER, FP8>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((grouped_gemm_kernel<MB, 1, 2, GATHER, FP8>), grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL((grouped_gemm_kernel<MB, 1, 4, GATHER, FP8>), grid, block, 0, s, a); break;
+    case 8:
+      if constexpr (MB == 1) {
+        hipLaunchKernelGGL((grouped_gemm_kernel<MB, 1, 8, GATHER, FP8>), grid, block, 0, s, a);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -16,7 +16,7 @@ using moe_host::GemmArgs;
 using moe_host::GemmPlan;
 
 constexpr size_t kNone = ~(size_t)0;
-constexpr long kTargetItems = 2048;   // work items that fill 256 CUs x 8 waves
+constexpr long kTargetItems = 4096;   // two work items per wave of 256 CUs x 8 waves
 // The plan is a fixed function of the sizes (the layout queries run without
 // a device), so it balances work for MI355X's compute-unit count; launches
 // use the device's actual count.
@@ -236,10 +236,12 @@ struct StageScope {
   hipStream_t s;
   int stage;
   StageScope(hipStream_t s_, int st) : s(s_), stage(st) {
-    if (g_events_on) (void)hipEventRecord(static_cast<hipEvent_t>(g_events[2 * stage]), s);
+    if (g_events_on && g_events[2 * stage])
+      (void)hipEventRecord(static_cast<hipEvent_t>(g_events[2 * stage]), s);
   }
   ~StageScope() {
-    if (g_events_on) (void)hipEventRecord(static_cast<hipEvent_t>(g_events[2 * stage + 1]), s);
+    if (g_events_on && g_events[2 * stage + 1])
+      (void)hipEventRecord(static_cast<hipEvent_t>(g_events[2 * stage + 1]), s);
   }
 };
 
@@ -572,10 +574,13 @@ int moe_set_stage_events(void* const* events, int n) {
     return MOE_OK;
   }
   if (n < 10) return MOE_ERR_INVALID_ARG;
-  for (int i = 0; i < 10; i++) {
-    if (!events[i]) return MOE_ERR_INVALID_ARG;
-    g_events[i] = events[i];
+  int pairs = 0;
+  for (int st = 0; st < 5; st++) {
+    if (!events[2 * st] != !events[2 * st + 1]) return MOE_ERR_INVALID_ARG;
+    if (events[2 * st]) pairs++;
   }
+  if (pairs == 0) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < 10; i++) g_events[i] = events[i];
   g_events_on = true;
   return MOE_OK;
 }

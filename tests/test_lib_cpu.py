@@ -128,5 +128,9 @@ def test_stage_event_hook_argument_checks(m):
     arr = (ctypes.c_void_p * 4)(*[1, 2, 3, 4])
     assert lib.moe_set_stage_events(arr, 4) == -1
     arr = (ctypes.c_void_p * 10)(*([1] * 9 + [0]))
-    assert lib.moe_set_stage_events(arr, 10) == -1
+    assert lib.moe_set_stage_events(arr, 10) == -1      # half a pair
+    arr = (ctypes.c_void_p * 10)(*([0] * 10))
+    assert lib.moe_set_stage_events(arr, 10) == -1      # nothing to record
+    arr = (ctypes.c_void_p * 10)(*([0, 0, 1, 2] + [0] * 6))
+    assert lib.moe_set_stage_events(arr, 10) == 0       # gate-up only
     assert lib.moe_set_stage_events(None, 0) == 0
