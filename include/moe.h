@@ -90,7 +90,8 @@ typedef struct {
     int32_t num_pairs;     /* P = T * k */
     int32_t num_experts;   /* E */
     int32_t max_tasks;     /* capacity of the task map */
-    int32_t reserved[10];
+    int32_t max_expert_tiles; /* largest number of tiles of one expert (0 if none) */
+    int32_t reserved[9];
 } moe_routing_header_t;
 
 /* Byte offsets of the parts of a routing buffer (all 16-byte aligned). */

@@ -107,11 +107,15 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   const int esz_t = dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2;
   const int nsteps1 = H * esz_t / 64, nsteps2 = I * esz_t / 64;
   // Few rows per expert (decode): register streaming, tiles of 16 rows.
-  // A few dozen to ~80 rows: strips (token rows in LDS, weights streamed),
+  // A few dozen to ~80 rows (fp8: ~160): strips (token rows in LDS, weights streamed),
   // tiles of about twice the mean rows per active expert so that the usual
   // spread of a uniform routing still fits one tile per expert.  More rows:
   // LDS tiles of both operands.
-  if (avg > 8 && avg <= 80 && (2 * I) % kStripCols == 0 && H % kStripCols == 0) {
+  // Measured crossover to LDS tiles: ~80 rows per expert for bf16 (Qwen2-57B
+  // T=1024: 287 us tiles, 332 us strips) and above 128 for fp8 (DeepSeek-V3
+  // T=4096: 3285 us strips, 3484 us tiles).
+  const long strip_max = dtype == MOE_DTYPE_FP8_W8A8 ? 160 : 80;
+  if (avg > 8 && avg <= strip_max && (2 * I) % kStripCols == 0 && H % kStripCols == 0) {
     // tile height about twice the mean rows per expert
     const int mb = avg <= 16 ? 2 : (avg <= 40 ? 4 : 8);
     long tasks = (P + 16 * mb - 1) / (16 * mb);

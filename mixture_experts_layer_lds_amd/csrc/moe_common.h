@@ -27,6 +27,7 @@ constexpr int kHdrBlockM = 2;
 constexpr int kHdrNumPairs = 3;
 constexpr int kHdrNumExperts = 4;
 constexpr int kHdrMaxTasks = 5;
+constexpr int kHdrMaxExpertTiles = 6;   // largest number of row tiles of one expert
 
 // fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {

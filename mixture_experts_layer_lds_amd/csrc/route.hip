@@ -32,6 +32,15 @@ constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kKeys = kMaxExperts + 1;   // expert ids plus the dropped bucket
 constexpr int kBatch = 8;                // 64-pair steps whose loads are issued together
 
+// Largest of in[0..n) (n >= 0; 0 when empty) by one wave, returned to every lane.
+__device__ int wave_max_tiles(const int* in, int n, int lane) {
+  int m = 0;
+  for (int i = lane; i < n; i += kWave) m = max(m, in[i]);
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, kWave));
+  return m;
+}
+
 // Exclusive prefix sum of in[0..n) into out[0..n) by one wave (n <= 64*64);
 // in and out may alias.  Returns the total to every lane.
 __device__ int wave_exclusive_scan(const int* in, int* out, int n, int lane) {
@@ -76,7 +85,7 @@ route_kernel(const int32_t* __restrict__ ids, int P, int E, int block_m, int max
   __shared__ int s_start[kKeys + 1];
   __shared__ int s_wcount[kRouteWaves][kKeys];
   __shared__ int s_task0[kKeys];
-  __shared__ int s_total_tasks;
+  __shared__ int s_total_tasks, s_max_tiles;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -178,8 +187,12 @@ route_kernel(const int32_t* __restrict__ ids, int P, int E, int block_m, int max
 
   // D. task map
   if (wave == 0) {
+    const int most = wave_max_tiles(s_task0, E, lane);
     const int total = wave_exclusive_scan(s_task0, s_task0, E, lane);
-    if (lane == 0) s_total_tasks = total;
+    if (lane == 0) {
+      s_total_tasks = total;
+      s_max_tiles = most;
+    }
   }
   lds_barrier();
   for (int e = tid; e < E; e += kRouteThreads) {
@@ -202,6 +215,7 @@ route_kernel(const int32_t* __restrict__ ids, int P, int E, int block_m, int max
     else if (tid == kHdrNumPairs) v = P;
     else if (tid == kHdrNumExperts) v = E;
     else if (tid == kHdrMaxTasks) v = max_tasks;
+    else if (tid == kHdrMaxExpertTiles) v = s_max_tiles;
     header[tid] = v;
   }
 }
@@ -297,7 +311,7 @@ route_scan_kernel(int P, int E, int block_m, int max_tasks, int32_t* __restrict_
   __shared__ int s_count[kKeys];
   __shared__ int s_start[kKeys + 1];
   __shared__ int s_task0[kKeys];
-  __shared__ int s_total_tasks;
+  __shared__ int s_total_tasks, s_max_tiles;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int nkeys = E + 1;
   const int nseg = (P + kSegPairs - 1) / kSegPairs;
@@ -327,8 +341,12 @@ route_scan_kernel(int P, int E, int block_m, int max_tasks, int32_t* __restrict_
   }
   lds_barrier();
   if (wave == 0) {
+    const int most = wave_max_tiles(s_task0, E, lane);
     const int total = wave_exclusive_scan(s_task0, s_task0, E, lane);
-    if (lane == 0) s_total_tasks = total;
+    if (lane == 0) {
+      s_total_tasks = total;
+      s_max_tiles = most;
+    }
   }
   lds_barrier();
   for (int e = tid; e < E; e += kRouteThreads) {
@@ -351,6 +369,7 @@ route_scan_kernel(int P, int E, int block_m, int max_tasks, int32_t* __restrict_
     else if (tid == kHdrNumPairs) v = P;
     else if (tid == kHdrNumExperts) v = E;
     else if (tid == kHdrMaxTasks) v = max_tasks;
+    else if (tid == kHdrMaxExpertTiles) v = s_max_tiles;
     header[tid] = v;
   }
 }

@@ -71,23 +71,24 @@ def test_small_shapes_all_outputs(lib, E, H, I, k, T, p_drop, dtype):
 # weights streamed to registers), with split reductions, ragged last tiles,
 # dropped pairs and more work items than compute units.
 STRIP = [
-    # E, H, I, k, T, p_drop
-    (16, 512, 256, 4, 48, 0.05),      # 32-row tiles
-    (8, 1024, 512, 2, 128, 0.0),      # 64-row tiles, deep K splits
-    (8, 512, 256, 2, 300, 0.02),      # 128-row tiles
-    (64, 1024, 640, 8, 256, 0.02),    # 5 strips of 2I, 20-step down reduction
-    (64, 2048, 512, 4, 512, 0.0),     # more work items than CUs
+    # E, H, I, k, T, p_drop, expected tiling (bf16, fp8): 2 strips, 1 LDS tiles,
+    # 0 register streaming (fp8 rows too short for any strip stage split)
+    (16, 512, 256, 4, 48, 0.05, 2, 0),      # 32-row tiles
+    (8, 1024, 512, 2, 128, 0.0, 2, 2),      # 64-row tiles, deep K splits
+    (8, 512, 256, 2, 300, 0.02, 2, 2),      # 128-row tiles
+    (64, 1024, 640, 8, 256, 0.02, 2, 0),    # 5 strips of 2I, 20-step down reduction
+    (64, 2048, 512, 4, 512, 0.0, 2, 2),     # more work items than CUs
+    (16, 512, 256, 4, 512, 0.01, 1, 2),     # 128 rows per expert: LDS tiles on bf16, strips on fp8
 ]
 
 
-@pytest.mark.parametrize("E,H,I,k,T,p_drop", STRIP)
+@pytest.mark.parametrize("E,H,I,k,T,p_drop,til_bf16,til_fp8", STRIP)
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_strip_shapes_all_outputs(lib, E, H, I, k, T, p_drop, dtype):
+def test_strip_shapes_all_outputs(lib, E, H, I, k, T, p_drop, til_bf16, til_fp8, dtype):
     L = lib.moe_workspace_layout(T, k, E, H, I, dtype)
     log(f"strip {dtype} E={E} H={H} I={I} k={k} T={T} tiling={L['tiling']} "
         f"splits={L['split_k1']},{L['split_k2']}")
-    if dtype == "bf16":
-        assert L["tiling"] == 2
+    assert L["tiling"] == (til_bf16 if dtype == "bf16" else til_fp8)
     wl = custom_workload(E, H, I, k, dtype=dtype, seed=E + H + I + 1)
     W = device_weights(wl)
     x, _, _ = make_tokens(wl, T, seed=T + 15)

@@ -46,7 +46,9 @@ def check_route(lib, ids, E, H, I, dtype, what):
     assert np.array_equal(got["tasks"].numpy(), ref["tasks"]), "task map"
     hdr = got["header"].numpy()
     assert hdr[3] == ids.numel() and hdr[4] == E and hdr[5] == got["layout"]["max_tasks"]
-    assert not hdr[6:].any()
+    tiles = np.bincount(ref["tasks"][:, 0], minlength=1) if ref["num_tasks"] else np.zeros(1)
+    assert hdr[6] == int(tiles.max()), "largest number of tiles of one expert"
+    assert not hdr[7:].any()
 
 
 CASES = [(name, T) for name, wl in WORKLOADS.items() for T in wl.Ts]
