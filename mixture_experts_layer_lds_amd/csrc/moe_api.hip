@@ -107,28 +107,35 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   const int esz_t = dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2;
   const int nsteps1 = H * esz_t / 64, nsteps2 = I * esz_t / 64;
   // Few rows per expert (decode): register streaming, tiles of 16 rows.
-  // A few dozen to ~80 rows (fp8: ~160): strips (token rows in LDS, weights streamed),
+  // 9 to ~80 rows (fp8: 3 to ~160): strips (token rows in LDS, weights streamed),
   // tiles of about twice the mean rows per active expert so that the usual
   // spread of a uniform routing still fits one tile per expert.  More rows:
   // LDS tiles of both operands.
   // Measured crossover to LDS tiles: ~80 rows per expert for bf16 (Qwen2-57B
   // T=1024: 287 us tiles, 332 us strips) and above 128 for fp8 (DeepSeek-V3
   // T=4096: 3285 us strips, 3484 us tiles).
+  // The low end likewise: strips from 3 rows on fp8 (DeepSeek-V3 T=128: 1814
+  // us strips, 1942 us streaming), from 9 on bf16 (Mixtral-8x7B T=16: 464 us
+  // streaming, 508 us strips).
   const long strip_max = dtype == MOE_DTYPE_FP8_W8A8 ? 160 : 80;
-  if (avg > 8 && avg <= strip_max && (2 * I) % kStripCols == 0 && H % kStripCols == 0) {
-    // tile height about twice the mean rows per expert
-    const int mb = avg <= 16 ? 2 : (avg <= 40 ? 4 : 8);
-    long tasks = (P + 16 * mb - 1) / (16 * mb);
-    if (tasks < active) tasks = active;
-    Plan q = p;
+  const long strip_min = dtype == MOE_DTYPE_FP8_W8A8 ? 3 : 9;
+  if (avg >= strip_min && avg <= strip_max && (2 * I) % kStripCols == 0 && H % kStripCols == 0) {
+    // Tile height about twice the mean rows per expert; when no strip
+    // configuration divides the reductions at that height, a taller one
+    // (emptier tiles cost MFMA time, which this weight-bound range has spare).
     const bool fp8 = dtype == MOE_DTYPE_FP8_W8A8;
-    if (choose_strip(nsteps1, mb, fp8, tasks * (2L * I / kStripCols), &q.split1, &q.ks1, &q.nbuf1) &&
-        choose_strip(nsteps2, mb, fp8, tasks * ((long)H / kStripCols), &q.split2, &q.ks2, &q.nbuf2)) {
-      q.tiling = kStrips;
-      q.mb = mb;
-      q.block_m = 16 * mb;
-      q.max_tasks = (int)(P / q.block_m + (P < E ? P : E));
-      return q;
+    for (int mb = avg <= 16 ? 2 : (avg <= 40 ? 4 : 8); mb <= 8; mb *= 2) {
+      long tasks = (P + 16 * mb - 1) / (16 * mb);
+      if (tasks < active) tasks = active;
+      Plan q = p;
+      if (choose_strip(nsteps1, mb, fp8, tasks * (2L * I / kStripCols), &q.split1, &q.ks1, &q.nbuf1) &&
+          choose_strip(nsteps2, mb, fp8, tasks * ((long)H / kStripCols), &q.split2, &q.ks2, &q.nbuf2)) {
+        q.tiling = kStrips;
+        q.mb = mb;
+        q.block_m = 16 * mb;
+        q.max_tasks = (int)(P / q.block_m + (P < E ? P : E));
+        return q;
+      }
     }
   }
   const bool tiled = avg > 48;
