@@ -216,33 +216,49 @@ def test_empty_batch_is_a_no_op(lib):
     assert out.shape == (0, 128)
 
 
-def test_graph_capture_replays_match_eager(lib):
-    wl = custom_workload(16, 256, 192, 4, seed=12)
-    W = device_weights(wl)
-    T, k, E, H, I = 33, 4, 16, 256, 192
+@pytest.mark.parametrize("E,H,I,k,T,dtype", [
+    (16, 256, 192, 4, 33, "bf16"),      # register streaming
+    (32, 512, 256, 4, 256, "bf16"),     # strips
+    (32, 512, 256, 4, 256, "fp8"),      # strips, fp8
+    (8, 256, 192, 2, 700, "bf16"),      # LDS tiles
+    (8, 256, 192, 2, 700, "fp8"),       # LDS tiles, fp8 (in-graph clearing of the row amax slots)
+])
+def test_graph_capture_replays_match_eager(lib, E, H, I, k, T, dtype):
+    log(f"graph {dtype} E={E} H={H} I={I} k={k} T={T} "
+        f"tiling={lib.moe_workspace_layout(T, k, E, H, I, dtype)['tiling']}")
+    wl = custom_workload(E, H, I, k, dtype=dtype, seed=12)
+    Wr = device_weights(wl)
     x, _, _ = make_tokens(wl, T, seed=13)
     x = x.cuda()
     ids = random_ids(T, k, E, seed=14).cuda()
     w = random_weights_w(T, k, seed=15).cuda()
-    routing = lib.alloc_routing(T, k, E, H, I)
-    ws = lib.alloc_workspace(T, k, E, H, I)
+    routing = lib.alloc_routing(T, k, E, H, I, dtype)
+    ws = lib.alloc_workspace(T, k, E, H, I, dtype)
     out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
-    Wr = W
-    W = lib.pack_weights(Wr)
+    W = lib.pack_weights(Wr, dtype)
+
+    def chain():
+        if dtype == "bf16":
+            lib.moe_build_routing_bf16(ids, E, H, I, routing)
+            lib.moe_forward_bf16(x, w, routing, W["w1"], W["w2"], ws, out)
+        else:
+            lib.moe_build_routing_fp8(ids, E, H, I, routing)
+            lib.moe_forward_fp8(x, w, routing, W["w1"], W["w1_scale"], W["w2"], W["w2_scale"], ws,
+                                out)
+
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        lib.moe_build_routing_bf16(ids, E, H, I, routing)
-        lib.moe_forward_bf16(x, w, routing, W["w1"], W["w2"], ws, out)
+        chain()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     eager = out.clone()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        lib.moe_build_routing_bf16(ids, E, H, I, routing)
-        lib.moe_forward_bf16(x, w, routing, W["w1"], W["w2"], ws, out)
+        chain()
     # new routing between replays: the captured grids serve any routing
     ids2 = random_ids(T, k, E, seed=16).cuda()
+    ids2[:, 0] = 0                      # and a hot expert: several tiles of one expert
     for rep in range(4):
         out.zero_()
         ws.fill_(0x7F)
@@ -252,8 +268,24 @@ def test_graph_capture_replays_match_eager(lib):
     ids.copy_(ids2)
     g.replay()
     torch.cuda.synchronize()
-    ref2, _, _ = run_gpu(lib, x, ids2, w, Wr, "bf16")
+    ref2, _, _ = run_gpu(lib, x, ids2, w, Wr, dtype)
     assert torch.equal(out, ref2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_strip_all_pairs_dropped(lib, dtype):
+    # a strip-sized batch whose ids all fall outside [0, E): no task, zero output
+    E, H, I, k, T = 32, 512, 256, 4, 256
+    assert lib.moe_workspace_layout(T, k, E, H, I, dtype)["tiling"] == 2
+    wl = custom_workload(E, H, I, k, dtype=dtype, seed=31)
+    W = device_weights(wl)
+    x, _, _ = make_tokens(wl, T, seed=32)
+    ids = torch.full((T, k), E, dtype=torch.int32)
+    ids[::3, 1] = -5
+    w = random_weights_w(T, k, seed=33)
+    out, routing, _ = run_gpu(lib, x, ids, w, W, dtype)
+    assert lib.read_routing(routing, T, k, E, H, I, dtype)["num_tasks"] == 0
+    assert torch.equal(out.float().cpu(), torch.zeros(T, H))
 
 
 @pytest.mark.parametrize("dtype,E,rows,cols", [("bf16", 3, 32, 64), ("bf16", 2, 48, 160),
