@@ -126,6 +126,7 @@ typedef struct {
 typedef struct {
     size_t xq;          /* fp8: uint8 [T][H]   per-token e4m3 codes of x */
     size_t x_scale;     /* fp8: fp32  [T]      per-token scales of x */
+    size_t x_scale_rows;/* fp8, tiling 0: fp32 [P + 16] the token's scale at each sorted row */
     size_t g;           /* tilings 0, 2: fp32 [split_k1][P][2I] gate-up partial
                            sums (fp8: tiling 0 fully scaled, tiling 2 weight
                            scales only); tiling 1 + fp8: fp32 [P][I]

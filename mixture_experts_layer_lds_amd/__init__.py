@@ -50,7 +50,8 @@ class RoutingLayout(ctypes.Structure):
 
 
 class WorkspaceLayout(ctypes.Structure):
-    _fields_ = [("xq", ctypes.c_size_t), ("x_scale", ctypes.c_size_t), ("g", ctypes.c_size_t),
+    _fields_ = [("xq", ctypes.c_size_t), ("x_scale", ctypes.c_size_t),
+                ("x_scale_rows", ctypes.c_size_t), ("g", ctypes.c_size_t),
                 ("h", ctypes.c_size_t), ("h_scale", ctypes.c_size_t), ("y", ctypes.c_size_t),
                 ("total_bytes", ctypes.c_size_t), ("split_k1", ctypes.c_int32),
                 ("split_k2", ctypes.c_int32), ("tiling", ctypes.c_int32)]

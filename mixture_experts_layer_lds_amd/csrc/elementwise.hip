@@ -23,10 +23,12 @@ __device__ __forceinline__ float block_max_256(float v, float* s_red) {
   return r;
 }
 
-// x[T][H] bf16 -> xq[T][H] e4m3 + scale[T]; H % 8 == 0.
+// x[T][H] bf16 -> xq[T][H] e4m3 + scale[T]; H % 8 == 0.  With scale_rows,
+// the token's scale is also written at the sorted row of each of its zk pairs.
 __global__ void __launch_bounds__(kRowThreads)
 quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restrict__ xq,
-                       float* __restrict__ scale, float* __restrict__ zero_rows, int zk) {
+                       float* __restrict__ scale, float* __restrict__ zero_rows, int zk,
+                       const int32_t* __restrict__ pair_pos, float* __restrict__ scale_rows) {
   __shared__ float s_red[4];
   const int t = blockIdx.x;
   if (zero_rows && threadIdx.x < zk) zero_rows[(size_t)t * zk + threadIdx.x] = 0.0f;
@@ -59,6 +61,7 @@ quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restric
     out[i] = q;
   }
   if (threadIdx.x == 0) scale[t] = sc;
+  if (scale_rows && threadIdx.x < zk) scale_rows[pair_pos[(size_t)t * zk + threadIdx.x]] = sc;
 }
 
 // h[r][n] = SiLU(rs * sum_s g[s][r][n]) * (rs * sum_s g[s][r][I + n]) for the
@@ -200,9 +203,10 @@ reduce_kernel(const void* __restrict__ yv, int S, int P, const float* __restrict
 namespace moe_host {
 
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* scale,
-                                  float* zero_rows, int zk, hipStream_t s) {
+                                  float* zero_rows, int zk, const int32_t* pair_pos,
+                                  float* scale_rows, hipStream_t s) {
   hipLaunchKernelGGL(moe::quant_rows_bf16_kernel, dim3(T), dim3(moe::kRowThreads), 0, s, x, H,
-                     xq, scale, zero_rows, zk);
+                     xq, scale, zero_rows, zk, pair_pos, scale_rows);
   return hipGetLastError();
 }
 

@@ -56,6 +56,13 @@ __device__ __forceinline__ i32x16_t load16_scalar(const void* p) {
   return v;
 }
 
+// Scalar load of one wave-uniform dword.
+__device__ __forceinline__ int load1_scalar(const void* p) {
+  int v;
+  __asm__ volatile("s_load_dword %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
 // Lane l receives v[l % 16].
 __device__ __forceinline__ int spread16(const i32x16_t& v, int lane) {
   const int j = lane & 15;

@@ -12,11 +12,9 @@
 
 namespace {
 
-using moe_host::GemmArgs;
-using moe_host::GemmPlan;
 
 constexpr size_t kNone = ~(size_t)0;
-constexpr long kTargetItems = 4096;   // two work items per wave of 256 CUs x 8 waves
+constexpr long kStreamWaves = 2048;   // waves that fill 256 CUs x 8
 // The plan is a fixed function of the sizes (the layout queries run without
 // a device), so it balances work for MI355X's compute-unit count; launches
 // use the device's actual count.
@@ -32,8 +30,9 @@ struct Plan {
   int tiling = kStreaming;
   int bm_t = 128;                // LDS tiles: rows per tile (128 or 256)
   int bn1 = 128, bn2 = 128;      // LDS tiles: N tile of gate-up / down
-  int split1 = 1, unroll1 = 1;   // streaming / strips gate-up: K = H
-  int split2 = 1, unroll2 = 1;   // streaming / strips down:    K = I
+  int split1 = 1, split2 = 1;    // strips: K slices of gate-up (K = H) / down (K = I)
+  int sw1 = 1, su1 = 2;          // streaming gate-up: waves per workgroup, K steps per stage
+  int sw2 = 1, su2 = 2;          // streaming down
   int ks1 = 4, nbuf1 = 4;        // strips: K steps per stage, stages in flight (gate-up)
   int ks2 = 4, nbuf2 = 4;        // (down)
 };
@@ -48,21 +47,37 @@ int check_shape(int T, int k, int E, int H, int I) {
   return MOE_OK;
 }
 
-int choose_unroll(int nsteps, int mb) {
-  const int maxu = mb >= 2 ? 2 : 4;
-  for (int u = maxu; u > 1; u >>= 1)
-    if (nsteps % u == 0) return u;
-  return 1;
-}
-
-// Largest power-of-two K split (<= 16) that keeps >= 2 pipeline groups per
-// slice and stops once the estimated work items reach the target.
-int choose_split(int nsteps, int unroll, long items) {
-  const int groups = nsteps / unroll;
-  int s = 1;
-  while (s < 16 && items * s < kTargetItems && groups % (2 * s) == 0 && groups / (2 * s) >= 2)
-    s *= 2;
-  return s;
+// Register-streaming split of a reduction of nsteps 64-byte steps over the
+// waves of a workgroup for `items` work items, each wave taking a whole
+// number of two-step stages; one-step stages, unsplit, when the steps are
+// odd.
+void choose_stream(int nsteps, int mb, long items, int* waves, int* u) {
+  // Each wave of a launch (kStreamWaves of them) runs whole items in turn, so
+  // a launch lasts (items per workgroup, rounded up) x (K steps per wave +
+  // the latency of an item's first loads, about kItemSteps steps).  The
+  // split that minimises this is taken, the smallest on a tie.
+  constexpr long kItemSteps = 4;
+  int best = 0;
+  long best_cost = 0;
+  for (int w = 1; w <= 8; w *= 2) {
+    if (nsteps % (2 * w) || !moe_host::stream_config_supported(mb, w, 2)) continue;
+    long grid = kStreamWaves / w;
+    if (items < grid) grid = items;
+    if (grid < 1) grid = 1;
+    const long rounds = (items + grid - 1) / grid;
+    const long cost = rounds * (nsteps / w + kItemSteps);
+    if (!best || cost < best_cost) {
+      best = w;
+      best_cost = cost;
+    }
+  }
+  if (best) {
+    *waves = best;
+    *u = 2;
+  } else {
+    *waves = 1;
+    *u = 1;
+  }
 }
 
 // Strip GEMM configuration for a reduction of nsteps 64-byte steps and
@@ -157,10 +172,8 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   long est_tasks = (P + p.block_m - 1) / p.block_m;
   if (est_tasks < active) est_tasks = active;
   if (!tiled) {
-    p.unroll1 = choose_unroll(nsteps1, p.mb);
-    p.unroll2 = choose_unroll(nsteps2, p.mb);
-    p.split1 = choose_split(nsteps1, p.unroll1, est_tasks * (2L * I / 16));
-    p.split2 = choose_split(nsteps2, p.unroll2, est_tasks * ((long)H / 16));
+    choose_stream(nsteps1, p.mb, est_tasks * ((long)I / 16), &p.sw1, &p.su1);
+    choose_stream(nsteps2, p.mb, est_tasks * ((long)H / 32), &p.sw2, &p.su2);
   }
   return p;
 }
@@ -199,17 +212,19 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
   };
   W->xq = fp8 ? take((size_t)T * H) : kNone;
   W->x_scale = fp8 ? take(4 * (size_t)T) : kNone;
-  if (p.tiling == kLdsTiles)
-    W->g = fp8 ? take(4 * P * I) : kNone;               // fp32 SiLU(gate)*up before requant
-  else
+  // per-sorted-row x scales, read 16 at a time by the streaming epilogue
+  W->x_scale_rows = fp8 && p.tiling == kStreaming ? take(4 * (P + 16)) : kNone;
+  if (p.tiling == kStrips)
     W->g = take(4 * (size_t)p.split1 * P * 2 * I);      // fp32 gate-up partial sums
+  else
+    W->g = fp8 ? take(4 * P * I) : kNone;               // fp32 SiLU(gate)*up before requant
   W->h = take(P * I * (fp8 ? 1 : 2));
   W->h_scale = fp8 ? take(4 * P) : kNone;
-  const bool y_bf16 = p.tiling == kLdsTiles || (p.tiling == kStrips && p.split2 == 1);
+  const bool y_bf16 = p.tiling != kStrips || p.split2 == 1;
   W->y = y_bf16 ? take(2 * P * H) : take(4 * (size_t)p.split2 * P * H);
   W->total_bytes = off;
-  W->split_k1 = p.tiling == kLdsTiles ? 1 : p.split1;
-  W->split_k2 = p.tiling == kLdsTiles ? 1 : p.split2;
+  W->split_k1 = p.tiling == kStrips ? p.split1 : 1;
+  W->split_k2 = p.tiling == kStrips ? p.split2 : 1;
   W->tiling = p.tiling;
 }
 
@@ -230,11 +245,11 @@ int cu_count(int* out) {
   return MOE_OK;
 }
 
-int gemm_grid(long max_items, int cus) {
-  long waves = (long)cus * 8;
-  if (max_items < waves) waves = max_items;
-  if (waves < 1) waves = 1;
-  return (int)((waves + 3) / 4);
+// Workgroups of a streaming launch: 8 waves per CU, no more than the items.
+int stream_grid(long max_items, int waves, int cus) {
+  long groups = (long)cus * 8 / waves;
+  if (max_items < groups) groups = max_items;
+  return (int)(groups < 1 ? 1 : groups);
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -324,8 +339,12 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
 
   if (fp8) {
     StageScope st(s, 0);
-    e = moe_host::launch_quant_rows_bf16(static_cast<const uint16_t*>(x), T, H, xq, x_scale,
-                                         p.tiling == kLdsTiles ? h_scale : nullptr, k, s);
+    // the row amax slots are cleared here for the epilogues that fold into
+    // them (LDS tiles, streaming)
+    e = moe_host::launch_quant_rows_bf16(
+        static_cast<const uint16_t*>(x), T, H, xq, x_scale, p.tiling != kStrips ? h_scale : nullptr,
+        k, R.pair_pos, p.tiling == kStreaming ? reinterpret_cast<float*>(ws + W.x_scale_rows) : nullptr,
+        s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (p.tiling == kStrips) {
@@ -446,60 +465,59 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     return MOE_OK;
   }
 
-  float* g = reinterpret_cast<float*>(ws + W.g);
-  float* y = reinterpret_cast<float*>(ws + W.y);
+  // Register streaming: the gate-up epilogue forms SiLU(gate)*up (bf16 h, or
+  // fp32 h + row amax then requantised on fp8); down writes bf16 rows.
+  float* h32 = fp8 ? reinterpret_cast<float*>(ws + W.g) : nullptr;
   {
     StageScope st(s, 1);
-    GemmArgs a{};
+    moe_host::StreamArgs a{};
     a.a = fp8 ? static_cast<const void*>(xq) : x;
-    a.a_scale = x_scale;
     a.b = w1;
     a.b_scale = w1_scale;
+    a.row_scale = fp8 ? reinterpret_cast<const float*>(ws + W.x_scale_rows) : nullptr;
     a.sorted_pairs = R.sorted_pairs;
     a.header = R.header;
     a.tasks = R.tasks;
-    a.c = g;
+    a.c = fp8 ? static_cast<void*>(h32) : h;
+    a.row_amax = h_scale;
     a.K = H;
-    a.N = 2 * I;
-    a.P = P;
+    a.N_out = I;
+    a.w_rows = 2 * I;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    a.split = p.split1;
-    GemmPlan gp{p.mb, 1, p.unroll1, gemm_grid((long)p.max_tasks * (2L * I / 16) * p.split1, cus)};
-    e = moe_host::launch_grouped_gemm(a, true, fp8, gp, s);
+    e = moe_host::launch_stream_gemm(a, true, fp8, p.mb, p.sw1, p.su1,
+                                     stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
-  {
+  if (fp8) {
     StageScope st(s, 2);
-    e = moe_host::launch_act(g, p.split1, P, I, R.expert_offsets, E, fp8, nullptr, nullptr, k, h,
-                             h_scale, s);
+    e = moe_host::launch_requant_rows(h32, P, I, R.expert_offsets, E, static_cast<uint8_t*>(h),
+                                      h_scale, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
     StageScope st(s, 3);
-    GemmArgs a{};
+    moe_host::StreamArgs a{};
     a.a = h;
-    a.a_scale = h_scale;
     a.b = w2;
     a.b_scale = w2_scale;
     a.sorted_pairs = R.sorted_pairs;
     a.header = R.header;
     a.tasks = R.tasks;
-    a.c = y;
+    a.c = ws + W.y;
     a.K = I;
-    a.N = H;
-    a.P = P;
+    a.N_out = H;
+    a.w_rows = H;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    a.split = p.split2;
-    GemmPlan gp{p.mb, 1, p.unroll2, gemm_grid((long)p.max_tasks * (H / 16) * p.split2, cus)};
-    e = moe_host::launch_grouped_gemm(a, false, fp8, gp, s);
+    e = moe_host::launch_stream_gemm(a, false, fp8, p.mb, p.sw2, p.su2,
+                                     stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
     StageScope st(s, 4);
-    e = moe_host::launch_reduce(y, false, p.split2, P, topk_w, R.pair_pos, R.expert_offsets,
-                                nullptr, E, T, k, H, static_cast<uint16_t*>(out), s);
+    e = moe_host::launch_reduce(ws + W.y, true, 1, P, topk_w, R.pair_pos, R.expert_offsets,
+                                fp8 ? h_scale : nullptr, E, T, k, H, static_cast<uint16_t*>(out), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;

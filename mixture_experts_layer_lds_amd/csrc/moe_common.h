@@ -91,6 +91,13 @@ __device__ __forceinline__ void mfma_fp8_k128(f32x4& acc, const u32x4& a0, const
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
+// Max of v over the 16 lanes that share (lane >> 4).
+__device__ __forceinline__ float max16(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
@@ -108,9 +115,12 @@ hipError_t launch_route(const int32_t* ids, int P, int E, int block_m, int max_t
 size_t route_scratch_bytes(int P);
 
 // Per-token e4m3 quantisation of bf16 rows x[T][H]; when zero_rows is not
-// null the same launch also clears zero_rows[0 .. T*zk) (row amax slots).
+// null the same launch also clears zero_rows[0 .. T*zk) (row amax slots);
+// when scale_rows is not null it also writes each token's scale at the
+// sorted rows pair_pos[t*zk + j] of its zk pairs.
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* scale,
-                                  float* zero_rows, int zk, hipStream_t s);
+                                  float* zero_rows, int zk, const int32_t* pair_pos,
+                                  float* scale_rows, hipStream_t s);
 
 // SiLU-and-mul of the gate-up partial sums g[S][P][2I] for the valid sorted
 // rows; writes bf16 h[P][I] (fp8 = false) or e4m3 codes h[P][I] + scales.
@@ -127,36 +137,9 @@ hipError_t launch_reduce(const void* y, bool y_bf16, int S, int P, const float* 
                          const int32_t* pair_pos, const int32_t* expert_offsets, const float* row_scale,
                          int E, int T, int k, int H, uint16_t* out, hipStream_t s);
 
-struct GemmArgs {
-  const void* a;            // gathered: x / xq [T][K]; contiguous: h / hq [P][K]
-  const float* a_scale;     // fp8: per-row scales of a ([T] gathered, [P] contiguous)
-  const void* b;            // per-expert weights [E][N][K], packed by launch_pack
-  const float* b_scale;     // fp8: per-output-channel scales [E][N]
-  const int32_t* sorted_pairs;  // gathered: pair index of each sorted row
-  const int32_t* header;        // routing header (num_tasks at index 0)
-  const moe_task_t* tasks;
-  float* c;                 // fp32 partial sums [S][P][N]
-  int K;                    // reduction length (elements)
-  int N;                    // output columns
-  int P;                    // rows of each partial slice (T*k)
-  int topk;                 // k: a pair index divided by k is its token
-  int max_tasks;
-  int split;                // S: slices of the reduction
-};
-
-struct GemmPlan {
-  int mb;                   // 16-row MFMA blocks per task tile (block_m / 16)
-  int nsub;                 // 16-column MFMA blocks per work item
-  int unroll;               // 64-byte K steps per pipeline stage
-  int grid;                 // workgroups of the persistent launch (4 waves each)
-};
-
 // Byte permutation of W[E][rows][row_bytes] into 1 KiB MFMA-fragment chunks.
 hipError_t launch_pack(const void* w, int E, int rows, int row_bytes, void* packed,
                        hipStream_t s);
-
-hipError_t launch_grouped_gemm(const GemmArgs& a, bool gather, bool fp8, const GemmPlan& plan,
-                               hipStream_t s);
 
 // LDS-tiled grouped GEMM (128-row task tiles).  Gate-up mode writes
 // SiLU(gate)*up (bf16, or fp32 + row amax on the fp8 path); down mode writes
@@ -206,6 +189,32 @@ struct StripArgs {
 bool strip_config_supported(int mb, int ks, int nbuf, bool fp8);
 hipError_t launch_strip_gemm(const StripArgs& a, bool gather, bool fp8, int mb, int ks, int nbuf,
                              int grid, hipStream_t s);
+
+// Register-streaming GEMM with the reduction split over the W waves of a
+// workgroup (few rows per expert).  Gate-up mode writes SiLU(gate)*up (bf16,
+// or fp32 + row amax on fp8); down mode writes bf16 rows (fp8: weight column
+// scale applied, row scale left to the reduction).
+struct StreamArgs {
+  const void* a;                // gate-up: x / xq [T][K] (gathered); down: h / hq [P][K]
+  const void* b;                // packed weights, w_rows rows per expert
+  const float* b_scale;         // fp8: [E][w_rows]
+  const float* row_scale;       // fp8 gate-up: activation scale of each sorted row [P + 16]
+  const int32_t* sorted_pairs;
+  const int32_t* header;
+  const moe_task_t* tasks;
+  void* c;                      // gate-up: h [P][N_out] (bf16, or fp32 on fp8); down: y [P][N_out] bf16
+  float* row_amax;              // fp8 gate-up: [P] atomic-max slots (pre-cleared)
+  int K;                        // reduction length (elements)
+  int N_out;                    // output columns (I for gate-up, H for down)
+  int w_rows;                   // weight rows per expert (2I or H)
+  int topk;
+  int max_tasks;
+};
+
+// (mb, waves, u) = 16-row blocks per tile, waves per workgroup, K steps per stage.
+bool stream_config_supported(int mb, int waves, int u);
+hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int mb, int waves, int u,
+                              int grid, hipStream_t s);
 
 // fp32 rows -> e4m3 codes with the row amax held in h_scale (replaced by the scale).
 hipError_t launch_requant_rows(const float* h32, int P, int I, const int32_t* expert_offsets,

@@ -1,0 +1,293 @@
+// Grouped expert GEMM for few rows per expert (decode and small batches):
+// weights streamed into registers, the reduction split over the waves of a
+// workgroup and summed through LDS, SiLU-and-mul fused into the gate-up
+// epilogue.
+//
+// Same pipeline role as the other grouped GEMMs (HPC-Ops x SGLang blog,
+// section "MoE": gate-up reads tokens through the route index; a persistent
+// grid consumes the per-tile task map; the activation follows the gate-up
+// GEMM).
+//
+//  * Work item = (task tile of 16*MB rows, 32 output columns).  Gate-up: a
+//    16-column block of gate rows of W1 and the matching block of up rows, so
+//    the item holds both halves of its 16 h columns; down: two adjacent
+//    16-column blocks of W2.
+//  * A workgroup of W waves takes one item; wave w reduces K slice w
+//    (nsteps / W 64-byte steps), streaming the item's two packed weight
+//    blocks into registers (1 KiB non-temporal loads, two register stages of
+//    two steps) and reading token rows through the route index (gate-up) or
+//    contiguously (down).  Few rows per expert leave few items, and the split
+//    keeps enough loads in flight; unlike a split over workgroups it needs no
+//    partial sums in memory and no extra kernel to add them.
+//  * The waves' partial sums meet in LDS and are added in ascending wave
+//    order (deterministic).  Gate-up then writes h = SiLU(gate) * up: bf16,
+//    or on fp8 the fp32 values plus each row's amax (an order-independent
+//    atomic max on the non-negative float bits) for the requantisation pass.
+//    Down writes bf16 rows; on fp8 only the weight column scale is applied
+//    there and the row scale by the top-k reduction.
+//  * Per-item metadata (task record, token indices, fp8 scales) comes from
+//    scalar loads.
+#include <type_traits>
+
+#include "lds_dma.h"
+
+namespace moe {
+
+constexpr int kStreamNB = 2;   // 16-column weight blocks per item
+
+template <bool FP8>
+__device__ __forceinline__ void stream_mfma(f32x4& acc, const u32x4& a, const u32x4& b) {
+  if constexpr (FP8) {
+    const i64x2 a2 = __builtin_bit_cast(i64x2, a);
+    const i64x2 b2 = __builtin_bit_cast(i64x2, b);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[0], b2[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[1], b2[1], acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+}
+
+// MB 16-row blocks per task tile, W waves per workgroup (K slices), U
+// 64-byte K steps per register stage.
+template <int MB, int W, int U, bool GATEUP, bool FP8>
+__global__ void __launch_bounds__(W * 64)
+stream_gemm_kernel(moe_host::StreamArgs g) {
+  constexpr int NB = kStreamNB;
+  __shared__ f32x4 red[W][MB][NB][64];   // the waves' partial sums of one item
+  const int lane = threadIdx.x & 63;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
+  const int n_groups = g.N_out / 16 / (GATEUP ? 1 : NB);   // column groups per task
+  const int total = num_tasks * n_groups;
+  const size_t row_bytes = (size_t)g.K * (FP8 ? 1 : 2);
+  const int nsteps = (int)(row_bytes / 64);
+  const int spw = nsteps / W;            // K steps of each wave, a positive multiple of U
+  const int ngroups = spw / U;
+  const int w_blocks = g.w_rows / 16;
+  const char* __restrict__ A = static_cast<const char*>(g.a);
+  const char* __restrict__ B = static_cast<const char*>(g.b);
+
+  // XCD-aware numbering: consecutive items (the column groups of one task)
+  // on the workgroups of one XCD, sharing the task's token rows in L2.
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per_xcd = G / 8, extra = G % 8;
+  const int vid = (xcd < extra ? xcd * (per_xcd + 1) : extra * (per_xcd + 1) + (xcd - extra) * per_xcd) + slot;
+
+  for (int item = vid; item < total; item += G) {
+    const int ti = item / n_groups;
+    const int cg = item - ti * n_groups;
+    const moe_task_t task = load_task_scalar(g.tasks + ti);
+    // weight 16-row blocks of this item
+    int blk[NB];
+    if constexpr (GATEUP) {
+      blk[0] = cg;                      // gate rows [16 cg, 16 cg + 16)
+      blk[1] = g.N_out / 16 + cg;       // the matching up rows
+    } else {
+#pragma unroll
+      for (int q = 0; q < NB; q++) blk[q] = cg * NB + q;
+    }
+    const int step0 = wave * spw;
+    // Rows past the tile re-read the tile's first row: a valid address whose
+    // products land only in rows that are never stored.  The loads stay
+    // unconditional, so the compiler's vmcnt waits count exactly and the
+    // next register stage stays in flight while this one is multiplied (a
+    // load under a branch would make it wait for everything).
+    const char* ap[MB];
+#pragma unroll
+    for (int b = 0; b < MB; b++) {
+      const int rb = b * 16 < task.rows ? b : 0;
+      int arow;
+      if constexpr (GATEUP) {
+        const i32x16_t sp = load16_scalar(g.sorted_pairs + task.row_begin + rb * 16);
+        const int p = rb * 16 + lrow < task.rows ? spread16(sp, lane) : sp[0];
+        arow = p / g.topk;
+      } else {
+        arow = task.row_begin + (rb * 16 + lrow < task.rows ? rb * 16 + lrow : 0);
+      }
+      ap[b] = A + (size_t)arow * row_bytes + (size_t)step0 * 64 + 16 * lgrp;
+    }
+    const char* bp[NB];
+#pragma unroll
+    for (int q = 0; q < NB; q++)
+      bp[q] = B + (((size_t)task.expert * w_blocks + blk[q]) * nsteps + step0) * 1024 + 16 * lane;
+
+    f32x4 acc[MB][NB];
+#pragma unroll
+    for (int m = 0; m < MB; m++)
+#pragma unroll
+      for (int q = 0; q < NB; q++) acc[m][q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    u32x4 fa0[U][MB], fb0[U][NB], fa1[U][MB], fb1[U][NB];
+    auto load = [&](u32x4 (&fa)[U][MB], u32x4 (&fb)[U][NB], int grp) {
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int step = grp * U + u;
+#pragma unroll
+        for (int q = 0; q < NB; q++)
+          fb[u][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp[q] + (size_t)step * 1024));
+#pragma unroll
+        for (int b = 0; b < MB; b++) fa[u][b] = *reinterpret_cast<const u32x4*>(ap[b] + (size_t)step * 64);
+      }
+    };
+    auto compute = [&](const u32x4 (&fa)[U][MB], const u32x4 (&fb)[U][NB]) {
+#pragma unroll
+      for (int u = 0; u < U; u++)
+#pragma unroll
+        for (int b = 0; b < MB; b++)
+#pragma unroll
+          for (int q = 0; q < NB; q++) stream_mfma<FP8>(acc[b][q], fa[u][b], fb[u][q]);
+    };
+    // Two register stages in turn.  No load sits under a condition: the
+    // loop runs whole pairs and the tail (one stage or two) is chosen after
+    // it, so each multiply waits for exactly its own stage while the next
+    // one is in flight.
+    load(fa0, fb0, 0);
+    int grp = 0;
+    for (; grp + 2 < ngroups; grp += 2) {
+      load(fa1, fb1, grp + 1);
+      compute(fa0, fb0);
+      load(fa0, fb0, grp + 2);
+      compute(fa1, fb1);
+    }
+    if (grp + 1 < ngroups) {
+      load(fa1, fb1, grp + 1);
+      compute(fa0, fb0);
+      compute(fa1, fb1);
+    } else {
+      compute(fa0, fb0);
+    }
+
+    // ---- the waves' partial sums meet in LDS (lane-contiguous 16-byte slots)
+#pragma unroll
+    for (int m = 0; m < MB; m++)
+#pragma unroll
+      for (int q = 0; q < NB; q++) red[wave][m][q][lane] = acc[m][q];
+    __syncthreads();
+
+    // Epilogue of row block m by wave m % W: lane holds column (lane % 16)
+    // and rows 4*(lane / 16) + i of each 16 x 16 block.
+    for (int m = wave; m < MB; m += W) {
+      f32x4 tot[NB];
+#pragma unroll
+      for (int q = 0; q < NB; q++) {
+        tot[q] = red[0][m][q][lane];
+#pragma unroll
+        for (int s = 1; s < W; s++) tot[q] += red[s][m][q][lane];
+      }
+      float cs[NB];   // fp8: this lane's weight column scales
+      float rs[4];    // fp8 gate-up: activation scales of this lane's four rows
+#pragma unroll
+      for (int q = 0; q < NB; q++) cs[q] = 1.0f;
+#pragma unroll
+      for (int i = 0; i < 4; i++) rs[i] = 1.0f;
+      if constexpr (FP8) {
+#pragma unroll
+        for (int q = 0; q < NB; q++) {
+          const i32x16_t v = load16_scalar(g.b_scale + (size_t)task.expert * g.w_rows + blk[q] * 16);
+          cs[q] = __int_as_float(spread16(v, lane));
+        }
+        if constexpr (GATEUP) {
+          const int rb = m * 16 < task.rows ? m : 0;
+          const i32x16_t v = load16_scalar(g.row_scale + task.row_begin + rb * 16);
+          const float mine = __int_as_float(spread16(v, lane));
+#pragma unroll
+          for (int i = 0; i < 4; i++) rs[i] = __shfl(mine, 4 * lgrp + i, 64);
+        }
+      }
+      if constexpr (GATEUP) {
+        const int col = cg * 16 + lrow;
+        float hv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float gv = tot[0][i], uv = tot[1][i];
+          if constexpr (FP8) {
+            gv = (gv * rs[i]) * cs[0];
+            uv = (uv * rs[i]) * cs[1];
+          }
+          hv[i] = silu_f32(gv) * uv;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int rr = m * 16 + 4 * lgrp + i;
+          const bool ok = rr < task.rows;
+          if (ok) {
+            const size_t r = (size_t)(task.row_begin + rr);
+            if constexpr (FP8) static_cast<float*>(g.c)[r * g.N_out + col] = hv[i];
+            else static_cast<uint16_t*>(g.c)[r * g.N_out + col] = f32_to_bf16_bits(hv[i]);
+          }
+          if constexpr (FP8) {
+            // row amax over this item's 16 columns, folded into the row's slot
+            const float mx = max16(ok ? __builtin_fabsf(hv[i]) : 0.0f);
+            if (ok && lrow == 0)
+              atomicMax(reinterpret_cast<unsigned int*>(g.row_amax) + task.row_begin + rr,
+                        __float_as_uint(mx));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int rr = m * 16 + 4 * lgrp + i;
+          if (rr < task.rows) {
+            const size_t r = (size_t)(task.row_begin + rr);
+#pragma unroll
+            for (int q = 0; q < NB; q++) {
+              const int col = blk[q] * 16 + lrow;
+              static_cast<uint16_t*>(g.c)[r * g.N_out + col] = f32_to_bf16_bits(tot[q][i] * cs[q]);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();   // LDS free for the next item
+  }
+}
+
+template <int MB, int W, int U, bool GATEUP, bool FP8>
+static hipError_t launch_stream_t(const moe_host::StreamArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((stream_gemm_kernel<MB, W, U, GATEUP, FP8>), dim3(grid), dim3(W * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int MB, int W, int U>
+static hipError_t launch_stream_w(const moe_host::StreamArgs& a, bool gateup, bool fp8, int grid,
+                                  hipStream_t s) {
+  if (gateup) return fp8 ? launch_stream_t<MB, W, U, true, true>(a, grid, s)
+                         : launch_stream_t<MB, W, U, true, false>(a, grid, s);
+  return fp8 ? launch_stream_t<MB, W, U, false, true>(a, grid, s)
+             : launch_stream_t<MB, W, U, false, false>(a, grid, s);
+}
+
+}  // namespace moe
+
+namespace moe_host {
+
+// (16-row blocks per tile, waves per workgroup, K steps per register stage)
+// built here: two-step stages for any split, one-step stages unsplit (odd
+// numbers of K steps).
+#define MOE_STREAM_CONFIGS(X) \
+  X(1, 1, 2) X(1, 2, 2) X(1, 4, 2) X(1, 8, 2) \
+  X(2, 1, 2) X(2, 2, 2) X(2, 4, 2) X(2, 8, 2) \
+  X(4, 1, 2) X(4, 2, 2) X(4, 4, 2) X(4, 8, 2) \
+  X(1, 1, 1) X(2, 1, 1) X(4, 1, 1)
+
+bool stream_config_supported(int mb, int waves, int u) {
+#define MOE_STREAM_CASE(M, Wv, Uv) if (mb == M && waves == Wv && u == Uv) return true;
+  MOE_STREAM_CONFIGS(MOE_STREAM_CASE)
+#undef MOE_STREAM_CASE
+  return false;
+}
+
+hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int mb, int waves, int u,
+                              int grid, hipStream_t s) {
+#define MOE_STREAM_CASE(M, Wv, Uv) \
+  if (mb == M && waves == Wv && u == Uv) return moe::launch_stream_w<M, Wv, Uv>(a, gateup, fp8, grid, s);
+  MOE_STREAM_CONFIGS(MOE_STREAM_CASE)
+#undef MOE_STREAM_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe_host

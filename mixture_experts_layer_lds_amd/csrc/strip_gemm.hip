@@ -3,7 +3,7 @@
 // task tile holds too many token rows for register streaming, which would
 // re-read every row of the tile from L2 once per 16 weight columns.
 //
-// Same pipeline role as grouped_gemm.hip (HPC-Ops x SGLang blog, section
+// Same pipeline role as stream_gemm.hip (HPC-Ops x SGLang blog, section
 // "MoE": gate-up reads tokens through the route index with no separate
 // gather; a persistent grid consumes the per-tile task map).
 //

@@ -1,7 +1,7 @@
 // LDS-tiled grouped expert GEMM for large token counts (many rows per
 // expert), where the layer turns from HBM-bound to MFMA-bound.
 //
-// Same pipeline role as grouped_gemm.hip (HPC-Ops x SGLang blog, section
+// Same pipeline role as stream_gemm.hip (HPC-Ops x SGLang blog, section
 // "MoE": gate-up reads tokens through the route index, persistent grid over
 // the task map), but each workgroup owns a BM x BN output tile of one task
 // and stages its operands through LDS, so every A row and weight column is
@@ -56,13 +56,6 @@ __device__ __forceinline__ void mfma_step_t(f32x4& acc, const u32x4& a, const u3
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
   }
-}
-
-// Max of v over the 16 lanes that share (lane >> 4).
-__device__ __forceinline__ float max16(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
 }
 
 template <int BM, int BN, bool GATEUP, bool FP8>

@@ -53,14 +53,27 @@ def test_routing_layout_sizes(m):
 
 
 def test_workspace_layout(m):
+    # register streaming (DeepSeek-V3 decode): fp32 h rows for the requantisation,
+    # bf16 down rows, per-sorted-row x scales
     W = m.moe_workspace_layout(16, 8, 256, 7168, 2048, "fp8")
     P = 128
+    assert W["tiling"] == 0 and W["split_k1"] == 1 and W["split_k2"] == 1
     assert W["xq"] == 0 and W["x_scale"] >= 16 * 7168
-    assert W["g"] >= W["x_scale"] + 4 * 16
-    assert W["h"] >= W["g"] + 4 * W["split_k1"] * P * 4096
-    assert W["y"] + 4 * W["split_k2"] * P * 7168 <= W["total_bytes"]
-    for key in ("xq", "x_scale", "g", "h", "h_scale", "y"):
+    assert W["x_scale_rows"] >= W["x_scale"] + 4 * 16
+    assert W["g"] >= W["x_scale_rows"] + 4 * (P + 16)
+    assert W["h"] >= W["g"] + 4 * P * 2048
+    assert W["h_scale"] >= W["h"] + P * 2048
+    assert W["y"] >= W["h_scale"] + 4 * P
+    assert W["y"] + 2 * P * 7168 <= W["total_bytes"]
+    for key in ("xq", "x_scale", "x_scale_rows", "g", "h", "h_scale", "y"):
         assert W[key] % 256 == 0
+    # strips (T=1024): fp32 gate-up partial sums, down rows bf16 or fp32 partials
+    S = m.moe_workspace_layout(1024, 8, 256, 7168, 2048, "fp8")
+    P = 8192
+    assert S["tiling"] == 2 and S["x_scale_rows"] == 2 ** 64 - 1
+    assert S["h"] >= S["g"] + 4 * S["split_k1"] * P * 4096
+    ybytes = 2 * P * 7168 if S["split_k2"] == 1 else 4 * S["split_k2"] * P * 7168
+    assert S["y"] + ybytes <= S["total_bytes"]
     Wb = m.moe_workspace_layout(16, 8, 256, 7168, 2048, "bf16")
     assert Wb["xq"] == 2 ** 64 - 1 and Wb["h_scale"] == 2 ** 64 - 1
 
