@@ -118,6 +118,73 @@ def test_strip_hot_expert_many_tiles(lib, dtype):
     check_tol(out64(out), ref, dtype, "out")
 
 
+# Few rows per expert: register streaming, the reduction split over the
+# waves of a workgroup (split chosen from the shape); odd fp8 step counts
+# (one-step stages), 32- and 64-row task tiles, many tasks.
+STREAM = [
+    # E, H, I, k, T, p_drop, 16-row blocks per tile
+    (8, 2048, 768, 2, 4, 0.0, 1),       # decode-like: few items, deep splits
+    (64, 1024, 320, 8, 2, 0.0, 1),
+    (16, 576, 192, 4, 3, 0.0, 1),       # 9 fp8 / 18 bf16 steps
+    (8, 320, 192, 2, 48, 0.05, 2),      # no strip divides H: 32-row tiles
+    (8, 320, 192, 2, 160, 0.02, 4),     # 64-row tiles
+    (128, 2048, 768, 8, 8, 0.0, 1),     # 64 tasks
+]
+
+
+def _hot_first_slot(ids):
+    ids = ids.clone()
+    ids[:, 0] = 0
+    return ids
+
+
+@pytest.mark.parametrize("E,H,I,k,T,p_drop,mb", STREAM)
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_stream_shapes_all_outputs(lib, E, H, I, k, T, p_drop, mb, dtype):
+    L = lib.moe_workspace_layout(T, k, E, H, I, dtype)
+    R = lib.moe_routing_layout(T, k, E, H, I, dtype)
+    log(f"stream {dtype} E={E} H={H} I={I} k={k} T={T} tiling={L['tiling']} block_m={R['block_m']}")
+    assert L["tiling"] == 0 and R["block_m"] == 16 * mb
+    wl = custom_workload(E, H, I, k, dtype=dtype, seed=E + H + I + 2)
+    W = device_weights(wl)
+    x, _, _ = make_tokens(wl, T, seed=T + 25)
+    ids = random_ids(T, k, E, seed=T + 26, p_drop=p_drop)
+    w = random_weights_w(T, k, seed=T + 27)
+    out, _, _ = run_gpu(lib, x, ids, w, W, dtype)
+    ref = oracle_rows(x, ids, w, W, dtype)
+    check_tol(out64(out), ref, dtype, "out")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_stream_repeat_forward_same_routing_bitwise(lib, dtype):
+    # The same routing buffer serves several forwards; the waves' partial
+    # sums are added in a fixed order, so outputs are identical.
+    E, H, I, k, T = 8, 2048, 768, 2, 5
+    wl = custom_workload(E, H, I, k, dtype=dtype, seed=31)
+    W = lib.pack_weights(device_weights(wl), dtype)
+    x, _, _ = make_tokens(wl, T, seed=32)
+    x = x.cuda()
+    ids = _hot_first_slot(random_ids(T, k, E, seed=33)).cuda()
+    w = random_weights_w(T, k, seed=34).cuda()
+    assert lib.moe_workspace_layout(T, k, E, H, I, dtype)["tiling"] == 0
+    routing = lib.alloc_routing(T, k, E, H, I, dtype)
+    ws = lib.alloc_workspace(T, k, E, H, I, dtype)
+    outs = []
+    for rep in range(3):
+        out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+        if rep == 0:
+            (lib.moe_build_routing_bf16 if dtype == "bf16" else lib.moe_build_routing_fp8)(ids, E, H, I, routing)
+        if dtype == "bf16":
+            lib.moe_forward_bf16(x, w, routing, W["w1"], W["w2"], ws, out)
+        else:
+            lib.moe_forward_fp8(x, w, routing, W["w1"], W["w1_scale"], W["w2"], W["w2_scale"], ws, out)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    Wc = {kk: v.cpu() for kk, v in device_weights(wl).items()}
+    check_tol(out64(outs[0]), oracle_rows(x, ids, w, Wc, dtype), dtype, "out")
+
+
 def test_tiny_workload(lib):
     wl = WORKLOADS["tiny"]
     W32 = make_weights(wl)                    # fp32 data, drawn on the host
