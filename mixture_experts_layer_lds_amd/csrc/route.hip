@@ -101,41 +101,45 @@ route_kernel(const int32_t* __restrict__ ids, int P, int E, int block_m, int max
   const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   int* wrow = s_wcount[wave];
 
-  // A. ranks inside the segment (kept in pair_pos until phase C).  The ids
-  // of kBatch consecutive 64-pair steps are loaded together, so one memory
-  // latency covers kBatch steps.
-  for (int b0 = p0; b0 < p1; b0 += kWave * kBatch) {
-    // unconditional loads of a clamped index: a load under a branch gets its
-    // own wait, which would serialise the batch
-    int raw[kBatch], keys[kBatch];
+  // A. ranks inside the segment.  A segment holds at most kBatch 64-pair
+  // steps (P <= kOneGroupPairs), so one batch of loads covers it, and the
+  // keys and ranks stay in registers until phase C.
+  // Unconditional loads of a clamped index (p1 - 1 >= 0 as P >= 1): a load
+  // under a branch gets its own wait, which would serialise the batch.
+  // Waves and 64-pair steps past the pairs skip the work (wave-uniform tests).
+  int keys[kBatch], ranks[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; u++) raw[u] = ids[min(b0 + u * kWave + lane, p1 - 1)];
+  for (int u = 0; u < kBatch; u++) keys[u] = -1;
+  if (p0 < p1) {
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) keys[u] = ids[min(p0 + u * kWave + lane, p1 - 1)];
 #pragma unroll
     for (int u = 0; u < kBatch; u++) {
-      const int p = b0 + u * kWave + lane;
-      const int e = raw[u];
+      const int p = p0 + u * kWave + lane;
+      const int e = keys[u];
       keys[u] = p < p1 ? ((e >= 0 && e < E) ? e : E) : -1;   // -1: beyond the segment
     }
+  }
 #pragma unroll
-    for (int u = 0; u < kBatch; u++) {
-      const int p = b0 + u * kWave + lane;
-      const int key = keys[u];
-      const bool have = key >= 0;
-      uint64_t same = __ballot(have);
+  for (int u = 0; u < kBatch; u++) {
+    ranks[u] = 0;
+    if (p0 + u * kWave >= p1) continue;
+    const int key = keys[u];
+    const bool have = key >= 0;
+    uint64_t same = __ballot(have);
 #pragma unroll
-      for (int bit = 0; bit < 9; bit++) {   // keys < 512
-        const bool set = (key >> bit) & 1;
-        const uint64_t m = __ballot(have && set);
-        same &= set ? m : ~m;
-      }
-      const int below = __popcll(same & lanes_below);
-      int before = 0;
-      if (have) before = wrow[key];
-      __builtin_amdgcn_wave_barrier();      // every lane has read the counter ...
-      if (have && below == 0) wrow[key] = before + __popcll(same);   // ... before its first lane advances it
-      __builtin_amdgcn_wave_barrier();
-      if (have) pair_pos[p] = before + below;
+    for (int bit = 0; bit < 9; bit++) {   // keys < 512
+      const bool set = (key >> bit) & 1;
+      const uint64_t m = __ballot(have && set);
+      same &= set ? m : ~m;
     }
+    const int below = __popcll(same & lanes_below);
+    int before = 0;
+    if (have) before = wrow[key];
+    __builtin_amdgcn_wave_barrier();      // every lane has read the counter ...
+    if (have && below == 0) wrow[key] = before + __popcll(same);   // ... before its first lane advances it
+    __builtin_amdgcn_wave_barrier();
+    ranks[u] = before + below;
   }
   lds_barrier();
 
@@ -158,29 +162,14 @@ route_kernel(const int32_t* __restrict__ ids, int P, int E, int block_m, int max
     expert_offsets[i] = s_start[i];   // key E: number of valid pairs
   }
 
-  // C. scatter (ids and in-segment ranks of kBatch steps loaded together)
-  for (int b0 = p0; b0 < p1; b0 += kWave * kBatch) {
-    int raw[kBatch], keys[kBatch], ranks[kBatch];
+  // C. scatter
 #pragma unroll
-    for (int u = 0; u < kBatch; u++) {
-      const int pc = min(b0 + u * kWave + lane, p1 - 1);
-      raw[u] = ids[pc];
-      ranks[u] = pair_pos[pc];
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; u++) {
-      const int p = b0 + u * kWave + lane;
-      const int e = raw[u];
-      keys[u] = p < p1 ? ((e >= 0 && e < E) ? e : E) : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; u++) {
-      const int p = b0 + u * kWave + lane;
-      if (keys[u] >= 0) {
-        const int r = s_start[keys[u]] + wrow[keys[u]] + ranks[u];
-        sorted_pairs[r] = p;
-        pair_pos[p] = r;
-      }
+  for (int u = 0; u < kBatch; u++) {
+    const int p = p0 + u * kWave + lane;
+    if (p0 + u * kWave < p1 && keys[u] >= 0) {
+      const int r = s_start[keys[u]] + wrow[keys[u]] + ranks[u];
+      sorted_pairs[r] = p;
+      pair_pos[p] = r;
     }
   }
   lds_barrier();
@@ -233,6 +222,8 @@ route_kernel(const int32_t* __restrict__ ids, int P, int E, int block_m, int max
 //            phases B and D above;
 //   scatter: one workgroup per segment: row = base[segment][key] + rank.
 constexpr int kOneGroupPairs = 4096;
+static_assert(kOneGroupPairs <= kRouteWaves * kWave * kBatch,
+              "the one-workgroup build holds each wave's segment in one batch of registers");
 constexpr int kSegThreads = 256;
 constexpr int kSegWaves = kSegThreads / kWave;                 // 4
 constexpr int kSegPairs = kSegWaves * kWave * kBatch;          // 2048: one batch per wave
