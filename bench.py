@@ -60,7 +60,10 @@ def layer_bytes_and_flops(wl, ids, T):
 
 
 def stage_bytes(wl, active, P_valid, T):
-    """Algorithmic bytes each stage must move (its own inputs and outputs)."""
+    """Algorithmic bytes each stage must move: its own inputs and outputs in
+    their minimal form (weights and scales of the active experts once, the
+    activations it reads, SiLU(gate)*up as bf16 or e4m3 codes, down rows as
+    bf16); partial sums and padding rows are not counted."""
     E, H, I = wl.E, wl.H, wl.I
     fp8 = wl.dtype == "fp8"
     bw = 1 if fp8 else 2
@@ -70,11 +73,11 @@ def stage_bytes(wl, active, P_valid, T):
         "routing": P * 4 + P * 12,
         "quant_x": T * H * 2 + T * H + T * 4 if fp8 else 0,
         "gate_up": active * (2 * I * H * bw + (2 * I * 4 if fp8 else 0)) + T * H * bx
-                   + P_valid * 2 * I * 4,
-        "act": P_valid * 2 * I * 4 + P_valid * I * (1 if fp8 else 2),
-        "down": active * (H * I * bw + (H * 4 if fp8 else 0)) + P_valid * I * (1 if fp8 else 2)
-                + P_valid * H * 4,
-        "reduce": P_valid * H * 4 + T * H * 2,
+                   + P_valid * I * bx,
+        "act": P_valid * I * 4 + P_valid * I * bx,
+        "down": active * (H * I * bw + (H * 4 if fp8 else 0)) + P_valid * I * bx
+                + P_valid * H * 2,
+        "reduce": P_valid * H * 2 + T * H * 2,
     }
 
 

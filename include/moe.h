@@ -115,7 +115,9 @@ typedef struct {
 /* Byte offsets of the parts of a forward workspace (all 256-byte aligned);
  * an offset of (size_t)-1 marks a part these sizes do not use.  Three tilings
  * exist, chosen by a fixed function of the sizes and dtype (`tiling`):
- *  0 register streaming (few rows per expert, e.g. decode) and
+ *  0 register streaming (few rows per expert, e.g. decode): the waves of a
+ *    workgroup split each reduction and add their sums in LDS; SiLU(gate)*up
+ *    is formed in the gate-up GEMM's epilogue and the down rows are bf16;
  *  2 strips (token rows staged in LDS, weights streamed to registers; a few
  *    dozen to ~80 rows per expert): the GEMMs may split their reduction into
  *    split_k1 / split_k2 slices whose fp32 partial sums the next kernel adds
@@ -127,18 +129,18 @@ typedef struct {
     size_t xq;          /* fp8: uint8 [T][H]   per-token e4m3 codes of x */
     size_t x_scale;     /* fp8: fp32  [T]      per-token scales of x */
     size_t x_scale_rows;/* fp8, tiling 0: fp32 [P + 16] the token's scale at each sorted row */
-    size_t g;           /* tilings 0, 2: fp32 [split_k1][P][2I] gate-up partial
-                           sums (fp8: tiling 0 fully scaled, tiling 2 weight
-                           scales only); tiling 1 + fp8: fp32 [P][I]
-                           SiLU(gate)*up before requantisation */
+    size_t g;           /* tiling 2: fp32 [split_k1][P][2I] gate-up partial
+                           sums (weight scales only on fp8); tilings 0, 1 +
+                           fp8: fp32 [P][I] SiLU(gate)*up before
+                           requantisation */
     size_t h;           /* bf16 [P][I] SiLU(gate)*up (bf16), or uint8 e4m3 codes [P][I] (fp8) */
     size_t h_scale;     /* fp8: fp32  [P]      per-row scales of h */
-    size_t y;           /* tiling 0, or 2 with split_k2 > 1: fp32 [split_k2][P][H]
-                           unweighted down partial sums; tiling 1, or 2 with
-                           split_k2 == 1: bf16 [P][H] unweighted down rows
-                           (fp8, tiling 2: weight scales only) */
+    size_t y;           /* tiling 2 with split_k2 > 1: fp32 [split_k2][P][H]
+                           unweighted down partial sums; otherwise bf16
+                           [P][H] unweighted down rows (fp8, tilings 0 and 2:
+                           weight scales only) */
     size_t total_bytes; /* minimum size of the workspace */
-    int32_t split_k1;   /* slices of the gate-up reduction over H */
+    int32_t split_k1;   /* slices of the gate-up reduction over H (1 unless tiling 2) */
     int32_t split_k2;   /* slices of the down reduction over I */
     int32_t tiling;     /* 0 register streaming, 1 LDS tiles, 2 strips */
 } moe_workspace_layout_t;
