@@ -139,7 +139,10 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     // configuration divides the reductions at that height, a taller one
     // (emptier tiles cost MFMA time, which this weight-bound range has spare).
     const bool fp8 = dtype == MOE_DTYPE_FP8_W8A8;
-    for (int mb = avg <= 16 ? 2 : (avg <= 40 ? 4 : 8); mb <= 8; mb *= 2) {
+    // heights 2, 4, 8 and 12 row blocks (12 only for fp8, whose strips run to
+    // 160 mean rows: 192-row tiles keep an expert's rows in one tile)
+    const int first = avg <= 16 ? 2 : (avg <= 40 ? 4 : (avg <= 96 || !fp8 ? 8 : 12));
+    for (int mb = first; mb <= 12; mb = mb == 8 ? 12 : mb * 2) {
       long tasks = (P + 16 * mb - 1) / (16 * mb);
       if (tasks < active) tasks = active;
       Plan q = p;
