@@ -174,9 +174,15 @@ def timed_steps(layer, steps, warmup, dom_stage):
     return wall, [a.elapsed_time(b) for a, b in ev]
 
 
-def graph_time_us(layer, weight_sets, reps=50, warmup=10):
-    """Median per-layer time by HIP-graph replay, rotating weight copies so
-    no replay finds the previous one's weights in the caches."""
+def graph_time_us(layer, weight_sets, reps=20, warmup=3, calls=10):
+    """Per-layer time by HIP-graph replay: `calls` layer calls (routing build
+    + forward) captured back to back in one graph, as the tuning guide's
+    benchmark does, each on the next weight copy in turn so that no call
+    finds the weights of the one before in the caches; the replay time
+    divided by `calls`, median (and best) over `reps` replays.  Several calls
+    per graph keep the host's packet submission ahead of the device, which a
+    one-call graph does not: there the first kernels wait several
+    microseconds each for their dispatch packets."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -185,24 +191,22 @@ def graph_time_us(layer, weight_sets, reps=50, warmup=10):
             layer.run(W)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    graphs = []
-    for W in weight_sets:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            layer.run(W)
-        graphs.append(g)
-    for i in range(warmup):
-        graphs[i % len(graphs)].replay()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            layer.run(weight_sets[i % len(weight_sets)])
+    for _ in range(warmup):
+        g.replay()
     torch.cuda.synchronize()
     times = []
-    for i in range(reps):
+    for _ in range(reps):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        graphs[i % len(graphs)].replay()
+        g.replay()
         b.record()
         b.synchronize()
-        times.append(a.elapsed_time(b) * 1000.0)
+        times.append(a.elapsed_time(b) * 1000.0 / calls)
     return statistics.median(times), min(times)
 
 
