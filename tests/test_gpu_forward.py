@@ -122,13 +122,15 @@ def test_strip_hot_expert_many_tiles(lib, dtype):
 # waves of a workgroup (split chosen from the shape); odd fp8 step counts
 # (one-step stages), 32- and 64-row task tiles, many tasks.
 STREAM = [
-    # E, H, I, k, T, p_drop, 16-row blocks per tile
-    (8, 2048, 768, 2, 4, 0.0, 1),       # decode-like: few items, deep splits
-    (64, 1024, 320, 8, 2, 0.0, 1),
-    (16, 576, 192, 4, 3, 0.0, 1),       # 9 fp8 / 18 bf16 steps
-    (8, 320, 192, 2, 48, 0.05, 2),      # no strip divides H: 32-row tiles
-    (8, 320, 192, 2, 160, 0.02, 4),     # 64-row tiles
-    (128, 2048, 768, 8, 8, 0.0, 1),     # 64 tasks
+    # E, H, I, k, T, p_drop, hot expert 0 in every token's first slot,
+    # 16-row blocks per tile
+    (8, 2048, 768, 2, 4, 0.0, False, 1),     # decode-like: few items, deep splits
+    (64, 1024, 320, 8, 2, 0.0, False, 1),
+    (16, 576, 192, 4, 3, 0.0, False, 1),     # 9 fp8 / 18 bf16 steps
+    (8, 320, 192, 2, 48, 0.05, False, 2),    # no strip divides H: 32-row tiles
+    (8, 320, 192, 2, 160, 0.02, False, 4),   # 64-row tiles
+    (8, 320, 192, 2, 160, 0.02, True, 4),    # hot expert: several 64-row tiles of one expert
+    (128, 2048, 768, 8, 8, 0.0, False, 1),   # 64 tasks
 ]
 
 
@@ -138,9 +140,9 @@ def _hot_first_slot(ids):
     return ids
 
 
-@pytest.mark.parametrize("E,H,I,k,T,p_drop,mb", STREAM)
+@pytest.mark.parametrize("E,H,I,k,T,p_drop,hot,mb", STREAM)
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_stream_shapes_all_outputs(lib, E, H, I, k, T, p_drop, mb, dtype):
+def test_stream_shapes_all_outputs(lib, E, H, I, k, T, p_drop, hot, mb, dtype):
     L = lib.moe_workspace_layout(T, k, E, H, I, dtype)
     R = lib.moe_routing_layout(T, k, E, H, I, dtype)
     log(f"stream {dtype} E={E} H={H} I={I} k={k} T={T} tiling={L['tiling']} block_m={R['block_m']}")
@@ -149,8 +151,12 @@ def test_stream_shapes_all_outputs(lib, E, H, I, k, T, p_drop, mb, dtype):
     W = device_weights(wl)
     x, _, _ = make_tokens(wl, T, seed=T + 25)
     ids = random_ids(T, k, E, seed=T + 26, p_drop=p_drop)
+    if hot:
+        ids = _hot_first_slot(ids)
     w = random_weights_w(T, k, seed=T + 27)
-    out, _, _ = run_gpu(lib, x, ids, w, W, dtype)
+    out, routing, _ = run_gpu(lib, x, ids, w, W, dtype)
+    if hot:
+        assert lib.read_routing(routing, T, k, E, H, I, dtype)["num_tasks"] > E
     ref = oracle_rows(x, ids, w, W, dtype)
     check_tol(out64(out), ref, dtype, "out")
 
