@@ -161,6 +161,44 @@ def test_stream_shapes_all_outputs(lib, E, H, I, k, T, p_drop, hot, mb, dtype):
     check_tol(out64(out), ref, dtype, "out")
 
 
+# One token (decode): k from 1 to 16, odd fp8 step counts, dropped pairs, a
+# token whose pairs are all dropped (zero row) and an expert named twice by
+# one token.
+DECODE = [
+    # E, H, I, k
+    (8, 256, 192, 1),
+    (8, 512, 256, 2),
+    (16, 320, 576, 3),      # 9 fp8 steps: one-step stages
+    (64, 1024, 640, 8),
+    (32, 256, 128, 16),
+]
+
+
+@pytest.mark.parametrize("E,H,I,k", DECODE)
+@pytest.mark.parametrize("case", ["plain", "dropped", "all_dropped", "repeated"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_decode_single_token(lib, E, H, I, k, case, dtype):
+    log(f"decode {dtype} E={E} H={H} I={I} k={k} {case}")
+    assert lib.moe_workspace_layout(1, k, E, H, I, dtype)["tiling"] == 0
+    wl = custom_workload(E, H, I, k, dtype=dtype, seed=E + H + I + k)
+    W = device_weights(wl)
+    x, _, _ = make_tokens(wl, 1, seed=k + 40)
+    ids = random_ids(1, k, E, seed=k + 41)
+    if case == "dropped" and k > 1:
+        ids[0, k // 2] = E + 3
+    elif case == "all_dropped":
+        ids[0, :] = -1
+    elif case == "repeated" and k > 1:
+        ids[0, 1] = ids[0, 0]
+    w = random_weights_w(1, k, seed=k + 42)
+    out, _, _ = run_gpu(lib, x, ids, w, W, dtype)
+    ref = oracle_rows(x, ids, w, W, dtype)
+    if case == "all_dropped":
+        assert not out.float().abs().sum().item() and not np.abs(ref).sum()
+    else:
+        check_tol(out64(out), ref, dtype, "out")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_stream_repeat_forward_same_routing_bitwise(lib, dtype):
     # The same routing buffer serves several forwards; the waves' partial
@@ -291,6 +329,8 @@ def test_empty_batch_is_a_no_op(lib):
 
 @pytest.mark.parametrize("E,H,I,k,T,dtype", [
     (16, 256, 192, 4, 33, "bf16"),      # register streaming
+    (16, 256, 192, 4, 1, "bf16"),       # one token
+    (16, 256, 192, 4, 1, "fp8"),
     (32, 512, 256, 4, 256, "bf16"),     # strips
     (32, 512, 256, 4, 256, "fp8"),      # strips, fp8
     (8, 256, 192, 2, 700, "bf16"),      # LDS tiles
