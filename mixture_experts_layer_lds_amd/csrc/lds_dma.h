@@ -35,12 +35,23 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// A wave-uniform address, placed in scalar registers: the compiler may have
+// computed it with vector instructions (under scalar-register pressure), and
+// a scalar load takes its address from scalar registers only.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return reinterpret_cast<const T*>(((unsigned long long)hi << 32) | lo);
+}
+
 // Scalar load of a wave-uniform 16-byte task record.  Its wait is on
 // lgkmcnt, so it does not drain in-flight vector loads as a vector load's
 // vmcnt wait would.
 __device__ __forceinline__ moe_task_t load_task_scalar(const moe_task_t* p) {
   i32x4_t v;
-  __asm__ volatile("s_load_dwordx4 %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  __asm__ volatile("s_load_dwordx4 %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(p)) : "memory");
   moe_task_t t;
   t.expert = v[0];
   t.row_begin = v[1];
@@ -52,14 +63,14 @@ __device__ __forceinline__ moe_task_t load_task_scalar(const moe_task_t* p) {
 // Scalar load of 16 consecutive wave-uniform dwords (64 bytes, 4-byte aligned).
 __device__ __forceinline__ i32x16_t load16_scalar(const void* p) {
   i32x16_t v;
-  __asm__ volatile("s_load_dwordx16 %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  __asm__ volatile("s_load_dwordx16 %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(p)) : "memory");
   return v;
 }
 
 // Scalar load of one wave-uniform dword.
 __device__ __forceinline__ int load1_scalar(const void* p) {
   int v;
-  __asm__ volatile("s_load_dword %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  __asm__ volatile("s_load_dword %0, %1, 0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(uniform_ptr(p)) : "memory");
   return v;
 }
 

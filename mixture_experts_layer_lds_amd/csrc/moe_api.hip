@@ -217,8 +217,8 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
   W->x_scale = fp8 ? take(4 * (size_t)T) : kNone;
   // per-sorted-row x scales, read 16 at a time by the streaming epilogue
   W->x_scale_rows = fp8 && p.tiling == kStreaming ? take(4 * (P + 16)) : kNone;
-  if (p.tiling == kStrips)
-    W->g = take(4 * (size_t)p.split1 * P * 2 * I);      // fp32 gate-up partial sums
+  if (p.tiling == kStrips)   // fp32 gate-up partial sums (none when the bf16 epilogue forms h)
+    W->g = !fp8 && p.split1 == 1 ? kNone : take(4 * (size_t)p.split1 * P * 2 * I);
   else
     W->g = fp8 ? take(4 * P * I) : kNone;               // fp32 SiLU(gate)*up before requant
   W->h = take(P * I * (fp8 ? 1 : 2));
@@ -345,14 +345,19 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     // the row amax slots are cleared here for the epilogues that fold into
     // them (LDS tiles, streaming)
     e = moe_host::launch_quant_rows_bf16(
-        static_cast<const uint16_t*>(x), T, H, xq, x_scale, p.tiling != kStrips ? h_scale : nullptr,
+        static_cast<const uint16_t*>(x), T, H, xq, x_scale,
+        p.tiling != kStrips ? h_scale : nullptr,
         k, R.pair_pos, p.tiling == kStreaming ? reinterpret_cast<float*>(ws + W.x_scale_rows) : nullptr,
         s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (p.tiling == kStrips) {
-    float* g = reinterpret_cast<float*>(ws + W.g);
+    float* g = W.g == kNone ? nullptr : reinterpret_cast<float*>(ws + W.g);
     const bool y_bf16 = p.split2 == 1;
+    // bf16 with one gate-up slice: SiLU-and-mul in the GEMM's epilogue;
+    // else fp32 partial sums that the activation kernel adds (and, on fp8,
+    // requantises).
+    const bool fuse_act = p.split1 == 1 && !fp8;
     {
       StageScope st(s, 1);
       moe_host::StripArgs a{};
@@ -362,7 +367,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
       a.sorted_pairs = R.sorted_pairs;
       a.header = R.header;
       a.tasks = R.tasks;
-      a.c = g;
+      a.c = fuse_act ? h : static_cast<void*>(g);
       a.K = H;
       a.N = 2 * I;
       a.P = P;
@@ -370,10 +375,13 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
       a.max_tasks = p.max_tasks;
       a.split = p.split1;
       a.out_bf16 = 0;
+      a.act = fuse_act ? 1 : 0;
+      a.x_scale = x_scale;
+      a.row_amax = h_scale;
       e = moe_host::launch_strip_gemm(a, true, fp8, p.mb, p.ks1, p.nbuf1, cus, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
-    {
+    if (!fuse_act) {
       StageScope st(s, 2);
       e = moe_host::launch_act(g, p.split1, P, I, R.expert_offsets, E, fp8, x_scale,
                                R.sorted_pairs, k, h, h_scale, s);

@@ -183,6 +183,13 @@ struct StripArgs {
   int max_tasks;
   int split;                    // K slices
   int out_bf16;                 // 1: bf16 rows (split == 1)
+  // gate-up with one K slice: a wave's two 16-row weight blocks are a gate
+  // block and the matching up block, and c receives h = SiLU(gate) * up,
+  // [P][N/2]: bf16, or on fp8 fp32 with each row's amax folded into
+  // row_amax (pre-cleared) and x's per-token scales applied
+  int act;
+  const float* x_scale;         // fp8 act: [T] per-token scales of x
+  float* row_amax;              // fp8 act: [P]
 };
 
 // (mb, ks, nbuf) = 16-row blocks per tile, 64-byte K steps per stage, stages in flight.

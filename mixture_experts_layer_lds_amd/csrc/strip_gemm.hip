@@ -25,10 +25,12 @@
 //    the vector-memory queue holds only the ring's loads and the epilogue's
 //    stores, and the explicit vmcnt waits below count exactly those.
 //
-// Output: fp32 partial sums c[s][P][N], or bf16 rows c[P][N] (one slice,
-// out_bf16).  On fp8 the per-column weight scale is applied here and the
-// per-row activation scale by the consumer (SiLU-and-mul, or the top-k
-// reduction).
+// Output: fp32 partial sums c[s][P][N], bf16 rows c[P][N] (one slice,
+// out_bf16), or on gate-up with one slice h = SiLU(gate) * up (act: the
+// wave's two blocks are a gate block and its up block; fp8 writes fp32 h and
+// each row's amax for the requantisation).  On fp8 the per-column weight
+// scale is applied here, and the per-row activation scale by the consumer
+// (SiLU-and-mul, the top-k reduction) or, with act, here.
 #include <type_traits>
 
 #include "lds_dma.h"
@@ -42,11 +44,18 @@ template <int MB, int KS, int NSUB>
 struct StripItem {
   static constexpr int NA = MB * KS / kStripWaves;   // token chunks this wave copies per stage
   int row_begin, rows, s;
-  int col;                     // first output column of this wave
+  int col;                     // first output column of this wave (of h when fusing SiLU-and-mul)
   const char* a[NA];           // this lane's token sources (K step and lane offsets applied)
   const char* b;               // this lane's packed-weight source of column block 0
   float bs[NSUB];              // fp8: weight scale of this lane's column in each block
 };
+
+// Distance between a wave's column blocks in the packed weights: adjacent
+// blocks, or with SiLU-and-mul fused the gate block and its up block N/2
+// columns further.
+__device__ __forceinline__ size_t strip_block_stride(const moe_host::StripArgs& g, int nsteps) {
+  return (size_t)(g.act ? g.N / 32 : 1) * nsteps * 1024;
+}
 
 template <int MB, int KS, int NSUB, bool GATHER, bool FP8>
 __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::StripArgs& g, int item,
@@ -63,7 +72,7 @@ __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::St
   it.row_begin = task.row_begin;
   it.rows = task.rows;
   it.s = s;
-  it.col = nt * kCols + wave * (NSUB * 16);
+  it.col = g.act ? (nt * kStripWaves + wave) * 16 : nt * kCols + wave * (NSUB * 16);
   const int step0 = s * nk * KS;
   const int lrow = lane & 15;
 #pragma unroll
@@ -92,7 +101,8 @@ __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::St
   for (int q = 0; q < NSUB; q++) {
     it.bs[q] = 1.0f;
     if constexpr (FP8) {
-      const i32x16_t v = load16_scalar(g.b_scale + (size_t)task.expert * g.N + it.col + 16 * q);
+      const int wcol = g.act ? it.col + q * (g.N / 2) : it.col + 16 * q;   // weight row of block q
+      const i32x16_t v = load16_scalar(g.b_scale + (size_t)task.expert * g.N + wcol);
       it.bs[q] = __int_as_float(spread16(v, lane));
     }
   }
@@ -134,6 +144,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
   const size_t row_bytes = (size_t)g.K * (FP8 ? 1 : 2);
   const int nsteps = (int)(row_bytes / 64);
   const int nk = nsteps / (KS * g.split);   // stages per item: a multiple of NBUF, >= NBUF
+  const size_t bq = strip_block_stride(g, nsteps);
 
   // XCD-aware numbering: workgroups are dispatched round-robin over the 8
   // XCDs; give each XCD a contiguous run of items, so the strips of one task
@@ -182,9 +193,9 @@ strip_gemm_kernel(moe_host::StripArgs g) {
         for (int q = 0; q < NSUB; q++)
           if constexpr (NT_B)
             b[u][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                bsrc + ((size_t)q * nsteps + (size_t)kt * KS + u) * 1024));
+                bsrc + q * bq + ((size_t)kt * KS + u) * 1024));
           else
-            b[u][q] = *reinterpret_cast<const u32x4*>(bsrc + ((size_t)q * nsteps + (size_t)kt * KS + u) * 1024);
+            b[u][q] = *reinterpret_cast<const u32x4*>(bsrc + q * bq + ((size_t)kt * KS + u) * 1024);
     };
 
     // The empty asm statements keep each stage's operations together in
@@ -248,22 +259,60 @@ strip_gemm_kernel(moe_host::StripArgs g) {
 
       // Epilogue: lane holds column (lane % 16) and rows 4*(lane / 16) + i of
       // each 16 x 16 block.
+      // SiLU-and-mul in this epilogue (bf16 gate-up, one K slice).  Not on
+      // fp8: there the per-row amax would take one atomic per row and 16
+      // columns (measured slower at DeepSeek-V3 T=4096 than the separate
+      // activation kernel).
+      bool fused = false;
+      if constexpr (GATHER && NSUB == 2 && !FP8) fused = g.act != 0;
+      if (fused) {
+        // h = SiLU(gate) * up: the wave's gate block and its up block
+        const int hn = g.N / 2;
   #pragma unroll
-      for (int m = 0; m < MB; m++) {
+        for (int m = 0; m < MB; m++) {
   #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int rr = 16 * m + 4 * lgrp + i;
-          if (rr < cur.rows) {
-            const size_t r = (size_t)(cur.row_begin + rr);
+          for (int i = 0; i < 4; i++) {
+            const int rr = 16 * m + 4 * lgrp + i;
+            const bool ok = rr < cur.rows;
+            const size_t r = (size_t)(cur.row_begin + (ok ? rr : 0));
+            float gv = acc[m][0][i], uv = acc[m][1][i];
+            if constexpr (FP8) {
+              const float xs = g.x_scale[g.sorted_pairs[r] / g.topk];
+              gv = (gv * cur.bs[0]) * xs;
+              uv = (uv * cur.bs[1]) * xs;
+            }
+            const float hv = silu_f32(gv) * uv;
+            const int col = cur.col + lrow;
+            if (ok) {
+              if constexpr (FP8) static_cast<float*>(g.c)[r * hn + col] = hv;
+              else static_cast<uint16_t*>(g.c)[r * hn + col] = f32_to_bf16_bits(hv);
+            }
+            if constexpr (FP8) {
+              // row amax over these 16 columns, folded into the row's slot
+              const float mx = max16(ok ? __builtin_fabsf(hv) : 0.0f);
+              if (ok && lrow == 0)
+                atomicMax(reinterpret_cast<unsigned int*>(g.row_amax) + r, __float_as_uint(mx));
+            }
+          }
+        }
+      } else {
   #pragma unroll
-            for (int q = 0; q < NSUB; q++) {
-              const int col = cur.col + 16 * q + lrow;
-              float v = acc[m][q][i];
-              if constexpr (FP8) v = v * cur.bs[q];
-              if (g.out_bf16)
-                static_cast<uint16_t*>(g.c)[r * g.N + col] = f32_to_bf16_bits(v);
-              else
-                static_cast<float*>(g.c)[((size_t)cur.s * g.P + r) * g.N + col] = v;
+        for (int m = 0; m < MB; m++) {
+  #pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int rr = 16 * m + 4 * lgrp + i;
+            if (rr < cur.rows) {
+              const size_t r = (size_t)(cur.row_begin + rr);
+  #pragma unroll
+              for (int q = 0; q < NSUB; q++) {
+                const int col = cur.col + 16 * q + lrow;
+                float v = acc[m][q][i];
+                if constexpr (FP8) v = v * cur.bs[q];
+                if (g.out_bf16)
+                  static_cast<uint16_t*>(g.c)[r * g.N + col] = f32_to_bf16_bits(v);
+                else
+                  static_cast<float*>(g.c)[((size_t)cur.s * g.P + r) * g.N + col] = v;
+              }
             }
           }
         }
