@@ -15,6 +15,11 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                                  448 row, power-of-two rows) and torch's cast.
   route                       -- pinned: brute-force stable sort, invariants,
                                  exhaustive tiny cases.
+  router_topk                 -- pinned: closed-form weights (logits log 1..4,
+                                 equal logits, two-expert sigmoid), brute-force
+                                 ranking of every tiny case, softmax of all E
+                                 at k = E, ratio and shift laws, torch's
+                                 stable sort + softmax on random rows.
   forward_f64/f32/bf16        -- pinned: dense fp64 torch matmul references
                                  (k=1, k=E mean, scattered gate matrix),
                                  structural invariants.
@@ -77,6 +82,8 @@ def lib():
             f.argtypes = [P, P, P, P, P, i, i, i, i, i, P, i, P]
         L.oracle_forward_fp8.restype = None
         L.oracle_forward_fp8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P, P, P, P, P]
+        L.oracle_router_topk.restype = None
+        L.oracle_router_topk.argtypes = [P, i, i, i, i, i, P, P]
         L.oracle_num_threads.restype = i
         L.oracle_init()
         _lib = L
@@ -173,6 +180,23 @@ def route(ids, E: int, BM: int):
     n = int(nt[0])
     return {"offsets": offsets, "sorted": srt[:P], "pos": pos[:P], "tasks": tasks[:n].copy(),
             "num_tasks": n, "num_dropped": int(nd[0])}
+
+
+def router_topk(logits, k: int, renormalize: bool = True, n_shared: int = 0):
+    """Router top-k from fp32 logits [T][E]: (ids int32 [T][k+n_shared],
+    weights fp64 [T][k+n_shared]).  Softmax over E, top-k by descending
+    score (ties: lower expert id), optional renormalisation over the k
+    selected, then n_shared shared-expert columns (ids E.., weight 1)."""
+    la = _np(logits, np.float32)
+    T, E = la.shape
+    if not (1 <= k <= E) or n_shared < 0:
+        raise ValueError("need 1 <= k <= E and n_shared >= 0")
+    ncol = k + n_shared
+    ids = np.zeros((T, ncol), dtype=np.int32)
+    w = np.zeros((T, ncol), dtype=np.float64)
+    if T:
+        lib().oracle_router_topk(_p(la), T, E, k, int(bool(renormalize)), n_shared, _p(ids), _p(w))
+    return ids, w
 
 
 def _rows_arg(rows, T):

@@ -390,6 +390,79 @@ void oracle_forward_fp8(const uint16_t *x, const float *topk_w, const int32_t *i
     }
 }
 
+/*
+ * Router top-k (HPC-Ops x SGLang blog, section "Router GEMM: balancing
+ * routing precision and throughput": the router's fp32 expert scores feed
+ * a top-k choice that decides which experts run; SGLang fused-MoE tuning
+ * guide, section on model-config parsing: shared experts fused into the
+ * expert tensor as extra expert ids).  The steps, in order, for one token:
+ *
+ *  1. softmax over all E scores: p_e = exp(l_e - max) / sum_e' exp(l_e' - max);
+ *  2. top-k: the k experts of largest p_e, listed by descending p_e, equal
+ *     scores by ascending expert id.  Softmax is strictly increasing in the
+ *     logit, so the ranking is made on the fp32 logits themselves: ranking
+ *     the rounded probabilities would invent ties that the exact softmax
+ *     does not have;
+ *  3. renormalise (when asked): w_j = p_j / sum of the k selected p;
+ *     otherwise w_j = p_j;
+ *  4. shared experts: n_shared extra columns j = k .. k+n_shared-1 hold
+ *     expert ids E, E+1, ... with weight 1 (every token runs them, and
+ *     their output adds to the routed mixture unscaled).
+ *
+ * A NaN logit ranks as -infinity.  Weights are exact fp64 arithmetic on
+ * the fp32 inputs; they are meaningful only when the selected logits are
+ * finite.  ids is [T][k+n_shared], w is [T][k+n_shared] fp64.
+ */
+static double rank_value(float v) { return isnan(v) ? -INFINITY : (double)v; }
+
+void oracle_router_topk(const float *logits, int T, int E, int k, int renormalize,
+                        int n_shared, int32_t *ids, double *w)
+{
+    const int ncol = k + n_shared;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; t++) {
+        const float *l = logits + (size_t)t * E;
+        double *p = malloc(sizeof(double) * (size_t)E);
+        char *taken = calloc((size_t)E, 1);
+        double mx = -INFINITY;
+        for (int e = 0; e < E; e++)
+            if (rank_value(l[e]) > mx)
+                mx = rank_value(l[e]);
+        double total = 0.0;
+        for (int e = 0; e < E; e++) {
+            p[e] = exp(rank_value(l[e]) - mx);
+            total += p[e];
+        }
+        for (int e = 0; e < E; e++)
+            p[e] /= total;
+        int32_t *row_ids = ids + (size_t)t * ncol;
+        double *row_w = w + (size_t)t * ncol;
+        double sel_sum = 0.0;
+        for (int j = 0; j < k; j++) {   /* selection: best remaining, lowest id on ties */
+            int best = -1;
+            for (int e = 0; e < E; e++) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || rank_value(l[e]) > rank_value(l[best]))
+                    best = e;
+            }
+            taken[best] = 1;
+            row_ids[j] = best;
+            row_w[j] = p[best];
+            sel_sum += p[best];
+        }
+        if (renormalize)
+            for (int j = 0; j < k; j++)
+                row_w[j] /= sel_sum;
+        for (int s = 0; s < n_shared; s++) {
+            row_ids[k + s] = E + s;
+            row_w[k + s] = 1.0;
+        }
+        free(p);
+        free(taken);
+    }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
