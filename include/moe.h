@@ -26,7 +26,9 @@
  *    calls can be captured into a HIP graph.  Grids depend only on the
  *    host-side sizes, so one capture serves any routing at those sizes.
  *  - Shapes: T tokens (0 <= T, T*k <= 65536), k experts per token
- *    (1..16), E experts (1..256), hidden size H and expert intermediate
+ *    (1..16), E experts (1..511: the keys of the routing sort, expert ids
+ *    plus one dropped bucket, are nine bits wide; fused shared experts
+ *    count as experts), hidden size H and expert intermediate
  *    size I (positive multiples of 64, at most 65536).
  *  - Layouts (row-major, last index contiguous):
  *      x        [T][H]      bf16 hidden states
@@ -188,6 +190,27 @@ int moe_build_routing_bf16(const int32_t *topk_ids, int T, int k, int E, int H, 
                            void *routing, size_t routing_bytes, void *stream);
 int moe_build_routing_fp8(const int32_t *topk_ids, int T, int k, int E, int H, int I,
                           void *routing, size_t routing_bytes, void *stream);
+
+/* Router top-k (blog section "Router GEMM": the router's fp32 expert
+ * scores decide, through a top-k choice, which experts run; SGLang tuning
+ * guide, model-config section: shared experts fused into the expert tensor
+ * as extra expert ids).  The step before the routing build: from logits
+ * (device) fp32 [T][E], for each token, softmax over the E scores, the k
+ * largest in descending order (equal scores: ascending expert id; a NaN
+ * logit ranks as -infinity), their weights renormalised to sum to one
+ * (renormalize = 1) or left as softmax probabilities over all E
+ * (renormalize = 0), then n_shared columns for the fused shared experts:
+ * ids E .. E+n_shared-1 with weight 1.  Writes topk_ids (device) int32
+ * [T][k+n_shared] and topk_w (device) fp32 [T][k+n_shared], which the
+ * routing build and the forward pass take with k' = k+n_shared and
+ * E' = E+n_shared (expert E+s is the s-th shared expert's weights).
+ * The ranking compares the fp32 logits exactly, so the ids are a
+ * deterministic function of the input; weights are fp32 and meaningful
+ * when the selected logits are finite.  Requires 1 <= k <= E <= 256,
+ * n_shared >= 0, k + n_shared <= 16, E + n_shared <= 511, renormalize in
+ * {0, 1}; buffers 4-byte aligned.  T == 0 returns MOE_OK with no launch. */
+int moe_router_topk(const float *logits, int T, int E, int k, int renormalize, int n_shared,
+                    int32_t *topk_ids, float *topk_w, void *stream);
 
 /* bf16 forward (blog section "MoE", gate-up & activation, PDL chaining;
  * operator table: BF16 hidden states).  x (device) bf16 [T][H]; topk_w

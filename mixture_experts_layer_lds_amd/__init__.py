@@ -10,6 +10,7 @@ Functions carry the C names:
     moe_pack_weights(w, dtype)                          -> packed copy (one-time)
     moe_routing_layout(T, k, E, H, I, dtype)            -> dict (host only)
     moe_workspace_layout(T, k, E, H, I, dtype)          -> dict (host only)
+    moe_router_topk(logits, k, renormalize, n_shared)    -> (topk_ids, topk_w)
     moe_build_routing_bf16(topk_ids, E, H, I, routing)  -> None
     moe_build_routing_fp8(topk_ids, E, H, I, routing)   -> None
     moe_forward_bf16(x, topk_w, routing, w1, w2, workspace, out) -> out
@@ -58,7 +59,7 @@ class WorkspaceLayout(ctypes.Structure):
 
 
 EXPORTS = ("moe_status_string", "moe_pack_weights", "moe_routing_layout", "moe_workspace_layout",
-           "moe_build_routing_bf16", "moe_build_routing_fp8", "moe_forward_bf16",
+           "moe_router_topk", "moe_build_routing_bf16", "moe_build_routing_fp8", "moe_forward_bf16",
            "moe_forward_fp8", "moe_set_stage_events", "moe_device_cu_count")
 
 
@@ -79,6 +80,8 @@ def _load():
         f = getattr(L, n)
         f.restype = i
         f.argtypes = [P, i, i, i, i, i, P, sz, P]
+    L.moe_router_topk.restype = i
+    L.moe_router_topk.argtypes = [P, i, i, i, i, i, P, P, P]
     L.moe_forward_bf16.restype = i
     L.moe_forward_bf16.argtypes = [P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
     L.moe_forward_fp8.restype = i
@@ -154,6 +157,27 @@ def alloc_routing(T, k, E, H, I, dtype="bf16", device="cuda"):
 def alloc_workspace(T, k, E, H, I, dtype="bf16", device="cuda"):
     n = moe_workspace_layout(T, k, E, H, I, dtype)["total_bytes"]
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_router_topk(logits, k, renormalize=True, n_shared=0, topk_ids=None, topk_w=None,
+                    stream=None):
+    """Router top-k of fp32 logits [T][E] into (topk_ids int32, topk_w fp32),
+    both [T][k + n_shared]; the last n_shared columns are the fused shared
+    experts (ids E.., weight 1)."""
+    if logits.dtype != torch.float32 or logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous fp32 [T][E] tensor")
+    T, E = logits.shape
+    ncol = k + n_shared
+    if topk_ids is None:
+        topk_ids = torch.empty(T, ncol, dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, ncol, dtype=torch.float32, device=logits.device)
+    _check_tensor("topk_ids", topk_ids, torch.int32, (T, ncol))
+    _check_tensor("topk_w", topk_w, torch.float32, (T, ncol))
+    _check("moe_router_topk", _lib.moe_router_topk(
+        _ptr(logits), T, E, k, int(bool(renormalize)), n_shared, _ptr(topk_ids), _ptr(topk_w),
+        _stream(stream)))
+    return topk_ids, topk_w
 
 
 def _shape_tk(topk_ids):

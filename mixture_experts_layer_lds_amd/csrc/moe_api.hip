@@ -593,6 +593,21 @@ int moe_build_routing_fp8(const int32_t* topk_ids, int T, int k, int E, int H, i
                        stream);
 }
 
+int moe_router_topk(const float* logits, int T, int E, int k, int renormalize, int n_shared,
+                    int32_t* topk_ids, float* topk_w, void* stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E || n_shared < 0 || (renormalize != 0 && renormalize != 1))
+    return MOE_ERR_INVALID_ARG;
+  if (E > moe_host::router_max_experts() || k + n_shared > moe::kMaxTopK ||
+      E + n_shared > moe::kMaxExperts)
+    return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARG;
+  const hipError_t e = moe_host::launch_router_topk(logits, T, E, k, renormalize, n_shared, topk_ids,
+                                                    topk_w, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 int moe_forward_bf16(const void* x, const float* topk_w, const void* routing, const void* w1,
                      const void* w2, int T, int k, int E, int H, int I, void* workspace,
                      size_t workspace_bytes, void* out, void* stream) {

@@ -17,7 +17,7 @@ typedef long i64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kMaxPairs = 65536;
-constexpr int kMaxExperts = 256;
+constexpr int kMaxExperts = 511;   // keys of the routing sort (ids and the dropped bucket) fit nine bits
 constexpr int kMaxTopK = 16;
 
 // Routing-buffer header fields (int32 index into the 64-byte header).
@@ -108,6 +108,12 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // Host-side launch helpers implemented by the kernel translation units.
 namespace moe_host {
+
+// Router top-k over fp32 logits[T][E] into ids/w [T][k + n_shared].
+hipError_t launch_router_topk(const float* logits, int T, int E, int k, int renorm, int n_shared,
+                              int32_t* ids, float* w, hipStream_t s);
+// Largest E the router kernel takes.
+int router_max_experts();
 
 hipError_t launch_route(const int32_t* ids, int P, int E, int block_m, int max_tasks,
                         void* routing, const moe_routing_layout_t& L, hipStream_t s);

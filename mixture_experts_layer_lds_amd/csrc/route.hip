@@ -92,7 +92,7 @@ route_kernel(const int32_t* __restrict__ ids, int P, int E, int block_m, int max
   const int wave = tid >> 6;
   const int nkeys = E + 1;
 
-  for (int i = tid; i < kRouteWaves * kKeys; i += kRouteThreads) (&s_wcount[0][0])[i] = 0;
+  for (int kk = lane; kk < nkeys; kk += kWave) s_wcount[wave][kk] = 0;   // a wave's own row
   lds_barrier();
 
   // segment of this wave: a multiple of 64 pairs
@@ -235,7 +235,7 @@ route_count_kernel(const int32_t* __restrict__ ids, int P, int E, int32_t* __res
   __shared__ int s_w[kSegWaves][kKeys];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int nkeys = E + 1;
-  for (int i = tid; i < kSegWaves * kKeys; i += kSegThreads) (&s_w[0][0])[i] = 0;
+  for (int kk = lane; kk < nkeys; kk += kWave) s_w[wave][kk] = 0;   // a wave's own row
   lds_barrier();
   const int p0 = blockIdx.x * kSegPairs + wave * kWave * kBatch;
   const int pend = min(P, (int)(blockIdx.x + 1) * kSegPairs);

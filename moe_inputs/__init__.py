@@ -114,14 +114,44 @@ def route_from_logits(logits: torch.Tensor, k: int, force_expert0_even: bool = F
     return ids.to(torch.int32).contiguous(), w.contiguous()
 
 
-def make_tokens(wl: Workload, T: int, device="cpu", seed: Optional[int] = None):
-    """x [T][H] (fp32 for the tiny case, else bf16), topk_ids, topk_w."""
+def make_router_inputs(wl: Workload, T: int, device="cpu", seed: Optional[int] = None):
+    """x [T][H] fp32 and the router logits [T][E] fp32 of a workload's token
+    batch (the same draws make_tokens routes from)."""
     s = (1000 * wl.seed + T) if seed is None else seed
     g = _gen(s, device)
     x = torch.randn(T, wl.H, generator=g, device=device, dtype=torch.float32)
     logits = torch.randn(T, wl.E, generator=g, device=device, dtype=torch.float32)
     if wl.routing == "biased":
         logits = logits + expert_bias(wl.E, wl.seed).to(device)
+    return x, logits.contiguous()
+
+
+LOGIT_KINDS = ("normal", "ties", "const", "wide", "nan")
+
+
+def router_logits(T: int, E: int, seed: int, kind: str = "normal") -> torch.Tensor:
+    """Synthetic fp32 router logits [T][E] (CPU) of one of these recipes:
+    normal N(0, 1); ties: N(0, 1) rounded to multiples of 1/4 (many equal
+    scores per row); const: every score 0.5; wide: N(0, 1) * 1e30; nan:
+    N(0, 1) with about 5% of the scores NaN."""
+    g = _gen(seed, "cpu")
+    l = torch.randn(T, E, generator=g, dtype=torch.float32)
+    if kind == "ties":
+        l = torch.round(l * 4) / 4
+    elif kind == "const":
+        l = torch.full((T, E), 0.5, dtype=torch.float32)
+    elif kind == "wide":
+        l = l * 1e30
+    elif kind == "nan":
+        l = torch.where(torch.rand(T, E, generator=g) < 0.05, torch.full_like(l, float("nan")), l)
+    elif kind != "normal":
+        raise ValueError(kind)
+    return l.contiguous()
+
+
+def make_tokens(wl: Workload, T: int, device="cpu", seed: Optional[int] = None):
+    """x [T][H] (fp32 for the tiny case, else bf16), topk_ids, topk_w."""
+    x, logits = make_router_inputs(wl, T, device, seed)
     ids, w = route_from_logits(logits.cpu(), wl.k, force_expert0_even=(wl.routing == "hot0"))
     if wl.dtype != "f32":
         x = x.to(torch.bfloat16)

@@ -80,7 +80,7 @@ def test_workspace_layout(m):
 
 @pytest.mark.parametrize("args,code", [
     ((-1, 2, 8, 128, 64), -1), ((4, 0, 8, 128, 64), -1), ((4, 17, 8, 128, 64), -1),
-    ((4, 2, 0, 128, 64), -1), ((4, 2, 257, 128, 64), -1), ((4, 2, 8, 0, 64), -1),
+    ((4, 2, 0, 128, 64), -1), ((4, 2, 512, 128, 64), -1), ((4, 2, 8, 0, 64), -1),
     ((4, 2, 8, 96, 64), -2), ((4, 2, 8, 128, 100), -2), ((8193, 8, 8, 128, 64), -2),
     ((4, 2, 8, 128 * 1024, 64), -2),
 ])
@@ -133,6 +133,44 @@ def test_calls_reject_bad_arguments_without_launching(m):
     a = list(fargs)
     a[13] = Wf - 1
     assert lib.moe_forward_fp8(*a) == -3
+
+
+def test_expert_limit_is_nine_bit_keys(m):
+    # 511 experts plus the dropped bucket: the routing sort's keys fit nine bits
+    L = m.RoutingLayout()
+    assert m._lib.moe_routing_layout(4, 2, 511, 128, 64, 0, ctypes.byref(L)) == 0
+    assert m._lib.moe_routing_layout(4, 2, 257, 128, 64, 1, ctypes.byref(L)) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 8, 2, 1, 0), -1),     # T < 0
+    ((4, 0, 1, 1, 0), -1),      # E < 1
+    ((4, 8, 0, 1, 0), -1),      # k < 1
+    ((4, 8, 9, 1, 0), -1),      # k > E
+    ((4, 8, 2, 2, 0), -1),      # renormalize not 0/1
+    ((4, 8, 2, 1, -1), -1),     # n_shared < 0
+    ((4, 257, 8, 1, 0), -2),    # E beyond one wave's 256 logits
+    ((4, 64, 16, 1, 1), -2),    # k + n_shared > 16
+    ((4, 256, 8, 1, 256), -2),  # k + n_shared > 16 (and E + n_shared > 511)
+])
+def test_router_rejects_bad_arguments(m, args, code):
+    lib = m._lib
+    fake = ctypes.c_void_p(4096)
+    T, E, k, renorm, ns = args
+    assert lib.moe_router_topk(fake, T, E, k, renorm, ns, fake, fake, None) == code
+
+
+def test_router_pointer_checks(m):
+    lib = m._lib
+    fake = ctypes.c_void_p(4096)
+    odd = ctypes.c_void_p(4098)
+    assert lib.moe_router_topk(None, 4, 8, 2, 1, 0, fake, fake, None) == -1
+    assert lib.moe_router_topk(fake, 4, 8, 2, 1, 0, None, fake, None) == -1
+    assert lib.moe_router_topk(fake, 4, 8, 2, 1, 0, fake, None, None) == -1
+    assert lib.moe_router_topk(odd, 4, 8, 2, 1, 0, fake, fake, None) == -1
+    assert lib.moe_router_topk(fake, 4, 8, 2, 1, 0, fake, odd, None) == -1
+    # T == 0: no launch, null pointers accepted
+    assert lib.moe_router_topk(None, 0, 8, 2, 1, 1, None, None, None) == 0
 
 
 def test_stage_event_hook_argument_checks(m):
