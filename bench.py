@@ -242,6 +242,11 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (3 times); under rocprofv3 "
                          "--pmc it gives the FETCH_SIZE/WRITE_SIZE a copy of known size reads")
+    ap.add_argument("--router", action="store_true",
+                    help="measure the router top-k kernel (the step before the routing build) over "
+                         "the workload's token grid instead of the layer")
+    ap.add_argument("--shared", type=int, default=0,
+                    help="with --router: fused shared experts appended to each token's top-k")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -265,6 +270,9 @@ def main():
         log("[bench] copy calibration: 3 x 1 GiB device copies done")
         return
     wl = WORKLOADS[args.workload]
+    if args.router:
+        router_bench(moe, wl, args)
+        return
     dtype = "fp8" if wl.dtype == "fp8" else "bf16"
     T = args.tokens
     log(f"[bench] workload={wl.name} T={T} dtype={dtype}: generating weights")
@@ -376,6 +384,75 @@ def main():
         "sweep": sweep,
     }
     print(json.dumps(rec), flush=True)
+
+
+def router_bench(moe, wl, args):
+    """Router top-k over fp32 logits [T][E]: per T of the workload's grid, the
+    time per call of a 10-call HIP graph replay (HIP events around each replay
+    on the launch stream, median of 20), i.e. the launch duration of the kernel
+    in a chain of dependent launches.  (Events around single eager launches
+    would time the host's launch path instead.)  Algorithmic bytes per call:
+    the logits read once (T*E*4) and ids + weights written once
+    (T*(k+shared)*8)."""
+    import torch
+    import oracle
+    from moe_inputs import make_router_inputs
+    k, ns = wl.k, args.shared
+    sweep = []
+    for T in wl.Ts:
+        _, logits = make_router_inputs(wl, T)
+        dev = logits.cuda()
+        ids = torch.empty(T, k + ns, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, k + ns, dtype=torch.float32, device="cuda")
+        nbytes = T * wl.E * 4 + T * (k + ns) * 8
+
+        def call():
+            moe.moe_router_topk(dev, k, True, ns, topk_ids=ids, topk_w=w)
+
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            call()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for _ in range(10):
+                call()
+        times = []
+        for _ in range(20):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1000.0 / 10)
+        gr_us = statistics.median(times)
+        sweep.append({"T": T, "us_per_call": round(gr_us, 2), "algorithmic_bytes": nbytes,
+                      "GBs": round(nbytes / (gr_us * 1e-6) / 1e9, 1),
+                      "hbm_frac": round(nbytes / (gr_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+        log(f"[bench] router T={T}: {gr_us:.2f} us/call")
+        del g
+    cpu = None
+    if not args.no_cpu_baseline:
+        T = wl.Ts[-1]
+        _, logits = make_router_inputs(wl, T)
+        la = logits.numpy()
+        oracle.router_topk(la, k, True, ns)
+        t0 = time.perf_counter()
+        reps = 5
+        for _ in range(reps):
+            oracle.router_topk(la, k, True, ns)
+        sec = (time.perf_counter() - t0) / reps
+        cpu = {"value": round(sec * 1e6, 1), "unit": "us per call", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": f"T={T}, fp64 C oracle, mean of {reps} calls"}
+    print(json.dumps({"metric": "router top-k us per call + algorithmic GB/s, 1 GPU",
+                      "workload": wl.label, "E": wl.E, "k": k, "n_shared": ns,
+                      "dtype": "f32", "data": "synthetic (the workload's seeded router logits)",
+                      "sweep": sweep, "cpu_baseline": cpu}), flush=True)
 
 
 def counted_traffic(stage, workload, T):
