@@ -149,6 +149,24 @@ def router_logits(T: int, E: int, seed: int, kind: str = "normal") -> torch.Tens
     return l.contiguous()
 
 
+def router_weight(N: int, K: int, seed: int, std: float = 0.02) -> torch.Tensor:
+    """fp32 router weights [N][K] ~ N(0, std^2) (a typical router init), CPU."""
+    g = _gen(seed, "cpu")
+    return (torch.randn(N, K, generator=g, dtype=torch.float32) * std).contiguous()
+
+
+def router_hidden(T: int, K: int, seed: int) -> torch.Tensor:
+    """bf16 hidden states [T][K] for the router: N(0, 1) per channel, with eight
+    outlier channels scaled by 30-60 (LLM residual streams carry a few such
+    channels; they are what makes the low mantissa bits of the router weights
+    matter).  CPU."""
+    g = _gen(seed, "cpu")
+    scale = torch.ones(K)
+    idx = torch.randperm(K, generator=g)[: min(8, K)]
+    scale[idx] = 30.0 + 30.0 * torch.rand(idx.numel(), generator=g)
+    return (torch.randn(T, K, generator=g) * scale).bfloat16().contiguous()
+
+
 def make_tokens(wl: Workload, T: int, device="cpu", seed: Optional[int] = None):
     """x [T][H] (fp32 for the tiny case, else bf16), topk_ids, topk_w."""
     x, logits = make_router_inputs(wl, T, device, seed)

@@ -15,6 +15,11 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                                  448 row, power-of-two rows) and torch's cast.
   route                       -- pinned: brute-force stable sort, invariants,
                                  exhaustive tiny cases.
+  router_split / router_scores -- pinned: truncation bracket (W_high <= |W| <
+                                 next bf16), torch's RNE cast of the exact
+                                 residual, the 2^-15 approximation bound,
+                                 exact cases, unit-vector and linearity
+                                 laws, fp64 matmul within the bound.
   router_topk                 -- pinned: closed-form weights (logits log 1..4,
                                  equal logits, two-expert sigmoid), brute-force
                                  ranking of every tiny case, softmax of all E
@@ -84,6 +89,10 @@ def lib():
         L.oracle_forward_fp8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P, P, P, P, P]
         L.oracle_router_topk.restype = None
         L.oracle_router_topk.argtypes = [P, i, i, i, i, i, P, P]
+        L.oracle_router_split.restype = None
+        L.oracle_router_split.argtypes = [P, ctypes.c_long, P, P]
+        L.oracle_router_scores.restype = None
+        L.oracle_router_scores.argtypes = [P, P, P, i, i, i, P]
         L.oracle_num_threads.restype = i
         L.oracle_init()
         _lib = L
@@ -197,6 +206,31 @@ def router_topk(logits, k: int, renormalize: bool = True, n_shared: int = 0):
     if T:
         lib().oracle_router_topk(_p(la), T, E, k, int(bool(renormalize)), n_shared, _p(ids), _p(w))
     return ids, w
+
+
+def router_split(w):
+    """Split fp32 router weights [N][K] into (W_high, W_low) bf16 codes (uint16):
+    W_high = truncation of W to bf16, W_low = bf16_rne((W - W_high) * 256)."""
+    wa = _np(w, np.float32)
+    hi = np.zeros(wa.shape, dtype=np.uint16)
+    lo = np.zeros(wa.shape, dtype=np.uint16)
+    lib().oracle_router_split(_p(wa), wa.size, _p(hi), _p(lo))
+    return hi, lo
+
+
+def router_scores(x, hi, lo):
+    """fp64 scores [T][N] = x . W_high^T + (x . W_low^T) / 256 from bf16 x [T][K]
+    (torch bf16 or uint16 codes) and the split weights (uint16 codes [N][K])."""
+    xa = _np(x, np.uint16)
+    ha = _np(hi, np.uint16)
+    la = _np(lo, np.uint16)
+    T, K = xa.shape
+    N = ha.shape[0]
+    assert ha.shape == (N, K) and la.shape == (N, K)
+    out = np.zeros((T, N), dtype=np.float64)
+    if T and N:
+        lib().oracle_router_scores(_p(xa), _p(ha), _p(la), T, N, K, _p(out))
+    return out
 
 
 def _rows_arg(rows, T):

@@ -463,6 +463,79 @@ void oracle_router_topk(const float *logits, int T, int E, int k, int renormaliz
     }
 }
 
+/*
+ * Precision-aware router GEMM (HPC-Ops x SGLang blog, section "Router
+ * GEMM", "a precision-aware BF16 formulation"): the router keeps fp32
+ * weights W [N][K] while the hidden states x [T][K] are bf16.  W is split
+ * once into two bf16 parts:
+ *
+ *   W_high = W cut to bf16 by truncation (the low 16 bits of the fp32
+ *            pattern dropped: rounds toward zero);
+ *   W_low  = bf16 of the residual scaled by 256, (W - W_high) * 256, with
+ *            round-to-nearest-even (the residual and the scaling are exact
+ *            in fp32, so only this rounding loses anything);
+ *
+ * so that W ~ W_high + W_low / 256, and the scores are two bf16 products
+ * combined with the scale in the epilogue:
+ *
+ *   score[t][n] = sum_k x[t][k] W_high[n][k] + (sum_k x[t][k] W_low[n][k]) / 256.
+ *
+ * Both sums in fp64 here (bf16 x bf16 products are exact in fp64).
+ */
+
+/* bf16 code nearest to a finite fp32 value, ties to the even code, found
+ * from the value table: the truncated code and the next code away from
+ * zero bracket v. */
+static uint16_t bf16_rne(float v)
+{
+    uint32_t u;
+    memcpy(&u, &v, 4);
+    const uint16_t c0 = (uint16_t)(u >> 16);
+    const uint16_t c1 = (uint16_t)(c0 + 1);
+    const double dv = (double)v;
+    const double d0 = fabs(dv - BF16_VALUE[c0]);
+    const double d1 = fabs(BF16_VALUE[c1] - dv);
+    if (d0 < d1)
+        return c0;
+    if (d1 < d0)
+        return c1;
+    return (c0 & 1) ? c1 : c0;
+}
+
+void oracle_router_split(const float *w, long n, uint16_t *hi, uint16_t *lo)
+{
+    oracle_init();
+    for (long i = 0; i < n; i++) {
+        uint32_t u;
+        memcpy(&u, &w[i], 4);
+        hi[i] = (uint16_t)(u >> 16);                                  /* truncation */
+        const float high = (float)BF16_VALUE[hi[i]];
+        const float resid = (w[i] - high) * 256.0f;                   /* exact in fp32 */
+        lo[i] = bf16_rne(resid);
+    }
+}
+
+void oracle_router_scores(const uint16_t *x, const uint16_t *hi, const uint16_t *lo, int T, int N,
+                          int K, double *out)
+{
+    oracle_init();
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; t++) {
+        const uint16_t *xr = x + (size_t)t * K;
+        for (int n = 0; n < N; n++) {
+            const uint16_t *hr = hi + (size_t)n * K;
+            const uint16_t *lr = lo + (size_t)n * K;
+            double s_hi = 0.0, s_lo = 0.0;
+            for (int k = 0; k < K; k++) {
+                const double xv = BF16_VALUE[xr[k]];
+                s_hi += xv * BF16_VALUE[hr[k]];
+                s_lo += xv * BF16_VALUE[lr[k]];
+            }
+            out[(size_t)t * N + n] = s_hi + s_lo / 256.0;
+        }
+    }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
