@@ -245,6 +245,9 @@ def main():
     ap.add_argument("--router", action="store_true",
                     help="measure the router top-k kernel (the step before the routing build) over "
                          "the workload's token grid instead of the layer")
+    ap.add_argument("--router-gemm", action="store_true",
+                    help="measure the precision-aware router GEMM (and GEMM + top-k) on the blog's "
+                         "K=4096, N=192 sweep, or with --workload on that layer's router shape")
     ap.add_argument("--shared", type=int, default=0,
                     help="with --router: fused shared experts appended to each token's top-k")
     args = ap.parse_args()
@@ -270,6 +273,9 @@ def main():
         log("[bench] copy calibration: 3 x 1 GiB device copies done")
         return
     wl = WORKLOADS[args.workload]
+    if args.router_gemm:
+        router_gemm_bench(moe, wl if "--workload" in sys.argv else None, args)
+        return
     if args.router:
         router_bench(moe, wl, args)
         return
@@ -452,6 +458,102 @@ def router_bench(moe, wl, args):
     print(json.dumps({"metric": "router top-k us per call + algorithmic GB/s, 1 GPU",
                       "workload": wl.label, "E": wl.E, "k": k, "n_shared": ns,
                       "dtype": "f32", "data": "synthetic (the workload's seeded router logits)",
+                      "sweep": sweep, "cpu_baseline": cpu}), flush=True)
+
+
+ROUTER_GEMM_TS = (1, 16, 48, 96, 208, 512, 1024, 2048, 4096)   # the blog's Table 2 grid
+
+
+def router_gemm_bench(moe, wl, args):
+    """Precision-aware router GEMM, bf16 x [T][K] against the split fp32
+    weights [N][K]: per T, the time per call of a HIP graph of C back-to-back
+    calls, each on its own copy of x and of the weight pair, C chosen so that
+    one replay touches at least 512 MB (no call finds its operands in the
+    256 MB last-level cache from the previous replay); median of 20
+    replays / C.  Timed both alone (scores) and followed by the router top-k
+    (k of the workload, or 8) in the two-launch fused call.  Algorithmic
+    bytes: the split pair (4 N K, the size of the fp32 weights), x (2 T K)
+    and the scores (4 T N); MFMA work: two bf16 products, 4 T N K flops."""
+    import torch
+    import oracle
+    from moe_inputs import router_hidden, router_weight
+    if wl is None:
+        name, N, K, Ts, k = "blog Router GEMM sweep shape", 192, 4096, ROUTER_GEMM_TS, 8
+    else:
+        name, N, K, Ts, k = wl.label + " (router)", wl.E, wl.H, wl.Ts, wl.k
+    w = router_weight(N, K, seed=8).cuda()
+    pair = moe.moe_router_split_weights(w)
+    pair_bytes = pair.numel()
+    sweep = []
+    for T in Ts:
+        xb = T * K * 2
+        C = max(2, min(64, math.ceil(512e6 / (pair_bytes + xb))))
+        pairs = [pair] + [pair.clone() for _ in range(C - 1)]
+        x0 = router_hidden(T, K, seed=9 + T).cuda()
+        xs = [x0] + [x0.clone() for _ in range(C - 1)]
+        ws = torch.empty(max(moe.moe_router_workspace_bytes(T, N, K), 16), dtype=torch.uint8, device="cuda")
+        sc = torch.empty(T, N, dtype=torch.float32, device="cuda")
+        ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+        tw = torch.empty(T, k, dtype=torch.float32, device="cuda")
+
+        def gemm(c):
+            moe.moe_router_gemm(xs[c], pairs[c], N, scores=sc, workspace=ws)
+
+        def fused(c):
+            moe.moe_router_gemm_topk(xs[c], pairs[c], N, k, topk_ids=ids, topk_w=tw, workspace=ws)
+
+        res = {}
+        for label, fn in (("gemm", gemm), ("gemm_topk", fused)):
+            if label == "gemm_topk" and N > 256:
+                continue
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for c in range(C):
+                    fn(c)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in range(C):
+                    fn(c)
+            times = []
+            for _ in range(20):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b) * 1000.0 / C)
+            res[label] = statistics.median(times)
+            del g
+        nbytes = pair_bytes + xb + T * N * 4
+        flops = 4.0 * T * N * K
+        us = res["gemm"]
+        sweep.append({"T": T, "us_per_call": round(us, 2),
+                      "us_per_call_with_topk": round(res["gemm_topk"], 2) if "gemm_topk" in res else None,
+                      "algorithmic_bytes": nbytes, "GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                      "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "TFLOPs": round(flops / (us * 1e-6) / 1e12, 2),
+                      "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+                      "copies": C})
+        log(f"[bench] router gemm T={T}: {us:.2f} us/call ({sweep[-1]['GBs']} GB/s, "
+            f"{sweep[-1]['TFLOPs']} TFLOP/s), with top-k {sweep[-1]['us_per_call_with_topk']}")
+        del pairs, xs
+        torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu_baseline:
+        T = 64
+        hi, lo = oracle.router_split(w.cpu().numpy())
+        x = router_hidden(T, K, seed=9 + T)
+        t0 = time.perf_counter()
+        oracle.router_scores(x, hi, lo)
+        sec = time.perf_counter() - t0
+        cpu = {"value": round(sec * 1e6, 1), "unit": "us per call", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": f"T={T}, N={N}, K={K}: fp64 C oracle, one call"}
+    print(json.dumps({"metric": "router GEMM us per call (+ achieved GB/s and TFLOP/s), 1 GPU",
+                      "workload": name, "N": N, "K": K, "dtype": "bf16 x bf16 (split fp32 weights)",
+                      "data": "synthetic (N(0, 0.02) fp32 weights, bf16 hidden states with outlier channels)",
                       "sweep": sweep, "cpu_baseline": cpu}), flush=True)
 
 

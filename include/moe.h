@@ -212,6 +212,47 @@ int moe_build_routing_fp8(const int32_t *topk_ids, int T, int k, int E, int H, i
 int moe_router_topk(const float *logits, int T, int E, int k, int renormalize, int n_shared,
                     int32_t *topk_ids, float *topk_w, void *stream);
 
+/* Precision-aware router GEMM (blog section "Router GEMM", precision-aware
+ * BF16 formulation): fp32 router weights W [N][K], bf16 hidden states
+ * x [T][K], fp32 scores [T][N].  W is split once (at weight load) into
+ * W_high = W truncated to bf16 and W_low = RNE bf16 of (W - W_high) * 256,
+ * and the scores are x . W_high + (x . W_low) / 256: two bf16 MFMA products
+ * sharing each activation fragment, fp32 accumulation, the 1/256 applied in
+ * the epilogue.  Against an fp32-weight product the split keeps the error
+ * per weight below 2^-15 |W|.  Requires K a multiple of 64 (at most 65536),
+ * 1 <= N <= 65536.
+ *
+ * moe_router_pair_bytes: size (host) of the split pair: 4 * N16 * K bytes,
+ * N16 = N rounded up to a multiple of 16.
+ * moe_router_split_weights: w (device) fp32 [N][K] row-major -> w_pair
+ * (device, 16-byte aligned, at least moe_router_pair_bytes): W_high then
+ * W_low, each N16 * K bf16 in the fragment order of moe_pack_weights (rows
+ * N..N16-1 zero). */
+int moe_router_pair_bytes(int N, int K, size_t *bytes /* host */);
+int moe_router_split_weights(const float *w, int N, int K, void *w_pair, size_t w_pair_bytes,
+                             void *stream);
+
+/* Workspace (host query) of moe_router_gemm / moe_router_gemm_topk for these
+ * sizes: partial-score planes when few tokens split K over workgroups. */
+int moe_router_workspace_bytes(int T, int N, int K, size_t *bytes /* host */);
+
+/* scores (device) fp32 [T][N] = router GEMM of x (device, bf16 [T][K],
+ * 16-byte aligned) with the split pair w_pair.  workspace (device, 16-byte
+ * aligned) of at least moe_router_workspace_bytes (may be NULL when that is
+ * 0).  Deterministic: partial planes are added in a fixed order.  T == 0
+ * returns MOE_OK with no launch. */
+int moe_router_gemm(const void *x, const void *w_pair, int T, int N, int K, void *workspace,
+                    size_t workspace_bytes, float *scores, void *stream);
+
+/* Router GEMM followed by the router top-k (moe_router_topk) on its
+ * scores, N = E experts (E <= 256), in two launches: the top-k kernel adds
+ * the GEMM's partial planes as it loads them.  scores (device, fp32
+ * [T][E]) receives the scores when not NULL.  topk_ids / topk_w as in
+ * moe_router_topk; same argument rules as both calls. */
+int moe_router_gemm_topk(const void *x, const void *w_pair, int T, int E, int K, int k,
+                         int renormalize, int n_shared, void *workspace, size_t workspace_bytes,
+                         float *scores, int32_t *topk_ids, float *topk_w, void *stream);
+
 /* bf16 forward (blog section "MoE", gate-up & activation, PDL chaining;
  * operator table: BF16 hidden states).  x (device) bf16 [T][H]; topk_w
  * (device) fp32 [T][k]; routing (device) built by moe_build_routing_bf16

@@ -10,6 +10,9 @@ Functions carry the C names:
     moe_pack_weights(w, dtype)                          -> packed copy (one-time)
     moe_routing_layout(T, k, E, H, I, dtype)            -> dict (host only)
     moe_workspace_layout(T, k, E, H, I, dtype)          -> dict (host only)
+    moe_router_split_weights(w)                         -> split fp32 router weight pair (one-time)
+    moe_router_gemm(x, w_pair, N)                       -> fp32 router scores
+    moe_router_gemm_topk(x, w_pair, E, k, ...)          -> (topk_ids, topk_w[, scores])
     moe_router_topk(logits, k, renormalize, n_shared)    -> (topk_ids, topk_w)
     moe_build_routing_bf16(topk_ids, E, H, I, routing)  -> None
     moe_build_routing_fp8(topk_ids, E, H, I, routing)   -> None
@@ -59,7 +62,9 @@ class WorkspaceLayout(ctypes.Structure):
 
 
 EXPORTS = ("moe_status_string", "moe_pack_weights", "moe_routing_layout", "moe_workspace_layout",
-           "moe_router_topk", "moe_build_routing_bf16", "moe_build_routing_fp8", "moe_forward_bf16",
+           "moe_router_topk", "moe_router_pair_bytes", "moe_router_split_weights",
+           "moe_router_workspace_bytes", "moe_router_gemm", "moe_router_gemm_topk",
+           "moe_build_routing_bf16", "moe_build_routing_fp8", "moe_forward_bf16",
            "moe_forward_fp8", "moe_set_stage_events", "moe_device_cu_count")
 
 
@@ -81,6 +86,16 @@ def _load():
         f.restype = i
         f.argtypes = [P, i, i, i, i, i, P, sz, P]
     L.moe_router_topk.restype = i
+    L.moe_router_pair_bytes.restype = i
+    L.moe_router_pair_bytes.argtypes = [i, i, ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_router_split_weights.restype = i
+    L.moe_router_split_weights.argtypes = [P, i, i, P, sz, P]
+    L.moe_router_workspace_bytes.restype = i
+    L.moe_router_workspace_bytes.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_router_gemm.restype = i
+    L.moe_router_gemm.argtypes = [P, P, i, i, i, P, sz, P, P]
+    L.moe_router_gemm_topk.restype = i
+    L.moe_router_gemm_topk.argtypes = [P, P, i, i, i, i, i, i, P, sz, P, P, P, P]
     L.moe_router_topk.argtypes = [P, i, i, i, i, i, P, P, P]
     L.moe_forward_bf16.restype = i
     L.moe_forward_bf16.argtypes = [P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
@@ -178,6 +193,78 @@ def moe_router_topk(logits, k, renormalize=True, n_shared=0, topk_ids=None, topk
         _ptr(logits), T, E, k, int(bool(renormalize)), n_shared, _ptr(topk_ids), _ptr(topk_w),
         _stream(stream)))
     return topk_ids, topk_w
+
+
+def moe_router_pair_bytes(N, K) -> int:
+    n = ctypes.c_size_t()
+    _check("moe_router_pair_bytes", _lib.moe_router_pair_bytes(N, K, ctypes.byref(n)))
+    return n.value
+
+
+def moe_router_workspace_bytes(T, N, K) -> int:
+    n = ctypes.c_size_t()
+    _check("moe_router_workspace_bytes", _lib.moe_router_workspace_bytes(T, N, K, ctypes.byref(n)))
+    return n.value
+
+
+def moe_router_split_weights(w, out=None, stream=None):
+    """Split pair (uint8 tensor of moe_router_pair_bytes) of fp32 router weights [N][K]."""
+    if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous fp32 [N][K] tensor")
+    N, K = w.shape
+    nbytes = moe_router_pair_bytes(N, K)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    _check("moe_router_split_weights", _lib.moe_router_split_weights(
+        _ptr(w), N, K, _ptr(out), out.numel() * out.element_size(), _stream(stream)))
+    return out
+
+
+def _router_ws(T, N, K, workspace, device):
+    n = moe_router_workspace_bytes(T, N, K)
+    if workspace is None:
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def moe_router_gemm(x, w_pair, N, scores=None, workspace=None, stream=None):
+    """fp32 scores [T][N] of bf16 x [T][K] against a split router weight pair."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [T][K] tensor")
+    T, K = x.shape
+    workspace = _router_ws(T, N, K, workspace, x.device)
+    if scores is None:
+        scores = torch.empty(T, N, dtype=torch.float32, device=x.device)
+    _check_tensor("scores", scores, torch.float32, (T, N))
+    _check("moe_router_gemm", _lib.moe_router_gemm(
+        _ptr(x), _ptr(w_pair), T, N, K, _ptr(workspace), workspace.numel(), _ptr(scores),
+        _stream(stream)))
+    return scores
+
+
+def moe_router_gemm_topk(x, w_pair, E, k, renormalize=True, n_shared=0, want_scores=False,
+                         topk_ids=None, topk_w=None, scores=None, workspace=None, stream=None):
+    """Router GEMM + top-k: (topk_ids, topk_w) [T][k + n_shared], plus the fp32
+    scores [T][E] when want_scores (or a scores tensor is given)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [T][K] tensor")
+    T, K = x.shape
+    ncol = k + n_shared
+    workspace = _router_ws(T, E, K, workspace, x.device)
+    if topk_ids is None:
+        topk_ids = torch.empty(T, ncol, dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, ncol, dtype=torch.float32, device=x.device)
+    if scores is None and want_scores:
+        scores = torch.empty(T, E, dtype=torch.float32, device=x.device)
+    if scores is not None:
+        _check_tensor("scores", scores, torch.float32, (T, E))
+    _check_tensor("topk_ids", topk_ids, torch.int32, (T, ncol))
+    _check_tensor("topk_w", topk_w, torch.float32, (T, ncol))
+    _check("moe_router_gemm_topk", _lib.moe_router_gemm_topk(
+        _ptr(x), _ptr(w_pair), T, E, K, k, int(bool(renormalize)), n_shared, _ptr(workspace),
+        workspace.numel(), _ptr(scores), _ptr(topk_ids), _ptr(topk_w), _stream(stream)))
+    return (topk_ids, topk_w, scores) if scores is not None else (topk_ids, topk_w)
 
 
 def _shape_tk(topk_ids):

@@ -6,6 +6,7 @@
 // sits between the caller and the kernels (the FlagOS C++ launch wrapper
 // article makes the same point about interpreter overhead on the launch
 // path).
+#include <algorithm>
 #include <mutex>
 
 #include "moe_common.h"
@@ -603,8 +604,88 @@ int moe_router_topk(const float* logits, int T, int E, int k, int renormalize, i
   if (T == 0) return MOE_OK;
   if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARG;
-  const hipError_t e = moe_host::launch_router_topk(logits, T, E, k, renormalize, n_shared, topk_ids,
-                                                    topk_w, static_cast<hipStream_t>(stream));
+  const hipError_t e = moe_host::launch_router_topk(logits, 1, nullptr, T, E, k, renormalize, n_shared,
+                                                    topk_ids, topk_w, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_router_pair_bytes(int N, int K, size_t* bytes) {
+  if (!bytes || N < 1 || K < 1) return MOE_ERR_INVALID_ARG;
+  if (K % 64 || K > 65536 || N > 65536) return MOE_ERR_UNSUPPORTED_SHAPE;
+  *bytes = (size_t)4 * ((N + 15) / 16 * 16) * K;
+  return MOE_OK;
+}
+
+int moe_router_split_weights(const float* w, int N, int K, void* w_pair, size_t w_pair_bytes,
+                             void* stream) {
+  size_t need = 0;
+  const int rc = moe_router_pair_bytes(N, K, &need);
+  if (rc != MOE_OK) return rc;
+  if (!w || !w_pair || !aligned(w, 4) || !aligned(w_pair, 16)) return MOE_ERR_INVALID_ARG;
+  if (w_pair_bytes < need) return MOE_ERR_BUFFER_TOO_SMALL;
+  const hipError_t e = moe_host::launch_router_split(w, N, K, w_pair, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_router_workspace_bytes(int T, int N, int K, size_t* bytes) {
+  if (!bytes || T < 0 || N < 1 || K < 1) return MOE_ERR_INVALID_ARG;
+  if (K % 64 || K > 65536 || N > 65536) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) {
+    *bytes = 0;
+    return MOE_OK;
+  }
+  const moe_host::RouterGemmPlan p = moe_host::plan_router_gemm(T, N, K, kPlanCUs);
+  *bytes = (size_t)std::max(p.S, 1) * T * N * 4;
+  return MOE_OK;
+}
+
+int router_gemm_common(const void* x, const void* w_pair, int T, int N, int K, void* workspace,
+                       size_t workspace_bytes, moe_host::RouterGemmPlan* plan) {
+  size_t need = 0;
+  const int rc = moe_router_workspace_bytes(T, N, K, &need);
+  if (rc != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_pair || !aligned(x, 16) || !aligned(w_pair, 16)) return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return MOE_ERR_BUFFER_TOO_SMALL;
+  if (need && (!workspace || !aligned(workspace, 16))) return MOE_ERR_INVALID_ARG;
+  *plan = moe_host::plan_router_gemm(T, N, K, kPlanCUs);
+  return MOE_OK;
+}
+
+int moe_router_gemm(const void* x, const void* w_pair, int T, int N, int K, void* workspace,
+                    size_t workspace_bytes, float* scores, void* stream) {
+  moe_host::RouterGemmPlan p;
+  const int rc = router_gemm_common(x, w_pair, T, N, K, workspace, workspace_bytes, &p);
+  if (rc != MOE_OK || T == 0) return rc;
+  if (!scores || !aligned(scores, 4)) return MOE_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  float* planes = static_cast<float*>(workspace);
+  hipError_t e = moe_host::launch_router_gemm(x, w_pair, T, N, K, p, p.S > 1 ? planes : scores, s);
+  if (e == hipSuccess && p.S > 1) e = moe_host::launch_router_reduce(planes, p.S, T, N, scores, s);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_router_gemm_topk(const void* x, const void* w_pair, int T, int E, int K, int k,
+                         int renormalize, int n_shared, void* workspace, size_t workspace_bytes,
+                         float* scores, int32_t* topk_ids, float* topk_w, void* stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E || n_shared < 0 || (renormalize != 0 && renormalize != 1))
+    return MOE_ERR_INVALID_ARG;
+  if (E > moe_host::router_max_experts() || k + n_shared > moe::kMaxTopK ||
+      E + n_shared > moe::kMaxExperts)
+    return MOE_ERR_UNSUPPORTED_SHAPE;
+  moe_host::RouterGemmPlan p;
+  const int rc = router_gemm_common(x, w_pair, T, E, K, workspace, workspace_bytes, &p);
+  if (rc != MOE_OK || T == 0) return rc;
+  if (!topk_ids || !topk_w || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARG;
+  if (scores && !aligned(scores, 4)) return MOE_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the GEMM's planes (or, unsplit, its scores) go to the workspace; the
+  // top-k kernel adds the planes and writes the scores when asked
+  float* planes = static_cast<float*>(workspace);
+  hipError_t e = moe_host::launch_router_gemm(x, w_pair, T, E, K, p, planes, s);
+  if (e == hipSuccess)
+    e = moe_host::launch_router_topk(planes, p.S, scores, T, E, k, renormalize, n_shared, topk_ids,
+                                     topk_w, s);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

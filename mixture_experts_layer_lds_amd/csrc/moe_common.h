@@ -109,9 +109,32 @@ __device__ __forceinline__ float wave_max(float v) {
 // Host-side launch helpers implemented by the kernel translation units.
 namespace moe_host {
 
-// Router top-k over fp32 logits[T][E] into ids/w [T][k + n_shared].
-hipError_t launch_router_topk(const float* logits, int T, int E, int k, int renorm, int n_shared,
-                              int32_t* ids, float* w, hipStream_t s);
+// Router top-k over fp32 logits[T][E] into ids/w [T][k + n_shared]; with
+// S > 1 the logits are the sum of S planes [S][T][E] (added in ascending
+// plane order), written to logits_out when it is not null.
+hipError_t launch_router_topk(const float* logits, int S, float* logits_out, int T, int E, int k,
+                              int renorm, int n_shared, int32_t* ids, float* w, hipStream_t s);
+
+// Precision-aware router GEMM.
+struct RouterGemmArgs {
+  const void* x;        // bf16 [T][K]
+  const void* w_hi;     // packed bf16 W_high, rows padded to 16
+  const void* w_lo;     // packed bf16 W_low (the residual x 256)
+  float* out;           // [S][T][N] partial planes, or [T][N] scores when S == 1
+  int T, N, K, S;
+  int tb_count, nb_count;
+  long slice_stride;    // floats between planes (T * N)
+};
+struct RouterGemmPlan {
+  int mb = 1, nb = 1, waves = 4, S = 1;   // token / expert 16-blocks per item, waves, K slices
+  int tb_count = 1, nb_count = 1;
+};
+RouterGemmPlan plan_router_gemm(int T, int N, int K, int cus);
+size_t router_partial_bytes(int T, int N, const RouterGemmPlan& p);
+hipError_t launch_router_split(const float* w, int N, int K, void* pair, hipStream_t s);
+hipError_t launch_router_gemm(const void* x, const void* pair, int T, int N, int K,
+                              const RouterGemmPlan& p, float* out, hipStream_t s);
+hipError_t launch_router_reduce(const float* partials, int S, int T, int N, float* out, hipStream_t s);
 // Largest E the router kernel takes.
 int router_max_experts();
 

@@ -99,8 +99,9 @@ __device__ __forceinline__ float group_sum(float v, int lane) {
 
 template <int L>
 __global__ void __launch_bounds__(kRouterThreads)
-router_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int renorm,
-                   int n_shared, int vec, int32_t* __restrict__ ids, float* __restrict__ w) {
+router_topk_kernel(const float* __restrict__ logits, int S, long slice_stride,
+                   float* __restrict__ logits_out, int T, int E, int k, int renorm, int n_shared,
+                   int vec, int32_t* __restrict__ ids, float* __restrict__ w) {
   constexpr int kSlots = (kMaxTopK + L - 1) / L;   // selected entries kept per lane
   const int lane = threadIdx.x & (kWave - 1);
   const int sl = lane & (L - 1);
@@ -111,14 +112,33 @@ router_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int re
   const bool active = t < T;
   const float* row = logits + (active ? t : T - 1) * (long)E;
   const int e0 = 4 * sl;
+  // S planes of partial scores (the router GEMM's K slices) are added in
+  // ascending plane order as they are loaded; S = 1 is a plain logits row.
   float v[4];
   if (vec) {   // E % 4 == 0 and 16-byte aligned rows
     float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (e0 < E) q = *reinterpret_cast<const float4*>(row + e0);
+    if (e0 < E) {
+      q = *reinterpret_cast<const float4*>(row + e0);
+      for (int p = 1; p < S; p++) {
+        const float4 r = *reinterpret_cast<const float4*>(row + p * slice_stride + e0);
+        q.x += r.x, q.y += r.y, q.z += r.z, q.w += r.w;
+      }
+    }
     v[0] = q.x, v[1] = q.y, v[2] = q.z, v[3] = q.w;
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; i++) v[i] = e0 + i < E ? row[e0 + i] : 0.f;
+    for (int i = 0; i < 4; i++) {
+      v[i] = 0.f;
+      if (e0 + i < E) {
+        v[i] = row[e0 + i];
+        for (int p = 1; p < S; p++) v[i] += row[p * slice_stride + e0 + i];
+      }
+    }
+  }
+  if (logits_out && active) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      if (e0 + i < E) logits_out[t * E + e0 + i] = v[i];
   }
   // Keys of the lane's 4 slots (0 for slots past E: every real key is
   // above 0), sorted once into descending order, equal keys by ascending
@@ -215,8 +235,8 @@ namespace moe_host {
 
 int router_max_experts() { return moe::kRouterMaxExperts; }
 
-hipError_t launch_router_topk(const float* logits, int T, int E, int k, int renorm, int n_shared,
-                              int32_t* ids, float* w, hipStream_t s) {
+hipError_t launch_router_topk(const float* logits, int S, float* logits_out, int T, int E, int k,
+                              int renorm, int n_shared, int32_t* ids, float* w, hipStream_t s) {
   int L = 1;
   while (4 * L < E) L *= 2;
   const int vec = (E % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0) ? 1 : 0;
@@ -225,8 +245,8 @@ hipError_t launch_router_topk(const float* logits, int T, int E, int k, int reno
   const dim3 block(moe::kRouterThreads);
 #define MOE_ROUTER_CASE(LL)                                                                  \
   case LL:                                                                                   \
-    hipLaunchKernelGGL(moe::router_topk_kernel<LL>, grid, block, 0, s, logits, T, E, k, renorm, \
-                       n_shared, vec, ids, w);                                               \
+    hipLaunchKernelGGL(moe::router_topk_kernel<LL>, grid, block, 0, s, logits, S, (long)T * E,   \
+                       logits_out, T, E, k, renorm, n_shared, vec, ids, w);                    \
     break;
   switch (L) {
     MOE_ROUTER_CASE(1)
