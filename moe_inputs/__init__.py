@@ -54,7 +54,7 @@ class Workload:
     H: int
     I: int
     k: int
-    dtype: str          # "f32" (tiny parity case), "bf16" or "fp8"
+    dtype: str          # "f32" (tiny parity case), "bf16", "fp8" or "mxfp8"
     Ts: tuple
     routing: str        # "softmax", "biased" or "hot0"
     label: str
@@ -76,6 +76,9 @@ WORKLOADS = {
     "dsv3": Workload("dsv3", 5, 256, 7168, 2048, 8, "fp8",
                      (1, 16, 128, 1024, 4096), "softmax",
                      "DeepSeek-V3-shaped MoE layer, fp8 w8a8, E=256 H=7168 I=2048 top-8"),
+    "dsv3mx": Workload("dsv3mx", 5, 256, 7168, 2048, 8, "mxfp8",
+                       (1, 16, 128, 1024, 4096), "softmax",
+                       "DeepSeek-V3-shaped MoE layer, MXFP8 (OCP MX, 32-element blocks), E=256 H=7168 I=2048 top-8"),
 }
 
 
@@ -211,6 +214,35 @@ def _fp8_experts(E, rows, cols, std, g, device, chunk_elems=1 << 27):
     return codes, scales
 
 
+def quantize_weight_mx(w: torch.Tensor):
+    """OCP MXFP8 codes of fp32 weights [.., rows, cols] (cols % 32 == 0), one
+    e8m0 scale per 32 consecutive values of a row: shared exponent
+    s = floor(log2(amax)) - 8 clamped to [-127, 127] (-127 for a zero
+    block), codes = torch's RNE e4m3 cast of w / 2^s clamped to +-448.
+    Returns (uint8 codes [.., rows, cols], uint8 scale codes [.., rows, cols/32])."""
+    *lead, cols = w.shape
+    blk = w.reshape(*lead, cols // 32, 32)
+    amax = blk.abs().amax(dim=-1)
+    _, e = torch.frexp(amax)
+    s = torch.where(amax > 0, e - 1 - 8, torch.full_like(e, -127)).clamp(-127, 127)
+    v = blk * torch.exp2(-s.float()).unsqueeze(-1)
+    q = v.clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q.reshape(*lead, cols).contiguous(), (s + 127).to(torch.uint8).contiguous()
+
+
+def _mx_experts(E, rows, cols, std, g, device, chunk_elems=1 << 27):
+    codes = torch.empty(E, rows, cols, dtype=torch.uint8, device=device)
+    scales = torch.empty(E, rows, cols // 32, dtype=torch.uint8, device=device)
+    per = max(1, chunk_elems // (rows * cols))
+    for e0 in range(0, E, per):
+        e1 = min(E, e0 + per)
+        blk = torch.randn(e1 - e0, rows, cols, generator=g, device=device, dtype=torch.float32) * std
+        q, sc = quantize_weight_mx(blk)
+        codes[e0:e1] = q
+        scales[e0:e1] = sc
+    return codes, scales
+
+
 def make_weights(wl: Workload, device="cpu", seed: Optional[int] = None, E: Optional[int] = None):
     """Expert weights of a workload.
 
@@ -225,6 +257,10 @@ def make_weights(wl: Workload, device="cpu", seed: Optional[int] = None, E: Opti
     if wl.dtype == "fp8":
         w1, s1 = _fp8_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device)
         w2, s2 = _fp8_experts(E, H, I, 1.0 / math.sqrt(I), g, device)
+        return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2}
+    if wl.dtype == "mxfp8":
+        w1, s1 = _mx_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device)
+        w2, s2 = _mx_experts(E, H, I, 1.0 / math.sqrt(I), g, device)
         return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2}
     dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
     w1 = _randn_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device, dt)

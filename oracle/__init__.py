@@ -15,6 +15,11 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                                  448 row, power-of-two rows) and torch's cast.
   route                       -- pinned: brute-force stable sort, invariants,
                                  exhaustive tiny cases.
+  mx_quant_rows / forward_mxfp8 -- pinned: OCP worked cases (amax 448, 1,
+                                 500, 0, subnormal), torch's e4m3 cast and
+                                 frexp on random blocks, dequantisation
+                                 bound, dense torch reference of the MX
+                                 layer (k=1 single expert, general k).
   router_split / router_scores -- pinned: truncation bracket (W_high <= |W| <
                                  next bf16), torch's RNE cast of the exact
                                  residual, the 2^-15 approximation bound,
@@ -89,6 +94,12 @@ def lib():
         L.oracle_forward_fp8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P, P, P, P, P]
         L.oracle_router_topk.restype = None
         L.oracle_router_topk.argtypes = [P, i, i, i, i, i, P, P]
+        L.oracle_mx_quant_rows.restype = None
+        L.oracle_mx_quant_rows.argtypes = [P, i, i, P, P]
+        L.oracle_mx_quant_rows_bf16.restype = None
+        L.oracle_mx_quant_rows_bf16.argtypes = [P, i, i, P, P]
+        L.oracle_forward_mxfp8.restype = None
+        L.oracle_forward_mxfp8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P, P, P, P, P]
         L.oracle_router_split.restype = None
         L.oracle_router_split.argtypes = [P, ctypes.c_long, P, P]
         L.oracle_router_scores.restype = None
@@ -206,6 +217,67 @@ def router_topk(logits, k: int, renormalize: bool = True, n_shared: int = 0):
     if T:
         lib().oracle_router_topk(_p(la), T, E, k, int(bool(renormalize)), n_shared, _p(ids), _p(w))
     return ids, w
+
+
+def mx_quant_rows(v):
+    """OCP MXFP8 quantisation of fp32 rows [R][n] (n % 32 == 0): (e4m3 codes
+    uint8 [R][n], e8m0 scale codes uint8 [R][n/32])."""
+    va = _np(v, np.float32)
+    R, n = va.shape
+    assert n % 32 == 0
+    codes = np.zeros((R, n), dtype=np.uint8)
+    scales = np.zeros((R, n // 32), dtype=np.uint8)
+    if R:
+        lib().oracle_mx_quant_rows(_p(va), R, n, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mx_quant_rows_bf16(x):
+    xa = _np(x, np.uint16)
+    T, H = xa.shape
+    codes = np.zeros((T, H), dtype=np.uint8)
+    scales = np.zeros((T, H // 32), dtype=np.uint8)
+    if T:
+        lib().oracle_mx_quant_rows_bf16(_p(xa), T, H, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mx_values(codes, scales):
+    """fp64 values of MX rows (codes [R][n], scale codes [R][n/32])."""
+    c = _np(codes, np.uint8)
+    s = _np(scales, np.uint8).astype(np.int64)
+    vals = np.array([lib().oracle_e4m3_value(i) for i in range(256)])[c]
+    return np.ldexp(vals, np.repeat(s, 32, axis=-1) - 127)
+
+
+def forward_mxfp8(x, topk_w, ids, W1, s1, W2, s2, rows=None, want_quant=False):
+    """MXFP8 layer output in fp64.  x bf16 [T][H]; W1/W2 e4m3 codes; s1 e8m0
+    codes [E][2I][H/32], s2 [E][H][I/32].  With want_quant also returns
+    (xq, sx, hq, sh) of the rows."""
+    xa = _np(x, np.uint16)
+    T, H = xa.shape
+    ida = _np(ids, np.int32)
+    k = ida.shape[1]
+    wa = _np(topk_w, np.float32)
+    W1a = _np(W1, np.uint8)
+    W2a = _np(W2, np.uint8)
+    s1a = _np(s1, np.uint8)
+    s2a = _np(s2, np.uint8)
+    E, I2, _ = W1a.shape
+    I = I2 // 2
+    assert s1a.shape == (E, 2 * I, H // 32) and s2a.shape == (E, H, I // 32)
+    r, n = _rows_arg(rows, T)
+    out = np.zeros((n, H), dtype=np.float64)
+    xq = sx = hq = sh = None
+    if want_quant:
+        xq = np.zeros((n, H), dtype=np.uint8)
+        sx = np.zeros((n, H // 32), dtype=np.uint8)
+        hq = np.zeros((n, k, I), dtype=np.uint8)
+        sh = np.zeros((n, k, I // 32), dtype=np.uint8)
+    lib().oracle_forward_mxfp8(_p(xa), _p(wa), _p(ida), _p(W1a), _p(s1a), _p(W2a), _p(s2a),
+                               T, k, E, H, I, _p(r) if r is not None else None, n, _p(out),
+                               *(None if a is None else _p(a) for a in (xq, sx, hq, sh)))
+    return (out, xq, sx, hq, sh) if want_quant else out
 
 
 def router_split(w):

@@ -464,6 +464,150 @@ void oracle_router_topk(const float *logits, int T, int E, int k, int renormaliz
 }
 
 /*
+ * MXFP8 block-scaled fp8 (SGLang tuning guide, section on block shapes:
+ * gfx95 devices keep MXFP8's [1, 32] block shape instead of remapping it
+ * to [128, 128]).  OCP Microscaling format: every 32 consecutive elements
+ * along the reduction dimension share one E8M0 scale X = 2^(c - 127)
+ * (c = 0..254) and hold E4M3 elements; the value is X * element.
+ * Quantisation of a block (the OCP rule): shared exponent
+ *   s = floor(log2(max |v|)) - 8   (8 = the largest E4M3 exponent),
+ * clamped to [-127, 127]; an all-zero block takes s = -127;
+ * element = e4m3_rne_satfinite(v / 2^s).  v / 2^s is exact in fp32.
+ */
+static int mx_shared_exp(float amax)
+{
+    if (!(amax > 0.0f))
+        return -127;
+    int e;
+    frexp((double)amax, &e);          /* amax = m * 2^e, m in [0.5, 1) */
+    int s = (e - 1) - 8;              /* floor(log2(amax)) - 8 */
+    if (s < -127)
+        s = -127;
+    if (s > 127)
+        s = 127;
+    return s;
+}
+
+void oracle_mx_quant_block(const float *v, uint8_t *codes, uint8_t *scale_code)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < 32; i++)
+        if (fabsf(v[i]) > amax)
+            amax = fabsf(v[i]);
+    const int s = mx_shared_exp(amax);
+    for (int i = 0; i < 32; i++)
+        codes[i] = (uint8_t)oracle_e4m3_encode((float)ldexp((double)v[i], -s));
+    *scale_code = (uint8_t)(s + 127);
+}
+
+/* rows x n values (n % 32 == 0) -> codes [rows][n], scales [rows][n/32] */
+void oracle_mx_quant_rows(const float *v, int rows, int n, uint8_t *codes, uint8_t *scales)
+{
+    oracle_init();
+    for (long r = 0; r < rows; r++)
+        for (int b = 0; b < n / 32; b++)
+            oracle_mx_quant_block(v + r * n + 32 * b, codes + r * n + 32 * b, scales + r * (n / 32) + b);
+}
+
+void oracle_mx_quant_rows_bf16(const uint16_t *x, int T, int H, uint8_t *codes, uint8_t *scales)
+{
+    oracle_init();
+    float *row = (float *)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
+    for (int t = 0; t < T; t++) {
+        for (int h = 0; h < H; h++)
+            row[h] = (float)BF16_VALUE[x[(size_t)t * H + h]];
+        oracle_mx_quant_rows(row, 1, H, codes + (size_t)t * H, scales + (size_t)t * (H / 32));
+    }
+    free(row);
+}
+
+/* dequantised MX row: n values from codes and per-32 scale codes */
+static void mx_row(const uint8_t *codes, const uint8_t *scales, int n, double *dst)
+{
+    for (int i = 0; i < n; i++)
+        dst[i] = ldexp(E4M3_VALUE[codes[i]], (int)scales[i / 32] - 127);
+}
+
+static void token_mxfp8(const uint16_t *x, const float *topk_w, const int32_t *ids,
+                        const uint8_t *W1, const uint8_t *s1, const uint8_t *W2, const uint8_t *s2,
+                        int t, int k, int E, int H, int I, double *acc,
+                        uint8_t *xq_out, uint8_t *sx_out, uint8_t *hq_out, uint8_t *sh_out)
+{
+    float *xf = (float *)malloc(sizeof(float) * (size_t)H);
+    uint8_t *xq = (uint8_t *)malloc((size_t)H);
+    uint8_t *sx = (uint8_t *)malloc((size_t)H / 32);
+    double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+    double *wr = (double *)malloc(sizeof(double) * (size_t)(H > I ? H : I));
+    float *af = (float *)malloc(sizeof(float) * (size_t)I);
+    uint8_t *hq = (uint8_t *)malloc((size_t)I);
+    uint8_t *sh = (uint8_t *)malloc((size_t)I / 32);
+    double *hd = (double *)malloc(sizeof(double) * (size_t)I);
+
+    for (int h = 0; h < H; h++)
+        xf[h] = (float)BF16_VALUE[x[(size_t)t * H + h]];
+    oracle_mx_quant_rows(xf, 1, H, xq, sx);
+    if (xq_out) {
+        memcpy(xq_out, xq, (size_t)H);
+        memcpy(sx_out, sx, (size_t)H / 32);
+    }
+    mx_row(xq, sx, H, xd);
+    for (int m = 0; m < H; m++)
+        acc[m] = 0.0;
+    for (int j = 0; j < k; j++) {
+        int p = t * k + j;
+        int e = ids[p];
+        if (e < 0 || e >= E)
+            continue;
+        double w = (double)topk_w[p];
+        for (int n = 0; n < I; n++) {
+            size_t rg = (size_t)e * 2 * I + n, ru = rg + I;
+            mx_row(W1 + rg * H, s1 + rg * (H / 32), H, wr);
+            double g = dot(wr, xd, H);
+            mx_row(W1 + ru * H, s1 + ru * (H / 32), H, wr);
+            double u = dot(wr, xd, H);
+            af[n] = (float)(silu(g) * u);
+        }
+        oracle_mx_quant_rows(af, 1, I, hq, sh);
+        if (hq_out) {
+            memcpy(hq_out + (size_t)j * I, hq, (size_t)I);
+            memcpy(sh_out + (size_t)j * (I / 32), sh, (size_t)I / 32);
+        }
+        mx_row(hq, sh, I, hd);
+        for (int m = 0; m < H; m++) {
+            size_t r2 = (size_t)e * H + m;
+            mx_row(W2 + r2 * I, s2 + r2 * (I / 32), I, wr);
+            acc[m] += w * dot(wr, hd, I);
+        }
+    }
+    free(xf); free(xq); free(sx); free(xd); free(wr); free(af); free(hq); free(sh); free(hd);
+}
+
+/* MXFP8 forward: x bf16 [T][H]; W1/W2 e4m3 codes with e8m0 scale codes
+ * s1 [E][2I][H/32], s2 [E][H][I/32]; x quantised per token and the
+ * SiLU-and-mul intermediate per (token, expert) row, both in MX blocks of
+ * 32.  Optional outputs as oracle_forward_fp8, with scale codes
+ * sx_out [nrows][H/32] and sh_out [nrows][k][I/32]. */
+void oracle_forward_mxfp8(const uint16_t *x, const float *topk_w, const int32_t *ids,
+                          const uint8_t *W1, const uint8_t *s1, const uint8_t *W2, const uint8_t *s2,
+                          int T, int k, int E, int H, int I, const int32_t *rows, int nrows,
+                          double *out, uint8_t *xq_out, uint8_t *sx_out, uint8_t *hq_out,
+                          uint8_t *sh_out)
+{
+    oracle_init();
+    if (!rows)
+        nrows = T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; r++) {
+        int t = rows ? rows[r] : r;
+        token_mxfp8(x, topk_w, ids, W1, s1, W2, s2, t, k, E, H, I, out + (size_t)r * H,
+                    xq_out ? xq_out + (size_t)r * H : NULL,
+                    sx_out ? sx_out + (size_t)r * (H / 32) : NULL,
+                    hq_out ? hq_out + (size_t)r * k * I : NULL,
+                    sh_out ? sh_out + (size_t)r * k * (I / 32) : NULL);
+    }
+}
+
+/*
  * Precision-aware router GEMM (HPC-Ops x SGLang blog, section "Router
  * GEMM", "a precision-aware BF16 formulation"): the router keeps fp32
  * weights W [N][K] while the hidden states x [T][K] are bf16.  W is split
