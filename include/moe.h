@@ -71,8 +71,10 @@ typedef enum {
 
 typedef enum {
     MOE_DTYPE_BF16 = 0,      /* bf16 activations and weights, fp32 accumulation */
-    MOE_DTYPE_FP8_W8A8 = 1   /* e4m3 weights (per-output-channel fp32 scales) and
+    MOE_DTYPE_FP8_W8A8 = 1,  /* e4m3 weights (per-output-channel fp32 scales) and
                                 e4m3 activations (per-row fp32 scales) */
+    MOE_DTYPE_MXFP8 = 2      /* OCP MXFP8: e4m3 values with one e8m0 scale per 32
+                                consecutive K values, weights and activations */
 } moe_dtype_t;
 
 /* One row tile of the task map: rows [row_begin, row_begin + rows) of the
@@ -281,6 +283,27 @@ int moe_forward_fp8(const void *x, const float *topk_w, const void *routing,
                     const uint8_t *w2, const float *w2_scale,
                     int T, int k, int E, int H, int I,
                     void *workspace, size_t workspace_bytes, void *out, void *stream);
+
+/* MXFP8 (SGLang tuning guide, block shapes: gfx95 devices keep MXFP8's
+ * [1, 32] blocks).  Routing build: as moe_build_routing_bf16, with the
+ * tile height of the MXFP8 forward.  Forward: as moe_forward_fp8 except the
+ * scales: w1_scale (device) uint8 e8m0 codes [E][2I][H/32] and w2_scale
+ * (device) uint8 [E][H][I/32], code c meaning 2^(c - 127), one per 32
+ * consecutive values of a weight row (4-byte aligned); w1/w2 are e4m3 codes
+ * packed by moe_pack_weights with dtype MOE_DTYPE_MXFP8 (the fp8 layout).
+ * x is quantised per token and SiLU(gate)*up per (token, expert) row in
+ * blocks of 32 by the OCP rule: scale 2^s, s = floor(log2(max|v|)) - 8
+ * clamped to [-127, 127] (-127 for an all-zero block), codes =
+ * e4m3_rne_satfinite(v * 2^-s); codes and scale codes stay in the
+ * workspace.  The block scales are applied by the scaled MFMA instruction
+ * inside the K loop.  H and I must be multiples of 128. */
+int moe_build_routing_mxfp8(const int32_t *topk_ids, int T, int k, int E, int H, int I,
+                            void *routing, size_t routing_bytes, void *stream);
+int moe_forward_mxfp8(const void *x, const float *topk_w, const void *routing,
+                      const uint8_t *w1, const uint8_t *w1_scale,
+                      const uint8_t *w2, const uint8_t *w2_scale,
+                      int T, int k, int E, int H, int I,
+                      void *workspace, size_t workspace_bytes, void *out, void *stream);
 
 /* Measurement hook.  When `events` is non-NULL (n >= 10 hipEvent_t
  * handles, host array), every later forward call records events[2*s]

@@ -40,10 +40,16 @@ struct Plan {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-int check_shape(int T, int k, int E, int H, int I) {
+bool known_dtype(int dtype) {
+  return dtype == MOE_DTYPE_BF16 || dtype == MOE_DTYPE_FP8_W8A8 || dtype == MOE_DTYPE_MXFP8;
+}
+
+int check_shape(int T, int k, int E, int H, int I, int dtype = MOE_DTYPE_BF16) {
   if (T < 0 || k < 1 || k > moe::kMaxTopK || E < 1 || E > moe::kMaxExperts || H <= 0 || I <= 0)
     return MOE_ERR_INVALID_ARG;
   if (H % 64 || I % 64 || H > 65536 || I > 65536) return MOE_ERR_UNSUPPORTED_SHAPE;
+  // MX: both reductions in whole 128-value units of the scaled instruction
+  if (dtype == MOE_DTYPE_MXFP8 && (H % 128 || I % 128)) return MOE_ERR_UNSUPPORTED_SHAPE;
   if ((long)T * k > moe::kMaxPairs) return MOE_ERR_UNSUPPORTED_SHAPE;
   return MOE_OK;
 }
@@ -120,8 +126,23 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   const long P = (long)T * k;
   const long active = P < E ? P : E;
   const long avg = active > 0 ? (P + active - 1) / active : 1;
-  const int esz_t = dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2;
+  const int esz_t = dtype == MOE_DTYPE_BF16 ? 2 : 1;
   const int nsteps1 = H * esz_t / 64, nsteps2 = I * esz_t / 64;
+  if (dtype == MOE_DTYPE_MXFP8) {
+    // MXFP8: register streaming at every size (its activation block scales
+    // ride with the register stages; the strips' and tiles' LDS rings count
+    // their loads exactly and carry no scale stream).  Two-step stages: one
+    // 128-value unit of the scaled instruction each.
+    p.tiling = kStreaming;
+    p.block_m = avg <= 8 ? 16 : (avg <= 16 ? 32 : 64);
+    p.mb = p.block_m / 16;
+    p.max_tasks = (int)(P / p.block_m + (P < E ? P : E));
+    long est = (P + p.block_m - 1) / p.block_m;
+    if (est < active) est = active;
+    choose_stream(nsteps1, p.mb, est * ((long)I / 16), &p.sw1, &p.su1);
+    choose_stream(nsteps2, p.mb, est * ((long)H / 32), &p.sw2, &p.su2);
+    return p;
+  }
   // Few rows per expert (decode): register streaming, tiles of 16 rows.
   // 9 to ~80 rows (fp8: 3 to ~160): strips (token rows in LDS, weights streamed),
   // tiles of about twice the mean rows per active expert so that the usual
@@ -214,6 +235,19 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
     off = align_up(off + bytes, 256);
     return at;
   };
+  if (dtype == MOE_DTYPE_MXFP8) {   // e4m3 codes + e8m0 codes per 32 values
+    W->xq = take((size_t)T * H);
+    W->x_scale = take((size_t)T * H / 32);
+    W->x_scale_rows = kNone;
+    W->g = take(4 * P * I);          // fp32 SiLU(gate)*up before requantisation
+    W->h = take(P * I);
+    W->h_scale = take(P * I / 32);
+    W->y = take(2 * P * H);
+    W->total_bytes = off;
+    W->split_k1 = W->split_k2 = 1;
+    W->tiling = p.tiling;
+    return;
+  }
   W->xq = fp8 ? take((size_t)T * H) : kNone;
   W->x_scale = fp8 ? take(4 * (size_t)T) : kNone;
   // per-sorted-row x scales, read 16 at a time by the streaming epilogue
@@ -277,7 +311,7 @@ struct StageScope {
 
 int build_routing(int dtype, const int32_t* ids, int T, int k, int E, int H, int I,
                   void* routing, size_t routing_bytes, void* stream) {
-  int rc = check_shape(T, k, E, H, I);
+  int rc = check_shape(T, k, E, H, I, dtype);
   if (rc != MOE_OK) return rc;
   if (T == 0) return MOE_OK;
   if (!ids || !routing) return MOE_ERR_INVALID_ARG;
@@ -306,6 +340,99 @@ RoutingView view_routing(const void* routing, const moe_routing_layout_t& L) {
                      reinterpret_cast<const int32_t*>(b + L.sorted_pairs),
                      reinterpret_cast<const int32_t*>(b + L.pair_pos),
                      reinterpret_cast<const moe_task_t*>(b + L.tasks)};
+}
+
+// MXFP8 forward: x to MX blocks, register-streaming gate-up on the scaled
+// instruction (fp32 SiLU(gate)*up), MX requantisation of h, register-
+// streaming down (bf16 rows), top-k reduction.
+int forward_mx(const void* x, const float* topk_w, const void* routing, const void* w1,
+               const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, int T, int k, int E,
+               int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  int rc = check_shape(T, k, E, H, I, MOE_DTYPE_MXFP8);
+  if (rc != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !topk_w || !routing || !w1 || !w2 || !w1_scale || !w2_scale || !workspace || !out)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16) ||
+      !aligned(topk_w, 4) || !aligned(routing, 16) || !aligned(workspace, 256) ||
+      !aligned(w1_scale, 4) || !aligned(w2_scale, 4))
+    return MOE_ERR_INVALID_ARG;
+  const Plan p = make_plan(MOE_DTYPE_MXFP8, T, k, E, H, I);
+  if (p.su1 != 2 || p.su2 != 2) return MOE_ERR_UNSUPPORTED_SHAPE;
+  moe_routing_layout_t L;
+  routing_layout(T, k, E, p, &L);
+  moe_workspace_layout_t W;
+  workspace_layout(MOE_DTYPE_MXFP8, T, k, H, I, p, &W);
+  if (workspace_bytes < W.total_bytes) return MOE_ERR_BUFFER_TOO_SMALL;
+  int cus = 0;
+  if ((rc = cu_count(&cus)) != MOE_OK) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const RoutingView R = view_routing(routing, L);
+  char* ws = static_cast<char*>(workspace);
+  const int P = T * k;
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws + W.xq);
+  uint8_t* sx = reinterpret_cast<uint8_t*>(ws + W.x_scale);
+  float* h32 = reinterpret_cast<float*>(ws + W.g);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(ws + W.h);
+  uint8_t* sh = reinterpret_cast<uint8_t*>(ws + W.h_scale);
+  hipError_t e;
+  {
+    StageScope st(s, 0);
+    e = moe_host::launch_mx_quant_bf16(static_cast<const uint16_t*>(x), T, H, xq, sx, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 1);
+    moe_host::StreamArgs a{};
+    a.a = xq;
+    a.b = w1;
+    a.a_mx = sx;
+    a.b_mx = w1_scale;
+    a.sorted_pairs = R.sorted_pairs;
+    a.header = R.header;
+    a.tasks = R.tasks;
+    a.c = h32;
+    a.K = H;
+    a.N_out = I;
+    a.w_rows = 2 * I;
+    a.topk = k;
+    a.max_tasks = p.max_tasks;
+    e = moe_host::launch_stream_gemm(a, true, true, true, p.mb, p.sw1, p.su1,
+                                     stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 2);
+    e = moe_host::launch_mx_requant(h32, P, I, R.expert_offsets, E, hq, sh, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 3);
+    moe_host::StreamArgs a{};
+    a.a = hq;
+    a.b = w2;
+    a.a_mx = sh;
+    a.b_mx = w2_scale;
+    a.sorted_pairs = R.sorted_pairs;
+    a.header = R.header;
+    a.tasks = R.tasks;
+    a.c = ws + W.y;
+    a.K = I;
+    a.N_out = H;
+    a.w_rows = H;
+    a.topk = k;
+    a.max_tasks = p.max_tasks;
+    e = moe_host::launch_stream_gemm(a, false, true, true, p.mb, p.sw2, p.su2,
+                                     stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 4);
+    e = moe_host::launch_reduce(ws + W.y, true, 1, P, topk_w, R.pair_pos, R.expert_offsets, nullptr,
+                                E, T, k, H, static_cast<uint16_t*>(out), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
 }
 
 int forward(int dtype, const void* x, const float* topk_w, const void* routing, const void* w1,
@@ -497,7 +624,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     a.w_rows = 2 * I;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    e = moe_host::launch_stream_gemm(a, true, fp8, p.mb, p.sw1, p.su1,
+    e = moe_host::launch_stream_gemm(a, true, fp8, false, p.mb, p.sw1, p.su1,
                                      stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -522,7 +649,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     a.w_rows = H;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    e = moe_host::launch_stream_gemm(a, false, fp8, p.mb, p.sw2, p.su2,
+    e = moe_host::launch_stream_gemm(a, false, fp8, false, p.mb, p.sw2, p.su2,
                                      stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -551,16 +678,16 @@ const char* moe_status_string(int status) {
 }
 
 int moe_routing_layout(int T, int k, int E, int H, int I, int dtype, moe_routing_layout_t* out) {
-  if (!out || (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_W8A8)) return MOE_ERR_INVALID_ARG;
-  const int rc = check_shape(T, k, E, H, I);
+  if (!out || !known_dtype(dtype)) return MOE_ERR_INVALID_ARG;
+  const int rc = check_shape(T, k, E, H, I, dtype);
   if (rc != MOE_OK) return rc;
   routing_layout(T, k, E, make_plan(dtype, T, k, E, H, I), out);
   return MOE_OK;
 }
 
 int moe_workspace_layout(int T, int k, int E, int H, int I, int dtype, moe_workspace_layout_t* out) {
-  if (!out || (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_W8A8)) return MOE_ERR_INVALID_ARG;
-  const int rc = check_shape(T, k, E, H, I);
+  if (!out || !known_dtype(dtype)) return MOE_ERR_INVALID_ARG;
+  const int rc = check_shape(T, k, E, H, I, dtype);
   if (rc != MOE_OK) return rc;
   workspace_layout(dtype, T, k, H, I, make_plan(dtype, T, k, E, H, I), out);
   return MOE_OK;
@@ -568,9 +695,9 @@ int moe_workspace_layout(int T, int k, int E, int H, int I, int dtype, moe_works
 
 int moe_pack_weights(const void* w, int E, int rows, int cols, int dtype, void* packed,
                      void* stream) {
-  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_W8A8) return MOE_ERR_INVALID_ARG;
+  if (!known_dtype(dtype)) return MOE_ERR_INVALID_ARG;
   if (E < 1 || rows < 1 || cols < 1) return MOE_ERR_INVALID_ARG;
-  const long row_bytes = (long)cols * (dtype == MOE_DTYPE_FP8_W8A8 ? 1 : 2);
+  const long row_bytes = (long)cols * (dtype == MOE_DTYPE_BF16 ? 2 : 1);
   if (rows % 16 || row_bytes % 64 || rows > 2 * 65536 || cols > 65536)
     return MOE_ERR_UNSUPPORTED_SHAPE;
   if (!w || !packed || !aligned(w, 16) || !aligned(packed, 16)) return MOE_ERR_INVALID_ARG;
@@ -687,6 +814,19 @@ int moe_router_gemm_topk(const void* x, const void* w_pair, int T, int E, int K,
     e = moe_host::launch_router_topk(planes, p.S, scores, T, E, k, renormalize, n_shared, topk_ids,
                                      topk_w, s);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_build_routing_mxfp8(const int32_t* topk_ids, int T, int k, int E, int H, int I,
+                            void* routing, size_t routing_bytes, void* stream) {
+  return build_routing(MOE_DTYPE_MXFP8, topk_ids, T, k, E, H, I, routing, routing_bytes, stream);
+}
+
+int moe_forward_mxfp8(const void* x, const float* topk_w, const void* routing, const uint8_t* w1,
+                      const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale, int T,
+                      int k, int E, int H, int I, void* workspace, size_t workspace_bytes, void* out,
+                      void* stream) {
+  return forward_mx(x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
+                    workspace_bytes, out, stream);
 }
 
 int moe_forward_bf16(const void* x, const float* topk_w, const void* routing, const void* w1,

@@ -76,9 +76,10 @@ __device__ __forceinline__ void e4m3_row_scales(float amax, float* scale, float*
 // instruction (v_mfma_scale_f32_16x16x128_f8f6f4, both block scales 2^0).
 // (a0, a1) and (b0, b1) are the lane's 16-byte fragments of two consecutive
 // 64-byte K steps in the packed lane order (lane l: row/column l % 16,
-// bytes 16*(l/16) of each step).  The instruction reads a lane's 32 bytes
-// as one run of K; A and B lanes of the same group l/16 supply the same K
-// positions, so the sum runs over exactly the 128 products of the two steps.
+// bytes 16*(l/16) of each step).  The instruction's K order (measured on
+// the device) puts a lane's first 16 bytes at K 16*(l/16).. and its last 16
+// at K 64 + 16*(l/16)..; with the two steps' fragments in that order its K
+// is exactly the memory order of the 128 bytes.
 __device__ __forceinline__ void mfma_fp8_k128(f32x4& acc, const u32x4& a0, const u32x4& a1,
                                               const u32x4& b0, const u32x4& b1) {
   typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -87,6 +88,20 @@ __device__ __forceinline__ void mfma_fp8_k128(f32x4& acc, const u32x4& a0, const
   const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
                    (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
   acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+}
+
+// As mfma_fp8_k128 with MX block scales: sa / sb hold, in their low byte,
+// the e8m0 code (2^(c-127)) of K block l/16 of the lane's row / column
+// (the instruction takes lane 16*g + r's scale for row r's 32 values
+// K 32*g.. of the unit).
+__device__ __forceinline__ void mfma_mx_k128(f32x4& acc, const u32x4& a0, const u32x4& a1,
+                                             const u32x4& b0, const u32x4& b1, int sa, int sb) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                   (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, sa, 0, sb);
 }
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
@@ -240,6 +255,8 @@ struct StreamArgs {
   const moe_task_t* tasks;
   void* c;                      // gate-up: h [P][N_out] (bf16, or fp32 on fp8); down: y [P][N_out] bf16
   float* row_amax;              // fp8 gate-up: [P] atomic-max slots (pre-cleared)
+  const uint8_t* a_mx;          // MX: e8m0 codes of a's rows [rows][K/32] (gate-up: token rows)
+  const uint8_t* b_mx;          // MX: e8m0 codes of the weights [E][w_rows][K/32]
   int K;                        // reduction length (elements)
   int N_out;                    // output columns (I for gate-up, H for down)
   int w_rows;                   // weight rows per expert (2I or H)
@@ -249,8 +266,13 @@ struct StreamArgs {
 
 // (mb, waves, u) = 16-row blocks per tile, waves per workgroup, K steps per stage.
 bool stream_config_supported(int mb, int waves, int u);
-hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int mb, int waves, int u,
-                              int grid, hipStream_t s);
+hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, bool mx, int mb, int waves,
+                              int u, int grid, hipStream_t s);
+// MXFP8 quantisation: bf16 rows x[T][H] -> e4m3 xq + e8m0 codes [T][H/32];
+// fp32 rows h[P][I] (valid sorted rows only) -> hq + codes [P][I/32].
+hipError_t launch_mx_quant_bf16(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* sx, hipStream_t s);
+hipError_t launch_mx_requant(const float* h, int P, int I, const int32_t* expert_offsets, int E,
+                             uint8_t* hq, uint8_t* sh, hipStream_t s);
 
 // fp32 rows -> e4m3 codes with the row amax held in h_scale (replaced by the scale).
 hipError_t launch_requant_rows(const float* h32, int P, int I, const int32_t* expert_offsets,

@@ -27,6 +27,14 @@
 //    there and the row scale by the top-k reduction.
 //  * Per-item metadata (task record, token indices, fp8 scales) comes from
 //    scalar loads.
+//  * MXFP8 (MX): every 32 K values of a row carry their own e8m0 scale, in
+//    both operands.  Each register stage is one 128-value K unit (two
+//    64-byte steps), multiplied by the scaled gfx950 instruction, which
+//    applies the lane's activation and weight block scales itself: lane
+//    16g + r supplies the scale of row r's K block 4u + g, the dword of the
+//    row's four block scales of unit u shifted to the lane's byte.  The
+//    epilogue then applies no scale; gate-up writes fp32 h for the MX
+//    requantisation pass.
 #include <type_traits>
 
 #include "lds_dma.h"
@@ -50,10 +58,11 @@ __device__ __forceinline__ void stream_mfma(f32x4& acc, const u32x4& a, const u3
 
 // MB 16-row blocks per task tile, W waves per workgroup (K slices), U
 // 64-byte K steps per register stage.
-template <int MB, int W, int U, bool GATEUP, bool FP8>
+template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX>
 __global__ void __launch_bounds__(W * 64)
 stream_gemm_kernel(moe_host::StreamArgs g) {
   constexpr int NB = kStreamNB;
+  static_assert(!MX || (FP8 && U == 2), "MX stages are one 128-value K unit");
   __shared__ f32x4 red[W][MB][NB][64];   // the waves' partial sums of one item
   const int lane = threadIdx.x & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
@@ -114,6 +123,29 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
 #pragma unroll
     for (int q = 0; q < NB; q++)
       bp[q] = B + (((size_t)task.expert * w_blocks + blk[q]) * nsteps + step0) * 1024 + 16 * lane;
+    // MX: this lane's rows' block-scale codes, from the wave's first unit
+    // (K / 32 codes per row, four per 128-value unit)
+    const uint8_t* asp[MB];
+    const uint8_t* bsp[NB];
+    if constexpr (MX) {
+      const size_t nblk = (size_t)g.K / 32;
+#pragma unroll
+      for (int b = 0; b < MB; b++) {
+        const int rb = b * 16 < task.rows ? b : 0;
+        int arow;
+        if constexpr (GATEUP) {
+          const i32x16_t sp = load16_scalar(g.sorted_pairs + task.row_begin + rb * 16);
+          const int p = rb * 16 + lrow < task.rows ? spread16(sp, lane) : sp[0];
+          arow = p / g.topk;
+        } else {
+          arow = task.row_begin + (rb * 16 + lrow < task.rows ? rb * 16 + lrow : 0);
+        }
+        asp[b] = g.a_mx + (size_t)arow * nblk + (size_t)step0 * 2;
+      }
+#pragma unroll
+      for (int q = 0; q < NB; q++)
+        bsp[q] = g.b_mx + ((size_t)task.expert * g.w_rows + blk[q] * 16 + lrow) * nblk + (size_t)step0 * 2;
+    }
 
     f32x4 acc[MB][NB];
 #pragma unroll
@@ -122,6 +154,15 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
       for (int q = 0; q < NB; q++) acc[m][q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     u32x4 fa0[U][MB], fb0[U][NB], fa1[U][MB], fb1[U][NB];
+    uint32_t sa0[MB], sb0[NB], sa1[MB], sb1[NB];   // MX: block-scale dwords of the stage's unit
+    auto load_scales = [&](uint32_t (&sa)[MB], uint32_t (&sb)[NB], int grp) __attribute__((always_inline)) {
+      if constexpr (MX) {
+#pragma unroll
+        for (int b = 0; b < MB; b++) sa[b] = *reinterpret_cast<const uint32_t*>(asp[b] + (size_t)grp * 4);
+#pragma unroll
+        for (int q = 0; q < NB; q++) sb[q] = *reinterpret_cast<const uint32_t*>(bsp[q] + (size_t)grp * 4);
+      }
+    };
     auto load = [&](u32x4 (&fa)[U][MB], u32x4 (&fb)[U][NB], int grp) {
 #pragma unroll
       for (int u = 0; u < U; u++) {
@@ -133,32 +174,47 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
         for (int b = 0; b < MB; b++) fa[u][b] = *reinterpret_cast<const u32x4*>(ap[b] + (size_t)step * 64);
       }
     };
-    auto compute = [&](const u32x4 (&fa)[U][MB], const u32x4 (&fb)[U][NB]) {
-#pragma unroll
-      for (int u = 0; u < U; u++)
+    auto compute = [&](const u32x4 (&fa)[U][MB], const u32x4 (&fb)[U][NB], const uint32_t (&sa)[MB],
+                       const uint32_t (&sb)[NB]) {
+      if constexpr (MX) {
+        const int sh = 8 * lgrp;   // the lane's block within the unit
 #pragma unroll
         for (int b = 0; b < MB; b++)
 #pragma unroll
-          for (int q = 0; q < NB; q++) stream_mfma<FP8>(acc[b][q], fa[u][b], fb[u][q]);
+          for (int q = 0; q < NB; q++)
+            mfma_mx_k128(acc[b][q], fa[0][b], fa[1][b], fb[0][q], fb[1][q], (int)(sa[b] >> sh),
+                         (int)(sb[q] >> sh));
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; u++)
+#pragma unroll
+          for (int b = 0; b < MB; b++)
+#pragma unroll
+            for (int q = 0; q < NB; q++) stream_mfma<FP8>(acc[b][q], fa[u][b], fb[u][q]);
+      }
     };
     // Two register stages in turn.  No load sits under a condition: the
     // loop runs whole pairs and the tail (one stage or two) is chosen after
     // it, so each multiply waits for exactly its own stage while the next
     // one is in flight.
     load(fa0, fb0, 0);
+    load_scales(sa0, sb0, 0);
     int grp = 0;
     for (; grp + 2 < ngroups; grp += 2) {
       load(fa1, fb1, grp + 1);
-      compute(fa0, fb0);
+      load_scales(sa1, sb1, grp + 1);
+      compute(fa0, fb0, sa0, sb0);
       load(fa0, fb0, grp + 2);
-      compute(fa1, fb1);
+      load_scales(sa0, sb0, grp + 2);
+      compute(fa1, fb1, sa1, sb1);
     }
     if (grp + 1 < ngroups) {
       load(fa1, fb1, grp + 1);
-      compute(fa0, fb0);
-      compute(fa1, fb1);
+      load_scales(sa1, sb1, grp + 1);
+      compute(fa0, fb0, sa0, sb0);
+      compute(fa1, fb1, sa1, sb1);
     } else {
-      compute(fa0, fb0);
+      compute(fa0, fb0, sa0, sb0);
     }
 
     // ---- the waves' partial sums meet in LDS (lane-contiguous 16-byte slots)
@@ -184,7 +240,7 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
       for (int q = 0; q < NB; q++) cs[q] = 1.0f;
 #pragma unroll
       for (int i = 0; i < 4; i++) rs[i] = 1.0f;
-      if constexpr (FP8) {
+      if constexpr (FP8 && !MX) {
 #pragma unroll
         for (int q = 0; q < NB; q++) {
           const i32x16_t v = load16_scalar(g.b_scale + (size_t)task.expert * g.w_rows + blk[q] * 16);
@@ -204,7 +260,7 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           float gv = tot[0][i], uv = tot[1][i];
-          if constexpr (FP8) {
+          if constexpr (FP8 && !MX) {
             gv = (gv * rs[i]) * cs[0];
             uv = (uv * rs[i]) * cs[1];
           }
@@ -219,7 +275,7 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
             if constexpr (FP8) static_cast<float*>(g.c)[r * g.N_out + col] = hv[i];
             else static_cast<uint16_t*>(g.c)[r * g.N_out + col] = f32_to_bf16_bits(hv[i]);
           }
-          if constexpr (FP8) {
+          if constexpr (FP8 && !MX) {
             // row amax over this item's 16 columns, folded into the row's slot
             const float mx = max16(ok ? __builtin_fabsf(hv[i]) : 0.0f);
             if (ok && lrow == 0)
@@ -246,19 +302,25 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
   }
 }
 
-template <int MB, int W, int U, bool GATEUP, bool FP8>
+template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX>
 static hipError_t launch_stream_t(const moe_host::StreamArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((stream_gemm_kernel<MB, W, U, GATEUP, FP8>), dim3(grid), dim3(W * 64), 0, s, a);
+  hipLaunchKernelGGL((stream_gemm_kernel<MB, W, U, GATEUP, FP8, MX>), dim3(grid), dim3(W * 64), 0, s, a);
   return hipGetLastError();
 }
 
 template <int MB, int W, int U>
-static hipError_t launch_stream_w(const moe_host::StreamArgs& a, bool gateup, bool fp8, int grid,
-                                  hipStream_t s) {
-  if (gateup) return fp8 ? launch_stream_t<MB, W, U, true, true>(a, grid, s)
-                         : launch_stream_t<MB, W, U, true, false>(a, grid, s);
-  return fp8 ? launch_stream_t<MB, W, U, false, true>(a, grid, s)
-             : launch_stream_t<MB, W, U, false, false>(a, grid, s);
+static hipError_t launch_stream_w(const moe_host::StreamArgs& a, bool gateup, bool fp8, bool mx,
+                                  int grid, hipStream_t s) {
+  if (mx) {
+    if constexpr (U == 2)
+      return gateup ? launch_stream_t<MB, W, U, true, true, true>(a, grid, s)
+                    : launch_stream_t<MB, W, U, false, true, true>(a, grid, s);
+    return hipErrorInvalidValue;
+  }
+  if (gateup) return fp8 ? launch_stream_t<MB, W, U, true, true, false>(a, grid, s)
+                         : launch_stream_t<MB, W, U, true, false, false>(a, grid, s);
+  return fp8 ? launch_stream_t<MB, W, U, false, true, false>(a, grid, s)
+             : launch_stream_t<MB, W, U, false, false, false>(a, grid, s);
 }
 
 }  // namespace moe
@@ -281,10 +343,10 @@ bool stream_config_supported(int mb, int waves, int u) {
   return false;
 }
 
-hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int mb, int waves, int u,
-                              int grid, hipStream_t s) {
+hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, bool mx, int mb, int waves,
+                              int u, int grid, hipStream_t s) {
 #define MOE_STREAM_CASE(M, Wv, Uv) \
-  if (mb == M && waves == Wv && u == Uv) return moe::launch_stream_w<M, Wv, Uv>(a, gateup, fp8, grid, s);
+  if (mb == M && waves == Wv && u == Uv) return moe::launch_stream_w<M, Wv, Uv>(a, gateup, fp8, mx, grid, s);
   MOE_STREAM_CONFIGS(MOE_STREAM_CASE)
 #undef MOE_STREAM_CASE
   return hipErrorInvalidValue;

@@ -27,8 +27,7 @@ def gpu_route(lib, ids, E, H, I, dtype):
     T, k = ids.shape
     routing = lib.alloc_routing(T, k, E, H, I, dtype)
     routing.fill_(0xAB)           # poison: every compared word must be written
-    build = lib.moe_build_routing_bf16 if dtype == "bf16" else lib.moe_build_routing_fp8
-    build(ids.cuda().contiguous(), E, H, I, routing)
+    lib.build_routing(ids.cuda().contiguous(), E, H, I, routing, dtype)
     torch.cuda.synchronize()
     return lib.read_routing(routing, T, k, E, H, I, dtype)
 
@@ -58,7 +57,7 @@ CASES = [(name, T) for name, wl in WORKLOADS.items() for T in wl.Ts]
 def test_routing_workloads(lib, name, T):
     wl = WORKLOADS[name]
     _, ids, _ = make_tokens(wl, T)
-    dtype = "fp8" if wl.dtype == "fp8" else "bf16"
+    dtype = wl.dtype if wl.dtype in ("fp8", "mxfp8") else "bf16"
     check_route(lib, ids, wl.E, wl.H, wl.I, dtype, name)
 
 
