@@ -54,7 +54,7 @@ class Workload:
     H: int
     I: int
     k: int
-    dtype: str          # "f32" (tiny parity case), "bf16", "fp8" or "mxfp8"
+    dtype: str          # "f32" (tiny parity case), "bf16", "fp8", "mxfp8" or "int8"
     Ts: tuple
     routing: str        # "softmax", "biased" or "hot0"
     label: str
@@ -76,6 +76,9 @@ WORKLOADS = {
     "dsv3": Workload("dsv3", 5, 256, 7168, 2048, 8, "fp8",
                      (1, 16, 128, 1024, 4096), "softmax",
                      "DeepSeek-V3-shaped MoE layer, fp8 w8a8, E=256 H=7168 I=2048 top-8"),
+    "dsv3i8": Workload("dsv3i8", 5, 256, 7168, 2048, 8, "int8",
+                       (1, 16, 128, 1024, 4096), "softmax",
+                       "DeepSeek-V3-shaped MoE layer, int8 w8a8 per-channel, E=256 H=7168 I=2048 top-8"),
     "dsv3mx": Workload("dsv3mx", 5, 256, 7168, 2048, 8, "mxfp8",
                        (1, 16, 128, 1024, 4096), "softmax",
                        "DeepSeek-V3-shaped MoE layer, MXFP8 (OCP MX, 32-element blocks), E=256 H=7168 I=2048 top-8"),
@@ -214,6 +217,30 @@ def _fp8_experts(E, rows, cols, std, g, device, chunk_elems=1 << 27):
     return codes, scales
 
 
+def quantize_weight_int8(w: torch.Tensor):
+    """Per-output-channel symmetric int8 codes of fp32 weights [.., rows, cols]:
+    scale = amax(row) / 127 (1 for an all-zero row), codes = torch's
+    half-to-even rounding of w / scale, clamped to [-127, 127].
+    Returns (int8 codes, fp32 scales [.., rows])."""
+    amax = w.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / 127.0, torch.ones_like(amax)).float()
+    q = torch.round(w / scale.unsqueeze(-1)).clamp(-127, 127).to(torch.int8)
+    return q.contiguous(), scale.contiguous()
+
+
+def _int8_experts(E, rows, cols, std, g, device, chunk_elems=1 << 27):
+    codes = torch.empty(E, rows, cols, dtype=torch.int8, device=device)
+    scales = torch.empty(E, rows, dtype=torch.float32, device=device)
+    per = max(1, chunk_elems // (rows * cols))
+    for e0 in range(0, E, per):
+        e1 = min(E, e0 + per)
+        blk = torch.randn(e1 - e0, rows, cols, generator=g, device=device, dtype=torch.float32) * std
+        q, sc = quantize_weight_int8(blk)
+        codes[e0:e1] = q
+        scales[e0:e1] = sc
+    return codes, scales
+
+
 def quantize_weight_mx(w: torch.Tensor):
     """OCP MXFP8 codes of fp32 weights [.., rows, cols] (cols % 32 == 0), one
     e8m0 scale per 32 consecutive values of a row: shared exponent
@@ -257,6 +284,10 @@ def make_weights(wl: Workload, device="cpu", seed: Optional[int] = None, E: Opti
     if wl.dtype == "fp8":
         w1, s1 = _fp8_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device)
         w2, s2 = _fp8_experts(E, H, I, 1.0 / math.sqrt(I), g, device)
+        return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2}
+    if wl.dtype == "int8":
+        w1, s1 = _int8_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device)
+        w2, s2 = _int8_experts(E, H, I, 1.0 / math.sqrt(I), g, device)
         return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2}
     if wl.dtype == "mxfp8":
         w1, s1 = _mx_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device)

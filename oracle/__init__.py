@@ -15,6 +15,10 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                                  448 row, power-of-two rows) and torch's cast.
   route                       -- pinned: brute-force stable sort, invariants,
                                  exhaustive tiny cases.
+  int8_quant_row / forward_int8 -- pinned: worked cases (integers at amax
+                                 127, ties to even, clamping), an independent
+                                 torch quantiser, a dense torch reference
+                                 (exact integer products).
   mx_quant_rows / forward_mxfp8 -- pinned: OCP worked cases (amax 448, 1,
                                  500, 0, subnormal), torch's e4m3 cast and
                                  frexp on random blocks, dequantisation
@@ -94,6 +98,12 @@ def lib():
         L.oracle_forward_fp8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P, P, P, P, P]
         L.oracle_router_topk.restype = None
         L.oracle_router_topk.argtypes = [P, i, i, i, i, i, P, P]
+        L.oracle_int8_quant_row.restype = None
+        L.oracle_int8_quant_row.argtypes = [P, i, P, P]
+        L.oracle_int8_quant_rows_bf16.restype = None
+        L.oracle_int8_quant_rows_bf16.argtypes = [P, i, i, P, P]
+        L.oracle_forward_int8.restype = None
+        L.oracle_forward_int8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P, P, P, P, P]
         L.oracle_mx_quant_rows.restype = None
         L.oracle_mx_quant_rows.argtypes = [P, i, i, P, P]
         L.oracle_mx_quant_rows_bf16.restype = None
@@ -217,6 +227,54 @@ def router_topk(logits, k: int, renormalize: bool = True, n_shared: int = 0):
     if T:
         lib().oracle_router_topk(_p(la), T, E, k, int(bool(renormalize)), n_shared, _p(ids), _p(w))
     return ids, w
+
+
+def int8_quant_row(v):
+    """int8 codes (int8 array) and fp32 scale of one fp32 row (symmetric, amax/127)."""
+    va = _np(v, np.float32).reshape(-1)
+    q = np.zeros(va.size, dtype=np.int8)
+    sc = np.zeros(1, dtype=np.float32)
+    lib().oracle_int8_quant_row(_p(va), va.size, _p(q), _p(sc))
+    return q, float(sc[0])
+
+
+def int8_quant_rows_bf16(x):
+    xa = _np(x, np.uint16)
+    T, H = xa.shape
+    q = np.zeros((T, H), dtype=np.int8)
+    sc = np.zeros(T, dtype=np.float32)
+    if T:
+        lib().oracle_int8_quant_rows_bf16(_p(xa), T, H, _p(q), _p(sc))
+    return q, sc
+
+
+def forward_int8(x, topk_w, ids, W1, s1, W2, s2, rows=None, want_quant=False):
+    """int8 w8a8 (per-channel weight scales) layer output in fp64.  x bf16
+    [T][H]; W1/W2 int8 codes (int8 or uint8 tensors of the same bytes);
+    s1 fp32 [E][2I], s2 fp32 [E][H]."""
+    xa = _np(x, np.uint16)
+    T, H = xa.shape
+    ida = _np(ids, np.int32)
+    k = ida.shape[1]
+    wa = _np(topk_w, np.float32)
+    W1a = _np(W1, np.int8)
+    W2a = _np(W2, np.int8)
+    s1a = _np(s1, np.float32)
+    s2a = _np(s2, np.float32)
+    E, I2, _ = W1a.shape
+    I = I2 // 2
+    r, n = _rows_arg(rows, T)
+    out = np.zeros((n, H), dtype=np.float64)
+    xq = sx = hq = sh = None
+    if want_quant:
+        xq = np.zeros((n, H), dtype=np.int8)
+        sx = np.zeros(n, dtype=np.float32)
+        hq = np.zeros((n, k, I), dtype=np.int8)
+        sh = np.zeros((n, k), dtype=np.float32)
+    lib().oracle_forward_int8(_p(xa), _p(wa), _p(ida), _p(W1a), _p(s1a), _p(W2a), _p(s2a),
+                              T, k, E, H, I, _p(r) if r is not None else None, n, _p(out),
+                              *(None if a is None else _p(a) for a in (xq, sx, hq, sh)))
+    return (out, xq, sx, hq, sh) if want_quant else out
 
 
 def mx_quant_rows(v):

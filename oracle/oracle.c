@@ -464,6 +464,121 @@ void oracle_router_topk(const float *logits, int T, int E, int k, int renormaliz
 }
 
 /*
+ * int8 w8a8 with per-channel weight scales (SGLang tuning guide: the
+ * int8_w8a8 dtype with per-channel quantisation, for channel-INT8 MoE
+ * checkpoints).  Symmetric per-row rule, the fp8 rule with 127 for 448:
+ * amax = max|v|, scale = fp32(amax/127), inv = fp32(127/amax) (divisions in
+ * fp64), code = clamp(round_half_even(fp32(v * inv)), -127, 127); an
+ * all-zero row gets scale 1 and codes 0.  Weights carry one fp32 scale per
+ * output row; x is quantised per token and the intermediate per (token,
+ * expert) row.  int8 dot products are exact in fp64.
+ */
+void oracle_int8_quant_row(const float *v, int n, int8_t *q, float *scale)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; i++)
+        if (fabsf(v[i]) > amax)
+            amax = fabsf(v[i]);
+    if (amax == 0.0f) {
+        *scale = 1.0f;
+        memset(q, 0, (size_t)n);
+        return;
+    }
+    const float inv = (float)(127.0 / (double)amax);
+    for (int i = 0; i < n; i++) {
+        float prod = v[i] * inv;                      /* one fp32 multiply */
+        double r = nearbyint((double)prod);           /* ties to even (default mode) */
+        if (r > 127.0)
+            r = 127.0;
+        if (r < -127.0)
+            r = -127.0;
+        q[i] = (int8_t)r;
+    }
+    *scale = (float)((double)amax / 127.0);
+}
+
+void oracle_int8_quant_rows_bf16(const uint16_t *x, int T, int H, int8_t *q, float *scales)
+{
+    oracle_init();
+    float *row = (float *)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
+    for (int t = 0; t < T; t++) {
+        for (int h = 0; h < H; h++)
+            row[h] = (float)BF16_VALUE[x[(size_t)t * H + h]];
+        oracle_int8_quant_row(row, H, q + (size_t)t * H, scales + t);
+    }
+    free(row);
+}
+
+static double dot_i8(const int8_t *a, const int8_t *b, int n)
+{
+    long long s = 0;
+    for (int i = 0; i < n; i++)
+        s += (long long)a[i] * (long long)b[i];
+    return (double)s;
+}
+
+static void token_int8(const uint16_t *x, const float *topk_w, const int32_t *ids,
+                       const int8_t *W1, const float *s1, const int8_t *W2, const float *s2,
+                       int t, int k, int E, int H, int I, double *acc,
+                       int8_t *xq_out, float *sx_out, int8_t *hq_out, float *sh_out)
+{
+    float *xf = (float *)malloc(sizeof(float) * (size_t)H);
+    int8_t *xq = (int8_t *)malloc((size_t)H);
+    float *af = (float *)malloc(sizeof(float) * (size_t)I);
+    int8_t *hq = (int8_t *)malloc((size_t)I);
+    float sx, sh;
+    for (int h = 0; h < H; h++)
+        xf[h] = (float)BF16_VALUE[x[(size_t)t * H + h]];
+    oracle_int8_quant_row(xf, H, xq, &sx);
+    if (xq_out) {
+        memcpy(xq_out, xq, (size_t)H);
+        *sx_out = sx;
+    }
+    for (int m = 0; m < H; m++)
+        acc[m] = 0.0;
+    for (int j = 0; j < k; j++) {
+        int p = t * k + j;
+        int e = ids[p];
+        if (e < 0 || e >= E)
+            continue;
+        double w = (double)topk_w[p];
+        for (int n = 0; n < I; n++) {
+            size_t rg = (size_t)e * 2 * I + n, ru = rg + I;
+            double g = (double)sx * (double)s1[rg] * dot_i8(W1 + rg * H, xq, H);
+            double u = (double)sx * (double)s1[ru] * dot_i8(W1 + ru * H, xq, H);
+            af[n] = (float)(silu(g) * u);
+        }
+        oracle_int8_quant_row(af, I, hq, &sh);
+        if (hq_out) {
+            memcpy(hq_out + (size_t)j * I, hq, (size_t)I);
+            sh_out[j] = sh;
+        }
+        for (int m = 0; m < H; m++) {
+            size_t r2 = (size_t)e * H + m;
+            acc[m] += w * ((double)sh * (double)s2[r2] * dot_i8(W2 + r2 * I, hq, I));
+        }
+    }
+    free(xf); free(xq); free(af); free(hq);
+}
+
+void oracle_forward_int8(const uint16_t *x, const float *topk_w, const int32_t *ids,
+                         const int8_t *W1, const float *s1, const int8_t *W2, const float *s2,
+                         int T, int k, int E, int H, int I, const int32_t *rows, int nrows,
+                         double *out, int8_t *xq_out, float *sx_out, int8_t *hq_out, float *sh_out)
+{
+    oracle_init();
+    if (!rows)
+        nrows = T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; r++) {
+        int t = rows ? rows[r] : r;
+        token_int8(x, topk_w, ids, W1, s1, W2, s2, t, k, E, H, I, out + (size_t)r * H,
+                   xq_out ? xq_out + (size_t)r * H : NULL, sx_out ? sx_out + r : NULL,
+                   hq_out ? hq_out + (size_t)r * k * I : NULL, sh_out ? sh_out + (size_t)r * k : NULL);
+    }
+}
+
+/*
  * MXFP8 block-scaled fp8 (SGLang tuning guide, section on block shapes:
  * gfx95 devices keep MXFP8's [1, 32] block shape instead of remapping it
  * to [128, 128]).  OCP Microscaling format: every 32 consecutive elements
