@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "us per MoE layer + achieved HBM GB/s (% of peak), T=1..4096 tokens, 1 GPU"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0, "int8": 5000.0}   # int8: POP/s
 STAGES = ("quant_x", "gate_up", "act", "down", "reduce")
 
 
@@ -51,9 +51,10 @@ def layer_bytes_and_flops(wl, ids, T):
     flat = ids.reshape(-1).to(torch.int64).cpu()
     valid = flat[(flat >= 0) & (flat < E)]
     active = int(torch.unique(valid).numel())
-    bw = 1 if wl.dtype in ("fp8", "mxfp8") else 2
-    # scales: fp32 per output channel (fp8), one e8m0 byte per 32 weights (MX)
-    per_expert = 3 * H * I * bw + {"fp8": (2 * I + H) * 4, "mxfp8": 3 * H * I // 32}.get(wl.dtype, 0)
+    bw = 1 if wl.dtype in ("fp8", "mxfp8", "int8") else 2
+    # scales: fp32 per output channel (fp8, int8), one e8m0 byte per 32 weights (MX)
+    per_expert = 3 * H * I * bw + {"fp8": (2 * I + H) * 4, "int8": (2 * I + H) * 4,
+                                   "mxfp8": 3 * H * I // 32}.get(wl.dtype, 0)
     P = flat.numel()
     nbytes = active * per_expert + T * H * 2 + T * H * 2 + P * 8
     flops = 6.0 * valid.numel() * H * I
@@ -67,7 +68,7 @@ def stage_bytes(wl, active, P_valid, T):
     bf16); partial sums and padding rows are not counted."""
     E, H, I = wl.E, wl.H, wl.I
     mx = wl.dtype == "mxfp8"
-    fp8 = wl.dtype == "fp8" or mx
+    fp8 = wl.dtype in ("fp8", "int8") or mx   # one-byte codes
     bw = 1 if fp8 else 2
     bx = 1 if fp8 else 2
     P = T * wl.k
@@ -109,7 +110,8 @@ class Layer:
         if self.dtype == "bf16":
             m.moe_forward_bf16(self.x, self.w, self.routing, W["w1"], W["w2"], self.ws, self.out)
         else:
-            fwd = m.moe_forward_fp8 if self.dtype == "fp8" else m.moe_forward_mxfp8
+            fwd = {"fp8": m.moe_forward_fp8, "mxfp8": m.moe_forward_mxfp8,
+                   "int8": m.moe_forward_int8}[self.dtype]
             fwd(self.x, self.w, self.routing, W["w1"], W["w1_scale"], W["w2"], W["w2_scale"],
                 self.ws, self.out)
 
@@ -226,7 +228,8 @@ def cpu_baseline(wl, layer, W_host, dtype, reps=3):
         if dtype == "bf16":
             oracle.forward_bf16(x, w, ids, W_host["w1"], W_host["w2"])
         else:
-            fwd = oracle.forward_fp8 if dtype == "fp8" else oracle.forward_mxfp8
+            fwd = {"fp8": oracle.forward_fp8, "mxfp8": oracle.forward_mxfp8,
+                   "int8": oracle.forward_int8}[dtype]
             fwd(x, w, ids, W_host["w1"], W_host["w1_scale"], W_host["w2"], W_host["w2_scale"])
         times.append(time.perf_counter() - t0)
     return statistics.median(times), oracle.num_threads()
@@ -238,7 +241,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral",
-                    choices=["tiny", "mixtral", "qwen3", "qwen2", "dsv3", "dsv3mx"])
+                    choices=["tiny", "mixtral", "qwen3", "qwen2", "dsv3", "dsv3mx", "dsv3i8"])
     ap.add_argument("--tokens", type=int, default=16)
     ap.add_argument("--no-sweep", action="store_true", help="skip the graph-replay T sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -284,7 +287,7 @@ def main():
     if args.router:
         router_bench(moe, wl, args)
         return
-    dtype = wl.dtype if wl.dtype in ("fp8", "mxfp8") else "bf16"
+    dtype = wl.dtype if wl.dtype in ("fp8", "mxfp8", "int8") else "bf16"
     T = args.tokens
     log(f"[bench] workload={wl.name} T={T} dtype={dtype}: generating weights")
     W_rows = make_weights(wl, device="cuda")

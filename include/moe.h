@@ -73,8 +73,10 @@ typedef enum {
     MOE_DTYPE_BF16 = 0,      /* bf16 activations and weights, fp32 accumulation */
     MOE_DTYPE_FP8_W8A8 = 1,  /* e4m3 weights (per-output-channel fp32 scales) and
                                 e4m3 activations (per-row fp32 scales) */
-    MOE_DTYPE_MXFP8 = 2      /* OCP MXFP8: e4m3 values with one e8m0 scale per 32
+    MOE_DTYPE_MXFP8 = 2,     /* OCP MXFP8: e4m3 values with one e8m0 scale per 32
                                 consecutive K values, weights and activations */
+    MOE_DTYPE_INT8_W8A8 = 3  /* int8 weights (per-output-channel fp32 scales) and
+                                int8 activations (per-row fp32 scales) */
 } moe_dtype_t;
 
 /* One row tile of the task map: rows [row_begin, row_begin + rows) of the
@@ -304,6 +306,23 @@ int moe_forward_mxfp8(const void *x, const float *topk_w, const void *routing,
                       const uint8_t *w2, const uint8_t *w2_scale,
                       int T, int k, int E, int H, int I,
                       void *workspace, size_t workspace_bytes, void *out, void *stream);
+
+/* int8 w8a8 with per-channel weight scales (SGLang tuning guide: the
+ * int8_w8a8 dtype with per-channel quantisation).  As the fp8 pair, with
+ * int8 codes: w1/w2 (device) int8 [E][2I][H] / [E][H][I] packed by
+ * moe_pack_weights with dtype MOE_DTYPE_INT8_W8A8, w1_scale / w2_scale
+ * fp32 per output row.  x is quantised per token and SiLU(gate)*up per
+ * (token, expert) row by scale = fp32(amax/127), code =
+ * clamp(round_half_even(fp32(v * fp32(127/amax))), -127, 127) (an
+ * all-zero row: scale 1); the products run on the int8 MFMA with int32
+ * accumulation. */
+int moe_build_routing_int8(const int32_t *topk_ids, int T, int k, int E, int H, int I,
+                           void *routing, size_t routing_bytes, void *stream);
+int moe_forward_int8(const void *x, const float *topk_w, const void *routing,
+                     const int8_t *w1, const float *w1_scale,
+                     const int8_t *w2, const float *w2_scale,
+                     int T, int k, int E, int H, int I,
+                     void *workspace, size_t workspace_bytes, void *out, void *stream);
 
 /* Measurement hook.  When `events` is non-NULL (n >= 10 hipEvent_t
  * handles, host array), every later forward call records events[2*s]

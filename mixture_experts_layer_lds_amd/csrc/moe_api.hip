@@ -41,7 +41,8 @@ struct Plan {
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool known_dtype(int dtype) {
-  return dtype == MOE_DTYPE_BF16 || dtype == MOE_DTYPE_FP8_W8A8 || dtype == MOE_DTYPE_MXFP8;
+  return dtype == MOE_DTYPE_BF16 || dtype == MOE_DTYPE_FP8_W8A8 || dtype == MOE_DTYPE_MXFP8 ||
+         dtype == MOE_DTYPE_INT8_W8A8;
 }
 
 int check_shape(int T, int k, int E, int H, int I, int dtype = MOE_DTYPE_BF16) {
@@ -128,8 +129,8 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   const long avg = active > 0 ? (P + active - 1) / active : 1;
   const int esz_t = dtype == MOE_DTYPE_BF16 ? 2 : 1;
   const int nsteps1 = H * esz_t / 64, nsteps2 = I * esz_t / 64;
-  if (dtype == MOE_DTYPE_MXFP8) {
-    // MXFP8: register streaming at every size (its activation block scales
+  if (dtype == MOE_DTYPE_MXFP8 || dtype == MOE_DTYPE_INT8_W8A8) {
+    // MXFP8 and int8: register streaming at every size (its activation block scales
     // ride with the register stages; the strips' and tiles' LDS rings count
     // their loads exactly and carry no scale stream).  Two-step stages: one
     // 128-value unit of the scaled instruction each.
@@ -235,6 +236,19 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
     off = align_up(off + bytes, 256);
     return at;
   };
+  if (dtype == MOE_DTYPE_INT8_W8A8) {   // the fp8 streaming layout, int8 codes
+    W->xq = take((size_t)T * H);
+    W->x_scale = take(4 * (size_t)T);
+    W->x_scale_rows = take(4 * (P + 16));
+    W->g = take(4 * P * I);
+    W->h = take(P * I);
+    W->h_scale = take(4 * P);
+    W->y = take(2 * P * H);
+    W->total_bytes = off;
+    W->split_k1 = W->split_k2 = 1;
+    W->tiling = p.tiling;
+    return;
+  }
   if (dtype == MOE_DTYPE_MXFP8) {   // e4m3 codes + e8m0 codes per 32 values
     W->xq = take((size_t)T * H);
     W->x_scale = take((size_t)T * H / 32);
@@ -397,7 +411,7 @@ int forward_mx(const void* x, const float* topk_w, const void* routing, const vo
     a.w_rows = 2 * I;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    e = moe_host::launch_stream_gemm(a, true, true, true, p.mb, p.sw1, p.su1,
+    e = moe_host::launch_stream_gemm(a, true, true, 1, p.mb, p.sw1, p.su1,
                                      stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -422,13 +436,106 @@ int forward_mx(const void* x, const float* topk_w, const void* routing, const vo
     a.w_rows = H;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    e = moe_host::launch_stream_gemm(a, false, true, true, p.mb, p.sw2, p.su2,
+    e = moe_host::launch_stream_gemm(a, false, true, 1, p.mb, p.sw2, p.su2,
                                      stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
     StageScope st(s, 4);
     e = moe_host::launch_reduce(ws + W.y, true, 1, P, topk_w, R.pair_pos, R.expert_offsets, nullptr,
+                                E, T, k, H, static_cast<uint16_t*>(out), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+// int8 w8a8 forward (per-channel weight scales), register streaming: the
+// fp8 streaming sequence with int8 quantisation and the integer MFMA.
+int forward_i8(const void* x, const float* topk_w, const void* routing, const void* w1,
+               const float* w1_scale, const void* w2, const float* w2_scale, int T, int k, int E,
+               int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  int rc = check_shape(T, k, E, H, I, MOE_DTYPE_INT8_W8A8);
+  if (rc != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !topk_w || !routing || !w1 || !w2 || !w1_scale || !w2_scale || !workspace || !out)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16) ||
+      !aligned(topk_w, 4) || !aligned(routing, 16) || !aligned(workspace, 256) ||
+      !aligned(w1_scale, 4) || !aligned(w2_scale, 4))
+    return MOE_ERR_INVALID_ARG;
+  const Plan p = make_plan(MOE_DTYPE_INT8_W8A8, T, k, E, H, I);
+  moe_routing_layout_t L;
+  routing_layout(T, k, E, p, &L);
+  moe_workspace_layout_t W;
+  workspace_layout(MOE_DTYPE_INT8_W8A8, T, k, H, I, p, &W);
+  if (workspace_bytes < W.total_bytes) return MOE_ERR_BUFFER_TOO_SMALL;
+  int cus = 0;
+  if ((rc = cu_count(&cus)) != MOE_OK) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const RoutingView R = view_routing(routing, L);
+  char* ws = static_cast<char*>(workspace);
+  const int P = T * k;
+  int8_t* xq = reinterpret_cast<int8_t*>(ws + W.xq);
+  float* x_scale = reinterpret_cast<float*>(ws + W.x_scale);
+  float* x_rows = reinterpret_cast<float*>(ws + W.x_scale_rows);
+  float* h32 = reinterpret_cast<float*>(ws + W.g);
+  int8_t* hq = reinterpret_cast<int8_t*>(ws + W.h);
+  float* h_scale = reinterpret_cast<float*>(ws + W.h_scale);
+  hipError_t e;
+  {
+    StageScope st(s, 0);   // also clears the row-amax slots the gate-up epilogue folds into
+    e = moe_host::launch_quant_rows_i8(static_cast<const uint16_t*>(x), T, H, xq, x_scale, h_scale, k,
+                                       R.pair_pos, x_rows, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 1);
+    moe_host::StreamArgs a{};
+    a.a = xq;
+    a.b = w1;
+    a.b_scale = w1_scale;
+    a.row_scale = x_rows;
+    a.sorted_pairs = R.sorted_pairs;
+    a.header = R.header;
+    a.tasks = R.tasks;
+    a.c = h32;
+    a.row_amax = h_scale;
+    a.K = H;
+    a.N_out = I;
+    a.w_rows = 2 * I;
+    a.topk = k;
+    a.max_tasks = p.max_tasks;
+    e = moe_host::launch_stream_gemm(a, true, true, 2, p.mb, p.sw1, p.su1,
+                                     stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 2);
+    e = moe_host::launch_requant_rows_i8(h32, P, I, R.expert_offsets, E, hq, h_scale, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 3);
+    moe_host::StreamArgs a{};
+    a.a = hq;
+    a.b = w2;
+    a.b_scale = w2_scale;
+    a.sorted_pairs = R.sorted_pairs;
+    a.header = R.header;
+    a.tasks = R.tasks;
+    a.c = ws + W.y;
+    a.K = I;
+    a.N_out = H;
+    a.w_rows = H;
+    a.topk = k;
+    a.max_tasks = p.max_tasks;
+    e = moe_host::launch_stream_gemm(a, false, true, 2, p.mb, p.sw2, p.su2,
+                                     stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 4);
+    e = moe_host::launch_reduce(ws + W.y, true, 1, P, topk_w, R.pair_pos, R.expert_offsets, h_scale,
                                 E, T, k, H, static_cast<uint16_t*>(out), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -624,7 +731,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     a.w_rows = 2 * I;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    e = moe_host::launch_stream_gemm(a, true, fp8, false, p.mb, p.sw1, p.su1,
+    e = moe_host::launch_stream_gemm(a, true, fp8, 0, p.mb, p.sw1, p.su1,
                                      stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -649,7 +756,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     a.w_rows = H;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    e = moe_host::launch_stream_gemm(a, false, fp8, false, p.mb, p.sw2, p.su2,
+    e = moe_host::launch_stream_gemm(a, false, fp8, 0, p.mb, p.sw2, p.su2,
                                      stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -826,6 +933,19 @@ int moe_forward_mxfp8(const void* x, const float* topk_w, const void* routing, c
                       int k, int E, int H, int I, void* workspace, size_t workspace_bytes, void* out,
                       void* stream) {
   return forward_mx(x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
+                    workspace_bytes, out, stream);
+}
+
+int moe_build_routing_int8(const int32_t* topk_ids, int T, int k, int E, int H, int I,
+                           void* routing, size_t routing_bytes, void* stream) {
+  return build_routing(MOE_DTYPE_INT8_W8A8, topk_ids, T, k, E, H, I, routing, routing_bytes, stream);
+}
+
+int moe_forward_int8(const void* x, const float* topk_w, const void* routing, const int8_t* w1,
+                     const float* w1_scale, const int8_t* w2, const float* w2_scale, int T, int k,
+                     int E, int H, int I, void* workspace, size_t workspace_bytes, void* out,
+                     void* stream) {
+  return forward_i8(x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
                     workspace_bytes, out, stream);
 }
 

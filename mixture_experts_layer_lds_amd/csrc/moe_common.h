@@ -266,8 +266,18 @@ struct StreamArgs {
 
 // (mb, waves, u) = 16-row blocks per tile, waves per workgroup, K steps per stage.
 bool stream_config_supported(int mb, int waves, int u);
-hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, bool mx, int mb, int waves,
+// kind: 0 per-channel scales (bf16, or fp8 by `fp8`), 1 MXFP8 block scales,
+// 2 int8 w8a8 (per-channel scales).
+hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int kind, int mb, int waves,
                               int u, int grid, hipStream_t s);
+// int8 w8a8: per-token quantisation of bf16 x (row-amax slots cleared,
+// per-sorted-row scales written as the fp8 variant) and per-row
+// requantisation of fp32 h with the amax held in h_scale.
+hipError_t launch_quant_rows_i8(const uint16_t* x, int T, int H, int8_t* xq, float* scale,
+                                float* zero_rows, int zk, const int32_t* pair_pos, float* scale_rows,
+                                hipStream_t s);
+hipError_t launch_requant_rows_i8(const float* h32, int P, int I, const int32_t* expert_offsets, int E,
+                                  int8_t* hq, float* h_scale, hipStream_t s);
 // MXFP8 quantisation: bf16 rows x[T][H] -> e4m3 xq + e8m0 codes [T][H/32];
 // fp32 rows h[P][I] (valid sorted rows only) -> hq + codes [P][I/32].
 hipError_t launch_mx_quant_bf16(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* sx, hipStream_t s);

@@ -35,6 +35,10 @@
 //    row's four block scales of unit u shifted to the lane's byte.  The
 //    epilogue then applies no scale; gate-up writes fp32 h for the MX
 //    requantisation pass.
+//  * int8 w8a8 (I8): one integer instruction (v_mfma_i32_16x16x64_i8) per
+//    64-byte step on the same fragments; the int32 sums become fp32 where
+//    the waves' partial sums meet, and the per-channel epilogue of the fp8
+//    path follows.
 #include <type_traits>
 
 #include "lds_dma.h"
@@ -58,11 +62,12 @@ __device__ __forceinline__ void stream_mfma(f32x4& acc, const u32x4& a, const u3
 
 // MB 16-row blocks per task tile, W waves per workgroup (K slices), U
 // 64-byte K steps per register stage.
-template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX>
+template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX, bool I8>
 __global__ void __launch_bounds__(W * 64)
 stream_gemm_kernel(moe_host::StreamArgs g) {
   constexpr int NB = kStreamNB;
   static_assert(!MX || (FP8 && U == 2), "MX stages are one 128-value K unit");
+  static_assert(!I8 || (FP8 && !MX), "int8 uses the 1-byte per-channel path");
   __shared__ f32x4 red[W][MB][NB][64];   // the waves' partial sums of one item
   const int lane = threadIdx.x & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
@@ -184,6 +189,18 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
           for (int q = 0; q < NB; q++)
             mfma_mx_k128(acc[b][q], fa[0][b], fa[1][b], fb[0][q], fb[1][q], (int)(sa[b] >> sh),
                          (int)(sb[q] >> sh));
+      } else if constexpr (I8) {
+        typedef int i32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int u = 0; u < U; u++)
+#pragma unroll
+          for (int b = 0; b < MB; b++)
+#pragma unroll
+            for (int q = 0; q < NB; q++)
+              acc[b][q] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, fa[u][b]),
+                                                              __builtin_bit_cast(i32x4, fb[u][q]),
+                                                              __builtin_bit_cast(i32x4, acc[b][q]), 0, 0, 0));
       } else {
 #pragma unroll
         for (int u = 0; u < U; u++)
@@ -221,7 +238,14 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
 #pragma unroll
     for (int m = 0; m < MB; m++)
 #pragma unroll
-      for (int q = 0; q < NB; q++) red[wave][m][q][lane] = acc[m][q];
+      for (int q = 0; q < NB; q++) {
+        if constexpr (I8) {   // int32 sums (|sum| <= 127^2 K < 2^31) to fp32
+          typedef int i32x4 __attribute__((ext_vector_type(4)));
+          red[wave][m][q][lane] = __builtin_convertvector(__builtin_bit_cast(i32x4, acc[m][q]), f32x4);
+        } else {
+          red[wave][m][q][lane] = acc[m][q];
+        }
+      }
     __syncthreads();
 
     // Epilogue of row block m by wave m % W: lane holds column (lane % 16)
@@ -302,21 +326,25 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
   }
 }
 
-template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX>
+template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX, bool I8 = false>
 static hipError_t launch_stream_t(const moe_host::StreamArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((stream_gemm_kernel<MB, W, U, GATEUP, FP8, MX>), dim3(grid), dim3(W * 64), 0, s, a);
+  hipLaunchKernelGGL((stream_gemm_kernel<MB, W, U, GATEUP, FP8, MX, I8>), dim3(grid), dim3(W * 64), 0, s, a);
   return hipGetLastError();
 }
 
+// kind: 0 per-channel (bf16 or fp8 by `fp8`), 1 MX, 2 int8
 template <int MB, int W, int U>
-static hipError_t launch_stream_w(const moe_host::StreamArgs& a, bool gateup, bool fp8, bool mx,
+static hipError_t launch_stream_w(const moe_host::StreamArgs& a, bool gateup, bool fp8, int kind,
                                   int grid, hipStream_t s) {
-  if (mx) {
+  if (kind == 1) {
     if constexpr (U == 2)
       return gateup ? launch_stream_t<MB, W, U, true, true, true>(a, grid, s)
                     : launch_stream_t<MB, W, U, false, true, true>(a, grid, s);
     return hipErrorInvalidValue;
   }
+  if (kind == 2)
+    return gateup ? launch_stream_t<MB, W, U, true, true, false, true>(a, grid, s)
+                  : launch_stream_t<MB, W, U, false, true, false, true>(a, grid, s);
   if (gateup) return fp8 ? launch_stream_t<MB, W, U, true, true, false>(a, grid, s)
                          : launch_stream_t<MB, W, U, true, false, false>(a, grid, s);
   return fp8 ? launch_stream_t<MB, W, U, false, true, false>(a, grid, s)
@@ -343,10 +371,10 @@ bool stream_config_supported(int mb, int waves, int u) {
   return false;
 }
 
-hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, bool mx, int mb, int waves,
+hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int kind, int mb, int waves,
                               int u, int grid, hipStream_t s) {
 #define MOE_STREAM_CASE(M, Wv, Uv) \
-  if (mb == M && waves == Wv && u == Uv) return moe::launch_stream_w<M, Wv, Uv>(a, gateup, fp8, mx, grid, s);
+  if (mb == M && waves == Wv && u == Uv) return moe::launch_stream_w<M, Wv, Uv>(a, gateup, fp8, kind, grid, s);
   MOE_STREAM_CONFIGS(MOE_STREAM_CASE)
 #undef MOE_STREAM_CASE
   return hipErrorInvalidValue;
