@@ -54,7 +54,7 @@ class Workload:
     H: int
     I: int
     k: int
-    dtype: str          # "f32" (tiny parity case), "bf16", "fp8", "mxfp8" or "int8"
+    dtype: str          # "f32" (tiny parity case), "bf16", "fp8", "mxfp8", "int8" or "int4"
     Ts: tuple
     routing: str        # "softmax", "biased" or "hot0"
     label: str
@@ -79,6 +79,9 @@ WORKLOADS = {
     "dsv3i8": Workload("dsv3i8", 5, 256, 7168, 2048, 8, "int8",
                        (1, 16, 128, 1024, 4096), "softmax",
                        "DeepSeek-V3-shaped MoE layer, int8 w8a8 per-channel, E=256 H=7168 I=2048 top-8"),
+    "mixtral4": Workload("mixtral4", 2, 8, 4096, 14336, 2, "int4",
+                         (1, 2, 4, 8, 16, 32, 64), "softmax",
+                         "Mixtral-8x7B-shaped MoE layer, int4 w4a16 (group 128), E=8 H=4096 I=14336 top-2"),
     "dsv3mx": Workload("dsv3mx", 5, 256, 7168, 2048, 8, "mxfp8",
                        (1, 16, 128, 1024, 4096), "softmax",
                        "DeepSeek-V3-shaped MoE layer, MXFP8 (OCP MX, 32-element blocks), E=256 H=7168 I=2048 top-8"),
@@ -217,6 +220,36 @@ def _fp8_experts(E, rows, cols, std, g, device, chunk_elems=1 << 27):
     return codes, scales
 
 
+def quantize_weight_int4(w: torch.Tensor, group: int = 128):
+    """Symmetric int4 codes of fp32 weights [.., rows, cols] (cols % group
+    == 0) with one fp32 scale per `group` consecutive values of a row:
+    scale = amax / 7 (1 for an all-zero group), q = torch's half-to-even
+    rounding of w / scale clamped to [-8, 7], two codes per byte (the lower
+    column in the low nibble, two's complement).  Returns (uint8 [.., rows,
+    cols/2], fp32 scales [.., rows, cols/group])."""
+    *lead, cols = w.shape
+    g = w.reshape(*lead, cols // group, group)
+    amax = g.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / 7.0, torch.ones_like(amax)).float()
+    q = torch.round(g / scale.unsqueeze(-1)).clamp(-8, 7).to(torch.int16).reshape(*lead, cols)
+    n = (q & 0xF).to(torch.uint8)
+    packed = n[..., 0::2] | (n[..., 1::2] << 4)
+    return packed.contiguous(), scale.contiguous()
+
+
+def _int4_experts(E, rows, cols, std, g, device, chunk_elems=1 << 27):
+    codes = torch.empty(E, rows, cols // 2, dtype=torch.uint8, device=device)
+    scales = torch.empty(E, rows, cols // 128, dtype=torch.float32, device=device)
+    per = max(1, chunk_elems // (rows * cols))
+    for e0 in range(0, E, per):
+        e1 = min(E, e0 + per)
+        blk = torch.randn(e1 - e0, rows, cols, generator=g, device=device, dtype=torch.float32) * std
+        q, sc = quantize_weight_int4(blk)
+        codes[e0:e1] = q
+        scales[e0:e1] = sc
+    return codes, scales
+
+
 def quantize_weight_int8(w: torch.Tensor):
     """Per-output-channel symmetric int8 codes of fp32 weights [.., rows, cols]:
     scale = amax(row) / 127 (1 for an all-zero row), codes = torch's
@@ -284,6 +317,10 @@ def make_weights(wl: Workload, device="cpu", seed: Optional[int] = None, E: Opti
     if wl.dtype == "fp8":
         w1, s1 = _fp8_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device)
         w2, s2 = _fp8_experts(E, H, I, 1.0 / math.sqrt(I), g, device)
+        return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2}
+    if wl.dtype == "int4":
+        w1, s1 = _int4_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device)
+        w2, s2 = _int4_experts(E, H, I, 1.0 / math.sqrt(I), g, device)
         return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2}
     if wl.dtype == "int8":
         w1, s1 = _int8_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device)

@@ -15,6 +15,10 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                                  448 row, power-of-two rows) and torch's cast.
   route                       -- pinned: brute-force stable sort, invariants,
                                  exhaustive tiny cases.
+  w4_dequant / forward_w4a16    -- pinned: nibble order and sign against
+                                 torch bit operations, exact cases, a
+                                 dense torch reference on dequantised
+                                 weights.
   int8_quant_row / forward_int8 -- pinned: worked cases (integers at amax
                                  127, ties to even, clamping), an independent
                                  torch quantiser, a dense torch reference
@@ -98,6 +102,10 @@ def lib():
         L.oracle_forward_fp8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P, P, P, P, P]
         L.oracle_router_topk.restype = None
         L.oracle_router_topk.argtypes = [P, i, i, i, i, i, P, P]
+        L.oracle_forward_w4a16.restype = None
+        L.oracle_forward_w4a16.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P]
+        L.oracle_w4_dequant.restype = None
+        L.oracle_w4_dequant.argtypes = [P, P, i, i, P]
         L.oracle_int8_quant_row.restype = None
         L.oracle_int8_quant_row.argtypes = [P, i, P, P]
         L.oracle_int8_quant_rows_bf16.restype = None
@@ -227,6 +235,41 @@ def router_topk(logits, k: int, renormalize: bool = True, n_shared: int = 0):
     if T:
         lib().oracle_router_topk(_p(la), T, E, k, int(bool(renormalize)), n_shared, _p(ids), _p(w))
     return ids, w
+
+
+def w4_dequant(codes, scales):
+    """fp64 values [R][n] of int4 rows: codes uint8 [R][n/2] (low nibble =
+    lower K index, two's complement), fp32 scales [R][n/128]."""
+    c = _np(codes, np.uint8)
+    sc = _np(scales, np.float32)
+    R, nb = c.shape
+    n = 2 * nb
+    out = np.zeros((R, n), dtype=np.float64)
+    lib().oracle_w4_dequant(_p(c), _p(sc), R, n, _p(out))
+    return out
+
+
+def forward_w4a16(x, topk_w, ids, W1, s1, W2, s2, rows=None):
+    """int4 w4a16 layer output in fp64: x bf16 [T][H]; W1 uint8 [E][2I][H/2],
+    s1 fp32 [E][2I][H/128]; W2 uint8 [E][H][I/2], s2 fp32 [E][H][I/128]."""
+    xa = _np(x, np.uint16)
+    T, H = xa.shape
+    ida = _np(ids, np.int32)
+    k = ida.shape[1]
+    wa = _np(topk_w, np.float32)
+    W1a = _np(W1, np.uint8)
+    W2a = _np(W2, np.uint8)
+    s1a = _np(s1, np.float32)
+    s2a = _np(s2, np.float32)
+    E, I2, _ = W1a.shape
+    I = I2 // 2
+    assert W1a.shape == (E, I2, H // 2) and s1a.shape == (E, I2, H // 128)
+    assert W2a.shape == (E, H, I // 2) and s2a.shape == (E, H, I // 128)
+    r, n = _rows_arg(rows, T)
+    out = np.zeros((n, H), dtype=np.float64)
+    lib().oracle_forward_w4a16(_p(xa), _p(wa), _p(ida), _p(W1a), _p(s1a), _p(W2a), _p(s2a),
+                               T, k, E, H, I, _p(r) if r is not None else None, n, _p(out))
+    return out
 
 
 def int8_quant_row(v):

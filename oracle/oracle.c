@@ -579,6 +579,82 @@ void oracle_forward_int8(const uint16_t *x, const float *topk_w, const int32_t *
 }
 
 /*
+ * int4 w4a16 (SGLang tuning guide dtype list: int4_w4a16): int4 weights
+ * with one fp32 scale per 128 consecutive K values of a row (a group), bf16
+ * activations.  Weight element (n, k) = q * scale[n][k / 128] with q a
+ * two's-complement nibble in [-8, 7]; bytes hold two elements, the lower
+ * K index in the low nibble.  The activations are not quantised: the layer
+ * is the bf16 layer on the dequantised weights, in fp64 here.
+ */
+static int nibble(const uint8_t *row, int k)
+{
+    const int v = (row[k / 2] >> (4 * (k & 1))) & 0xF;
+    return v >= 8 ? v - 16 : v;
+}
+
+static void w4_row(const uint8_t *codes, const float *scales, int n, double *dst)
+{
+    for (int k = 0; k < n; k++)
+        dst[k] = (double)nibble(codes, k) * (double)scales[k / 128];
+}
+
+static void token_w4a16(const uint16_t *x, const float *topk_w, const int32_t *ids,
+                        const uint8_t *W1, const float *s1, const uint8_t *W2, const float *s2,
+                        int t, int k, int E, int H, int I, double *acc)
+{
+    double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+    double *wr = (double *)malloc(sizeof(double) * (size_t)(H > I ? H : I));
+    double *hd = (double *)malloc(sizeof(double) * (size_t)I);
+    for (int h = 0; h < H; h++)
+        xd[h] = BF16_VALUE[x[(size_t)t * H + h]];
+    for (int m = 0; m < H; m++)
+        acc[m] = 0.0;
+    for (int j = 0; j < k; j++) {
+        int p = t * k + j;
+        int e = ids[p];
+        if (e < 0 || e >= E)
+            continue;
+        double w = (double)topk_w[p];
+        for (int n = 0; n < I; n++) {
+            size_t rg = (size_t)e * 2 * I + n, ru = rg + I;
+            w4_row(W1 + rg * (H / 2), s1 + rg * (H / 128), H, wr);
+            double g = dot(wr, xd, H);
+            w4_row(W1 + ru * (H / 2), s1 + ru * (H / 128), H, wr);
+            double u = dot(wr, xd, H);
+            hd[n] = silu(g) * u;
+        }
+        for (int m = 0; m < H; m++) {
+            size_t r2 = (size_t)e * H + m;
+            w4_row(W2 + r2 * (I / 2), s2 + r2 * (I / 128), I, wr);
+            acc[m] += w * dot(wr, hd, I);
+        }
+    }
+    free(xd); free(wr); free(hd);
+}
+
+void oracle_forward_w4a16(const uint16_t *x, const float *topk_w, const int32_t *ids,
+                          const uint8_t *W1, const float *s1, const uint8_t *W2, const float *s2,
+                          int T, int k, int E, int H, int I, const int32_t *rows, int nrows,
+                          double *out)
+{
+    oracle_init();
+    if (!rows)
+        nrows = T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; r++) {
+        int t = rows ? rows[r] : r;
+        token_w4a16(x, topk_w, ids, W1, s1, W2, s2, t, k, E, H, I, out + (size_t)r * H);
+    }
+}
+
+/* dequantised int4 rows: codes [rows][n/2], scales [rows][n/128] -> dst [rows][n] */
+void oracle_w4_dequant(const uint8_t *codes, const float *scales, int rows, int n, double *dst)
+{
+    for (long r = 0; r < rows; r++)
+        w4_row(codes + r * (n / 2), scales + r * (n / 128), n, dst + r * n);
+}
+
+/*
  * MXFP8 block-scaled fp8 (SGLang tuning guide, section on block shapes:
  * gfx95 devices keep MXFP8's [1, 32] block shape instead of remapping it
  * to [128, 128]).  OCP Microscaling format: every 32 consecutive elements
