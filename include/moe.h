@@ -75,8 +75,10 @@ typedef enum {
                                 e4m3 activations (per-row fp32 scales) */
     MOE_DTYPE_MXFP8 = 2,     /* OCP MXFP8: e4m3 values with one e8m0 scale per 32
                                 consecutive K values, weights and activations */
-    MOE_DTYPE_INT8_W8A8 = 3  /* int8 weights (per-output-channel fp32 scales) and
+    MOE_DTYPE_INT8_W8A8 = 3, /* int8 weights (per-output-channel fp32 scales) and
                                 int8 activations (per-row fp32 scales) */
+    MOE_DTYPE_INT4_W4A16 = 4 /* int4 weights (fp32 scale per 128 K values of a row),
+                                bf16 activations */
 } moe_dtype_t;
 
 /* One row tile of the task map: rows [row_begin, row_begin + rows) of the
@@ -321,6 +323,23 @@ int moe_build_routing_int8(const int32_t *topk_ids, int T, int k, int E, int H, 
 int moe_forward_int8(const void *x, const float *topk_w, const void *routing,
                      const int8_t *w1, const float *w1_scale,
                      const int8_t *w2, const float *w2_scale,
+                     int T, int k, int E, int H, int I,
+                     void *workspace, size_t workspace_bytes, void *out, void *stream);
+
+/* int4 w4a16 (SGLang tuning guide dtype list: int4_w4a16).  w1 (device)
+ * uint8 [E][2I][H/2] and w2 (device) uint8 [E][H][I/2]: two's-complement
+ * int4 codes, two a byte, the lower K index in the low nibble, packed by
+ * moe_pack_weights with dtype MOE_DTYPE_INT4_W4A16 (cols = the K length);
+ * w1_scale (device) fp32 [E][2I][H/128], w2_scale (device) fp32
+ * [E][H][I/128]: weight (n, k) = code * scale[n][k / 128].  x and the
+ * intermediate stay bf16 (bf16 MFMA on weights converted in registers,
+ * fp32 accumulation, the group scale applied per 128 K values).  H and I
+ * must be multiples of 128. */
+int moe_build_routing_int4(const int32_t *topk_ids, int T, int k, int E, int H, int I,
+                           void *routing, size_t routing_bytes, void *stream);
+int moe_forward_int4(const void *x, const float *topk_w, const void *routing,
+                     const uint8_t *w1, const float *w1_scale,
+                     const uint8_t *w2, const float *w2_scale,
                      int T, int k, int E, int H, int I,
                      void *workspace, size_t workspace_bytes, void *out, void *stream);
 

@@ -42,7 +42,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool known_dtype(int dtype) {
   return dtype == MOE_DTYPE_BF16 || dtype == MOE_DTYPE_FP8_W8A8 || dtype == MOE_DTYPE_MXFP8 ||
-         dtype == MOE_DTYPE_INT8_W8A8;
+         dtype == MOE_DTYPE_INT8_W8A8 || dtype == MOE_DTYPE_INT4_W4A16;
 }
 
 int check_shape(int T, int k, int E, int H, int I, int dtype = MOE_DTYPE_BF16) {
@@ -50,7 +50,8 @@ int check_shape(int T, int k, int E, int H, int I, int dtype = MOE_DTYPE_BF16) {
     return MOE_ERR_INVALID_ARG;
   if (H % 64 || I % 64 || H > 65536 || I > 65536) return MOE_ERR_UNSUPPORTED_SHAPE;
   // MX: both reductions in whole 128-value units of the scaled instruction
-  if (dtype == MOE_DTYPE_MXFP8 && (H % 128 || I % 128)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if ((dtype == MOE_DTYPE_MXFP8 || dtype == MOE_DTYPE_INT4_W4A16) && (H % 128 || I % 128))
+    return MOE_ERR_UNSUPPORTED_SHAPE;   // whole 128-value units / scale groups
   if ((long)T * k > moe::kMaxPairs) return MOE_ERR_UNSUPPORTED_SHAPE;
   return MOE_OK;
 }
@@ -129,6 +130,33 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   const long avg = active > 0 ? (P + active - 1) / active : 1;
   const int esz_t = dtype == MOE_DTYPE_BF16 ? 2 : 1;
   const int nsteps1 = H * esz_t / 64, nsteps2 = I * esz_t / 64;
+  if (dtype == MOE_DTYPE_INT4_W4A16) {
+    // int4 weights: register streaming (128-value K steps) at every size;
+    // waves per workgroup by the streaming cost model on whole steps
+    p.tiling = kStreaming;
+    p.block_m = avg <= 8 ? 16 : (avg <= 16 ? 32 : 64);
+    p.mb = p.block_m / 16;
+    p.max_tasks = (int)(P / p.block_m + (P < E ? P : E));
+    long est = (P + p.block_m - 1) / p.block_m;
+    if (est < active) est = active;
+    auto pick = [&](int steps, long items) {
+      int best = 1;
+      long best_cost = -1;
+      for (int w = 1; w <= 8; w *= 2) {
+        if (steps % w) continue;
+        long grid = kStreamWaves / w;
+        if (items < grid) grid = items;
+        if (grid < 1) grid = 1;
+        const long cost = (items + grid - 1) / grid * (steps / w + 2);
+        if (best_cost < 0 || cost < best_cost) best = w, best_cost = cost;
+      }
+      return best;
+    };
+    p.sw1 = pick(H / 128, est * ((long)I / 16));
+    p.sw2 = pick(I / 128, est * ((long)H / 32));
+    p.su1 = p.su2 = 1;
+    return p;
+  }
   if (dtype == MOE_DTYPE_MXFP8 || dtype == MOE_DTYPE_INT8_W8A8) {
     // MXFP8 and int8: register streaming at every size (its activation block scales
     // ride with the register stages; the strips' and tiles' LDS rings count
@@ -236,6 +264,15 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
     off = align_up(off + bytes, 256);
     return at;
   };
+  if (dtype == MOE_DTYPE_INT4_W4A16) {   // bf16 activations: bf16 h and y rows
+    W->xq = W->x_scale = W->x_scale_rows = W->g = W->h_scale = kNone;
+    W->h = take(2 * P * I);
+    W->y = take(2 * P * H);
+    W->total_bytes = off;
+    W->split_k1 = W->split_k2 = 1;
+    W->tiling = p.tiling;
+    return;
+  }
   if (dtype == MOE_DTYPE_INT8_W8A8) {   // the fp8 streaming layout, int8 codes
     W->xq = take((size_t)T * H);
     W->x_scale = take(4 * (size_t)T);
@@ -438,6 +475,81 @@ int forward_mx(const void* x, const float* topk_w, const void* routing, const vo
     a.max_tasks = p.max_tasks;
     e = moe_host::launch_stream_gemm(a, false, true, 1, p.mb, p.sw2, p.su2,
                                      stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 4);
+    e = moe_host::launch_reduce(ws + W.y, true, 1, P, topk_w, R.pair_pos, R.expert_offsets, nullptr,
+                                E, T, k, H, static_cast<uint16_t*>(out), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+// int4 w4a16 forward: register-streaming gate-up (int4 weights converted in
+// registers, SiLU-and-mul in the epilogue, bf16 h), down (bf16 rows), the
+// top-k reduction.
+int forward_w4(const void* x, const float* topk_w, const void* routing, const void* w1,
+               const float* w1_scale, const void* w2, const float* w2_scale, int T, int k, int E,
+               int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  int rc = check_shape(T, k, E, H, I, MOE_DTYPE_INT4_W4A16);
+  if (rc != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !topk_w || !routing || !w1 || !w2 || !w1_scale || !w2_scale || !workspace || !out)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16) ||
+      !aligned(topk_w, 4) || !aligned(routing, 16) || !aligned(workspace, 256) ||
+      !aligned(w1_scale, 4) || !aligned(w2_scale, 4))
+    return MOE_ERR_INVALID_ARG;
+  const Plan p = make_plan(MOE_DTYPE_INT4_W4A16, T, k, E, H, I);
+  moe_routing_layout_t L;
+  routing_layout(T, k, E, p, &L);
+  moe_workspace_layout_t W;
+  workspace_layout(MOE_DTYPE_INT4_W4A16, T, k, H, I, p, &W);
+  if (workspace_bytes < W.total_bytes) return MOE_ERR_BUFFER_TOO_SMALL;
+  int cus = 0;
+  if ((rc = cu_count(&cus)) != MOE_OK) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const RoutingView R = view_routing(routing, L);
+  char* ws = static_cast<char*>(workspace);
+  const int P = T * k;
+  hipError_t e;
+  {
+    StageScope st(s, 1);
+    moe_host::StreamArgs a{};
+    a.a = x;
+    a.b = w1;
+    a.b_scale = w1_scale;
+    a.sorted_pairs = R.sorted_pairs;
+    a.header = R.header;
+    a.tasks = R.tasks;
+    a.c = ws + W.h;
+    a.K = H;
+    a.N_out = I;
+    a.w_rows = 2 * I;
+    a.topk = k;
+    a.max_tasks = p.max_tasks;
+    e = moe_host::launch_stream_w4(a, true, p.mb, p.sw1,
+                                   stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 3);
+    moe_host::StreamArgs a{};
+    a.a = ws + W.h;
+    a.b = w2;
+    a.b_scale = w2_scale;
+    a.sorted_pairs = R.sorted_pairs;
+    a.header = R.header;
+    a.tasks = R.tasks;
+    a.c = ws + W.y;
+    a.K = I;
+    a.N_out = H;
+    a.w_rows = H;
+    a.topk = k;
+    a.max_tasks = p.max_tasks;
+    e = moe_host::launch_stream_w4(a, false, p.mb, p.sw2,
+                                   stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
@@ -804,7 +916,9 @@ int moe_pack_weights(const void* w, int E, int rows, int cols, int dtype, void* 
                      void* stream) {
   if (!known_dtype(dtype)) return MOE_ERR_INVALID_ARG;
   if (E < 1 || rows < 1 || cols < 1) return MOE_ERR_INVALID_ARG;
-  const long row_bytes = (long)cols * (dtype == MOE_DTYPE_BF16 ? 2 : 1);
+  const long row_bytes = dtype == MOE_DTYPE_INT4_W4A16 ? (long)cols / 2
+                                                      : (long)cols * (dtype == MOE_DTYPE_BF16 ? 2 : 1);
+  if (dtype == MOE_DTYPE_INT4_W4A16 && cols % 2) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (rows % 16 || row_bytes % 64 || rows > 2 * 65536 || cols > 65536)
     return MOE_ERR_UNSUPPORTED_SHAPE;
   if (!w || !packed || !aligned(w, 16) || !aligned(packed, 16)) return MOE_ERR_INVALID_ARG;
@@ -933,6 +1047,19 @@ int moe_forward_mxfp8(const void* x, const float* topk_w, const void* routing, c
                       int k, int E, int H, int I, void* workspace, size_t workspace_bytes, void* out,
                       void* stream) {
   return forward_mx(x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
+                    workspace_bytes, out, stream);
+}
+
+int moe_build_routing_int4(const int32_t* topk_ids, int T, int k, int E, int H, int I,
+                           void* routing, size_t routing_bytes, void* stream) {
+  return build_routing(MOE_DTYPE_INT4_W4A16, topk_ids, T, k, E, H, I, routing, routing_bytes, stream);
+}
+
+int moe_forward_int4(const void* x, const float* topk_w, const void* routing, const uint8_t* w1,
+                     const float* w1_scale, const uint8_t* w2, const float* w2_scale, int T, int k,
+                     int E, int H, int I, void* workspace, size_t workspace_bytes, void* out,
+                     void* stream) {
+  return forward_w4(x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
                     workspace_bytes, out, stream);
 }
 

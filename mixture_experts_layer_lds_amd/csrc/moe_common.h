@@ -278,6 +278,10 @@ hipError_t launch_quant_rows_i8(const uint16_t* x, int T, int H, int8_t* xq, flo
                                 hipStream_t s);
 hipError_t launch_requant_rows_i8(const float* h32, int P, int I, const int32_t* expert_offsets, int E,
                                   int8_t* hq, float* h_scale, hipStream_t s);
+// int4 w4a16 register-streaming GEMM: a bf16 activations, b packed int4
+// weights, b_scale fp32 [E][w_rows][K/128] group scales; gate-up writes bf16
+// SiLU(gate)*up, down bf16 rows.
+hipError_t launch_stream_w4(const StreamArgs& a, bool gateup, int mb, int waves, int grid, hipStream_t s);
 // MXFP8 quantisation: bf16 rows x[T][H] -> e4m3 xq + e8m0 codes [T][H/32];
 // fp32 rows h[P][I] (valid sorted rows only) -> hq + codes [P][I/32].
 hipError_t launch_mx_quant_bf16(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* sx, hipStream_t s);
