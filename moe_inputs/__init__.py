@@ -54,7 +54,7 @@ class Workload:
     H: int
     I: int
     k: int
-    dtype: str          # "f32" (tiny parity case), "bf16", "fp8", "mxfp8", "int8" or "int4"
+    dtype: str          # "f32" (tiny parity case), "bf16", "fp8", "fp8b" (block-scaled), "mxfp8", "int8" or "int4"
     Ts: tuple
     routing: str        # "softmax", "biased" or "hot0"
     label: str
@@ -82,6 +82,9 @@ WORKLOADS = {
     "mixtral4": Workload("mixtral4", 2, 8, 4096, 14336, 2, "int4",
                          (1, 2, 4, 8, 16, 32, 64), "softmax",
                          "Mixtral-8x7B-shaped MoE layer, int4 w4a16 (group 128), E=8 H=4096 I=14336 top-2"),
+    "dsv3b": Workload("dsv3b", 5, 256, 7168, 2048, 8, "fp8b",
+                      (1, 16, 128, 1024, 4096), "softmax",
+                      "DeepSeek-V3-shaped MoE layer, fp8 w8a8 with 128x128 weight blocks and 1x128 token groups, E=256 H=7168 I=2048 top-8"),
     "dsv3mx": Workload("dsv3mx", 5, 256, 7168, 2048, 8, "mxfp8",
                        (1, 16, 128, 1024, 4096), "softmax",
                        "DeepSeek-V3-shaped MoE layer, MXFP8 (OCP MX, 32-element blocks), E=256 H=7168 I=2048 top-8"),
@@ -220,6 +223,32 @@ def _fp8_experts(E, rows, cols, std, g, device, chunk_elems=1 << 27):
     return codes, scales
 
 
+def quantize_weight_block_fp8(w: torch.Tensor, block: int = 128):
+    """e4m3 codes of fp32 weights [.., rows, cols] (both multiples of `block`)
+    with one fp32 scale per block x block tile: scale = amax(tile) / 448 (1 for
+    an all-zero tile), codes = torch's RNE e4m3 cast of w / scale.  Returns
+    (uint8 codes [.., rows, cols], fp32 scales [.., rows/block, cols/block])."""
+    *lead, rows, cols = w.shape
+    t = w.reshape(*lead, rows // block, block, cols // block, block)
+    amax = t.abs().amax(dim=(-3, -1))
+    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax)).float()
+    q = (t / scale.unsqueeze(-1).unsqueeze(-3)).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).reshape(*lead, rows, cols).contiguous(), scale.contiguous()
+
+
+def _block_fp8_experts(E, rows, cols, std, g, device, chunk_elems=1 << 27):
+    codes = torch.empty(E, rows, cols, dtype=torch.uint8, device=device)
+    scales = torch.empty(E, rows // 128, cols // 128, dtype=torch.float32, device=device)
+    per = max(1, chunk_elems // (rows * cols))
+    for e0 in range(0, E, per):
+        e1 = min(E, e0 + per)
+        blk = torch.randn(e1 - e0, rows, cols, generator=g, device=device, dtype=torch.float32) * std
+        q, sc = quantize_weight_block_fp8(blk)
+        codes[e0:e1] = q
+        scales[e0:e1] = sc
+    return codes, scales
+
+
 def quantize_weight_int4(w: torch.Tensor, group: int = 128):
     """Symmetric int4 codes of fp32 weights [.., rows, cols] (cols % group
     == 0) with one fp32 scale per `group` consecutive values of a row:
@@ -317,6 +346,10 @@ def make_weights(wl: Workload, device="cpu", seed: Optional[int] = None, E: Opti
     if wl.dtype == "fp8":
         w1, s1 = _fp8_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device)
         w2, s2 = _fp8_experts(E, H, I, 1.0 / math.sqrt(I), g, device)
+        return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2}
+    if wl.dtype == "fp8b":
+        w1, s1 = _block_fp8_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device)
+        w2, s2 = _block_fp8_experts(E, H, I, 1.0 / math.sqrt(I), g, device)
         return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2}
     if wl.dtype == "int4":
         w1, s1 = _int4_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device)

@@ -15,6 +15,9 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                                  448 row, power-of-two rows) and torch's cast.
   route                       -- pinned: brute-force stable sort, invariants,
                                  exhaustive tiny cases.
+  quant_groups / forward_fp8_block -- pinned: groups equal the per-row rule
+                                 on each group, a dense torch reference on
+                                 dequantised block weights and activations.
   w4_dequant / forward_w4a16    -- pinned: nibble order and sign against
                                  torch bit operations, exact cases, a
                                  dense torch reference on dequantised
@@ -102,6 +105,10 @@ def lib():
         L.oracle_forward_fp8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P, P, P, P, P]
         L.oracle_router_topk.restype = None
         L.oracle_router_topk.argtypes = [P, i, i, i, i, i, P, P]
+        L.oracle_quant_groups.restype = None
+        L.oracle_quant_groups.argtypes = [P, i, P, P]
+        L.oracle_forward_fp8_block.restype = None
+        L.oracle_forward_fp8_block.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P, P, P, P, P]
         L.oracle_forward_w4a16.restype = None
         L.oracle_forward_w4a16.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P]
         L.oracle_w4_dequant.restype = None
@@ -235,6 +242,46 @@ def router_topk(logits, k: int, renormalize: bool = True, n_shared: int = 0):
     if T:
         lib().oracle_router_topk(_p(la), T, E, k, int(bool(renormalize)), n_shared, _p(ids), _p(w))
     return ids, w
+
+
+def quant_groups(v):
+    """Per-128-group fp8 quantisation of one fp32 row (n % 128 == 0): e4m3
+    codes uint8 [n] and fp32 scales [n/128], each group by the per-row rule."""
+    va = _np(v, np.float32).reshape(-1)
+    codes = np.zeros(va.size, dtype=np.uint8)
+    sc = np.zeros(va.size // 128, dtype=np.float32)
+    lib().oracle_quant_groups(_p(va), va.size, _p(codes), _p(sc))
+    return codes, sc
+
+
+def forward_fp8_block(x, topk_w, ids, W1, s1, W2, s2, rows=None, want_quant=False):
+    """Block-scaled fp8 layer output in fp64: W1/W2 e4m3 codes, s1 fp32
+    [E][2I/128][H/128], s2 fp32 [E][H/128][I/128]; x and the intermediate
+    quantised per 128-value group of a row."""
+    xa = _np(x, np.uint16)
+    T, H = xa.shape
+    ida = _np(ids, np.int32)
+    k = ida.shape[1]
+    wa = _np(topk_w, np.float32)
+    W1a = _np(W1, np.uint8)
+    W2a = _np(W2, np.uint8)
+    s1a = _np(s1, np.float32)
+    s2a = _np(s2, np.float32)
+    E, I2, _ = W1a.shape
+    I = I2 // 2
+    assert s1a.shape == (E, I2 // 128, H // 128) and s2a.shape == (E, H // 128, I // 128)
+    r, n = _rows_arg(rows, T)
+    out = np.zeros((n, H), dtype=np.float64)
+    xq = sx = hq = sh = None
+    if want_quant:
+        xq = np.zeros((n, H), dtype=np.uint8)
+        sx = np.zeros((n, H // 128), dtype=np.float32)
+        hq = np.zeros((n, k, I), dtype=np.uint8)
+        sh = np.zeros((n, k, I // 128), dtype=np.float32)
+    lib().oracle_forward_fp8_block(_p(xa), _p(wa), _p(ida), _p(W1a), _p(s1a), _p(W2a), _p(s2a),
+                                   T, k, E, H, I, _p(r) if r is not None else None, n, _p(out),
+                                   *(None if a is None else _p(a) for a in (xq, sx, hq, sh)))
+    return (out, xq, sx, hq, sh) if want_quant else out
 
 
 def w4_dequant(codes, scales):

@@ -579,6 +579,108 @@ void oracle_forward_int8(const uint16_t *x, const float *topk_w, const int32_t *
 }
 
 /*
+ * Block-scaled fp8 w8a8 (SGLang tuning guide: block_shape [128, 128], the
+ * quantisation of DeepSeek-V3's checkpoints).  Weights: e4m3 codes with one
+ * fp32 scale per 128 x 128 block of a [rows][K] matrix (scale[r/128][k/128]).
+ * Activations: e4m3 codes with one fp32 scale per 128 consecutive K values
+ * of a row (per-token groups), quantised by the per-row rule of the fp8
+ * path applied to each group.  A dot product is the sum over the 128-value
+ * groups of (group scale of x) * (block scale of w) * (integer-exact sum of
+ * code products).
+ */
+void oracle_quant_groups(const float *v, int n, uint8_t *codes, float *scales)
+{
+    for (int g = 0; g < n / 128; g++)
+        oracle_quant_row(v + 128 * g, 128, codes + 128 * g, scales + g);
+}
+
+static double dot_blocked(const uint8_t *wq, const float *wscale_row, const uint8_t *xq,
+                          const float *xscale, int K)
+{
+    double s = 0.0;
+    for (int g = 0; g < K / 128; g++) {
+        double part = 0.0;
+        for (int k = 128 * g; k < 128 * (g + 1); k++)
+            part += E4M3_VALUE[wq[k]] * E4M3_VALUE[xq[k]];
+        s += (double)xscale[g] * (double)wscale_row[g] * part;
+    }
+    return s;
+}
+
+static void token_fp8b(const uint16_t *x, const float *topk_w, const int32_t *ids,
+                       const uint8_t *W1, const float *s1, const uint8_t *W2, const float *s2,
+                       int t, int k, int E, int H, int I, double *acc,
+                       uint8_t *xq_out, float *sx_out, uint8_t *hq_out, float *sh_out)
+{
+    float *xf = (float *)malloc(sizeof(float) * (size_t)H);
+    uint8_t *xq = (uint8_t *)malloc((size_t)H);
+    float *sx = (float *)malloc(sizeof(float) * (size_t)H / 128);
+    float *af = (float *)malloc(sizeof(float) * (size_t)I);
+    uint8_t *hq = (uint8_t *)malloc((size_t)I);
+    float *sh = (float *)malloc(sizeof(float) * (size_t)I / 128);
+    for (int h = 0; h < H; h++)
+        xf[h] = (float)BF16_VALUE[x[(size_t)t * H + h]];
+    oracle_quant_groups(xf, H, xq, sx);
+    if (xq_out) {
+        memcpy(xq_out, xq, (size_t)H);
+        memcpy(sx_out, sx, sizeof(float) * (size_t)H / 128);
+    }
+    for (int m = 0; m < H; m++)
+        acc[m] = 0.0;
+    const int kb1 = H / 128, kb2 = I / 128;
+    for (int j = 0; j < k; j++) {
+        int p = t * k + j;
+        int e = ids[p];
+        if (e < 0 || e >= E)
+            continue;
+        double w = (double)topk_w[p];
+        for (int n = 0; n < I; n++) {
+            size_t rg = (size_t)e * 2 * I + n, ru = rg + I;
+            /* scale rows of W1[e]: block row (row / 128) of [2I/128][H/128] */
+            const float *sg = s1 + ((size_t)e * (2 * I / 128) + (size_t)n / 128) * kb1;
+            const float *su = s1 + ((size_t)e * (2 * I / 128) + (size_t)(I + n) / 128) * kb1;
+            double g = dot_blocked(W1 + rg * H, sg, xq, sx, H);
+            double u = dot_blocked(W1 + ru * H, su, xq, sx, H);
+            af[n] = (float)(silu(g) * u);
+        }
+        oracle_quant_groups(af, I, hq, sh);
+        if (hq_out) {
+            memcpy(hq_out + (size_t)j * I, hq, (size_t)I);
+            memcpy(sh_out + (size_t)j * (I / 128), sh, sizeof(float) * (size_t)I / 128);
+        }
+        for (int m = 0; m < H; m++) {
+            size_t r2 = (size_t)e * H + m;
+            const float *s2r = s2 + ((size_t)e * (H / 128) + (size_t)m / 128) * kb2;
+            acc[m] += w * dot_blocked(W2 + r2 * I, s2r, hq, sh, I);
+        }
+    }
+    free(xf); free(xq); free(sx); free(af); free(hq); free(sh);
+}
+
+/* Block-scaled fp8 forward.  s1 fp32 [E][2I/128][H/128], s2 fp32
+ * [E][H/128][I/128].  Optional outputs: xq_out [nrows][H], sx_out
+ * [nrows][H/128], hq_out [nrows][k][I], sh_out [nrows][k][I/128]. */
+void oracle_forward_fp8_block(const uint16_t *x, const float *topk_w, const int32_t *ids,
+                              const uint8_t *W1, const float *s1, const uint8_t *W2, const float *s2,
+                              int T, int k, int E, int H, int I, const int32_t *rows, int nrows,
+                              double *out, uint8_t *xq_out, float *sx_out, uint8_t *hq_out,
+                              float *sh_out)
+{
+    oracle_init();
+    if (!rows)
+        nrows = T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; r++) {
+        int t = rows ? rows[r] : r;
+        token_fp8b(x, topk_w, ids, W1, s1, W2, s2, t, k, E, H, I, out + (size_t)r * H,
+                   xq_out ? xq_out + (size_t)r * H : NULL,
+                   sx_out ? sx_out + (size_t)r * (H / 128) : NULL,
+                   hq_out ? hq_out + (size_t)r * k * I : NULL,
+                   sh_out ? sh_out + (size_t)r * k * (I / 128) : NULL);
+    }
+}
+
+/*
  * int4 w4a16 (SGLang tuning guide dtype list: int4_w4a16): int4 weights
  * with one fp32 scale per 128 consecutive K values of a row (a group), bf16
  * activations.  Weight element (n, k) = q * scale[n][k / 128] with q a
