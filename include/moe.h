@@ -77,8 +77,10 @@ typedef enum {
                                 consecutive K values, weights and activations */
     MOE_DTYPE_INT8_W8A8 = 3, /* int8 weights (per-output-channel fp32 scales) and
                                 int8 activations (per-row fp32 scales) */
-    MOE_DTYPE_INT4_W4A16 = 4 /* int4 weights (fp32 scale per 128 K values of a row),
-                                bf16 activations */
+    MOE_DTYPE_INT4_W4A16 = 4, /* int4 weights (fp32 scale per 128 K values of a row),
+                                 bf16 activations */
+    MOE_DTYPE_FP8_BLOCK = 5   /* e4m3 weights with an fp32 scale per 128 x 128 block,
+                                 e4m3 activations with one per 128-value row group */
 } moe_dtype_t;
 
 /* One row tile of the task map: rows [row_begin, row_begin + rows) of the
@@ -325,6 +327,22 @@ int moe_forward_int8(const void *x, const float *topk_w, const void *routing,
                      const int8_t *w2, const float *w2_scale,
                      int T, int k, int E, int H, int I,
                      void *workspace, size_t workspace_bytes, void *out, void *stream);
+
+/* Block-scaled fp8 (SGLang tuning guide: block_shape [128, 128], the
+ * quantisation of DeepSeek-V3 checkpoints).  As the fp8 pair except the
+ * scales: w1_scale (device) fp32 [E][2I/128][H/128] and w2_scale (device)
+ * fp32 [E][H/128][I/128], one per 128 x 128 block of the weight matrix;
+ * x is quantised per token and SiLU(gate)*up per (token, expert) row in
+ * groups of 128 values, each group by the per-row rule of moe_forward_fp8.
+ * w1/w2 packed by moe_pack_weights with dtype MOE_DTYPE_FP8_BLOCK (the
+ * fp8 layout).  H and I must be multiples of 128. */
+int moe_build_routing_fp8_block(const int32_t *topk_ids, int T, int k, int E, int H, int I,
+                                void *routing, size_t routing_bytes, void *stream);
+int moe_forward_fp8_block(const void *x, const float *topk_w, const void *routing,
+                          const uint8_t *w1, const float *w1_scale,
+                          const uint8_t *w2, const float *w2_scale,
+                          int T, int k, int E, int H, int I,
+                          void *workspace, size_t workspace_bytes, void *out, void *stream);
 
 /* int4 w4a16 (SGLang tuning guide dtype list: int4_w4a16).  w1 (device)
  * uint8 [E][2I][H/2] and w2 (device) uint8 [E][H][I/2]: two's-complement

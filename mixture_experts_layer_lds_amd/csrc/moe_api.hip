@@ -42,7 +42,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool known_dtype(int dtype) {
   return dtype == MOE_DTYPE_BF16 || dtype == MOE_DTYPE_FP8_W8A8 || dtype == MOE_DTYPE_MXFP8 ||
-         dtype == MOE_DTYPE_INT8_W8A8 || dtype == MOE_DTYPE_INT4_W4A16;
+         dtype == MOE_DTYPE_INT8_W8A8 || dtype == MOE_DTYPE_INT4_W4A16 ||
+         dtype == MOE_DTYPE_FP8_BLOCK;
 }
 
 int check_shape(int T, int k, int E, int H, int I, int dtype = MOE_DTYPE_BF16) {
@@ -50,7 +51,8 @@ int check_shape(int T, int k, int E, int H, int I, int dtype = MOE_DTYPE_BF16) {
     return MOE_ERR_INVALID_ARG;
   if (H % 64 || I % 64 || H > 65536 || I > 65536) return MOE_ERR_UNSUPPORTED_SHAPE;
   // MX: both reductions in whole 128-value units of the scaled instruction
-  if ((dtype == MOE_DTYPE_MXFP8 || dtype == MOE_DTYPE_INT4_W4A16) && (H % 128 || I % 128))
+  if ((dtype == MOE_DTYPE_MXFP8 || dtype == MOE_DTYPE_INT4_W4A16 || dtype == MOE_DTYPE_FP8_BLOCK) &&
+      (H % 128 || I % 128))
     return MOE_ERR_UNSUPPORTED_SHAPE;   // whole 128-value units / scale groups
   if ((long)T * k > moe::kMaxPairs) return MOE_ERR_UNSUPPORTED_SHAPE;
   return MOE_OK;
@@ -130,8 +132,8 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   const long avg = active > 0 ? (P + active - 1) / active : 1;
   const int esz_t = dtype == MOE_DTYPE_BF16 ? 2 : 1;
   const int nsteps1 = H * esz_t / 64, nsteps2 = I * esz_t / 64;
-  if (dtype == MOE_DTYPE_INT4_W4A16) {
-    // int4 weights: register streaming (128-value K steps) at every size;
+  if (dtype == MOE_DTYPE_INT4_W4A16 || dtype == MOE_DTYPE_FP8_BLOCK) {
+    // int4 weights, block-scaled fp8: register streaming (128-value K steps) at every size;
     // waves per workgroup by the streaming cost model on whole steps
     p.tiling = kStreaming;
     p.block_m = avg <= 8 ? 16 : (avg <= 16 ? 32 : 64);
@@ -264,6 +266,19 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
     off = align_up(off + bytes, 256);
     return at;
   };
+  if (dtype == MOE_DTYPE_FP8_BLOCK) {   // e4m3 codes, group scales per token and per sorted row
+    W->xq = take((size_t)T * H);
+    W->x_scale = take(4 * (size_t)T * (H / 128));
+    W->x_scale_rows = take(4 * P * (H / 128));
+    W->g = take(4 * P * I);
+    W->h = take(P * I);
+    W->h_scale = take(4 * P * (I / 128));
+    W->y = take(2 * P * H);
+    W->total_bytes = off;
+    W->split_k1 = W->split_k2 = 1;
+    W->tiling = p.tiling;
+    return;
+  }
   if (dtype == MOE_DTYPE_INT4_W4A16) {   // bf16 activations: bf16 h and y rows
     W->xq = W->x_scale = W->x_scale_rows = W->g = W->h_scale = kNone;
     W->h = take(2 * P * I);
@@ -474,6 +489,102 @@ int forward_mx(const void* x, const float* topk_w, const void* routing, const vo
     a.topk = k;
     a.max_tasks = p.max_tasks;
     e = moe_host::launch_stream_gemm(a, false, true, 1, p.mb, p.sw2, p.su2,
+                                     stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 4);
+    e = moe_host::launch_reduce(ws + W.y, true, 1, P, topk_w, R.pair_pos, R.expert_offsets, nullptr,
+                                E, T, k, H, static_cast<uint16_t*>(out), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+// Block-scaled fp8 forward: group quantisation of x, register-streaming
+// gate-up (fp32 SiLU(gate)*up), group requantisation of h, down (bf16
+// rows), top-k reduction.
+int forward_fp8b(const void* x, const float* topk_w, const void* routing, const void* w1,
+                 const float* w1_scale, const void* w2, const float* w2_scale, int T, int k, int E,
+                 int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  int rc = check_shape(T, k, E, H, I, MOE_DTYPE_FP8_BLOCK);
+  if (rc != MOE_OK) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !topk_w || !routing || !w1 || !w2 || !w1_scale || !w2_scale || !workspace || !out)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16) ||
+      !aligned(topk_w, 4) || !aligned(routing, 16) || !aligned(workspace, 256) ||
+      !aligned(w1_scale, 4) || !aligned(w2_scale, 4))
+    return MOE_ERR_INVALID_ARG;
+  const Plan p = make_plan(MOE_DTYPE_FP8_BLOCK, T, k, E, H, I);
+  moe_routing_layout_t L;
+  routing_layout(T, k, E, p, &L);
+  moe_workspace_layout_t W;
+  workspace_layout(MOE_DTYPE_FP8_BLOCK, T, k, H, I, p, &W);
+  if (workspace_bytes < W.total_bytes) return MOE_ERR_BUFFER_TOO_SMALL;
+  int cus = 0;
+  if ((rc = cu_count(&cus)) != MOE_OK) return rc;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const RoutingView R = view_routing(routing, L);
+  char* ws = static_cast<char*>(workspace);
+  const int P = T * k;
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws + W.xq);
+  float* x_rows = reinterpret_cast<float*>(ws + W.x_scale_rows);
+  float* h32 = reinterpret_cast<float*>(ws + W.g);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(ws + W.h);
+  float* h_rows = reinterpret_cast<float*>(ws + W.h_scale);
+  hipError_t e;
+  {
+    StageScope st(s, 0);
+    e = moe_host::launch_quant_groups_bf16(static_cast<const uint16_t*>(x), T, H, xq,
+                                           reinterpret_cast<float*>(ws + W.x_scale), x_rows, P, k,
+                                           R.pair_pos, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 1);
+    moe_host::StreamArgs a{};
+    a.a = xq;
+    a.b = w1;
+    a.b_scale = w1_scale;
+    a.row_scale = x_rows;
+    a.sorted_pairs = R.sorted_pairs;
+    a.header = R.header;
+    a.tasks = R.tasks;
+    a.c = h32;
+    a.P = P;
+    a.K = H;
+    a.N_out = I;
+    a.w_rows = 2 * I;
+    a.topk = k;
+    a.max_tasks = p.max_tasks;
+    e = moe_host::launch_stream_fp8b(a, true, p.mb, p.sw1,
+                                     stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 2);
+    e = moe_host::launch_requant_groups(h32, P, I, R.expert_offsets, E, hq, h_rows, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageScope st(s, 3);
+    moe_host::StreamArgs a{};
+    a.a = hq;
+    a.b = w2;
+    a.b_scale = w2_scale;
+    a.row_scale = h_rows;
+    a.sorted_pairs = R.sorted_pairs;
+    a.header = R.header;
+    a.tasks = R.tasks;
+    a.c = ws + W.y;
+    a.P = P;
+    a.K = I;
+    a.N_out = H;
+    a.w_rows = H;
+    a.topk = k;
+    a.max_tasks = p.max_tasks;
+    e = moe_host::launch_stream_fp8b(a, false, p.mb, p.sw2,
                                      stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -1048,6 +1159,19 @@ int moe_forward_mxfp8(const void* x, const float* topk_w, const void* routing, c
                       void* stream) {
   return forward_mx(x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
                     workspace_bytes, out, stream);
+}
+
+int moe_build_routing_fp8_block(const int32_t* topk_ids, int T, int k, int E, int H, int I,
+                                void* routing, size_t routing_bytes, void* stream) {
+  return build_routing(MOE_DTYPE_FP8_BLOCK, topk_ids, T, k, E, H, I, routing, routing_bytes, stream);
+}
+
+int moe_forward_fp8_block(const void* x, const float* topk_w, const void* routing, const uint8_t* w1,
+                          const float* w1_scale, const uint8_t* w2, const float* w2_scale, int T,
+                          int k, int E, int H, int I, void* workspace, size_t workspace_bytes,
+                          void* out, void* stream) {
+  return forward_fp8b(x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
+                      workspace_bytes, out, stream);
 }
 
 int moe_build_routing_int4(const int32_t* topk_ids, int T, int k, int E, int H, int I,

@@ -257,6 +257,7 @@ struct StreamArgs {
   float* row_amax;              // fp8 gate-up: [P] atomic-max slots (pre-cleared)
   const uint8_t* a_mx;          // MX: e8m0 codes of a's rows [rows][K/32] (gate-up: token rows)
   const uint8_t* b_mx;          // MX: e8m0 codes of the weights [E][w_rows][K/32]
+  int P;                        // block fp8: sorted rows (stride of the unit-major row scales)
   int K;                        // reduction length (elements)
   int N_out;                    // output columns (I for gate-up, H for down)
   int w_rows;                   // weight rows per expert (2I or H)
@@ -278,6 +279,20 @@ hipError_t launch_quant_rows_i8(const uint16_t* x, int T, int H, int8_t* xq, flo
                                 hipStream_t s);
 hipError_t launch_requant_rows_i8(const float* h32, int P, int I, const int32_t* expert_offsets, int E,
                                   int8_t* hq, float* h_scale, hipStream_t s);
+// Block-scaled fp8 register-streaming GEMM: a e4m3 rows with unit-major
+// group scales row_scale [K/128][P] (per sorted row), b packed e4m3 weights
+// with b_scale fp32 [E][w_rows/128][K/128]; gate-up writes fp32
+// SiLU(gate)*up, down bf16 rows.
+hipError_t launch_stream_fp8b(const StreamArgs& a, bool gateup, int mb, int waves, int grid, hipStream_t s);
+// Group (128-value) fp8 quantisation: bf16 token rows x (scales also per
+// token [T][H/128] and per sorted row of each of the token's zk pairs,
+// unit-major [H/128][P]); fp32 rows h of the valid sorted rows (scales
+// unit-major [I/128][P]).
+hipError_t launch_quant_groups_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* group_scale,
+                                    float* rows_scale, int P, int zk, const int32_t* pair_pos,
+                                    hipStream_t s);
+hipError_t launch_requant_groups(const float* h, int P, int I, const int32_t* expert_offsets, int E,
+                                 uint8_t* hq, float* rows_scale, hipStream_t s);
 // int4 w4a16 register-streaming GEMM: a bf16 activations, b packed int4
 // weights, b_scale fp32 [E][w_rows][K/128] group scales; gate-up writes bf16
 // SiLU(gate)*up, down bf16 rows.
