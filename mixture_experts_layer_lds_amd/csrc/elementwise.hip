@@ -142,52 +142,77 @@ act_fp8_kernel(const float* __restrict__ g, int S, int P, int I,
 
 // out[t][:] = bf16( sum_{j ascending, pair valid} w[t][j] * rs[pos] * sum_s y[s][pos][:] ),
 // rs = row_scale (the fp8 activation scale of the row when y carries only
-// the weight scales) or 1.
+// the weight scales) or 1; each term is rounded once after its products and
+// once after its sum (no fused multiply-add).
 // y is fp32 [S][P][H] (4 columns per thread, 16-byte loads), or bf16 [P][H]
 // when Y_BF16 (8 columns per thread, 16-byte loads).  Grid (token, column
 // chunk of kRowThreads * columns-per-thread).
-template <bool Y_BF16>
+// Latency, not bandwidth, sets the time at small T: the token's KM (>= k)
+// row indices and weights are workgroup-uniform scalar loads, then every
+// row load is issued before the first is added (slots past k and dropped
+// pairs read row 0, a valid address, and are skipped), so a call waits
+// about one round trip for the rows instead of k.
+template <bool Y_BF16, int KM>
 __global__ void __launch_bounds__(kRowThreads)
 reduce_kernel(const void* __restrict__ yv, int S, int P, const float* __restrict__ topk_w,
               const int32_t* __restrict__ pair_pos, const int32_t* __restrict__ expert_offsets,
               const float* __restrict__ row_scale, int E, int k, int H,
               uint16_t* __restrict__ out) {
+#pragma clang fp contract(off)
   constexpr int C = Y_BF16 ? 8 : 4;
   const int t = blockIdx.x;
   const int c0 = (blockIdx.y * kRowThreads + threadIdx.x) * C;   // first column
   if (c0 >= H) return;
   const int valid = expert_offsets[E];
   const size_t slice = (size_t)P * H;
+  bool ok[KM];
+  size_t at[KM];   // element offset of the row's columns
+  float w[KM], rs[KM];
+#pragma unroll
+  for (int j = 0; j < KM; j++) {
+    const int jj = j < k ? j : k - 1;
+    const int r = pair_pos[t * k + jj];
+    w[j] = topk_w[t * k + jj];
+    ok[j] = j < k && r < valid;   // dropped pairs are skipped
+    at[j] = (size_t)(ok[j] ? r : 0) * H + c0;
+    rs[j] = row_scale ? row_scale[ok[j] ? r : 0] : 1.0f;
+  }
+  f32x4 a[KM][C / 4];
+  if constexpr (Y_BF16) {
+    u32x4 raw[KM];
+#pragma unroll
+    for (int j = 0; j < KM; j++) raw[j] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(yv) + at[j]);
+#pragma unroll
+    for (int j = 0; j < KM; j++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        a[j][q / 2][2 * (q % 2)] = bf16_bits_to_f32(raw[j][q] & 0xffffu);
+        a[j][q / 2][2 * (q % 2) + 1] = bf16_bits_to_f32(raw[j][q] >> 16);
+      }
+  } else {
+    const float* y = static_cast<const float*>(yv);
+#pragma unroll
+    for (int j = 0; j < KM; j++) a[j][0] = *reinterpret_cast<const f32x4*>(y + at[j]);
+    for (int s = 1; s < S; s++) {   // ascending slices, each slice's loads together
+      f32x4 b[KM];
+#pragma unroll
+      for (int j = 0; j < KM; j++) b[j] = *reinterpret_cast<const f32x4*>(y + s * slice + at[j]);
+#pragma unroll
+      for (int j = 0; j < KM; j++) a[j][0] += b[j];
+    }
+  }
   float acc[C];
 #pragma unroll
   for (int q = 0; q < C; q++) acc[q] = 0.0f;
-  for (int j = 0; j < k; j++) {
-    const int p = t * k + j;
-    const int r = pair_pos[p];
-    if (r >= valid) continue;   // dropped pair
-    float v[C];
-    if constexpr (Y_BF16) {
-      const u32x4 b = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(yv) + (size_t)r * H + c0);
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        v[2 * q] = bf16_bits_to_f32(b[q] & 0xffffu);
-        v[2 * q + 1] = bf16_bits_to_f32(b[q] >> 16);
-      }
-    } else {
-      const float* yrow = static_cast<const float*>(yv) + (size_t)r * H + c0;
-      f32x4 a = *reinterpret_cast<const f32x4*>(yrow);
-      for (int s = 1; s < S; s++) a += *reinterpret_cast<const f32x4*>(yrow + s * slice);
+  for (int j = 0; j < KM; j++) {
+    if (!ok[j]) continue;
 #pragma unroll
-      for (int q = 0; q < 4; q++) v[q] = a[q];
+    for (int q = 0; q < C; q++) {
+      float v = a[j][q / 4][q % 4];
+      if (row_scale) v = v * rs[j];
+      acc[q] = acc[q] + w[j] * v;
     }
-    if (row_scale) {
-      const float rs = row_scale[r];
-#pragma unroll
-      for (int q = 0; q < C; q++) v[q] = __fmul_rn(v[q], rs);
-    }
-    const float w = topk_w[p];
-#pragma unroll
-    for (int q = 0; q < C; q++) acc[q] = __fadd_rn(acc[q], __fmul_rn(w, v[q]));
   }
   uint32_t packed[C / 2];
 #pragma unroll
@@ -196,6 +221,20 @@ reduce_kernel(const void* __restrict__ yv, int S, int P, const float* __restrict
   uint16_t* o = out + (size_t)t * H + c0;
   if constexpr (Y_BF16) *reinterpret_cast<u32x4*>(o) = u32x4{packed[0], packed[1], packed[2], packed[3]};
   else *reinterpret_cast<u32x2*>(o) = u32x2{packed[0], packed[1]};
+}
+
+template <bool Y_BF16>
+static void launch_reduce_t(dim3 grid, const void* y, int S, int P, const float* topk_w,
+                            const int32_t* pair_pos, const int32_t* expert_offsets, const float* row_scale,
+                            int E, int T, int k, int H, uint16_t* out, hipStream_t s) {
+#define MOE_REDUCE_KM(KMv)                                                                              \
+  hipLaunchKernelGGL((reduce_kernel<Y_BF16, KMv>), grid, dim3(kRowThreads), 0, s, y, S, P, topk_w,      \
+                     pair_pos, expert_offsets, row_scale, E, k, H, out)
+  if (k <= 2) MOE_REDUCE_KM(2);
+  else if (k <= 4) MOE_REDUCE_KM(4);
+  else if (k <= 8) MOE_REDUCE_KM(8);
+  else MOE_REDUCE_KM(16);
+#undef MOE_REDUCE_KM
 }
 
 }  // namespace moe
@@ -231,11 +270,9 @@ hipError_t launch_reduce(const void* y, bool y_bf16, int S, int P, const float* 
   const int cols = y_bf16 ? 8 : 4;
   const dim3 grid(T, (H / cols + moe::kRowThreads - 1) / moe::kRowThreads);
   if (y_bf16)
-    hipLaunchKernelGGL(moe::reduce_kernel<true>, grid, dim3(moe::kRowThreads), 0, s, y, S, P,
-                       topk_w, pair_pos, expert_offsets, row_scale, E, k, H, out);
+    moe::launch_reduce_t<true>(grid, y, S, P, topk_w, pair_pos, expert_offsets, row_scale, E, T, k, H, out, s);
   else
-    hipLaunchKernelGGL(moe::reduce_kernel<false>, grid, dim3(moe::kRowThreads), 0, s, y, S, P,
-                       topk_w, pair_pos, expert_offsets, row_scale, E, k, H, out);
+    moe::launch_reduce_t<false>(grid, y, S, P, topk_w, pair_pos, expert_offsets, row_scale, E, T, k, H, out, s);
   return hipGetLastError();
 }
 
