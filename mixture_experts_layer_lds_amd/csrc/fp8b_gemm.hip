@@ -18,13 +18,21 @@
 //    output columns per lane.
 //  * Activation group scales come per sorted row, unit-major ([K/128][P]),
 //    written by the quantisation passes.
+//  * Per-channel mode (BLOCK false: the fp8 w8a8 layer, one scale per weight
+//    row and per token row): the same operand arrangement and 128-value
+//    units, and the per-channel epilogue of the fp8 path: gate-up forms
+//    SiLU(g * rs * cs_g) * (u * rs * cs_u) in fp32 (the requantisation pass
+//    finds each row's amax: folding it here with atomics cost 8% of the
+//    gate-up time at T=16); down applies the weight row scales (the row
+//    scale is the top-k reduction's).  Four MFMAs of 16x16x32 per 128
+//    values become one of 16x16x128.
 #include "lds_dma.h"
 
 namespace moe {
 
 constexpr int kFp8bNB = 2;
 
-template <int MB, int W, bool GATEUP>
+template <int MB, int W, bool GATEUP, bool BLOCK>
 __global__ void __launch_bounds__(W * 64)
 stream_fp8b_kernel(moe_host::StreamArgs g) {
   constexpr int NB = kFp8bNB;
@@ -79,14 +87,15 @@ stream_fp8b_kernel(moe_host::StreamArgs g) {
         arow = srow;
       }
       xp[b] = A + (size_t)arow * g.K + (size_t)unit0 * 128 + 16 * lgrp;
-      xsp[b] = g.row_scale + (size_t)unit0 * P + srow;
+      xsp[b] = BLOCK ? g.row_scale + (size_t)unit0 * P + srow : g.row_scale + srow;
     }
     const char* wp[NB];
     const float* wsp[NB];
 #pragma unroll
     for (int q = 0; q < NB; q++) {
       wp[q] = B + (((size_t)task.expert * w_blocks + blk[q]) * nsteps + (size_t)unit0 * 2) * 1024 + 16 * lane;
-      wsp[q] = g.b_scale + ((size_t)task.expert * (g.w_rows / 128) + (blk[q] * 16) / 128) * units + unit0;
+      wsp[q] = BLOCK ? g.b_scale + ((size_t)task.expert * (g.w_rows / 128) + (blk[q] * 16) / 128) * units + unit0
+                     : g.b_scale + (size_t)task.expert * g.w_rows + blk[q] * 16 + 4 * lgrp;
     }
 
     f32x4 acc[MB][NB];
@@ -103,13 +112,13 @@ stream_fp8b_kernel(moe_host::StreamArgs g) {
       for (int q = 0; q < NB; q++) {
         fw[q][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[q] + (size_t)u * 2048));
         fw[q][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[q] + (size_t)u * 2048 + 1024));
-        sw[q] = wsp[q][u];
+        if constexpr (BLOCK) sw[q] = wsp[q][u];
       }
 #pragma unroll
       for (int b = 0; b < MB; b++) {
         fx[b][0] = *reinterpret_cast<const u32x4*>(xp[b] + (size_t)u * 128);
         fx[b][1] = *reinterpret_cast<const u32x4*>(xp[b] + (size_t)u * 128 + 64);
-        sx[b] = xsp[b][(size_t)u * P];
+        if constexpr (BLOCK) sx[b] = xsp[b][(size_t)u * P];
       }
     };
     auto compute = [&](const u32x4 (&fx)[MB][2], const u32x4 (&fw)[NB][2], const float (&sx)[MB],
@@ -118,9 +127,12 @@ stream_fp8b_kernel(moe_host::StreamArgs g) {
       for (int b = 0; b < MB; b++)
 #pragma unroll
         for (int q = 0; q < NB; q++) {
+          // a fresh accumulator per unit: consecutive MFMAs do not wait on
+          // each other's results; the unit sums are added in fp32
           f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
           mfma_fp8_k128(t, fw[q][0], fw[q][1], fx[b][0], fx[b][1]);
-          acc[b][q] += t * (sx[b] * sw[q]);
+          if constexpr (BLOCK) acc[b][q] += t * (sx[b] * sw[q]);
+          else acc[b][q] += t;
         }
     };
     load(fx0, fw0, sx0, sw0, 0);
@@ -156,6 +168,20 @@ stream_fp8b_kernel(moe_host::StreamArgs g) {
         for (int s = 1; s < W; s++) tot[q] += red[s][b][q][lane];
       }
       const int rr = b * 16 + lrow;
+      if constexpr (!BLOCK) {   // per-channel scales: this lane's four weight rows, its token row
+#pragma unroll
+        for (int q = 0; q < NB; q++) {
+          const f32x4 cs = *reinterpret_cast<const f32x4*>(wsp[q]);
+          if constexpr (GATEUP) {
+            const float rs = *xsp[b];
+#pragma unroll
+            for (int i4 = 0; i4 < 4; i4++) tot[q][i4] = (tot[q][i4] * rs) * cs[i4];
+          } else {
+#pragma unroll
+            for (int i4 = 0; i4 < 4; i4++) tot[q][i4] = tot[q][i4] * cs[i4];
+          }
+        }
+      }
       if (rr < task.rows) {
         const size_t r = (size_t)(task.row_begin + rr);
         if constexpr (GATEUP) {
@@ -234,11 +260,19 @@ quant_groups_kernel(const void* __restrict__ in, int n, int nrows, const int32_t
 }
 
 template <int MB, int W>
-static hipError_t launch_fp8b_t(const moe_host::StreamArgs& a, bool gateup, int grid, hipStream_t s) {
-  if (gateup)
-    hipLaunchKernelGGL((stream_fp8b_kernel<MB, W, true>), dim3(grid), dim3(W * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((stream_fp8b_kernel<MB, W, false>), dim3(grid), dim3(W * 64), 0, s, a);
+static hipError_t launch_fp8b_t(const moe_host::StreamArgs& a, bool gateup, bool block, int grid,
+                                hipStream_t s) {
+  if (block) {
+    if (gateup)
+      hipLaunchKernelGGL((stream_fp8b_kernel<MB, W, true, true>), dim3(grid), dim3(W * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((stream_fp8b_kernel<MB, W, false, true>), dim3(grid), dim3(W * 64), 0, s, a);
+  } else {
+    if (gateup)
+      hipLaunchKernelGGL((stream_fp8b_kernel<MB, W, true, false>), dim3(grid), dim3(W * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((stream_fp8b_kernel<MB, W, false, false>), dim3(grid), dim3(W * 64), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -246,9 +280,10 @@ static hipError_t launch_fp8b_t(const moe_host::StreamArgs& a, bool gateup, int 
 
 namespace moe_host {
 
-hipError_t launch_stream_fp8b(const StreamArgs& a, bool gateup, int mb, int waves, int grid, hipStream_t s) {
+hipError_t launch_stream_fp8b(const StreamArgs& a, bool gateup, bool block, int mb, int waves, int grid,
+                              hipStream_t s) {
 #define MOE_FP8B_CASE(M, Wv) \
-  if (mb == M && waves == Wv) return moe::launch_fp8b_t<M, Wv>(a, gateup, grid, s);
+  if (mb == M && waves == Wv) return moe::launch_fp8b_t<M, Wv>(a, gateup, block, grid, s);
   MOE_FP8B_CASE(1, 1) MOE_FP8B_CASE(1, 2) MOE_FP8B_CASE(1, 4) MOE_FP8B_CASE(1, 8)
   MOE_FP8B_CASE(2, 1) MOE_FP8B_CASE(2, 2) MOE_FP8B_CASE(2, 4) MOE_FP8B_CASE(2, 8)
   MOE_FP8B_CASE(4, 1) MOE_FP8B_CASE(4, 2) MOE_FP8B_CASE(4, 4) MOE_FP8B_CASE(4, 8)

@@ -83,15 +83,14 @@ quant_rows_i8_kernel(const uint16_t* __restrict__ x, int H, int8_t* __restrict__
   if (scale_rows && threadIdx.x < zk) scale_rows[pair_pos[(size_t)t * zk + threadIdx.x]] = sc;
 }
 
-// fp32 rows h32[r][0..I) of the valid sorted rows, with the row amax
-// accumulated in h_scale[r] (replaced by the row scale) -> int8 codes.
+// fp32 rows h32[r][0..I) of the valid sorted rows -> int8 codes, with the
+// row amax found here from the row (h_scale[r] then holds the row scale).
 __global__ void __launch_bounds__(kI8Threads)
 requant_rows_i8_kernel(const float* __restrict__ h32, int I, const int32_t* __restrict__ expert_offsets,
                        int E, int8_t* __restrict__ hq, float* __restrict__ h_scale) {
   const int r = blockIdx.x;
   if (r >= expert_offsets[E]) return;
-  const float amax = h_scale[r];
-  __syncthreads();   // every thread has read the amax before it is replaced
+  const float amax = row_amax_f32<kI8Threads>(h32 + (size_t)r * I, I);
   float sc, inv;
   i8_row_scales(amax, &sc, &inv);
   const f32x4* row = reinterpret_cast<const f32x4*>(h32 + (size_t)r * I);

@@ -36,6 +36,7 @@ struct Plan {
   int sw2 = 1, su2 = 2;          // streaming down
   int ks1 = 4, nbuf1 = 4;        // strips: K steps per stage, stages in flight (gate-up)
   int ks2 = 4, nbuf2 = 4;        // (down)
+  bool fp8_units = false;        // fp8 streaming on 128-value units (fp8b_gemm.hip, per-channel mode)
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -125,6 +126,24 @@ bool choose_strip(int nsteps, int mb, bool fp8, long items, int* split, int* ks,
 
 // Tile plan: a fixed function of the shape and dtype, shared by the routing
 // build, the workspace layout and the forward pass.
+// Waves per workgroup for the 128-value-unit streaming kernels (int4,
+// block fp8, per-channel fp8 on units): the wave count w dividing the units
+// that minimises (items per workgroup slot) x (units per wave + 2), the
+// number of register stages on the critical path plus the ramp.
+int pick_unit_waves(int units, long items) {
+  int best = 1;
+  long best_cost = -1;
+  for (int w = 1; w <= 8; w *= 2) {
+    if (units % w) continue;
+    long grid = kStreamWaves / w;
+    if (items < grid) grid = items;
+    if (grid < 1) grid = 1;
+    const long cost = (items + grid - 1) / grid * (units / w + 2);
+    if (best_cost < 0 || cost < best_cost) best = w, best_cost = cost;
+  }
+  return best;
+}
+
 Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   Plan p;
   const long P = (long)T * k;
@@ -141,21 +160,8 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     p.max_tasks = (int)(P / p.block_m + (P < E ? P : E));
     long est = (P + p.block_m - 1) / p.block_m;
     if (est < active) est = active;
-    auto pick = [&](int steps, long items) {
-      int best = 1;
-      long best_cost = -1;
-      for (int w = 1; w <= 8; w *= 2) {
-        if (steps % w) continue;
-        long grid = kStreamWaves / w;
-        if (items < grid) grid = items;
-        if (grid < 1) grid = 1;
-        const long cost = (items + grid - 1) / grid * (steps / w + 2);
-        if (best_cost < 0 || cost < best_cost) best = w, best_cost = cost;
-      }
-      return best;
-    };
-    p.sw1 = pick(H / 128, est * ((long)I / 16));
-    p.sw2 = pick(I / 128, est * ((long)H / 32));
+    p.sw1 = pick_unit_waves(H / 128, est * ((long)I / 16));
+    p.sw2 = pick_unit_waves(I / 128, est * ((long)H / 32));
     p.su1 = p.su2 = 1;
     return p;
   }
@@ -230,6 +236,13 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   if (!tiled) {
     choose_stream(nsteps1, p.mb, est_tasks * ((long)I / 16), &p.sw1, &p.su1);
     choose_stream(nsteps2, p.mb, est_tasks * ((long)H / 32), &p.sw2, &p.su2);
+    if (dtype == MOE_DTYPE_FP8_W8A8 && H % 128 == 0 && I % 128 == 0) {
+      // whole 128-value units: one 16x16x128 MFMA per unit instead of four 16x16x32
+      p.fp8_units = true;
+      p.sw1 = pick_unit_waves(H / 128, est_tasks * ((long)I / 16));
+      p.sw2 = pick_unit_waves(I / 128, est_tasks * ((long)H / 32));
+      p.su1 = p.su2 = 2;
+    }
   }
   return p;
 }
@@ -558,7 +571,7 @@ int forward_fp8b(const void* x, const float* topk_w, const void* routing, const 
     a.w_rows = 2 * I;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    e = moe_host::launch_stream_fp8b(a, true, p.mb, p.sw1,
+    e = moe_host::launch_stream_fp8b(a, true, true, p.mb, p.sw1,
                                      stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -584,7 +597,7 @@ int forward_fp8b(const void* x, const float* topk_w, const void* routing, const 
     a.w_rows = H;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    e = moe_host::launch_stream_fp8b(a, false, p.mb, p.sw2,
+    e = moe_host::launch_stream_fp8b(a, false, true, p.mb, p.sw2,
                                      stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -706,8 +719,8 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
   float* h_scale = reinterpret_cast<float*>(ws + W.h_scale);
   hipError_t e;
   {
-    StageScope st(s, 0);   // also clears the row-amax slots the gate-up epilogue folds into
-    e = moe_host::launch_quant_rows_i8(static_cast<const uint16_t*>(x), T, H, xq, x_scale, h_scale, k,
+    StageScope st(s, 0);
+    e = moe_host::launch_quant_rows_i8(static_cast<const uint16_t*>(x), T, H, xq, x_scale, nullptr, k,
                                        R.pair_pos, x_rows, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
@@ -722,7 +735,7 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
     a.header = R.header;
     a.tasks = R.tasks;
     a.c = h32;
-    a.row_amax = h_scale;
+    a.row_amax = nullptr;   // the requantisation pass finds the row amax
     a.K = H;
     a.N_out = I;
     a.w_rows = 2 * I;
@@ -800,11 +813,11 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
 
   if (fp8) {
     StageScope st(s, 0);
-    // the row amax slots are cleared here for the epilogues that fold into
-    // them (LDS tiles, streaming)
+    // the row amax slots are cleared here for the epilogue that folds into
+    // them (LDS tiles; the streaming requantisation finds the amax itself)
     e = moe_host::launch_quant_rows_bf16(
         static_cast<const uint16_t*>(x), T, H, xq, x_scale,
-        p.tiling != kStrips ? h_scale : nullptr,
+        p.tiling == kLdsTiles ? h_scale : nullptr,
         k, R.pair_pos, p.tiling == kStreaming ? reinterpret_cast<float*>(ws + W.x_scale_rows) : nullptr,
         s);
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -902,7 +915,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
       StageScope st(s, 2);
       if (fp8) {
         e = moe_host::launch_requant_rows(h32, P, I, R.expert_offsets, E,
-                                          static_cast<uint8_t*>(h), h_scale, s);
+                                          static_cast<uint8_t*>(h), h_scale, false, s);
         if (e != hipSuccess) return MOE_ERR_HIP;
       }
     }
@@ -948,20 +961,23 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     a.header = R.header;
     a.tasks = R.tasks;
     a.c = fp8 ? static_cast<void*>(h32) : h;
-    a.row_amax = h_scale;
+    a.row_amax = nullptr;   // the requantisation pass finds the row amax
     a.K = H;
     a.N_out = I;
     a.w_rows = 2 * I;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    e = moe_host::launch_stream_gemm(a, true, fp8, 0, p.mb, p.sw1, p.su1,
-                                     stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
+    a.P = P;
+    e = p.fp8_units ? moe_host::launch_stream_fp8b(a, true, false, p.mb, p.sw1,
+                                                   stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s)
+                    : moe_host::launch_stream_gemm(a, true, fp8, 0, p.mb, p.sw1, p.su1,
+                                                   stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (fp8) {
     StageScope st(s, 2);
     e = moe_host::launch_requant_rows(h32, P, I, R.expert_offsets, E, static_cast<uint8_t*>(h),
-                                      h_scale, s);
+                                      h_scale, true, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
@@ -979,8 +995,11 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     a.w_rows = H;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    e = moe_host::launch_stream_gemm(a, false, fp8, 0, p.mb, p.sw2, p.su2,
-                                     stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
+    a.P = P;
+    e = p.fp8_units ? moe_host::launch_stream_fp8b(a, false, false, p.mb, p.sw2,
+                                                   stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s)
+                    : moe_host::launch_stream_gemm(a, false, fp8, 0, p.mb, p.sw2, p.su2,
+                                                   stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {

@@ -119,6 +119,27 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Largest |v| of a row of n fp32 values (n % 4 == 0) by a workgroup of NT
+// threads (NT / 64 <= 8 waves), returned to every thread.
+template <int NT>
+__device__ float row_amax_f32(const float* __restrict__ v, int n) {
+  __shared__ float s_max[NT / 64];
+  const f32x4* row = reinterpret_cast<const f32x4*>(v);
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n / 4; i += NT) {
+    const f32x4 a = row[i];
+    m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a[0]), __builtin_fabsf(a[1])),
+                                           __builtin_fmaxf(__builtin_fabsf(a[2]), __builtin_fabsf(a[3]))));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = s_max[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; w++) r = __builtin_fmaxf(r, s_max[w]);
+  return r;
+}
+
 }  // namespace moe
 
 // Host-side launch helpers implemented by the kernel translation units.
@@ -254,7 +275,8 @@ struct StreamArgs {
   const int32_t* header;
   const moe_task_t* tasks;
   void* c;                      // gate-up: h [P][N_out] (bf16, or fp32 on fp8); down: y [P][N_out] bf16
-  float* row_amax;              // fp8 gate-up: [P] atomic-max slots (pre-cleared)
+  float* row_amax;              // fp8 / int8 gate-up: [P] atomic-max slots (pre-cleared), or
+                                // null when the requantisation pass finds the row amax itself
   const uint8_t* a_mx;          // MX: e8m0 codes of a's rows [rows][K/32] (gate-up: token rows)
   const uint8_t* b_mx;          // MX: e8m0 codes of the weights [E][w_rows][K/32]
   int P;                        // block fp8: sorted rows (stride of the unit-major row scales)
@@ -273,17 +295,21 @@ hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int ki
                               int u, int grid, hipStream_t s);
 // int8 w8a8: per-token quantisation of bf16 x (row-amax slots cleared,
 // per-sorted-row scales written as the fp8 variant) and per-row
-// requantisation of fp32 h with the amax held in h_scale.
+// requantisation of fp32 h (the row amax found from the row).
 hipError_t launch_quant_rows_i8(const uint16_t* x, int T, int H, int8_t* xq, float* scale,
                                 float* zero_rows, int zk, const int32_t* pair_pos, float* scale_rows,
                                 hipStream_t s);
 hipError_t launch_requant_rows_i8(const float* h32, int P, int I, const int32_t* expert_offsets, int E,
                                   int8_t* hq, float* h_scale, hipStream_t s);
-// Block-scaled fp8 register-streaming GEMM: a e4m3 rows with unit-major
-// group scales row_scale [K/128][P] (per sorted row), b packed e4m3 weights
-// with b_scale fp32 [E][w_rows/128][K/128]; gate-up writes fp32
-// SiLU(gate)*up, down bf16 rows.
-hipError_t launch_stream_fp8b(const StreamArgs& a, bool gateup, int mb, int waves, int grid, hipStream_t s);
+// Block-scaled fp8 register-streaming GEMM (K % 128 == 0): a e4m3 rows, b
+// packed e4m3 weights.  block: unit-major group scales row_scale [K/128][P]
+// (per sorted row), b_scale fp32 [E][w_rows/128][K/128]; gate-up writes fp32
+// SiLU(gate)*up, down bf16 rows.  !block (per-channel fp8 w8a8): row_scale
+// the per-sorted-row x scales, b_scale [E][w_rows]; gate-up writes fp32
+// SiLU(gate)*up (the requantisation pass finds the row amax), down applies
+// the weight row scales only.
+hipError_t launch_stream_fp8b(const StreamArgs& a, bool gateup, bool block, int mb, int waves, int grid,
+                              hipStream_t s);
 // Group (128-value) fp8 quantisation: bf16 token rows x (scales also per
 // token [T][H/128] and per sorted row of each of the token's zk pairs,
 // unit-major [H/128][P]); fp32 rows h of the valid sorted rows (scales
@@ -305,6 +331,6 @@ hipError_t launch_mx_requant(const float* h, int P, int I, const int32_t* expert
 
 // fp32 rows -> e4m3 codes with the row amax held in h_scale (replaced by the scale).
 hipError_t launch_requant_rows(const float* h32, int P, int I, const int32_t* expert_offsets,
-                               int E, uint8_t* hq, float* h_scale, hipStream_t s);
+                               int E, uint8_t* hq, float* h_scale, bool find_amax, hipStream_t s);
 
 }  // namespace moe_host

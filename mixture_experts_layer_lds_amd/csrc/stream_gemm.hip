@@ -21,8 +21,10 @@
 //    partial sums in memory and no extra kernel to add them.
 //  * The waves' partial sums meet in LDS and are added in ascending wave
 //    order (deterministic).  Gate-up then writes h = SiLU(gate) * up: bf16,
-//    or on fp8 the fp32 values plus each row's amax (an order-independent
-//    atomic max on the non-negative float bits) for the requantisation pass.
+//    or on fp8 the fp32 values for the requantisation pass, which finds
+//    each row's amax (with row_amax set, the epilogue also folds it into the
+//    row's slot by an order-independent atomic max on the non-negative
+//    float bits; those atomics cost about 8% of the gate-up time).
 //    Down writes bf16 rows; on fp8 only the weight column scale is applied
 //    there and the row scale by the top-k reduction.
 //  * Per-item metadata (task record, token indices, fp8 scales) comes from
@@ -299,7 +301,7 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
             if constexpr (FP8) static_cast<float*>(g.c)[r * g.N_out + col] = hv[i];
             else static_cast<uint16_t*>(g.c)[r * g.N_out + col] = f32_to_bf16_bits(hv[i]);
           }
-          if constexpr (FP8 && !MX) {
+          if (FP8 && !MX && g.row_amax) {
             // row amax over this item's 16 columns, folded into the row's slot
             const float mx = max16(ok ? __builtin_fabsf(hv[i]) : 0.0f);
             if (ok && lrow == 0)

@@ -554,14 +554,21 @@ static hipError_t launch_dma_shape(const moe_host::TiledArgs& a, bool gateup, bo
 }
 
 // requantise fp32 rows h32[r][0..I) of the valid sorted rows with the
-// row amax accumulated in h_scale[r] (replaced by the row scale).
+// row amax accumulated in h_scale[r] by the GEMM epilogue, or, with
+// find_amax, found here from the row itself; h_scale[r] then holds the row
+// scale.
 __global__ void __launch_bounds__(256)
 requant_rows_kernel(const float* __restrict__ h32, int I, const int32_t* __restrict__ expert_offsets,
-                    int E, uint8_t* __restrict__ hq, float* __restrict__ h_scale) {
+                    int E, uint8_t* __restrict__ hq, float* __restrict__ h_scale, int find_amax) {
   const int r = blockIdx.x;
   if (r >= expert_offsets[E]) return;
-  const float amax = h_scale[r];
-  __syncthreads();   // every thread has read the amax before it is replaced
+  float amax;
+  if (find_amax) {
+    amax = row_amax_f32<256>(h32 + (size_t)r * I, I);
+  } else {
+    amax = h_scale[r];
+    __syncthreads();   // every thread has read the amax before it is replaced
+  }
   float sc, inv;
   e4m3_row_scales(amax, &sc, &inv);
   const f32x4* row = reinterpret_cast<const f32x4*>(h32 + (size_t)r * I);
@@ -599,9 +606,9 @@ hipError_t launch_tiled_gemm(const TiledArgs& a, bool gateup, bool fp8, int bm, 
 }
 
 hipError_t launch_requant_rows(const float* h32, int P, int I, const int32_t* expert_offsets,
-                               int E, uint8_t* hq, float* h_scale, hipStream_t s) {
+                               int E, uint8_t* hq, float* h_scale, bool find_amax, hipStream_t s) {
   hipLaunchKernelGGL(moe::requant_rows_kernel, dim3(P), dim3(256), 0, s, h32, I, expert_offsets,
-                     E, hq, h_scale);
+                     E, hq, h_scale, find_amax ? 1 : 0);
   return hipGetLastError();
 }
 
