@@ -54,7 +54,8 @@ class Workload:
     H: int
     I: int
     k: int
-    dtype: str          # "f32" (tiny parity case), "bf16", "fp8", "fp8b" (block-scaled), "mxfp8", "int8" or "int4"
+    dtype: str          # "f32" (tiny parity case), "bf16", "fp8", "fp8b" (block-scaled), "mxfp8", "int8",
+                        # "int8w" (weight-only int8, bf16 activations) or "int4"
     Ts: tuple
     routing: str        # "softmax", "biased" or "hot0"
     label: str
@@ -82,6 +83,9 @@ WORKLOADS = {
     "mixtral4": Workload("mixtral4", 2, 8, 4096, 14336, 2, "int4",
                          (1, 2, 4, 8, 16, 32, 64), "softmax",
                          "Mixtral-8x7B-shaped MoE layer, int4 w4a16 (group 128), E=8 H=4096 I=14336 top-2"),
+    "mixtral8": Workload("mixtral8", 2, 8, 4096, 14336, 2, "int8w",
+                         (1, 2, 4, 8, 16, 32, 64), "softmax",
+                         "Mixtral-8x7B-shaped MoE layer, int8 w8a16 (per-channel weight scales), E=8 H=4096 I=14336 top-2"),
     "dsv3b": Workload("dsv3b", 5, 256, 7168, 2048, 8, "fp8b",
                       (1, 16, 128, 1024, 4096), "softmax",
                       "DeepSeek-V3-shaped MoE layer, fp8 w8a8 with 128x128 weight blocks and 1x128 token groups, E=256 H=7168 I=2048 top-8"),
@@ -355,7 +359,7 @@ def make_weights(wl: Workload, device="cpu", seed: Optional[int] = None, E: Opti
         w1, s1 = _int4_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device)
         w2, s2 = _int4_experts(E, H, I, 1.0 / math.sqrt(I), g, device)
         return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2}
-    if wl.dtype == "int8":
+    if wl.dtype in ("int8", "int8w"):   # the same per-channel weights; int8w keeps bf16 activations
         w1, s1 = _int8_experts(E, 2 * I, H, 1.0 / math.sqrt(H), g, device)
         w2, s2 = _int8_experts(E, H, I, 1.0 / math.sqrt(I), g, device)
         return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2}

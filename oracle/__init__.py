@@ -22,6 +22,9 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                                  torch bit operations, exact cases, a
                                  dense torch reference on dequantised
                                  weights.
+  forward_w8a16               -- pinned: a dense torch reference on the
+                                 dequantised int8 weights (every code, both
+                                 signs, per-row scales), k=1 single expert.
   int8_quant_row / forward_int8 -- pinned: worked cases (integers at amax
                                  127, ties to even, clamping), an independent
                                  torch quantiser, a dense torch reference
@@ -113,6 +116,8 @@ def lib():
         L.oracle_forward_w4a16.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P]
         L.oracle_w4_dequant.restype = None
         L.oracle_w4_dequant.argtypes = [P, P, i, i, P]
+        L.oracle_forward_w8a16.restype = None
+        L.oracle_forward_w8a16.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, i, P]
         L.oracle_int8_quant_row.restype = None
         L.oracle_int8_quant_row.argtypes = [P, i, P, P]
         L.oracle_int8_quant_rows_bf16.restype = None
@@ -293,6 +298,30 @@ def w4_dequant(codes, scales):
     n = 2 * nb
     out = np.zeros((R, n), dtype=np.float64)
     lib().oracle_w4_dequant(_p(c), _p(sc), R, n, _p(out))
+    return out
+
+
+def forward_w8a16(x, topk_w, ids, W1, s1, W2, s2, rows=None):
+    """int8 w8a16 layer output in fp64: x bf16 [T][H]; W1 int8 [E][2I][H],
+    s1 fp32 [E][2I] (one scale per weight row); W2 int8 [E][H][I], s2 fp32
+    [E][H]."""
+    xa = _np(x, np.uint16)
+    T, H = xa.shape
+    ida = _np(ids, np.int32)
+    k = ida.shape[1]
+    wa = _np(topk_w, np.float32)
+    W1a = _np(W1, np.int8)
+    W2a = _np(W2, np.int8)
+    s1a = _np(s1, np.float32)
+    s2a = _np(s2, np.float32)
+    E, I2, _ = W1a.shape
+    I = I2 // 2
+    assert W1a.shape == (E, I2, H) and s1a.shape == (E, I2)
+    assert W2a.shape == (E, H, I) and s2a.shape == (E, H)
+    r, n = _rows_arg(rows, T)
+    out = np.zeros((n, H), dtype=np.float64)
+    lib().oracle_forward_w8a16(_p(xa), _p(wa), _p(ida), _p(W1a), _p(s1a), _p(W2a), _p(s2a),
+                               T, k, E, H, I, _p(r) if r is not None else None, n, _p(out))
     return out
 
 

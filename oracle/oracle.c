@@ -757,6 +757,68 @@ void oracle_w4_dequant(const uint8_t *codes, const float *scales, int rows, int 
 }
 
 /*
+ * int8 w8a16 (SGLang tuning guide dtype list: int8_w8a16, weight-only
+ * int8): int8 weight codes with one fp32 scale per weight row (per output
+ * channel), bf16 activations.  Weight element (n, k) = q[n][k] * scale[n].
+ * The activations are not quantised: the layer is the bf16 layer on the
+ * dequantised weights, in fp64 here.
+ */
+static void w8_row(const int8_t *codes, float scale, int n, double *dst)
+{
+    for (int k = 0; k < n; k++)
+        dst[k] = (double)codes[k] * (double)scale;
+}
+
+static void token_w8a16(const uint16_t *x, const float *topk_w, const int32_t *ids,
+                        const int8_t *W1, const float *s1, const int8_t *W2, const float *s2,
+                        int t, int k, int E, int H, int I, double *acc)
+{
+    double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+    double *wr = (double *)malloc(sizeof(double) * (size_t)(H > I ? H : I));
+    double *hd = (double *)malloc(sizeof(double) * (size_t)I);
+    for (int h = 0; h < H; h++)
+        xd[h] = BF16_VALUE[x[(size_t)t * H + h]];
+    for (int m = 0; m < H; m++)
+        acc[m] = 0.0;
+    for (int j = 0; j < k; j++) {
+        int p = t * k + j;
+        int e = ids[p];
+        if (e < 0 || e >= E)
+            continue;
+        double w = (double)topk_w[p];
+        for (int n = 0; n < I; n++) {
+            size_t rg = (size_t)e * 2 * I + n, ru = rg + I;
+            w8_row(W1 + rg * H, s1[rg], H, wr);
+            double g = dot(wr, xd, H);
+            w8_row(W1 + ru * H, s1[ru], H, wr);
+            double u = dot(wr, xd, H);
+            hd[n] = silu(g) * u;
+        }
+        for (int m = 0; m < H; m++) {
+            size_t r2 = (size_t)e * H + m;
+            w8_row(W2 + r2 * I, s2[r2], I, wr);
+            acc[m] += w * dot(wr, hd, I);
+        }
+    }
+    free(xd); free(wr); free(hd);
+}
+
+void oracle_forward_w8a16(const uint16_t *x, const float *topk_w, const int32_t *ids,
+                          const int8_t *W1, const float *s1, const int8_t *W2, const float *s2,
+                          int T, int k, int E, int H, int I, const int32_t *rows, int nrows,
+                          double *out)
+{
+    oracle_init();
+    if (!rows)
+        nrows = T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; r++) {
+        int t = rows ? rows[r] : r;
+        token_w8a16(x, topk_w, ids, W1, s1, W2, s2, t, k, E, H, I, out + (size_t)r * H);
+    }
+}
+
+/*
  * MXFP8 block-scaled fp8 (SGLang tuning guide, section on block shapes:
  * gfx95 devices keep MXFP8's [1, 32] block shape instead of remapping it
  * to [128, 128]).  OCP Microscaling format: every 32 consecutive elements
