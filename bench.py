@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "us per MoE layer + achieved HBM GB/s (% of peak), T=1..4096 tokens, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0, "int8": 5000.0,   # int8: POP/s
-                    "int4": 2500.0, "fp8b": 5000.0}                                                   # bf16 MFMA
+                    "int4": 2500.0, "fp8b": 5000.0, "int8w": 2500.0}                                                   # bf16 MFMA
 STAGES = ("quant_x", "gate_up", "act", "down", "reduce")
 
 
@@ -52,10 +52,11 @@ def layer_bytes_and_flops(wl, ids, T):
     flat = ids.reshape(-1).to(torch.int64).cpu()
     valid = flat[(flat >= 0) & (flat < E)]
     active = int(torch.unique(valid).numel())
-    bw = {"fp8": 1, "fp8b": 1, "mxfp8": 1, "int8": 1, "int4": 0.5}.get(wl.dtype, 2)
+    bw = {"fp8": 1, "fp8b": 1, "mxfp8": 1, "int8": 1, "int4": 0.5, "int8w": 1}.get(wl.dtype, 2)
     # scales: fp32 per output channel (fp8, int8), one e8m0 byte per 32 weights (MX),
     # one fp32 per 128 weights (int4)
     per_expert = int(3 * H * I * bw) + {"fp8": (2 * I + H) * 4, "int8": (2 * I + H) * 4,
+                                        "int8w": (2 * I + H) * 4,
                                         "mxfp8": 3 * H * I // 32,
                                         "int4": 3 * H * I // 128 * 4,
                                         "fp8b": 3 * H * I // (128 * 128) * 4}.get(wl.dtype, 0)
@@ -74,16 +75,16 @@ def stage_bytes(wl, active, P_valid, T):
     mx = wl.dtype == "mxfp8"
     blk = wl.dtype == "fp8b"
     fp8 = wl.dtype in ("fp8", "int8") or mx or blk   # one-byte activation codes
-    bw = 0.5 if wl.dtype == "int4" else (1 if fp8 else 2)
+    bw = 0.5 if wl.dtype == "int4" else (1 if fp8 or wl.dtype == "int8w" else 2)
     bx = 1 if fp8 else 2
     P = T * wl.k
     # per-row activation scales: 4 bytes (fp8) or one byte per 32 values (MX)
     xs = (H // 32 if mx else (H // 128 * 4 if blk else 4)) if fp8 else 0
     hs = (I // 32 if mx else (I // 128 * 4 if blk else 4)) if fp8 else 0
     w1s = ((2 * I * H // 32 if mx else (2 * I * H // 16384 * 4 if blk else 2 * I * 4)) if fp8
-           else (2 * I * H // 128 * 4 if wl.dtype == "int4" else 0))
+           else (2 * I * H // 128 * 4 if wl.dtype == "int4" else (2 * I * 4 if wl.dtype == "int8w" else 0)))
     w2s = ((H * I // 32 if mx else (H * I // 16384 * 4 if blk else H * 4)) if fp8
-           else (H * I // 128 * 4 if wl.dtype == "int4" else 0))
+           else (H * I // 128 * 4 if wl.dtype == "int4" else (H * 4 if wl.dtype == "int8w" else 0)))
     return {
         "routing": P * 4 + P * 12,
         "quant_x": T * H * 2 + T * H + T * xs if fp8 else 0,
@@ -122,6 +123,7 @@ class Layer:
         else:
             fwd = {"fp8": m.moe_forward_fp8, "mxfp8": m.moe_forward_mxfp8,
                    "int8": m.moe_forward_int8, "int4": m.moe_forward_int4,
+                   "int8w": m.moe_forward_int8_w8a16,
                    "fp8b": m.moe_forward_fp8_block}[self.dtype]
             fwd(self.x, self.w, self.routing, W["w1"], W["w1_scale"], W["w2"], W["w2_scale"],
                 self.ws, self.out)
@@ -156,7 +158,7 @@ def stage_pass(layer, steps):
     stage_ms["routing"] = [a.elapsed_time(b) for a, b in rt]
     for i in range(steps):
         for si, s in enumerate(STAGES):
-            if layer.dtype in ("bf16", "int4") and s == "quant_x":
+            if layer.dtype in ("bf16", "int4", "int8w") and s == "quant_x":
                 continue
             if s == "act" and not layer.has_act:   # formed in the gate-up epilogue
                 continue
@@ -243,6 +245,7 @@ def cpu_baseline(wl, layer, W_host, dtype, reps=3):
         else:
             fwd = {"fp8": oracle.forward_fp8, "mxfp8": oracle.forward_mxfp8,
                    "int8": oracle.forward_int8, "int4": oracle.forward_w4a16,
+                   "int8w": oracle.forward_w8a16,
                    "fp8b": oracle.forward_fp8_block}[dtype]
             fwd(x, w, ids, W_host["w1"], W_host["w1_scale"], W_host["w2"], W_host["w2_scale"])
         times.append(time.perf_counter() - t0)
@@ -255,7 +258,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral",
-                    choices=["tiny", "mixtral", "qwen3", "qwen2", "dsv3", "dsv3b", "dsv3mx", "dsv3i8",
+                    choices=["tiny", "mixtral", "qwen3", "qwen2", "dsv3", "dsv3b", "dsv3mx", "dsv3i8", "mixtral8",
                              "mixtral4"])
     ap.add_argument("--tokens", type=int, default=16)
     ap.add_argument("--no-sweep", action="store_true", help="skip the graph-replay T sweep")
@@ -302,7 +305,7 @@ def main():
     if args.router:
         router_bench(moe, wl, args)
         return
-    dtype = wl.dtype if wl.dtype in ("fp8", "fp8b", "mxfp8", "int8", "int4") else "bf16"
+    dtype = wl.dtype if wl.dtype in ("fp8", "fp8b", "mxfp8", "int8", "int4", "int8w") else "bf16"
     T = args.tokens
     log(f"[bench] workload={wl.name} T={T} dtype={dtype}: generating weights")
     W_rows = make_weights(wl, device="cuda")

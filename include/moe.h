@@ -79,8 +79,10 @@ typedef enum {
                                 int8 activations (per-row fp32 scales) */
     MOE_DTYPE_INT4_W4A16 = 4, /* int4 weights (fp32 scale per 128 K values of a row),
                                  bf16 activations */
-    MOE_DTYPE_FP8_BLOCK = 5   /* e4m3 weights with an fp32 scale per 128 x 128 block,
+    MOE_DTYPE_FP8_BLOCK = 5,  /* e4m3 weights with an fp32 scale per 128 x 128 block,
                                  e4m3 activations with one per 128-value row group */
+    MOE_DTYPE_INT8_W8A16 = 6  /* int8 weights (per-output-channel fp32 scales),
+                                 bf16 activations */
 } moe_dtype_t;
 
 /* One row tile of the task map: rows [row_begin, row_begin + rows) of the
@@ -360,6 +362,21 @@ int moe_forward_int4(const void *x, const float *topk_w, const void *routing,
                      const uint8_t *w2, const float *w2_scale,
                      int T, int k, int E, int H, int I,
                      void *workspace, size_t workspace_bytes, void *out, void *stream);
+
+/* int8 w8a16 (SGLang tuning guide dtype list: int8_w8a16, weight-only
+ * int8).  w1 (device) int8 [E][2I][H] and w2 (device) int8 [E][H][I],
+ * packed by moe_pack_weights with dtype MOE_DTYPE_INT8_W8A16; w1_scale
+ * (device) fp32 [E][2I], w2_scale (device) fp32 [E][H]: weight (n, k) =
+ * code * scale[n].  x and the intermediate stay bf16 (bf16 MFMA on weights
+ * converted in registers, fp32 accumulation, the row scale applied to the
+ * sums).  Register streaming at every T.  Errors as moe_forward_bf16. */
+int moe_build_routing_int8_w8a16(const int32_t *topk_ids, int T, int k, int E, int H, int I,
+                                 void *routing, size_t routing_bytes, void *stream);
+int moe_forward_int8_w8a16(const void *x, const float *topk_w, const void *routing,
+                           const int8_t *w1, const float *w1_scale,
+                           const int8_t *w2, const float *w2_scale,
+                           int T, int k, int E, int H, int I,
+                           void *workspace, size_t workspace_bytes, void *out, void *stream);
 
 /* Measurement hook.  When `events` is non-NULL (n >= 10 hipEvent_t
  * handles, host array), every later forward call records events[2*s]

@@ -22,6 +22,7 @@ Functions carry the C names:
     moe_build_routing_int8 / moe_forward_int8   (as the fp8 pair, int8 codes)
     moe_build_routing_int4 / moe_forward_int4   (int4 weights + group scales, bf16 activations)
     moe_build_routing_fp8_block / moe_forward_fp8_block (128x128 weight blocks, 1x128 token groups)
+    moe_build_routing_int8_w8a16 / moe_forward_int8_w8a16 (int8 weights + row scales, bf16 activations)
 
 plus allocation helpers (alloc_routing, alloc_workspace), pack_weights() for a
 whole weight dict, and a convenience moe_layer() that runs routing + forward
@@ -44,8 +45,10 @@ MOE_DTYPE_MXFP8 = 2
 MOE_DTYPE_INT8_W8A8 = 3
 MOE_DTYPE_INT4_W4A16 = 4
 MOE_DTYPE_FP8_BLOCK = 5
+MOE_DTYPE_INT8_W8A16 = 6
 DTYPES = {"bf16": MOE_DTYPE_BF16, "fp8": MOE_DTYPE_FP8_W8A8, "mxfp8": MOE_DTYPE_MXFP8,
-          "int8": MOE_DTYPE_INT8_W8A8, "int4": MOE_DTYPE_INT4_W4A16, "fp8b": MOE_DTYPE_FP8_BLOCK}
+          "int8": MOE_DTYPE_INT8_W8A8, "int4": MOE_DTYPE_INT4_W4A16, "fp8b": MOE_DTYPE_FP8_BLOCK,
+          "int8w": MOE_DTYPE_INT8_W8A16}
 
 
 class MoeError(RuntimeError):
@@ -76,7 +79,8 @@ EXPORTS = ("moe_status_string", "moe_pack_weights", "moe_routing_layout", "moe_w
            "moe_build_routing_bf16", "moe_build_routing_fp8", "moe_build_routing_mxfp8",
            "moe_build_routing_int8", "moe_build_routing_int4", "moe_forward_bf16",
            "moe_forward_fp8", "moe_forward_mxfp8", "moe_forward_int8", "moe_forward_int4",
-           "moe_build_routing_fp8_block", "moe_forward_fp8_block", "moe_set_stage_events", "moe_device_cu_count")
+           "moe_build_routing_fp8_block", "moe_forward_fp8_block",
+           "moe_build_routing_int8_w8a16", "moe_forward_int8_w8a16", "moe_set_stage_events", "moe_device_cu_count")
 
 
 def _load():
@@ -120,6 +124,8 @@ def _load():
     L.moe_forward_int4.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
     L.moe_forward_int8.restype = i
     L.moe_forward_int8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
+    L.moe_forward_int8_w8a16.restype = i
+    L.moe_forward_int8_w8a16.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
     L.moe_set_stage_events.restype = i
     L.moe_set_stage_events.argtypes = [ctypes.POINTER(P), i]
     L.moe_device_cu_count.restype = i
@@ -153,7 +159,7 @@ def moe_pack_weights(w, dtype="bf16", out=None, stream=None):
     """Packed copy of a row-major [E][rows][cols] weight tensor (bf16; uint8
     e4m3 codes for dtype "fp8", "fp8b" and "mxfp8"; int8 codes for "int8"; uint8 bytes
     of two int4 codes for "int4", whose K length is twice the byte count)."""
-    want = {"bf16": torch.bfloat16, "int8": torch.int8}.get(dtype, torch.uint8)
+    want = {"bf16": torch.bfloat16, "int8": torch.int8, "int8w": torch.int8}.get(dtype, torch.uint8)
     if w.dtype != want or w.dim() != 3 or not w.is_contiguous():
         raise ValueError(f"moe_pack_weights: expected contiguous {want} [E][rows][cols]")
     E, rows, cols = w.shape
@@ -323,6 +329,11 @@ def moe_build_routing_int4(topk_ids, E, H, I, routing, stream=None):
                    stream)
 
 
+def moe_build_routing_int8_w8a16(topk_ids, E, H, I, routing, stream=None):
+    _build_routing(_lib.moe_build_routing_int8_w8a16, "moe_build_routing_int8_w8a16", topk_ids, E, H, I,
+                   routing, stream)
+
+
 def moe_build_routing_fp8_block(topk_ids, E, H, I, routing, stream=None):
     _build_routing(_lib.moe_build_routing_fp8_block, "moe_build_routing_fp8_block", topk_ids, E, H, I,
                    routing, stream)
@@ -332,7 +343,8 @@ def build_routing(topk_ids, E, H, I, routing, dtype="bf16", stream=None):
     """The routing build of the given dtype's forward."""
     {"bf16": moe_build_routing_bf16, "fp8": moe_build_routing_fp8,
      "mxfp8": moe_build_routing_mxfp8, "int8": moe_build_routing_int8,
-     "int4": moe_build_routing_int4, "fp8b": moe_build_routing_fp8_block}[dtype](
+     "int4": moe_build_routing_int4, "fp8b": moe_build_routing_fp8_block,
+     "int8w": moe_build_routing_int8_w8a16}[dtype](
         topk_ids, E, H, I, routing, stream)
 
 
@@ -411,6 +423,24 @@ def moe_forward_fp8_block(x, topk_w, routing, w1, w1_scale, w2, w2_scale, worksp
     return out
 
 
+def moe_forward_int8_w8a16(x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, out, stream=None):
+    T, H = x.shape
+    k = topk_w.shape[1]
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    _check_tensor("x", x, torch.bfloat16, (T, H))
+    _check_tensor("topk_w", topk_w, torch.float32, (T, k))
+    _check_tensor("w1", w1, torch.int8, (E, 2 * I, H))
+    _check_tensor("w1_scale", w1_scale, torch.float32, (E, 2 * I))
+    _check_tensor("w2", w2, torch.int8, (E, H, I))
+    _check_tensor("w2_scale", w2_scale, torch.float32, (E, H))
+    _check_tensor("out", out, torch.bfloat16, (T, H))
+    _check("moe_forward_int8_w8a16", _lib.moe_forward_int8_w8a16(
+        _ptr(x), _ptr(topk_w), _ptr(routing), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale),
+        T, k, E, H, I, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
 def moe_forward_int4(x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, out, stream=None):
     T, H = x.shape
     k = topk_w.shape[1]
@@ -484,7 +514,8 @@ def moe_layer(x, topk_ids, topk_w, weights, dtype="bf16", out=None, stream=None)
         moe_forward_bf16(x, topk_w, routing, weights["w1"], weights["w2"], ws, out, stream)
     else:
         fwd = {"fp8": moe_forward_fp8, "mxfp8": moe_forward_mxfp8, "int8": moe_forward_int8,
-               "int4": moe_forward_int4, "fp8b": moe_forward_fp8_block}[dtype]
+               "int4": moe_forward_int4, "fp8b": moe_forward_fp8_block,
+               "int8w": moe_forward_int8_w8a16}[dtype]
         fwd(x, topk_w, routing, weights["w1"], weights["w1_scale"], weights["w2"],
             weights["w2_scale"], ws, out, stream)
     return out, routing, ws

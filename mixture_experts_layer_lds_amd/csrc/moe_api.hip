@@ -44,7 +44,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 bool known_dtype(int dtype) {
   return dtype == MOE_DTYPE_BF16 || dtype == MOE_DTYPE_FP8_W8A8 || dtype == MOE_DTYPE_MXFP8 ||
          dtype == MOE_DTYPE_INT8_W8A8 || dtype == MOE_DTYPE_INT4_W4A16 ||
-         dtype == MOE_DTYPE_FP8_BLOCK;
+         dtype == MOE_DTYPE_FP8_BLOCK || dtype == MOE_DTYPE_INT8_W8A16;
 }
 
 int check_shape(int T, int k, int E, int H, int I, int dtype = MOE_DTYPE_BF16) {
@@ -151,17 +151,19 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   const long avg = active > 0 ? (P + active - 1) / active : 1;
   const int esz_t = dtype == MOE_DTYPE_BF16 ? 2 : 1;
   const int nsteps1 = H * esz_t / 64, nsteps2 = I * esz_t / 64;
-  if (dtype == MOE_DTYPE_INT4_W4A16 || dtype == MOE_DTYPE_FP8_BLOCK) {
-    // int4 weights, block-scaled fp8: register streaming (128-value K steps) at every size;
-    // waves per workgroup by the streaming cost model on whole steps
+  if (dtype == MOE_DTYPE_INT4_W4A16 || dtype == MOE_DTYPE_FP8_BLOCK || dtype == MOE_DTYPE_INT8_W8A16) {
+    // int4 and int8 weights, block-scaled fp8: register streaming (128-value K steps;
+    // int8: 64-value steps) at every size; waves per workgroup by the streaming cost
+    // model on whole steps
     p.tiling = kStreaming;
     p.block_m = avg <= 8 ? 16 : (avg <= 16 ? 32 : 64);
     p.mb = p.block_m / 16;
     p.max_tasks = (int)(P / p.block_m + (P < E ? P : E));
     long est = (P + p.block_m - 1) / p.block_m;
     if (est < active) est = active;
-    p.sw1 = pick_unit_waves(H / 128, est * ((long)I / 16));
-    p.sw2 = pick_unit_waves(I / 128, est * ((long)H / 32));
+    const int per = dtype == MOE_DTYPE_INT8_W8A16 ? 64 : 128;   // K values per step
+    p.sw1 = pick_unit_waves(H / per, est * ((long)I / 16));
+    p.sw2 = pick_unit_waves(I / per, est * ((long)H / 32));
     p.su1 = p.su2 = 1;
     return p;
   }
@@ -292,7 +294,7 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
     W->tiling = p.tiling;
     return;
   }
-  if (dtype == MOE_DTYPE_INT4_W4A16) {   // bf16 activations: bf16 h and y rows
+  if (dtype == MOE_DTYPE_INT4_W4A16 || dtype == MOE_DTYPE_INT8_W8A16) {   // bf16 activations: bf16 h, y
     W->xq = W->x_scale = W->x_scale_rows = W->g = W->h_scale = kNone;
     W->h = take(2 * P * I);
     W->y = take(2 * P * H);
@@ -610,13 +612,13 @@ int forward_fp8b(const void* x, const float* topk_w, const void* routing, const 
   return MOE_OK;
 }
 
-// int4 w4a16 forward: register-streaming gate-up (int4 weights converted in
-// registers, SiLU-and-mul in the epilogue, bf16 h), down (bf16 rows), the
-// top-k reduction.
-int forward_w4(const void* x, const float* topk_w, const void* routing, const void* w1,
+// Weight-only forward (int4 w4a16, int8 w8a16): register-streaming gate-up
+// (weights converted in registers, SiLU-and-mul in the epilogue, bf16 h),
+// down (bf16 rows), the top-k reduction.
+int forward_w4(int dtype, const void* x, const float* topk_w, const void* routing, const void* w1,
                const float* w1_scale, const void* w2, const float* w2_scale, int T, int k, int E,
                int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
-  int rc = check_shape(T, k, E, H, I, MOE_DTYPE_INT4_W4A16);
+  int rc = check_shape(T, k, E, H, I, dtype);
   if (rc != MOE_OK) return rc;
   if (T == 0) return MOE_OK;
   if (!x || !topk_w || !routing || !w1 || !w2 || !w1_scale || !w2_scale || !workspace || !out)
@@ -625,11 +627,12 @@ int forward_w4(const void* x, const float* topk_w, const void* routing, const vo
       !aligned(topk_w, 4) || !aligned(routing, 16) || !aligned(workspace, 256) ||
       !aligned(w1_scale, 4) || !aligned(w2_scale, 4))
     return MOE_ERR_INVALID_ARG;
-  const Plan p = make_plan(MOE_DTYPE_INT4_W4A16, T, k, E, H, I);
+  const Plan p = make_plan(dtype, T, k, E, H, I);
   moe_routing_layout_t L;
   routing_layout(T, k, E, p, &L);
   moe_workspace_layout_t W;
-  workspace_layout(MOE_DTYPE_INT4_W4A16, T, k, H, I, p, &W);
+  workspace_layout(dtype, T, k, H, I, p, &W);
+  const bool w8 = dtype == MOE_DTYPE_INT8_W8A16;
   if (workspace_bytes < W.total_bytes) return MOE_ERR_BUFFER_TOO_SMALL;
   int cus = 0;
   if ((rc = cu_count(&cus)) != MOE_OK) return rc;
@@ -653,8 +656,9 @@ int forward_w4(const void* x, const float* topk_w, const void* routing, const vo
     a.w_rows = 2 * I;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    e = moe_host::launch_stream_w4(a, true, p.mb, p.sw1,
-                                   stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
+    const int grid = stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus);
+    e = w8 ? moe_host::launch_stream_w8(a, true, p.mb, p.sw1, grid, s)
+           : moe_host::launch_stream_w4(a, true, p.mb, p.sw1, grid, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
@@ -672,8 +676,9 @@ int forward_w4(const void* x, const float* topk_w, const void* routing, const vo
     a.w_rows = H;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    e = moe_host::launch_stream_w4(a, false, p.mb, p.sw2,
-                                   stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
+    const int grid = stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus);
+    e = w8 ? moe_host::launch_stream_w8(a, false, p.mb, p.sw2, grid, s)
+           : moe_host::launch_stream_w4(a, false, p.mb, p.sw2, grid, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
@@ -1202,8 +1207,21 @@ int moe_forward_int4(const void* x, const float* topk_w, const void* routing, co
                      const float* w1_scale, const uint8_t* w2, const float* w2_scale, int T, int k,
                      int E, int H, int I, void* workspace, size_t workspace_bytes, void* out,
                      void* stream) {
-  return forward_w4(x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
-                    workspace_bytes, out, stream);
+  return forward_w4(MOE_DTYPE_INT4_W4A16, x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I,
+                    workspace, workspace_bytes, out, stream);
+}
+
+int moe_build_routing_int8_w8a16(const int32_t* topk_ids, int T, int k, int E, int H, int I,
+                                 void* routing, size_t routing_bytes, void* stream) {
+  return build_routing(MOE_DTYPE_INT8_W8A16, topk_ids, T, k, E, H, I, routing, routing_bytes, stream);
+}
+
+int moe_forward_int8_w8a16(const void* x, const float* topk_w, const void* routing, const int8_t* w1,
+                           const float* w1_scale, const int8_t* w2, const float* w2_scale, int T, int k,
+                           int E, int H, int I, void* workspace, size_t workspace_bytes, void* out,
+                           void* stream) {
+  return forward_w4(MOE_DTYPE_INT8_W8A16, x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I,
+                    workspace, workspace_bytes, out, stream);
 }
 
 int moe_build_routing_int8(const int32_t* topk_ids, int T, int k, int E, int H, int I,

@@ -301,6 +301,10 @@ hipError_t launch_quant_rows_i8(const uint16_t* x, int T, int H, int8_t* xq, flo
                                 hipStream_t s);
 hipError_t launch_requant_rows_i8(const float* h32, int P, int I, const int32_t* expert_offsets, int E,
                                   int8_t* hq, float* h_scale, hipStream_t s);
+// int8 w8a16 register-streaming GEMM: a bf16 rows, b packed int8 weights
+// with per-row fp32 scales b_scale [E][w_rows]; gate-up writes bf16
+// SiLU(gate)*up, down bf16 rows.
+hipError_t launch_stream_w8(const StreamArgs& a, bool gateup, int mb, int waves, int grid, hipStream_t s);
 // Block-scaled fp8 register-streaming GEMM (K % 128 == 0): a e4m3 rows, b
 // packed e4m3 weights.  block: unit-major group scales row_scale [K/128][P]
 // (per sorted row), b_scale fp32 [E][w_rows/128][K/128]; gate-up writes fp32

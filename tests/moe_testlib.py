@@ -29,7 +29,7 @@ def device_weights(wl, device="cuda"):
 
 
 def path_dtype(wl):
-    return wl.dtype if wl.dtype in ("fp8", "fp8b", "mxfp8", "int8", "int4") else "bf16"
+    return wl.dtype if wl.dtype in ("fp8", "fp8b", "mxfp8", "int8", "int4", "int8w") else "bf16"
 
 
 def run_gpu(lib, x, ids, w, W, dtype, packed=None):
@@ -55,6 +55,9 @@ def oracle_rows(x, ids, w, W, dtype, rows=None, want_quant=False):
     if dtype == "fp8b":
         return oracle.forward_fp8_block(xb, wc, idc, W["w1"].cpu(), W["w1_scale"].cpu(), W["w2"].cpu(),
                                         W["w2_scale"].cpu(), rows=rows, want_quant=want_quant)
+    if dtype == "int8w":
+        return oracle.forward_w8a16(xb, wc, idc, W["w1"].cpu(), W["w1_scale"].cpu(), W["w2"].cpu(),
+                                    W["w2_scale"].cpu(), rows=rows)
     if dtype == "int4":
         return oracle.forward_w4a16(xb, wc, idc, W["w1"].cpu(), W["w1_scale"].cpu(), W["w2"].cpu(),
                                     W["w2_scale"].cpu(), rows=rows)
@@ -73,8 +76,8 @@ def check_tol(got, ref, dtype, what=""):
     ref = np.asarray(ref, dtype=np.float64)
     err = float(np.max(np.abs(got - ref))) if got.size else 0.0
     scale = float(np.max(np.abs(ref))) if ref.size else 0.0
-    # bf16 activations (bf16, int4 weights) or 8-bit activations (fp8, fp8b, mxfp8, int8)
-    bound = BF16_REL * scale + BF16_ABS if dtype in ("bf16", "int4") else FP8_REL * scale
+    # bf16 activations (bf16, int4 / int8 weights) or 8-bit activations (fp8, fp8b, mxfp8, int8)
+    bound = BF16_REL * scale + BF16_ABS if dtype in ("bf16", "int4", "int8w") else FP8_REL * scale
     cos = float(np.dot(got.ravel(), ref.ravel()) /
                 max(np.linalg.norm(got) * np.linalg.norm(ref), 1e-300)) if got.size else 1.0
     log(f"  {what} max|err|={err:.3e} max|ref|={scale:.3e} bound={bound:.3e} cos={cos:.6f}")

@@ -260,7 +260,7 @@ def workload_weights(name):
     return _weights_cache[name]
 
 
-FULL = [(name, T) for name in ("mixtral", "qwen3", "qwen2", "dsv3", "dsv3b", "dsv3mx", "dsv3i8", "mixtral4") for T in WORKLOADS[name].Ts]
+FULL = [(name, T) for name in ("mixtral", "qwen3", "qwen2", "dsv3", "dsv3b", "dsv3mx", "dsv3i8", "mixtral4", "mixtral8") for T in WORKLOADS[name].Ts]
 
 
 @pytest.mark.parametrize("name,T", FULL)

@@ -57,7 +57,7 @@ CASES = [(name, T) for name, wl in WORKLOADS.items() for T in wl.Ts]
 def test_routing_workloads(lib, name, T):
     wl = WORKLOADS[name]
     _, ids, _ = make_tokens(wl, T)
-    dtype = wl.dtype if wl.dtype in ("fp8", "fp8b", "mxfp8", "int8", "int4") else "bf16"
+    dtype = wl.dtype if wl.dtype in ("fp8", "fp8b", "mxfp8", "int8", "int4", "int8w") else "bf16"
     check_route(lib, ids, wl.E, wl.H, wl.I, dtype, name)
 
 
