@@ -37,6 +37,7 @@ struct Plan {
   int ks1 = 4, nbuf1 = 4;        // strips: K steps per stage, stages in flight (gate-up)
   int ks2 = 4, nbuf2 = 4;        // (down)
   bool fp8_units = false;        // fp8 streaming on 128-value units (fp8b_gemm.hip, per-channel mode)
+  bool half1 = false;            // bf16 streaming gate-up on half-width (8-column) items
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -238,6 +239,26 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   if (!tiled) {
     choose_stream(nsteps1, p.mb, est_tasks * ((long)I / 16), &p.sw1, &p.su1);
     choose_stream(nsteps2, p.mb, est_tasks * ((long)H / 32), &p.sw2, &p.su2);
+    if (dtype == MOE_DTYPE_BF16 && p.mb == 1 && I % 8 == 0) {
+      // Half-width gate-up items when the full-width count leaves some CUs
+      // one item more than others: the busiest CU streams ceil(n / CUs)
+      // items' bytes (Qwen3-30B-A3B T=1: 384 items, 2 on some of 256 CUs;
+      // as 768 half items, 1.5).
+      // Only where every workgroup still runs a single item with at least
+      // half the full-width split (more rounds of first-load latency, or
+      // twice the K steps per wave, cost more than the balance gains:
+      // Qwen2-57B T=1 with three half items per workgroup, 33.1 -> 34.0 us).
+      const long full = est_tasks * ((long)I / 16), cus = kStreamWaves / 8;
+      if ((2 * full + cus - 1) / cus < 2 * ((full + cus - 1) / cus)) {
+        for (int w = 8; w >= 1 && w * 2 >= p.sw1; w /= 2) {
+          if (nsteps1 % (2 * w) || 2 * full > kStreamWaves / w) continue;
+          p.half1 = true;
+          p.sw1 = w;
+          p.su1 = 2;
+          break;
+        }
+      }
+    }
     if (dtype == MOE_DTYPE_FP8_W8A8 && H % 128 == 0 && I % 128 == 0) {
       // whole 128-value units: one 16x16x128 MFMA per unit instead of four 16x16x32
       p.fp8_units = true;
@@ -973,10 +994,14 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     a.topk = k;
     a.max_tasks = p.max_tasks;
     a.P = P;
-    e = p.fp8_units ? moe_host::launch_stream_fp8b(a, true, false, p.mb, p.sw1,
-                                                   stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s)
-                    : moe_host::launch_stream_gemm(a, true, fp8, 0, p.mb, p.sw1, p.su1,
-                                                   stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
+    if (p.half1)
+      e = moe_host::launch_stream_half_gateup(a, p.sw1, stream_grid((long)p.max_tasks * (I / 8), p.sw1, cus), s);
+    else if (p.fp8_units)
+      e = moe_host::launch_stream_fp8b(a, true, false, p.mb, p.sw1,
+                                       stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
+    else
+      e = moe_host::launch_stream_gemm(a, true, fp8, 0, p.mb, p.sw1, p.su1,
+                                       stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (fp8) {

@@ -287,6 +287,9 @@ struct StreamArgs {
   int max_tasks;
 };
 
+// bf16 gate-up on 16-row tiles with half-width items (8 h columns each; K
+// steps a multiple of 2 * waves).
+hipError_t launch_stream_half_gateup(const StreamArgs& a, int waves, int grid, hipStream_t s);
 // (mb, waves, u) = 16-row blocks per tile, waves per workgroup, K steps per stage.
 bool stream_config_supported(int mb, int waves, int u);
 // kind: 0 per-channel scales (bf16, or fp8 by `fp8`), 1 MXFP8 block scales,

@@ -328,6 +328,105 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
   }
 }
 
+// bf16 gate-up with half-width items (decode): item = (16-row task tile, 8
+// h columns), its 16-row weight block made of 8 gate rows and the matching
+// 8 up rows, so twice as many items of half the bytes spread evenly when
+// the full-width count leaves CUs with one more item than others (e.g. 384
+// items on 256 CUs).  Lanes of weight rows 0-7 read gate rows, 8-15 the up
+// rows (half of a packed 16-row chunk each); in the epilogue lane c (c < 8)
+// takes the up sum of lane c + 8 and writes h column 8 * item + c.
+template <int W>
+__global__ void __launch_bounds__(W * 64)
+stream_half_gateup_kernel(moe_host::StreamArgs g) {
+  constexpr int U = 2;
+  __shared__ f32x4 red[W][64];
+  const int lane = threadIdx.x & 63;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
+  const int n_groups = g.N_out / 8;
+  const int total = num_tasks * n_groups;
+  const size_t row_bytes = (size_t)g.K * 2;
+  const int nsteps = (int)(row_bytes / 64);
+  const int spw = nsteps / W;
+  const int ngroups = spw / U;
+  const int w_blocks = g.w_rows / 16;
+  const char* __restrict__ A = static_cast<const char*>(g.a);
+  const char* __restrict__ B = static_cast<const char*>(g.b);
+
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per_xcd = G / 8, extra = G % 8;
+  const int vid = (xcd < extra ? xcd * (per_xcd + 1) : extra * (per_xcd + 1) + (xcd - extra) * per_xcd) + slot;
+
+  for (int item = vid; item < total; item += G) {
+    const int ti = item / n_groups;
+    const int c8 = item - ti * n_groups;
+    const moe_task_t task = load_task_scalar(g.tasks + ti);
+    const int step0 = wave * spw;
+    // this lane's weight row: gate row 8 c8 + lrow, or up row I + 8 c8 + (lrow - 8)
+    const int wrow = lrow < 8 ? 8 * c8 + lrow : g.N_out + 8 * c8 + (lrow - 8);
+    const char* bp = B + (((size_t)task.expert * w_blocks + wrow / 16) * nsteps + step0) * 1024 +
+                     16 * ((wrow & 15) + 16 * lgrp);
+    const i32x16_t sp = load16_scalar(g.sorted_pairs + task.row_begin);
+    const int p = lrow < task.rows ? spread16(sp, lane) : sp[0];
+    const char* ap = A + (size_t)(p / g.topk) * row_bytes + (size_t)step0 * 64 + 16 * lgrp;
+
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    u32x4 fa0[U], fb0[U], fa1[U], fb1[U];
+    auto load = [&](u32x4 (&fa)[U], u32x4 (&fb)[U], int grp) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int step = grp * U + u;
+        fb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp + (size_t)step * 1024));
+        fa[u] = *reinterpret_cast<const u32x4*>(ap + (size_t)step * 64);
+      }
+    };
+    auto compute = [&](const u32x4 (&fa)[U], const u32x4 (&fb)[U]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < U; u++) stream_mfma<false>(acc, fa[u], fb[u]);
+    };
+    load(fa0, fb0, 0);
+    int grp = 0;
+    for (; grp + 2 < ngroups; grp += 2) {
+      load(fa1, fb1, grp + 1);
+      compute(fa0, fb0);
+      load(fa0, fb0, grp + 2);
+      compute(fa1, fb1);
+    }
+    if (grp + 1 < ngroups) {
+      load(fa1, fb1, grp + 1);
+      compute(fa0, fb0);
+      compute(fa1, fb1);
+    } else {
+      compute(fa0, fb0);
+    }
+
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+      f32x4 tot = red[0][lane];
+#pragma unroll
+      for (int s2 = 1; s2 < W; s2++) tot += red[s2][lane];
+      // lane holds weight row lrow (gate for lrow < 8) and token rows 4 lgrp + i
+      f32x4 up;
+#pragma unroll
+      for (int i = 0; i < 4; i++) up[i] = __shfl(tot[i], (lane & 48) | ((lrow + 8) & 15), 64);
+      if (lrow < 8) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int rr = 4 * lgrp + i;
+          if (rr < task.rows)
+            static_cast<uint16_t*>(g.c)[(size_t)(task.row_begin + rr) * g.N_out + 8 * c8 + lrow] =
+                f32_to_bf16_bits(silu_f32(tot[i]) * up[i]);
+        }
+      }
+    }
+    __syncthreads();   // LDS free for the next item
+  }
+}
+
 template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX, bool I8 = false>
 static hipError_t launch_stream_t(const moe_host::StreamArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL((stream_gemm_kernel<MB, W, U, GATEUP, FP8, MX, I8>), dim3(grid), dim3(W * 64), 0, s, a);
@@ -365,6 +464,17 @@ namespace moe_host {
   X(2, 1, 2) X(2, 2, 2) X(2, 4, 2) X(2, 8, 2) \
   X(4, 1, 2) X(4, 2, 2) X(4, 4, 2) X(4, 8, 2) \
   X(1, 1, 1) X(2, 1, 1) X(4, 1, 1)
+
+hipError_t launch_stream_half_gateup(const StreamArgs& a, int waves, int grid, hipStream_t s) {
+  switch (waves) {
+    case 1: hipLaunchKernelGGL(moe::stream_half_gateup_kernel<1>, dim3(grid), dim3(64), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(moe::stream_half_gateup_kernel<2>, dim3(grid), dim3(128), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(moe::stream_half_gateup_kernel<4>, dim3(grid), dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(moe::stream_half_gateup_kernel<8>, dim3(grid), dim3(512), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 bool stream_config_supported(int mb, int waves, int u) {
 #define MOE_STREAM_CASE(M, Wv, Uv) if (mb == M && waves == Wv && u == Uv) return true;
