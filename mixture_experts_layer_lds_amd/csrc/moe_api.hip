@@ -761,7 +761,6 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
     a.header = R.header;
     a.tasks = R.tasks;
     a.c = h32;
-    a.row_amax = nullptr;   // the requantisation pass finds the row amax
     a.K = H;
     a.N_out = I;
     a.w_rows = 2 * I;
@@ -987,7 +986,6 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     a.header = R.header;
     a.tasks = R.tasks;
     a.c = fp8 ? static_cast<void*>(h32) : h;
-    a.row_amax = nullptr;   // the requantisation pass finds the row amax
     a.K = H;
     a.N_out = I;
     a.w_rows = 2 * I;

@@ -275,8 +275,6 @@ struct StreamArgs {
   const int32_t* header;
   const moe_task_t* tasks;
   void* c;                      // gate-up: h [P][N_out] (bf16, or fp32 on fp8); down: y [P][N_out] bf16
-  float* row_amax;              // fp8 / int8 gate-up: [P] atomic-max slots (pre-cleared), or
-                                // null when the requantisation pass finds the row amax itself
   const uint8_t* a_mx;          // MX: e8m0 codes of a's rows [rows][K/32] (gate-up: token rows)
   const uint8_t* b_mx;          // MX: e8m0 codes of the weights [E][w_rows][K/32]
   int P;                        // block fp8: sorted rows (stride of the unit-major row scales)

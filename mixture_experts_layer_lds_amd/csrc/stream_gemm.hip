@@ -22,9 +22,8 @@
 //  * The waves' partial sums meet in LDS and are added in ascending wave
 //    order (deterministic).  Gate-up then writes h = SiLU(gate) * up: bf16,
 //    or on fp8 the fp32 values for the requantisation pass, which finds
-//    each row's amax (with row_amax set, the epilogue also folds it into the
-//    row's slot by an order-independent atomic max on the non-negative
-//    float bits; those atomics cost about 8% of the gate-up time).
+//    each row's amax from the row (folding it here with atomics cost about
+//    8% of the gate-up time).
 //    Down writes bf16 rows; on fp8 only the weight column scale is applied
 //    there and the row scale by the top-k reduction.
 //  * Per-item metadata (task record, token indices, fp8 scales) comes from
@@ -300,13 +299,6 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
             const size_t r = (size_t)(task.row_begin + rr);
             if constexpr (FP8) static_cast<float*>(g.c)[r * g.N_out + col] = hv[i];
             else static_cast<uint16_t*>(g.c)[r * g.N_out + col] = f32_to_bf16_bits(hv[i]);
-          }
-          if (FP8 && !MX && g.row_amax) {
-            // row amax over this item's 16 columns, folded into the row's slot
-            const float mx = max16(ok ? __builtin_fabsf(hv[i]) : 0.0f);
-            if (ok && lrow == 0)
-              atomicMax(reinterpret_cast<unsigned int*>(g.row_amax) + task.row_begin + rr,
-                        __float_as_uint(mx));
           }
         }
       } else {
