@@ -92,3 +92,12 @@ def sample_rows(T, n, seed=0):
     g = np.random.default_rng(seed)
     mid = sorted(g.choice(np.arange(1, T - 1), size=n - 2, replace=False).tolist())
     return [0] + mid + [T - 1]
+
+
+def golden(name):
+    """A fixture of values printed on the pages (tests/golden/<name>.json, each
+    with its citation)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", name + ".json")) as f:
+        return json.load(f)

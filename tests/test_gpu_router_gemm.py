@@ -20,7 +20,7 @@ import torch
 
 import oracle
 from moe_inputs import custom_workload, make_weights, router_hidden, router_weight
-from moe_testlib import check_tol, log
+from moe_testlib import check_tol, log, golden
 
 pytestmark = pytest.mark.gpu
 
@@ -103,7 +103,8 @@ def test_router_gemm_parity(lib, T, N, K):
 def test_pages_error_target(lib, T):
     # the blog's shape: K = 4096, N = 192; max abs error against the
     # fp32-weight product within 0.00177
-    N, K = 192, 4096
+    tgt = golden("router_gemm_error_target")
+    N, K = tgt["N"], tgt["K"]
     w = router_weight(N, K, seed=8)
     x = router_hidden(T, K, seed=9 + T)
     pair = lib.moe_router_split_weights(w.cuda())
@@ -111,8 +112,8 @@ def test_pages_error_target(lib, T):
     torch.cuda.synchronize()
     exact = x.double() @ w.double().T
     err = float((got - exact).abs().max())
-    log(f"  T={T}: max|err| vs fp32 weights {err:.3e} (target 1.77e-3)")
-    assert err <= 0.00177
+    log(f"  T={T}: max|err| vs fp32 weights {err:.3e} (target {tgt['max_abs_error']})")
+    assert err <= tgt["max_abs_error"]
 
 
 def test_router_gemm_large_sampled(lib):

@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle
+from moe_testlib import golden
 from moe_inputs import router_hidden, router_weight
 
 
@@ -101,7 +102,8 @@ def test_pages_shape_error_target():
     # the blog's sweep shape: K = 4096, N = 192; fp32 weights of a typical
     # router init (N(0, 0.02)); the error target is 0.00177 max abs error
     # against the fp32-weight product
-    T, N, K = 256, 192, 4096
+    tgt = golden("router_gemm_error_target")
+    T, N, K = 256, tgt["N"], tgt["K"]
     w = rand_w((N, K), 8)
     x = router_hidden(T, K, 9)
     hi, lo = oracle.router_split(w.numpy())
@@ -110,5 +112,5 @@ def test_pages_shape_error_target():
     err_split = float(np.abs(s - exact).max())
     err_bf16 = float(np.abs((x.double() @ w.bfloat16().double().T).numpy() - exact).max())
     print(f"max|err| split {err_split:.3e}, plain bf16 weights {err_bf16:.3e}")
-    assert err_split <= 0.00177
-    assert err_bf16 > 0.00177
+    assert err_split <= tgt["max_abs_error"]
+    assert err_bf16 > tgt["max_abs_error"]
