@@ -402,12 +402,19 @@ def test_strip_all_pairs_dropped(lib, dtype):
 
 
 @pytest.mark.parametrize("dtype,E,rows,cols", [("bf16", 3, 32, 64), ("bf16", 2, 48, 160),
-                                                ("fp8", 3, 16, 128), ("fp8", 1, 64, 192)])
+                                                ("fp8", 3, 16, 128), ("fp8", 1, 64, 192),
+                                                ("int8w", 2, 32, 128), ("int4", 2, 32, 256)])
 def test_pack_weights_is_the_documented_permutation(lib, dtype, E, rows, cols):
     g = torch.Generator().manual_seed(rows + cols)
     if dtype == "bf16":
         w = torch.randn(E, rows, cols, generator=g).bfloat16()
         raw = w.view(torch.uint8).view(E, rows, cols * 2)
+    elif dtype == "int8w":
+        w = torch.randint(-128, 128, (E, rows, cols), generator=g, dtype=torch.int8)
+        raw = w.view(torch.uint8)
+    elif dtype == "int4":
+        w = torch.randint(0, 256, (E, rows, cols // 2), generator=g, dtype=torch.uint8)   # two codes a byte
+        raw = w
     else:
         w = torch.randint(0, 256, (E, rows, cols), generator=g, dtype=torch.uint8)
         raw = w
