@@ -30,19 +30,22 @@
 
 namespace moe {
 
-constexpr int kFp8bNB = 2;
-
-template <int MB, int W, bool GATEUP, bool BLOCK>
+// NB weight blocks per item: 2 (gate-up: one gate and one up block; down:
+// 32 columns), or 4 on 64-row tiles (gate-up: two of each, 32 h columns;
+// down: 64 columns), which halves the re-reads of the tile's token rows
+// across an expert's column groups.
+template <int MB, int W, bool GATEUP, bool BLOCK, int NB = 2>
 __global__ void __launch_bounds__(W * 64)
 stream_fp8b_kernel(moe_host::StreamArgs g) {
-  constexpr int NB = kFp8bNB;
+  static_assert(NB == 2 || NB == 4, "two or four weight blocks per item");
+  constexpr int NH = GATEUP ? NB / 2 : NB;   // 16-column output blocks per item
   __shared__ f32x4 red[W][MB][NB][64];
   const int lane = threadIdx.x & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
-  const int n_groups = g.N_out / 16 / (GATEUP ? 1 : NB);
+  const int n_groups = g.N_out / 16 / NH;
   const int total = num_tasks * n_groups;
   const int nsteps = g.K / 64;    // 64-byte steps of e4m3
   const int units = g.K / 128;    // 128-value units = scale groups
@@ -63,8 +66,11 @@ stream_fp8b_kernel(moe_host::StreamArgs g) {
     const moe_task_t task = load_task_scalar(g.tasks + ti);
     int blk[NB];
     if constexpr (GATEUP) {
-      blk[0] = cg;
-      blk[1] = g.N_out / 16 + cg;
+#pragma unroll
+      for (int h = 0; h < NH; h++) {
+        blk[h] = cg * NH + h;                        // gate rows
+        blk[NH + h] = g.N_out / 16 + cg * NH + h;    // the matching up rows
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < NB; q++) blk[q] = cg * NB + q;
@@ -185,10 +191,13 @@ stream_fp8b_kernel(moe_host::StreamArgs g) {
       if (rr < task.rows) {
         const size_t r = (size_t)(task.row_begin + rr);
         if constexpr (GATEUP) {
-          f32x4 hv;
 #pragma unroll
-          for (int i4 = 0; i4 < 4; i4++) hv[i4] = silu_f32(tot[0][i4]) * tot[1][i4];
-          *reinterpret_cast<f32x4*>(static_cast<float*>(g.c) + r * g.N_out + cg * 16 + 4 * lgrp) = hv;
+          for (int h = 0; h < NH; h++) {
+            f32x4 hv;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; i4++) hv[i4] = silu_f32(tot[h][i4]) * tot[NH + h][i4];
+            *reinterpret_cast<f32x4*>(static_cast<float*>(g.c) + r * g.N_out + blk[h] * 16 + 4 * lgrp) = hv;
+          }
         } else {
 #pragma unroll
           for (int q = 0; q < NB; q++) {
@@ -260,8 +269,18 @@ quant_groups_kernel(const void* __restrict__ in, int n, int nrows, const int32_t
 }
 
 template <int MB, int W>
-static hipError_t launch_fp8b_t(const moe_host::StreamArgs& a, bool gateup, bool block, int grid,
+static hipError_t launch_fp8b_t(const moe_host::StreamArgs& a, bool gateup, bool block, int nb, int grid,
                                 hipStream_t s) {
+  if (block && nb == 4) {
+    if constexpr (MB == 4 && W <= 2) {
+      if (gateup)
+        hipLaunchKernelGGL((stream_fp8b_kernel<MB, W, true, true, 4>), dim3(grid), dim3(W * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((stream_fp8b_kernel<MB, W, false, true, 4>), dim3(grid), dim3(W * 64), 0, s, a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (block) {
     if (gateup)
       hipLaunchKernelGGL((stream_fp8b_kernel<MB, W, true, true>), dim3(grid), dim3(W * 64), 0, s, a);
@@ -281,9 +300,9 @@ static hipError_t launch_fp8b_t(const moe_host::StreamArgs& a, bool gateup, bool
 namespace moe_host {
 
 hipError_t launch_stream_fp8b(const StreamArgs& a, bool gateup, bool block, int mb, int waves, int grid,
-                              hipStream_t s) {
+                              hipStream_t s, int nb) {
 #define MOE_FP8B_CASE(M, Wv) \
-  if (mb == M && waves == Wv) return moe::launch_fp8b_t<M, Wv>(a, gateup, block, grid, s);
+  if (mb == M && waves == Wv) return moe::launch_fp8b_t<M, Wv>(a, gateup, block, nb, grid, s);
   MOE_FP8B_CASE(1, 1) MOE_FP8B_CASE(1, 2) MOE_FP8B_CASE(1, 4) MOE_FP8B_CASE(1, 8)
   MOE_FP8B_CASE(2, 1) MOE_FP8B_CASE(2, 2) MOE_FP8B_CASE(2, 4) MOE_FP8B_CASE(2, 8)
   MOE_FP8B_CASE(4, 1) MOE_FP8B_CASE(4, 2) MOE_FP8B_CASE(4, 4) MOE_FP8B_CASE(4, 8)

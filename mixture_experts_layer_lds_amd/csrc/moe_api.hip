@@ -38,6 +38,7 @@ struct Plan {
   int ks2 = 4, nbuf2 = 4;        // (down)
   bool fp8_units = false;        // fp8 streaming on 128-value units (fp8b_gemm.hip, per-channel mode)
   bool half1 = false;            // bf16 streaming gate-up on half-width (8-column) items
+  int nb = 2;                    // block fp8 streaming: weight blocks per item (2 or 4)
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -165,6 +166,13 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     const int per = dtype == MOE_DTYPE_INT8_W8A16 ? 64 : 128;   // K values per step
     p.sw1 = pick_unit_waves(H / per, est * ((long)I / 16));
     p.sw2 = pick_unit_waves(I / per, est * ((long)H / 32));
+    if (dtype == MOE_DTYPE_FP8_BLOCK && p.mb == 4 && I % 32 == 0 && H % 64 == 0) {
+      // 64-row tiles: four weight blocks per item halve the token-row
+      // re-reads (the register tile allows at most two waves)
+      p.nb = 4;
+      p.sw1 = std::min(pick_unit_waves(H / per, est * ((long)I / 32)), 2);
+      p.sw2 = std::min(pick_unit_waves(I / per, est * ((long)H / 64)), 2);
+    }
     p.su1 = p.su2 = 1;
     return p;
   }
@@ -595,7 +603,8 @@ int forward_fp8b(const void* x, const float* topk_w, const void* routing, const 
     a.topk = k;
     a.max_tasks = p.max_tasks;
     e = moe_host::launch_stream_fp8b(a, true, true, p.mb, p.sw1,
-                                     stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
+                                     stream_grid((long)p.max_tasks * (I / 16) / (p.nb / 2), p.sw1, cus), s,
+                                     p.nb);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
@@ -621,7 +630,7 @@ int forward_fp8b(const void* x, const float* topk_w, const void* routing, const 
     a.topk = k;
     a.max_tasks = p.max_tasks;
     e = moe_host::launch_stream_fp8b(a, false, true, p.mb, p.sw2,
-                                     stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
+                                     stream_grid((long)p.max_tasks * (H / 16) / p.nb, p.sw2, cus), s, p.nb);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {

@@ -313,8 +313,9 @@ hipError_t launch_stream_w8(const StreamArgs& a, bool gateup, int mb, int waves,
 // the per-sorted-row x scales, b_scale [E][w_rows]; gate-up writes fp32
 // SiLU(gate)*up (the requantisation pass finds the row amax), down applies
 // the weight row scales only.
+// nb: weight blocks per item, 2, or 4 (block scales, 64-row tiles, waves <= 2).
 hipError_t launch_stream_fp8b(const StreamArgs& a, bool gateup, bool block, int mb, int waves, int grid,
-                              hipStream_t s);
+                              hipStream_t s, int nb = 2);
 // Group (128-value) fp8 quantisation: bf16 token rows x (scales also per
 // token [T][H/128] and per sorted row of each of the token's zk pairs,
 // unit-major [H/128][P]); fp32 rows h of the valid sorted rows (scales
