@@ -189,6 +189,14 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     if (est < active) est = active;
     choose_stream(nsteps1, p.mb, est * ((long)I / 16), &p.sw1, &p.su1);
     choose_stream(nsteps2, p.mb, est * ((long)H / 32), &p.sw2, &p.su2);
+    if (p.mb == 4 && I % 32 == 0 && H % 64 == 0 && nsteps1 % 2 == 0 && nsteps2 % 2 == 0) {
+      // 64-row tiles: four weight blocks per item halve the token-row
+      // re-reads (the register tile allows at most two waves)
+      p.nb = 4;
+      p.su1 = p.su2 = 2;
+      p.sw1 = nsteps1 % 4 == 0 ? std::min(p.sw1, 2) : 1;
+      p.sw2 = nsteps2 % 4 == 0 ? std::min(p.sw2, 2) : 1;
+    }
     return p;
   }
   // Few rows per expert (decode): register streaming, tiles of 16 rows.
@@ -508,7 +516,8 @@ int forward_mx(const void* x, const float* topk_w, const void* routing, const vo
     a.topk = k;
     a.max_tasks = p.max_tasks;
     e = moe_host::launch_stream_gemm(a, true, true, 1, p.mb, p.sw1, p.su1,
-                                     stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
+                                     stream_grid((long)p.max_tasks * (I / 16) / (p.nb / 2), p.sw1, cus), s,
+                                     p.nb);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
@@ -533,7 +542,7 @@ int forward_mx(const void* x, const float* topk_w, const void* routing, const vo
     a.topk = k;
     a.max_tasks = p.max_tasks;
     e = moe_host::launch_stream_gemm(a, false, true, 1, p.mb, p.sw2, p.su2,
-                                     stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
+                                     stream_grid((long)p.max_tasks * (H / 16) / p.nb, p.sw2, cus), s, p.nb);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
@@ -776,7 +785,8 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
     a.topk = k;
     a.max_tasks = p.max_tasks;
     e = moe_host::launch_stream_gemm(a, true, true, 2, p.mb, p.sw1, p.su1,
-                                     stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
+                                     stream_grid((long)p.max_tasks * (I / 16) / (p.nb / 2), p.sw1, cus), s,
+                                     p.nb);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
@@ -800,7 +810,7 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
     a.topk = k;
     a.max_tasks = p.max_tasks;
     e = moe_host::launch_stream_gemm(a, false, true, 2, p.mb, p.sw2, p.su2,
-                                     stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
+                                     stream_grid((long)p.max_tasks * (H / 16) / p.nb, p.sw2, cus), s, p.nb);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {

@@ -292,8 +292,10 @@ hipError_t launch_stream_half_gateup(const StreamArgs& a, int waves, int grid, h
 bool stream_config_supported(int mb, int waves, int u);
 // kind: 0 per-channel scales (bf16, or fp8 by `fp8`), 1 MXFP8 block scales,
 // 2 int8 w8a8 (per-channel scales).
+// nb: weight blocks per item, 2, or 4 (MX or int8 on 64-row tiles, two-step
+// stages, at most two waves).
 hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int kind, int mb, int waves,
-                              int u, int grid, hipStream_t s);
+                              int u, int grid, hipStream_t s, int nb = 2);
 // int8 w8a8: per-token quantisation of bf16 x (row-amax slots cleared,
 // per-sorted-row scales written as the fp8 variant) and per-row
 // requantisation of fp32 h (the row amax found from the row).

@@ -62,11 +62,13 @@ __device__ __forceinline__ void stream_mfma(f32x4& acc, const u32x4& a, const u3
 }
 
 // MB 16-row blocks per task tile, W waves per workgroup (K slices), U
-// 64-byte K steps per register stage.
-template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX, bool I8>
+// 64-byte K steps per register stage, NB weight blocks per item: 2, or 4 on
+// 64-row tiles of the 1-byte paths (gate-up: two gate and two up blocks,
+// down: 64 columns), halving the re-reads of the tile's token rows.
+template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX, bool I8, int NB = kStreamNB>
 __global__ void __launch_bounds__(W * 64)
 stream_gemm_kernel(moe_host::StreamArgs g) {
-  constexpr int NB = kStreamNB;
+  constexpr int NH = GATEUP ? NB / 2 : NB;   // 16-column output blocks per item
   static_assert(!MX || (FP8 && U == 2), "MX stages are one 128-value K unit");
   static_assert(!I8 || (FP8 && !MX), "int8 uses the 1-byte per-channel path");
   __shared__ f32x4 red[W][MB][NB][64];   // the waves' partial sums of one item
@@ -75,7 +77,7 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
-  const int n_groups = g.N_out / 16 / (GATEUP ? 1 : NB);   // column groups per task
+  const int n_groups = g.N_out / 16 / NH;   // column groups per task
   const int total = num_tasks * n_groups;
   const size_t row_bytes = (size_t)g.K * (FP8 ? 1 : 2);
   const int nsteps = (int)(row_bytes / 64);
@@ -99,8 +101,11 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
     // weight 16-row blocks of this item
     int blk[NB];
     if constexpr (GATEUP) {
-      blk[0] = cg;                      // gate rows [16 cg, 16 cg + 16)
-      blk[1] = g.N_out / 16 + cg;       // the matching up rows
+#pragma unroll
+      for (int h = 0; h < NH; h++) {
+        blk[h] = cg * NH + h;                        // gate rows [16 blk, 16 blk + 16)
+        blk[NH + h] = g.N_out / 16 + cg * NH + h;    // the matching up rows
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < NB; q++) blk[q] = cg * NB + q;
@@ -280,25 +285,27 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
         }
       }
       if constexpr (GATEUP) {
-        const int col = cg * 16 + lrow;
-        float hv[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          float gv = tot[0][i], uv = tot[1][i];
-          if constexpr (FP8 && !MX) {
-            gv = (gv * rs[i]) * cs[0];
-            uv = (uv * rs[i]) * cs[1];
+        for (int h = 0; h < NH; h++) {
+          const int col = blk[h] * 16 + lrow;
+          float hv[4];
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            float gv = tot[h][i], uv = tot[NH + h][i];
+            if constexpr (FP8 && !MX) {
+              gv = (gv * rs[i]) * cs[h];
+              uv = (uv * rs[i]) * cs[NH + h];
+            }
+            hv[i] = silu_f32(gv) * uv;
           }
-          hv[i] = silu_f32(gv) * uv;
-        }
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int rr = m * 16 + 4 * lgrp + i;
-          const bool ok = rr < task.rows;
-          if (ok) {
-            const size_t r = (size_t)(task.row_begin + rr);
-            if constexpr (FP8) static_cast<float*>(g.c)[r * g.N_out + col] = hv[i];
-            else static_cast<uint16_t*>(g.c)[r * g.N_out + col] = f32_to_bf16_bits(hv[i]);
+          for (int i = 0; i < 4; i++) {
+            const int rr = m * 16 + 4 * lgrp + i;
+            if (rr < task.rows) {
+              const size_t r = (size_t)(task.row_begin + rr);
+              if constexpr (FP8) static_cast<float*>(g.c)[r * g.N_out + col] = hv[i];
+              else static_cast<uint16_t*>(g.c)[r * g.N_out + col] = f32_to_bf16_bits(hv[i]);
+            }
           }
         }
       } else {
@@ -425,6 +432,26 @@ static hipError_t launch_stream_t(const moe_host::StreamArgs& a, int grid, hipSt
   return hipGetLastError();
 }
 
+// four weight blocks per item: 64-row tiles, MX or int8, at most two waves
+hipError_t launch_stream_nb4(const moe_host::StreamArgs& a, bool gateup, int kind, int waves, int grid,
+                             hipStream_t s) {
+#define MOE_NB4(Wv, GU, MXv, I8v) \
+  hipLaunchKernelGGL((stream_gemm_kernel<4, Wv, 2, GU, true, MXv, I8v, 4>), dim3(grid), dim3(Wv * 64), 0, s, a)
+  if (kind == 1) {
+    if (waves == 1) { if (gateup) MOE_NB4(1, true, true, false); else MOE_NB4(1, false, true, false); }
+    else if (waves == 2) { if (gateup) MOE_NB4(2, true, true, false); else MOE_NB4(2, false, true, false); }
+    else return hipErrorInvalidValue;
+  } else if (kind == 2) {
+    if (waves == 1) { if (gateup) MOE_NB4(1, true, false, true); else MOE_NB4(1, false, false, true); }
+    else if (waves == 2) { if (gateup) MOE_NB4(2, true, false, true); else MOE_NB4(2, false, false, true); }
+    else return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef MOE_NB4
+  return hipGetLastError();
+}
+
 // kind: 0 per-channel (bf16 or fp8 by `fp8`), 1 MX, 2 int8
 template <int MB, int W, int U>
 static hipError_t launch_stream_w(const moe_host::StreamArgs& a, bool gateup, bool fp8, int kind,
@@ -476,7 +503,11 @@ bool stream_config_supported(int mb, int waves, int u) {
 }
 
 hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int kind, int mb, int waves,
-                              int u, int grid, hipStream_t s) {
+                              int u, int grid, hipStream_t s, int nb) {
+  if (nb == 4) {
+    if (mb != 4 || u != 2) return hipErrorInvalidValue;
+    return moe::launch_stream_nb4(a, gateup, kind, waves, grid, s);
+  }
 #define MOE_STREAM_CASE(M, Wv, Uv) \
   if (mb == M && waves == Wv && u == Uv) return moe::launch_stream_w<M, Wv, Uv>(a, gateup, fp8, kind, grid, s);
   MOE_STREAM_CONFIGS(MOE_STREAM_CASE)
