@@ -166,6 +166,14 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     const int per = dtype == MOE_DTYPE_INT8_W8A16 ? 64 : 128;   // K values per step
     p.sw1 = pick_unit_waves(H / per, est * ((long)I / 16));
     p.sw2 = pick_unit_waves(I / per, est * ((long)H / 32));
+    if ((dtype == MOE_DTYPE_INT4_W4A16 || dtype == MOE_DTYPE_INT8_W8A16) && p.mb >= 2 && I % 32 == 0 &&
+        H % 64 == 0) {
+      // tiles of 32 or 64 rows: four weight blocks per item halve the token-row re-reads
+      p.nb = 4;
+      const int wmax = 16 / p.mb;   // the waves' partial sums within 64 KiB of LDS
+      p.sw1 = std::min(pick_unit_waves(H / per, est * ((long)I / 32)), wmax);
+      p.sw2 = std::min(pick_unit_waves(I / per, est * ((long)H / 64)), wmax);
+    }
     if (dtype == MOE_DTYPE_FP8_BLOCK && p.mb == 4 && I % 32 == 0 && H % 64 == 0) {
       // 64-row tiles: four weight blocks per item halve the token-row
       // re-reads (the register tile allows at most two waves)
@@ -695,9 +703,9 @@ int forward_w4(int dtype, const void* x, const float* topk_w, const void* routin
     a.w_rows = 2 * I;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    const int grid = stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus);
-    e = w8 ? moe_host::launch_stream_w8(a, true, p.mb, p.sw1, grid, s)
-           : moe_host::launch_stream_w4(a, true, p.mb, p.sw1, grid, s);
+    const int grid = stream_grid((long)p.max_tasks * (I / 16) / (p.nb / 2), p.sw1, cus);
+    e = w8 ? moe_host::launch_stream_w8(a, true, p.mb, p.sw1, grid, s, p.nb)
+           : moe_host::launch_stream_w4(a, true, p.mb, p.sw1, grid, s, p.nb);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
@@ -715,9 +723,9 @@ int forward_w4(int dtype, const void* x, const float* topk_w, const void* routin
     a.w_rows = H;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    const int grid = stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus);
-    e = w8 ? moe_host::launch_stream_w8(a, false, p.mb, p.sw2, grid, s)
-           : moe_host::launch_stream_w4(a, false, p.mb, p.sw2, grid, s);
+    const int grid = stream_grid((long)p.max_tasks * (H / 16) / p.nb, p.sw2, cus);
+    e = w8 ? moe_host::launch_stream_w8(a, false, p.mb, p.sw2, grid, s, p.nb)
+           : moe_host::launch_stream_w4(a, false, p.mb, p.sw2, grid, s, p.nb);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {

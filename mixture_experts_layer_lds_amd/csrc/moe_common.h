@@ -307,7 +307,8 @@ hipError_t launch_requant_rows_i8(const float* h32, int P, int I, const int32_t*
 // int8 w8a16 register-streaming GEMM: a bf16 rows, b packed int8 weights
 // with per-row fp32 scales b_scale [E][w_rows]; gate-up writes bf16
 // SiLU(gate)*up, down bf16 rows.
-hipError_t launch_stream_w8(const StreamArgs& a, bool gateup, int mb, int waves, int grid, hipStream_t s);
+hipError_t launch_stream_w8(const StreamArgs& a, bool gateup, int mb, int waves, int grid, hipStream_t s,
+                            int nb = 2);
 // Block-scaled fp8 register-streaming GEMM (K % 128 == 0): a e4m3 rows, b
 // packed e4m3 weights.  block: unit-major group scales row_scale [K/128][P]
 // (per sorted row), b_scale fp32 [E][w_rows/128][K/128]; gate-up writes fp32
@@ -330,7 +331,8 @@ hipError_t launch_requant_groups(const float* h, int P, int I, const int32_t* ex
 // int4 w4a16 register-streaming GEMM: a bf16 activations, b packed int4
 // weights, b_scale fp32 [E][w_rows][K/128] group scales; gate-up writes bf16
 // SiLU(gate)*up, down bf16 rows.
-hipError_t launch_stream_w4(const StreamArgs& a, bool gateup, int mb, int waves, int grid, hipStream_t s);
+hipError_t launch_stream_w4(const StreamArgs& a, bool gateup, int mb, int waves, int grid, hipStream_t s,
+                            int nb = 2);
 // MXFP8 quantisation: bf16 rows x[T][H] -> e4m3 xq + e8m0 codes [T][H/32];
 // fp32 rows h[P][I] (valid sorted rows only) -> hq + codes [P][I/32].
 hipError_t launch_mx_quant_bf16(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* sx, hipStream_t s);

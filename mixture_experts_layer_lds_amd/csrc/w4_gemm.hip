@@ -49,17 +49,20 @@ __device__ __forceinline__ u32x4 w4_expand(uint32_t packed) {
   return r;
 }
 
-template <int MB, int W, bool GATEUP>
+// NB weight blocks per item: 2, or 4 on tiles of 32 or more rows (gate-up:
+// two gate and two up blocks, down: 64 columns), halving the re-reads of
+// the tile's token rows.
+template <int MB, int W, bool GATEUP, int NB = kW4NB>
 __global__ void __launch_bounds__(W * 64)
 stream_w4_kernel(moe_host::StreamArgs g) {
-  constexpr int NB = kW4NB;
+  constexpr int NH = GATEUP ? NB / 2 : NB;   // 16-column output blocks per item
   __shared__ f32x4 red[W][MB][NB][64];
   const int lane = threadIdx.x & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
-  const int n_groups = g.N_out / 16 / (GATEUP ? 1 : NB);
+  const int n_groups = g.N_out / 16 / NH;
   const int total = num_tasks * n_groups;
   const size_t x_row_bytes = (size_t)g.K * 2;
   const int nsteps = g.K / 128;   // 128 K values per step
@@ -80,8 +83,11 @@ stream_w4_kernel(moe_host::StreamArgs g) {
     const moe_task_t task = load_task_scalar(g.tasks + ti);
     int blk[NB];
     if constexpr (GATEUP) {
-      blk[0] = cg;
-      blk[1] = g.N_out / 16 + cg;
+#pragma unroll
+      for (int h = 0; h < NH; h++) {
+        blk[h] = cg * NH + h;                        // gate rows
+        blk[NH + h] = g.N_out / 16 + cg * NH + h;    // the matching up rows
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < NB; q++) blk[q] = cg * NB + q;
@@ -192,9 +198,10 @@ stream_w4_kernel(moe_host::StreamArgs g) {
         if (rr >= task.rows) continue;
         const size_t r = (size_t)(task.row_begin + rr);
         if constexpr (GATEUP) {
-          const int col = cg * 16 + lrow;
-          static_cast<uint16_t*>(g.c)[r * g.N_out + col] =
-              f32_to_bf16_bits(silu_f32(tot[0][r4]) * tot[1][r4]);
+#pragma unroll
+          for (int h = 0; h < NH; h++)
+            static_cast<uint16_t*>(g.c)[r * g.N_out + blk[h] * 16 + lrow] =
+                f32_to_bf16_bits(silu_f32(tot[h][r4]) * tot[NH + h][r4]);
         } else {
 #pragma unroll
           for (int q = 0; q < NB; q++)
@@ -207,7 +214,17 @@ stream_w4_kernel(moe_host::StreamArgs g) {
 }
 
 template <int MB, int W>
-static hipError_t launch_w4_t(const moe_host::StreamArgs& a, bool gateup, int grid, hipStream_t s) {
+static hipError_t launch_w4_t(const moe_host::StreamArgs& a, bool gateup, int nb, int grid, hipStream_t s) {
+  if (nb == 4) {
+    if constexpr (MB >= 2 && MB * W <= 16) {   // partial sums within 64 KiB of LDS
+      if (gateup)
+        hipLaunchKernelGGL((stream_w4_kernel<MB, W, true, 4>), dim3(grid), dim3(W * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((stream_w4_kernel<MB, W, false, 4>), dim3(grid), dim3(W * 64), 0, s, a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (gateup)
     hipLaunchKernelGGL((stream_w4_kernel<MB, W, true>), dim3(grid), dim3(W * 64), 0, s, a);
   else
@@ -219,9 +236,10 @@ static hipError_t launch_w4_t(const moe_host::StreamArgs& a, bool gateup, int gr
 
 namespace moe_host {
 
-hipError_t launch_stream_w4(const StreamArgs& a, bool gateup, int mb, int waves, int grid, hipStream_t s) {
+hipError_t launch_stream_w4(const StreamArgs& a, bool gateup, int mb, int waves, int grid, hipStream_t s,
+                            int nb) {
 #define MOE_W4_CASE(M, Wv) \
-  if (mb == M && waves == Wv) return moe::launch_w4_t<M, Wv>(a, gateup, grid, s);
+  if (mb == M && waves == Wv) return moe::launch_w4_t<M, Wv>(a, gateup, nb, grid, s);
   MOE_W4_CASE(1, 1) MOE_W4_CASE(1, 2) MOE_W4_CASE(1, 4) MOE_W4_CASE(1, 8)
   MOE_W4_CASE(2, 1) MOE_W4_CASE(2, 2) MOE_W4_CASE(2, 4) MOE_W4_CASE(2, 8)
   MOE_W4_CASE(4, 1) MOE_W4_CASE(4, 2) MOE_W4_CASE(4, 4) MOE_W4_CASE(4, 8)

@@ -48,17 +48,20 @@ __device__ __forceinline__ void w8_expand(const u32x4& c, u32x4& first, u32x4& l
   last = u32x4{w8_pair(c[2], 0), w8_pair(c[2], 2), w8_pair(c[3], 0), w8_pair(c[3], 2)};
 }
 
-template <int MB, int W, bool GATEUP>
+// NB weight blocks per item: 2, or 4 on tiles of 32 or more rows (gate-up:
+// two gate and two up blocks, down: 64 columns), halving the re-reads of
+// the tile's token rows.
+template <int MB, int W, bool GATEUP, int NB = kW8NB>
 __global__ void __launch_bounds__(W * 64)
 stream_w8_kernel(moe_host::StreamArgs g) {
-  constexpr int NB = kW8NB;
+  constexpr int NH = GATEUP ? NB / 2 : NB;   // 16-column output blocks per item
   __shared__ f32x4 red[W][MB][NB][64];
   const int lane = threadIdx.x & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
-  const int n_groups = g.N_out / 16 / (GATEUP ? 1 : NB);
+  const int n_groups = g.N_out / 16 / NH;
   const int total = num_tasks * n_groups;
   const size_t x_row_bytes = (size_t)g.K * 2;
   const int nsteps = g.K / 64;   // 64 K values per step
@@ -78,8 +81,11 @@ stream_w8_kernel(moe_host::StreamArgs g) {
     const moe_task_t task = load_task_scalar(g.tasks + ti);
     int blk[NB];
     if constexpr (GATEUP) {
-      blk[0] = cg;
-      blk[1] = g.N_out / 16 + cg;
+#pragma unroll
+      for (int h = 0; h < NH; h++) {
+        blk[h] = cg * NH + h;                        // gate rows
+        blk[NH + h] = g.N_out / 16 + cg * NH + h;    // the matching up rows
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < NB; q++) blk[q] = cg * NB + q;
@@ -175,9 +181,10 @@ stream_w8_kernel(moe_host::StreamArgs g) {
         if (rr >= task.rows) continue;
         const size_t r = (size_t)(task.row_begin + rr);
         if constexpr (GATEUP) {
-          const int col = cg * 16 + lrow;
-          static_cast<uint16_t*>(g.c)[r * g.N_out + col] =
-              f32_to_bf16_bits(silu_f32(tot[0][r4] * cs[0]) * (tot[1][r4] * cs[1]));
+#pragma unroll
+          for (int h = 0; h < NH; h++)
+            static_cast<uint16_t*>(g.c)[r * g.N_out + blk[h] * 16 + lrow] =
+                f32_to_bf16_bits(silu_f32(tot[h][r4] * cs[h]) * (tot[NH + h][r4] * cs[NH + h]));
         } else {
 #pragma unroll
           for (int q = 0; q < NB; q++)
@@ -190,7 +197,17 @@ stream_w8_kernel(moe_host::StreamArgs g) {
 }
 
 template <int MB, int W>
-static hipError_t launch_w8_t(const moe_host::StreamArgs& a, bool gateup, int grid, hipStream_t s) {
+static hipError_t launch_w8_t(const moe_host::StreamArgs& a, bool gateup, int nb, int grid, hipStream_t s) {
+  if (nb == 4) {
+    if constexpr (MB >= 2 && MB * W <= 16) {   // partial sums within 64 KiB of LDS
+      if (gateup)
+        hipLaunchKernelGGL((stream_w8_kernel<MB, W, true, 4>), dim3(grid), dim3(W * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((stream_w8_kernel<MB, W, false, 4>), dim3(grid), dim3(W * 64), 0, s, a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (gateup)
     hipLaunchKernelGGL((stream_w8_kernel<MB, W, true>), dim3(grid), dim3(W * 64), 0, s, a);
   else
@@ -202,9 +219,10 @@ static hipError_t launch_w8_t(const moe_host::StreamArgs& a, bool gateup, int gr
 
 namespace moe_host {
 
-hipError_t launch_stream_w8(const StreamArgs& a, bool gateup, int mb, int waves, int grid, hipStream_t s) {
+hipError_t launch_stream_w8(const StreamArgs& a, bool gateup, int mb, int waves, int grid, hipStream_t s,
+                            int nb) {
 #define MOE_W8_CASE(M, Wv) \
-  if (mb == M && waves == Wv) return moe::launch_w8_t<M, Wv>(a, gateup, grid, s);
+  if (mb == M && waves == Wv) return moe::launch_w8_t<M, Wv>(a, gateup, nb, grid, s);
   MOE_W8_CASE(1, 1) MOE_W8_CASE(1, 2) MOE_W8_CASE(1, 4) MOE_W8_CASE(1, 8)
   MOE_W8_CASE(2, 1) MOE_W8_CASE(2, 2) MOE_W8_CASE(2, 4) MOE_W8_CASE(2, 8)
   MOE_W8_CASE(4, 1) MOE_W8_CASE(4, 2) MOE_W8_CASE(4, 4) MOE_W8_CASE(4, 8)
