@@ -220,6 +220,25 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   // streaming, 508 us strips).
   const long strip_max = dtype == MOE_DTYPE_FP8_W8A8 ? 160 : 80;
   const long strip_min = dtype == MOE_DTYPE_FP8_W8A8 ? 3 : 9;
+  if (dtype == MOE_DTYPE_BF16 && avg >= 9 && avg <= 16 && H >= 3072 && I % 32 == 0 && H % 64 == 0) {
+    // 32-row tiles on register streaming with four weight blocks per item,
+    // for long reductions (same-box A/B against the strips: Mixtral-8x7B T=64
+    // 463 -> 453 us, Qwen2-57B T=128 194 -> 180 us; with H = 2048, Qwen3-30B-A3B
+    // T=256, the strips stay ahead, 159 against 194 us)
+    p.tiling = kStreaming;
+    p.block_m = 32;
+    p.mb = 2;
+    p.nb = 4;
+    p.max_tasks = (int)(P / p.block_m + (P < E ? P : E));
+    long est = (P + p.block_m - 1) / p.block_m;
+    if (est < active) est = active;
+    choose_stream(nsteps1, p.mb, est * ((long)I / 32), &p.sw1, &p.su1);
+    choose_stream(nsteps2, p.mb, est * ((long)H / 64), &p.sw2, &p.su2);
+    p.sw1 = std::min(p.sw1, 4);
+    p.sw2 = std::min(p.sw2, 4);
+    if (p.su1 == 2 && p.su2 == 2) return p;
+    p = Plan();
+  }
   if (avg >= strip_min && avg <= strip_max && (2 * I) % kStripCols == 0 && H % kStripCols == 0) {
     // Tile height about twice the mean rows per expert; when no strip
     // configuration divides the reductions at that height, a taller one
@@ -1026,7 +1045,8 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
                                        stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
     else
       e = moe_host::launch_stream_gemm(a, true, fp8, 0, p.mb, p.sw1, p.su1,
-                                       stream_grid((long)p.max_tasks * (I / 16), p.sw1, cus), s);
+                                       stream_grid((long)p.max_tasks * (I / 16) / (p.nb / 2), p.sw1, cus), s,
+                                       p.nb);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (fp8) {
@@ -1054,7 +1074,8 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     e = p.fp8_units ? moe_host::launch_stream_fp8b(a, false, false, p.mb, p.sw2,
                                                    stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s)
                     : moe_host::launch_stream_gemm(a, false, fp8, 0, p.mb, p.sw2, p.su2,
-                                                   stream_grid((long)p.max_tasks * (H / 32), p.sw2, cus), s);
+                                                   stream_grid((long)p.max_tasks * (H / 16) / p.nb, p.sw2, cus),
+                                                   s, p.nb);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {

@@ -445,6 +445,14 @@ hipError_t launch_stream_nb4(const moe_host::StreamArgs& a, bool gateup, int kin
     if (waves == 1) { if (gateup) MOE_NB4(1, true, false, true); else MOE_NB4(1, false, false, true); }
     else if (waves == 2) { if (gateup) MOE_NB4(2, true, false, true); else MOE_NB4(2, false, false, true); }
     else return hipErrorInvalidValue;
+  } else if (kind == 3) {   // bf16, 32-row tiles
+#define MOE_NB4B(Wv, GU) \
+  hipLaunchKernelGGL((stream_gemm_kernel<2, Wv, 2, GU, false, false, false, 4>), dim3(grid), dim3(Wv * 64), 0, s, a)
+    if (waves == 1) { if (gateup) MOE_NB4B(1, true); else MOE_NB4B(1, false); }
+    else if (waves == 2) { if (gateup) MOE_NB4B(2, true); else MOE_NB4B(2, false); }
+    else if (waves == 4) { if (gateup) MOE_NB4B(4, true); else MOE_NB4B(4, false); }
+    else return hipErrorInvalidValue;
+#undef MOE_NB4B
   } else {
     return hipErrorInvalidValue;
   }
@@ -505,7 +513,10 @@ bool stream_config_supported(int mb, int waves, int u) {
 hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int kind, int mb, int waves,
                               int u, int grid, hipStream_t s, int nb) {
   if (nb == 4) {
-    if (mb != 4 || u != 2) return hipErrorInvalidValue;
+    if (u != 2) return hipErrorInvalidValue;
+    if (kind == 0 && !fp8) return mb == 2 ? moe::launch_stream_nb4(a, gateup, 3, waves, grid, s)
+                                          : hipErrorInvalidValue;
+    if (mb != 4) return hipErrorInvalidValue;
     return moe::launch_stream_nb4(a, gateup, kind, waves, grid, s);
   }
 #define MOE_STREAM_CASE(M, Wv, Uv) \
