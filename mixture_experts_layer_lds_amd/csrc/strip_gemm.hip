@@ -363,7 +363,7 @@ namespace moe_host {
   X(2, 4, 4) X(2, 4, 3) X(2, 4, 2)                       \
   X(4, 2, 4) X(4, 4, 3) X(4, 4, 4) X(4, 2, 3) X(4, 4, 2) X(4, 2, 2) \
   X(8, 2, 4) X(8, 2, 3) X(8, 1, 4) X(8, 2, 2)             \
-  X(12, 2, 3) X(12, 2, 2)
+  X(12, 2, 4) X(12, 2, 3) X(12, 2, 2)
 
 bool strip_config_supported(int mb, int ks, int nbuf, bool fp8) {
   // 192-row tiles serve fp8 only (the bf16 ones would spill registers)
