@@ -2,24 +2,29 @@
 """Benchmark of the fused MoE layer on one MI355X.
 
 One step = one pass of the whole hot path over one batch: the routing/index
-build and the forward pass (gate-up GEMM, SiLU-and-mul [+ fp8 requant],
-down GEMM, top-k weighted reduction), launched through the C ABI on
-torch's current stream with every input already resident in HBM.
+build and the forward pass ([fp8: per-token quantisation of x], gate-up GEMM,
+SiLU-and-mul [+ fp8 requant], down GEMM, top-k weighted reduction), launched
+through the C ABI on torch's current stream with every input already resident
+in HBM.
 
-Default workload: a Mixtral-8x7B-shaped layer (bf16, E=8, H=4096, I=14336,
-top-2, uniform softmax routing) at T=16 tokens, with seeded synthetic
-weights and tokens.  `value` is the layer's essential HBM bytes (weights of
-the experts that receive tokens + x + out + ids + weights) divided by the
-measured time per layer, in GB/s.
+Default workload: the largest single-GPU configuration, a DeepSeek-V3-shaped
+layer in fp8 w8a8 (E=256, H=7168, I=2048, top-8, e4m3 weights with
+per-output-channel fp32 scales, per-token e4m3 activations, bf16 output,
+uniform softmax routing) at T=4096 tokens, with seeded synthetic weights and
+tokens.  `value` is the layer's essential HBM bytes (weights and scales of the
+experts that receive tokens + x + out + ids + weights) divided by the measured
+time per layer, in GB/s.
 
 W1/W2 are packed once into the kernels' MFMA-fragment order before timing
 (moe_pack_weights, a load-time byte permutation); the CPU oracle reads the
 row-major originals.
 
-Printed: one JSON line (rank 0, N=1 only) with the timed-region figures,
-the dominant kernel's roofline (HIP events recorded around each stage on the
-launch stream inside the timed region), per-stage times, a T sweep timed by
-HIP-graph replay, and the CPU oracle timed on the host as a baseline.
+Printed: one JSON line (rank 0, N=1 only) with the timed-region figures, the
+dominant kernel's roofline (HIP events recorded around it on the launch stream
+inside the timed region), per-stage times, the workload's T sweep timed by
+HIP-graph replay (median, p10, p90), the event and graph-launch overheads, the
+attainable streaming-read rate of the device, and the CPU oracle timed on the
+host as a baseline.
 """
 from __future__ import annotations
 
@@ -229,27 +234,129 @@ def graph_time_us(layer, weight_sets, reps=20, warmup=3, calls=10):
         b.record()
         b.synchronize()
         times.append(a.elapsed_time(b) * 1000.0 / calls)
-    return statistics.median(times), min(times)
+    dec = statistics.quantiles(times, n=10)
+    return {"median": statistics.median(times), "best": min(times), "p10": dec[0], "p90": dec[-1]}
+
+
+def overheads_us(reps=50):
+    """What the timing method itself costs: two HIP events recorded back to
+    back on one stream (nothing between them), and the replay of a graph
+    holding ten one-element kernels, per kernel (the floor of a chain of ten
+    dependent launches in one graph, as the sweep replays them)."""
+    import torch
+    pair = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.record()
+        b.synchronize()
+        pair.append(a.elapsed_time(b) * 1000.0)
+    t = torch.zeros(1, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        t.add_(1.0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(10):
+            t.add_(1.0)
+    g.replay()
+    torch.cuda.synchronize()
+    tiny = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        tiny.append(a.elapsed_time(b) * 1000.0 / 10)
+    return {"event_pair_us": round(statistics.median(pair), 2),
+            "tiny_kernel_in_graph_us": round(statistics.median(tiny), 2)}
+
+
+def stream_read_ceiling(moe, gib=4, reps=10):
+    """Attainable HBM read rate: the library's plain streaming-read kernel over
+    a buffer far larger than the last-level cache (median of `reps` reads,
+    HIP events around each)."""
+    import torch
+    buf = torch.ones(gib << 30, dtype=torch.uint8, device="cuda")
+    nbytes = buf.numel()
+    cus = moe.moe_device_cu_count()
+    best = None
+    for per_cu in (2, 4, 8):          # workgroups per compute unit (4 waves each)
+        sink = torch.empty(cus * per_cu, dtype=torch.int32, device="cuda")
+        moe.moe_stream_read(buf, sink)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            moe.moe_stream_read(buf, sink)
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+        gbs = nbytes / statistics.median(times) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, per_cu)
+    del buf
+    torch.cuda.empty_cache()
+    return {"kernel": "moe_stream_read (non-temporal 16-byte loads, 32 KiB chunks per workgroup)",
+            "bytes": nbytes, "workgroups_per_cu": best[1], "GBs": round(best[0], 1),
+            "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# Whole-layer oracle cost (multiply-adds, 3*H*I per pair) above which the CPU
+# baseline runs on a seeded token subset and is scaled to the full batch.
+CPU_FULL_MACS = 6e10
+CPU_SUBSET = 256
 
 
 def cpu_baseline(wl, layer, W_host, dtype, reps=3):
+    """The oracle as it stands (fp64 C, OpenMP over tokens) on the host's
+    cores: the whole layer when that is a few seconds of work, else a seeded
+    subset of CPU_SUBSET tokens (always the first and the last) whose time is
+    scaled by T / CPU_SUBSET (the oracle's cost is linear in the tokens)."""
+    import numpy as np
     import oracle
     x = layer.x.cpu()
     ids = layer.ids.cpu()
     w = layer.w.cpu()
+    T = x.shape[0]
+    rows = None
+    if T * wl.k * 3.0 * wl.H * wl.I > CPU_FULL_MACS and T > CPU_SUBSET:
+        g = np.random.default_rng(T)
+        mid = sorted(g.choice(np.arange(1, T - 1), size=CPU_SUBSET - 2, replace=False).tolist())
+        rows = [0] + mid + [T - 1]
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
         if dtype == "bf16":
-            oracle.forward_bf16(x, w, ids, W_host["w1"], W_host["w2"])
+            oracle.forward_bf16(x, w, ids, W_host["w1"], W_host["w2"], rows=rows)
         else:
             fwd = {"fp8": oracle.forward_fp8, "mxfp8": oracle.forward_mxfp8,
                    "int8": oracle.forward_int8, "int4": oracle.forward_w4a16,
                    "int8w": oracle.forward_w8a16,
                    "fp8b": oracle.forward_fp8_block}[dtype]
-            fwd(x, w, ids, W_host["w1"], W_host["w1_scale"], W_host["w2"], W_host["w2_scale"])
+            fwd(x, w, ids, W_host["w1"], W_host["w1_scale"], W_host["w2"], W_host["w2_scale"], rows=rows)
         times.append(time.perf_counter() - t0)
-    return statistics.median(times), oracle.num_threads()
+    sec = statistics.median(times)
+    scale = 1.0 if rows is None else T / len(rows)
+    return sec * scale, sec, (None if rows is None else len(rows)), oracle.num_threads()
 
 
 def main():
@@ -257,10 +364,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mixtral",
+    ap.add_argument("--workload", default="dsv3",
                     choices=["tiny", "mixtral", "qwen3", "qwen2", "dsv3", "dsv3b", "dsv3mx", "dsv3i8", "mixtral8",
                              "mixtral4"])
-    ap.add_argument("--tokens", type=int, default=16)
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="tokens of the timed step (default: the workload's largest T)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the graph-replay T sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--once", action="store_true",
@@ -268,6 +376,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (3 times); under rocprofv3 "
                          "--pmc it gives the FETCH_SIZE/WRITE_SIZE a copy of known size reads")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="measure only the attainable HBM read rate (the library's streaming-read "
+                         "kernel over 4 GiB) and print it")
     ap.add_argument("--router", action="store_true",
                     help="measure the router top-k kernel (the step before the routing build) over "
                          "the workload's token grid instead of the layer")
@@ -298,6 +409,10 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copy calibration: 3 x 1 GiB device copies done")
         return
+    if args.ceiling:
+        print(json.dumps({"metric": "attainable HBM read rate, 1 GPU", **stream_read_ceiling(moe)}),
+              flush=True)
+        return
     wl = WORKLOADS[args.workload]
     if args.router_gemm:
         router_gemm_bench(moe, wl if "--workload" in sys.argv else None, args)
@@ -306,7 +421,7 @@ def main():
         router_bench(moe, wl, args)
         return
     dtype = wl.dtype if wl.dtype in ("fp8", "fp8b", "mxfp8", "int8", "int4", "int8w") else "bf16"
-    T = args.tokens
+    T = args.tokens if args.tokens is not None else max(wl.Ts)
     log(f"[bench] workload={wl.name} T={T} dtype={dtype}: generating weights")
     W_rows = make_weights(wl, device="cuda")
     if wl.dtype == "f32":
@@ -356,7 +471,9 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = counted_traffic(dom, wl.name, T)
     roof["algorithmic_bytes"] = dom_bytes
+    roof["algorithmic_flops"] = dom_flops
     roof["avg_launch_us"] = dom_us
+    roof["mfma_frac"] = round(dom_flops / (dom_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS[dtype], 4)
 
     sweep = []
     if not args.no_sweep:
@@ -368,8 +485,11 @@ def main():
                 per_copy = sum(v.numel() * v.element_size() for v in W.values())
                 copies = max(1, min(8, math.ceil(1e9 / nb), int(40e9 // per_copy)))
             sets = [W] + [{k: v.clone() for k, v in W.items()} for _ in range(copies - 1)]
-            med, best = graph_time_us(lay, sets)
-            sweep.append({"T": Ts, "us_per_layer": round(med, 2), "best_us": round(best, 2),
+            q = graph_time_us(lay, sets)
+            med = q["median"]
+            sweep.append({"T": Ts, "us_per_layer": round(med, 2), "p10_us": round(q["p10"], 2),
+                          "p90_us": round(q["p90"], 2), "best_us": round(q["best"], 2),
+                          "tokens_per_s": round(Ts / (med * 1e-6), 1),
                           "active_experts": act_e, "essential_MB": round(nb / 1e6, 2),
                           "GBs": round(nb / (med * 1e-6) / 1e9, 1),
                           "hbm_frac": round(nb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -378,15 +498,25 @@ def main():
             del sets, lay
             torch.cuda.empty_cache()
             log(f"[bench] sweep T={Ts}: {sweep[-1]['us_per_layer']} us, {sweep[-1]['GBs']} GB/s")
+    over = overheads_us()
+    ceiling = stream_read_ceiling(moe)
+    log(f"[bench] streaming-read ceiling {ceiling['GBs']} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on the host)")
-        sec, cores = cpu_baseline(wl, layer, W_host, dtype)
+        sec, sec_run, subset, cores = cpu_baseline(wl, layer, W_host, dtype)
+        if subset is None:
+            sample = (f"the full {wl.name} layer at T={T} ({T * wl.k} pairs), fp64 C oracle, "
+                      f"OpenMP over tokens, median of 3 runs")
+        else:
+            sample = (f"a seeded subset of {subset} of the {T} tokens (first and last included) of the "
+                      f"{wl.name} layer, fp64 C oracle, OpenMP over tokens, median of 3 runs of "
+                      f"{sec_run:.2f} s, scaled by {T}/{subset} to the whole batch (extrapolated)")
         cpu = {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": cores,
                "kind": "oracle", "us_per_layer": round(sec * 1e6, 1),
-               "sample": f"the full {wl.name} layer at T={T} ({T * wl.k} pairs), fp64 C oracle, "
-                         f"OpenMP over tokens, median of 3 runs"}
+               "tokens_per_s": round(T / sec, 2), "extrapolated": subset is not None,
+               "nproc": os.cpu_count(), "cpu_model": cpu_model(), "sample": sample}
 
     rec = {
         "metric": METRIC,
@@ -406,14 +536,20 @@ def main():
         "us_per_layer": round(ms_per_step * 1000.0, 2),
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[dtype], 4),
         "essential_bytes": nbytes,
+        "algorithmic_flops": flops,
         "active_experts": active,
         "stages": stages,
         "stages_note": "per-stage HIP events from a separate untimed pass (events around every "
                        "stage); the timed region records events around the dominant GEMM only",
         "roofline": roof,
+        "ceiling": ceiling,
+        "overheads": over,
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "sweep_note": "HIP-graph replay of ten back-to-back layer calls (routing build + forward), "
+                      "20 replays; per-layer median, p10, p90 and best",
     }
     print(json.dumps(rec), flush=True)
 
@@ -583,12 +719,22 @@ def router_gemm_bench(moe, wl, args):
                       "sweep": sweep, "cpu_baseline": cpu}), flush=True)
 
 
+def sources_hash(paths):
+    """First 16 hex digits of the sha256 of the listed files, concatenated in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def counted_traffic(stage, workload, T):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     FETCH_SIZE/WRITE_SIZE summary (copy-calibrated), or None when no summary
-    covers this kernel and workload or the kernel source changed since."""
+    covers this kernel and workload, or when any source that decides the
+    kernel (its file, the launch plan, the shared headers) changed since."""
     import glob
-    import hashlib
     import re
     for path in glob.glob(os.path.join(ROOT, "profiles", "traffic_*.md")):
         m = re.search(r"```json\s*(\{.*?\})\s*```", open(path).read(), re.S)
@@ -598,10 +744,10 @@ def counted_traffic(stage, workload, T):
         if rec.get("kernel") != f"grouped_gemm ({stage})" or rec.get("workload") != workload \
                 or rec.get("T") != T:
             continue
-        src = os.path.join(ROOT, rec["source"])
-        if not os.path.exists(src):
+        srcs = rec.get("sources")
+        if not srcs or not all(os.path.exists(os.path.join(ROOT, p)) for p in srcs):
             continue
-        if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != rec["source_sha256_16"]:
+        if sources_hash(srcs) != rec.get("sources_sha256_16"):
             return None
         return rec["traffic_bytes"]
     return None

@@ -40,7 +40,8 @@
  *      W2       [E][H][I]
  *      out      [T][H]      bf16
  *    The forward calls take W1 and W2 pre-packed by moe_pack_weights (same
- *    byte size, MFMA-fragment order); everything else is row-major.
+ *    byte size, MFMA-fragment order), through the moe_packed_weights_t
+ *    descriptor that moe_pack_weights fills; everything else is row-major.
  *    bf16 is IEEE binary16-brain (1/8/7); fp8 is OCP E4M3 ("e4m3fn",
  *    max finite 448).
  *  - Stage order: [fp8: quantise x] -> gate-up GEMM -> SiLU-and-mul
@@ -160,6 +161,25 @@ typedef struct {
     int32_t tiling;     /* 0 register streaming, 1 LDS tiles, 2 strips */
 } moe_workspace_layout_t;
 
+/* A weight tensor packed by moe_pack_weights, as the forward calls take W1
+ * and W2 (a host struct; the bytes it names are device memory).
+ * moe_pack_weights fills every field, and `check` binds the others
+ * together: a forward call accepts a descriptor only if it was made by
+ * moe_pack_weights for that call's dtype, expert count and matrix shape
+ * (W1: rows = 2I, cols = H; W2: rows = H, cols = I), and returns
+ * MOE_ERR_INVALID_ARG for anything else, including row-major weights or a
+ * hand-made descriptor.  The check runs on the host and reads no device
+ * memory.  The descriptor owns nothing; it is valid while the packed buffer
+ * lives and is unchanged. */
+typedef struct {
+    const void *data;   /* device: the packed bytes */
+    int32_t dtype;      /* moe_dtype_t the bytes were packed for */
+    int32_t experts;    /* E */
+    int32_t rows;       /* rows per expert */
+    int32_t cols;       /* elements per row (the reduction length) */
+    uint64_t check;     /* written by moe_pack_weights */
+} moe_packed_weights_t;
+
 /* Human-readable name of a status code (static string). */
 const char *moe_status_string(int status);
 
@@ -184,9 +204,19 @@ int moe_workspace_layout(int T, int k, int E, int H, int I, int dtype,
  * chunks are ordered (expert, 16-row block, 64-byte step).  Pack W1 with
  * rows = 2I, cols = H and W2 with rows = H, cols = I.  Requires rows % 16
  * == 0 and cols * element size % 64 == 0; both pointers 16-byte aligned.
- * Scales are not packed. */
+ * Scales are not packed.  On MOE_OK, desc (host, not NULL) describes
+ * `packed` for the forward calls; on an error it is left unchanged. */
 int moe_pack_weights(const void *w, int E, int rows, int cols, int dtype, void *packed,
-                     void *stream);
+                     moe_packed_weights_t *desc /* host, out */, void *stream);
+
+/* Descriptor (host, no device access) for bytes that are already in the
+ * packed order of moe_pack_weights: a device copy of a packed buffer, or
+ * packed weights stored once and loaded again.  Same size and pointer rules
+ * as moe_pack_weights.  The library cannot tell packed bytes from row-major
+ * ones; this explicit call is the caller's statement that `packed` holds
+ * the output of moe_pack_weights for these sizes and dtype. */
+int moe_describe_packed_weights(const void *packed, int E, int rows, int cols, int dtype,
+                                moe_packed_weights_t *desc /* host, out */);
 
 /* Routing & index build (blog section "MoE", routing & index build): one
  * workgroup counting-sorts the P = T*k pairs by expert id in LDS, writing
@@ -266,20 +296,21 @@ int moe_router_gemm_topk(const void *x, const void *w_pair, int T, int E, int K,
 /* bf16 forward (blog section "MoE", gate-up & activation, PDL chaining;
  * operator table: BF16 hidden states).  x (device) bf16 [T][H]; topk_w
  * (device) fp32 [T][k]; routing (device) built by moe_build_routing_bf16
- * with the same sizes; w1 (device) bf16 [E][2I][H] and w2 (device) bf16
- * [E][H][I], both packed by moe_pack_weights; workspace (device, 256-byte aligned, at least
+ * with the same sizes; w1 and w2 (host) descriptors, from moe_pack_weights
+ * with dtype MOE_DTYPE_BF16, of bf16 W1 [E][2I][H] and W2 [E][H][I]
+ * (any other descriptor: MOE_ERR_INVALID_ARG); workspace (device, 256-byte aligned, at least
  * moe_workspace_layout().total_bytes); out (device) bf16 [T][H].
  * Experts that receive no pair are never read.  Accumulation is fp32; the
  * intermediate SiLU(gate)*up and the per-pair down rows are stored as bf16;
  * the top-k reduction adds the pairs of a token in ascending j in fp32. */
 int moe_forward_bf16(const void *x, const float *topk_w, const void *routing,
-                     const void *w1, const void *w2,
+                     const moe_packed_weights_t *w1, const moe_packed_weights_t *w2,
                      int T, int k, int E, int H, int I,
                      void *workspace, size_t workspace_bytes, void *out, void *stream);
 
 /* fp8 w8a8 forward (operator table: FP8 E4M3 expert weights; gate-up &
  * activation: FP8 requant before the down GEMM).  As moe_forward_bf16,
- * except: w1/w2 (device) are e4m3 codes (packed by moe_pack_weights with
+ * except: w1/w2 (host) describe e4m3 codes (packed by moe_pack_weights with
  * dtype MOE_DTYPE_FP8_W8A8), w1_scale (device) fp32 [E][2I] and
  * w2_scale (device) fp32 [E][H] are per-output-channel scales.  x is
  * quantised per token and SiLU(gate)*up per (token, expert) row with the
@@ -287,8 +318,8 @@ int moe_forward_bf16(const void *x, const float *topk_w, const void *routing,
  * fp32(448/amax))) (an all-zero row gets scale 1); the e4m3 codes and
  * scales are left in the workspace (see moe_workspace_layout_t). */
 int moe_forward_fp8(const void *x, const float *topk_w, const void *routing,
-                    const uint8_t *w1, const float *w1_scale,
-                    const uint8_t *w2, const float *w2_scale,
+                    const moe_packed_weights_t *w1, const float *w1_scale,
+                    const moe_packed_weights_t *w2, const float *w2_scale,
                     int T, int k, int E, int H, int I,
                     void *workspace, size_t workspace_bytes, void *out, void *stream);
 
@@ -297,8 +328,9 @@ int moe_forward_fp8(const void *x, const float *topk_w, const void *routing,
  * tile height of the MXFP8 forward.  Forward: as moe_forward_fp8 except the
  * scales: w1_scale (device) uint8 e8m0 codes [E][2I][H/32] and w2_scale
  * (device) uint8 [E][H][I/32], code c meaning 2^(c - 127), one per 32
- * consecutive values of a weight row (4-byte aligned); w1/w2 are e4m3 codes
- * packed by moe_pack_weights with dtype MOE_DTYPE_MXFP8 (the fp8 layout).
+ * consecutive values of a weight row (4-byte aligned); w1/w2 (host)
+ * describe e4m3 codes packed by moe_pack_weights with dtype MOE_DTYPE_MXFP8
+ * (the fp8 layout).
  * x is quantised per token and SiLU(gate)*up per (token, expert) row in
  * blocks of 32 by the OCP rule: scale 2^s, s = floor(log2(max|v|)) - 8
  * clamped to [-127, 127] (-127 for an all-zero block), codes =
@@ -308,14 +340,14 @@ int moe_forward_fp8(const void *x, const float *topk_w, const void *routing,
 int moe_build_routing_mxfp8(const int32_t *topk_ids, int T, int k, int E, int H, int I,
                             void *routing, size_t routing_bytes, void *stream);
 int moe_forward_mxfp8(const void *x, const float *topk_w, const void *routing,
-                      const uint8_t *w1, const uint8_t *w1_scale,
-                      const uint8_t *w2, const uint8_t *w2_scale,
+                      const moe_packed_weights_t *w1, const uint8_t *w1_scale,
+                      const moe_packed_weights_t *w2, const uint8_t *w2_scale,
                       int T, int k, int E, int H, int I,
                       void *workspace, size_t workspace_bytes, void *out, void *stream);
 
 /* int8 w8a8 with per-channel weight scales (SGLang tuning guide: the
  * int8_w8a8 dtype with per-channel quantisation).  As the fp8 pair, with
- * int8 codes: w1/w2 (device) int8 [E][2I][H] / [E][H][I] packed by
+ * int8 codes: w1/w2 (host) describe int8 [E][2I][H] / [E][H][I] packed by
  * moe_pack_weights with dtype MOE_DTYPE_INT8_W8A8, w1_scale / w2_scale
  * fp32 per output row.  x is quantised per token and SiLU(gate)*up per
  * (token, expert) row by scale = fp32(amax/127), code =
@@ -325,8 +357,8 @@ int moe_forward_mxfp8(const void *x, const float *topk_w, const void *routing,
 int moe_build_routing_int8(const int32_t *topk_ids, int T, int k, int E, int H, int I,
                            void *routing, size_t routing_bytes, void *stream);
 int moe_forward_int8(const void *x, const float *topk_w, const void *routing,
-                     const int8_t *w1, const float *w1_scale,
-                     const int8_t *w2, const float *w2_scale,
+                     const moe_packed_weights_t *w1, const float *w1_scale,
+                     const moe_packed_weights_t *w2, const float *w2_scale,
                      int T, int k, int E, int H, int I,
                      void *workspace, size_t workspace_bytes, void *out, void *stream);
 
@@ -336,18 +368,18 @@ int moe_forward_int8(const void *x, const float *topk_w, const void *routing,
  * fp32 [E][H/128][I/128], one per 128 x 128 block of the weight matrix;
  * x is quantised per token and SiLU(gate)*up per (token, expert) row in
  * groups of 128 values, each group by the per-row rule of moe_forward_fp8.
- * w1/w2 packed by moe_pack_weights with dtype MOE_DTYPE_FP8_BLOCK (the
+ * w1/w2 (host) describe codes packed by moe_pack_weights with dtype MOE_DTYPE_FP8_BLOCK (the
  * fp8 layout).  H and I must be multiples of 128. */
 int moe_build_routing_fp8_block(const int32_t *topk_ids, int T, int k, int E, int H, int I,
                                 void *routing, size_t routing_bytes, void *stream);
 int moe_forward_fp8_block(const void *x, const float *topk_w, const void *routing,
-                          const uint8_t *w1, const float *w1_scale,
-                          const uint8_t *w2, const float *w2_scale,
+                          const moe_packed_weights_t *w1, const float *w1_scale,
+                          const moe_packed_weights_t *w2, const float *w2_scale,
                           int T, int k, int E, int H, int I,
                           void *workspace, size_t workspace_bytes, void *out, void *stream);
 
-/* int4 w4a16 (SGLang tuning guide dtype list: int4_w4a16).  w1 (device)
- * uint8 [E][2I][H/2] and w2 (device) uint8 [E][H][I/2]: two's-complement
+/* int4 w4a16 (SGLang tuning guide dtype list: int4_w4a16).  w1 / w2 (host)
+ * describe uint8 [E][2I][H/2] / [E][H][I/2] (device): two's-complement
  * int4 codes, two a byte, the lower K index in the low nibble, packed by
  * moe_pack_weights with dtype MOE_DTYPE_INT4_W4A16 (cols = the K length);
  * w1_scale (device) fp32 [E][2I][H/128], w2_scale (device) fp32
@@ -358,13 +390,13 @@ int moe_forward_fp8_block(const void *x, const float *topk_w, const void *routin
 int moe_build_routing_int4(const int32_t *topk_ids, int T, int k, int E, int H, int I,
                            void *routing, size_t routing_bytes, void *stream);
 int moe_forward_int4(const void *x, const float *topk_w, const void *routing,
-                     const uint8_t *w1, const float *w1_scale,
-                     const uint8_t *w2, const float *w2_scale,
+                     const moe_packed_weights_t *w1, const float *w1_scale,
+                     const moe_packed_weights_t *w2, const float *w2_scale,
                      int T, int k, int E, int H, int I,
                      void *workspace, size_t workspace_bytes, void *out, void *stream);
 
 /* int8 w8a16 (SGLang tuning guide dtype list: int8_w8a16, weight-only
- * int8).  w1 (device) int8 [E][2I][H] and w2 (device) int8 [E][H][I],
+ * int8).  w1 / w2 (host) describe int8 [E][2I][H] / [E][H][I] (device),
  * packed by moe_pack_weights with dtype MOE_DTYPE_INT8_W8A16; w1_scale
  * (device) fp32 [E][2I], w2_scale (device) fp32 [E][H]: weight (n, k) =
  * code * scale[n].  x and the intermediate stay bf16 (bf16 MFMA on weights
@@ -373,8 +405,8 @@ int moe_forward_int4(const void *x, const float *topk_w, const void *routing,
 int moe_build_routing_int8_w8a16(const int32_t *topk_ids, int T, int k, int E, int H, int I,
                                  void *routing, size_t routing_bytes, void *stream);
 int moe_forward_int8_w8a16(const void *x, const float *topk_w, const void *routing,
-                           const int8_t *w1, const float *w1_scale,
-                           const int8_t *w2, const float *w2_scale,
+                           const moe_packed_weights_t *w1, const float *w1_scale,
+                           const moe_packed_weights_t *w2, const float *w2_scale,
                            int T, int k, int E, int H, int I,
                            void *workspace, size_t workspace_bytes, void *out, void *stream);
 
@@ -389,6 +421,16 @@ int moe_forward_int8_w8a16(const void *x, const float *topk_w, const void *routi
  * off.  The setting is process-wide and not thread-safe; do not enable it
  * while a forward call is being captured into a graph. */
 int moe_set_stage_events(void *const *events, int n);
+
+/* Measurement aid (the attainable HBM read rate that the weight stream of the
+ * layer is set against): reads `bytes` of buf (device, 16-byte aligned,
+ * bytes a multiple of 16) once, with non-temporal 16-byte loads in whole
+ * 1 KiB runs per wave and 32 KiB contiguous chunks per workgroup, spread
+ * over every compute unit, and writes one word per workgroup to sink
+ * (device, 4-byte aligned, sink_words >= 1 words; min(sink_words, 8 x
+ * compute units) workgroups run).  The words are a fold of the data read
+ * and carry no other meaning.  bytes == 0 returns MOE_OK with no launch. */
+int moe_stream_read(const void *buf, size_t bytes, uint32_t *sink, size_t sink_words, void *stream);
 
 /* Number of compute units of the current device as cached by the library
  * (queried once per device), or a negative status. */

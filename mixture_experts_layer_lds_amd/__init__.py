@@ -7,7 +7,7 @@ or cannot be loaded, importing this module raises.
 
 Functions carry the C names:
 
-    moe_pack_weights(w, dtype)                          -> packed copy (one-time)
+    moe_pack_weights(w, dtype)                          -> PackedWeight (packed copy + descriptor, one-time)
     moe_routing_layout(T, k, E, H, I, dtype)            -> dict (host only)
     moe_workspace_layout(T, k, E, H, I, dtype)          -> dict (host only)
     moe_router_split_weights(w)                         -> split fp32 router weight pair (one-time)
@@ -73,25 +73,58 @@ class WorkspaceLayout(ctypes.Structure):
                 ("split_k2", ctypes.c_int32), ("tiling", ctypes.c_int32)]
 
 
-EXPORTS = ("moe_status_string", "moe_pack_weights", "moe_routing_layout", "moe_workspace_layout",
+class PackedWeightsDesc(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("experts", ctypes.c_int32),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("check", ctypes.c_uint64)]
+
+
+class PackedWeight:
+    """A weight tensor packed by moe_pack_weights together with the
+    library's descriptor of it, which the forward calls take.  `tensor` is
+    the packed device tensor (same shape and dtype as the row-major one)."""
+
+    def __init__(self, tensor, desc):
+        self.tensor = tensor
+        self.desc = desc
+
+    shape = property(lambda self: self.tensor.shape)
+    dtype = property(lambda self: self.tensor.dtype)
+    device = property(lambda self: self.tensor.device)
+
+    def clone(self):
+        """A device copy of the packed bytes, with its own descriptor."""
+        return moe_describe_packed_weights(self.tensor.clone(), self.desc.dtype)
+
+    def numel(self):
+        return self.tensor.numel()
+
+    def element_size(self):
+        return self.tensor.element_size()
+
+
+EXPORTS = ("moe_status_string", "moe_pack_weights", "moe_describe_packed_weights", "moe_routing_layout",
+           "moe_workspace_layout",
            "moe_router_topk", "moe_router_pair_bytes", "moe_router_split_weights",
            "moe_router_workspace_bytes", "moe_router_gemm", "moe_router_gemm_topk",
            "moe_build_routing_bf16", "moe_build_routing_fp8", "moe_build_routing_mxfp8",
            "moe_build_routing_int8", "moe_build_routing_int4", "moe_forward_bf16",
            "moe_forward_fp8", "moe_forward_mxfp8", "moe_forward_int8", "moe_forward_int4",
            "moe_build_routing_fp8_block", "moe_forward_fp8_block",
-           "moe_build_routing_int8_w8a16", "moe_forward_int8_w8a16", "moe_set_stage_events", "moe_device_cu_count")
+           "moe_build_routing_int8_w8a16", "moe_forward_int8_w8a16", "moe_set_stage_events", "moe_device_cu_count",
+           "moe_stream_read")
 
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m mixture_experts_layer_lds_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python mixture_experts_layer_lds_amd/build.py` (or __graft_entry__.build())")
     L = ctypes.CDLL(LIB_PATH)
     i, P, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [i]
     L.moe_pack_weights.restype = i
-    L.moe_pack_weights.argtypes = [P, i, i, i, i, P, P]
+    L.moe_pack_weights.argtypes = [P, i, i, i, i, P, ctypes.POINTER(PackedWeightsDesc), P]
+    L.moe_describe_packed_weights.restype = i
+    L.moe_describe_packed_weights.argtypes = [P, i, i, i, i, ctypes.POINTER(PackedWeightsDesc)]
     L.moe_routing_layout.restype = i
     L.moe_routing_layout.argtypes = [i, i, i, i, i, i, ctypes.POINTER(RoutingLayout)]
     L.moe_workspace_layout.restype = i
@@ -113,23 +146,26 @@ def _load():
     L.moe_router_gemm_topk.argtypes = [P, P, i, i, i, i, i, i, P, sz, P, P, P, P]
     L.moe_router_topk.argtypes = [P, i, i, i, i, i, P, P, P]
     L.moe_forward_bf16.restype = i
-    L.moe_forward_bf16.argtypes = [P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
+    D = ctypes.POINTER(PackedWeightsDesc)
+    L.moe_forward_bf16.argtypes = [P, P, P, D, D, i, i, i, i, i, P, sz, P, P]
     L.moe_forward_fp8.restype = i
-    L.moe_forward_fp8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
+    L.moe_forward_fp8.argtypes = [P, P, P, D, P, D, P, i, i, i, i, i, P, sz, P, P]
     L.moe_forward_mxfp8.restype = i
-    L.moe_forward_mxfp8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
+    L.moe_forward_mxfp8.argtypes = [P, P, P, D, P, D, P, i, i, i, i, i, P, sz, P, P]
     L.moe_forward_fp8_block.restype = i
-    L.moe_forward_fp8_block.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
+    L.moe_forward_fp8_block.argtypes = [P, P, P, D, P, D, P, i, i, i, i, i, P, sz, P, P]
     L.moe_forward_int4.restype = i
-    L.moe_forward_int4.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
+    L.moe_forward_int4.argtypes = [P, P, P, D, P, D, P, i, i, i, i, i, P, sz, P, P]
     L.moe_forward_int8.restype = i
-    L.moe_forward_int8.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
+    L.moe_forward_int8.argtypes = [P, P, P, D, P, D, P, i, i, i, i, i, P, sz, P, P]
     L.moe_forward_int8_w8a16.restype = i
-    L.moe_forward_int8_w8a16.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
+    L.moe_forward_int8_w8a16.argtypes = [P, P, P, D, P, D, P, i, i, i, i, i, P, sz, P, P]
     L.moe_set_stage_events.restype = i
     L.moe_set_stage_events.argtypes = [ctypes.POINTER(P), i]
     L.moe_device_cu_count.restype = i
     L.moe_device_cu_count.argtypes = []
+    L.moe_stream_read.restype = i
+    L.moe_stream_read.argtypes = [P, sz, P, sz, P]
     return L
 
 
@@ -158,7 +194,8 @@ def _stream(stream):
 def moe_pack_weights(w, dtype="bf16", out=None, stream=None):
     """Packed copy of a row-major [E][rows][cols] weight tensor (bf16; uint8
     e4m3 codes for dtype "fp8", "fp8b" and "mxfp8"; int8 codes for "int8"; uint8 bytes
-    of two int4 codes for "int4", whose K length is twice the byte count)."""
+    of two int4 codes for "int4", whose K length is twice the byte count), as a
+    PackedWeight (the packed tensor and its descriptor for the forward calls)."""
     want = {"bf16": torch.bfloat16, "int8": torch.int8, "int8w": torch.int8}.get(dtype, torch.uint8)
     if w.dtype != want or w.dim() != 3 or not w.is_contiguous():
         raise ValueError(f"moe_pack_weights: expected contiguous {want} [E][rows][cols]")
@@ -167,9 +204,24 @@ def moe_pack_weights(w, dtype="bf16", out=None, stream=None):
         cols *= 2
     if out is None:
         out = torch.empty_like(w)
+    desc = PackedWeightsDesc()
     _check("moe_pack_weights", _lib.moe_pack_weights(_ptr(w), E, rows, cols, DTYPES[dtype],
-                                                     _ptr(out), _stream(stream)))
-    return out
+                                                     _ptr(out), ctypes.byref(desc), _stream(stream)))
+    return PackedWeight(out, desc)
+
+
+def moe_describe_packed_weights(packed, dtype):
+    """PackedWeight for a tensor that already holds packed bytes (a copy of a
+    packed tensor, or packed weights loaded from storage); dtype is a name of
+    DTYPES or its code."""
+    code = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    E, rows, cols = packed.shape
+    if code == MOE_DTYPE_INT4_W4A16:
+        cols *= 2
+    desc = PackedWeightsDesc()
+    _check("moe_describe_packed_weights",
+           _lib.moe_describe_packed_weights(_ptr(packed), E, rows, cols, code, ctypes.byref(desc)))
+    return PackedWeight(packed, desc)
 
 
 def pack_weights(weights, dtype="bf16", stream=None):
@@ -349,8 +401,18 @@ def build_routing(topk_ids, E, H, I, routing, dtype="bf16", stream=None):
 
 
 def _check_tensor(name, t, dtype, shape):
+    if isinstance(t, PackedWeight):
+        t = t.tensor
     if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
         raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
+def _desc(name, w):
+    """The library descriptor of a packed weight (forward calls take nothing else)."""
+    if not isinstance(w, PackedWeight):
+        raise TypeError(f"{name}: expected a PackedWeight from moe_pack_weights / pack_weights, "
+                        f"got {type(w).__name__} (the forward calls take packed weights only)")
+    return ctypes.byref(w.desc)
 
 
 def moe_forward_bf16(x, topk_w, routing, w1, w2, workspace, out, stream=None):
@@ -364,7 +426,7 @@ def moe_forward_bf16(x, topk_w, routing, w1, w2, workspace, out, stream=None):
     _check_tensor("w2", w2, torch.bfloat16, (E, H, I))
     _check_tensor("out", out, torch.bfloat16, (T, H))
     _check("moe_forward_bf16", _lib.moe_forward_bf16(
-        _ptr(x), _ptr(topk_w), _ptr(routing), _ptr(w1), _ptr(w2), T, k, E, H, I,
+        _ptr(x), _ptr(topk_w), _ptr(routing), _desc("w1", w1), _desc("w2", w2), T, k, E, H, I,
         _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
     return out
 
@@ -382,7 +444,7 @@ def moe_forward_fp8(x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, o
     _check_tensor("w2_scale", w2_scale, torch.float32, (E, H))
     _check_tensor("out", out, torch.bfloat16, (T, H))
     _check("moe_forward_fp8", _lib.moe_forward_fp8(
-        _ptr(x), _ptr(topk_w), _ptr(routing), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale),
+        _ptr(x), _ptr(topk_w), _ptr(routing), _desc("w1", w1), _ptr(w1_scale), _desc("w2", w2), _ptr(w2_scale),
         T, k, E, H, I, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
     return out
 
@@ -400,7 +462,7 @@ def moe_forward_mxfp8(x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace,
     _check_tensor("w2_scale", w2_scale, torch.uint8, (E, H, I // 32))
     _check_tensor("out", out, torch.bfloat16, (T, H))
     _check("moe_forward_mxfp8", _lib.moe_forward_mxfp8(
-        _ptr(x), _ptr(topk_w), _ptr(routing), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale),
+        _ptr(x), _ptr(topk_w), _ptr(routing), _desc("w1", w1), _ptr(w1_scale), _desc("w2", w2), _ptr(w2_scale),
         T, k, E, H, I, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
     return out
 
@@ -418,7 +480,7 @@ def moe_forward_fp8_block(x, topk_w, routing, w1, w1_scale, w2, w2_scale, worksp
     _check_tensor("w2_scale", w2_scale, torch.float32, (E, H // 128, I // 128))
     _check_tensor("out", out, torch.bfloat16, (T, H))
     _check("moe_forward_fp8_block", _lib.moe_forward_fp8_block(
-        _ptr(x), _ptr(topk_w), _ptr(routing), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale),
+        _ptr(x), _ptr(topk_w), _ptr(routing), _desc("w1", w1), _ptr(w1_scale), _desc("w2", w2), _ptr(w2_scale),
         T, k, E, H, I, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
     return out
 
@@ -436,7 +498,7 @@ def moe_forward_int8_w8a16(x, topk_w, routing, w1, w1_scale, w2, w2_scale, works
     _check_tensor("w2_scale", w2_scale, torch.float32, (E, H))
     _check_tensor("out", out, torch.bfloat16, (T, H))
     _check("moe_forward_int8_w8a16", _lib.moe_forward_int8_w8a16(
-        _ptr(x), _ptr(topk_w), _ptr(routing), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale),
+        _ptr(x), _ptr(topk_w), _ptr(routing), _desc("w1", w1), _ptr(w1_scale), _desc("w2", w2), _ptr(w2_scale),
         T, k, E, H, I, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
     return out
 
@@ -454,7 +516,7 @@ def moe_forward_int4(x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, 
     _check_tensor("w2_scale", w2_scale, torch.float32, (E, H, I // 128))
     _check_tensor("out", out, torch.bfloat16, (T, H))
     _check("moe_forward_int4", _lib.moe_forward_int4(
-        _ptr(x), _ptr(topk_w), _ptr(routing), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale),
+        _ptr(x), _ptr(topk_w), _ptr(routing), _desc("w1", w1), _ptr(w1_scale), _desc("w2", w2), _ptr(w2_scale),
         T, k, E, H, I, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
     return out
 
@@ -472,7 +534,7 @@ def moe_forward_int8(x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, 
     _check_tensor("w2_scale", w2_scale, torch.float32, (E, H))
     _check_tensor("out", out, torch.bfloat16, (T, H))
     _check("moe_forward_int8", _lib.moe_forward_int8(
-        _ptr(x), _ptr(topk_w), _ptr(routing), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale),
+        _ptr(x), _ptr(topk_w), _ptr(routing), _desc("w1", w1), _ptr(w1_scale), _desc("w2", w2), _ptr(w2_scale),
         T, k, E, H, I, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
     return out
 
@@ -494,6 +556,14 @@ def moe_device_cu_count() -> int:
     if n < 0:
         raise MoeError("moe_device_cu_count", n)
     return n
+
+
+def moe_stream_read(buf, sink, stream=None):
+    """Measurement aid: one streaming read of the device tensor `buf` (its
+    whole storage) into per-workgroup words of the uint32/int32 tensor `sink`."""
+    nbytes = buf.numel() * buf.element_size()
+    _check("moe_stream_read", _lib.moe_stream_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(),
+                                                   _stream(stream)))
 
 
 def moe_layer(x, topk_ids, topk_w, weights, dtype="bf16", out=None, stream=None):

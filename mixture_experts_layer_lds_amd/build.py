@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["router.hip", "router_gemm.hip", "route.hip", "elementwise.hip", "mx.hip", "int8.hip", "stream_gemm.hip", "w4_gemm.hip", "w8_gemm.hip", "fp8b_gemm.hip", "tiled_gemm.hip", "strip_gemm.hip", "pack.hip", "moe_api.hip"]
+SOURCES = ["router.hip", "router_gemm.hip", "route.hip", "elementwise.hip", "mx.hip", "int8.hip", "stream_gemm.hip", "w4_gemm.hip", "w8_gemm.hip", "fp8b_gemm.hip", "tiled_gemm.hip", "strip_gemm.hip", "pack.hip", "ceiling.hip", "moe_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -437,6 +437,46 @@ int stream_grid(long max_items, int waves, int cus) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Check value of a packed-weight descriptor: a 64-bit mix of its other
+// fields (the splitmix64 finaliser applied after each, from a fixed seed).
+// It tells a descriptor from moe_pack_weights apart from raw weight
+// pointers and hand-made descriptors; it is not a secret.
+uint64_t mix64(uint64_t h, uint64_t v) {
+  h ^= v + 0x9e3779b97f4a7c15ull + (h << 6) + (h >> 2);
+  h ^= h >> 30;
+  h *= 0xbf58476d1ce4e5b9ull;
+  h ^= h >> 27;
+  h *= 0x94d049bb133111ebull;
+  h ^= h >> 31;
+  return h;
+}
+
+uint64_t packed_check(const moe_packed_weights_t& d) {
+  uint64_t h = 0x4d6f4550616b6564ull;
+  h = mix64(h, reinterpret_cast<uintptr_t>(d.data));
+  h = mix64(h, (uint32_t)d.dtype);
+  h = mix64(h, (uint32_t)d.experts);
+  h = mix64(h, (uint32_t)d.rows);
+  h = mix64(h, (uint32_t)d.cols);
+  return h;
+}
+
+// The W1 and W2 descriptors of a forward call, after the sizes: made by
+// moe_pack_weights for this dtype, E experts and the matrices [2I][H] and
+// [H][I].  T == 0 passes with any descriptors (nothing is read).
+int check_packed(int dtype, const moe_packed_weights_t* w1, const moe_packed_weights_t* w2, int T,
+                 int k, int E, int H, int I) {
+  const int rc = check_shape(T, k, E, H, I, dtype);
+  if (rc != MOE_OK || T == 0) return rc;
+  auto ok = [&](const moe_packed_weights_t* d, int rows, int cols) {
+    return d && d->data && d->dtype == dtype && d->experts == E && d->rows == rows && d->cols == cols &&
+           d->check == packed_check(*d);
+  };
+  return ok(w1, 2 * I, H) && ok(w2, H, I) ? MOE_OK : MOE_ERR_INVALID_ARG;
+}
+
+const void* packed_data(const moe_packed_weights_t* d) { return d ? d->data : nullptr; }
+
 // Stage-event hook (measurement only).
 void* g_events[10];
 bool g_events_on = false;
@@ -1087,6 +1127,30 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
   return MOE_OK;
 }
 
+// Shape and pointer rules of a packed weight tensor; its row length in bytes.
+int packed_shape(const void* packed, int E, int rows, int cols, int dtype, long* row_bytes) {
+  if (!known_dtype(dtype)) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || rows < 1 || cols < 1) return MOE_ERR_INVALID_ARG;
+  const long rb = dtype == MOE_DTYPE_INT4_W4A16 ? (long)cols / 2
+                                                : (long)cols * (dtype == MOE_DTYPE_BF16 ? 2 : 1);
+  if (dtype == MOE_DTYPE_INT4_W4A16 && cols % 2) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (rows % 16 || rb % 64 || rows > 2 * 65536 || cols > 65536) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (!packed || !aligned(packed, 16)) return MOE_ERR_INVALID_ARG;
+  *row_bytes = rb;
+  return MOE_OK;
+}
+
+void describe(const void* packed, int E, int rows, int cols, int dtype, moe_packed_weights_t* desc) {
+  moe_packed_weights_t d{};
+  d.data = packed;
+  d.dtype = dtype;
+  d.experts = E;
+  d.rows = rows;
+  d.cols = cols;
+  d.check = packed_check(d);
+  *desc = d;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1119,22 +1183,31 @@ int moe_workspace_layout(int T, int k, int E, int H, int I, int dtype, moe_works
 }
 
 int moe_pack_weights(const void* w, int E, int rows, int cols, int dtype, void* packed,
-                     void* stream) {
-  if (!known_dtype(dtype)) return MOE_ERR_INVALID_ARG;
-  if (E < 1 || rows < 1 || cols < 1) return MOE_ERR_INVALID_ARG;
-  const long row_bytes = dtype == MOE_DTYPE_INT4_W4A16 ? (long)cols / 2
-                                                      : (long)cols * (dtype == MOE_DTYPE_BF16 ? 2 : 1);
-  if (dtype == MOE_DTYPE_INT4_W4A16 && cols % 2) return MOE_ERR_UNSUPPORTED_SHAPE;
-  if (rows % 16 || row_bytes % 64 || rows > 2 * 65536 || cols > 65536)
-    return MOE_ERR_UNSUPPORTED_SHAPE;
-  if (!w || !packed || !aligned(w, 16) || !aligned(packed, 16)) return MOE_ERR_INVALID_ARG;
+                     moe_packed_weights_t* desc, void* stream) {
+  if (!desc) return MOE_ERR_INVALID_ARG;
+  long row_bytes = 0;
+  const int rc = packed_shape(packed, E, rows, cols, dtype, &row_bytes);
+  if (rc != MOE_OK) return rc;
+  if (!w || !aligned(w, 16)) return MOE_ERR_INVALID_ARG;
   const size_t total = (size_t)E * rows * row_bytes;
   const char* a = static_cast<const char*>(w);
   const char* b = static_cast<const char*>(packed);
   if (a < b + total && b < a + total) return MOE_ERR_INVALID_ARG;   // overlap
   const hipError_t e = moe_host::launch_pack(w, E, rows, (int)row_bytes, packed,
                                              static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  describe(packed, E, rows, cols, dtype, desc);
+  return MOE_OK;
+}
+
+int moe_describe_packed_weights(const void* packed, int E, int rows, int cols, int dtype,
+                                moe_packed_weights_t* desc) {
+  if (!desc) return MOE_ERR_INVALID_ARG;
+  long row_bytes = 0;
+  const int rc = packed_shape(packed, E, rows, cols, dtype, &row_bytes);
+  if (rc != MOE_OK) return rc;
+  describe(packed, E, rows, cols, dtype, desc);
+  return MOE_OK;
 }
 
 int moe_build_routing_bf16(const int32_t* topk_ids, int T, int k, int E, int H, int I,
@@ -1248,11 +1321,12 @@ int moe_build_routing_mxfp8(const int32_t* topk_ids, int T, int k, int E, int H,
   return build_routing(MOE_DTYPE_MXFP8, topk_ids, T, k, E, H, I, routing, routing_bytes, stream);
 }
 
-int moe_forward_mxfp8(const void* x, const float* topk_w, const void* routing, const uint8_t* w1,
-                      const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale, int T,
-                      int k, int E, int H, int I, void* workspace, size_t workspace_bytes, void* out,
-                      void* stream) {
-  return forward_mx(x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
+int moe_forward_mxfp8(const void* x, const float* topk_w, const void* routing, const moe_packed_weights_t* w1,
+    const uint8_t* w1_scale, const moe_packed_weights_t* w2, const uint8_t* w2_scale, int T, int k, int E,
+    int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const int rc = check_packed(MOE_DTYPE_MXFP8, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return forward_mx(x, topk_w, routing, packed_data(w1), w1_scale, packed_data(w2), w2_scale, T, k, E, H, I, workspace,
                     workspace_bytes, out, stream);
 }
 
@@ -1261,12 +1335,13 @@ int moe_build_routing_fp8_block(const int32_t* topk_ids, int T, int k, int E, in
   return build_routing(MOE_DTYPE_FP8_BLOCK, topk_ids, T, k, E, H, I, routing, routing_bytes, stream);
 }
 
-int moe_forward_fp8_block(const void* x, const float* topk_w, const void* routing, const uint8_t* w1,
-                          const float* w1_scale, const uint8_t* w2, const float* w2_scale, int T,
-                          int k, int E, int H, int I, void* workspace, size_t workspace_bytes,
-                          void* out, void* stream) {
-  return forward_fp8b(x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
-                      workspace_bytes, out, stream);
+int moe_forward_fp8_block(const void* x, const float* topk_w, const void* routing, const moe_packed_weights_t* w1,
+    const float* w1_scale, const moe_packed_weights_t* w2, const float* w2_scale, int T, int k, int E,
+    int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const int rc = check_packed(MOE_DTYPE_FP8_BLOCK, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return forward_fp8b(x, topk_w, routing, packed_data(w1), w1_scale, packed_data(w2), w2_scale, T, k, E, H, I,
+                      workspace, workspace_bytes, out, stream);
 }
 
 int moe_build_routing_int4(const int32_t* topk_ids, int T, int k, int E, int H, int I,
@@ -1274,12 +1349,13 @@ int moe_build_routing_int4(const int32_t* topk_ids, int T, int k, int E, int H, 
   return build_routing(MOE_DTYPE_INT4_W4A16, topk_ids, T, k, E, H, I, routing, routing_bytes, stream);
 }
 
-int moe_forward_int4(const void* x, const float* topk_w, const void* routing, const uint8_t* w1,
-                     const float* w1_scale, const uint8_t* w2, const float* w2_scale, int T, int k,
-                     int E, int H, int I, void* workspace, size_t workspace_bytes, void* out,
-                     void* stream) {
-  return forward_w4(MOE_DTYPE_INT4_W4A16, x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I,
-                    workspace, workspace_bytes, out, stream);
+int moe_forward_int4(const void* x, const float* topk_w, const void* routing, const moe_packed_weights_t* w1,
+    const float* w1_scale, const moe_packed_weights_t* w2, const float* w2_scale, int T, int k, int E,
+    int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const int rc = check_packed(MOE_DTYPE_INT4_W4A16, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return forward_w4(MOE_DTYPE_INT4_W4A16, x, topk_w, routing, packed_data(w1), w1_scale, packed_data(w2), w2_scale, T,
+                    k, E, H, I, workspace, workspace_bytes, out, stream);
 }
 
 int moe_build_routing_int8_w8a16(const int32_t* topk_ids, int T, int k, int E, int H, int I,
@@ -1287,12 +1363,13 @@ int moe_build_routing_int8_w8a16(const int32_t* topk_ids, int T, int k, int E, i
   return build_routing(MOE_DTYPE_INT8_W8A16, topk_ids, T, k, E, H, I, routing, routing_bytes, stream);
 }
 
-int moe_forward_int8_w8a16(const void* x, const float* topk_w, const void* routing, const int8_t* w1,
-                           const float* w1_scale, const int8_t* w2, const float* w2_scale, int T, int k,
-                           int E, int H, int I, void* workspace, size_t workspace_bytes, void* out,
-                           void* stream) {
-  return forward_w4(MOE_DTYPE_INT8_W8A16, x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I,
-                    workspace, workspace_bytes, out, stream);
+int moe_forward_int8_w8a16(const void* x, const float* topk_w, const void* routing, const moe_packed_weights_t* w1,
+    const float* w1_scale, const moe_packed_weights_t* w2, const float* w2_scale, int T, int k, int E,
+    int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const int rc = check_packed(MOE_DTYPE_INT8_W8A16, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return forward_w4(MOE_DTYPE_INT8_W8A16, x, topk_w, routing, packed_data(w1), w1_scale, packed_data(w2), w2_scale,
+                    T, k, E, H, I, workspace, workspace_bytes, out, stream);
 }
 
 int moe_build_routing_int8(const int32_t* topk_ids, int T, int k, int E, int H, int I,
@@ -1300,27 +1377,31 @@ int moe_build_routing_int8(const int32_t* topk_ids, int T, int k, int E, int H, 
   return build_routing(MOE_DTYPE_INT8_W8A8, topk_ids, T, k, E, H, I, routing, routing_bytes, stream);
 }
 
-int moe_forward_int8(const void* x, const float* topk_w, const void* routing, const int8_t* w1,
-                     const float* w1_scale, const int8_t* w2, const float* w2_scale, int T, int k,
-                     int E, int H, int I, void* workspace, size_t workspace_bytes, void* out,
-                     void* stream) {
-  return forward_i8(x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
+int moe_forward_int8(const void* x, const float* topk_w, const void* routing, const moe_packed_weights_t* w1,
+    const float* w1_scale, const moe_packed_weights_t* w2, const float* w2_scale, int T, int k, int E,
+    int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const int rc = check_packed(MOE_DTYPE_INT8_W8A8, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return forward_i8(x, topk_w, routing, packed_data(w1), w1_scale, packed_data(w2), w2_scale, T, k, E, H, I, workspace,
                     workspace_bytes, out, stream);
 }
 
-int moe_forward_bf16(const void* x, const float* topk_w, const void* routing, const void* w1,
-                     const void* w2, int T, int k, int E, int H, int I, void* workspace,
-                     size_t workspace_bytes, void* out, void* stream) {
-  return forward(MOE_DTYPE_BF16, x, topk_w, routing, w1, nullptr, w2, nullptr, T, k, E, H, I,
-                 workspace, workspace_bytes, out, stream);
+int moe_forward_bf16(const void* x, const float* topk_w, const void* routing,
+                     const moe_packed_weights_t* w1, const moe_packed_weights_t* w2, int T, int k, int E,
+                     int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const int rc = check_packed(MOE_DTYPE_BF16, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return forward(MOE_DTYPE_BF16, x, topk_w, routing, packed_data(w1), nullptr, packed_data(w2), nullptr, T,
+                 k, E, H, I, workspace, workspace_bytes, out, stream);
 }
 
-int moe_forward_fp8(const void* x, const float* topk_w, const void* routing, const uint8_t* w1,
-                    const float* w1_scale, const uint8_t* w2, const float* w2_scale, int T, int k,
-                    int E, int H, int I, void* workspace, size_t workspace_bytes, void* out,
-                    void* stream) {
-  return forward(MOE_DTYPE_FP8_W8A8, x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H,
-                 I, workspace, workspace_bytes, out, stream);
+int moe_forward_fp8(const void* x, const float* topk_w, const void* routing, const moe_packed_weights_t* w1,
+    const float* w1_scale, const moe_packed_weights_t* w2, const float* w2_scale, int T, int k, int E,
+    int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const int rc = check_packed(MOE_DTYPE_FP8_W8A8, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return forward(MOE_DTYPE_FP8_W8A8, x, topk_w, routing, packed_data(w1), w1_scale, packed_data(w2), w2_scale, T, k,
+                 E, H, I, workspace, workspace_bytes, out, stream);
 }
 
 int moe_set_stage_events(void* const* events, int n) {
@@ -1338,6 +1419,18 @@ int moe_set_stage_events(void* const* events, int n) {
   for (int i = 0; i < 10; i++) g_events[i] = events[i];
   g_events_on = true;
   return MOE_OK;
+}
+
+int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
+  if (!buf || !sink || sink_words < 1 || bytes % 16 || !aligned(buf, 16) || !aligned(sink, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (bytes == 0) return MOE_OK;
+  int cus = 0;
+  const int rc = cu_count(&cus);
+  if (rc != MOE_OK) return rc;
+  const int groups = (int)std::min<size_t>(sink_words, (size_t)cus * 8);
+  const hipError_t e = moe_host::launch_stream_read(buf, bytes, sink, groups, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int moe_device_cu_count(void) {

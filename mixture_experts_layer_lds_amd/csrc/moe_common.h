@@ -339,6 +339,10 @@ hipError_t launch_mx_quant_bf16(const uint16_t* x, int T, int H, uint8_t* xq, ui
 hipError_t launch_mx_requant(const float* h, int P, int I, const int32_t* expert_offsets, int E,
                              uint8_t* hq, uint8_t* sh, hipStream_t s);
 
+// Streaming read of `bytes` (multiple of 16) of buf by `groups` workgroups,
+// one folded word per workgroup written to sink.
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int groups, hipStream_t s);
+
 // fp32 rows -> e4m3 codes with the row amax held in h_scale (replaced by the scale).
 hipError_t launch_requant_rows(const float* h32, int P, int I, const int32_t* expert_offsets,
                                int E, uint8_t* hq, float* h_scale, bool find_amax, hipStream_t s);

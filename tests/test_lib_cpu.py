@@ -93,10 +93,23 @@ def test_layout_rejects_bad_shapes(m, args, code):
     assert lib.moe_routing_layout(4, 2, 8, 128, 64, 7, ctypes.byref(L)) == -1
 
 
+def describe(m, addr, E, rows, cols, dtype):
+    """Descriptor of (fake) packed bytes at addr, made by the library on the host."""
+    d = m.PackedWeightsDesc()
+    rc = m._lib.moe_describe_packed_weights(ctypes.c_void_p(addr), E, rows, cols, m.DTYPES[dtype],
+                                            ctypes.byref(d))
+    assert rc == 0
+    return d
+
+
 def test_calls_reject_bad_arguments_without_launching(m):
     lib = m._lib
     fake = ctypes.c_void_p(4096)            # never dereferenced: every call fails its checks
     odd = ctypes.c_void_p(4097)
+    w1 = ctypes.byref(describe(m, 4096, 8, 128, 128, "bf16"))   # E=8, 2I=128, H=128
+    w2 = ctypes.byref(describe(m, 4096, 8, 128, 64, "bf16"))    # H=128, I=64
+    f1 = ctypes.byref(describe(m, 4096, 8, 128, 128, "fp8"))
+    f2 = ctypes.byref(describe(m, 4096, 8, 128, 64, "fp8"))
     L = m.moe_routing_layout(4, 2, 8, 128, 64, "bf16")
     n = L["total_bytes"]
     # null ids / routing
@@ -112,7 +125,7 @@ def test_calls_reject_bad_arguments_without_launching(m):
     assert lib.moe_build_routing_bf16(None, 0, 2, 8, 128, 64, None, 0, None) == 0
     assert lib.moe_forward_bf16(None, None, None, None, None, 0, 2, 8, 128, 64, None, 0, None, None) == 0
     W = m.moe_workspace_layout(4, 2, 8, 128, 64, "bf16")["total_bytes"]
-    args = [fake, fake, fake, fake, fake, 4, 2, 8, 128, 64, fake, W, fake, None]
+    args = [fake, fake, fake, w1, w2, 4, 2, 8, 128, 64, fake, W, fake, None]
     a = list(args)
     a[0] = None
     assert lib.moe_forward_bf16(*a) == -1                 # null x
@@ -122,11 +135,8 @@ def test_calls_reject_bad_arguments_without_launching(m):
     a = list(args)
     a[10] = ctypes.c_void_p(4096 + 16)
     assert lib.moe_forward_bf16(*a) == -1                 # workspace not 256-byte aligned
-    a = list(args)
-    a[3] = odd
-    assert lib.moe_forward_bf16(*a) == -1                 # misaligned w1
     Wf = m.moe_workspace_layout(4, 2, 8, 128, 64, "fp8")["total_bytes"]
-    fargs = [fake, fake, fake, fake, fake, fake, fake, 4, 2, 8, 128, 64, fake, Wf, fake, None]
+    fargs = [fake, fake, fake, f1, fake, f2, fake, 4, 2, 8, 128, 64, fake, Wf, fake, None]
     a = list(fargs)
     a[4] = None
     assert lib.moe_forward_fp8(*a) == -1                  # null w1_scale
@@ -185,3 +195,55 @@ def test_stage_event_hook_argument_checks(m):
     arr = (ctypes.c_void_p * 10)(*([0, 0, 1, 2] + [0] * 6))
     assert lib.moe_set_stage_events(arr, 10) == 0       # gate-up only
     assert lib.moe_set_stage_events(None, 0) == 0
+
+
+def test_forward_takes_only_packed_weight_descriptors(m):
+    """Row-major weights cannot reach the kernels: the forward calls take
+    descriptors that moe_pack_weights (or moe_describe_packed_weights) made
+    for the call's dtype, expert count and matrix shapes, and reject every
+    other one with MOE_ERR_INVALID_ARG before launching anything."""
+    lib = m._lib
+    fake = ctypes.c_void_p(4096)
+    E, H, I, T, k = 8, 128, 64, 4, 2
+    W = m.moe_workspace_layout(T, k, E, H, I, "bf16")["total_bytes"]
+    good1 = describe(m, 1 << 20, E, 2 * I, H, "bf16")
+    good2 = describe(m, 1 << 21, E, H, I, "bf16")
+
+    def fwd(d1, d2, ws=W):
+        return lib.moe_forward_bf16(fake, fake, fake, d1, d2, T, k, E, H, I, fake, ws, fake, None)
+
+    # with good descriptors the call gets past them (and then fails on the
+    # too-small workspace, so that nothing is launched)
+    assert fwd(ctypes.byref(good1), ctypes.byref(good2), W - 1) == -3
+    # row-major weights: a descriptor not made by the library
+    raw = m.PackedWeightsDesc(data=1 << 20, dtype=0, experts=E, rows=2 * I, cols=H, check=0)
+    assert fwd(ctypes.byref(raw), ctypes.byref(good2)) == -1
+    assert fwd(None, ctypes.byref(good2)) == -1
+    assert fwd(ctypes.byref(m.PackedWeightsDesc()), ctypes.byref(good2)) == -1
+    # a library descriptor with any field changed afterwards
+    for field, val in (("data", 1 << 22), ("dtype", 1), ("experts", 16), ("rows", 256), ("cols", 256)):
+        d = m.PackedWeightsDesc.from_buffer_copy(good1)
+        setattr(d, field, val)
+        assert fwd(ctypes.byref(d), ctypes.byref(good2)) == -1, field
+    # the right kind of descriptor in the wrong place or for another call
+    assert fwd(ctypes.byref(good2), ctypes.byref(good1)) == -1          # W1 and W2 swapped
+    fp8_1 = describe(m, 1 << 20, E, 2 * I, H, "fp8")
+    assert fwd(ctypes.byref(fp8_1), ctypes.byref(good2)) == -1          # packed for another dtype
+    other = describe(m, 1 << 20, 16, 2 * I, H, "bf16")
+    assert fwd(ctypes.byref(other), ctypes.byref(good2)) == -1          # another expert count
+    # describe checks the same size rules as the pack
+    d = m.PackedWeightsDesc()
+    assert lib.moe_describe_packed_weights(ctypes.c_void_p(4096), E, 24, H, 0, ctypes.byref(d)) == -2
+    assert lib.moe_describe_packed_weights(ctypes.c_void_p(4100), E, 32, H, 0, ctypes.byref(d)) == -1
+    assert lib.moe_describe_packed_weights(ctypes.c_void_p(4096), E, 32, H, 0, None) == -1
+
+
+def test_binding_refuses_unpacked_tensors(m):
+    import torch
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    w = torch.zeros(4, 2, dtype=torch.float32)
+    raw1 = torch.zeros(8, 128, 128, dtype=torch.bfloat16)
+    raw2 = torch.zeros(8, 128, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="PackedWeight"):
+        m.moe_forward_bf16(x, w, torch.zeros(16, dtype=torch.uint8), raw1, raw2,
+                           torch.zeros(256, dtype=torch.uint8), torch.zeros(4, 128, dtype=torch.bfloat16))
