@@ -3,9 +3,12 @@
 bf16: max|err| <= 1e-2*max|ref| + 1e-3.  fp8 w8a8: max|err| <= 4e-2*max|ref|
 against the oracle applying the same quantisation, and the per-token e4m3
 codes and scales of x bit-exact.  Small shapes are compared on every
-output; the five workloads at full size are compared on sampled tokens
-(always including the first and last), in the launch configuration the
-benchmark times.
+output (and, on fp8, the x codes and scales bit-exact and the requantised
+intermediate within one code step).  The workloads at full size, in the
+launch configuration the benchmark times, are compared on every token where
+the oracle costs a few seconds, else on a seeded 256-token subset that holds
+the first and last token and every token of the most loaded expert's first
+two row tiles.
 """
 import numpy as np
 import pytest
@@ -26,6 +29,82 @@ def lib():
 
 def out64(out):
     return out.float().cpu().double().numpy()
+
+
+def e4m3_ordinal(c):
+    """Position of e4m3 codes on the number line (+0 and -0 both 0)."""
+    c = c.astype(np.int64)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+_E4M3 = None
+
+
+def e4m3_values():
+    global _E4M3
+    if _E4M3 is None:
+        _E4M3 = np.array([oracle.e4m3_value(v) for v in range(256)])
+    return _E4M3
+
+
+def e4m3_spacing(v):
+    """Distance to the next e4m3 value above |v|: 2^(e-3) for |v| in [2^e, 2^(e+1)),
+    2^-9 among the subnormals (below 2^-6)."""
+    av = np.abs(v)
+    e = np.floor(np.log2(np.maximum(av, 2.0 ** -6)))
+    return np.where(av < 2.0 ** -6, 2.0 ** -9, 2.0 ** (e - 3))
+
+
+def check_fp8_quant(lib, T, k, E, H, I, ws, routing, ids, rows, xq, sx, hq, sh, what):
+    """fp8 w8a8 workspace against the oracle's quantisation, for the tokens
+    `rows` (the oracle's outputs xq, sx, hq, sh are for those tokens).
+
+    x codes and scales: bit-exact (the same rule on the same bf16 inputs).
+
+    The requantised intermediate of every valid pair of those tokens: >= 99%
+    of codes equal; every dequantised value within one e4m3 step (at the
+    larger of the two magnitudes) plus 2^-11 of its row's amax of the
+    oracle's; scales within 1e-3 relative.  The intermediate is not exact on
+    this path: the GPU's gate and up sums come from the fp8 MFMA, whose
+    128-value unit sums are truncated (the measured summation bound of the
+    instruction), and from fp32 adds, against the oracle's exact fp64 sums;
+    relative to the row's amax that error is about 1e-5.  So the scale
+    amax/448 moves by about that much, a code next to a rounding boundary
+    goes one step either way, and among the smallest values, whose e4m3
+    steps (2^-9 of the scale) are finer than that error, by a few steps: the
+    2^-11 term, far above the error and far below the output tolerance."""
+    L = lib.moe_workspace_layout(T, k, E, H, I, "fp8")
+    P = T * k
+    rsel = torch.tensor(rows, dtype=torch.long, device=ws.device)
+    gxq = ws[L["xq"]:L["xq"] + T * H].view(T, H)[rsel].cpu().numpy()
+    gsx = ws[L["x_scale"]:L["x_scale"] + 4 * T].view(torch.float32)[rsel].cpu().numpy()
+    assert np.array_equal(gxq, xq), f"{what}: x e4m3 codes"
+    assert np.array_equal(gsx, sx), f"{what}: x scales"
+    idc = ids.cpu().numpy()[rows]
+    valid = (idc >= 0) & (idc < E)
+    if not valid.any():
+        return
+    pos = lib.read_routing(routing, T, k, E, H, I, "fp8")["pos"].numpy().reshape(T, k)[rows]
+    psel = torch.from_numpy(pos[valid].astype(np.int64)).to(ws.device)
+    ghq = ws[L["h"]:L["h"] + P * I].view(P, I)[psel].cpu().numpy()
+    gsh = ws[L["h_scale"]:L["h_scale"] + 4 * P].view(torch.float32)[psel].cpu().numpy()
+    rhq, rsh = hq[valid], sh[valid]
+    same = float((ghq == rhq).mean())
+    step = int(np.abs(e4m3_ordinal(ghq) - e4m3_ordinal(rhq)).max())
+    srel = float(np.abs(gsh.astype(np.float64) / rsh - 1.0).max())
+    vg, vr = e4m3_values()[ghq], e4m3_values()[rhq]
+    ga, ra = vg * gsh[:, None], vr * rsh[:, None]
+    amax = 448.0 * rsh.astype(np.float64)[:, None]
+    allowed = np.maximum(e4m3_spacing(vg), e4m3_spacing(vr)) * rsh[:, None] * (1 + 1e-6) + 2.0 ** -11 * amax
+    dev = np.abs(ga - ra)
+    cos = float((ga * ra).sum() / max(np.linalg.norm(ga) * np.linalg.norm(ra), 1e-300))
+    log(f"  {what} h codes: {ghq.shape[0]} pair rows, {same:.5f} equal, max code step {step}, "
+        f"max |diff|/row amax {float((dev / amax).max()):.2e}, max scale rel diff {srel:.2e}, "
+        f"dequantised cosine {cos:.7f}")
+    assert same >= 0.99, f"{what}: intermediate codes equal {same}"
+    assert np.all(dev <= allowed), f"{what}: intermediate value beyond one step + 2^-11 amax"
+    assert srel <= 1e-3, f"{what}: intermediate scales"
 
 
 SMALL = [
@@ -58,12 +137,7 @@ def test_small_shapes_all_outputs(lib, E, H, I, k, T, p_drop, dtype):
         ref = oracle_rows(x, ids, w, W, dtype)
     else:
         ref, (xq, sx, hq, sh) = oracle_rows(x, ids, w, W, dtype, want_quant=True)
-        L = lib.moe_workspace_layout(T, k, E, H, I, "fp8")
-        wsc = ws.cpu()
-        gxq = wsc[L["xq"]:L["xq"] + T * H].view(T, H).numpy()
-        gsx = wsc[L["x_scale"]:L["x_scale"] + 4 * T].view(torch.float32).numpy()
-        assert np.array_equal(gxq, xq), "x e4m3 codes"
-        assert np.array_equal(gsx, sx), "x scales"
+        check_fp8_quant(lib, T, k, E, H, I, ws, routing, ids, list(range(T)), xq, sx, hq, sh, "small")
     check_tol(out64(out), ref, dtype, "out")
 
 
@@ -159,6 +233,38 @@ def test_stream_shapes_all_outputs(lib, E, H, I, k, T, p_drop, hot, mb, dtype):
         assert lib.read_routing(routing, T, k, E, H, I, dtype)["num_tasks"] > E
     ref = oracle_rows(x, ids, w, W, dtype)
     check_tol(out64(out), ref, dtype, "out")
+
+
+# bf16 layers with 9 to 16 rows per expert and H >= 3072: register streaming
+# on 32-row tiles with four weight blocks per item (two gate and two up
+# blocks, or 64 down columns): ragged second row blocks, dropped pairs, a hot
+# expert with several tiles, and the down reduction of I = 640 (one or two
+# waves per item).
+FOUR_BLOCK = [
+    # E, H, I, k, T, p_drop, hot expert 0 in every token's first slot
+    (8, 3072, 256, 2, 64, 0.05, False),
+    (8, 3072, 256, 2, 64, 0.05, True),
+    (16, 3584, 640, 4, 50, 0.02, False),
+]
+
+
+@pytest.mark.parametrize("E,H,I,k,T,p_drop,hot", FOUR_BLOCK)
+def test_stream_four_block_bf16_all_outputs(lib, E, H, I, k, T, p_drop, hot):
+    L = lib.moe_workspace_layout(T, k, E, H, I, "bf16")
+    R = lib.moe_routing_layout(T, k, E, H, I, "bf16")
+    log(f"four-block stream bf16 E={E} H={H} I={I} k={k} T={T} hot={hot}")
+    assert L["tiling"] == 0 and R["block_m"] == 32
+    wl = custom_workload(E, H, I, k, dtype="bf16", seed=E + H + I + 3)
+    W = device_weights(wl)
+    x, _, _ = make_tokens(wl, T, seed=T + 35)
+    ids = random_ids(T, k, E, seed=T + 36, p_drop=p_drop)
+    if hot:
+        ids = _hot_first_slot(ids)
+    w = random_weights_w(T, k, seed=T + 37)
+    out, routing, _ = run_gpu(lib, x, ids, w, W, "bf16")
+    if hot:
+        assert lib.read_routing(routing, T, k, E, H, I, "bf16")["num_tasks"] > E
+    check_tol(out64(out), oracle_rows(x, ids, w, W, "bf16"), "bf16", "out")
 
 
 # One token (decode): k from 1 to 16, odd fp8 step counts, dropped pairs, a
@@ -262,20 +368,50 @@ def workload_weights(name):
 
 FULL = [(name, T) for name in ("mixtral", "qwen3", "qwen2", "dsv3", "dsv3b", "dsv3mx", "dsv3i8", "mixtral4", "mixtral8") for T in WORKLOADS[name].Ts]
 
+# Whole-layer oracle cost (multiply-adds, 3*H*I per pair) up to which every
+# token of a full-size case is compared: the fp64 oracle runs about 2e10
+# multiply-adds a second on 16 host threads, so this is a few seconds.
+FULL_COMPARE_MACS = 1.2e11
+
+
+def full_size_rows(lib, wl, T, routing, dtype):
+    """Tokens compared at full size: all of them when the oracle is cheap,
+    else a seeded 256-token subset (always t = 0 and t = T-1) plus every token
+    of the first two row tiles of the most loaded expert (the hot expert of
+    the Qwen2-57B routing, or the fullest tile of a uniform one)."""
+    k = wl.k
+    if T * k * 3.0 * wl.H * wl.I <= FULL_COMPARE_MACS:
+        return list(range(T)), "all tokens"
+    rows = set(sample_rows(T, 256, seed=T))
+    R = lib.read_routing(routing, T, k, wl.E, wl.H, wl.I, dtype)
+    off = R["offsets"].numpy().astype(np.int64)
+    counts = off[1:] - off[:-1]
+    e = int(np.argmax(counts))
+    n = int(min(counts[e], 2 * R["block_m"]))
+    hot = (R["sorted"].numpy()[off[e]:off[e] + n] // k).tolist()
+    rows |= set(hot)
+    return sorted(rows), (f"subset: {len(rows)} of {T} tokens (256 seeded incl. first and last, "
+                          f"+ the {n} rows of expert {e}'s first two {R['block_m']}-row tiles)")
+
 
 @pytest.mark.parametrize("name,T", FULL)
-def test_full_size_sampled(lib, name, T):
+def test_full_size_parity(lib, name, T):
     wl = WORKLOADS[name]
     dtype = path_dtype(wl)
-    log(f"full {name} T={T} {dtype}")
     Wp, Wc = workload_weights(name)
     x, ids, w = make_tokens(wl, T)
-    out, _, ws = run_gpu(lib, x, ids, w, None, dtype, packed=Wp)
-    rows = sample_rows(T, 6 if wl.I * wl.H > 2 ** 25 else 12, seed=T)
-    ref = oracle_rows(x, ids, w, Wc, dtype, rows=rows)
+    out, routing, ws = run_gpu(lib, x, ids, w, None, dtype, packed=Wp)
+    rows, how = full_size_rows(lib, wl, T, routing, dtype)
+    log(f"full {name} T={T} {dtype}: {how}")
+    if dtype == "fp8":
+        ref, (xq, sx, hq, sh) = oracle_rows(x, ids, w, Wc, dtype, rows=rows, want_quant=True)
+    else:
+        ref = oracle_rows(x, ids, w, Wc, dtype, rows=rows)
     check_tol(out64(out)[rows], ref, dtype, f"{name} T={T} rows={len(rows)}")
-    o = out.float()
-    assert torch.isfinite(o).all()
+    assert torch.isfinite(out.float()).all()
+    if dtype == "fp8":
+        check_fp8_quant(lib, T, wl.k, wl.E, wl.H, wl.I, ws, routing, ids, rows, xq, sx, hq, sh,
+                        f"{name} T={T}")
 
 
 def test_deterministic_and_permutation_equivariant(lib):
@@ -329,6 +465,7 @@ def test_empty_batch_is_a_no_op(lib):
 
 @pytest.mark.parametrize("E,H,I,k,T,dtype", [
     (16, 256, 192, 4, 33, "bf16"),      # register streaming
+    (8, 3072, 256, 2, 64, "bf16"),      # register streaming, 32-row tiles, four weight blocks per item
     (16, 256, 192, 4, 1, "bf16"),       # one token
     (16, 256, 192, 4, 1, "fp8"),
     (32, 512, 256, 4, 256, "bf16"),     # strips
@@ -418,7 +555,7 @@ def test_pack_weights_is_the_documented_permutation(lib, dtype, E, rows, cols):
     else:
         w = torch.randint(0, 256, (E, rows, cols), generator=g, dtype=torch.uint8)
         raw = w
-    packed = lib.moe_pack_weights(w.cuda(), dtype)
+    packed = lib.moe_pack_weights(w.cuda(), dtype).tensor
     torch.cuda.synchronize()
     got = packed.cpu().contiguous().view(torch.uint8).reshape(-1).numpy()
     # reference: chunk (e, row block, 64-byte step) of 1 KiB; piece l = row l%16, bytes 16*(l//16)
