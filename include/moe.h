@@ -323,6 +323,28 @@ int moe_forward_fp8(const void *x, const float *topk_w, const void *routing,
                     int T, int k, int E, int H, int I,
                     void *workspace, size_t workspace_bytes, void *out, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the fp8
+ * w8a8 forward of moe_forward_fp8, same arguments and results, without the
+ * workspace argument.  Its workspace is a fixed array in device memory that
+ * the library holds on every GPU it runs on until the process ends,
+ * MOE_STATIC_WORKSPACE_BYTES (64 MiB) per GPU: enough for decode and small
+ * batches (moe_workspace_layout().total_bytes tells; DeepSeek-V3-shaped
+ * layers up to T = 128 tokens).  A call whose workspace would be larger
+ * returns MOE_ERR_BUFFER_TOO_SMALL before anything is enqueued.  Nothing is
+ * allocated or freed: the first call on a device looks up the array's
+ * device address (hipGetSymbolAddress) and keeps it, so make that first
+ * call outside graph capture.  Every call on a GPU shares that GPU's
+ * array, which keeps the last call's contents (no part of it needs to start
+ * at any value): calls that overlap on one GPU, on different streams or
+ * threads, race.  The intermediate codes and scales are not readable by
+ * the caller (they are on moe_forward_fp8's workspace). */
+#define MOE_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+int moe_forward_fp8_noalloc(const void *x, const float *topk_w, const void *routing,
+                            const moe_packed_weights_t *w1, const float *w1_scale,
+                            const moe_packed_weights_t *w2, const float *w2_scale,
+                            int T, int k, int E, int H, int I, void *out, void *stream);
+
 /* MXFP8 (SGLang tuning guide, block shapes: gfx95 devices keep MXFP8's
  * [1, 32] blocks).  Routing build: as moe_build_routing_bf16, with the
  * tile height of the MXFP8 forward.  Forward: as moe_forward_fp8 except the

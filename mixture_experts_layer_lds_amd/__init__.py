@@ -111,7 +111,7 @@ EXPORTS = ("moe_status_string", "moe_pack_weights", "moe_describe_packed_weights
            "moe_forward_fp8", "moe_forward_mxfp8", "moe_forward_int8", "moe_forward_int4",
            "moe_build_routing_fp8_block", "moe_forward_fp8_block",
            "moe_build_routing_int8_w8a16", "moe_forward_int8_w8a16", "moe_set_stage_events", "moe_device_cu_count",
-           "moe_stream_read")
+           "moe_stream_read", "moe_forward_fp8_noalloc")
 
 
 def _load():
@@ -164,6 +164,8 @@ def _load():
     L.moe_set_stage_events.argtypes = [ctypes.POINTER(P), i]
     L.moe_device_cu_count.restype = i
     L.moe_device_cu_count.argtypes = []
+    L.moe_forward_fp8_noalloc.restype = i
+    L.moe_forward_fp8_noalloc.argtypes = [P, P, P, D, P, D, P, i, i, i, i, i, P, P]
     L.moe_stream_read.restype = i
     L.moe_stream_read.argtypes = [P, sz, P, sz, P]
     return L
@@ -446,6 +448,30 @@ def moe_forward_fp8(x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, o
     _check("moe_forward_fp8", _lib.moe_forward_fp8(
         _ptr(x), _ptr(topk_w), _ptr(routing), _desc("w1", w1), _ptr(w1_scale), _desc("w2", w2), _ptr(w2_scale),
         T, k, E, H, I, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+STATIC_WORKSPACE_BYTES = 64 << 20
+
+
+def moe_forward_fp8_noalloc(x, topk_w, routing, w1, w1_scale, w2, w2_scale, out, stream=None):
+    """moe_forward_fp8 on the library's fixed per-GPU workspace (no workspace
+    argument, nothing allocated); sizes whose workspace exceeds
+    STATIC_WORKSPACE_BYTES raise MoeError (MOE_ERR_BUFFER_TOO_SMALL)."""
+    T, H = x.shape
+    k = topk_w.shape[1]
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    _check_tensor("x", x, torch.bfloat16, (T, H))
+    _check_tensor("topk_w", topk_w, torch.float32, (T, k))
+    _check_tensor("w1", w1, torch.uint8, (E, 2 * I, H))
+    _check_tensor("w1_scale", w1_scale, torch.float32, (E, 2 * I))
+    _check_tensor("w2", w2, torch.uint8, (E, H, I))
+    _check_tensor("w2_scale", w2_scale, torch.float32, (E, H))
+    _check_tensor("out", out, torch.bfloat16, (T, H))
+    _check("moe_forward_fp8_noalloc", _lib.moe_forward_fp8_noalloc(
+        _ptr(x), _ptr(topk_w), _ptr(routing), _desc("w1", w1), _ptr(w1_scale), _desc("w2", w2),
+        _ptr(w2_scale), T, k, E, H, I, _ptr(out), _stream(stream)))
     return out
 
 

@@ -11,6 +11,11 @@
 
 #include "moe_common.h"
 
+// Workspace of moe_forward_fp8_noalloc: one array per GPU, held until the
+// process ends.  In host code its name is only a stand-in for the device
+// symbol; the device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_WORKSPACE_BYTES];
+
 namespace {
 
 
@@ -423,6 +428,23 @@ int cu_count(int* out) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       return MOE_ERR_HIP;
     cache[dev] = n;
+  }
+  *out = cache[dev];
+  return MOE_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* cache[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cache[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    cache[dev] = p;
   }
   *out = cache[dev];
   return MOE_OK;
@@ -1402,6 +1424,21 @@ int moe_forward_fp8(const void* x, const float* topk_w, const void* routing, con
   if (rc != MOE_OK || T == 0) return rc;
   return forward(MOE_DTYPE_FP8_W8A8, x, topk_w, routing, packed_data(w1), w1_scale, packed_data(w2), w2_scale, T, k,
                  E, H, I, workspace, workspace_bytes, out, stream);
+}
+
+int moe_forward_fp8_noalloc(const void* x, const float* topk_w, const void* routing,
+                            const moe_packed_weights_t* w1, const float* w1_scale,
+                            const moe_packed_weights_t* w2, const float* w2_scale, int T, int k, int E,
+                            int H, int I, void* out, void* stream) {
+  int rc = check_packed(MOE_DTYPE_FP8_W8A8, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  moe_workspace_layout_t W;
+  workspace_layout(MOE_DTYPE_FP8_W8A8, T, k, H, I, make_plan(MOE_DTYPE_FP8_W8A8, T, k, E, H, I), &W);
+  if (W.total_bytes > MOE_STATIC_WORKSPACE_BYTES) return MOE_ERR_BUFFER_TOO_SMALL;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws)) != MOE_OK) return rc;
+  return forward(MOE_DTYPE_FP8_W8A8, x, topk_w, routing, packed_data(w1), w1_scale, packed_data(w2),
+                 w2_scale, T, k, E, H, I, ws, MOE_STATIC_WORKSPACE_BYTES, out, stream);
 }
 
 int moe_set_stage_events(void* const* events, int n) {
