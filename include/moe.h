@@ -134,21 +134,22 @@ typedef struct {
  *  2 strips (token rows staged in LDS, weights streamed to registers; a few
  *    dozen to ~80 rows per expert): the GEMMs may split their reduction into
  *    split_k1 / split_k2 slices whose fp32 partial sums the next kernel adds
- *    in ascending slice order; on bf16 with split_k1 == 1 the gate-up
- *    epilogue forms SiLU(gate)*up; strips with split_k2 == 1 write bf16 down
- *    rows;
+ *    in ascending slice order; with split_k1 == 1 the gate-up epilogue
+ *    forms SiLU(gate)*up (fp8: in fp32, then requantised); strips with
+ *    split_k2 == 1 write bf16 down rows;
  *  1 LDS tiles of both operands (many rows per expert): no split;
  *    SiLU(gate)*up is formed in the gate-up GEMM's epilogue and the down rows
  *    are bf16. */
 typedef struct {
     size_t xq;          /* fp8: uint8 [T][H]   per-token e4m3 codes of x */
     size_t x_scale;     /* fp8: fp32  [T]      per-token scales of x */
-    size_t x_scale_rows;/* fp8, tiling 0: fp32 [P + 16] the token's scale at each sorted row */
-    size_t g;           /* tiling 2: fp32 [split_k1][P][2I] gate-up partial
-                           sums (weight scales only on fp8; unused on bf16
-                           with split_k1 == 1, where the gate-up epilogue
-                           forms h); tilings 0, 1 + fp8: fp32 [P][I]
-                           SiLU(gate)*up before requantisation */
+    size_t x_scale_rows;/* fp8, tiling 0, and tiling 2 with split_k1 == 1:
+                           fp32 [P + 16] the token's scale at each sorted row */
+    size_t g;           /* tiling 2 with split_k1 > 1: fp32 [split_k1][P][2I]
+                           gate-up partial sums (weight scales only on fp8);
+                           fp8 otherwise: fp32 [P][I] SiLU(gate)*up before
+                           requantisation; unused on bf16 outside tiling 2
+                           with split_k1 > 1 */
     size_t h;           /* bf16 [P][I] SiLU(gate)*up (bf16), or uint8 e4m3 codes [P][I] (fp8) */
     size_t h_scale;     /* fp8: fp32  [P]      per-row scales of h */
     size_t y;           /* tiling 2 with split_k2 > 1: fp32 [split_k2][P][H]

@@ -74,6 +74,14 @@ __device__ __forceinline__ int load1_scalar(const void* p) {
   return v;
 }
 
+// Lane l receives v[j] for its own j in [0, 16).
+__device__ __forceinline__ int pick16(const i32x16_t& v, int j) {
+  int r = v[0];
+#pragma unroll
+  for (int i = 1; i < 16; i++) r = (j == i) ? v[i] : r;
+  return r;
+}
+
 // Lane l receives v[l % 16].
 __device__ __forceinline__ int spread16(const i32x16_t& v, int lane) {
   const int j = lane & 15;

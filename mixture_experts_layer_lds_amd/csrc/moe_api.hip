@@ -401,9 +401,11 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
   W->xq = fp8 ? take((size_t)T * H) : kNone;
   W->x_scale = fp8 ? take(4 * (size_t)T) : kNone;
   // per-sorted-row x scales, read 16 at a time by the streaming epilogue
-  W->x_scale_rows = fp8 && p.tiling == kStreaming ? take(4 * (P + 16)) : kNone;
-  if (p.tiling == kStrips)   // fp32 gate-up partial sums (none when the bf16 epilogue forms h)
-    W->g = !fp8 && p.split1 == 1 ? kNone : take(4 * (size_t)p.split1 * P * 2 * I);
+  // and the strips' fused one
+  const bool strip_act = p.tiling == kStrips && p.split1 == 1;
+  W->x_scale_rows = fp8 && (p.tiling == kStreaming || strip_act) ? take(4 * (P + 16)) : kNone;
+  if (p.tiling == kStrips && !strip_act)   // fp32 gate-up partial sums
+    W->g = take(4 * (size_t)p.split1 * P * 2 * I);
   else
     W->g = fp8 ? take(4 * P * I) : kNone;               // fp32 SiLU(gate)*up before requant
   W->h = take(P * I * (fp8 ? 1 : 2));
@@ -947,21 +949,22 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
   if (fp8) {
     StageScope st(s, 0);
     // the row amax slots are cleared here for the epilogue that folds into
-    // them (LDS tiles; the streaming requantisation finds the amax itself)
+    // them (LDS tiles; the streaming and strip requantisation finds the amax
+    // itself); the per-sorted-row x scales serve the epilogues that apply them
     e = moe_host::launch_quant_rows_bf16(
         static_cast<const uint16_t*>(x), T, H, xq, x_scale,
         p.tiling == kLdsTiles ? h_scale : nullptr,
-        k, R.pair_pos, p.tiling == kStreaming ? reinterpret_cast<float*>(ws + W.x_scale_rows) : nullptr,
+        k, R.pair_pos, W.x_scale_rows != kNone ? reinterpret_cast<float*>(ws + W.x_scale_rows) : nullptr,
         s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (p.tiling == kStrips) {
     float* g = W.g == kNone ? nullptr : reinterpret_cast<float*>(ws + W.g);
     const bool y_bf16 = p.split2 == 1;
-    // bf16 with one gate-up slice: SiLU-and-mul in the GEMM's epilogue;
-    // else fp32 partial sums that the activation kernel adds (and, on fp8,
-    // requantises).
-    const bool fuse_act = p.split1 == 1 && !fp8;
+    // One gate-up slice: SiLU-and-mul in the GEMM's epilogue (fp8: fp32 h,
+    // then the requantisation pass); else fp32 partial sums that the
+    // activation kernel adds (and, on fp8, requantises).
+    const bool fuse_act = p.split1 == 1;
     {
       StageScope st(s, 1);
       moe_host::StripArgs a{};
@@ -971,7 +974,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
       a.sorted_pairs = R.sorted_pairs;
       a.header = R.header;
       a.tasks = R.tasks;
-      a.c = fuse_act ? h : static_cast<void*>(g);
+      a.c = fuse_act && !fp8 ? h : static_cast<void*>(g);
       a.K = H;
       a.N = 2 * I;
       a.P = P;
@@ -980,8 +983,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
       a.split = p.split1;
       a.out_bf16 = 0;
       a.act = fuse_act ? 1 : 0;
-      a.x_scale = x_scale;
-      a.row_amax = h_scale;
+      a.x_scale_rows = fuse_act && fp8 ? reinterpret_cast<const float*>(ws + W.x_scale_rows) : nullptr;
       e = moe_host::launch_strip_gemm(a, true, fp8, p.mb, p.ks1, p.nbuf1, cus, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
@@ -989,6 +991,11 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
       StageScope st(s, 2);
       e = moe_host::launch_act(g, p.split1, P, I, R.expert_offsets, E, fp8, x_scale,
                                R.sorted_pairs, k, h, h_scale, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    } else if (fp8) {
+      StageScope st(s, 2);
+      e = moe_host::launch_requant_rows(g, P, I, R.expert_offsets, E, static_cast<uint8_t*>(h), h_scale,
+                                        true, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
     {

@@ -14,6 +14,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef long i64x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 constexpr int kMaxPairs = 65536;
@@ -82,11 +83,16 @@ __device__ __forceinline__ void e4m3_row_scales(float amax, float* scale, float*
 // is exactly the memory order of the 128 bytes.
 __device__ __forceinline__ void mfma_fp8_k128(f32x4& acc, const u32x4& a0, const u32x4& a1,
                                               const u32x4& b0, const u32x4& b1) {
-  typedef int i32x8 __attribute__((ext_vector_type(8)));
   const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                    (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
   const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
                    (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+}
+
+// As mfma_fp8_k128, with each operand's two 16-byte fragments already in
+// one 8-dword tuple (first step in the low half).
+__device__ __forceinline__ void mfma_fp8_unit(f32x4& acc, const i32x8& a, const i32x8& b) {
   acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
 }
 
@@ -96,7 +102,6 @@ __device__ __forceinline__ void mfma_fp8_k128(f32x4& acc, const u32x4& a0, const
 // K 32*g.. of the unit).
 __device__ __forceinline__ void mfma_mx_k128(f32x4& acc, const u32x4& a0, const u32x4& a1,
                                              const u32x4& b0, const u32x4& b1, int sa, int sb) {
-  typedef int i32x8 __attribute__((ext_vector_type(8)));
   const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                    (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
   const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
@@ -250,11 +255,9 @@ struct StripArgs {
   int out_bf16;                 // 1: bf16 rows (split == 1)
   // gate-up with one K slice: a wave's two 16-row weight blocks are a gate
   // block and the matching up block, and c receives h = SiLU(gate) * up,
-  // [P][N/2]: bf16, or on fp8 fp32 with each row's amax folded into
-  // row_amax (pre-cleared) and x's per-token scales applied
+  // [P][N/2]: bf16, or on fp8 fp32 with the weight and x scales applied
   int act;
-  const float* x_scale;         // fp8 act: [T] per-token scales of x
-  float* row_amax;              // fp8 act: [P]
+  const float* x_scale_rows;    // fp8 act: x scale of each sorted row [P + 16]
 };
 
 // (mb, ks, nbuf) = 16-row blocks per tile, 64-byte K steps per stage, stages in flight.

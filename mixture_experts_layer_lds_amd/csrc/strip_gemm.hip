@@ -27,22 +27,26 @@
 //
 // Output: fp32 partial sums c[s][P][N], bf16 rows c[P][N] (one slice,
 // out_bf16), or on gate-up with one slice h = SiLU(gate) * up (act: the
-// wave's two blocks are a gate block and its up block; fp8 writes fp32 h and
-// each row's amax for the requantisation).  On fp8 the per-column weight
-// scale is applied here, and the per-row activation scale by the consumer
-// (SiLU-and-mul, the top-k reduction) or, with act, here.
+// wave's two blocks are a gate block and its up block; fp8 writes fp32 h for
+// the requantisation).  On fp8 the per-column weight scale is applied here,
+// and the per-row activation scale by the consumer (SiLU-and-mul, the top-k
+// reduction) or, with act, here.
 #include <type_traits>
 
 #include "lds_dma.h"
 
 namespace moe {
 
-constexpr int kStripWaves = 8;
-constexpr int kStripThreads = kStripWaves * 64;
+// A strip is 256 output columns: 16 * NSUB columns per wave, 16 / NSUB
+// waves per workgroup (8 waves of two column blocks).
+template <int NSUB>
+constexpr int strip_waves() {
+  return 16 / NSUB;
+}
 
 template <int MB, int KS, int NSUB>
 struct StripItem {
-  static constexpr int NA = MB * KS / kStripWaves;   // token chunks this wave copies per stage
+  static constexpr int NA = MB * KS / strip_waves<NSUB>();   // token chunks this wave copies per stage
   int row_begin, rows, s;
   int col;                     // first output column of this wave (of h when fusing SiLU-and-mul)
   const char* a[NA];           // this lane's token sources (K step and lane offsets applied)
@@ -61,7 +65,8 @@ template <int MB, int KS, int NSUB, bool GATHER, bool FP8>
 __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::StripArgs& g, int item,
                                                               int n_strips, int nk, size_t row_bytes,
                                                               int nsteps, int wave, int lane) {
-  constexpr int kCols = kStripWaves * NSUB * 16;
+  constexpr int W = strip_waves<NSUB>();
+  constexpr int kCols = W * NSUB * 16;
   StripItem<MB, KS, NSUB> it;
   const int s = item % g.split;
   const int rest = item / g.split;
@@ -72,25 +77,27 @@ __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::St
   it.row_begin = task.row_begin;
   it.rows = task.rows;
   it.s = s;
-  it.col = g.act ? (nt * kStripWaves + wave) * 16 : nt * kCols + wave * (NSUB * 16);
+  it.col = g.act ? (nt * W + wave) * 16 : nt * kCols + wave * (NSUB * 16);
   const int step0 = s * nk * KS;
   const int lrow = lane & 15;
 #pragma unroll
   for (int i = 0; i < StripItem<MB, KS, NSUB>::NA; i++) {
     // chunk c = 16-row block c / KS, K step c % KS of every stage
-    const int c = wave + kStripWaves * i;
+    const int c = wave + W * i;
     const int rb = c / KS, st = c % KS;
-    // row blocks past the tile, and rows past it inside the last block,
-    // re-read the tile's first row: always a valid address, never stored
-    const int rb_ld = rb * 16 < task.rows ? rb : 0;
-    const bool in_tile = rb_ld * 16 + lrow < task.rows;
+    // Row blocks past the tile, and rows past it inside the last block,
+    // re-read the tile's first row: always a valid address, never stored.
+    // A whole block past the tile thus reads one 64-byte line per step
+    // (every lane the same row), not 16 rows.
+    const bool blk_in = rb * 16 < task.rows;
+    const bool in_tile = blk_in && rb * 16 + lrow < task.rows;
     int arow;
     if constexpr (GATHER) {
-      const i32x16_t sp = load16_scalar(g.sorted_pairs + task.row_begin + rb_ld * 16);
+      const i32x16_t sp = load16_scalar(g.sorted_pairs + task.row_begin + (blk_in ? rb * 16 : 0));
       const int p = in_tile ? spread16(sp, lane) : sp[0];
       arow = p / g.topk;
     } else {
-      arow = task.row_begin + (in_tile ? rb_ld * 16 + lrow : 0);
+      arow = task.row_begin + (in_tile ? rb * 16 + lrow : 0);
     }
     it.a[i] = static_cast<const char*>(g.a) + (size_t)arow * row_bytes + (size_t)(step0 + st) * 64 +
               16 * (lane >> 4);
@@ -122,15 +129,38 @@ __device__ __forceinline__ void strip_mfma(f32x4& acc, const u32x4& a, const u32
   }
 }
 
+// One register stage of a wave's weights: KS 64-byte K steps of NSUB column
+// blocks.  On fp8 with whole 128-value units (PAIRS) two consecutive steps
+// of a block share one 8-dword tuple, the operand of the 128-value MFMA, so
+// each load lands in its half of the operand and nothing is copied to
+// assemble it.
+template <int KS, int NSUB, bool PAIRS>
+struct WeightStage {
+  u32x4 r[KS][NSUB];
+  __device__ __forceinline__ void set(int u, int q, const u32x4& v) { r[u][q] = v; }
+  __device__ __forceinline__ const u32x4& step(int u, int q) const { return r[u][q]; }
+};
+
+template <int KS, int NSUB>
+struct WeightStage<KS, NSUB, true> {
+  i32x8 r[KS / 2][NSUB];
+  __device__ __forceinline__ void set(int u, int q, const u32x4& v) {
+    if (u & 1) r[u >> 1][q].hi = __builtin_bit_cast(i32x4_t, v);
+    else r[u >> 1][q].lo = __builtin_bit_cast(i32x4_t, v);
+  }
+  __device__ __forceinline__ const i32x8& unit(int u2, int q) const { return r[u2][q]; }
+};
+
 template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8>
-__global__ void __launch_bounds__(kStripThreads, 1)
+__global__ void __launch_bounds__(strip_waves<NSUB>() * 64, 1)
 strip_gemm_kernel(moe_host::StripArgs g) {
   using It = StripItem<MB, KS, NSUB>;
   constexpr int NA = It::NA;
   constexpr int PER = NA + KS * NSUB;   // vector-memory operations per wave per stage
   constexpr int NST = NBUF + 1;         // LDS ring slots
   constexpr int SLOT = MB * KS * 1024;
-  static_assert(NA >= 1 && NA * kStripWaves == MB * KS, "token chunks split evenly over waves");
+  constexpr int W = strip_waves<NSUB>();
+  static_assert(NA >= 1 && NA * W == MB * KS, "token chunks split evenly over waves");
   static_assert(NBUF >= 2, "ring depth");
   static_assert((NBUF - 1) * PER < 64, "vmcnt range");
   extern __shared__ __attribute__((aligned(1024))) char lds[];
@@ -139,7 +169,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
-  const int n_strips = g.N / (kStripWaves * NSUB * 16);
+  const int n_strips = g.N / (W * NSUB * 16);
   const int total = num_tasks * n_strips * g.split;
   const size_t row_bytes = (size_t)g.K * (FP8 ? 1 : 2);
   const int nsteps = (int)(row_bytes / 64);
@@ -179,23 +209,24 @@ strip_gemm_kernel(moe_host::StripArgs g) {
     // (valid addresses, never used), so the wait before each stage is the
     // same count and the compiler's own waits for the weight registers see
     // the same queue on every path.
-    u32x4 bb[NBUF][KS][NSUB];
-    auto issue = [&](bool in_cur, int kt, int fslot, u32x4 (&b)[KS][NSUB]) {
+    constexpr bool PAIRS = FP8 && KS % 2 == 0;
+    WeightStage<KS, NSUB, PAIRS> bb[NBUF];
+    auto issue = [&](bool in_cur, int kt, int fslot, WeightStage<KS, NSUB, PAIRS>& b) {
       char* sb = lds + fslot * SLOT;
   #pragma unroll
       for (int i = 0; i < NA; i++)
         dma16((in_cur ? cur.a[i] : nxt.a[i]) + (size_t)kt * KS * 64,
-              sb + (wave + kStripWaves * i) * 1024);
+              sb + (wave + W * i) * 1024);
       const char* bsrc = in_cur ? cur.b : nxt.b;
   #pragma unroll
       for (int u = 0; u < KS; u++)
   #pragma unroll
         for (int q = 0; q < NSUB; q++)
           if constexpr (NT_B)
-            b[u][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                bsrc + q * bq + ((size_t)kt * KS + u) * 1024));
+            b.set(u, q, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                            bsrc + q * bq + ((size_t)kt * KS + u) * 1024)));
           else
-            b[u][q] = *reinterpret_cast<const u32x4*>(bsrc + q * bq + ((size_t)kt * KS + u) * 1024);
+            b.set(u, q, *reinterpret_cast<const u32x4*>(bsrc + q * bq + ((size_t)kt * KS + u) * 1024));
     };
 
     // The empty asm statements keep each stage's operations together in
@@ -225,17 +256,18 @@ strip_gemm_kernel(moe_host::StripArgs g) {
           wait_vm<(NBUF - 1) * PER>();
           barrier_nofence();
           const char* sb = lds + (fc % NST) * SLOT;
-          if constexpr (FP8 && KS % 2 == 0) {
-            // two K steps per full-rate fp8 instruction
+          if constexpr (PAIRS) {
+            // two K steps per full-rate fp8 instruction, both operands read
+            // into their 8-dword tuples as they are
   #pragma unroll
             for (int st = 0; st < KS; st += 2) {
   #pragma unroll
               for (int m = 0; m < MB; m++) {
-                const u32x4 a0 = *reinterpret_cast<const u32x4*>(sb + (m * KS + st) * 1024 + 16 * lane);
-                const u32x4 a1 = *reinterpret_cast<const u32x4*>(sb + (m * KS + st + 1) * 1024 + 16 * lane);
+                i32x8 a;
+                a.lo = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st) * 1024 + 16 * lane);
+                a.hi = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st + 1) * 1024 + 16 * lane);
   #pragma unroll
-                for (int q = 0; q < NSUB; q++)
-                  mfma_fp8_k128(acc[m][q], a0, a1, bb[u][st][q], bb[u][st + 1][q]);
+                for (int q = 0; q < NSUB; q++) mfma_fp8_unit(acc[m][q], a, bb[u].unit(st >> 1, q));
               }
             }
           } else {
@@ -245,7 +277,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
               for (int m = 0; m < MB; m++) {
                 const u32x4 a = *reinterpret_cast<const u32x4*>(sb + (m * KS + st) * 1024 + 16 * lane);
   #pragma unroll
-                for (int q = 0; q < NSUB; q++) strip_mfma<FP8>(acc[m][q], a, bb[u][st][q]);
+                for (int q = 0; q < NSUB; q++) strip_mfma<FP8>(acc[m][q], a, bb[u].step(st, q));
               }
             }
           }
@@ -259,17 +291,29 @@ strip_gemm_kernel(moe_host::StripArgs g) {
 
       // Epilogue: lane holds column (lane % 16) and rows 4*(lane / 16) + i of
       // each 16 x 16 block.
-      // SiLU-and-mul in this epilogue (bf16 gate-up, one K slice).  Not on
-      // fp8: there the per-row amax would take one atomic per row and 16
-      // columns (measured slower at DeepSeek-V3 T=4096 than the separate
-      // activation kernel).
+      // SiLU-and-mul in this epilogue (gate-up, one K slice): bf16 h, or on
+      // fp8 the fp32 h that the requantisation pass turns into codes (it
+      // finds each row's amax from the row: folding it here would take one
+      // atomic per row and 16 columns).  The fp8 row scales come through
+      // scalar loads, 16 rows at a time, so the epilogue issues no vector
+      // load whose wait would drain the ring.
       bool fused = false;
-      if constexpr (GATHER && NSUB == 2 && !FP8) fused = g.act != 0;
+      if constexpr (GATHER && NSUB == 2) fused = g.act != 0;
       if (fused) {
         // h = SiLU(gate) * up: the wave's gate block and its up block
         const int hn = g.N / 2;
   #pragma unroll
         for (int m = 0; m < MB; m++) {
+          float xs[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+          if constexpr (FP8) {
+            // the block's 16 row scales (rows inside the tile only: the array
+            // has 16 entries past its last row, not MB * 16)
+            if (16 * m < cur.rows) {
+              const i32x16_t sv = load16_scalar(g.x_scale_rows + cur.row_begin + 16 * m);
+  #pragma unroll
+              for (int i = 0; i < 4; i++) xs[i] = __int_as_float(pick16(sv, 4 * lgrp + i));
+            }
+          }
   #pragma unroll
           for (int i = 0; i < 4; i++) {
             const int rr = 16 * m + 4 * lgrp + i;
@@ -277,21 +321,14 @@ strip_gemm_kernel(moe_host::StripArgs g) {
             const size_t r = (size_t)(cur.row_begin + (ok ? rr : 0));
             float gv = acc[m][0][i], uv = acc[m][1][i];
             if constexpr (FP8) {
-              const float xs = g.x_scale[g.sorted_pairs[r] / g.topk];
-              gv = (gv * cur.bs[0]) * xs;
-              uv = (uv * cur.bs[1]) * xs;
+              gv = (gv * cur.bs[0]) * xs[i];
+              uv = (uv * cur.bs[1]) * xs[i];
             }
             const float hv = silu_f32(gv) * uv;
             const int col = cur.col + lrow;
             if (ok) {
               if constexpr (FP8) static_cast<float*>(g.c)[r * hn + col] = hv;
               else static_cast<uint16_t*>(g.c)[r * hn + col] = f32_to_bf16_bits(hv);
-            }
-            if constexpr (FP8) {
-              // row amax over these 16 columns, folded into the row's slot
-              const float mx = max16(ok ? __builtin_fabsf(hv) : 0.0f);
-              if (ok && lrow == 0)
-                atomicMax(reinterpret_cast<unsigned int*>(g.row_amax) + r, __float_as_uint(mx));
             }
           }
         }
@@ -341,7 +378,7 @@ static hipError_t launch_strip_t(const moe_host::StripArgs& a, int grid, hipStre
     attr_set = true;
   }
   hipLaunchKernelGGL((strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8>), dim3(grid),
-                     dim3(kStripThreads), lds_bytes, s, a);
+                     dim3(strip_waves<NSUB>() * 64), lds_bytes, s, a);
   return hipGetLastError();
 }
 

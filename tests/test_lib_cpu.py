@@ -67,11 +67,13 @@ def test_workspace_layout(m):
     assert W["y"] + 2 * P * 7168 <= W["total_bytes"]
     for key in ("xq", "x_scale", "x_scale_rows", "g", "h", "h_scale", "y"):
         assert W[key] % 256 == 0
-    # strips (T=1024): fp32 gate-up partial sums, down rows bf16 or fp32 partials
+    # strips (T=1024): one gate-up slice, so fp32 SiLU(gate)*up and the
+    # per-sorted-row x scales for its epilogue; down rows bf16 or fp32 partials
     S = m.moe_workspace_layout(1024, 8, 256, 7168, 2048, "fp8")
     P = 8192
-    assert S["tiling"] == 2 and S["x_scale_rows"] == 2 ** 64 - 1
-    assert S["h"] >= S["g"] + 4 * S["split_k1"] * P * 4096
+    assert S["tiling"] == 2 and S["split_k1"] == 1
+    assert S["g"] >= S["x_scale_rows"] + 4 * (P + 16)
+    assert S["h"] >= S["g"] + 4 * P * 2048
     ybytes = 2 * P * 7168 if S["split_k2"] == 1 else 4 * S["split_k2"] * P * 7168
     assert S["y"] + ybytes <= S["total_bytes"]
     Wb = m.moe_workspace_layout(16, 8, 256, 7168, 2048, "bf16")
