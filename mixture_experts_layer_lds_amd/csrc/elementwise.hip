@@ -23,8 +23,33 @@ __device__ __forceinline__ float block_max_256(float v, float* s_red) {
   return r;
 }
 
+__device__ __forceinline__ float amax8_bf16(const u32x4& v, float amax) {
+#pragma unroll
+  for (int w = 0; w < 4; w++) {
+    amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_bits_to_f32(v[w] & 0xffffu)));
+    amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_bits_to_f32(v[w] >> 16)));
+  }
+  return amax;
+}
+
+__device__ __forceinline__ u32x2 quant8_bf16(const u32x4& v, float inv) {
+  float f[8];
+#pragma unroll
+  for (int w = 0; w < 4; w++) {
+    f[2 * w] = __fmul_rn(bf16_bits_to_f32(v[w] & 0xffffu), inv);
+    f[2 * w + 1] = __fmul_rn(bf16_bits_to_f32(v[w] >> 16), inv);
+  }
+  u32x2 q;
+  q.x = f32x4_to_e4m3x4_sat(f[0], f[1], f[2], f[3]);
+  q.y = f32x4_to_e4m3x4_sat(f[4], f[5], f[6], f[7]);
+  return q;
+}
+
 // x[T][H] bf16 -> xq[T][H] e4m3 + scale[T]; H % 8 == 0.  With scale_rows,
 // the token's scale is also written at the sorted row of each of its zk pairs.
+// NV > 0: the row is read once into registers (H <= NV * 8 * 256), found
+// its amax and quantised from there; NV == 0: read twice (any H).
+template <int NV>
 __global__ void __launch_bounds__(kRowThreads)
 quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restrict__ xq,
                        float* __restrict__ scale, float* __restrict__ zero_rows, int zk,
@@ -33,32 +58,30 @@ quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restric
   const int t = blockIdx.x;
   if (zero_rows && threadIdx.x < zk) zero_rows[(size_t)t * zk + threadIdx.x] = 0.0f;
   const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
-  const int nvec = H / 8;
-  float amax = 0.0f;
-  for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
-    const u32x4 v = row[i];
-#pragma unroll
-    for (int w = 0; w < 4; w++) {
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_bits_to_f32(v[w] & 0xffffu)));
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_bits_to_f32(v[w] >> 16)));
-    }
-  }
-  amax = block_max_256(amax, s_red);
-  float sc, inv;
-  e4m3_row_scales(amax, &sc, &inv);
   u32x2* out = reinterpret_cast<u32x2*>(xq + (size_t)t * H);
-  for (int i = threadIdx.x; i < nvec; i += kRowThreads) {
-    const u32x4 v = row[i];
-    float f[8];
+  const int nvec = H / 8;
+  float amax = 0.0f, sc, inv;
+  if constexpr (NV > 0) {
+    u32x4 v[NV];
 #pragma unroll
-    for (int w = 0; w < 4; w++) {
-      f[2 * w] = __fmul_rn(bf16_bits_to_f32(v[w] & 0xffffu), inv);
-      f[2 * w + 1] = __fmul_rn(bf16_bits_to_f32(v[w] >> 16), inv);
+    for (int j = 0; j < NV; j++) {
+      const int i = threadIdx.x + j * kRowThreads;
+      v[j] = i < nvec ? row[i] : u32x4{0u, 0u, 0u, 0u};
     }
-    u32x2 q;
-    q.x = f32x4_to_e4m3x4_sat(f[0], f[1], f[2], f[3]);
-    q.y = f32x4_to_e4m3x4_sat(f[4], f[5], f[6], f[7]);
-    out[i] = q;
+#pragma unroll
+    for (int j = 0; j < NV; j++) amax = amax8_bf16(v[j], amax);
+    amax = block_max_256(amax, s_red);
+    e4m3_row_scales(amax, &sc, &inv);
+#pragma unroll
+    for (int j = 0; j < NV; j++) {
+      const int i = threadIdx.x + j * kRowThreads;
+      if (i < nvec) out[i] = quant8_bf16(v[j], inv);
+    }
+  } else {
+    for (int i = threadIdx.x; i < nvec; i += kRowThreads) amax = amax8_bf16(row[i], amax);
+    amax = block_max_256(amax, s_red);
+    e4m3_row_scales(amax, &sc, &inv);
+    for (int i = threadIdx.x; i < nvec; i += kRowThreads) out[i] = quant8_bf16(row[i], inv);
   }
   if (threadIdx.x == 0) scale[t] = sc;
   if (scale_rows && threadIdx.x < zk) scale_rows[pair_pos[(size_t)t * zk + threadIdx.x]] = sc;
@@ -244,8 +267,16 @@ namespace moe_host {
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* scale,
                                   float* zero_rows, int zk, const int32_t* pair_pos,
                                   float* scale_rows, hipStream_t s) {
-  hipLaunchKernelGGL(moe::quant_rows_bf16_kernel, dim3(T), dim3(moe::kRowThreads), 0, s, x, H,
-                     xq, scale, zero_rows, zk, pair_pos, scale_rows);
+  const int per = (H / 8 + moe::kRowThreads - 1) / moe::kRowThreads;   // 16-byte vectors per thread
+#define MOE_QUANT_NV(NVv)                                                                               \
+  hipLaunchKernelGGL(moe::quant_rows_bf16_kernel<NVv>, dim3(T), dim3(moe::kRowThreads), 0, s, x, H, xq, \
+                     scale, zero_rows, zk, pair_pos, scale_rows)
+  if (per <= 1) MOE_QUANT_NV(1);
+  else if (per <= 2) MOE_QUANT_NV(2);
+  else if (per <= 4) MOE_QUANT_NV(4);
+  else if (per <= 8) MOE_QUANT_NV(8);
+  else MOE_QUANT_NV(0);
+#undef MOE_QUANT_NV
   return hipGetLastError();
 }
 

@@ -124,6 +124,20 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Max of v over a workgroup of NT threads (NT / 64 <= 8 waves), returned to
+// every thread.
+template <int NT>
+__device__ float block_max_f32(float v) {
+  __shared__ float s_max[NT / 64];
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = s_max[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; w++) r = __builtin_fmaxf(r, s_max[w]);
+  return r;
+}
+
 // Largest |v| of a row of n fp32 values (n % 4 == 0) by a workgroup of NT
 // threads (NT / 64 <= 8 waves), returned to every thread.
 template <int NT>

@@ -557,26 +557,57 @@ static hipError_t launch_dma_shape(const moe_host::TiledArgs& a, bool gateup, bo
 // row amax accumulated in h_scale[r] by the GEMM epilogue, or, with
 // find_amax, found here from the row itself; h_scale[r] then holds the row
 // scale.
+// NV > 0: the row is read once into registers (I <= NV * 4 * 256), its amax
+// found (find_amax) and the codes written from there; NV == 0: read twice.
+template <int NV>
 __global__ void __launch_bounds__(256)
 requant_rows_kernel(const float* __restrict__ h32, int I, const int32_t* __restrict__ expert_offsets,
                     int E, uint8_t* __restrict__ hq, float* __restrict__ h_scale, int find_amax) {
   const int r = blockIdx.x;
   if (r >= expert_offsets[E]) return;
+  const f32x4* row = reinterpret_cast<const f32x4*>(h32 + (size_t)r * I);
+  uint32_t* q = reinterpret_cast<uint32_t*>(hq + (size_t)r * I);
+  const int nv = I / 4;
+  f32x4 v[NV > 0 ? NV : 1];
   float amax;
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int j = 0; j < NV; j++) {
+      const int i = threadIdx.x + j * 256;
+      v[j] = i < nv ? row[i] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  }
   if (find_amax) {
-    amax = row_amax_f32<256>(h32 + (size_t)r * I, I);
+    if constexpr (NV > 0) {
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NV; j++)
+        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[j][0]), __builtin_fabsf(v[j][1])),
+                                               __builtin_fmaxf(__builtin_fabsf(v[j][2]), __builtin_fabsf(v[j][3]))));
+      amax = block_max_f32<256>(m);
+    } else {
+      amax = row_amax_f32<256>(h32 + (size_t)r * I, I);
+    }
   } else {
     amax = h_scale[r];
     __syncthreads();   // every thread has read the amax before it is replaced
   }
   float sc, inv;
   e4m3_row_scales(amax, &sc, &inv);
-  const f32x4* row = reinterpret_cast<const f32x4*>(h32 + (size_t)r * I);
-  uint32_t* q = reinterpret_cast<uint32_t*>(hq + (size_t)r * I);
-  for (int i = threadIdx.x; i < I / 4; i += 256) {
-    const f32x4 v = row[i];
-    q[i] = f32x4_to_e4m3x4_sat(__fmul_rn(v[0], inv), __fmul_rn(v[1], inv), __fmul_rn(v[2], inv),
-                               __fmul_rn(v[3], inv));
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int j = 0; j < NV; j++) {
+      const int i = threadIdx.x + j * 256;
+      if (i < nv)
+        q[i] = f32x4_to_e4m3x4_sat(__fmul_rn(v[j][0], inv), __fmul_rn(v[j][1], inv), __fmul_rn(v[j][2], inv),
+                                   __fmul_rn(v[j][3], inv));
+    }
+  } else {
+    for (int i = threadIdx.x; i < nv; i += 256) {
+      const f32x4 w = row[i];
+      q[i] = f32x4_to_e4m3x4_sat(__fmul_rn(w[0], inv), __fmul_rn(w[1], inv), __fmul_rn(w[2], inv),
+                                 __fmul_rn(w[3], inv));
+    }
   }
   if (threadIdx.x == 0) h_scale[r] = sc;
 }
@@ -607,8 +638,16 @@ hipError_t launch_tiled_gemm(const TiledArgs& a, bool gateup, bool fp8, int bm, 
 
 hipError_t launch_requant_rows(const float* h32, int P, int I, const int32_t* expert_offsets,
                                int E, uint8_t* hq, float* h_scale, bool find_amax, hipStream_t s) {
-  hipLaunchKernelGGL(moe::requant_rows_kernel, dim3(P), dim3(256), 0, s, h32, I, expert_offsets,
-                     E, hq, h_scale, find_amax ? 1 : 0);
+  const int per = (I / 4 + 255) / 256;   // 16-byte vectors per thread
+#define MOE_REQUANT_NV(NVv)                                                                             \
+  hipLaunchKernelGGL(moe::requant_rows_kernel<NVv>, dim3(P), dim3(256), 0, s, h32, I, expert_offsets, E, \
+                     hq, h_scale, find_amax ? 1 : 0)
+  if (per <= 1) MOE_REQUANT_NV(1);
+  else if (per <= 2) MOE_REQUANT_NV(2);
+  else if (per <= 4) MOE_REQUANT_NV(4);
+  else if (per <= 8) MOE_REQUANT_NV(8);
+  else MOE_REQUANT_NV(0);
+#undef MOE_REQUANT_NV
   return hipGetLastError();
 }
 
