@@ -24,3 +24,14 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    try:
+        from moe_testlib import SUMMARY
+    except ImportError:
+        return
+    if SUMMARY:
+        terminalreporter.write_sep("-", "full-size parity against the oracle")
+        for line in SUMMARY:
+            terminalreporter.write_line(line)

@@ -14,6 +14,11 @@ BF16_REL, BF16_ABS = 1e-2, 1e-3      # max|err| <= 1e-2*max|ref| + 1e-3
 FP8_REL = 4e-2                        # max|err| <= 4e-2*max|ref|
 
 
+# One line per full-size parity case, printed at the end of the session
+# (conftest.py), so that the counts stay visible when pytest captures output.
+SUMMARY = []
+
+
 def log(msg):
     print(msg, flush=True)
     sys.stdout.flush()

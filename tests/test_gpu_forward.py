@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from moe_inputs import WORKLOADS, custom_workload, make_tokens, make_weights, random_ids, random_weights_w
-from moe_testlib import check_tol, device_weights, log, oracle_rows, path_dtype, run_gpu, sample_rows
+from moe_testlib import SUMMARY, check_tol, device_weights, log, oracle_rows, path_dtype, run_gpu, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +84,7 @@ def check_fp8_quant(lib, T, k, E, H, I, ws, routing, ids, rows, xq, sx, hq, sh, 
     idc = ids.cpu().numpy()[rows]
     valid = (idc >= 0) & (idc < E)
     if not valid.any():
-        return
+        return 1.0
     pos = lib.read_routing(routing, T, k, E, H, I, "fp8")["pos"].numpy().reshape(T, k)[rows]
     psel = torch.from_numpy(pos[valid].astype(np.int64)).to(ws.device)
     ghq = ws[L["h"]:L["h"] + P * I].view(P, I)[psel].cpu().numpy()
@@ -105,6 +105,7 @@ def check_fp8_quant(lib, T, k, E, H, I, ws, routing, ids, rows, xq, sx, hq, sh, 
     assert same >= 0.99, f"{what}: intermediate codes equal {same}"
     assert np.all(dev <= allowed), f"{what}: intermediate value beyond one step + 2^-11 amax"
     assert srel <= 1e-3, f"{what}: intermediate scales"
+    return same
 
 
 SMALL = [
@@ -407,11 +408,15 @@ def test_full_size_parity(lib, name, T):
         ref, (xq, sx, hq, sh) = oracle_rows(x, ids, w, Wc, dtype, rows=rows, want_quant=True)
     else:
         ref = oracle_rows(x, ids, w, Wc, dtype, rows=rows)
-    check_tol(out64(out)[rows], ref, dtype, f"{name} T={T} rows={len(rows)}")
+    err, bound, cos = check_tol(out64(out)[rows], ref, dtype, f"{name} T={T} rows={len(rows)}")
     assert torch.isfinite(out.float()).all()
+    line = (f"{name} T={T} {dtype}: {len(rows)}/{T} tokens, max|err| {err:.3e} = {err / bound:.2f} of the "
+            f"bound, cosine {cos:.6f}")
     if dtype == "fp8":
-        check_fp8_quant(lib, T, wl.k, wl.E, wl.H, wl.I, ws, routing, ids, rows, xq, sx, hq, sh,
-                        f"{name} T={T}")
+        same = check_fp8_quant(lib, T, wl.k, wl.E, wl.H, wl.I, ws, routing, ids, rows, xq, sx, hq, sh,
+                               f"{name} T={T}")
+        line += f"; x codes bit-exact, h codes {100 * same:.2f}% equal"
+    SUMMARY.append(line)
 
 
 def test_deterministic_and_permutation_equivariant(lib):
