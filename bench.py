@@ -71,11 +71,12 @@ def layer_bytes_and_flops(wl, ids, T):
     return nbytes, flops, active, int(valid.numel())
 
 
-def stage_bytes(wl, active, P_valid, T):
+def stage_bytes(wl, active, P_valid, T, fused_reduce=False):
     """Algorithmic bytes each stage must move: its own inputs and outputs in
     their minimal form (weights and scales of the active experts once, the
     activations it reads, SiLU(gate)*up as bf16 or e4m3 codes, down rows as
-    bf16); partial sums and padding rows are not counted."""
+    bf16); partial sums and padding rows are not counted.  fused_reduce: the
+    down launch adds the top-k rows and writes the token rows itself."""
     E, H, I = wl.E, wl.H, wl.I
     mx = wl.dtype == "mxfp8"
     blk = wl.dtype == "fp8b"
@@ -95,8 +96,9 @@ def stage_bytes(wl, active, P_valid, T):
         "quant_x": T * H * 2 + T * H + T * xs if fp8 else 0,
         "gate_up": int(active * (2 * I * H * bw + w1s)) + T * (H * bx + xs) + P_valid * I * bx,
         "act": P_valid * I * 4 + P_valid * (I * bx + hs),
-        "down": int(active * (H * I * bw + w2s)) + P_valid * (I * bx + hs) + P_valid * H * 2,
-        "reduce": P_valid * H * 2 + T * H * 2,
+        "down": int(active * (H * I * bw + w2s)) + P_valid * (I * bx + hs) +
+                (T * H * 2 if fused_reduce else P_valid * H * 2),
+        "reduce": 0 if fused_reduce else P_valid * H * 2 + T * H * 2,
     }
 
 
@@ -115,7 +117,10 @@ class Layer:
         self.out = torch.empty(T, H, dtype=torch.bfloat16, device=device)
         # a separate activation / requantisation launch exists only where the
         # gate-up GEMM leaves fp32 sums (workspace part "g")
-        self.has_act = moe.moe_workspace_layout(T, k, E, H, I, dtype)["g"] != 2 ** 64 - 1
+        lay = moe.moe_workspace_layout(T, k, E, H, I, dtype)
+        self.has_act = lay["g"] != 2 ** 64 - 1
+        # one token: the down launch adds the top-k rows (no reduction launch)
+        self.has_reduce = lay["y"] != 2 ** 64 - 1
 
     def run_routing(self):
         m, wl = self.moe, self.wl
@@ -166,6 +171,8 @@ def stage_pass(layer, steps):
             if layer.dtype in ("bf16", "int4", "int8w") and s == "quant_x":
                 continue
             if s == "act" and not layer.has_act:   # formed in the gate-up epilogue
+                continue
+            if s == "reduce" and not layer.has_reduce:   # added by the down launch
                 continue
             stage_ms[s].append(ev[i][2 * si].elapsed_time(ev[i][2 * si + 1]))
     return stage_ms
@@ -443,7 +450,7 @@ def main():
     for _ in range(args.warmup):
         layer.run()
     stage_ms = stage_pass(layer, max(5, min(args.steps, 20)))
-    sb = stage_bytes(wl, active, P_valid, T)
+    sb = stage_bytes(wl, active, P_valid, T, fused_reduce=not layer.has_reduce)
     stages = {}
     for s, v in stage_ms.items():
         if v:

@@ -305,6 +305,14 @@ struct StreamArgs {
 // bf16 gate-up on 16-row tiles with half-width items (8 h columns each; K
 // steps a multiple of 2 * waves).
 hipError_t launch_stream_half_gateup(const StreamArgs& a, int waves, int grid, hipStream_t s);
+// Down GEMM and top-k weighted sum of a single token in one launch (T = 1,
+// at most 16 pairs; `half`: at most 8): one workgroup of `waves` waves per
+// 16 output columns (`half`: 8), writing the bf16 token row `out`; topk_w
+// [k], h_scale (fp8) per sorted row.  (waves, u) in (4, 2), (8, 2), (16, 2),
+// (8, 4), (16, 4); the K steps (K * element bytes / 64) a multiple of u
+// (`half`: 2u).
+hipError_t launch_stream_down_reduce(const StreamArgs& a, bool fp8, int waves, int u, bool half,
+                                     const float* topk_w, const float* h_scale, uint16_t* out, hipStream_t s);
 // (mb, waves, u) = 16-row blocks per tile, waves per workgroup, K steps per stage.
 bool stream_config_supported(int mb, int waves, int u);
 // kind: 0 per-channel scales (bf16, or fp8 by `fp8`), 1 MXFP8 block scales,

@@ -426,6 +426,153 @@ stream_half_gateup_kernel(moe_host::StreamArgs g) {
   }
 }
 
+// Down GEMM and top-k weighted sum of a single token in one launch (decode):
+// out[c] = sum over the token's sorted rows r of w_r * (h_r . W2[e_r][:, c])
+// (fp8: each product also times the row's activation scale and its
+// expert's column scale).
+//  * Item = 16 output columns (HALF: 8), one per workgroup.  Its reduction
+//    runs over the concatenation of the token's experts (every task's K
+//    steps in turn), cut into equal runs of whole register stages, one per
+//    wave; the waves' sums meet in LDS, so the top-k sum needs neither a
+//    second launch nor partial rows in memory.
+//  * One token has at most 16 pairs, so the A tile's row r is sorted row r
+//    at every step, zeroed unless r belongs to the step's task: accumulator
+//    row r collects only the products of its own expert's weights, and the
+//    epilogue weights each row and adds the rows of each column.
+//  * HALF (at most 8 pairs): twice the items at half the bytes each.  One
+//    instruction covers two K steps of the item's 8 columns: B columns 0-7
+//    take the columns from step 2m, columns 8-15 the same columns from step
+//    2m + 1, and A rows 0-7 / 8-15 the token's rows at those two steps; the
+//    two diagonal 8 x 8 quarters of the product are the useful ones, and
+//    column c of the item is the sum of accumulator columns c and c + 8.
+//  * Task records go to LDS first; the per-row weights and scales are loaded
+//    before the weight stream starts and used after it.
+template <int W, int U, bool HALF, bool FP8>
+__global__ void __launch_bounds__(W * 64)
+stream_down_reduce_kernel(moe_host::StreamArgs g, const float* __restrict__ topk_w,
+                          const float* __restrict__ h_scale, uint16_t* __restrict__ out) {
+#pragma clang fp contract(off)
+  constexpr int KS = HALF ? 2 : 1;   // 64-byte K steps per instruction step
+  __shared__ f32x4 red[W][64];
+  __shared__ moe_task_t tk[16];
+  const int lane = threadIdx.x & 63;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (threadIdx.x < 16 && (int)threadIdx.x < g.max_tasks) tk[threadIdx.x] = g.tasks[threadIdx.x];
+  const int nt = min(min(g.header[kHdrNumTasks], g.max_tasks), 16);
+  const i32x16_t sp = load16_scalar(g.sorted_pairs);
+  __syncthreads();
+
+  const size_t row_bytes = (size_t)g.K * (FP8 ? 1 : 2);
+  const int nsteps = (int)(row_bytes / 64);
+  const int nm = nsteps / KS;                  // instruction steps per task, a multiple of U
+  const int total = nt * nm;
+  int spw = (total + W - 1) / W;
+  spw = (spw + U - 1) / U * U;
+  const int s0 = min(total, wave * spw);
+  const int ngroups = (min(total, s0 + spw) - s0) / U;
+  // this lane's A row (a sorted row) and K step within the instruction
+  // step, and its offset in a packed 1 KiB weight chunk
+  const int arow = HALF ? (lrow & 7) : lrow;
+  const int ksub = HALF ? (lrow >> 3) : 0;
+  const int cb = HALF ? (int)(blockIdx.x >> 1) : (int)blockIdx.x;   // 16-column weight block
+  const int col0 = HALF ? 8 * (int)blockIdx.x : 16 * (int)blockIdx.x;
+  const int boff = HALF ? 16 * (lgrp * 16 + (blockIdx.x & 1) * 8 + (lrow & 7)) : 16 * lane;
+  const char* __restrict__ A = static_cast<const char*>(g.a);
+  const char* __restrict__ B = static_cast<const char*>(g.b);
+  const size_t expert_bytes = (size_t)(g.w_rows / 16) * nsteps * 1024;
+  const char* bcol = B + ((size_t)cb * nsteps + ksub) * 1024 + boff;
+
+  // Accumulator rows 4 lgrp + i of this lane's column: the sorted row each
+  // holds, its weight w_r (times the row scale on fp8; 0 for rows outside
+  // every task, dropped pairs and rows past the token's pairs, and for the
+  // off-diagonal quarters of HALF) and its expert's scale of the lane's
+  // output column.
+  const int ocol = col0 + (HALF ? (lrow & 7) : lrow);
+  float wr[4], cs[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int r = HALF ? ((4 * lgrp + i) & 7) : 4 * lgrp + i;
+    const bool diag = !HALF || ((lrow < 8) == (lgrp < 2));
+    int e = -1;
+    for (int t = 0; t < nt; t++)
+      if ((unsigned)(r - tk[t].row_begin) < (unsigned)tk[t].rows) e = tk[t].expert;
+    // the loads stay unconditional (entry 0 when the row is unused)
+    const bool use = e >= 0 && diag;
+    const float w = topk_w[use ? pick16(sp, r) : 0];
+    wr[i] = use ? w : 0.0f;
+    cs[i] = 1.0f;
+    if constexpr (FP8) {
+      const float rs = h_scale[use ? r : 0];
+      const float c = g.b_scale[(size_t)(use ? e : 0) * g.w_rows + ocol];
+      wr[i] = wr[i] * rs;
+      cs[i] = c;
+    }
+  }
+
+  f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  u32x4 fa0[U], fb0[U], fa1[U], fb1[U];
+  bool in0 = false, in1 = false;
+  auto load = [&](u32x4 (&fa)[U], u32x4 (&fb)[U], bool& in, int grp) __attribute__((always_inline)) {
+    const int s = s0 + grp * U;
+    const int t = s / nm;
+    const int ks = (s - t * nm) * KS;   // first 64-byte step of the stage
+    const moe_task_t task = tk[t];
+    in = (unsigned)(arow - task.row_begin) < (unsigned)task.rows;
+    // lanes of other rows read the task's first row (one line per step) and drop it
+    const char* ap = A + (size_t)(in ? arow : task.row_begin) * row_bytes + (size_t)(ks + ksub) * 64 + 16 * lgrp;
+    const char* bp = bcol + (size_t)task.expert * expert_bytes + (size_t)ks * 1024;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      fb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp + (size_t)u * KS * 1024));
+      fa[u] = *reinterpret_cast<const u32x4*>(ap + (size_t)u * KS * 64);
+    }
+  };
+  auto compute = [&](const u32x4 (&fa)[U], const u32x4 (&fb)[U], bool in) __attribute__((always_inline)) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < U; u++) stream_mfma<FP8>(acc, in ? fa[u] : zero, fb[u]);
+  };
+  if (ngroups > 0) {
+    load(fa0, fb0, in0, 0);
+    int grp = 0;
+    for (; grp + 2 < ngroups; grp += 2) {
+      load(fa1, fb1, in1, grp + 1);
+      compute(fa0, fb0, in0);
+      load(fa0, fb0, in0, grp + 2);
+      compute(fa1, fb1, in1);
+    }
+    if (grp + 1 < ngroups) {
+      load(fa1, fb1, in1, grp + 1);
+      compute(fa0, fb0, in0);
+      compute(fa1, fb1, in1);
+    } else {
+      compute(fa0, fb0, in0);
+    }
+  }
+
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 tot = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < W; w++) tot += red[w][lane];
+    // weight the lane's rows, add the four row groups of the column (and on
+    // HALF the two accumulator columns of each output column)
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) v = v + wr[i] * (tot[i] * cs[i]);
+    v = v + __shfl_xor(v, 16, 64);
+    v = v + __shfl_xor(v, 32, 64);
+    if constexpr (HALF) {
+      v = v + __shfl_xor(v, 8, 64);
+      if (lane < 8) out[ocol] = f32_to_bf16_bits(v);
+    } else {
+      if (lgrp == 0) out[ocol] = f32_to_bf16_bits(v);
+    }
+  }
+}
+
 template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX, bool I8 = false>
 static hipError_t launch_stream_t(const moe_host::StreamArgs& a, int grid, hipStream_t s) {
   hipLaunchKernelGGL((stream_gemm_kernel<MB, W, U, GATEUP, FP8, MX, I8>), dim3(grid), dim3(W * 64), 0, s, a);
@@ -501,6 +648,29 @@ hipError_t launch_stream_half_gateup(const StreamArgs& a, int waves, int grid, h
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_stream_down_reduce(const StreamArgs& a, bool fp8, int waves, int u, bool half,
+                                     const float* topk_w, const float* h_scale, uint16_t* out, hipStream_t s) {
+  const int nsteps = a.K * (fp8 ? 1 : 2) / 64;
+  if (a.P > (half ? 8 : 16) || nsteps % ((half ? 2 : 1) * u) || a.N_out % 16) return hipErrorInvalidValue;
+  const dim3 grid(a.N_out / (half ? 8 : 16));
+#define MOE_DR(Wv, Uv, Hv)                                                                              \
+  {                                                                                                     \
+    if (fp8)                                                                                            \
+      hipLaunchKernelGGL((moe::stream_down_reduce_kernel<Wv, Uv, Hv, true>), grid, dim3(Wv * 64), 0, s, \
+                         a, topk_w, h_scale, out);                                                      \
+    else                                                                                                \
+      hipLaunchKernelGGL((moe::stream_down_reduce_kernel<Wv, Uv, Hv, false>), grid, dim3(Wv * 64), 0,   \
+                         s, a, topk_w, h_scale, out);                                                   \
+    return hipGetLastError();                                                                           \
+  }
+#define MOE_DR_CASE(Wv, Uv) \
+  if (waves == Wv && u == Uv) { if (half) MOE_DR(Wv, Uv, true) else MOE_DR(Wv, Uv, false) }
+  MOE_DR_CASE(4, 2) MOE_DR_CASE(8, 2) MOE_DR_CASE(16, 2) MOE_DR_CASE(8, 4) MOE_DR_CASE(16, 4)
+#undef MOE_DR_CASE
+#undef MOE_DR
+  return hipErrorInvalidValue;
 }
 
 bool stream_config_supported(int mb, int waves, int u) {

@@ -78,6 +78,15 @@ def test_workspace_layout(m):
     assert S["y"] + ybytes <= S["total_bytes"]
     Wb = m.moe_workspace_layout(16, 8, 256, 7168, 2048, "bf16")
     assert Wb["xq"] == 2 ** 64 - 1 and Wb["h_scale"] == 2 ** 64 - 1
+    # one token: the down launch adds the top-k rows, no down rows in memory
+    # (bf16 and fp8 whenever an I row is an even number of 64-byte steps)
+    for dt, I in (("fp8", 2048), ("bf16", 768), ("bf16", 576)):
+        D = m.moe_workspace_layout(1, 8, 256, 7168, I, dt)
+        assert D["tiling"] == 0 and D["y"] == 2 ** 64 - 1 and D["h"] < D["total_bytes"]
+    # ... but not with an odd number (fp8, I = 576: 9 steps) or another dtype
+    assert m.moe_workspace_layout(1, 3, 16, 320, 576, "fp8")["y"] != 2 ** 64 - 1
+    assert m.moe_workspace_layout(1, 8, 256, 7168, 2048, "int8")["y"] != 2 ** 64 - 1
+    assert m.moe_workspace_layout(2, 8, 256, 7168, 2048, "fp8")["y"] != 2 ** 64 - 1
 
 
 @pytest.mark.parametrize("args,code", [
