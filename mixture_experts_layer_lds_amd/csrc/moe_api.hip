@@ -7,6 +7,7 @@
 // article makes the same point about interpreter overhead on the launch
 // path).
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 
 #include "moe_common.h"
@@ -43,7 +44,9 @@ struct Plan {
   int ks2 = 4, nbuf2 = 4;        // (down)
   bool fp8_units = false;        // fp8 streaming on 128-value units (fp8b_gemm.hip, per-channel mode)
   bool half1 = false;            // bf16 streaming gate-up on half-width (8-column) items
-  int nb = 2;                    // block fp8 streaming: weight blocks per item (2 or 4)
+  int nb = 2;                    // streaming: weight blocks per item, 2 or 4 (bf16 on 32-row
+                                 // tiles; MX, int8, block fp8 on 64-row tiles; int4 and
+                                 // int8 w8a16 on 32- or 64-row tiles)
   int dr_waves = 0;              // streaming, one token: down GEMM and top-k sum in one launch
   int dr_u = 2;                  // with this many waves per workgroup (0: two launches), K steps
   bool dr_half = false;          // per register stage and 8-column items
@@ -154,10 +157,27 @@ int pick_unit_waves(int units, long items) {
   return best;
 }
 
+// Expected number of distinct experts among T tokens that each pick k
+// distinct experts uniformly: E (1 - (1 - k/E)^T), at least 1.
+long expected_active(int T, int k, int E) {
+  if (k >= E) return E;
+  const double miss = std::pow(1.0 - (double)k / E, (double)T);
+  const long ex = (long)std::ceil(E * (1.0 - miss) - 1e-9);
+  return ex < 1 ? 1 : ex;
+}
+
 Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   Plan p;
   const long P = (long)T * k;
   const long active = P < E ? P : E;
+  // The down GEMM's wave split is chosen for the expected number of active
+  // experts, the gate-up's for the bound min(P, E).  Same-box A/B (graph
+  // replay) of the expected count in the down choice: Mixtral-8x7B T=4 355
+  // -> 338 us, int4 153 -> 143, int8 w8a16 197 -> 192, Qwen2-57B T=4 71.1
+  // -> 66.7, T=8 110.4 -> 106.6; in the gate-up choice as well it helped
+  // Qwen3-30B-A3B T=8 (56.8 -> 53.5) but cost DeepSeek-V3 T=16 (714 -> 734)
+  // and Qwen2-57B T=8 (110 -> 112).
+  const long active_d = std::min(active, expected_active(T, k, E));
   const long avg = active > 0 ? (P + active - 1) / active : 1;
   const int esz_t = dtype == MOE_DTYPE_BF16 ? 2 : 1;
   const int nsteps1 = H * esz_t / 64, nsteps2 = I * esz_t / 64;
@@ -173,21 +193,23 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     if (est < active) est = active;
     const int per = dtype == MOE_DTYPE_INT8_W8A16 ? 64 : 128;   // K values per step
     p.sw1 = pick_unit_waves(H / per, est * ((long)I / 16));
-    p.sw2 = pick_unit_waves(I / per, est * ((long)H / 32));
+    long est_d = (P + p.block_m - 1) / p.block_m;
+    if (est_d < active_d) est_d = active_d;
+    p.sw2 = pick_unit_waves(I / per, est_d * ((long)H / 32));
     if ((dtype == MOE_DTYPE_INT4_W4A16 || dtype == MOE_DTYPE_INT8_W8A16) && p.mb >= 2 && I % 32 == 0 &&
         H % 64 == 0) {
       // tiles of 32 or 64 rows: four weight blocks per item halve the token-row re-reads
       p.nb = 4;
       const int wmax = 16 / p.mb;   // the waves' partial sums within 64 KiB of LDS
       p.sw1 = std::min(pick_unit_waves(H / per, est * ((long)I / 32)), wmax);
-      p.sw2 = std::min(pick_unit_waves(I / per, est * ((long)H / 64)), wmax);
+      p.sw2 = std::min(pick_unit_waves(I / per, est_d * ((long)H / 64)), wmax);
     }
     if (dtype == MOE_DTYPE_FP8_BLOCK && p.mb == 4 && I % 32 == 0 && H % 64 == 0) {
       // 64-row tiles: four weight blocks per item halve the token-row
       // re-reads (the register tile allows at most two waves)
       p.nb = 4;
       p.sw1 = std::min(pick_unit_waves(H / per, est * ((long)I / 32)), 2);
-      p.sw2 = std::min(pick_unit_waves(I / per, est * ((long)H / 64)), 2);
+      p.sw2 = std::min(pick_unit_waves(I / per, est_d * ((long)H / 64)), 2);
     }
     p.su1 = p.su2 = 1;
     return p;
@@ -204,7 +226,9 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     long est = (P + p.block_m - 1) / p.block_m;
     if (est < active) est = active;
     choose_stream(nsteps1, p.mb, est * ((long)I / 16), &p.sw1, &p.su1);
-    choose_stream(nsteps2, p.mb, est * ((long)H / 32), &p.sw2, &p.su2);
+    long est_d = (P + p.block_m - 1) / p.block_m;
+    if (est_d < active_d) est_d = active_d;
+    choose_stream(nsteps2, p.mb, est_d * ((long)H / 32), &p.sw2, &p.su2);
     if (p.mb == 4 && I % 32 == 0 && H % 64 == 0 && nsteps1 % 2 == 0 && nsteps2 % 2 == 0) {
       // 64-row tiles: four weight blocks per item halve the token-row
       // re-reads (the register tile allows at most two waves)
@@ -241,7 +265,9 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     long est = (P + p.block_m - 1) / p.block_m;
     if (est < active) est = active;
     choose_stream(nsteps1, p.mb, est * ((long)I / 32), &p.sw1, &p.su1);
-    choose_stream(nsteps2, p.mb, est * ((long)H / 64), &p.sw2, &p.su2);
+    long est_d = (P + p.block_m - 1) / p.block_m;
+    if (est_d < active_d) est_d = active_d;
+    choose_stream(nsteps2, p.mb, est_d * ((long)H / 64), &p.sw2, &p.su2);
     p.sw1 = std::min(p.sw1, 4);
     p.sw2 = std::min(p.sw2, 4);
     if (p.su1 == 2 && p.su2 == 2) return p;
@@ -287,9 +313,11 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   p.max_tasks = (int)(P / p.block_m + (P < E ? P : E));
   long est_tasks = (P + p.block_m - 1) / p.block_m;
   if (est_tasks < active) est_tasks = active;
+  long est_tasks_d = (P + p.block_m - 1) / p.block_m;
+  if (est_tasks_d < active_d) est_tasks_d = active_d;
   if (!tiled) {
     choose_stream(nsteps1, p.mb, est_tasks * ((long)I / 16), &p.sw1, &p.su1);
-    choose_stream(nsteps2, p.mb, est_tasks * ((long)H / 32), &p.sw2, &p.su2);
+    choose_stream(nsteps2, p.mb, est_tasks_d * ((long)H / 32), &p.sw2, &p.su2);
     if (dtype == MOE_DTYPE_BF16 && p.mb == 1 && I % 8 == 0) {
       // Half-width gate-up items when the full-width count leaves some CUs
       // one item more than others: the busiest CU streams ceil(n / CUs)
@@ -314,7 +342,7 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
       // whole 128-value units: one 16x16x128 MFMA per unit instead of four 16x16x32
       p.fp8_units = true;
       p.sw1 = pick_unit_waves(H / 128, est_tasks * ((long)I / 16));
-      p.sw2 = pick_unit_waves(I / 128, est_tasks * ((long)H / 32));
+      p.sw2 = pick_unit_waves(I / 128, est_tasks_d * ((long)H / 32));
       p.su1 = p.su2 = 2;
     }
     if (T == 1 && nsteps2 % 2 == 0) {

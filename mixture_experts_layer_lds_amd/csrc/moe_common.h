@@ -317,8 +317,9 @@ hipError_t launch_stream_down_reduce(const StreamArgs& a, bool fp8, int waves, i
 bool stream_config_supported(int mb, int waves, int u);
 // kind: 0 per-channel scales (bf16, or fp8 by `fp8`), 1 MXFP8 block scales,
 // 2 int8 w8a8 (per-channel scales).
-// nb: weight blocks per item, 2, or 4 (MX or int8 on 64-row tiles, two-step
-// stages, at most two waves).
+// nb: weight blocks per item, 2, or 4 (two-step stages): MX or int8 w8a8 on
+// 64-row tiles with one or two waves, bf16 (kind 0, !fp8) on 32-row tiles
+// with one, two or four waves.
 hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int kind, int mb, int waves,
                               int u, int grid, hipStream_t s, int nb = 2);
 // int8 w8a8: per-token quantisation of bf16 x (row-amax slots cleared,

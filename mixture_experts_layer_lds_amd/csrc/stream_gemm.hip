@@ -8,10 +8,10 @@
 // grid consumes the per-tile task map; the activation follows the gate-up
 // GEMM).
 //
-//  * Work item = (task tile of 16*MB rows, 32 output columns).  Gate-up: a
-//    16-column block of gate rows of W1 and the matching block of up rows, so
-//    the item holds both halves of its 16 h columns; down: two adjacent
-//    16-column blocks of W2.
+//  * Work item = (task tile of 16*MB rows, 32 output columns; 64 with four
+//    weight blocks).  Gate-up: 16-column blocks of gate rows of W1 and the
+//    matching blocks of up rows, so the item holds both halves of its h
+//    columns; down: adjacent 16-column blocks of W2.
 //  * A workgroup of W waves takes one item; wave w reduces K slice w
 //    (nsteps / W 64-byte steps), streaming the item's two packed weight
 //    blocks into registers (1 KiB non-temporal loads, two register stages of
@@ -62,9 +62,10 @@ __device__ __forceinline__ void stream_mfma(f32x4& acc, const u32x4& a, const u3
 }
 
 // MB 16-row blocks per task tile, W waves per workgroup (K slices), U
-// 64-byte K steps per register stage, NB weight blocks per item: 2, or 4 on
-// 64-row tiles of the 1-byte paths (gate-up: two gate and two up blocks,
-// down: 64 columns), halving the re-reads of the tile's token rows.
+// 64-byte K steps per register stage, NB weight blocks per item: 2, or 4
+// (gate-up: two gate and two up blocks, down: 64 columns), halving the
+// re-reads of the tile's token rows: MX and int8 w8a8 on 64-row tiles (one
+// or two waves), bf16 on 32-row tiles (one, two or four waves).
 template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX, bool I8, int NB = kStreamNB>
 __global__ void __launch_bounds__(W * 64)
 stream_gemm_kernel(moe_host::StreamArgs g) {
@@ -579,7 +580,9 @@ static hipError_t launch_stream_t(const moe_host::StreamArgs& a, int grid, hipSt
   return hipGetLastError();
 }
 
-// four weight blocks per item: 64-row tiles, MX or int8, at most two waves
+// Four weight blocks per item: MX or int8 w8a8 on 64-row tiles with one or
+// two waves (kind 1, 2), bf16 on 32-row tiles with one, two or four waves
+// (kind 3); two-step stages.
 hipError_t launch_stream_nb4(const moe_host::StreamArgs& a, bool gateup, int kind, int waves, int grid,
                              hipStream_t s) {
 #define MOE_NB4(Wv, GU, MXv, I8v) \
