@@ -274,13 +274,18 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     p = Plan();
   }
   if (avg >= strip_min && avg <= strip_max && (2 * I) % kStripCols == 0 && H % kStripCols == 0) {
-    // Tile height about twice the mean rows per expert; when no strip
-    // configuration divides the reductions at that height, a taller one
-    // (emptier tiles cost MFMA time, which this weight-bound range has spare).
+    // Tile height about twice the mean rows per expert, and at least 64
+    // rows: a skewed routing puts several times the mean on its hottest
+    // experts, whose weights a shorter tile would stream once per tile, and
+    // emptier tiles cost MFMA time, which this weight-bound range has spare.
+    // Same-box A/B of 64- against 32-row tiles (graph replay): Qwen3-30B-A3B
+    // T=256 skewed 158 -> 146 us, uniform 222 -> 216 us; DeepSeek-V3 fp8
+    // T=128 1767 -> 1759 us.  When no strip configuration divides the
+    // reductions at that height, a taller one.
     const bool fp8 = dtype == MOE_DTYPE_FP8_W8A8;
-    // heights 2, 4, 8 and 12 row blocks (12 only for fp8, whose strips run to
+    // heights 4, 8 and 12 row blocks (12 only for fp8, whose strips run to
     // 160 mean rows: 192-row tiles keep an expert's rows in one tile)
-    const int first = avg <= 16 ? 2 : (avg <= 40 ? 4 : (avg <= 96 || !fp8 ? 8 : 12));
+    const int first = avg <= 40 ? 4 : (avg <= 96 || !fp8 ? 8 : 12);
     for (int mb = first; mb <= 12; mb = mb == 8 ? 12 : mb * 2) {
       long tasks = (P + 16 * mb - 1) / (16 * mb);
       if (tasks < active) tasks = active;

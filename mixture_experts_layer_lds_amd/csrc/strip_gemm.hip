@@ -397,7 +397,6 @@ namespace moe_host {
 
 // (16-row blocks per tile, K steps per stage, stages in flight) built here.
 #define MOE_STRIP_CONFIGS(X) \
-  X(2, 4, 4) X(2, 4, 3) X(2, 4, 2)                       \
   X(4, 2, 4) X(4, 4, 3) X(4, 4, 4) X(4, 2, 3) X(4, 4, 2) X(4, 2, 2) \
   X(8, 2, 4) X(8, 2, 3) X(8, 1, 4) X(8, 2, 2)             \
   X(12, 2, 4) X(12, 2, 3) X(12, 2, 2)
