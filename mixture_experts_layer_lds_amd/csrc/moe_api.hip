@@ -26,6 +26,12 @@ constexpr long kStreamWaves = 2048;   // waves that fill 256 CUs x 8
 // a device), so it balances work for MI355X's compute-unit count; launches
 // use the device's actual count.
 constexpr long kPlanCUs = 256;
+// One-byte per-channel layers (fp8, int8 w8a8): strips from this many mean
+// rows per expert on, register streaming below.  Same-box A/B (graph replay,
+// DeepSeek-V3 shape): T=128 (4 rows) fp8 1759 us strips against 1700
+// streaming, int8 1750 / 1703; T=256 (8) fp8 1816 / 1765, int8 1807 / 1778;
+// T=512 (16) fp8 1891 / 2099, int8 1877 / 2099.
+constexpr long kOneByteStripMin = 12;
 constexpr int kStripCols = 256;       // output columns per strip work item
 
 enum Tiling { kStreaming = 0, kLdsTiles = 1, kStrips = 2 };
@@ -214,11 +220,33 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     p.su1 = p.su2 = 1;
     return p;
   }
+  if (dtype == MOE_DTYPE_INT8_W8A8 && avg >= kOneByteStripMin && avg <= 160 && (2 * I) % kStripCols == 0 &&
+      H % kStripCols == 0) {
+    // int8 w8a8 with many rows per expert: the fp8 strips (same one-byte
+    // layout and per-channel scales) on the integer MFMA, with the fp8 tile
+    // heights; only an unsplit gate-up, whose epilogue forms the fp32 h that
+    // the int8 requantisation reads.
+    const int first = avg <= 40 ? 4 : (avg <= 96 ? 8 : 12);
+    for (int mb = first; mb <= 12; mb = mb == 8 ? 12 : mb * 2) {
+      long tasks = (P + 16 * mb - 1) / (16 * mb);
+      if (tasks < active) tasks = active;
+      Plan q = p;
+      if (choose_strip(nsteps1, mb, true, tasks * (2L * I / kStripCols), &q.split1, &q.ks1, &q.nbuf1) &&
+          q.split1 == 1 &&
+          choose_strip(nsteps2, mb, true, tasks * ((long)H / kStripCols), &q.split2, &q.ks2, &q.nbuf2)) {
+        q.tiling = kStrips;
+        q.mb = mb;
+        q.block_m = 16 * mb;
+        q.max_tasks = (int)(P / q.block_m + (P < E ? P : E));
+        return q;
+      }
+    }
+  }
   if (dtype == MOE_DTYPE_MXFP8 || dtype == MOE_DTYPE_INT8_W8A8) {
-    // MXFP8 and int8: register streaming at every size (its activation block scales
-    // ride with the register stages; the strips' and tiles' LDS rings count
-    // their loads exactly and carry no scale stream).  Two-step stages: one
-    // 128-value unit of the scaled instruction each.
+    // MXFP8 and int8: register streaming (MXFP8 at every size: its activation
+    // block scales ride with the register stages; the strips' and tiles' LDS
+    // rings count their loads exactly and carry no scale stream).  Two-step
+    // stages: one 128-value unit of the scaled instruction each.
     p.tiling = kStreaming;
     p.block_m = avg <= 8 ? 16 : (avg <= 16 ? 32 : 64);
     p.mb = p.block_m / 16;
@@ -240,18 +268,17 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     return p;
   }
   // Few rows per expert (decode): register streaming, tiles of 16 rows.
-  // 9 to ~80 rows (fp8: 3 to ~160): strips (token rows in LDS, weights streamed),
+  // 9 to ~80 rows (fp8: 12 to ~160): strips (token rows in LDS, weights streamed),
   // tiles of about twice the mean rows per active expert so that the usual
   // spread of a uniform routing still fits one tile per expert.  More rows:
   // LDS tiles of both operands.
   // Measured crossover to LDS tiles: ~80 rows per expert for bf16 (Qwen2-57B
   // T=1024: 287 us tiles, 332 us strips) and above 128 for fp8 (DeepSeek-V3
   // T=4096: 3285 us strips, 3484 us tiles).
-  // The low end likewise: strips from 3 rows on fp8 (DeepSeek-V3 T=128: 1814
-  // us strips, 1942 us streaming), from 9 on bf16 (Mixtral-8x7B T=16: 464 us
-  // streaming, 508 us strips).
+  // The low end likewise: strips from 12 rows on fp8 (kOneByteStripMin), from
+  // 9 on bf16 (Mixtral-8x7B T=16: 464 us streaming, 508 us strips).
   const long strip_max = dtype == MOE_DTYPE_FP8_W8A8 ? 160 : 80;
-  const long strip_min = dtype == MOE_DTYPE_FP8_W8A8 ? 3 : 9;
+  const long strip_min = dtype == MOE_DTYPE_FP8_W8A8 ? kOneByteStripMin : 9;
   if (dtype == MOE_DTYPE_BF16 && avg >= 9 && avg <= 16 && H >= 3072 && I % 32 == 0 && H % 64 == 0) {
     // 32-row tiles on register streaming with four weight blocks per item,
     // for long reductions (same-box A/B against the strips: Mixtral-8x7B T=64
@@ -421,16 +448,18 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
     W->tiling = p.tiling;
     return;
   }
-  if (dtype == MOE_DTYPE_INT8_W8A8) {   // the fp8 streaming layout, int8 codes
+  if (dtype == MOE_DTYPE_INT8_W8A8) {   // the fp8 streaming / unsplit-strip layout, int8 codes
+    const int s2 = p.tiling == kStrips ? p.split2 : 1;
     W->xq = take((size_t)T * H);
     W->x_scale = take(4 * (size_t)T);
     W->x_scale_rows = take(4 * (P + 16));
     W->g = take(4 * P * I);
     W->h = take(P * I);
     W->h_scale = take(4 * P);
-    W->y = take(2 * P * H);
+    W->y = s2 == 1 ? take(2 * P * H) : take(4 * (size_t)s2 * P * H);
     W->total_bytes = off;
-    W->split_k1 = W->split_k2 = 1;
+    W->split_k1 = 1;
+    W->split_k2 = s2;
     W->tiling = p.tiling;
     return;
   }
@@ -910,6 +939,66 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
     e = moe_host::launch_quant_rows_i8(static_cast<const uint16_t*>(x), T, H, xq, x_scale, nullptr, k,
                                        R.pair_pos, x_rows, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (p.tiling == kStrips) {
+    // strips (the fp8 sequence on the integer MFMA): gate-up with SiLU(gate)*up
+    // in its epilogue (fp32 h), int8 requantisation, down (bf16 rows, or fp32
+    // partial sums of split_k2 slices), reduction
+    const bool y_bf16 = p.split2 == 1;
+    {
+      StageScope st(s, 1);
+      moe_host::StripArgs a{};
+      a.a = xq;
+      a.b = w1;
+      a.b_scale = w1_scale;
+      a.sorted_pairs = R.sorted_pairs;
+      a.header = R.header;
+      a.tasks = R.tasks;
+      a.c = h32;
+      a.K = H;
+      a.N = 2 * I;
+      a.P = P;
+      a.topk = k;
+      a.max_tasks = p.max_tasks;
+      a.split = 1;
+      a.out_bf16 = 0;
+      a.act = 1;
+      a.x_scale_rows = x_rows;
+      e = moe_host::launch_strip_gemm(a, true, true, p.mb, p.ks1, p.nbuf1, cus, s, true);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 2);
+      e = moe_host::launch_requant_rows_i8(h32, P, I, R.expert_offsets, E, hq, h_scale, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 3);
+      moe_host::StripArgs a{};
+      a.a = hq;
+      a.b = w2;
+      a.b_scale = w2_scale;
+      a.sorted_pairs = R.sorted_pairs;
+      a.header = R.header;
+      a.tasks = R.tasks;
+      a.c = ws + W.y;
+      a.K = I;
+      a.N = H;
+      a.P = P;
+      a.topk = k;
+      a.max_tasks = p.max_tasks;
+      a.split = p.split2;
+      a.out_bf16 = y_bf16 ? 1 : 0;
+      e = moe_host::launch_strip_gemm(a, false, true, p.mb, p.ks2, p.nbuf2, cus, s, true);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 4);
+      e = moe_host::launch_reduce(ws + W.y, y_bf16, p.split2, P, topk_w, R.pair_pos, R.expert_offsets,
+                                  h_scale, E, T, k, H, static_cast<uint16_t*>(out), s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
   }
   {
     StageScope st(s, 1);

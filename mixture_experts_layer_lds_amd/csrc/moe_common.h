@@ -271,13 +271,14 @@ struct StripArgs {
   // block and the matching up block, and c receives h = SiLU(gate) * up,
   // [P][N/2]: bf16, or on fp8 fp32 with the weight and x scales applied
   int act;
-  const float* x_scale_rows;    // fp8 act: x scale of each sorted row [P + 16]
+  const float* x_scale_rows;    // fp8 / int8 act: x scale of each sorted row [P + 16]
 };
 
 // (mb, ks, nbuf) = 16-row blocks per tile, 64-byte K steps per stage, stages in flight.
+// i8 (with fp8 set): int8 w8a8 codes and the integer MFMA, scales as on fp8.
 bool strip_config_supported(int mb, int ks, int nbuf, bool fp8);
 hipError_t launch_strip_gemm(const StripArgs& a, bool gather, bool fp8, int mb, int ks, int nbuf,
-                             int grid, hipStream_t s);
+                             int grid, hipStream_t s, bool i8 = false);
 
 // Register-streaming GEMM with the reduction split over the W waves of a
 // workgroup (few rows per expert).  Gate-up mode writes SiLU(gate)*up (bf16,

@@ -25,6 +25,11 @@
 //    the vector-memory queue holds only the ring's loads and the epilogue's
 //    stores, and the explicit vmcnt waits below count exactly those.
 //
+// int8 w8a8 (I8, with FP8 set: the same one-byte layout and per-channel
+// scales): one v_mfma_i32_16x16x64_i8 per 64-byte step; the int32 sums
+// (|sum| <= 127^2 K < 2^31) become fp32 at the start of the epilogue, which
+// then applies the scales as on fp8.
+//
 // Output: fp32 partial sums c[s][P][N], bf16 rows c[P][N] (one slice,
 // out_bf16), or on gate-up with one slice h = SiLU(gate) * up (act: the
 // wave's two blocks are a gate block and its up block; fp8 writes fp32 h for
@@ -116,9 +121,14 @@ __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::St
   return it;
 }
 
-template <bool FP8>
+template <bool FP8, bool I8 = false>
 __device__ __forceinline__ void strip_mfma(f32x4& acc, const u32x4& a, const u32x4& b) {
-  if constexpr (FP8) {
+  if constexpr (I8) {
+    acc = __builtin_bit_cast(f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
+                                                                         __builtin_bit_cast(i32x4_t, b),
+                                                                         __builtin_bit_cast(i32x4_t, acc),
+                                                                         0, 0, 0));
+  } else if constexpr (FP8) {
     const i64x2 a2 = __builtin_bit_cast(i64x2, a);
     const i64x2 b2 = __builtin_bit_cast(i64x2, b);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[0], b2[0], acc, 0, 0, 0);
@@ -151,9 +161,10 @@ struct WeightStage<KS, NSUB, true> {
   __device__ __forceinline__ const i32x8& unit(int u2, int q) const { return r[u2][q]; }
 };
 
-template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8>
+template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8, bool I8 = false>
 __global__ void __launch_bounds__(strip_waves<NSUB>() * 64, 1)
 strip_gemm_kernel(moe_host::StripArgs g) {
+  static_assert(!I8 || FP8, "int8 uses the one-byte per-channel path");
   using It = StripItem<MB, KS, NSUB>;
   constexpr int NA = It::NA;
   constexpr int PER = NA + KS * NSUB;   // vector-memory operations per wave per stage
@@ -209,7 +220,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
     // (valid addresses, never used), so the wait before each stage is the
     // same count and the compiler's own waits for the weight registers see
     // the same queue on every path.
-    constexpr bool PAIRS = FP8 && KS % 2 == 0;
+    constexpr bool PAIRS = FP8 && !I8 && KS % 2 == 0;
     WeightStage<KS, NSUB, PAIRS> bb[NBUF];
     auto issue = [&](bool in_cur, int kt, int fslot, WeightStage<KS, NSUB, PAIRS>& b) {
       char* sb = lds + fslot * SLOT;
@@ -277,7 +288,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
               for (int m = 0; m < MB; m++) {
                 const u32x4 a = *reinterpret_cast<const u32x4*>(sb + (m * KS + st) * 1024 + 16 * lane);
   #pragma unroll
-                for (int q = 0; q < NSUB; q++) strip_mfma<FP8>(acc[m][q], a, bb[u].step(st, q));
+                for (int q = 0; q < NSUB; q++) strip_mfma<FP8, I8>(acc[m][q], a, bb[u].step(st, q));
               }
             }
           }
@@ -291,6 +302,13 @@ strip_gemm_kernel(moe_host::StripArgs g) {
 
       // Epilogue: lane holds column (lane % 16) and rows 4*(lane / 16) + i of
       // each 16 x 16 block.
+      if constexpr (I8) {   // int32 sums to fp32
+  #pragma unroll
+        for (int m = 0; m < MB; m++)
+  #pragma unroll
+          for (int q = 0; q < NSUB; q++)
+            acc[m][q] = __builtin_convertvector(__builtin_bit_cast(i32x4_t, acc[m][q]), f32x4);
+      }
       // SiLU-and-mul in this epilogue (gate-up, one K slice): bf16 h, or on
       // fp8 the fp32 h that the requantisation pass turns into codes (it
       // finds each row's amax from the row: folding it here would take one
@@ -366,29 +384,32 @@ strip_gemm_kernel(moe_host::StripArgs g) {
   else body(std::true_type{});
 }
 
-template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8>
+template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8, bool I8>
 static hipError_t launch_strip_t(const moe_host::StripArgs& a, int grid, hipStream_t s) {
   constexpr int lds_bytes = (NBUF + 1) * MB * KS * 1024;
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8>),
+        reinterpret_cast<const void*>(&strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8, I8>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8>), dim3(grid),
+  hipLaunchKernelGGL((strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8, I8>), dim3(grid),
                      dim3(strip_waves<NSUB>() * 64), lds_bytes, s, a);
   return hipGetLastError();
 }
 
+// kind: 0 bf16, 1 fp8, 2 int8 (one-byte per-channel path with the integer MFMA)
 template <int MB, int KS, int NBUF, int NSUB>
-static hipError_t launch_strip_cfg(const moe_host::StripArgs& a, bool gather, bool fp8, int grid,
+static hipError_t launch_strip_cfg(const moe_host::StripArgs& a, bool gather, int kind, int grid,
                                    hipStream_t s) {
-  if (gather) return fp8 ? launch_strip_t<MB, KS, NBUF, NSUB, true, true>(a, grid, s)
-                         : launch_strip_t<MB, KS, NBUF, NSUB, true, false>(a, grid, s);
-  return fp8 ? launch_strip_t<MB, KS, NBUF, NSUB, false, true>(a, grid, s)
-             : launch_strip_t<MB, KS, NBUF, NSUB, false, false>(a, grid, s);
+  if (kind == 2) return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, true>(a, grid, s)
+                               : launch_strip_t<MB, KS, NBUF, NSUB, false, true, true>(a, grid, s);
+  if (gather) return kind == 1 ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false>(a, grid, s)
+                               : launch_strip_t<MB, KS, NBUF, NSUB, true, false, false>(a, grid, s);
+  return kind == 1 ? launch_strip_t<MB, KS, NBUF, NSUB, false, true, false>(a, grid, s)
+                   : launch_strip_t<MB, KS, NBUF, NSUB, false, false, false>(a, grid, s);
 }
 
 }  // namespace moe
@@ -411,9 +432,11 @@ bool strip_config_supported(int mb, int ks, int nbuf, bool fp8) {
 }
 
 hipError_t launch_strip_gemm(const StripArgs& a, bool gather, bool fp8, int mb, int ks, int nbuf,
-                             int grid, hipStream_t s) {
+                             int grid, hipStream_t s, bool i8) {
+  const int kind = i8 ? 2 : (fp8 ? 1 : 0);
+  if (i8 && !fp8) return hipErrorInvalidValue;
 #define MOE_STRIP_CASE(M, K, N) \
-  if (mb == M && ks == K && nbuf == N) return moe::launch_strip_cfg<M, K, N, 2>(a, gather, fp8, grid, s);
+  if (mb == M && ks == K && nbuf == N) return moe::launch_strip_cfg<M, K, N, 2>(a, gather, kind, grid, s);
   MOE_STRIP_CONFIGS(MOE_STRIP_CASE)
 #undef MOE_STRIP_CASE
   return hipErrorInvalidValue;

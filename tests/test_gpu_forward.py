@@ -471,8 +471,10 @@ def test_empty_batch_is_a_no_op(lib):
 @pytest.mark.parametrize("E,H,I,k,T,dtype", [
     (16, 256, 192, 4, 33, "bf16"),      # register streaming
     (8, 3072, 256, 2, 64, "bf16"),      # register streaming, 32-row tiles, four weight blocks per item
-    (16, 256, 192, 4, 1, "bf16"),       # one token
-    (16, 256, 192, 4, 1, "fp8"),
+    (16, 256, 192, 4, 1, "bf16"),       # one token: down with the top-k sum, 16-column items
+    (16, 256, 192, 4, 1, "fp8"),        # one token, odd fp8 step count: down + reduction
+    (16, 256, 256, 4, 1, "bf16"),       # one token: down with the top-k sum, 8-column items
+    (16, 256, 256, 4, 1, "fp8"),
     (32, 512, 256, 4, 256, "bf16"),     # strips
     (32, 512, 256, 4, 256, "fp8"),      # strips, fp8
     (8, 256, 192, 2, 700, "bf16"),      # LDS tiles

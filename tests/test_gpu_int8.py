@@ -66,6 +66,48 @@ def test_int8_layer_parity(lib, E, H, I, k, T, p_drop):
     check_tol(out.float().cpu().numpy(), ref_out(x, ids, w, W), "int8", f"int8 E={E} T={T}")
 
 
+# Strips (from 24 mean rows per expert): 64-, 128- and 192-row tiles, the
+# down reduction unsplit or split into fp32 partial sums (2 and 8 slices).
+STRIP_SHAPES = [
+    # E, H, I, k, T, p_drop, block_m, split_k2
+    (128, 512, 512, 8, 400, 0.02, 64, 1),
+    (16, 256, 256, 8, 100, 0.0, 128, 1),
+    (64, 512, 512, 8, 1200, 0.0, 192, 2),
+    (32, 256, 2048, 4, 200, 0.05, 64, 8),
+]
+
+
+@pytest.mark.parametrize("E,H,I,k,T,p_drop,bm,s2", STRIP_SHAPES)
+def test_int8_strip_shapes(lib, E, H, I, k, T, p_drop, bm, s2):
+    log(f"int8 strips E={E} H={H} I={I} k={k} T={T} p_drop={p_drop}")
+    L = lib.moe_workspace_layout(T, k, E, H, I, "int8")
+    assert L["tiling"] == 2 and L["split_k1"] == 1 and L["split_k2"] == s2
+    assert lib.moe_routing_layout(T, k, E, H, I, "int8")["block_m"] == bm
+    wl = custom_workload(E, H, I, k, dtype="int8", seed=E + T + 5)
+    W = make_weights(wl)
+    x, _, _ = make_tokens(wl, T, seed=T + 6)
+    ids = random_ids(T, k, E, seed=T + 7, p_drop=p_drop)
+    w = random_weights_w(T, k, seed=T + 8)
+    out, routing, ws = run(lib, x, ids, w, W)
+    ref, _, _, hq_ref, sh_ref = ref_out(x, ids, w, W, want_quant=True)
+    # the requantised intermediate, at the rows of the valid pairs
+    R = lib.read_routing(routing, T, k, E, H, I, "int8")
+    pos = R["pos"].numpy().reshape(T, k)
+    valid = (ids.numpy() >= 0) & (ids.numpy() < E)
+    b = ws.cpu()
+    P = T * k
+    hq = b[L["h"]:L["h"] + P * I].view(torch.int8).numpy().reshape(P, I)[pos[valid]]
+    sh = b[L["h_scale"]:L["h_scale"] + 4 * P].view(torch.float32).numpy()[pos[valid]]
+    hr = hq_ref.reshape(T, k, I)[valid]
+    sr = sh_ref.reshape(T, k)[valid]
+    same = (hq == hr).mean()
+    log(f"  h codes equal {same:.4f}, max scale rel diff {np.abs(sh / sr - 1).max():.2e}")
+    assert same >= 0.99
+    assert np.abs(hq.astype(int) - hr.astype(int)).max() <= 1
+    assert np.abs(sh / sr - 1).max() <= 1e-6
+    check_tol(out.float().cpu().numpy(), ref, "int8", f"int8 strips E={E} T={T}")
+
+
 def test_int8_quant_and_requant(lib):
     E, H, I, k, T = 16, 512, 256, 4, 24
     wl = custom_workload(E, H, I, k, dtype="int8", seed=9)
