@@ -18,6 +18,12 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
 }
 
+// global_load_lds_dword: each lane copies 4 bytes; one wave instruction fills
+// 256 bytes at lds_dst (lane l writes bytes 4l..4l+3).
+__device__ __forceinline__ void dma4(const void* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 4, 0, 0);
+}
+
 // Workgroup barrier without a memory fence (a fence would drain every
 // in-flight load); the empty asm statements keep the compiler from moving
 // memory accesses across it.

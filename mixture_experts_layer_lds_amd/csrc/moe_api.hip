@@ -117,13 +117,14 @@ void choose_stream(int nsteps, int mb, long items, int* waves, int* u) {
 // power-of-two K split whose items spread evenly (>= 80%) over the CUs, else
 // the best-spread one.  Returns false if no configuration divides the
 // reduction.
-bool choose_strip(int nsteps, int mb, bool fp8, long items, int* split, int* ks, int* nbuf) {
+bool choose_strip(int nsteps, int mb, bool fp8, long items, int* split, int* ks, int* nbuf,
+                  bool even_ks = false) {
   // about 12-24 KiB of weights in flight per wave first
   static const int kCfg[8][2] = {{2, 4}, {4, 3}, {4, 4}, {2, 3}, {4, 2}, {1, 4}, {2, 2}, {1, 2}};
   double best_eff = -1.0;
   for (int S = 1; S <= 8; S *= 2) {
     for (const auto& c : kCfg) {
-      if (!moe_host::strip_config_supported(mb, c[0], c[1], fp8)) continue;
+      if (!moe_host::strip_config_supported(mb, c[0], c[1], fp8) || (even_ks && c[0] % 2)) continue;
       if (nsteps % (c[0] * S)) continue;
       const int nk = nsteps / (c[0] * S);
       if (nk < c[1] || nk % c[1]) continue;
@@ -187,6 +188,30 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
   const long avg = active > 0 ? (P + active - 1) / active : 1;
   const int esz_t = dtype == MOE_DTYPE_BF16 ? 2 : 1;
   const int nsteps1 = H * esz_t / 64, nsteps2 = I * esz_t / 64;
+  if (dtype == MOE_DTYPE_FP8_BLOCK && avg >= kOneByteStripMin && avg <= 160 && (2 * I) % kStripCols == 0 &&
+      H % kStripCols == 0) {
+    // [128,128] block fp8 with many rows per expert: the strips, each
+    // 128-value unit rescaled by its row group and weight block scales, with
+    // the fp8 tile heights (192-row tiles spill ten registers here and are
+    // still ahead: DeepSeek-V3 T=4096 3653 us on 128-row tiles, 3463 us on
+    // 192), an unsplit gate-up (its epilogue forms the fp32 h of the group
+    // requantisation)
+    const int first = avg <= 40 ? 4 : (avg <= 96 ? 8 : 12);
+    for (int mb = first; mb <= 12; mb = mb == 8 ? 12 : mb * 2) {
+      long tasks = (P + 16 * mb - 1) / (16 * mb);
+      if (tasks < active) tasks = active;
+      Plan q = p;
+      if (choose_strip(nsteps1, mb, true, tasks * (2L * I / kStripCols), &q.split1, &q.ks1, &q.nbuf1, true) &&
+          q.split1 == 1 &&
+          choose_strip(nsteps2, mb, true, tasks * ((long)H / kStripCols), &q.split2, &q.ks2, &q.nbuf2, true)) {
+        q.tiling = kStrips;
+        q.mb = mb;
+        q.block_m = 16 * mb;
+        q.max_tasks = (int)(P / q.block_m + (P < E ? P : E));
+        return q;
+      }
+    }
+  }
   if (dtype == MOE_DTYPE_INT4_W4A16 || dtype == MOE_DTYPE_FP8_BLOCK || dtype == MOE_DTYPE_INT8_W8A16) {
     // int4 and int8 weights, block-scaled fp8: register streaming (128-value K steps;
     // int8: 64-value steps) at every size; waves per workgroup by the streaming cost
@@ -427,15 +452,17 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
     return at;
   };
   if (dtype == MOE_DTYPE_FP8_BLOCK) {   // e4m3 codes, group scales per token and per sorted row
+    const int s2 = p.tiling == kStrips ? p.split2 : 1;
     W->xq = take((size_t)T * H);
     W->x_scale = take(4 * (size_t)T * (H / 128));
     W->x_scale_rows = take(4 * P * (H / 128));
     W->g = take(4 * P * I);
     W->h = take(P * I);
     W->h_scale = take(4 * P * (I / 128));
-    W->y = take(2 * P * H);
+    W->y = s2 == 1 ? take(2 * P * H) : take(4 * (size_t)s2 * P * H);
     W->total_bytes = off;
-    W->split_k1 = W->split_k2 = 1;
+    W->split_k1 = 1;
+    W->split_k2 = s2;
     W->tiling = p.tiling;
     return;
   }
@@ -766,6 +793,67 @@ int forward_fp8b(const void* x, const float* topk_w, const void* routing, const 
                                            R.pair_pos, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
+  if (p.tiling == kStrips) {
+    // strips: gate-up with SiLU(gate)*up in its epilogue (fp32 h), group
+    // requantisation, down (bf16 rows, or fp32 partial sums of split_k2
+    // slices), reduction; every product already carries both scales
+    const bool y_bf16 = p.split2 == 1;
+    {
+      StageScope st(s, 1);
+      moe_host::StripArgs a{};
+      a.a = xq;
+      a.b = w1;
+      a.b_scale = w1_scale;
+      a.rs_u = x_rows;
+      a.sorted_pairs = R.sorted_pairs;
+      a.header = R.header;
+      a.tasks = R.tasks;
+      a.c = h32;
+      a.K = H;
+      a.N = 2 * I;
+      a.P = P;
+      a.topk = k;
+      a.max_tasks = p.max_tasks;
+      a.split = 1;
+      a.out_bf16 = 0;
+      a.act = 1;
+      e = moe_host::launch_strip_gemm(a, true, true, p.mb, p.ks1, p.nbuf1, cus, s, 2);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 2);
+      e = moe_host::launch_requant_groups(h32, P, I, R.expert_offsets, E, hq, h_rows, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 3);
+      moe_host::StripArgs a{};
+      a.a = hq;
+      a.b = w2;
+      a.b_scale = w2_scale;
+      a.rs_u = h_rows;
+      a.sorted_pairs = R.sorted_pairs;
+      a.header = R.header;
+      a.tasks = R.tasks;
+      a.c = ws + W.y;
+      a.K = I;
+      a.N = H;
+      a.P = P;
+      a.topk = k;
+      a.max_tasks = p.max_tasks;
+      a.split = p.split2;
+      a.out_bf16 = y_bf16 ? 1 : 0;
+      e = moe_host::launch_strip_gemm(a, false, true, p.mb, p.ks2, p.nbuf2, cus, s, 2);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 4);
+      e = moe_host::launch_reduce(ws + W.y, y_bf16, p.split2, P, topk_w, R.pair_pos, R.expert_offsets,
+                                  nullptr, E, T, k, H, static_cast<uint16_t*>(out), s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+  }
   {
     StageScope st(s, 1);
     moe_host::StreamArgs a{};
@@ -964,7 +1052,7 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
       a.out_bf16 = 0;
       a.act = 1;
       a.x_scale_rows = x_rows;
-      e = moe_host::launch_strip_gemm(a, true, true, p.mb, p.ks1, p.nbuf1, cus, s, true);
+      e = moe_host::launch_strip_gemm(a, true, true, p.mb, p.ks1, p.nbuf1, cus, s, 1);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
     {
@@ -989,7 +1077,7 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
       a.max_tasks = p.max_tasks;
       a.split = p.split2;
       a.out_bf16 = y_bf16 ? 1 : 0;
-      e = moe_host::launch_strip_gemm(a, false, true, p.mb, p.ks2, p.nbuf2, cus, s, true);
+      e = moe_host::launch_strip_gemm(a, false, true, p.mb, p.ks2, p.nbuf2, cus, s, 1);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
     {

@@ -272,13 +272,17 @@ struct StripArgs {
   // [P][N/2]: bf16, or on fp8 fp32 with the weight and x scales applied
   int act;
   const float* x_scale_rows;    // fp8 / int8 act: x scale of each sorted row [P + 16]
+  // block fp8 (b_scale then [E][N/128][K/128]): group scales of the sorted
+  // rows, unit-major [K/128][P]
+  const float* rs_u;
 };
 
 // (mb, ks, nbuf) = 16-row blocks per tile, 64-byte K steps per stage, stages in flight.
-// i8 (with fp8 set): int8 w8a8 codes and the integer MFMA, scales as on fp8.
+// variant (with fp8 set): 1 int8 w8a8 codes and the integer MFMA, scales as
+// on fp8; 2 block fp8 (even ks, K % 128 == 0, one K slice with act).
 bool strip_config_supported(int mb, int ks, int nbuf, bool fp8);
 hipError_t launch_strip_gemm(const StripArgs& a, bool gather, bool fp8, int mb, int ks, int nbuf,
-                             int grid, hipStream_t s, bool i8 = false);
+                             int grid, hipStream_t s, int variant = 0);
 
 // Register-streaming GEMM with the reduction split over the W waves of a
 // workgroup (few rows per expert).  Gate-up mode writes SiLU(gate)*up (bf16,

@@ -57,7 +57,20 @@ struct StripItem {
   const char* a[NA];           // this lane's token sources (K step and lane offsets applied)
   const char* b;               // this lane's packed-weight source of column block 0
   float bs[NSUB];              // fp8: weight scale of this lane's column in each block
+  // block fp8: this lane's row scale in the stage's copy (float offset at
+  // the item's first stage), and per block q the index of its first unit in
+  // the weight-scale array
+  int sc_off;
+  int wq0[NSUB];
 };
+
+// Block fp8 row scales per stage: KS / 2 units of 16 * MB rows, copied in
+// parts of 64 rows (one 4-byte copy instruction each); wave w copies part
+// w % parts, so every wave issues one instruction per stage.
+template <int MB, int KS>
+constexpr int blk_row_parts() {
+  return MB * KS / 8;
+}
 
 // Distance between a wave's column blocks in the packed weights: adjacent
 // blocks, or with SiLU-and-mul fused the gate block and its up block N/2
@@ -66,7 +79,7 @@ __device__ __forceinline__ size_t strip_block_stride(const moe_host::StripArgs& 
   return (size_t)(g.act ? g.N / 32 : 1) * nsteps * 1024;
 }
 
-template <int MB, int KS, int NSUB, bool GATHER, bool FP8>
+template <int MB, int KS, int NSUB, bool GATHER, bool FP8, bool BLK = false>
 __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::StripArgs& g, int item,
                                                               int n_strips, int nk, size_t row_bytes,
                                                               int nsteps, int wave, int lane) {
@@ -112,11 +125,27 @@ __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::St
 #pragma unroll
   for (int q = 0; q < NSUB; q++) {
     it.bs[q] = 1.0f;
-    if constexpr (FP8) {
+    if constexpr (FP8 && !BLK) {
       const int wcol = g.act ? it.col + q * (g.N / 2) : it.col + 16 * q;   // weight row of block q
       const i32x16_t v = load16_scalar(g.b_scale + (size_t)task.expert * g.N + wcol);
       it.bs[q] = __int_as_float(spread16(v, lane));
     }
+  }
+  it.sc_off = 0;
+  if constexpr (BLK) {
+    // unit-major scales: activations [K/128][P] per sorted row, weights
+    // [E][N/128][K/128] per 128 x 128 block; the K slice starts at unit
+    // step0 / 2
+    const int units = g.K / 128, unit0 = step0 / 2;
+#pragma unroll
+    for (int q = 0; q < NSUB; q++) {
+      const int wrow = g.act ? it.col + q * (g.N / 2) : it.col + 16 * q;
+      it.wq0[q] = (task.expert * (g.N / 128) + wrow / 128) * units + unit0;
+    }
+    const int row = (wave % blk_row_parts<MB, KS>()) * 64 + lane;   // of the stage's KS / 2 units
+    const int uis = row / (16 * MB), r = row % (16 * MB);
+    // rows past the tile re-read its first row
+    it.sc_off = (unit0 + uis) * g.P + task.row_begin + (r < task.rows ? r : 0);
   }
   return it;
 }
@@ -161,16 +190,21 @@ struct WeightStage<KS, NSUB, true> {
   __device__ __forceinline__ const i32x8& unit(int u2, int q) const { return r[u2][q]; }
 };
 
-template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8, bool I8 = false>
+template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8, bool I8 = false, bool BLK = false>
 __global__ void __launch_bounds__(strip_waves<NSUB>() * 64, 1)
 strip_gemm_kernel(moe_host::StripArgs g) {
   static_assert(!I8 || FP8, "int8 uses the one-byte per-channel path");
+  static_assert(!BLK || (FP8 && !I8 && KS % 2 == 0), "block fp8: whole 128-value units per stage");
   using It = StripItem<MB, KS, NSUB>;
   constexpr int NA = It::NA;
-  constexpr int PER = NA + KS * NSUB;   // vector-memory operations per wave per stage
+  constexpr int PER = NA + KS * NSUB + (BLK ? 1 : 0);   // vector-memory operations per wave per stage
   constexpr int NST = NBUF + 1;         // LDS ring slots
-  constexpr int SLOT = MB * KS * 1024;
+  constexpr int TOK = MB * KS * 1024;   // a slot's token chunks
+  constexpr int SLOT = TOK + (BLK ? 1024 : 0);   // block fp8: then the row scales of its units
   constexpr int W = strip_waves<NSUB>();
+  static_assert(!BLK || (blk_row_parts<MB, KS>() >= 1 && blk_row_parts<MB, KS>() * 64 == KS / 2 * MB * 16 &&
+                         blk_row_parts<MB, KS>() <= W && KS / 2 * MB * 64 <= 1024),
+                "row-scale copy parts");
   static_assert(NA >= 1 && NA * W == MB * KS, "token chunks split evenly over waves");
   static_assert(NBUF >= 2, "ring depth");
   static_assert((NBUF - 1) * PER < 64, "vmcnt range");
@@ -208,12 +242,12 @@ strip_gemm_kernel(moe_host::StripArgs g) {
   // the compiler's waits on the weight registers exact.
   auto body = [&](auto nt_tag) {
     constexpr bool NT_B = decltype(nt_tag)::value;
-    It cur = strip_item<MB, KS, NSUB, GATHER, FP8>(g, vid, n_strips, nk, row_bytes, nsteps, wave,
-                                                   lane);
+    It cur = strip_item<MB, KS, NSUB, GATHER, FP8, BLK>(g, vid, n_strips, nk, row_bytes, nsteps, wave,
+                                                        lane);
     It nxt = cur;
     if (n_items > 1)
-      nxt = strip_item<MB, KS, NSUB, GATHER, FP8>(g, vid + G, n_strips, nk, row_bytes, nsteps, wave,
-                                                  lane);
+      nxt = strip_item<MB, KS, NSUB, GATHER, FP8, BLK>(g, vid + G, n_strips, nk, row_bytes, nsteps, wave,
+                                                       lane);
 
     // Every stage issues exactly PER vector-memory operations per wave: the
     // NBUF stages past the last one re-load the last item's first stages
@@ -222,12 +256,30 @@ strip_gemm_kernel(moe_host::StripArgs g) {
     // the same queue on every path.
     constexpr bool PAIRS = FP8 && !I8 && KS % 2 == 0;
     WeightStage<KS, NSUB, PAIRS> bb[NBUF];
-    auto issue = [&](bool in_cur, int kt, int fslot, WeightStage<KS, NSUB, PAIRS>& b) {
+    // block fp8: each stage's weight block scales (wave-uniform), loaded
+    // NBUF stages ahead through the scalar cache
+    float swb[NBUF][NSUB][KS / 2 > 0 ? KS / 2 : 1];
+    const __attribute__((address_space(4))) float* bsc =
+        (const __attribute__((address_space(4))) float*)(g.b_scale);
+    auto issue = [&](bool in_cur, int kt, int fslot, WeightStage<KS, NSUB, PAIRS>& b,
+                     float (&sw)[NSUB][KS / 2 > 0 ? KS / 2 : 1]) {
       char* sb = lds + fslot * SLOT;
   #pragma unroll
       for (int i = 0; i < NA; i++)
         dma16((in_cur ? cur.a[i] : nxt.a[i]) + (size_t)kt * KS * 64,
               sb + (wave + W * i) * 1024);
+      if constexpr (BLK) {
+        // the stage's row scales, one part per wave (parts copied by several
+        // waves get the same bytes twice; one instruction per wave keeps the
+        // per-stage counts equal)
+        dma4(g.rs_u + ((in_cur ? cur.sc_off : nxt.sc_off) + kt * (KS / 2) * g.P),
+             sb + TOK + (wave % blk_row_parts<MB, KS>()) * 256);
+#pragma unroll
+        for (int q = 0; q < NSUB; q++)
+#pragma unroll
+          for (int v = 0; v < KS / 2; v++)
+            sw[q][v] = bsc[(in_cur ? cur.wq0[q] : nxt.wq0[q]) + kt * (KS / 2) + v];
+      }
       const char* bsrc = in_cur ? cur.b : nxt.b;
   #pragma unroll
       for (int u = 0; u < KS; u++)
@@ -245,7 +297,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
     // counts rely on.
   #pragma unroll
     for (int d = 0; d < NBUF; d++) {
-      issue(true, d, d, bb[d]);
+      issue(true, d, d, bb[d], swb[d]);
       __asm__ volatile("" ::: "memory");
     }
 
@@ -267,7 +319,32 @@ strip_gemm_kernel(moe_host::StripArgs g) {
           wait_vm<(NBUF - 1) * PER>();
           barrier_nofence();
           const char* sb = lds + (fc % NST) * SLOT;
-          if constexpr (PAIRS) {
+          if constexpr (BLK) {
+            // block fp8: each 128-value unit into a fresh sum, then added
+            // times (row group scale x weight block scale)
+            const float* scs = reinterpret_cast<const float*>(sb + TOK);
+  #pragma unroll
+            for (int st = 0; st < KS; st += 2) {
+              const int uis = st >> 1;
+              float sw[NSUB];
+  #pragma unroll
+              for (int q = 0; q < NSUB; q++) sw[q] = swb[u][q][uis];
+  #pragma unroll
+              for (int m = 0; m < MB; m++) {
+                i32x8 a;
+                a.lo = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st) * 1024 + 16 * lane);
+                a.hi = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st + 1) * 1024 + 16 * lane);
+                const f32x4 sx = *reinterpret_cast<const f32x4*>(scs + uis * MB * 16 + 16 * m + 4 * lgrp);
+  #pragma unroll
+                for (int q = 0; q < NSUB; q++) {
+                  f32x4 t = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                  mfma_fp8_unit(t, a, bb[u].unit(st >> 1, q));
+  #pragma unroll
+                  for (int i = 0; i < 4; i++) acc[m][q][i] += t[i] * (sx[i] * sw[q]);
+                }
+              }
+            }
+          } else if constexpr (PAIRS) {
             // two K steps per full-rate fp8 instruction, both operands read
             // into their 8-dword tuples as they are
   #pragma unroll
@@ -296,7 +373,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
           // stage fc-1, which every wave finished reading before the barrier.
           const int ktn = kt0 + u + NBUF;
           const bool in_cur = ktn < nk;
-          issue(in_cur, in_cur ? ktn : ktn - nk, (fc + NBUF) % NST, bb[u]);
+          issue(in_cur, in_cur ? ktn : ktn - nk, (fc + NBUF) % NST, bb[u], swb[u]);
         }
       }
 
@@ -323,7 +400,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
   #pragma unroll
         for (int m = 0; m < MB; m++) {
           float xs[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-          if constexpr (FP8) {
+          if constexpr (FP8 && !BLK) {
             // the block's 16 row scales (rows inside the tile only: the array
             // has 16 entries past its last row, not MB * 16)
             if (16 * m < cur.rows) {
@@ -338,7 +415,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
             const bool ok = rr < cur.rows;
             const size_t r = (size_t)(cur.row_begin + (ok ? rr : 0));
             float gv = acc[m][0][i], uv = acc[m][1][i];
-            if constexpr (FP8) {
+            if constexpr (FP8 && !BLK) {
               gv = (gv * cur.bs[0]) * xs[i];
               uv = (uv * cur.bs[1]) * xs[i];
             }
@@ -362,7 +439,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
               for (int q = 0; q < NSUB; q++) {
                 const int col = cur.col + 16 * q + lrow;
                 float v = acc[m][q][i];
-                if constexpr (FP8) v = v * cur.bs[q];
+                if constexpr (FP8 && !BLK) v = v * cur.bs[q];
                 if (g.out_bf16)
                   static_cast<uint16_t*>(g.c)[r * g.N + col] = f32_to_bf16_bits(v);
                 else
@@ -374,8 +451,8 @@ strip_gemm_kernel(moe_host::StripArgs g) {
       }
       cur = nxt;
       if (ii + 2 < n_items)
-        nxt = strip_item<MB, KS, NSUB, GATHER, FP8>(g, vid + (ii + 2) * G, n_strips, nk, row_bytes,
-                                                    nsteps, wave, lane);
+        nxt = strip_item<MB, KS, NSUB, GATHER, FP8, BLK>(g, vid + (ii + 2) * G, n_strips, nk, row_bytes,
+                                                         nsteps, wave, lane);
     }
     // the trailing re-loads still write this workgroup's LDS: let them land
     wait_vm<0>();
@@ -384,26 +461,33 @@ strip_gemm_kernel(moe_host::StripArgs g) {
   else body(std::true_type{});
 }
 
-template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8, bool I8>
+template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8, bool I8, bool BLK = false>
 static hipError_t launch_strip_t(const moe_host::StripArgs& a, int grid, hipStream_t s) {
-  constexpr int lds_bytes = (NBUF + 1) * MB * KS * 1024;
+  constexpr int lds_bytes = (NBUF + 1) * (MB * KS * 1024 + (BLK ? 1024 : 0));
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8, I8>),
+        reinterpret_cast<const void*>(&strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8, I8, BLK>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8, I8>), dim3(grid),
+  hipLaunchKernelGGL((strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8, I8, BLK>), dim3(grid),
                      dim3(strip_waves<NSUB>() * 64), lds_bytes, s, a);
   return hipGetLastError();
 }
 
-// kind: 0 bf16, 1 fp8, 2 int8 (one-byte per-channel path with the integer MFMA)
+// kind: 0 bf16, 1 fp8, 2 int8 (one-byte per-channel path with the integer
+// MFMA), 3 block fp8 (128 x 128 weight blocks, 128-value activation groups)
 template <int MB, int KS, int NBUF, int NSUB>
 static hipError_t launch_strip_cfg(const moe_host::StripArgs& a, bool gather, int kind, int grid,
                                    hipStream_t s) {
+  if (kind == 3) {
+    if constexpr (KS % 2 == 0)
+      return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false, true>(a, grid, s)
+                    : launch_strip_t<MB, KS, NBUF, NSUB, false, true, false, true>(a, grid, s);
+    return hipErrorInvalidValue;
+  }
   if (kind == 2) return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, true>(a, grid, s)
                                : launch_strip_t<MB, KS, NBUF, NSUB, false, true, true>(a, grid, s);
   if (gather) return kind == 1 ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false>(a, grid, s)
@@ -432,9 +516,10 @@ bool strip_config_supported(int mb, int ks, int nbuf, bool fp8) {
 }
 
 hipError_t launch_strip_gemm(const StripArgs& a, bool gather, bool fp8, int mb, int ks, int nbuf,
-                             int grid, hipStream_t s, bool i8) {
-  const int kind = i8 ? 2 : (fp8 ? 1 : 0);
-  if (i8 && !fp8) return hipErrorInvalidValue;
+                             int grid, hipStream_t s, int variant) {
+  if (variant && !fp8) return hipErrorInvalidValue;
+  if (variant == 2 && (ks % 2 || a.K % 128 || (a.act && a.split != 1))) return hipErrorInvalidValue;
+  const int kind = variant == 1 ? 2 : (variant == 2 ? 3 : (fp8 ? 1 : 0));
 #define MOE_STRIP_CASE(M, K, N) \
   if (mb == M && ks == K && nbuf == N) return moe::launch_strip_cfg<M, K, N, 2>(a, gather, kind, grid, s);
   MOE_STRIP_CONFIGS(MOE_STRIP_CASE)

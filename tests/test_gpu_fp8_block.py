@@ -55,6 +55,13 @@ def e4m3_order(codes):
     return np.where(c & 0x80, -mag, mag)
 
 
+def e4m3_spacing(mag):
+    """Distance to the next e4m3 code above magnitude code mag (0..126):
+    2^-9 for subnormals (exponent field 0), else 2^(e - 10)."""
+    e = (np.asarray(mag).astype(np.int32) >> 3)
+    return np.where(e == 0, 2.0 ** -9, np.exp2(e.astype(np.float64) - 10.0))
+
+
 def e4m3_values(codes):
     return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double()
 
@@ -83,14 +90,18 @@ def dense_h(xq, sx, ids, W):
     s1 = W["w1_scale"].double().repeat_interleave(128, dim=1).repeat_interleave(128, dim=2)
     h = np.zeros((T, k, I))
     bound = np.zeros((T, k, I))
+    cache = {}
     for t in range(T):
         for j in range(k):
             e = int(ids[t, j])
             if not 0 <= e < E:
                 continue
-            wv = e4m3_values(W["w1"][e].numpy())
-            gu = ((wv * s1[e]) @ x[t]).numpy()
-            ab = ((wv.abs().clamp_min(2.0 ** -6) * s1[e]) @ xhat[t]).numpy()
+            if e not in cache:   # the expert's dequantised weights and their bound weights
+                wv = e4m3_values(W["w1"][e].numpy())
+                cache[e] = (wv * s1[e], wv.abs().clamp_min(2.0 ** -6) * s1[e])
+            wd, wb = cache[e]
+            gu = (wd @ x[t]).numpy()
+            ab = (wb @ xhat[t]).numpy()
             g, u = gu[:I], gu[I:]
             sg = g / (1 + np.exp(-g))
             h[t, j] = sg * u
@@ -121,6 +132,61 @@ def test_fp8b_layer_parity(lib, E, H, I, k, T, p_drop):
     check_tol(out.float().cpu().numpy(), ref_out(x, ids, w, W), "fp8b", f"fp8b E={E} T={T}")
 
 
+def check_intermediates(lib, x, ids, w, W, E, H, I, k, T, out, routing, ws, what):
+    """x codes and scales bit-exact, their copies at the sorted rows, the
+    fp32 intermediate within the MFMA's summation bound, its group
+    requantisation (codes and scales), and the layer output."""
+    L = lib.moe_workspace_layout(T, k, E, H, I, "fp8b")
+    b = ws.cpu()
+    xq = b[L["xq"]:L["xq"] + T * H].numpy().reshape(T, H)
+    sx = b[L["x_scale"]:L["x_scale"] + 4 * T * H // 128].view(torch.float32).numpy().reshape(T, H // 128)
+    ref, xq_ref, sx_ref, hq_ref, sh_ref = ref_out(x, ids, w, W, want_quant=True)
+    assert (xq == xq_ref).all() and (sx == sx_ref).all(), "x quantisation differs"
+    R = lib.read_routing(routing, T, k, E, H, I, "fp8b")
+    pos = R["pos"].numpy()
+    P = T * k
+    valid = ((ids.numpy() >= 0) & (ids.numpy() < E)).reshape(T, k)
+    # the scales of x, spread unit-major over the sorted rows of each pair
+    sxr = b[L["x_scale_rows"]:L["x_scale_rows"] + 4 * P * H // 128].view(torch.float32).numpy()
+    sxr = sxr.reshape(H // 128, P)[:, pos].T.reshape(T, k, H // 128)
+    assert (sxr[valid] == np.broadcast_to(sx_ref[:, None, :], sxr.shape)[valid]).all(), "x scales at sorted rows"
+    # the fp32 intermediate against fp64 products of the same codes, each
+    # error within the MFMA's summation bound
+    h32 = b[L["g"]:L["g"] + 4 * P * I].view(torch.float32).numpy().reshape(P, I)[pos].reshape(T, k, I)
+    h64, hbound = dense_h(xq_ref, sx_ref, ids, W)
+    dh = np.where(valid[..., None], np.abs(h32 - h64), 0.0)
+    ratio = np.where(hbound > 0, dh / np.where(hbound > 0, hbound, 1.0), np.where(dh > 0, np.inf, 0.0))
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    log(f"  h max |err|/bound {ratio.max():.3e} at {worst}: gpu {h32[worst]!r} fp64 {h64[worst]!r} "
+        f"bound {hbound[worst]:.3e}")
+    assert (dh <= hbound).all(), "intermediate outside the summation bound"
+    hq = b[L["h"]:L["h"] + P * I].numpy().reshape(P, I)[pos].reshape(T, k, I)
+    sh = b[L["h_scale"]:L["h_scale"] + 4 * P * I // 128].view(torch.float32).numpy()
+    sh = sh.reshape(I // 128, P)[:, pos].T.reshape(T, k, I // 128)
+    same = (hq[valid] == hq_ref[valid]).mean()
+    log(f"  h codes equal {same:.4f}, max scale rel diff {np.abs(sh[valid] / sh_ref[valid] - 1).max():.2e}")
+    assert same >= 0.99
+    # A code is decided on the fp32 intermediate here and on fp64 in the
+    # oracle; the two differ by at most dh.  Where an e4m3 step is larger
+    # than that (normal codes) the codes are at most one apart; in the
+    # subnormal range a step (2^-9 of the scale) can be smaller than dh, so
+    # the gate is on values: one step at the larger code plus dh.
+    step = e4m3_spacing(np.maximum(hq & 0x7F, hq_ref & 0x7F))
+    shx = np.repeat(sh, 128, axis=-1)
+    shrx = np.repeat(sh_ref, 128, axis=-1)
+    vdev = np.abs(e4m3_values(hq).numpy() * shx - e4m3_values(hq_ref).numpy() * shrx)
+    allowed = dh + step * np.maximum(shx, shrx) * (1 + 1e-6)
+    far = np.abs(e4m3_order(hq) - e4m3_order(hq_ref)) > 1
+    log(f"  codes more than one apart: {int(far[valid].sum())}, all subnormal: "
+        f"{bool(((np.maximum(hq & 0x7F, hq_ref & 0x7F) < 8) | ~far)[valid].all())}")
+    assert (vdev <= allowed)[valid].all(), "requantised values beyond one step plus the intermediate error"
+    # a group's scale is its max |h| / 448: it moves by at most the group's
+    # largest intermediate error / 448 (plus the scale's own rounding)
+    gerr = dh.reshape(T, k, I // 128, 128).max(-1) / 448.0
+    assert (np.abs(sh - sh_ref)[valid] <= (gerr * (1 + 1e-6) + 2 * np.spacing(sh_ref))[valid]).all()
+    check_tol(out.float().cpu().numpy(), ref, "fp8b", what)
+
+
 def test_fp8b_quant_and_requant(lib):
     E, H, I, k, T = 16, 512, 256, 4, 24
     wl = custom_workload(E, H, I, k, dtype="fp8b", seed=9)
@@ -133,44 +199,40 @@ def test_fp8b_quant_and_requant(lib):
     w = random_weights_w(T, k, seed=12)
     out, routing, ws = run(lib, x, ids, w, W)
     L = lib.moe_workspace_layout(T, k, E, H, I, "fp8b")
-    b = ws.cpu()
-    xq = b[L["xq"]:L["xq"] + T * H].numpy().reshape(T, H)
-    sx = b[L["x_scale"]:L["x_scale"] + 4 * T * H // 128].view(torch.float32).numpy().reshape(T, H // 128)
-    _, xq_ref, sx_ref, hq_ref, sh_ref = ref_out(x, ids, w, W, want_quant=True)
-    assert (xq == xq_ref).all() and (sx == sx_ref).all(), "x quantisation differs"
+    xq = ws.cpu()[L["xq"]:L["xq"] + T * H].numpy().reshape(T, H)
+    sx = ws.cpu()[L["x_scale"]:L["x_scale"] + 4 * T * H // 128].view(torch.float32).numpy().reshape(T, H // 128)
     for t in range(T):                                 # the oracle's rule, restated per row
         for gi in range(H // 128):
             qc, qs = oracle.quant_groups(x[t, gi * 128:(gi + 1) * 128].bfloat16().float().numpy())
             assert (qc == xq[t, gi * 128:(gi + 1) * 128]).all() and qs[0] == sx[t, gi]
-    R = lib.read_routing(routing, T, k, E, H, I, "fp8b")
-    pos = R["pos"].numpy()
-    P = T * k
-    # the scales of x, spread unit-major over the sorted rows of each pair
-    sxr = b[L["x_scale_rows"]:L["x_scale_rows"] + 4 * P * H // 128].view(torch.float32).numpy()
-    sxr = sxr.reshape(H // 128, P)[:, pos].T.reshape(T, k, H // 128)
-    assert (sxr == sx_ref[:, None, :]).all(), "x scales at sorted rows differ"
-    # the fp32 intermediate against fp64 products of the same codes, each
-    # error within the MFMA's summation bound
-    h32 = b[L["g"]:L["g"] + 4 * P * I].view(torch.float32).numpy().reshape(P, I)[pos].reshape(T, k, I)
-    h64, hbound = dense_h(xq_ref, sx_ref, ids, W)
-    dh = np.abs(h32 - h64)
-    ratio = np.where(hbound > 0, dh / np.where(hbound > 0, hbound, 1.0), np.where(dh > 0, np.inf, 0.0))
-    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
-    log(f"  h max |err|/bound {ratio.max():.3e} at {worst}: gpu {h32[worst]!r} fp64 {h64[worst]!r} "
-        f"bound {hbound[worst]:.3e}")
-    assert (dh <= hbound).all(), "intermediate outside the summation bound"
-    hq = b[L["h"]:L["h"] + P * I].numpy().reshape(P, I)[pos].reshape(T, k, I)
-    sh = b[L["h_scale"]:L["h_scale"] + 4 * P * I // 128].view(torch.float32).numpy()
-    sh = sh.reshape(I // 128, P)[:, pos].T.reshape(T, k, I // 128)
-    same = (hq == hq_ref).mean()
-    log(f"  h codes equal {same:.4f}, max scale rel diff {np.abs(sh / sh_ref - 1).max():.2e}")
-    assert same >= 0.99
-    assert np.abs(e4m3_order(hq) - e4m3_order(hq_ref)).max() <= 1
-    # a group's scale is its max |h| / 448: it moves by at most the group's
-    # largest intermediate error / 448 (plus the scale's own rounding)
-    gerr = dh.reshape(T, k, I // 128, 128).max(-1) / 448.0
-    assert (np.abs(sh - sh_ref) <= gerr * (1 + 1e-6) + 2 * np.spacing(sh_ref)).all()
-    check_tol(out.float().cpu().numpy(), ref_out(x, ids, w, W), "fp8b", "fp8b quant case")
+    check_intermediates(lib, x, ids, w, W, E, H, I, k, T, out, routing, ws, "fp8b quant case")
+
+
+# Strips (from 12 mean rows per expert): each 128-value unit rescaled by its
+# row group and weight block scales; 64-, 128- and 192-row tiles, the down
+# reduction unsplit or split into fp32 partial sums (2 and 8 slices).
+STRIP_SHAPES = [
+    # E, H, I, k, T, p_drop, block_m, split_k2
+    (128, 512, 512, 8, 400, 0.02, 64, 1),
+    (16, 256, 256, 8, 100, 0.0, 128, 1),
+    (32, 256, 2048, 4, 200, 0.05, 64, 8),
+    (128, 256, 512, 8, 1700, 0.01, 192, 2),
+]
+
+
+@pytest.mark.parametrize("E,H,I,k,T,p_drop,bm,s2", STRIP_SHAPES)
+def test_fp8b_strip_shapes(lib, E, H, I, k, T, p_drop, bm, s2):
+    log(f"fp8b strips E={E} H={H} I={I} k={k} T={T} p_drop={p_drop}")
+    L = lib.moe_workspace_layout(T, k, E, H, I, "fp8b")
+    assert L["tiling"] == 2 and L["split_k1"] == 1 and L["split_k2"] == s2
+    assert lib.moe_routing_layout(T, k, E, H, I, "fp8b")["block_m"] == bm
+    wl = custom_workload(E, H, I, k, dtype="fp8b", seed=E + T + 5)
+    W = make_weights(wl)
+    x, _, _ = make_tokens(wl, T, seed=T + 6)
+    ids = random_ids(T, k, E, seed=T + 7, p_drop=p_drop)
+    w = random_weights_w(T, k, seed=T + 8)
+    out, routing, ws = run(lib, x, ids, w, W)
+    check_intermediates(lib, x, ids, w, W, E, H, I, k, T, out, routing, ws, f"fp8b strips E={E} T={T}")
 
 
 def test_fp8b_dsv3_shape_decode(lib):
