@@ -245,20 +245,23 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     p.su1 = p.su2 = 1;
     return p;
   }
-  if (dtype == MOE_DTYPE_INT8_W8A8 && avg >= kOneByteStripMin && avg <= 160 && (2 * I) % kStripCols == 0 &&
-      H % kStripCols == 0) {
-    // int8 w8a8 with many rows per expert: the fp8 strips (same one-byte
-    // layout and per-channel scales) on the integer MFMA, with the fp8 tile
-    // heights; only an unsplit gate-up, whose epilogue forms the fp32 h that
-    // the int8 requantisation reads.
+  if ((dtype == MOE_DTYPE_INT8_W8A8 || dtype == MOE_DTYPE_MXFP8) && avg >= kOneByteStripMin && avg <= 160 &&
+      (2 * I) % kStripCols == 0 && H % kStripCols == 0) {
+    // int8 w8a8 and MXFP8 with many rows per expert: the fp8 strips (the
+    // same one-byte layout) on the integer MFMA (int8, per-channel scales)
+    // or the scaled one (MX: e8m0 codes of rows and weights copied per
+    // stage, whole 128-value units), with the fp8 tile heights; only an
+    // unsplit gate-up, whose epilogue forms the fp32 h that the
+    // requantisation reads.
+    const bool mx = dtype == MOE_DTYPE_MXFP8;
     const int first = avg <= 40 ? 4 : (avg <= 96 ? 8 : 12);
     for (int mb = first; mb <= 12; mb = mb == 8 ? 12 : mb * 2) {
       long tasks = (P + 16 * mb - 1) / (16 * mb);
       if (tasks < active) tasks = active;
       Plan q = p;
-      if (choose_strip(nsteps1, mb, true, tasks * (2L * I / kStripCols), &q.split1, &q.ks1, &q.nbuf1) &&
+      if (choose_strip(nsteps1, mb, true, tasks * (2L * I / kStripCols), &q.split1, &q.ks1, &q.nbuf1, mx) &&
           q.split1 == 1 &&
-          choose_strip(nsteps2, mb, true, tasks * ((long)H / kStripCols), &q.split2, &q.ks2, &q.nbuf2)) {
+          choose_strip(nsteps2, mb, true, tasks * ((long)H / kStripCols), &q.split2, &q.ks2, &q.nbuf2, mx)) {
         q.tiling = kStrips;
         q.mb = mb;
         q.block_m = 16 * mb;
@@ -491,15 +494,17 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
     return;
   }
   if (dtype == MOE_DTYPE_MXFP8) {   // e4m3 codes + e8m0 codes per 32 values
+    const int s2 = p.tiling == kStrips ? p.split2 : 1;
     W->xq = take((size_t)T * H);
     W->x_scale = take((size_t)T * H / 32);
     W->x_scale_rows = kNone;
     W->g = take(4 * P * I);          // fp32 SiLU(gate)*up before requantisation
     W->h = take(P * I);
     W->h_scale = take(P * I / 32);
-    W->y = take(2 * P * H);
+    W->y = s2 == 1 ? take(2 * P * H) : take(4 * (size_t)s2 * P * H);
     W->total_bytes = off;
-    W->split_k1 = W->split_k2 = 1;
+    W->split_k1 = 1;
+    W->split_k2 = s2;
     W->tiling = p.tiling;
     return;
   }
@@ -675,7 +680,7 @@ int forward_mx(const void* x, const float* topk_w, const void* routing, const vo
       !aligned(w1_scale, 4) || !aligned(w2_scale, 4))
     return MOE_ERR_INVALID_ARG;
   const Plan p = make_plan(MOE_DTYPE_MXFP8, T, k, E, H, I);
-  if (p.su1 != 2 || p.su2 != 2) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (p.tiling == kStreaming && (p.su1 != 2 || p.su2 != 2)) return MOE_ERR_UNSUPPORTED_SHAPE;
   moe_routing_layout_t L;
   routing_layout(T, k, E, p, &L);
   moe_workspace_layout_t W;
@@ -697,6 +702,67 @@ int forward_mx(const void* x, const float* topk_w, const void* routing, const vo
     StageScope st(s, 0);
     e = moe_host::launch_mx_quant_bf16(static_cast<const uint16_t*>(x), T, H, xq, sx, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (p.tiling == kStrips) {
+    // strips: gate-up with SiLU(gate)*up in its epilogue (fp32 h), MX
+    // requantisation, down (bf16 rows, or fp32 partial sums of split_k2
+    // slices), reduction; the scaled instruction applies every e8m0 code
+    const bool y_bf16 = p.split2 == 1;
+    {
+      StageScope st(s, 1);
+      moe_host::StripArgs a{};
+      a.a = xq;
+      a.a_mx = sx;
+      a.b = w1;
+      a.b_mx = w1_scale;
+      a.sorted_pairs = R.sorted_pairs;
+      a.header = R.header;
+      a.tasks = R.tasks;
+      a.c = h32;
+      a.K = H;
+      a.N = 2 * I;
+      a.P = P;
+      a.topk = k;
+      a.max_tasks = p.max_tasks;
+      a.split = 1;
+      a.out_bf16 = 0;
+      a.act = 1;
+      e = moe_host::launch_strip_gemm(a, true, true, p.mb, p.ks1, p.nbuf1, cus, s, 3);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 2);
+      e = moe_host::launch_mx_requant(h32, P, I, R.expert_offsets, E, hq, sh, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 3);
+      moe_host::StripArgs a{};
+      a.a = hq;
+      a.a_mx = sh;
+      a.b = w2;
+      a.b_mx = w2_scale;
+      a.sorted_pairs = R.sorted_pairs;
+      a.header = R.header;
+      a.tasks = R.tasks;
+      a.c = ws + W.y;
+      a.K = I;
+      a.N = H;
+      a.P = P;
+      a.topk = k;
+      a.max_tasks = p.max_tasks;
+      a.split = p.split2;
+      a.out_bf16 = y_bf16 ? 1 : 0;
+      e = moe_host::launch_strip_gemm(a, false, true, p.mb, p.ks2, p.nbuf2, cus, s, 3);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    {
+      StageScope st(s, 4);
+      e = moe_host::launch_reduce(ws + W.y, y_bf16, p.split2, P, topk_w, R.pair_pos, R.expert_offsets,
+                                  nullptr, E, T, k, H, static_cast<uint16_t*>(out), s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
   }
   {
     StageScope st(s, 1);

@@ -275,11 +275,15 @@ struct StripArgs {
   // block fp8 (b_scale then [E][N/128][K/128]): group scales of the sorted
   // rows, unit-major [K/128][P]
   const float* rs_u;
+  // MXFP8: e8m0 codes of a's rows ([T][K/32] per token when gathered, else
+  // [P][K/32] per sorted row) and of the weights [E][N][K/32]
+  const uint8_t* a_mx;
+  const uint8_t* b_mx;
 };
 
 // (mb, ks, nbuf) = 16-row blocks per tile, 64-byte K steps per stage, stages in flight.
 // variant (with fp8 set): 1 int8 w8a8 codes and the integer MFMA, scales as
-// on fp8; 2 block fp8 (even ks, K % 128 == 0, one K slice with act).
+// on fp8; 2 block fp8, 3 MXFP8 (even ks, K % 128 == 0, one K slice with act).
 bool strip_config_supported(int mb, int ks, int nbuf, bool fp8);
 hipError_t launch_strip_gemm(const StripArgs& a, bool gather, bool fp8, int mb, int ks, int nbuf,
                              int grid, hipStream_t s, int variant = 0);

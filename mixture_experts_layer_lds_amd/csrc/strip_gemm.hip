@@ -62,6 +62,10 @@ struct StripItem {
   // the weight-scale array
   int sc_off;
   int wq0[NSUB];
+  // MXFP8: this lane's weight row scale dword in the stage's copy (byte
+  // offset from wmx, the expert's e8m0 codes)
+  int sc_woff;
+  const uint8_t* wmx;
 };
 
 // Block fp8 row scales per stage: KS / 2 units of 16 * MB rows, copied in
@@ -79,7 +83,7 @@ __device__ __forceinline__ size_t strip_block_stride(const moe_host::StripArgs& 
   return (size_t)(g.act ? g.N / 32 : 1) * nsteps * 1024;
 }
 
-template <int MB, int KS, int NSUB, bool GATHER, bool FP8, bool BLK = false>
+template <int MB, int KS, int NSUB, bool GATHER, bool FP8, int SC = 0>
 __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::StripArgs& g, int item,
                                                               int n_strips, int nk, size_t row_bytes,
                                                               int nsteps, int wave, int lane) {
@@ -125,14 +129,50 @@ __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::St
 #pragma unroll
   for (int q = 0; q < NSUB; q++) {
     it.bs[q] = 1.0f;
-    if constexpr (FP8 && !BLK) {
+    if constexpr (FP8 && SC == 0) {
       const int wcol = g.act ? it.col + q * (g.N / 2) : it.col + 16 * q;   // weight row of block q
       const i32x16_t v = load16_scalar(g.b_scale + (size_t)task.expert * g.N + wcol);
       it.bs[q] = __int_as_float(spread16(v, lane));
     }
   }
   it.sc_off = 0;
-  if constexpr (BLK) {
+  it.sc_woff = 0;
+  it.wmx = nullptr;
+  if constexpr (SC == 2) {
+    // MXFP8: e8m0 codes, K / 32 bytes per row, one dword per row and
+    // 128-value unit; the K slice starts at unit step0 / 2
+    const int kb = g.K / 32, unit0 = step0 / 2;
+    // row scales: the lane's row of the part this wave copies (64 rows of
+    // one unit); rows past the tile take the tile's first row
+    const int lin = (wave % blk_row_parts<MB, KS>()) * 64;
+    const int uis = lin / (16 * MB), rb0 = lin % (16 * MB);
+    const int r = rb0 + lane;
+    int srow;
+    if constexpr (GATHER) {   // the token of the row (scalar loads of 16 indices)
+      const i32x16_t s0 = load16_scalar(g.sorted_pairs + task.row_begin);
+      int tk = s0[0];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (rb0 + 16 * j < task.rows) {
+          const i32x16_t sj = load16_scalar(g.sorted_pairs + task.row_begin + rb0 + 16 * j);
+          const int v = spread16(sj, lane);
+          tk = (lane >> 4) == j ? v : tk;
+        }
+      }
+      srow = (r < task.rows ? tk : s0[0]) / g.topk;
+    } else {
+      srow = task.row_begin + (r < task.rows ? r : 0);
+    }
+    it.sc_off = srow * kb + (unit0 + uis) * 4;
+    // weight scales: the rows of the wave's blocks, KS / 2 units (lanes
+    // past them repeat the first ones)
+    const int jw = lane % (KS / 2 * NSUB * 16);
+    const int wu = jw / (NSUB * 16), wq = (jw / 16) % NSUB, wc = jw % 16;
+    const int wrow = (g.act ? it.col + wq * (g.N / 2) : it.col + 16 * wq) + wc;
+    it.wmx = g.b_mx + (size_t)task.expert * g.N * kb;
+    it.sc_woff = wrow * kb + (unit0 + wu) * 4;
+  }
+  if constexpr (SC == 1) {
     // unit-major scales: activations [K/128][P] per sorted row, weights
     // [E][N/128][K/128] per 128 x 128 block; the K slice starts at unit
     // step0 / 2
@@ -190,21 +230,27 @@ struct WeightStage<KS, NSUB, true> {
   __device__ __forceinline__ const i32x8& unit(int u2, int q) const { return r[u2][q]; }
 };
 
-template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8, bool I8 = false, bool BLK = false>
+template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8, bool I8 = false, int SC = 0>
 __global__ void __launch_bounds__(strip_waves<NSUB>() * 64, 1)
 strip_gemm_kernel(moe_host::StripArgs g) {
-  static_assert(!I8 || FP8, "int8 uses the one-byte per-channel path");
-  static_assert(!BLK || (FP8 && !I8 && KS % 2 == 0), "block fp8: whole 128-value units per stage");
+  constexpr bool BLK = SC == 1, MXS = SC == 2;
+  static_assert(!I8 || (FP8 && SC == 0), "int8 uses the one-byte per-channel path");
+  static_assert(SC == 0 || (FP8 && KS % 2 == 0), "block scales: whole 128-value units per stage");
   using It = StripItem<MB, KS, NSUB>;
   constexpr int NA = It::NA;
-  constexpr int PER = NA + KS * NSUB + (BLK ? 1 : 0);   // vector-memory operations per wave per stage
+  // vector-memory operations per wave per stage: token chunks, weights, and
+  // the scale copies (block fp8: row scales; MXFP8: row and weight scales)
+  constexpr int PER = NA + KS * NSUB + (BLK ? 1 : (MXS ? 2 : 0));
   constexpr int NST = NBUF + 1;         // LDS ring slots
   constexpr int TOK = MB * KS * 1024;   // a slot's token chunks
-  constexpr int SLOT = TOK + (BLK ? 1024 : 0);   // block fp8: then the row scales of its units
   constexpr int W = strip_waves<NSUB>();
-  static_assert(!BLK || (blk_row_parts<MB, KS>() >= 1 && blk_row_parts<MB, KS>() * 64 == KS / 2 * MB * 16 &&
-                         blk_row_parts<MB, KS>() <= W && KS / 2 * MB * 64 <= 1024),
+  constexpr int RSB = KS / 2 * MB * 64;   // then the row scales (4 bytes per row and unit)
+  // then (MXFP8) 256 bytes of weight scales per wave
+  constexpr int SLOT = TOK + (BLK ? 1024 : (MXS ? RSB + W * 256 : 0));
+  static_assert(SC == 0 || (blk_row_parts<MB, KS>() >= 1 && blk_row_parts<MB, KS>() * 64 == KS / 2 * MB * 16 &&
+                            blk_row_parts<MB, KS>() <= W && RSB <= 1024),
                 "row-scale copy parts");
+  static_assert(!MXS || KS / 2 * NSUB * 16 <= 64, "one weight-scale copy per wave");
   static_assert(NA >= 1 && NA * W == MB * KS, "token chunks split evenly over waves");
   static_assert(NBUF >= 2, "ring depth");
   static_assert((NBUF - 1) * PER < 64, "vmcnt range");
@@ -242,12 +288,12 @@ strip_gemm_kernel(moe_host::StripArgs g) {
   // the compiler's waits on the weight registers exact.
   auto body = [&](auto nt_tag) {
     constexpr bool NT_B = decltype(nt_tag)::value;
-    It cur = strip_item<MB, KS, NSUB, GATHER, FP8, BLK>(g, vid, n_strips, nk, row_bytes, nsteps, wave,
-                                                        lane);
+    It cur = strip_item<MB, KS, NSUB, GATHER, FP8, SC>(g, vid, n_strips, nk, row_bytes, nsteps, wave,
+                                                       lane);
     It nxt = cur;
     if (n_items > 1)
-      nxt = strip_item<MB, KS, NSUB, GATHER, FP8, BLK>(g, vid + G, n_strips, nk, row_bytes, nsteps, wave,
-                                                       lane);
+      nxt = strip_item<MB, KS, NSUB, GATHER, FP8, SC>(g, vid + G, n_strips, nk, row_bytes, nsteps, wave,
+                                                      lane);
 
     // Every stage issues exactly PER vector-memory operations per wave: the
     // NBUF stages past the last one re-load the last item's first stages
@@ -279,6 +325,14 @@ strip_gemm_kernel(moe_host::StripArgs g) {
 #pragma unroll
           for (int v = 0; v < KS / 2; v++)
             sw[q][v] = bsc[(in_cur ? cur.wq0[q] : nxt.wq0[q]) + kt * (KS / 2) + v];
+      }
+      if constexpr (MXS) {
+        // the stage's row scale dwords (one part of 64 rows per wave, as on
+        // block fp8) and the wave's own weight scale dwords
+        dma4(g.a_mx + ((in_cur ? cur.sc_off : nxt.sc_off) + kt * (KS / 2) * 4),
+             sb + TOK + (wave % blk_row_parts<MB, KS>()) * 256);
+        dma4((in_cur ? cur.wmx : nxt.wmx) + ((in_cur ? cur.sc_woff : nxt.sc_woff) + kt * (KS / 2) * 4),
+             sb + TOK + RSB + wave * 256);
       }
       const char* bsrc = in_cur ? cur.b : nxt.b;
   #pragma unroll
@@ -319,7 +373,30 @@ strip_gemm_kernel(moe_host::StripArgs g) {
           wait_vm<(NBUF - 1) * PER>();
           barrier_nofence();
           const char* sb = lds + (fc % NST) * SLOT;
-          if constexpr (BLK) {
+          if constexpr (MXS) {
+            // MXFP8: the scaled instruction applies the lane's e8m0 codes,
+            // lane 16 g + r those of K block g of row / column r
+            const uint32_t* rsc = reinterpret_cast<const uint32_t*>(sb + TOK);
+            const uint32_t* wsc = reinterpret_cast<const uint32_t*>(sb + TOK + RSB + wave * 256);
+  #pragma unroll
+            for (int st = 0; st < KS; st += 2) {
+              const int uis = st >> 1;
+              int sbq[NSUB];
+  #pragma unroll
+              for (int q = 0; q < NSUB; q++) sbq[q] = (int)(wsc[(uis * NSUB + q) * 16 + lrow] >> (8 * lgrp));
+  #pragma unroll
+              for (int m = 0; m < MB; m++) {
+                i32x8 a;
+                a.lo = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st) * 1024 + 16 * lane);
+                a.hi = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st + 1) * 1024 + 16 * lane);
+                const int sa = (int)(rsc[uis * 16 * MB + 16 * m + lrow] >> (8 * lgrp));
+  #pragma unroll
+                for (int q = 0; q < NSUB; q++)
+                  acc[m][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bb[u].unit(uis, q), acc[m][q], 0,
+                                                                              0, 0, sa, 0, sbq[q]);
+              }
+            }
+          } else if constexpr (BLK) {
             // block fp8: each 128-value unit into a fresh sum, then added
             // times (row group scale x weight block scale)
             const float* scs = reinterpret_cast<const float*>(sb + TOK);
@@ -400,7 +477,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
   #pragma unroll
         for (int m = 0; m < MB; m++) {
           float xs[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-          if constexpr (FP8 && !BLK) {
+          if constexpr (FP8 && SC == 0) {
             // the block's 16 row scales (rows inside the tile only: the array
             // has 16 entries past its last row, not MB * 16)
             if (16 * m < cur.rows) {
@@ -415,7 +492,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
             const bool ok = rr < cur.rows;
             const size_t r = (size_t)(cur.row_begin + (ok ? rr : 0));
             float gv = acc[m][0][i], uv = acc[m][1][i];
-            if constexpr (FP8 && !BLK) {
+            if constexpr (FP8 && SC == 0) {
               gv = (gv * cur.bs[0]) * xs[i];
               uv = (uv * cur.bs[1]) * xs[i];
             }
@@ -439,7 +516,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
               for (int q = 0; q < NSUB; q++) {
                 const int col = cur.col + 16 * q + lrow;
                 float v = acc[m][q][i];
-                if constexpr (FP8 && !BLK) v = v * cur.bs[q];
+                if constexpr (FP8 && SC == 0) v = v * cur.bs[q];
                 if (g.out_bf16)
                   static_cast<uint16_t*>(g.c)[r * g.N + col] = f32_to_bf16_bits(v);
                 else
@@ -451,8 +528,8 @@ strip_gemm_kernel(moe_host::StripArgs g) {
       }
       cur = nxt;
       if (ii + 2 < n_items)
-        nxt = strip_item<MB, KS, NSUB, GATHER, FP8, BLK>(g, vid + (ii + 2) * G, n_strips, nk, row_bytes,
-                                                         nsteps, wave, lane);
+        nxt = strip_item<MB, KS, NSUB, GATHER, FP8, SC>(g, vid + (ii + 2) * G, n_strips, nk, row_bytes,
+                                                        nsteps, wave, lane);
     }
     // the trailing re-loads still write this workgroup's LDS: let them land
     wait_vm<0>();
@@ -461,31 +538,37 @@ strip_gemm_kernel(moe_host::StripArgs g) {
   else body(std::true_type{});
 }
 
-template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8, bool I8, bool BLK = false>
+template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8, bool I8, int SC = 0>
 static hipError_t launch_strip_t(const moe_host::StripArgs& a, int grid, hipStream_t s) {
-  constexpr int lds_bytes = (NBUF + 1) * (MB * KS * 1024 + (BLK ? 1024 : 0));
+  constexpr int lds_bytes =
+      (NBUF + 1) * (MB * KS * 1024 + (SC == 1 ? 1024 : (SC == 2 ? KS / 2 * MB * 64 + strip_waves<NSUB>() * 256 : 0)));
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8, I8, BLK>),
+        reinterpret_cast<const void*>(&strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8, I8, SC>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8, I8, BLK>), dim3(grid),
+  hipLaunchKernelGGL((strip_gemm_kernel<MB, KS, NBUF, NSUB, GATHER, FP8, I8, SC>), dim3(grid),
                      dim3(strip_waves<NSUB>() * 64), lds_bytes, s, a);
   return hipGetLastError();
 }
 
 // kind: 0 bf16, 1 fp8, 2 int8 (one-byte per-channel path with the integer
-// MFMA), 3 block fp8 (128 x 128 weight blocks, 128-value activation groups)
+// MFMA), 3 block fp8 (128 x 128 weight blocks, 128-value activation groups),
+// 4 MXFP8 (e8m0 codes per 32 values of both operands)
 template <int MB, int KS, int NBUF, int NSUB>
 static hipError_t launch_strip_cfg(const moe_host::StripArgs& a, bool gather, int kind, int grid,
                                    hipStream_t s) {
-  if (kind == 3) {
-    if constexpr (KS % 2 == 0)
-      return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false, true>(a, grid, s)
-                    : launch_strip_t<MB, KS, NBUF, NSUB, false, true, false, true>(a, grid, s);
+  if (kind == 3 || kind == 4) {
+    if constexpr (KS % 2 == 0) {
+      if (kind == 3)
+        return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false, 1>(a, grid, s)
+                      : launch_strip_t<MB, KS, NBUF, NSUB, false, true, false, 1>(a, grid, s);
+      return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false, 2>(a, grid, s)
+                    : launch_strip_t<MB, KS, NBUF, NSUB, false, true, false, 2>(a, grid, s);
+    }
     return hipErrorInvalidValue;
   }
   if (kind == 2) return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, true>(a, grid, s)
@@ -518,8 +601,8 @@ bool strip_config_supported(int mb, int ks, int nbuf, bool fp8) {
 hipError_t launch_strip_gemm(const StripArgs& a, bool gather, bool fp8, int mb, int ks, int nbuf,
                              int grid, hipStream_t s, int variant) {
   if (variant && !fp8) return hipErrorInvalidValue;
-  if (variant == 2 && (ks % 2 || a.K % 128 || (a.act && a.split != 1))) return hipErrorInvalidValue;
-  const int kind = variant == 1 ? 2 : (variant == 2 ? 3 : (fp8 ? 1 : 0));
+  if (variant >= 2 && (ks % 2 || a.K % 128 || (a.act && a.split != 1))) return hipErrorInvalidValue;
+  const int kind = variant == 1 ? 2 : (variant == 2 ? 3 : (variant == 3 ? 4 : (fp8 ? 1 : 0)));
 #define MOE_STRIP_CASE(M, K, N) \
   if (mb == M && ks == K && nbuf == N) return moe::launch_strip_cfg<M, K, N, 2>(a, gather, kind, grid, s);
   MOE_STRIP_CONFIGS(MOE_STRIP_CASE)
