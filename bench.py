@@ -139,14 +139,27 @@ class Layer:
                 self.ws, self.out)
 
     def run(self, W=None):
-        self.run_routing()
-        self.run_forward(W)
+        """One layer: routing build + forward.  bf16 and fp8 make it one
+        library call, which routes a single token inside the forward's first
+        kernel; the other dtypes call the routing build first."""
+        m, W = self.moe, (W or self.W)
+        if self.dtype == "bf16":
+            m.moe_route_forward_bf16(self.ids, self.x, self.w, self.routing, W["w1"], W["w2"], self.ws,
+                                     self.out)
+        elif self.dtype == "fp8":
+            m.moe_route_forward_fp8(self.ids, self.x, self.w, self.routing, W["w1"], W["w1_scale"], W["w2"],
+                                    W["w2_scale"], self.ws, self.out)
+        else:
+            self.run_routing()
+            self.run_forward(W)
 
 
 def stage_pass(layer, steps):
     """Untimed pass with HIP events around every stage (library stage hook)
-    and around the routing build.  Each event record costs a few
-    microseconds of stream time, so these steps are not the timed ones."""
+    and around the routing build, which runs here as its own launch (the
+    layer steps fold it into the forward's first kernel for one token).
+    Each event record costs a few microseconds of stream time, so these
+    steps are not the timed ones."""
     import torch
     moe = layer.moe
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(steps)]
@@ -200,8 +213,7 @@ def timed_steps(layer, steps, warmup, dom_stage):
     t0 = time.perf_counter()
     for i in range(steps):
         moe.moe_set_stage_events(hooks[i])
-        layer.run_routing()
-        layer.run_forward()
+        layer.run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     moe.moe_set_stage_events(None)

@@ -327,6 +327,31 @@ int moe_forward_fp8(const void *x, const float *topk_w, const void *routing,
                     int T, int k, int E, int H, int I,
                     void *workspace, size_t workspace_bytes, void *out, void *stream);
 
+/* Routing build and forward pass in one call (blog section "MoE", PDL
+ * chaining, and its observation that at decode the metadata build costs
+ * about as much as the expert GEMMs).  Results are those of
+ * moe_build_routing_bf16 / _fp8 on topk_ids followed by moe_forward_bf16 /
+ * _fp8: `routing` (device, 16-byte aligned, routing_bytes >=
+ * moe_routing_layout().total_bytes) receives the same bytes, `out` and the
+ * workspace the same values.  topk_ids (device) int32 [T][k]; the other
+ * arguments as in the forward calls.  A single token (T = 1) whose k pairs
+ * fit one row tile is routed inside the forward's first kernel (bf16: the
+ * gate-up GEMM, fp8: the x quantisation), whose workgroup 0 also writes the
+ * routing buffer: one dependent launch fewer.  Otherwise the routing build
+ * is launched first.  All arguments are checked before anything is
+ * enqueued. */
+int moe_route_forward_bf16(const int32_t *topk_ids, const void *x, const float *topk_w,
+                           void *routing, size_t routing_bytes,
+                           const moe_packed_weights_t *w1, const moe_packed_weights_t *w2,
+                           int T, int k, int E, int H, int I,
+                           void *workspace, size_t workspace_bytes, void *out, void *stream);
+int moe_route_forward_fp8(const int32_t *topk_ids, const void *x, const float *topk_w,
+                          void *routing, size_t routing_bytes,
+                          const moe_packed_weights_t *w1, const float *w1_scale,
+                          const moe_packed_weights_t *w2, const float *w2_scale,
+                          int T, int k, int E, int H, int I,
+                          void *workspace, size_t workspace_bytes, void *out, void *stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the fp8
  * w8a8 forward of moe_forward_fp8, same arguments and results, without the

@@ -111,7 +111,7 @@ EXPORTS = ("moe_status_string", "moe_pack_weights", "moe_describe_packed_weights
            "moe_forward_fp8", "moe_forward_mxfp8", "moe_forward_int8", "moe_forward_int4",
            "moe_build_routing_fp8_block", "moe_forward_fp8_block",
            "moe_build_routing_int8_w8a16", "moe_forward_int8_w8a16", "moe_set_stage_events", "moe_device_cu_count",
-           "moe_stream_read", "moe_forward_fp8_noalloc")
+           "moe_stream_read", "moe_forward_fp8_noalloc", "moe_route_forward_bf16", "moe_route_forward_fp8")
 
 
 def _load():
@@ -168,6 +168,10 @@ def _load():
     L.moe_forward_fp8_noalloc.argtypes = [P, P, P, D, P, D, P, i, i, i, i, i, P, P]
     L.moe_stream_read.restype = i
     L.moe_stream_read.argtypes = [P, sz, P, sz, P]
+    L.moe_route_forward_bf16.restype = i
+    L.moe_route_forward_bf16.argtypes = [P, P, P, P, sz, D, D, i, i, i, i, i, P, sz, P, P]
+    L.moe_route_forward_fp8.restype = i
+    L.moe_route_forward_fp8.argtypes = [P, P, P, P, sz, D, P, D, P, i, i, i, i, i, P, sz, P, P]
     return L
 
 
@@ -448,6 +452,48 @@ def moe_forward_fp8(x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, o
     _check("moe_forward_fp8", _lib.moe_forward_fp8(
         _ptr(x), _ptr(topk_w), _ptr(routing), _desc("w1", w1), _ptr(w1_scale), _desc("w2", w2), _ptr(w2_scale),
         T, k, E, H, I, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_route_forward_bf16(topk_ids, x, topk_w, routing, w1, w2, workspace, out, stream=None):
+    """moe_build_routing_bf16 + moe_forward_bf16 in one call (one token:
+    the routing build runs inside the gate-up launch)."""
+    T, H = x.shape
+    k = topk_w.shape[1]
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    _check_tensor("topk_ids", topk_ids, torch.int32, (T, k))
+    _check_tensor("x", x, torch.bfloat16, (T, H))
+    _check_tensor("topk_w", topk_w, torch.float32, (T, k))
+    _check_tensor("w1", w1, torch.bfloat16, (E, 2 * I, H))
+    _check_tensor("w2", w2, torch.bfloat16, (E, H, I))
+    _check_tensor("out", out, torch.bfloat16, (T, H))
+    _check("moe_route_forward_bf16", _lib.moe_route_forward_bf16(
+        _ptr(topk_ids), _ptr(x), _ptr(topk_w), _ptr(routing), routing.numel(), _desc("w1", w1), _desc("w2", w2),
+        T, k, E, H, I, _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_route_forward_fp8(topk_ids, x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, out,
+                          stream=None):
+    """moe_build_routing_fp8 + moe_forward_fp8 in one call (one token: the
+    routing build runs inside the x-quantisation launch)."""
+    T, H = x.shape
+    k = topk_w.shape[1]
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    _check_tensor("topk_ids", topk_ids, torch.int32, (T, k))
+    _check_tensor("x", x, torch.bfloat16, (T, H))
+    _check_tensor("topk_w", topk_w, torch.float32, (T, k))
+    _check_tensor("w1", w1, torch.uint8, (E, 2 * I, H))
+    _check_tensor("w1_scale", w1_scale, torch.float32, (E, 2 * I))
+    _check_tensor("w2", w2, torch.uint8, (E, H, I))
+    _check_tensor("w2_scale", w2_scale, torch.float32, (E, H))
+    _check_tensor("out", out, torch.bfloat16, (T, H))
+    _check("moe_route_forward_fp8", _lib.moe_route_forward_fp8(
+        _ptr(topk_ids), _ptr(x), _ptr(topk_w), _ptr(routing), routing.numel(), _desc("w1", w1), _ptr(w1_scale),
+        _desc("w2", w2), _ptr(w2_scale), T, k, E, H, I, _ptr(workspace), workspace.numel(), _ptr(out),
+        _stream(stream)))
     return out
 
 

@@ -8,6 +8,7 @@
 // contiguous dimension, one workgroup per row, no LDS beyond a 4-wave
 // max-reduction.
 #include "moe_common.h"
+#include "decode_route.h"
 
 namespace moe {
 
@@ -49,13 +50,21 @@ __device__ __forceinline__ u32x2 quant8_bf16(const u32x4& v, float inv) {
 // the token's scale is also written at the sorted row of each of its zk pairs.
 // NV > 0: the row is read once into registers (H <= NV * 8 * 256), found
 // its amax and quantised from there; NV == 0: read twice (any H).
-template <int NV>
+// ROUTE (one token): the launch also does the token's routing build, and
+// the sorted rows of its zk pairs come from there.
+template <int NV, bool ROUTE = false>
 __global__ void __launch_bounds__(kRowThreads)
 quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restrict__ xq,
                        float* __restrict__ scale, float* __restrict__ zero_rows, int zk,
-                       const int32_t* __restrict__ pair_pos, float* __restrict__ scale_rows) {
+                       const int32_t* __restrict__ pair_pos, float* __restrict__ scale_rows,
+                       moe_host::DecodeRouteOut route) {
   __shared__ float s_red[4];
   const int t = blockIdx.x;
+  DecodeRoute rt{};
+  if constexpr (ROUTE) {
+    rt = decode_route(route.ids, zk, route.E, threadIdx.x & 63);
+    decode_route_write(rt, route, zk, threadIdx.x, kRowThreads, threadIdx.x & 63, threadIdx.x >> 6);
+  }
   if (zero_rows && threadIdx.x < zk) zero_rows[(size_t)t * zk + threadIdx.x] = 0.0f;
   const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
   u32x2* out = reinterpret_cast<u32x2*>(xq + (size_t)t * H);
@@ -84,7 +93,8 @@ quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restric
     for (int i = threadIdx.x; i < nvec; i += kRowThreads) out[i] = quant8_bf16(row[i], inv);
   }
   if (threadIdx.x == 0) scale[t] = sc;
-  if (scale_rows && threadIdx.x < zk) scale_rows[pair_pos[(size_t)t * zk + threadIdx.x]] = sc;
+  if (scale_rows && threadIdx.x < zk)   // wave 0: lane j holds pair j
+    scale_rows[ROUTE ? rt.pos : pair_pos[(size_t)t * zk + threadIdx.x]] = sc;
 }
 
 // h[r][n] = SiLU(rs * sum_s g[s][r][n]) * (rs * sum_s g[s][r][I + n]) for the
@@ -266,16 +276,24 @@ namespace moe_host {
 
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* scale,
                                   float* zero_rows, int zk, const int32_t* pair_pos,
-                                  float* scale_rows, hipStream_t s) {
+                                  float* scale_rows, hipStream_t s, const DecodeRouteOut* route) {
+  if (route && (T != 1 || zk > moe::kMaxTopK || !route->ids)) return hipErrorInvalidValue;
   const int per = (H / 8 + moe::kRowThreads - 1) / moe::kRowThreads;   // 16-byte vectors per thread
-#define MOE_QUANT_NV(NVv)                                                                               \
-  hipLaunchKernelGGL(moe::quant_rows_bf16_kernel<NVv>, dim3(T), dim3(moe::kRowThreads), 0, s, x, H, xq, \
-                     scale, zero_rows, zk, pair_pos, scale_rows)
-  if (per <= 1) MOE_QUANT_NV(1);
-  else if (per <= 2) MOE_QUANT_NV(2);
-  else if (per <= 4) MOE_QUANT_NV(4);
-  else if (per <= 8) MOE_QUANT_NV(8);
-  else MOE_QUANT_NV(0);
+  const DecodeRouteOut ro = route ? *route : DecodeRouteOut{};
+#define MOE_QUANT_NV(NVv)                                                                                 \
+  {                                                                                                       \
+    if (route)                                                                                            \
+      hipLaunchKernelGGL((moe::quant_rows_bf16_kernel<NVv, true>), dim3(T), dim3(moe::kRowThreads), 0, s, \
+                         x, H, xq, scale, zero_rows, zk, pair_pos, scale_rows, ro);                       \
+    else                                                                                                  \
+      hipLaunchKernelGGL((moe::quant_rows_bf16_kernel<NVv, false>), dim3(T), dim3(moe::kRowThreads), 0,  \
+                         s, x, H, xq, scale, zero_rows, zk, pair_pos, scale_rows, ro);                    \
+  }
+  if (per <= 1) MOE_QUANT_NV(1)
+  else if (per <= 2) MOE_QUANT_NV(2)
+  else if (per <= 4) MOE_QUANT_NV(4)
+  else if (per <= 8) MOE_QUANT_NV(8)
+  else MOE_QUANT_NV(0)
 #undef MOE_QUANT_NV
   return hipGetLastError();
 }

@@ -301,6 +301,7 @@ namespace moe_host {
 
 hipError_t launch_stream_fp8b(const StreamArgs& a, bool gateup, bool block, int mb, int waves, int grid,
                               hipStream_t s, int nb) {
+  if (a.route.ids) return hipErrorInvalidValue;
 #define MOE_FP8B_CASE(M, Wv) \
   if (mb == M && waves == Wv) return moe::launch_fp8b_t<M, Wv>(a, gateup, block, nb, grid, s);
   MOE_FP8B_CASE(1, 1) MOE_FP8B_CASE(1, 2) MOE_FP8B_CASE(1, 4) MOE_FP8B_CASE(1, 8)

@@ -1213,12 +1213,13 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
   return MOE_OK;
 }
 
-int forward(int dtype, const void* x, const float* topk_w, const void* routing, const void* w1,
-            const float* w1_scale, const void* w2, const float* w2_scale, int T, int k, int E,
-            int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
-  int rc = check_shape(T, k, E, H, I);
-  if (rc != MOE_OK) return rc;
-  if (T == 0) return MOE_OK;
+// Pointer, alignment and workspace-size rules of the bf16 / fp8 forward
+// pass (checked before anything is launched).
+int check_forward_args(int dtype, const void* x, const float* topk_w, const void* routing, const void* w1,
+                       const float* w1_scale, const void* w2, const float* w2_scale, int T, int k, int E,
+                       int H, int I, const void* workspace, size_t workspace_bytes, const void* out) {
+  const int rc = check_shape(T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
   const bool fp8 = dtype == MOE_DTYPE_FP8_W8A8;
   if (!x || !topk_w || !routing || !w1 || !w2 || !workspace || !out) return MOE_ERR_INVALID_ARG;
   if (fp8 && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
@@ -1226,13 +1227,29 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
       !aligned(topk_w, 4) || !aligned(routing, 16) || !aligned(workspace, 256))
     return MOE_ERR_INVALID_ARG;
   if (fp8 && (!aligned(w1_scale, 4) || !aligned(w2_scale, 4))) return MOE_ERR_INVALID_ARG;
+  moe_workspace_layout_t W;
+  workspace_layout(dtype, T, k, H, I, make_plan(dtype, T, k, E, H, I), &W);
+  return workspace_bytes < W.total_bytes ? MOE_ERR_BUFFER_TOO_SMALL : MOE_OK;
+}
+
+// fold: the routing build of a decode token done by the forward's first
+// kernel (fp8: the x quantisation, bf16: the gate-up), which writes the
+// routing buffer for the kernels after it.
+int forward(int dtype, const void* x, const float* topk_w, const void* routing, const void* w1,
+            const float* w1_scale, const void* w2, const float* w2_scale, int T, int k, int E,
+            int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream,
+            const moe_host::DecodeRouteOut* fold = nullptr) {
+  int rc = check_forward_args(dtype, x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I,
+                              workspace, workspace_bytes, out);
+  if (rc != MOE_OK || T == 0) return rc;
+  const bool fp8 = dtype == MOE_DTYPE_FP8_W8A8;
 
   const Plan p = make_plan(dtype, T, k, E, H, I);
   moe_routing_layout_t L;
   routing_layout(T, k, E, p, &L);
   moe_workspace_layout_t W;
   workspace_layout(dtype, T, k, H, I, p, &W);
-  if (workspace_bytes < W.total_bytes) return MOE_ERR_BUFFER_TOO_SMALL;
+  if (fold && (T != 1 || p.tiling != kStreaming)) return MOE_ERR_INVALID_ARG;
   int cus = 0;
   if ((rc = cu_count(&cus)) != MOE_OK) return rc;
 
@@ -1255,7 +1272,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
         static_cast<const uint16_t*>(x), T, H, xq, x_scale,
         p.tiling == kLdsTiles ? h_scale : nullptr,
         k, R.pair_pos, W.x_scale_rows != kNone ? reinterpret_cast<float*>(ws + W.x_scale_rows) : nullptr,
-        s);
+        s, fold);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (p.tiling == kStrips) {
@@ -1407,6 +1424,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     a.topk = k;
     a.max_tasks = p.max_tasks;
     a.P = P;
+    if (fold && !fp8) a.route = *fold;
     if (p.half1)
       e = moe_host::launch_stream_half_gateup(a, p.sw1, stream_grid((long)p.max_tasks * (I / 8), p.sw1, cus), s);
     else if (p.fp8_units)
@@ -1460,6 +1478,43 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
     }
   }
   return MOE_OK;
+}
+
+// Routing build and forward pass in one call.  One decode token whose k
+// pairs fit one row tile is routed inside the forward's first kernel;
+// otherwise the routing build runs as its own launch first.
+int route_forward(int dtype, const int32_t* ids, const void* x, const float* topk_w, void* routing,
+                  size_t routing_bytes, const void* w1, const float* w1_scale, const void* w2,
+                  const float* w2_scale, int T, int k, int E, int H, int I, void* workspace,
+                  size_t workspace_bytes, void* out, void* stream) {
+  int rc = check_forward_args(dtype, x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I,
+                              workspace, workspace_bytes, out);
+  if (rc != MOE_OK || T == 0) return rc;
+  if (!ids || !aligned(ids, 4)) return MOE_ERR_INVALID_ARG;
+  const Plan p = make_plan(dtype, T, k, E, H, I);
+  moe_routing_layout_t L;
+  routing_layout(T, k, E, p, &L);
+  if (routing_bytes < L.total_bytes) return MOE_ERR_BUFFER_TOO_SMALL;
+  const bool first_takes_it = dtype == MOE_DTYPE_FP8_W8A8 || p.half1 || (p.mb == 1 && p.nb == 2);
+  if (T == 1 && p.tiling == kStreaming && k <= p.block_m && k <= moe::kMaxTopK && first_takes_it) {
+    char* b = static_cast<char*>(routing);
+    moe_host::DecodeRouteOut f;
+    f.ids = ids;
+    f.header = reinterpret_cast<int32_t*>(b + L.header);
+    f.expert_offsets = reinterpret_cast<int32_t*>(b + L.expert_offsets);
+    f.sorted_pairs = reinterpret_cast<int32_t*>(b + L.sorted_pairs);
+    f.pair_pos = reinterpret_cast<int32_t*>(b + L.pair_pos);
+    f.tasks = reinterpret_cast<moe_task_t*>(b + L.tasks);
+    f.E = E;
+    f.block_m = p.block_m;
+    f.max_tasks = p.max_tasks;
+    return forward(dtype, x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
+                   workspace_bytes, out, stream, &f);
+  }
+  rc = build_routing(dtype, ids, T, k, E, H, I, routing, routing_bytes, stream);
+  if (rc != MOE_OK) return rc;
+  return forward(dtype, x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
+                 workspace_bytes, out, stream);
 }
 
 // Shape and pointer rules of a packed weight tensor; its row length in bytes.
@@ -1737,6 +1792,27 @@ int moe_forward_fp8(const void* x, const float* topk_w, const void* routing, con
   if (rc != MOE_OK || T == 0) return rc;
   return forward(MOE_DTYPE_FP8_W8A8, x, topk_w, routing, packed_data(w1), w1_scale, packed_data(w2), w2_scale, T, k,
                  E, H, I, workspace, workspace_bytes, out, stream);
+}
+
+int moe_route_forward_bf16(const int32_t* topk_ids, const void* x, const float* topk_w, void* routing,
+                           size_t routing_bytes, const moe_packed_weights_t* w1, const moe_packed_weights_t* w2,
+                           int T, int k, int E, int H, int I, void* workspace, size_t workspace_bytes,
+                           void* out, void* stream) {
+  const int rc = check_packed(MOE_DTYPE_BF16, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return route_forward(MOE_DTYPE_BF16, topk_ids, x, topk_w, routing, routing_bytes, packed_data(w1), nullptr,
+                       packed_data(w2), nullptr, T, k, E, H, I, workspace, workspace_bytes, out, stream);
+}
+
+int moe_route_forward_fp8(const int32_t* topk_ids, const void* x, const float* topk_w, void* routing,
+                          size_t routing_bytes, const moe_packed_weights_t* w1, const float* w1_scale,
+                          const moe_packed_weights_t* w2, const float* w2_scale, int T, int k, int E, int H,
+                          int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const int rc = check_packed(MOE_DTYPE_FP8_W8A8, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return route_forward(MOE_DTYPE_FP8_W8A8, topk_ids, x, topk_w, routing, routing_bytes, packed_data(w1),
+                       w1_scale, packed_data(w2), w2_scale, T, k, E, H, I, workspace, workspace_bytes, out,
+                       stream);
 }
 
 int moe_forward_fp8_noalloc(const void* x, const float* topk_w, const void* routing,

@@ -193,6 +193,21 @@ hipError_t launch_router_reduce(const float* partials, int S, int T, int N, floa
 // Largest E the router kernel takes.
 int router_max_experts();
 
+// The routing build of one decode token (T = 1, k no larger than the row
+// tile) folded into the first kernel of the forward pass: every workgroup
+// sorts the token's k pairs in registers, and workgroup 0 also writes the
+// routing buffer's parts, byte for byte what the routing build writes.
+// ids == nullptr: the kernel reads a routing buffer built before it.
+struct DecodeRouteOut {
+  const int32_t* ids;          // the token's k expert ids
+  int32_t* header;             // 16 ints
+  int32_t* expert_offsets;     // E + 1
+  int32_t* sorted_pairs;       // k
+  int32_t* pair_pos;           // k
+  moe_task_t* tasks;           // max_tasks
+  int E, block_m, max_tasks;
+};
+
 hipError_t launch_route(const int32_t* ids, int P, int E, int block_m, int max_tasks,
                         void* routing, const moe_routing_layout_t& L, hipStream_t s);
 // Bytes of the routing work area (per-segment key counts) for P pairs.
@@ -202,9 +217,12 @@ size_t route_scratch_bytes(int P);
 // null the same launch also clears zero_rows[0 .. T*zk) (row amax slots);
 // when scale_rows is not null it also writes each token's scale at the
 // sorted rows pair_pos[t*zk + j] of its zk pairs.
+// With route (T = 1 only) the launch also does the token's routing build,
+// and the sorted rows of its pairs come from there instead of pair_pos.
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* scale,
                                   float* zero_rows, int zk, const int32_t* pair_pos,
-                                  float* scale_rows, hipStream_t s);
+                                  float* scale_rows, hipStream_t s,
+                                  const DecodeRouteOut* route = nullptr);
 
 // SiLU-and-mul of the gate-up partial sums g[S][P][2I] for the valid sorted
 // rows; writes bf16 h[P][I] (fp8 = false) or e4m3 codes h[P][I] + scales.
@@ -309,10 +327,12 @@ struct StreamArgs {
   int w_rows;                   // weight rows per expert (2I or H)
   int topk;
   int max_tasks;
+  DecodeRouteOut route;         // bf16 gate-up at T = 1: the routing build folded in
 };
 
 // bf16 gate-up on 16-row tiles with half-width items (8 h columns each; K
 // steps a multiple of 2 * waves).
+// With a.route.ids set (T = 1) the launch also does the routing build.
 hipError_t launch_stream_half_gateup(const StreamArgs& a, int waves, int grid, hipStream_t s);
 // Down GEMM and top-k weighted sum of a single token in one launch (T = 1,
 // at most 16 pairs; `half`: at most 8): one workgroup of `waves` waves per
@@ -328,7 +348,8 @@ bool stream_config_supported(int mb, int waves, int u);
 // 2 int8 w8a8 (per-channel scales).
 // nb: weight blocks per item, 2, or 4 (two-step stages): MX or int8 w8a8 on
 // 64-row tiles with one or two waves, bf16 (kind 0, !fp8) on 32-row tiles
-// with one, two or four waves.
+// with one, two or four waves.  a.route.ids set (the routing build folded
+// in): bf16 gate-up on 16-row tiles with nb = 2 only.
 hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int kind, int mb, int waves,
                               int u, int grid, hipStream_t s, int nb = 2);
 // int8 w8a8: per-token quantisation of bf16 x (row-amax slots cleared,

@@ -43,6 +43,7 @@
 #include <type_traits>
 
 #include "lds_dma.h"
+#include "decode_route.h"
 
 namespace moe {
 
@@ -66,18 +67,29 @@ __device__ __forceinline__ void stream_mfma(f32x4& acc, const u32x4& a, const u3
 // (gate-up: two gate and two up blocks, down: 64 columns), halving the
 // re-reads of the tile's token rows: MX and int8 w8a8 on 64-row tiles (one
 // or two waves), bf16 on 32-row tiles (one, two or four waves).
-template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX, bool I8, int NB = kStreamNB>
+// ROUTE: bf16 gate-up of one decode token with the routing build folded in
+// (tasks from decode_route; every row is the token's).
+template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX, bool I8, int NB = kStreamNB, bool ROUTE = false>
 __global__ void __launch_bounds__(W * 64)
 stream_gemm_kernel(moe_host::StreamArgs g) {
   constexpr int NH = GATEUP ? NB / 2 : NB;   // 16-column output blocks per item
   static_assert(!MX || (FP8 && U == 2), "MX stages are one 128-value K unit");
   static_assert(!I8 || (FP8 && !MX), "int8 uses the 1-byte per-channel path");
+  static_assert(!ROUTE || (GATEUP && !MX), "the folded routing build serves the gate-up");
   __shared__ f32x4 red[W][MB][NB][64];   // the waves' partial sums of one item
   const int lane = threadIdx.x & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
+  DecodeRoute rt{};
+  int num_tasks;
+  if constexpr (ROUTE) {
+    rt = decode_route(g.route.ids, g.topk, g.route.E, lane);
+    if (blockIdx.x == 0) decode_route_write(rt, g.route, g.topk, threadIdx.x, W * 64, lane, wave);
+    num_tasks = min(rt.ntasks, g.max_tasks);
+  } else {
+    num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
+  }
   const int n_groups = g.N_out / 16 / NH;   // column groups per task
   const int total = num_tasks * n_groups;
   const size_t row_bytes = (size_t)g.K * (FP8 ? 1 : 2);
@@ -98,7 +110,9 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
   for (int item = vid; item < total; item += G) {
     const int ti = item / n_groups;
     const int cg = item - ti * n_groups;
-    const moe_task_t task = load_task_scalar(g.tasks + ti);
+    moe_task_t task;
+    if constexpr (ROUTE) task = decode_task(rt, ti);
+    else task = load_task_scalar(g.tasks + ti);
     // weight 16-row blocks of this item
     int blk[NB];
     if constexpr (GATEUP) {
@@ -122,7 +136,9 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
     for (int b = 0; b < MB; b++) {
       const int rb = b * 16 < task.rows ? b : 0;
       int arow;
-      if constexpr (GATEUP) {
+      if constexpr (ROUTE) {
+        arow = 0;   // one token
+      } else if constexpr (GATEUP) {
         const i32x16_t sp = load16_scalar(g.sorted_pairs + task.row_begin + rb * 16);
         const int p = rb * 16 + lrow < task.rows ? spread16(sp, lane) : sp[0];
         arow = p / g.topk;
@@ -335,7 +351,8 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
 // items on 256 CUs).  Lanes of weight rows 0-7 read gate rows, 8-15 the up
 // rows (half of a packed 16-row chunk each); in the epilogue lane c (c < 8)
 // takes the up sum of lane c + 8 and writes h column 8 * item + c.
-template <int W>
+// ROUTE: one decode token with the routing build folded in.
+template <int W, bool ROUTE = false>
 __global__ void __launch_bounds__(W * 64)
 stream_half_gateup_kernel(moe_host::StreamArgs g) {
   constexpr int U = 2;
@@ -344,7 +361,15 @@ stream_half_gateup_kernel(moe_host::StreamArgs g) {
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
+  DecodeRoute rt{};
+  int num_tasks;
+  if constexpr (ROUTE) {
+    rt = decode_route(g.route.ids, g.topk, g.route.E, lane);
+    if (blockIdx.x == 0) decode_route_write(rt, g.route, g.topk, threadIdx.x, W * 64, lane, wave);
+    num_tasks = min(rt.ntasks, g.max_tasks);
+  } else {
+    num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
+  }
   const int n_groups = g.N_out / 8;
   const int total = num_tasks * n_groups;
   const size_t row_bytes = (size_t)g.K * 2;
@@ -363,15 +388,21 @@ stream_half_gateup_kernel(moe_host::StreamArgs g) {
   for (int item = vid; item < total; item += G) {
     const int ti = item / n_groups;
     const int c8 = item - ti * n_groups;
-    const moe_task_t task = load_task_scalar(g.tasks + ti);
+    moe_task_t task;
+    if constexpr (ROUTE) task = decode_task(rt, ti);
+    else task = load_task_scalar(g.tasks + ti);
     const int step0 = wave * spw;
     // this lane's weight row: gate row 8 c8 + lrow, or up row I + 8 c8 + (lrow - 8)
     const int wrow = lrow < 8 ? 8 * c8 + lrow : g.N_out + 8 * c8 + (lrow - 8);
     const char* bp = B + (((size_t)task.expert * w_blocks + wrow / 16) * nsteps + step0) * 1024 +
                      16 * ((wrow & 15) + 16 * lgrp);
-    const i32x16_t sp = load16_scalar(g.sorted_pairs + task.row_begin);
-    const int p = lrow < task.rows ? spread16(sp, lane) : sp[0];
-    const char* ap = A + (size_t)(p / g.topk) * row_bytes + (size_t)step0 * 64 + 16 * lgrp;
+    int arow = 0;   // ROUTE: one token
+    if constexpr (!ROUTE) {
+      const i32x16_t sp = load16_scalar(g.sorted_pairs + task.row_begin);
+      const int p = lrow < task.rows ? spread16(sp, lane) : sp[0];
+      arow = p / g.topk;
+    }
+    const char* ap = A + (size_t)arow * row_bytes + (size_t)step0 * 64 + 16 * lgrp;
 
     f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     u32x4 fa0[U], fb0[U], fa1[U], fb1[U];
@@ -614,6 +645,16 @@ hipError_t launch_stream_nb4(const moe_host::StreamArgs& a, bool gateup, int kin
 template <int MB, int W, int U>
 static hipError_t launch_stream_w(const moe_host::StreamArgs& a, bool gateup, bool fp8, int kind,
                                   int grid, hipStream_t s) {
+  if (a.route.ids) {   // the routing build folded in: bf16 gate-up on 16-row tiles
+    if constexpr (MB == 1) {
+      if (gateup && !fp8 && kind == 0) {
+        hipLaunchKernelGGL((stream_gemm_kernel<MB, W, U, true, false, false, false, kStreamNB, true>), dim3(grid),
+                           dim3(W * 64), 0, s, a);
+        return hipGetLastError();
+      }
+    }
+    return hipErrorInvalidValue;
+  }
   if (kind == 1) {
     if constexpr (U == 2)
       return gateup ? launch_stream_t<MB, W, U, true, true, true>(a, grid, s)
@@ -644,12 +685,21 @@ namespace moe_host {
 
 hipError_t launch_stream_half_gateup(const StreamArgs& a, int waves, int grid, hipStream_t s) {
   switch (waves) {
-    case 1: hipLaunchKernelGGL(moe::stream_half_gateup_kernel<1>, dim3(grid), dim3(64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(moe::stream_half_gateup_kernel<2>, dim3(grid), dim3(128), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(moe::stream_half_gateup_kernel<4>, dim3(grid), dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(moe::stream_half_gateup_kernel<8>, dim3(grid), dim3(512), 0, s, a); break;
+#define MOE_HALF(Wv)                                                                                    \
+  {                                                                                                     \
+    if (a.route.ids)                                                                                    \
+      hipLaunchKernelGGL((moe::stream_half_gateup_kernel<Wv, true>), dim3(grid), dim3(Wv * 64), 0, s, a); \
+    else                                                                                                \
+      hipLaunchKernelGGL((moe::stream_half_gateup_kernel<Wv, false>), dim3(grid), dim3(Wv * 64), 0, s, a); \
+    break;                                                                                              \
+  }
+    case 1: MOE_HALF(1)
+    case 2: MOE_HALF(2)
+    case 4: MOE_HALF(4)
+    case 8: MOE_HALF(8)
     default: return hipErrorInvalidValue;
   }
+#undef MOE_HALF
   return hipGetLastError();
 }
 
@@ -686,6 +736,7 @@ bool stream_config_supported(int mb, int waves, int u) {
 hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int kind, int mb, int waves,
                               int u, int grid, hipStream_t s, int nb) {
   if (nb == 4) {
+    if (a.route.ids) return hipErrorInvalidValue;
     if (u != 2) return hipErrorInvalidValue;
     if (kind == 0 && !fp8) return mb == 2 ? moe::launch_stream_nb4(a, gateup, 3, waves, grid, s)
                                           : hipErrorInvalidValue;

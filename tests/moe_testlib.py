@@ -8,7 +8,7 @@ import numpy as np
 import torch
 
 import oracle
-from moe_inputs import make_tokens, make_weights
+from moe_inputs import WORKLOADS, make_tokens, make_weights
 
 BF16_REL, BF16_ABS = 1e-2, 1e-3      # max|err| <= 1e-2*max|ref| + 1e-3
 FP8_REL = 4e-2                        # max|err| <= 4e-2*max|ref|
@@ -35,6 +35,24 @@ def device_weights(wl, device="cuda"):
 
 def path_dtype(wl):
     return wl.dtype if wl.dtype in ("fp8", "fp8b", "mxfp8", "int8", "int4", "int8w") else "bf16"
+
+
+# One full-size workload's weights at a time: packed on the GPU, row-major
+# on the host for the oracle.
+_weights_cache = {}
+
+
+def workload_weights(name):
+    if name not in _weights_cache:
+        _weights_cache.clear()
+        torch.cuda.empty_cache()
+        wl = WORKLOADS[name]
+        W = device_weights(wl)
+        Wc = {k: v.cpu() for k, v in W.items()}
+        Wp = __import__("mixture_experts_layer_lds_amd").pack_weights(W, path_dtype(wl))
+        del W
+        _weights_cache[name] = (Wp, Wc)
+    return _weights_cache[name]
 
 
 def run_gpu(lib, x, ids, w, W, dtype, packed=None):

@@ -16,7 +16,8 @@ import torch
 
 import oracle
 from moe_inputs import WORKLOADS, custom_workload, make_tokens, make_weights, random_ids, random_weights_w
-from moe_testlib import SUMMARY, check_tol, device_weights, log, oracle_rows, path_dtype, run_gpu, sample_rows
+from moe_testlib import (SUMMARY, check_tol, device_weights, log, oracle_rows, path_dtype, run_gpu,
+                         sample_rows, workload_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -351,20 +352,6 @@ def test_tiny_workload(lib):
     assert err < 3e-2
 
 
-_weights_cache = {}
-
-
-def workload_weights(name):
-    if name not in _weights_cache:
-        _weights_cache.clear()
-        torch.cuda.empty_cache()
-        wl = WORKLOADS[name]
-        W = device_weights(wl)
-        Wc = {k: v.cpu() for k, v in W.items()}
-        Wp = __import__("mixture_experts_layer_lds_amd").pack_weights(W, path_dtype(wl))
-        del W
-        _weights_cache[name] = (Wp, Wc)
-    return _weights_cache[name]
 
 
 FULL = [(name, T) for name in ("mixtral", "qwen3", "qwen2", "dsv3", "dsv3b", "dsv3mx", "dsv3i8", "mixtral4", "mixtral8") for T in WORKLOADS[name].Ts]
