@@ -297,6 +297,47 @@ def overheads_us(reps=50):
             "tiny_kernel_in_graph_us": round(statistics.median(tiny), 2)}
 
 
+def graph_read_us(moe, nbytes, calls=10, reps=20):
+    """The layer's graph method applied to a plain read of `nbytes`: `calls`
+    streaming reads (`moe_stream_read`, eight workgroups per compute unit)
+    captured back to back in one graph, each of another buffer in turn, so
+    that no read finds its bytes in the last-level cache; the replay time
+    divided by `calls`, median over `reps` replays.  The time a single kernel
+    needs to stream this many bytes, launch ramp included: the floor of a
+    decode layer that reads its weights once."""
+    import torch
+    nbytes = max(16, nbytes // 16 * 16)
+    nbuf = max(2, math.ceil(600e6 / nbytes) + 1)
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    sink = torch.empty(moe.moe_device_cu_count() * 8, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for b in bufs:
+            moe.moe_stream_read(b, sink)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            moe.moe_stream_read(bufs[i % nbuf], sink)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1000.0 / calls)
+    del g, bufs
+    torch.cuda.empty_cache()
+    return statistics.median(times)
+
+
 def stream_read_ceiling(moe, gib=4, reps=10):
     """Attainable HBM read rate: the library's plain streaming-read kernel over
     a buffer far larger than the last-level cache (median of `reps` reads,
@@ -516,6 +557,11 @@ def main():
                           "weight_copies": copies})
             del sets, lay
             torch.cuda.empty_cache()
+            if nb < 1e9:
+                # one plain streaming read of the layer's essential bytes, timed the same way
+                floor = graph_read_us(moe, int(nb))
+                sweep[-1]["read_floor_us"] = round(floor, 2)
+                sweep[-1]["of_read_floor"] = round(floor / med, 4)
             log(f"[bench] sweep T={Ts}: {sweep[-1]['us_per_layer']} us, {sweep[-1]['GBs']} GB/s")
     over = overheads_us()
     ceiling = stream_read_ceiling(moe)

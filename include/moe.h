@@ -334,12 +334,12 @@ int moe_forward_fp8(const void *x, const float *topk_w, const void *routing,
  * _fp8: `routing` (device, 16-byte aligned, routing_bytes >=
  * moe_routing_layout().total_bytes) receives the same bytes, `out` and the
  * workspace the same values.  topk_ids (device) int32 [T][k]; the other
- * arguments as in the forward calls.  A single token (T = 1) whose k pairs
- * fit one row tile is routed inside the forward's first kernel (bf16: the
- * gate-up GEMM, fp8: the x quantisation), whose workgroup 0 also writes the
- * routing buffer: one dependent launch fewer.  Otherwise the routing build
- * is launched first.  All arguments are checked before anything is
- * enqueued. */
+ * arguments as in the forward calls.  A decode batch of at most 64 pairs
+ * (T * k <= 64) on the register-streaming plan is routed inside the
+ * forward's first kernel (bf16: the gate-up GEMM, on 16-row tiles; fp8: the
+ * x quantisation), whose workgroup 0 also writes the routing buffer: one
+ * dependent launch fewer.  Otherwise the routing build is launched first.
+ * All arguments are checked before anything is enqueued. */
 int moe_route_forward_bf16(const int32_t *topk_ids, const void *x, const float *topk_w,
                            void *routing, size_t routing_bytes,
                            const moe_packed_weights_t *w1, const moe_packed_weights_t *w2,

@@ -50,8 +50,8 @@ __device__ __forceinline__ u32x2 quant8_bf16(const u32x4& v, float inv) {
 // the token's scale is also written at the sorted row of each of its zk pairs.
 // NV > 0: the row is read once into registers (H <= NV * 8 * 256), found
 // its amax and quantised from there; NV == 0: read twice (any H).
-// ROUTE (one token): the launch also does the token's routing build, and
-// the sorted rows of its zk pairs come from there.
+// ROUTE (at most 64 pairs): the launch also does the routing build, and the
+// sorted rows of each token's zk pairs come from there.
 template <int NV, bool ROUTE = false>
 __global__ void __launch_bounds__(kRowThreads)
 quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restrict__ xq,
@@ -61,9 +61,13 @@ quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restric
   __shared__ float s_red[4];
   const int t = blockIdx.x;
   DecodeRoute rt{};
+  int row_j = 0;   // ROUTE: the sorted row of pair t * zk + lane (lanes < zk)
   if constexpr (ROUTE) {
-    rt = decode_route(route.ids, zk, route.E, threadIdx.x & 63);
-    decode_route_write(rt, route, zk, threadIdx.x, kRowThreads, threadIdx.x & 63, threadIdx.x >> 6);
+    const int P = gridDim.x * zk;
+    const int lane = threadIdx.x & 63;
+    rt = decode_route(route.ids, P, route.E, route.block_m, lane);
+    if (t == 0) decode_route_write(rt, route, P, threadIdx.x, kRowThreads, lane, threadIdx.x >> 6);
+    row_j = __shfl(rt.pos, min(t * zk + lane, P - 1), kWave);
   }
   if (zero_rows && threadIdx.x < zk) zero_rows[(size_t)t * zk + threadIdx.x] = 0.0f;
   const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
@@ -94,7 +98,7 @@ quant_rows_bf16_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restric
   }
   if (threadIdx.x == 0) scale[t] = sc;
   if (scale_rows && threadIdx.x < zk)   // wave 0: lane j holds pair j
-    scale_rows[ROUTE ? rt.pos : pair_pos[(size_t)t * zk + threadIdx.x]] = sc;
+    scale_rows[ROUTE ? row_j : pair_pos[(size_t)t * zk + threadIdx.x]] = sc;
 }
 
 // h[r][n] = SiLU(rs * sum_s g[s][r][n]) * (rs * sum_s g[s][r][I + n]) for the
@@ -277,7 +281,7 @@ namespace moe_host {
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* scale,
                                   float* zero_rows, int zk, const int32_t* pair_pos,
                                   float* scale_rows, hipStream_t s, const DecodeRouteOut* route) {
-  if (route && (T != 1 || zk > moe::kMaxTopK || !route->ids)) return hipErrorInvalidValue;
+  if (route && ((long)T * zk > moe::kDecodeRoutePairs || !route->ids)) return hipErrorInvalidValue;
   const int per = (H / 8 + moe::kRowThreads - 1) / moe::kRowThreads;   // 16-byte vectors per thread
   const DecodeRouteOut ro = route ? *route : DecodeRouteOut{};
 #define MOE_QUANT_NV(NVv)                                                                                 \

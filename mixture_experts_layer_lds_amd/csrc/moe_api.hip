@@ -11,6 +11,7 @@
 #include <mutex>
 
 #include "moe_common.h"
+#include "decode_route.h"
 
 // Workspace of moe_forward_fp8_noalloc: one array per GPU, held until the
 // process ends.  In host code its name is only a stand-in for the device
@@ -1249,7 +1250,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
   routing_layout(T, k, E, p, &L);
   moe_workspace_layout_t W;
   workspace_layout(dtype, T, k, H, I, p, &W);
-  if (fold && (T != 1 || p.tiling != kStreaming)) return MOE_ERR_INVALID_ARG;
+  if (fold && ((long)T * k > moe::kDecodeRoutePairs || p.tiling != kStreaming)) return MOE_ERR_INVALID_ARG;
   int cus = 0;
   if ((rc = cu_count(&cus)) != MOE_OK) return rc;
 
@@ -1480,9 +1481,9 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
   return MOE_OK;
 }
 
-// Routing build and forward pass in one call.  One decode token whose k
-// pairs fit one row tile is routed inside the forward's first kernel;
-// otherwise the routing build runs as its own launch first.
+// Routing build and forward pass in one call.  A decode batch of at most 64
+// pairs on 16-row streaming tiles is routed inside the forward's first
+// kernel; otherwise the routing build runs as its own launch first.
 int route_forward(int dtype, const int32_t* ids, const void* x, const float* topk_w, void* routing,
                   size_t routing_bytes, const void* w1, const float* w1_scale, const void* w2,
                   const float* w2_scale, int T, int k, int E, int H, int I, void* workspace,
@@ -1495,8 +1496,10 @@ int route_forward(int dtype, const int32_t* ids, const void* x, const float* top
   moe_routing_layout_t L;
   routing_layout(T, k, E, p, &L);
   if (routing_bytes < L.total_bytes) return MOE_ERR_BUFFER_TOO_SMALL;
-  const bool first_takes_it = dtype == MOE_DTYPE_FP8_W8A8 || p.half1 || (p.mb == 1 && p.nb == 2);
-  if (T == 1 && p.tiling == kStreaming && k <= p.block_m && k <= moe::kMaxTopK && first_takes_it) {
+  // fp8: the x quantisation comes first and takes any plan; bf16: the
+  // gate-up kernels on 16-row tiles
+  const bool first_takes_it = dtype == MOE_DTYPE_FP8_W8A8 || (p.mb == 1 && (p.half1 || p.nb == 2));
+  if ((long)T * k <= moe::kDecodeRoutePairs && p.tiling == kStreaming && first_takes_it) {
     char* b = static_cast<char*>(routing);
     moe_host::DecodeRouteOut f;
     f.ids = ids;

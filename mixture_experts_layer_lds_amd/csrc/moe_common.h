@@ -193,17 +193,17 @@ hipError_t launch_router_reduce(const float* partials, int S, int T, int N, floa
 // Largest E the router kernel takes.
 int router_max_experts();
 
-// The routing build of one decode token (T = 1, k no larger than the row
-// tile) folded into the first kernel of the forward pass: every workgroup
-// sorts the token's k pairs in registers, and workgroup 0 also writes the
-// routing buffer's parts, byte for byte what the routing build writes.
-// ids == nullptr: the kernel reads a routing buffer built before it.
+// The routing build of a decode batch (at most 64 pairs) folded into the
+// first kernel of the forward pass: every workgroup sorts the pairs in
+// registers, and workgroup 0 also writes the routing buffer's parts, byte
+// for byte what the routing build writes.  ids == nullptr: the kernel reads
+// a routing buffer built before it.
 struct DecodeRouteOut {
-  const int32_t* ids;          // the token's k expert ids
+  const int32_t* ids;          // the T * k expert ids
   int32_t* header;             // 16 ints
   int32_t* expert_offsets;     // E + 1
-  int32_t* sorted_pairs;       // k
-  int32_t* pair_pos;           // k
+  int32_t* sorted_pairs;       // T * k
+  int32_t* pair_pos;           // T * k
   moe_task_t* tasks;           // max_tasks
   int E, block_m, max_tasks;
 };
@@ -217,8 +217,8 @@ size_t route_scratch_bytes(int P);
 // null the same launch also clears zero_rows[0 .. T*zk) (row amax slots);
 // when scale_rows is not null it also writes each token's scale at the
 // sorted rows pair_pos[t*zk + j] of its zk pairs.
-// With route (T = 1 only) the launch also does the token's routing build,
-// and the sorted rows of its pairs come from there instead of pair_pos.
+// With route (T * zk <= 64) the launch also does the routing build, and the
+// sorted rows of the pairs come from there instead of pair_pos.
 hipError_t launch_quant_rows_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* scale,
                                   float* zero_rows, int zk, const int32_t* pair_pos,
                                   float* scale_rows, hipStream_t s,
@@ -327,12 +327,12 @@ struct StreamArgs {
   int w_rows;                   // weight rows per expert (2I or H)
   int topk;
   int max_tasks;
-  DecodeRouteOut route;         // bf16 gate-up at T = 1: the routing build folded in
+  DecodeRouteOut route;         // bf16 gate-up, at most 64 pairs: the routing build folded in
 };
 
 // bf16 gate-up on 16-row tiles with half-width items (8 h columns each; K
 // steps a multiple of 2 * waves).
-// With a.route.ids set (T = 1) the launch also does the routing build.
+// With a.route.ids set (at most 64 pairs) the launch also does the routing build.
 hipError_t launch_stream_half_gateup(const StreamArgs& a, int waves, int grid, hipStream_t s);
 // Down GEMM and top-k weighted sum of a single token in one launch (T = 1,
 // at most 16 pairs; `half`: at most 8): one workgroup of `waves` waves per

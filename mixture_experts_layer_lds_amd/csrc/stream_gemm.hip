@@ -67,8 +67,8 @@ __device__ __forceinline__ void stream_mfma(f32x4& acc, const u32x4& a, const u3
 // (gate-up: two gate and two up blocks, down: 64 columns), halving the
 // re-reads of the tile's token rows: MX and int8 w8a8 on 64-row tiles (one
 // or two waves), bf16 on 32-row tiles (one, two or four waves).
-// ROUTE: bf16 gate-up of one decode token with the routing build folded in
-// (tasks from decode_route; every row is the token's).
+// ROUTE: bf16 gate-up of a decode batch (at most 64 pairs) with the routing
+// build folded in (tasks and row tokens from decode_route).
 template <int MB, int W, int U, bool GATEUP, bool FP8, bool MX, bool I8, int NB = kStreamNB, bool ROUTE = false>
 __global__ void __launch_bounds__(W * 64)
 stream_gemm_kernel(moe_host::StreamArgs g) {
@@ -84,8 +84,8 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
   DecodeRoute rt{};
   int num_tasks;
   if constexpr (ROUTE) {
-    rt = decode_route(g.route.ids, g.topk, g.route.E, lane);
-    if (blockIdx.x == 0) decode_route_write(rt, g.route, g.topk, threadIdx.x, W * 64, lane, wave);
+    rt = decode_route(g.route.ids, g.P, g.route.E, g.route.block_m, lane);
+    if (blockIdx.x == 0) decode_route_write(rt, g.route, g.P, threadIdx.x, W * 64, lane, wave);
     num_tasks = min(rt.ntasks, g.max_tasks);
   } else {
     num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
@@ -111,7 +111,7 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
     const int ti = item / n_groups;
     const int cg = item - ti * n_groups;
     moe_task_t task;
-    if constexpr (ROUTE) task = decode_task(rt, ti);
+    if constexpr (ROUTE) task = decode_task(rt, ti, g.route.block_m);
     else task = load_task_scalar(g.tasks + ti);
     // weight 16-row blocks of this item
     int blk[NB];
@@ -137,7 +137,7 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
       const int rb = b * 16 < task.rows ? b : 0;
       int arow;
       if constexpr (ROUTE) {
-        arow = 0;   // one token
+        arow = decode_sorted_pair(rt, task.row_begin + (rb * 16 + lrow < task.rows ? rb * 16 + lrow : 0)) / g.topk;
       } else if constexpr (GATEUP) {
         const i32x16_t sp = load16_scalar(g.sorted_pairs + task.row_begin + rb * 16);
         const int p = rb * 16 + lrow < task.rows ? spread16(sp, lane) : sp[0];
@@ -351,7 +351,7 @@ stream_gemm_kernel(moe_host::StreamArgs g) {
 // items on 256 CUs).  Lanes of weight rows 0-7 read gate rows, 8-15 the up
 // rows (half of a packed 16-row chunk each); in the epilogue lane c (c < 8)
 // takes the up sum of lane c + 8 and writes h column 8 * item + c.
-// ROUTE: one decode token with the routing build folded in.
+// ROUTE: a decode batch (at most 64 pairs) with the routing build folded in.
 template <int W, bool ROUTE = false>
 __global__ void __launch_bounds__(W * 64)
 stream_half_gateup_kernel(moe_host::StreamArgs g) {
@@ -364,8 +364,8 @@ stream_half_gateup_kernel(moe_host::StreamArgs g) {
   DecodeRoute rt{};
   int num_tasks;
   if constexpr (ROUTE) {
-    rt = decode_route(g.route.ids, g.topk, g.route.E, lane);
-    if (blockIdx.x == 0) decode_route_write(rt, g.route, g.topk, threadIdx.x, W * 64, lane, wave);
+    rt = decode_route(g.route.ids, g.P, g.route.E, g.route.block_m, lane);
+    if (blockIdx.x == 0) decode_route_write(rt, g.route, g.P, threadIdx.x, W * 64, lane, wave);
     num_tasks = min(rt.ntasks, g.max_tasks);
   } else {
     num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
@@ -389,15 +389,17 @@ stream_half_gateup_kernel(moe_host::StreamArgs g) {
     const int ti = item / n_groups;
     const int c8 = item - ti * n_groups;
     moe_task_t task;
-    if constexpr (ROUTE) task = decode_task(rt, ti);
+    if constexpr (ROUTE) task = decode_task(rt, ti, g.route.block_m);
     else task = load_task_scalar(g.tasks + ti);
     const int step0 = wave * spw;
     // this lane's weight row: gate row 8 c8 + lrow, or up row I + 8 c8 + (lrow - 8)
     const int wrow = lrow < 8 ? 8 * c8 + lrow : g.N_out + 8 * c8 + (lrow - 8);
     const char* bp = B + (((size_t)task.expert * w_blocks + wrow / 16) * nsteps + step0) * 1024 +
                      16 * ((wrow & 15) + 16 * lgrp);
-    int arow = 0;   // ROUTE: one token
-    if constexpr (!ROUTE) {
+    int arow;
+    if constexpr (ROUTE) {
+      arow = decode_sorted_pair(rt, task.row_begin + (lrow < task.rows ? lrow : 0)) / g.topk;
+    } else {
       const i32x16_t sp = load16_scalar(g.sorted_pairs + task.row_begin);
       const int p = lrow < task.rows ? spread16(sp, lane) : sp[0];
       arow = p / g.topk;

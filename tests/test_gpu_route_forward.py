@@ -1,7 +1,7 @@
 """The routing build and the forward pass in one call (moe_route_forward_bf16
-/ _fp8).  For one token whose pairs fit one row tile the routing build runs
-inside the forward's first kernel (bf16: the gate-up GEMM, fp8: the x
-quantisation), whose workgroup 0 writes the routing buffer.
+/ _fp8).  For a decode batch of at most 64 token-expert pairs the routing
+build runs inside the forward's first kernel (bf16: the gate-up GEMM, fp8:
+the x quantisation), whose workgroup 0 writes the routing buffer.
 
 Checked on every case:
 - the routing buffer holds the same bytes as after moe_build_routing_* (both
@@ -12,9 +12,11 @@ Checked on every case:
 - the output is within the forward tolerance of the oracle (bf16: max|err|
   <= 1e-2*max|ref| + 1e-3; fp8: 4e-2*max|ref|).
 Cases: k from 1 to 16, dropped ids, every pair dropped, an expert named
-twice, E = 1, the full-size bf16 and fp8 workloads at T = 1 in the launch
-configuration the benchmark times, more than one token (the routing build
-launched first), graph capture with new ids between replays.
+twice, E = 1, batches of up to 64 pairs with a hot expert cut into several
+row tiles, batches just past 64 pairs (the routing build launched first),
+the full-size bf16 and fp8 workloads at every swept T with at most 64 pairs
+in the launch configuration the benchmark times, graph capture with new ids
+between replays.
 """
 import numpy as np
 import pytest
@@ -121,40 +123,55 @@ def test_one_token(lib, E, H, I, k, case, dtype):
     check_case(lib, x, ids, w, Wp, Wc, E, H, I, dtype, case)
 
 
-@pytest.mark.parametrize("T", [2, 5, 64])
+SEVERAL = [
+    # T, k, E, case: pairs up to 64 take the folded build, more the launched one
+    (2, 4, 16, "plain"), (3, 5, 16, "dropped"), (2, 8, 64, "plain"), (4, 16, 32, "hot"),
+    (8, 8, 16, "hot"), (16, 4, 8, "dropped"), (32, 2, 8, "hot"), (8, 8, 1, "plain"),
+    (9, 8, 16, "plain"), (5, 13, 16, "hot"), (64, 4, 16, "dropped"),
+]
+
+
+@pytest.mark.parametrize("T,k,E,case", SEVERAL)
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_several_tokens_build_first(lib, T, dtype):
-    E, H, I, k = 16, 512, 256, 4
-    wl = custom_workload(E, H, I, k, dtype=dtype, seed=T + 60)
+def test_several_tokens(lib, T, k, E, case, dtype):
+    H, I = 512, 256
+    wl = custom_workload(E, H, I, k, dtype=dtype, seed=T + k + 60)
     Wr = device_weights(wl)
     Wp = lib.pack_weights(Wr, dtype)
     Wc = {n: v.cpu() for n, v in Wr.items()}
     x, _, _ = make_tokens(wl, T, seed=T + 61)
-    ids = random_ids(T, k, E, seed=T + 62, p_drop=0.1)
+    ids = random_ids(T, k, E, seed=T + k + 62, p_drop=0.1 if case == "dropped" else 0.0)
+    if case == "hot":          # one expert takes three pairs of every token: several row tiles
+        ids[:, :min(3, k)] = 0
     w = random_weights_w(T, k, seed=T + 63)
-    check_case(lib, x, ids, w, Wp, Wc, E, H, I, dtype, f"T={T}")
+    check_case(lib, x, ids, w, Wp, Wc, E, H, I, dtype, f"T={T} {case}")
 
 
-@pytest.mark.parametrize("name", [n for n in ("mixtral", "qwen3", "qwen2", "dsv3")])
-def test_full_size_one_token(lib, name):
+FULL_DECODE = [(n, T) for n in ("mixtral", "qwen3", "qwen2", "dsv3")
+               for T in sorted(set([1] + [t for t in WORKLOADS[n].Ts if t * WORKLOADS[n].k <= 64]))]
+
+
+@pytest.mark.parametrize("name,T", FULL_DECODE)
+def test_full_size_decode(lib, name, T):
     wl = WORKLOADS[name]
     dtype = path_dtype(wl)
     Wp, Wc = workload_weights(name)
-    x, ids, w = make_tokens(wl, 1)
-    check_case(lib, x, ids, w, Wp, Wc, wl.E, wl.H, wl.I, dtype, name)
+    x, ids, w = make_tokens(wl, T)
+    check_case(lib, x, ids, w, Wp, Wc, wl.E, wl.H, wl.I, dtype, f"{name} T={T}")
 
 
+@pytest.mark.parametrize("T", [1, 8])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_graph_capture_new_ids_between_replays(lib, dtype):
+def test_graph_capture_new_ids_between_replays(lib, T, dtype):
     E, H, I, k = 64, 1024, 640, 8
     wl = custom_workload(E, H, I, k, dtype=dtype, seed=70)
     Wr = device_weights(wl)
     Wp = lib.pack_weights(Wr, dtype)
-    x, _, _ = make_tokens(wl, 1, seed=71)
+    x, _, _ = make_tokens(wl, T, seed=71)
     x = x.cuda().bfloat16().contiguous()
-    ids = random_ids(1, k, E, seed=72).cuda()
-    w = random_weights_w(1, k, seed=73).cuda()
-    routing, ws, out = buffers(lib, 1, k, E, H, I, dtype)
+    ids = random_ids(T, k, E, seed=72).cuda()
+    w = random_weights_w(T, k, seed=73).cuda()
+    routing, ws, out = buffers(lib, T, k, E, H, I, dtype)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -165,8 +182,9 @@ def test_graph_capture_new_ids_between_replays(lib, dtype):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         combined(lib, ids, x, w, Wp, dtype, routing, ws, out)
-    draws = [random_ids(1, k, E, seed=74 + r) for r in range(3)]
-    draws[1][0, 3] = draws[1][0, 0]        # an expert named twice
+    draws = [random_ids(T, k, E, seed=74 + r) for r in range(3)]
+    draws[1][:, 3] = draws[1][:, 0]        # an expert named twice
+    draws[1][:, 2] = 5                     # and one in every token (T = 8: 8 pairs)
     draws[2][0, 1] = -1                    # a dropped pair
     for r, new in enumerate(draws):
         ids.copy_(new.cuda())
@@ -174,7 +192,7 @@ def test_graph_capture_new_ids_between_replays(lib, dtype):
         routing.fill_(0xAB)
         g.replay()
         torch.cuda.synchronize()
-        r0, ws0, out0 = buffers(lib, 1, k, E, H, I, dtype)
+        r0, ws0, out0 = buffers(lib, T, k, E, H, I, dtype)
         separate(lib, ids, x, w, Wp, dtype, E, H, I, r0, ws0, out0)
         torch.cuda.synchronize()
         assert torch.equal(out, out0), f"replay {r}: output"
