@@ -344,10 +344,14 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     // T=128 1767 -> 1759 us.  When no strip configuration divides the
     // reductions at that height, a taller one.
     const bool fp8 = dtype == MOE_DTYPE_FP8_W8A8;
-    // heights 4, 8 and 12 row blocks (12 only for fp8, whose strips run to
-    // 160 mean rows: 192-row tiles keep an expert's rows in one tile)
-    const int first = avg <= 40 ? 4 : (avg <= 96 || !fp8 ? 8 : 12);
-    for (int mb = first; mb <= 12; mb = mb == 8 ? 12 : mb * 2) {
+    // heights 4, 8, 10 and 12 row blocks (10 and 12 only for fp8, whose
+    // strips run to 160 mean rows: 160- and 192-row tiles keep an expert's
+    // rows in one tile).  160 rows up to 128 mean rows, where they still hold
+    // a uniform routing's fullest expert (same-box A/B, DeepSeek-V3 fp8:
+    // T=4096, 128 mean rows, 2768 -> 2708 us against 192-row tiles; T=3072,
+    // 96 mean rows, 2516 us against 2447 on 128-row tiles).
+    const int first = avg <= 40 ? 4 : (avg <= 96 || !fp8 ? 8 : (avg <= 128 ? 10 : 12));
+    for (int mb = first; mb <= 12; mb = mb == 8 ? (fp8 ? 10 : 12) : (mb == 10 ? 12 : mb * 2)) {
       long tasks = (P + 16 * mb - 1) / (16 * mb);
       if (tasks < active) tasks = active;
       Plan q = p;

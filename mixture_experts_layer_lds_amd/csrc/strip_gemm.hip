@@ -49,9 +49,13 @@ constexpr int strip_waves() {
   return 16 / NSUB;
 }
 
+// Token chunks a wave copies per stage: the tile's MB * KS chunks spread
+// over the waves, rounded up; the copies past the tile's chunks (160-row
+// tiles: 20 chunks over 8 waves) re-read one line of its first row, so that
+// every wave issues the same number of operations per stage.
 template <int MB, int KS, int NSUB>
 struct StripItem {
-  static constexpr int NA = MB * KS / strip_waves<NSUB>();   // token chunks this wave copies per stage
+  static constexpr int NA = (MB * KS + strip_waves<NSUB>() - 1) / strip_waves<NSUB>();
   int row_begin, rows, s;
   int col;                     // first output column of this wave (of h when fusing SiLU-and-mul)
   const char* a[NA];           // this lane's token sources (K step and lane offsets applied)
@@ -105,13 +109,15 @@ __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::St
 #pragma unroll
   for (int i = 0; i < StripItem<MB, KS, NSUB>::NA; i++) {
     // chunk c = 16-row block c / KS, K step c % KS of every stage
-    const int c = wave + W * i;
+    const int c0 = wave + W * i;
+    const bool pad = c0 >= MB * KS;   // a copy past the tile's chunks
+    const int c = pad ? 0 : c0;
     const int rb = c / KS, st = c % KS;
     // Row blocks past the tile, and rows past it inside the last block,
     // re-read the tile's first row: always a valid address, never stored.
     // A whole block past the tile thus reads one 64-byte line per step
     // (every lane the same row), not 16 rows.
-    const bool blk_in = rb * 16 < task.rows;
+    const bool blk_in = !pad && rb * 16 < task.rows;
     const bool in_tile = blk_in && rb * 16 + lrow < task.rows;
     int arow;
     if constexpr (GATHER) {
@@ -242,8 +248,8 @@ strip_gemm_kernel(moe_host::StripArgs g) {
   // the scale copies (block fp8: row scales; MXFP8: row and weight scales)
   constexpr int PER = NA + KS * NSUB + (BLK ? 1 : (MXS ? 2 : 0));
   constexpr int NST = NBUF + 1;         // LDS ring slots
-  constexpr int TOK = MB * KS * 1024;   // a slot's token chunks
   constexpr int W = strip_waves<NSUB>();
+  constexpr int TOK = NA * W * 1024;    // a slot's token chunks (and padding copies)
   constexpr int RSB = KS / 2 * MB * 64;   // then the row scales (4 bytes per row and unit)
   // then (MXFP8) 256 bytes of weight scales per wave
   constexpr int SLOT = TOK + (BLK ? 1024 : (MXS ? RSB + W * 256 : 0));
@@ -251,7 +257,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
                             blk_row_parts<MB, KS>() <= W && RSB <= 1024),
                 "row-scale copy parts");
   static_assert(!MXS || KS / 2 * NSUB * 16 <= 64, "one weight-scale copy per wave");
-  static_assert(NA >= 1 && NA * W == MB * KS, "token chunks split evenly over waves");
+  static_assert(NA >= 1 && (SC == 0 || NA * W == MB * KS), "token chunks split evenly over waves");
   static_assert(NBUF >= 2, "ring depth");
   static_assert((NBUF - 1) * PER < 64, "vmcnt range");
   extern __shared__ __attribute__((aligned(1024))) char lds[];
@@ -541,7 +547,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
 template <int MB, int KS, int NBUF, int NSUB, bool GATHER, bool FP8, bool I8, int SC = 0>
 static hipError_t launch_strip_t(const moe_host::StripArgs& a, int grid, hipStream_t s) {
   constexpr int lds_bytes =
-      (NBUF + 1) * (MB * KS * 1024 + (SC == 1 ? 1024 : (SC == 2 ? KS / 2 * MB * 64 + strip_waves<NSUB>() * 256 : 0)));
+      (NBUF + 1) * (StripItem<MB, KS, NSUB>::NA * strip_waves<NSUB>() * 1024 + (SC == 1 ? 1024 : (SC == 2 ? KS / 2 * MB * 64 + strip_waves<NSUB>() * 256 : 0)));
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
@@ -561,22 +567,29 @@ static hipError_t launch_strip_t(const moe_host::StripArgs& a, int grid, hipStre
 template <int MB, int KS, int NBUF, int NSUB>
 static hipError_t launch_strip_cfg(const moe_host::StripArgs& a, bool gather, int kind, int grid,
                                    hipStream_t s) {
-  if (kind == 3 || kind == 4) {
-    if constexpr (KS % 2 == 0) {
-      if (kind == 3)
-        return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false, 1>(a, grid, s)
-                      : launch_strip_t<MB, KS, NBUF, NSUB, false, true, false, 1>(a, grid, s);
-      return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false, 2>(a, grid, s)
-                    : launch_strip_t<MB, KS, NBUF, NSUB, false, true, false, 2>(a, grid, s);
+  if constexpr (MB * KS % strip_waves<NSUB>() != 0) {
+    // tiles whose chunks do not split evenly over the waves: per-channel fp8 only
+    if (kind != 1) return hipErrorInvalidValue;
+    return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false>(a, grid, s)
+                  : launch_strip_t<MB, KS, NBUF, NSUB, false, true, false>(a, grid, s);
+  } else {
+    if (kind == 3 || kind == 4) {
+      if constexpr (KS % 2 == 0) {
+        if (kind == 3)
+          return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false, 1>(a, grid, s)
+                        : launch_strip_t<MB, KS, NBUF, NSUB, false, true, false, 1>(a, grid, s);
+        return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false, 2>(a, grid, s)
+                      : launch_strip_t<MB, KS, NBUF, NSUB, false, true, false, 2>(a, grid, s);
+      }
+      return hipErrorInvalidValue;
     }
-    return hipErrorInvalidValue;
+    if (kind == 2) return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, true>(a, grid, s)
+                                 : launch_strip_t<MB, KS, NBUF, NSUB, false, true, true>(a, grid, s);
+    if (gather) return kind == 1 ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false>(a, grid, s)
+                                 : launch_strip_t<MB, KS, NBUF, NSUB, true, false, false>(a, grid, s);
+    return kind == 1 ? launch_strip_t<MB, KS, NBUF, NSUB, false, true, false>(a, grid, s)
+                     : launch_strip_t<MB, KS, NBUF, NSUB, false, false, false>(a, grid, s);
   }
-  if (kind == 2) return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, true>(a, grid, s)
-                               : launch_strip_t<MB, KS, NBUF, NSUB, false, true, true>(a, grid, s);
-  if (gather) return kind == 1 ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false>(a, grid, s)
-                               : launch_strip_t<MB, KS, NBUF, NSUB, true, false, false>(a, grid, s);
-  return kind == 1 ? launch_strip_t<MB, KS, NBUF, NSUB, false, true, false>(a, grid, s)
-                   : launch_strip_t<MB, KS, NBUF, NSUB, false, false, false>(a, grid, s);
 }
 
 }  // namespace moe
@@ -587,11 +600,12 @@ namespace moe_host {
 #define MOE_STRIP_CONFIGS(X) \
   X(4, 2, 4) X(4, 4, 3) X(4, 4, 4) X(4, 2, 3) X(4, 4, 2) X(4, 2, 2) \
   X(8, 2, 4) X(8, 2, 3) X(8, 1, 4) X(8, 2, 2)             \
-  X(12, 2, 4) X(12, 2, 3) X(12, 2, 2)
+  X(12, 2, 4) X(12, 2, 3) X(12, 2, 2) X(10, 2, 4) X(10, 2, 3) X(10, 2, 2)
 
 bool strip_config_supported(int mb, int ks, int nbuf, bool fp8) {
-  // 192-row tiles serve fp8 only (the bf16 ones would spill registers)
-  if (mb == 12 && !fp8) return false;
+  // 160- and 192-row tiles serve fp8 only (the bf16 ones would spill
+  // registers); the 160-row ones the per-channel scales only
+  if ((mb == 12 || mb == 10) && !fp8) return false;
 #define MOE_STRIP_CASE(M, K, N) if (mb == M && ks == K && nbuf == N) return true;
   MOE_STRIP_CONFIGS(MOE_STRIP_CASE)
 #undef MOE_STRIP_CASE

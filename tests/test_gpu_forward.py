@@ -154,7 +154,9 @@ STRIP = [
     (8, 512, 256, 2, 300, 0.02, 2, 2),      # 128-row tiles
     (64, 1024, 640, 8, 256, 0.02, 2, 0),    # 5 strips of 2I, 20-step down reduction
     (64, 2048, 512, 4, 512, 0.0, 2, 2),     # more work items than CUs
-    (16, 512, 256, 4, 512, 0.01, 1, 2),     # 128 rows per expert: LDS tiles on bf16, strips on fp8
+    (16, 512, 256, 4, 512, 0.01, 1, 2),     # 128 rows per expert: LDS tiles on bf16, 160-row strips on fp8
+    (8, 1024, 512, 2, 500, 0.0, 1, 2),      # 125 rows per expert, 160-row fp8 strips, 2-stage down ring
+    (16, 512, 256, 4, 600, 0.0, 1, 2),      # 150 rows per expert: 192-row fp8 strips
 ]
 
 
