@@ -123,10 +123,14 @@ bool choose_strip(int nsteps, int mb, bool fp8, long items, int* split, int* ks,
   // about 12-24 KiB of weights in flight per wave first.  The down GEMM
   // starts from a two-stage ring: its K is the short intermediate width, so
   // a deep ring's fill is a large part of each item (measured 1-2% faster
-  // on the whole layer at 128-4096 tokens, up to 7% on its down kernel).
+  // on the whole layer at 128-4096 tokens, up to 7% on its down kernel).  So
+  // do the 160- and 192-row tiles: there the four-stage ring spills
+  // registers on int8, MXFP8 and block fp8 (same-box A/B at DeepSeek-V3
+  // T=4096, us per layer: int8 2877 -> 2866, MXFP8 3500 -> 3481, block fp8
+  // 3453 -> 3417; per-channel fp8, which does not spill, 2736 against 2739).
   static const int kCfgUp[8][2] = {{2, 4}, {4, 3}, {4, 4}, {2, 3}, {4, 2}, {1, 4}, {2, 2}, {1, 2}};
   static const int kCfgDown[8][2] = {{2, 2}, {2, 4}, {4, 3}, {4, 4}, {2, 3}, {4, 2}, {1, 4}, {1, 2}};
-  const auto& kCfg = down ? kCfgDown : kCfgUp;
+  const auto& kCfg = down || mb >= 10 ? kCfgDown : kCfgUp;
   double best_eff = -1.0;
   for (int S = 1; S <= 8; S *= 2) {
     for (const auto& c : kCfg) {
@@ -260,8 +264,12 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
     // unsplit gate-up, whose epilogue forms the fp32 h that the
     // requantisation reads.
     const bool mx = dtype == MOE_DTYPE_MXFP8;
-    const int first = avg <= 40 ? 4 : (avg <= 96 ? 8 : 12);
-    for (int mb = first; mb <= 12; mb = mb == 8 ? 12 : mb * 2) {
+    // int8 takes 160-row tiles up to 128 mean rows, as per-channel fp8 does
+    // (DeepSeek-V3 int8 T=4096: 2866 -> 2733 us against 192-row tiles); the
+    // MX copies of row scales need whole 64-row parts
+    const bool i8 = dtype == MOE_DTYPE_INT8_W8A8;
+    const int first = avg <= 40 ? 4 : (avg <= 96 ? 8 : (avg <= 128 && i8 ? 10 : 12));
+    for (int mb = first; mb <= 12; mb = mb == 8 ? (i8 ? 10 : 12) : (mb == 10 ? 12 : mb * 2)) {
       long tasks = (P + 16 * mb - 1) / (16 * mb);
       if (tasks < active) tasks = active;
       Plan q = p;

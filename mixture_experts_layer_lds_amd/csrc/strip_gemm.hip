@@ -568,7 +568,10 @@ template <int MB, int KS, int NBUF, int NSUB>
 static hipError_t launch_strip_cfg(const moe_host::StripArgs& a, bool gather, int kind, int grid,
                                    hipStream_t s) {
   if constexpr (MB * KS % strip_waves<NSUB>() != 0) {
-    // tiles whose chunks do not split evenly over the waves: per-channel fp8 only
+    // tiles whose chunks do not split evenly over the waves: the one-byte
+    // per-channel paths (fp8, int8) only
+    if (kind == 2) return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, true>(a, grid, s)
+                                 : launch_strip_t<MB, KS, NBUF, NSUB, false, true, true>(a, grid, s);
     if (kind != 1) return hipErrorInvalidValue;
     return gather ? launch_strip_t<MB, KS, NBUF, NSUB, true, true, false>(a, grid, s)
                   : launch_strip_t<MB, KS, NBUF, NSUB, false, true, false>(a, grid, s);
@@ -603,8 +606,8 @@ namespace moe_host {
   X(12, 2, 4) X(12, 2, 3) X(12, 2, 2) X(10, 2, 4) X(10, 2, 3) X(10, 2, 2)
 
 bool strip_config_supported(int mb, int ks, int nbuf, bool fp8) {
-  // 160- and 192-row tiles serve fp8 only (the bf16 ones would spill
-  // registers); the 160-row ones the per-channel scales only
+  // 160- and 192-row tiles serve the one-byte paths only (the bf16 ones
+  // would spill registers); the 160-row ones per-channel fp8 and int8 only
   if ((mb == 12 || mb == 10) && !fp8) return false;
 #define MOE_STRIP_CASE(M, K, N) if (mb == M && ks == K && nbuf == N) return true;
   MOE_STRIP_CONFIGS(MOE_STRIP_CASE)

@@ -74,6 +74,8 @@ STRIP_SHAPES = [
     (16, 256, 256, 8, 100, 0.0, 128, 1),
     (64, 512, 512, 8, 1200, 0.0, 192, 2),
     (32, 256, 2048, 4, 200, 0.05, 64, 8),
+    (64, 512, 1024, 8, 960, 0.0, 160, 2),     # 120 rows per expert: 160-row tiles
+    (64, 1024, 1024, 8, 960, 0.02, 160, 1),
 ]
 
 
