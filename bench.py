@@ -140,8 +140,9 @@ class Layer:
 
     def run(self, W=None):
         """One layer: routing build + forward.  bf16 and fp8 make it one
-        library call, which routes a single token inside the forward's first
-        kernel; the other dtypes call the routing build first."""
+        library call, which routes a decode batch (at most 64 pairs) inside
+        the forward's first kernel; the other dtypes call the routing build
+        first."""
         m, W = self.moe, (W or self.W)
         if self.dtype == "bf16":
             m.moe_route_forward_bf16(self.ids, self.x, self.w, self.routing, W["w1"], W["w2"], self.ws,
@@ -157,7 +158,7 @@ class Layer:
 def stage_pass(layer, steps):
     """Untimed pass with HIP events around every stage (library stage hook)
     and around the routing build, which runs here as its own launch (the
-    layer steps fold it into the forward's first kernel for one token).
+    layer steps fold it into the forward's first kernel at decode).
     Each event record costs a few microseconds of stream time, so these
     steps are not the timed ones."""
     import torch
