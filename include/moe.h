@@ -351,6 +351,28 @@ int moe_route_forward_fp8(const int32_t *topk_ids, const void *x, const float *t
                           const moe_packed_weights_t *w2, const float *w2_scale,
                           int T, int k, int E, int H, int I,
                           void *workspace, size_t workspace_bytes, void *out, void *stream);
+/* The same for the quantised layers below: moe_build_routing_int8 /
+ * _fp8_block / _mxfp8 followed by moe_forward_int8 / _fp8_block / _mxfp8,
+ * in one call, with the same results; at most 64 pairs on the
+ * register-streaming plan are routed inside the x quantisation. */
+int moe_route_forward_int8(const int32_t *topk_ids, const void *x, const float *topk_w,
+                           void *routing, size_t routing_bytes,
+                           const moe_packed_weights_t *w1, const float *w1_scale,
+                           const moe_packed_weights_t *w2, const float *w2_scale,
+                           int T, int k, int E, int H, int I,
+                           void *workspace, size_t workspace_bytes, void *out, void *stream);
+int moe_route_forward_fp8_block(const int32_t *topk_ids, const void *x, const float *topk_w,
+                                void *routing, size_t routing_bytes,
+                                const moe_packed_weights_t *w1, const float *w1_scale,
+                                const moe_packed_weights_t *w2, const float *w2_scale,
+                                int T, int k, int E, int H, int I,
+                                void *workspace, size_t workspace_bytes, void *out, void *stream);
+int moe_route_forward_mxfp8(const int32_t *topk_ids, const void *x, const float *topk_w,
+                            void *routing, size_t routing_bytes,
+                            const moe_packed_weights_t *w1, const uint8_t *w1_scale,
+                            const moe_packed_weights_t *w2, const uint8_t *w2_scale,
+                            int T, int k, int E, int H, int I,
+                            void *workspace, size_t workspace_bytes, void *out, void *stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the fp8

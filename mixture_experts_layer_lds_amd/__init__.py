@@ -111,7 +111,8 @@ EXPORTS = ("moe_status_string", "moe_pack_weights", "moe_describe_packed_weights
            "moe_forward_fp8", "moe_forward_mxfp8", "moe_forward_int8", "moe_forward_int4",
            "moe_build_routing_fp8_block", "moe_forward_fp8_block",
            "moe_build_routing_int8_w8a16", "moe_forward_int8_w8a16", "moe_set_stage_events", "moe_device_cu_count",
-           "moe_stream_read", "moe_forward_fp8_noalloc", "moe_route_forward_bf16", "moe_route_forward_fp8")
+           "moe_stream_read", "moe_forward_fp8_noalloc", "moe_route_forward_bf16", "moe_route_forward_fp8",
+           "moe_route_forward_int8", "moe_route_forward_fp8_block", "moe_route_forward_mxfp8")
 
 
 def _load():
@@ -172,6 +173,9 @@ def _load():
     L.moe_route_forward_bf16.argtypes = [P, P, P, P, sz, D, D, i, i, i, i, i, P, sz, P, P]
     L.moe_route_forward_fp8.restype = i
     L.moe_route_forward_fp8.argtypes = [P, P, P, P, sz, D, P, D, P, i, i, i, i, i, P, sz, P, P]
+    for f in (L.moe_route_forward_int8, L.moe_route_forward_fp8_block, L.moe_route_forward_mxfp8):
+        f.restype = i
+        f.argtypes = [P, P, P, P, sz, D, P, D, P, i, i, i, i, i, P, sz, P, P]
     return L
 
 
@@ -495,6 +499,58 @@ def moe_route_forward_fp8(topk_ids, x, topk_w, routing, w1, w1_scale, w2, w2_sca
         _desc("w2", w2), _ptr(w2_scale), T, k, E, H, I, _ptr(workspace), workspace.numel(), _ptr(out),
         _stream(stream)))
     return out
+
+
+def _route_forward_q(fn, name, topk_ids, x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, out,
+                     stream, scale_dtype, scale_shape):
+    T, H = x.shape
+    k = topk_w.shape[1]
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    _check_tensor("topk_ids", topk_ids, torch.int32, (T, k))
+    _check_tensor("x", x, torch.bfloat16, (T, H))
+    _check_tensor("topk_w", topk_w, torch.float32, (T, k))
+    _check_tensor("w1_scale", w1_scale, scale_dtype, scale_shape(E, 2 * I, H))
+    _check_tensor("w2_scale", w2_scale, scale_dtype, scale_shape(E, H, I))
+    _check_tensor("out", out, torch.bfloat16, (T, H))
+    _check(name, fn(_ptr(topk_ids), _ptr(x), _ptr(topk_w), _ptr(routing), routing.numel(), _desc("w1", w1),
+                    _ptr(w1_scale), _desc("w2", w2), _ptr(w2_scale), T, k, E, H, I, _ptr(workspace),
+                    workspace.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_route_forward_int8(topk_ids, x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, out,
+                           stream=None):
+    """moe_build_routing_int8 + moe_forward_int8 in one call."""
+    return _route_forward_q(_lib.moe_route_forward_int8, "moe_route_forward_int8", topk_ids, x, topk_w, routing,
+                            w1, w1_scale, w2, w2_scale, workspace, out, stream, torch.float32,
+                            lambda E, N, K: (E, N))
+
+
+def moe_route_forward_fp8_block(topk_ids, x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, out,
+                                stream=None):
+    """moe_build_routing_fp8_block + moe_forward_fp8_block in one call."""
+    return _route_forward_q(_lib.moe_route_forward_fp8_block, "moe_route_forward_fp8_block", topk_ids, x, topk_w,
+                            routing, w1, w1_scale, w2, w2_scale, workspace, out, stream, torch.float32,
+                            lambda E, N, K: (E, N // 128, K // 128))
+
+
+def moe_route_forward_mxfp8(topk_ids, x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, out,
+                            stream=None):
+    """moe_build_routing_mxfp8 + moe_forward_mxfp8 in one call."""
+    return _route_forward_q(_lib.moe_route_forward_mxfp8, "moe_route_forward_mxfp8", topk_ids, x, topk_w,
+                            routing, w1, w1_scale, w2, w2_scale, workspace, out, stream, torch.uint8,
+                            lambda E, N, K: (E, N, K // 32))
+
+
+def route_forward(topk_ids, x, topk_w, routing, weights, workspace, out, dtype="bf16", stream=None):
+    """Routing build + forward in one library call (bf16, fp8, int8, fp8b, mxfp8)."""
+    W = weights
+    if dtype == "bf16":
+        return moe_route_forward_bf16(topk_ids, x, topk_w, routing, W["w1"], W["w2"], workspace, out, stream)
+    fn = {"fp8": moe_route_forward_fp8, "int8": moe_route_forward_int8, "fp8b": moe_route_forward_fp8_block,
+          "mxfp8": moe_route_forward_mxfp8}[dtype]
+    return fn(topk_ids, x, topk_w, routing, W["w1"], W["w1_scale"], W["w2"], W["w2_scale"], workspace, out, stream)
 
 
 STATIC_WORKSPACE_BYTES = 64 << 20

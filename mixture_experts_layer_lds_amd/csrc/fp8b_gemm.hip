@@ -27,6 +27,7 @@
 //    scale is the top-k reduction's).  Four MFMAs of 16x16x32 per 128
 //    values become one of 16x16x128.
 #include "lds_dma.h"
+#include "decode_route.h"
 
 namespace moe {
 
@@ -219,12 +220,25 @@ stream_fp8b_kernel(moe_host::StreamArgs g) {
 // Codes to q[row][..]; scales to group_scale[row][g] (when not null) and,
 // unit-major, to rows_scale[g][dst_row] for each destination row: the
 // sorted rows of the token's zk pairs (x), or the row itself (h).
-template <bool BF16_IN>
+// ROUTE (token rows, at most 64 pairs): the launch also does the routing
+// build, and the sorted rows of each token's zk pairs come from there.
+template <bool BF16_IN, bool ROUTE = false>
 __global__ void __launch_bounds__(256)
 quant_groups_kernel(const void* __restrict__ in, int n, int nrows, const int32_t* __restrict__ expert_offsets,
                     int E, uint8_t* __restrict__ q, float* __restrict__ group_scale,
-                    float* __restrict__ rows_scale, int P, int zk, const int32_t* __restrict__ pair_pos) {
+                    float* __restrict__ rows_scale, int P, int zk, const int32_t* __restrict__ pair_pos,
+                    moe_host::DecodeRouteOut route) {
+  static_assert(!ROUTE || BF16_IN, "the folded routing build serves the token rows");
   const int r = blockIdx.x;
+  __shared__ int s_rows[kMaxTopK];   // ROUTE: sorted rows of this token's pairs
+  if constexpr (ROUTE) {
+    const int lane = threadIdx.x & 63;
+    const DecodeRoute rt = decode_route(route.ids, P, route.E, route.block_m, lane);
+    if (r == 0) decode_route_write(rt, route, P, threadIdx.x, 256, lane, threadIdx.x >> 6);
+    const int pj = __shfl(rt.pos, min(r * zk + lane, P - 1), kWave);
+    if (threadIdx.x < zk) s_rows[threadIdx.x] = pj;
+    __syncthreads();
+  }
   const int valid = BF16_IN ? nrows : expert_offsets[E];
   if (r >= valid) return;   // block-uniform
   const int nvec = n / 8;
@@ -260,7 +274,8 @@ quant_groups_kernel(const void* __restrict__ in, int n, int nrows, const int32_t
       const int gidx = i / 16;
       if (group_scale) group_scale[(size_t)r * groups + gidx] = sc;
       if constexpr (BF16_IN) {
-        for (int j = 0; j < zk; j++) rows_scale[(size_t)gidx * P + pair_pos[(size_t)r * zk + j]] = sc;
+        for (int j = 0; j < zk; j++)
+          rows_scale[(size_t)gidx * P + (ROUTE ? s_rows[j] : pair_pos[(size_t)r * zk + j])] = sc;
       } else {
         rows_scale[(size_t)gidx * P + r] = sc;
       }
@@ -313,16 +328,22 @@ hipError_t launch_stream_fp8b(const StreamArgs& a, bool gateup, bool block, int 
 
 hipError_t launch_quant_groups_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* group_scale,
                                     float* rows_scale, int P, int zk, const int32_t* pair_pos,
-                                    hipStream_t s) {
-  hipLaunchKernelGGL(moe::quant_groups_kernel<true>, dim3(T), dim3(256), 0, s, x, H, T, nullptr, 0, xq,
-                     group_scale, rows_scale, P, zk, pair_pos);
+                                    hipStream_t s, const DecodeRouteOut* route) {
+  if (route && ((long)T * zk > moe::kDecodeRoutePairs || P != T * zk || !route->ids)) return hipErrorInvalidValue;
+  const DecodeRouteOut ro = route ? *route : DecodeRouteOut{};
+  if (route)
+    hipLaunchKernelGGL((moe::quant_groups_kernel<true, true>), dim3(T), dim3(256), 0, s, x, H, T, nullptr, 0, xq,
+                       group_scale, rows_scale, P, zk, pair_pos, ro);
+  else
+    hipLaunchKernelGGL((moe::quant_groups_kernel<true, false>), dim3(T), dim3(256), 0, s, x, H, T, nullptr, 0,
+                       xq, group_scale, rows_scale, P, zk, pair_pos, ro);
   return hipGetLastError();
 }
 
 hipError_t launch_requant_groups(const float* h, int P, int I, const int32_t* expert_offsets, int E,
                                  uint8_t* hq, float* rows_scale, hipStream_t s) {
-  hipLaunchKernelGGL(moe::quant_groups_kernel<false>, dim3(P), dim3(256), 0, s, h, I, P, expert_offsets,
-                     E, hq, nullptr, rows_scale, P, 1, nullptr);
+  hipLaunchKernelGGL((moe::quant_groups_kernel<false, false>), dim3(P), dim3(256), 0, s, h, I, P, expert_offsets,
+                     E, hq, nullptr, rows_scale, P, 1, nullptr, DecodeRouteOut{});
   return hipGetLastError();
 }
 

@@ -4,6 +4,7 @@
 // (divisions in fp64), code = clamp(round_half_even(fp32(v * inv)),
 // -127, 127); an all-zero row gets scale 1 and codes 0.
 #include "moe_common.h"
+#include "decode_route.h"
 
 namespace moe {
 
@@ -44,12 +45,24 @@ __device__ __forceinline__ float block_max_i8(float v, float* s_red) {
 // x[T][H] bf16 -> xq[T][H] int8 + scale[T]; one workgroup per token.  Also
 // clears the row-amax slots zero_rows[t*zk ..) of the token's pairs and
 // writes its scale at the sorted row of each of its zk pairs.
+// ROUTE (at most 64 pairs): the launch also does the routing build, and the
+// sorted rows of each token's zk pairs come from there.
+template <bool ROUTE>
 __global__ void __launch_bounds__(kI8Threads)
 quant_rows_i8_kernel(const uint16_t* __restrict__ x, int H, int8_t* __restrict__ xq,
                      float* __restrict__ scale, float* __restrict__ zero_rows, int zk,
-                     const int32_t* __restrict__ pair_pos, float* __restrict__ scale_rows) {
+                     const int32_t* __restrict__ pair_pos, float* __restrict__ scale_rows,
+                     moe_host::DecodeRouteOut route) {
   __shared__ float s_red[4];
   const int t = blockIdx.x;
+  int row_j = 0;   // ROUTE: the sorted row of pair t * zk + lane (lanes < zk)
+  if constexpr (ROUTE) {
+    const int P = gridDim.x * zk;
+    const int lane = threadIdx.x & 63;
+    const DecodeRoute rt = decode_route(route.ids, P, route.E, route.block_m, lane);
+    if (t == 0) decode_route_write(rt, route, P, threadIdx.x, kI8Threads, lane, threadIdx.x >> 6);
+    row_j = __shfl(rt.pos, min(t * zk + lane, P - 1), kWave);
+  }
   if (zero_rows && threadIdx.x < zk) zero_rows[(size_t)t * zk + threadIdx.x] = 0.0f;
   const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
   const int nvec = H / 8;
@@ -80,7 +93,8 @@ quant_rows_i8_kernel(const uint16_t* __restrict__ x, int H, int8_t* __restrict__
     out[i] = q;
   }
   if (threadIdx.x == 0) scale[t] = sc;
-  if (scale_rows && threadIdx.x < zk) scale_rows[pair_pos[(size_t)t * zk + threadIdx.x]] = sc;
+  if (scale_rows && threadIdx.x < zk)   // wave 0: lane j holds pair j of the token
+    scale_rows[ROUTE ? row_j : pair_pos[(size_t)t * zk + threadIdx.x]] = sc;
 }
 
 // fp32 rows h32[r][0..I) of the valid sorted rows -> int8 codes, with the
@@ -109,9 +123,15 @@ namespace moe_host {
 
 hipError_t launch_quant_rows_i8(const uint16_t* x, int T, int H, int8_t* xq, float* scale,
                                 float* zero_rows, int zk, const int32_t* pair_pos, float* scale_rows,
-                                hipStream_t s) {
-  hipLaunchKernelGGL(moe::quant_rows_i8_kernel, dim3(T), dim3(moe::kI8Threads), 0, s, x, H, xq, scale,
-                     zero_rows, zk, pair_pos, scale_rows);
+                                hipStream_t s, const DecodeRouteOut* route) {
+  if (route && ((long)T * zk > moe::kDecodeRoutePairs || !route->ids)) return hipErrorInvalidValue;
+  const DecodeRouteOut ro = route ? *route : DecodeRouteOut{};
+  if (route)
+    hipLaunchKernelGGL(moe::quant_rows_i8_kernel<true>, dim3(T), dim3(moe::kI8Threads), 0, s, x, H, xq, scale,
+                       zero_rows, zk, pair_pos, scale_rows, ro);
+  else
+    hipLaunchKernelGGL(moe::quant_rows_i8_kernel<false>, dim3(T), dim3(moe::kI8Threads), 0, s, x, H, xq, scale,
+                       zero_rows, zk, pair_pos, scale_rows, ro);
   return hipGetLastError();
 }
 

@@ -687,7 +687,8 @@ RoutingView view_routing(const void* routing, const moe_routing_layout_t& L) {
 // streaming down (bf16 rows), top-k reduction.
 int forward_mx(const void* x, const float* topk_w, const void* routing, const void* w1,
                const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, int T, int k, int E,
-               int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+               int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream,
+               const moe_host::DecodeRouteOut* fold = nullptr) {
   int rc = check_shape(T, k, E, H, I, MOE_DTYPE_MXFP8);
   if (rc != MOE_OK) return rc;
   if (T == 0) return MOE_OK;
@@ -718,7 +719,7 @@ int forward_mx(const void* x, const float* topk_w, const void* routing, const vo
   hipError_t e;
   {
     StageScope st(s, 0);
-    e = moe_host::launch_mx_quant_bf16(static_cast<const uint16_t*>(x), T, H, xq, sx, s);
+    e = moe_host::launch_mx_quant_bf16(static_cast<const uint16_t*>(x), T, H, xq, sx, s, fold, P);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (p.tiling == kStrips) {
@@ -842,7 +843,8 @@ int forward_mx(const void* x, const float* topk_w, const void* routing, const vo
 // rows), top-k reduction.
 int forward_fp8b(const void* x, const float* topk_w, const void* routing, const void* w1,
                  const float* w1_scale, const void* w2, const float* w2_scale, int T, int k, int E,
-                 int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+                 int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream,
+                 const moe_host::DecodeRouteOut* fold = nullptr) {
   int rc = check_shape(T, k, E, H, I, MOE_DTYPE_FP8_BLOCK);
   if (rc != MOE_OK) return rc;
   if (T == 0) return MOE_OK;
@@ -874,7 +876,7 @@ int forward_fp8b(const void* x, const float* topk_w, const void* routing, const 
     StageScope st(s, 0);
     e = moe_host::launch_quant_groups_bf16(static_cast<const uint16_t*>(x), T, H, xq,
                                            reinterpret_cast<float*>(ws + W.x_scale), x_rows, P, k,
-                                           R.pair_pos, s);
+                                           R.pair_pos, s, fold);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (p.tiling == kStrips) {
@@ -1077,7 +1079,8 @@ int forward_w4(int dtype, const void* x, const float* topk_w, const void* routin
 // fp8 streaming sequence with int8 quantisation and the integer MFMA.
 int forward_i8(const void* x, const float* topk_w, const void* routing, const void* w1,
                const float* w1_scale, const void* w2, const float* w2_scale, int T, int k, int E,
-               int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+               int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream,
+               const moe_host::DecodeRouteOut* fold = nullptr) {
   int rc = check_shape(T, k, E, H, I, MOE_DTYPE_INT8_W8A8);
   if (rc != MOE_OK) return rc;
   if (T == 0) return MOE_OK;
@@ -1109,7 +1112,7 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
   {
     StageScope st(s, 0);
     e = moe_host::launch_quant_rows_i8(static_cast<const uint16_t*>(x), T, H, xq, x_scale, nullptr, k,
-                                       R.pair_pos, x_rows, s);
+                                       R.pair_pos, x_rows, s, fold);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   if (p.tiling == kStrips) {
@@ -1229,19 +1232,23 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
 // Pointer, alignment and workspace-size rules of the bf16 / fp8 forward
 // pass (checked before anything is launched).
 int check_forward_args(int dtype, const void* x, const float* topk_w, const void* routing, const void* w1,
-                       const float* w1_scale, const void* w2, const float* w2_scale, int T, int k, int E,
+                       const void* w1_scale, const void* w2, const void* w2_scale, int T, int k, int E,
                        int H, int I, const void* workspace, size_t workspace_bytes, const void* out) {
-  const int rc = check_shape(T, k, E, H, I);
+  const bool generic = dtype == MOE_DTYPE_BF16 || dtype == MOE_DTYPE_FP8_W8A8;
+  const int rc = generic ? check_shape(T, k, E, H, I) : check_shape(T, k, E, H, I, dtype);
   if (rc != MOE_OK || T == 0) return rc;
-  const bool fp8 = dtype == MOE_DTYPE_FP8_W8A8;
+  const bool scaled = dtype != MOE_DTYPE_BF16;   // per-channel, block or MX scales
   if (!x || !topk_w || !routing || !w1 || !w2 || !workspace || !out) return MOE_ERR_INVALID_ARG;
-  if (fp8 && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (scaled && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16) ||
       !aligned(topk_w, 4) || !aligned(routing, 16) || !aligned(workspace, 256))
     return MOE_ERR_INVALID_ARG;
-  if (fp8 && (!aligned(w1_scale, 4) || !aligned(w2_scale, 4))) return MOE_ERR_INVALID_ARG;
+  if (scaled && (!aligned(w1_scale, 4) || !aligned(w2_scale, 4))) return MOE_ERR_INVALID_ARG;
+  const Plan p = make_plan(dtype, T, k, E, H, I);
+  if (dtype == MOE_DTYPE_MXFP8 && p.tiling == kStreaming && (p.su1 != 2 || p.su2 != 2))
+    return MOE_ERR_UNSUPPORTED_SHAPE;
   moe_workspace_layout_t W;
-  workspace_layout(dtype, T, k, H, I, make_plan(dtype, T, k, E, H, I), &W);
+  workspace_layout(dtype, T, k, H, I, p, &W);
   return workspace_bytes < W.total_bytes ? MOE_ERR_BUFFER_TOO_SMALL : MOE_OK;
 }
 
@@ -1494,11 +1501,13 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
 }
 
 // Routing build and forward pass in one call.  A decode batch of at most 64
-// pairs on 16-row streaming tiles is routed inside the forward's first
-// kernel; otherwise the routing build runs as its own launch first.
+// pairs on the register-streaming plan is routed inside the forward's first
+// kernel (the x quantisation on the dtypes with quantised activations, the
+// gate-up GEMM on bf16); otherwise the routing build runs as its own launch
+// first.  bf16, per-channel fp8, int8 w8a8, block fp8 and MXFP8.
 int route_forward(int dtype, const int32_t* ids, const void* x, const float* topk_w, void* routing,
-                  size_t routing_bytes, const void* w1, const float* w1_scale, const void* w2,
-                  const float* w2_scale, int T, int k, int E, int H, int I, void* workspace,
+                  size_t routing_bytes, const void* w1, const void* w1_scale, const void* w2,
+                  const void* w2_scale, int T, int k, int E, int H, int I, void* workspace,
                   size_t workspace_bytes, void* out, void* stream) {
   int rc = check_forward_args(dtype, x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I,
                               workspace, workspace_bytes, out);
@@ -1508,9 +1517,28 @@ int route_forward(int dtype, const int32_t* ids, const void* x, const float* top
   moe_routing_layout_t L;
   routing_layout(T, k, E, p, &L);
   if (routing_bytes < L.total_bytes) return MOE_ERR_BUFFER_TOO_SMALL;
-  // fp8: the x quantisation comes first and takes any plan; bf16: the
-  // gate-up kernels on 16-row tiles
-  const bool first_takes_it = dtype == MOE_DTYPE_FP8_W8A8 || (p.mb == 1 && (p.half1 || p.nb == 2));
+  auto run = [&](const moe_host::DecodeRouteOut* f) {
+    const float* s1 = static_cast<const float*>(w1_scale);
+    const float* s2 = static_cast<const float*>(w2_scale);
+    switch (dtype) {
+      case MOE_DTYPE_INT8_W8A8:
+        return forward_i8(x, topk_w, routing, w1, s1, w2, s2, T, k, E, H, I, workspace, workspace_bytes, out,
+                          stream, f);
+      case MOE_DTYPE_FP8_BLOCK:
+        return forward_fp8b(x, topk_w, routing, w1, s1, w2, s2, T, k, E, H, I, workspace, workspace_bytes,
+                            out, stream, f);
+      case MOE_DTYPE_MXFP8:
+        return forward_mx(x, topk_w, routing, w1, static_cast<const uint8_t*>(w1_scale), w2,
+                          static_cast<const uint8_t*>(w2_scale), T, k, E, H, I, workspace, workspace_bytes,
+                          out, stream, f);
+      default:
+        return forward(dtype, x, topk_w, routing, w1, s1, w2, s2, T, k, E, H, I, workspace,
+                       workspace_bytes, out, stream, f);
+    }
+  };
+  // the x quantisation comes first and takes any plan; bf16: the gate-up
+  // kernels on 16-row tiles
+  const bool first_takes_it = dtype != MOE_DTYPE_BF16 || (p.mb == 1 && (p.half1 || p.nb == 2));
   if ((long)T * k <= moe::kDecodeRoutePairs && p.tiling == kStreaming && first_takes_it) {
     char* b = static_cast<char*>(routing);
     moe_host::DecodeRouteOut f;
@@ -1523,13 +1551,11 @@ int route_forward(int dtype, const int32_t* ids, const void* x, const float* top
     f.E = E;
     f.block_m = p.block_m;
     f.max_tasks = p.max_tasks;
-    return forward(dtype, x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
-                   workspace_bytes, out, stream, &f);
+    return run(&f);
   }
   rc = build_routing(dtype, ids, T, k, E, H, I, routing, routing_bytes, stream);
   if (rc != MOE_OK) return rc;
-  return forward(dtype, x, topk_w, routing, w1, w1_scale, w2, w2_scale, T, k, E, H, I, workspace,
-                 workspace_bytes, out, stream);
+  return run(nullptr);
 }
 
 // Shape and pointer rules of a packed weight tensor; its row length in bytes.
@@ -1826,6 +1852,40 @@ int moe_route_forward_fp8(const int32_t* topk_ids, const void* x, const float* t
   const int rc = check_packed(MOE_DTYPE_FP8_W8A8, w1, w2, T, k, E, H, I);
   if (rc != MOE_OK || T == 0) return rc;
   return route_forward(MOE_DTYPE_FP8_W8A8, topk_ids, x, topk_w, routing, routing_bytes, packed_data(w1),
+                       w1_scale, packed_data(w2), w2_scale, T, k, E, H, I, workspace, workspace_bytes, out,
+                       stream);
+}
+
+int moe_route_forward_int8(const int32_t* topk_ids, const void* x, const float* topk_w, void* routing,
+                           size_t routing_bytes, const moe_packed_weights_t* w1, const float* w1_scale,
+                           const moe_packed_weights_t* w2, const float* w2_scale, int T, int k, int E, int H,
+                           int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const int rc = check_packed(MOE_DTYPE_INT8_W8A8, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return route_forward(MOE_DTYPE_INT8_W8A8, topk_ids, x, topk_w, routing, routing_bytes, packed_data(w1),
+                       w1_scale, packed_data(w2), w2_scale, T, k, E, H, I, workspace, workspace_bytes, out,
+                       stream);
+}
+
+int moe_route_forward_fp8_block(const int32_t* topk_ids, const void* x, const float* topk_w, void* routing,
+                                size_t routing_bytes, const moe_packed_weights_t* w1, const float* w1_scale,
+                                const moe_packed_weights_t* w2, const float* w2_scale, int T, int k, int E,
+                                int H, int I, void* workspace, size_t workspace_bytes, void* out,
+                                void* stream) {
+  const int rc = check_packed(MOE_DTYPE_FP8_BLOCK, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return route_forward(MOE_DTYPE_FP8_BLOCK, topk_ids, x, topk_w, routing, routing_bytes, packed_data(w1),
+                       w1_scale, packed_data(w2), w2_scale, T, k, E, H, I, workspace, workspace_bytes, out,
+                       stream);
+}
+
+int moe_route_forward_mxfp8(const int32_t* topk_ids, const void* x, const float* topk_w, void* routing,
+                            size_t routing_bytes, const moe_packed_weights_t* w1, const uint8_t* w1_scale,
+                            const moe_packed_weights_t* w2, const uint8_t* w2_scale, int T, int k, int E, int H,
+                            int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const int rc = check_packed(MOE_DTYPE_MXFP8, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return route_forward(MOE_DTYPE_MXFP8, topk_ids, x, topk_w, routing, routing_bytes, packed_data(w1),
                        w1_scale, packed_data(w2), w2_scale, T, k, E, H, I, workspace, workspace_bytes, out,
                        stream);
 }

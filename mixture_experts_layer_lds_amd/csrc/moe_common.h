@@ -355,9 +355,10 @@ hipError_t launch_stream_gemm(const StreamArgs& a, bool gateup, bool fp8, int ki
 // int8 w8a8: per-token quantisation of bf16 x (row-amax slots cleared,
 // per-sorted-row scales written as the fp8 variant) and per-row
 // requantisation of fp32 h (the row amax found from the row).
+// With route (T * zk <= 64) the x quantisation also does the routing build.
 hipError_t launch_quant_rows_i8(const uint16_t* x, int T, int H, int8_t* xq, float* scale,
                                 float* zero_rows, int zk, const int32_t* pair_pos, float* scale_rows,
-                                hipStream_t s);
+                                hipStream_t s, const DecodeRouteOut* route = nullptr);
 hipError_t launch_requant_rows_i8(const float* h32, int P, int I, const int32_t* expert_offsets, int E,
                                   int8_t* hq, float* h_scale, hipStream_t s);
 // int8 w8a16 register-streaming GEMM: a bf16 rows, b packed int8 weights
@@ -379,9 +380,10 @@ hipError_t launch_stream_fp8b(const StreamArgs& a, bool gateup, bool block, int 
 // token [T][H/128] and per sorted row of each of the token's zk pairs,
 // unit-major [H/128][P]); fp32 rows h of the valid sorted rows (scales
 // unit-major [I/128][P]).
+// With route (P = T * zk <= 64) the launch also does the routing build.
 hipError_t launch_quant_groups_bf16(const uint16_t* x, int T, int H, uint8_t* xq, float* group_scale,
                                     float* rows_scale, int P, int zk, const int32_t* pair_pos,
-                                    hipStream_t s);
+                                    hipStream_t s, const DecodeRouteOut* route = nullptr);
 hipError_t launch_requant_groups(const float* h, int P, int I, const int32_t* expert_offsets, int E,
                                  uint8_t* hq, float* rows_scale, hipStream_t s);
 // int4 w4a16 register-streaming GEMM: a bf16 activations, b packed int4
@@ -391,7 +393,9 @@ hipError_t launch_stream_w4(const StreamArgs& a, bool gateup, int mb, int waves,
                             int nb = 2);
 // MXFP8 quantisation: bf16 rows x[T][H] -> e4m3 xq + e8m0 codes [T][H/32];
 // fp32 rows h[P][I] (valid sorted rows only) -> hq + codes [P][I/32].
-hipError_t launch_mx_quant_bf16(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* sx, hipStream_t s);
+// With route (P <= 64 pairs) the launch also does the routing build.
+hipError_t launch_mx_quant_bf16(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* sx, hipStream_t s,
+                                const DecodeRouteOut* route = nullptr, int P = 0);
 hipError_t launch_mx_requant(const float* h, int P, int I, const int32_t* expert_offsets, int E,
                              uint8_t* hq, uint8_t* sh, hipStream_t s);
 

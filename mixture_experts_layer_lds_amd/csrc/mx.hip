@@ -11,6 +11,7 @@
 // loads, its 32 codes leave in two 16-byte stores and its scale code in one
 // byte; consecutive threads take consecutive blocks of a row.
 #include "moe_common.h"
+#include "decode_route.h"
 
 namespace moe {
 
@@ -33,9 +34,19 @@ __device__ __forceinline__ void mx_encode32(const float (&v)[32], int s, u32x4& 
   hi = u32x4{w[4], w[5], w[6], w[7]};
 }
 
+// ROUTE (at most 64 pairs): workgroup 0 also does the routing build (the
+// x codes do not depend on the routing).
+template <bool ROUTE>
 __global__ void __launch_bounds__(kMxThreads)
 mx_quant_bf16_kernel(const uint16_t* __restrict__ x, long nblocks, uint8_t* __restrict__ xq,
-                     uint8_t* __restrict__ sx) {
+                     uint8_t* __restrict__ sx, moe_host::DecodeRouteOut route, int P) {
+  if constexpr (ROUTE) {
+    if (blockIdx.x == 0) {
+      const int lane = threadIdx.x & 63;
+      const DecodeRoute rt = decode_route(route.ids, P, route.E, route.block_m, lane);
+      decode_route_write(rt, route, P, threadIdx.x, kMxThreads, lane, threadIdx.x >> 6);
+    }
+  }
   const long blk = (long)blockIdx.x * kMxThreads + threadIdx.x;
   if (blk >= nblocks) return;
   const u32x4* src = reinterpret_cast<const u32x4*>(x + blk * 32);
@@ -93,10 +104,16 @@ mx_requant_kernel(const float* __restrict__ h, int I, const int32_t* __restrict_
 
 namespace moe_host {
 
-hipError_t launch_mx_quant_bf16(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* sx, hipStream_t s) {
+hipError_t launch_mx_quant_bf16(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* sx, hipStream_t s,
+                                const DecodeRouteOut* route, int P) {
+  if (route && (P > moe::kDecodeRoutePairs || !route->ids)) return hipErrorInvalidValue;
   const long n = (long)T * (H / 32);
-  hipLaunchKernelGGL(moe::mx_quant_bf16_kernel, dim3((unsigned)((n + moe::kMxThreads - 1) / moe::kMxThreads)),
-                     dim3(moe::kMxThreads), 0, s, x, n, xq, sx);
+  const dim3 grid((unsigned)((n + moe::kMxThreads - 1) / moe::kMxThreads));
+  const DecodeRouteOut ro = route ? *route : DecodeRouteOut{};
+  if (route)
+    hipLaunchKernelGGL(moe::mx_quant_bf16_kernel<true>, grid, dim3(moe::kMxThreads), 0, s, x, n, xq, sx, ro, P);
+  else
+    hipLaunchKernelGGL(moe::mx_quant_bf16_kernel<false>, grid, dim3(moe::kMxThreads), 0, s, x, n, xq, sx, ro, P);
   return hipGetLastError();
 }
 

@@ -1,7 +1,8 @@
 """The routing build and the forward pass in one call (moe_route_forward_bf16
-/ _fp8).  For a decode batch of at most 64 token-expert pairs the routing
-build runs inside the forward's first kernel (bf16: the gate-up GEMM, fp8:
-the x quantisation), whose workgroup 0 writes the routing buffer.
+/ _fp8 / _int8 / _fp8_block / _mxfp8).  For a decode batch of at most 64 token-expert pairs the routing
+build runs inside the forward's first kernel (bf16: the gate-up GEMM, the
+quantised dtypes: the x quantisation), whose workgroup 0 writes the routing
+buffer.
 
 Checked on every case:
 - the routing buffer holds the same bytes as after moe_build_routing_* (both
@@ -40,15 +41,13 @@ def separate(lib, ids, x, w, Wp, dtype, E, H, I, routing, ws, out):
     if dtype == "bf16":
         lib.moe_forward_bf16(x, w, routing, Wp["w1"], Wp["w2"], ws, out)
     else:
-        lib.moe_forward_fp8(x, w, routing, Wp["w1"], Wp["w1_scale"], Wp["w2"], Wp["w2_scale"], ws, out)
+        fwd = {"fp8": lib.moe_forward_fp8, "int8": lib.moe_forward_int8, "fp8b": lib.moe_forward_fp8_block,
+               "mxfp8": lib.moe_forward_mxfp8}[dtype]
+        fwd(x, w, routing, Wp["w1"], Wp["w1_scale"], Wp["w2"], Wp["w2_scale"], ws, out)
 
 
 def combined(lib, ids, x, w, Wp, dtype, routing, ws, out):
-    if dtype == "bf16":
-        lib.moe_route_forward_bf16(ids, x, w, routing, Wp["w1"], Wp["w2"], ws, out)
-    else:
-        lib.moe_route_forward_fp8(ids, x, w, routing, Wp["w1"], Wp["w1_scale"], Wp["w2"], Wp["w2_scale"],
-                                  ws, out)
+    lib.route_forward(ids, x, w, routing, Wp, ws, out, dtype)
 
 
 def buffers(lib, T, k, E, H, I, dtype):
@@ -101,9 +100,20 @@ DECODE = [
 ]
 
 
-@pytest.mark.parametrize("E,H,I,k", DECODE)
+# shapes for the dtypes with 128-value groups (H and I multiples of 128)
+DECODE_Q = [
+    (1, 256, 128, 4),
+    (8, 256, 256, 1),
+    (16, 512, 256, 3),
+    (64, 1024, 512, 8),
+    (32, 256, 128, 16),
+]
+QUANT = ["int8", "fp8b", "mxfp8"]
+
+
+@pytest.mark.parametrize("E,H,I,k,dtype", [(*sh, dt) for dt in ("bf16", "fp8") for sh in DECODE] +
+                         [(*sh, dt) for dt in QUANT for sh in DECODE_Q])
 @pytest.mark.parametrize("case", ["plain", "dropped", "all_dropped", "repeated"])
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_one_token(lib, E, H, I, k, case, dtype):
     assert lib.moe_workspace_layout(1, k, E, H, I, dtype)["tiling"] == 0
     wl = custom_workload(E, H, I, k, dtype=dtype, seed=E + H + I + k + 5)
@@ -132,7 +142,7 @@ SEVERAL = [
 
 
 @pytest.mark.parametrize("T,k,E,case", SEVERAL)
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"] + QUANT)
 def test_several_tokens(lib, T, k, E, case, dtype):
     H, I = 512, 256
     wl = custom_workload(E, H, I, k, dtype=dtype, seed=T + k + 60)
@@ -147,7 +157,7 @@ def test_several_tokens(lib, T, k, E, case, dtype):
     check_case(lib, x, ids, w, Wp, Wc, E, H, I, dtype, f"T={T} {case}")
 
 
-FULL_DECODE = [(n, T) for n in ("mixtral", "qwen3", "qwen2", "dsv3")
+FULL_DECODE = [(n, T) for n in ("mixtral", "qwen3", "qwen2", "dsv3", "dsv3i8", "dsv3b", "dsv3mx")
                for T in sorted(set([1] + [t for t in WORKLOADS[n].Ts if t * WORKLOADS[n].k <= 64]))]
 
 
@@ -160,10 +170,10 @@ def test_full_size_decode(lib, name, T):
     check_case(lib, x, ids, w, Wp, Wc, wl.E, wl.H, wl.I, dtype, f"{name} T={T}")
 
 
-@pytest.mark.parametrize("T", [1, 8])
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("T,dtype", [(1, "bf16"), (8, "bf16"), (1, "fp8"), (8, "fp8"), (1, "int8"),
+                                     (8, "mxfp8"), (2, "fp8b")])
 def test_graph_capture_new_ids_between_replays(lib, T, dtype):
-    E, H, I, k = 64, 1024, 640, 8
+    E, H, I, k = 64, 1024, 512, 8
     wl = custom_workload(E, H, I, k, dtype=dtype, seed=70)
     Wr = device_weights(wl)
     Wp = lib.pack_weights(Wr, dtype)
