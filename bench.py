@@ -139,16 +139,11 @@ class Layer:
                 self.ws, self.out)
 
     def run(self, W=None):
-        """One layer: routing build + forward.  bf16, fp8, int8, block fp8 and
-        MXFP8 make it one library call, which routes a decode batch (at most
-        64 pairs) inside the forward's first kernel; int4 and int8 w8a16 call
-        the routing build first."""
+        """One layer: routing build + forward in one library call, which
+        routes a decode batch (at most 64 pairs) inside the forward's first
+        kernel."""
         m, W = self.moe, (W or self.W)
-        if self.dtype in ("bf16", "fp8", "int8", "fp8b", "mxfp8"):
-            m.route_forward(self.ids, self.x, self.w, self.routing, W, self.ws, self.out, self.dtype)
-        else:
-            self.run_routing()
-            self.run_forward(W)
+        m.route_forward(self.ids, self.x, self.w, self.routing, W, self.ws, self.out, self.dtype)
 
 
 def stage_pass(layer, steps):

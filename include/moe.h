@@ -352,9 +352,11 @@ int moe_route_forward_fp8(const int32_t *topk_ids, const void *x, const float *t
                           int T, int k, int E, int H, int I,
                           void *workspace, size_t workspace_bytes, void *out, void *stream);
 /* The same for the quantised layers below: moe_build_routing_int8 /
- * _fp8_block / _mxfp8 followed by moe_forward_int8 / _fp8_block / _mxfp8,
- * in one call, with the same results; at most 64 pairs on the
- * register-streaming plan are routed inside the x quantisation. */
+ * _fp8_block / _mxfp8 / _int4 / _int8_w8a16 followed by the forward call of
+ * the same dtype, in one call, with the same results; at most 64 pairs on
+ * the register-streaming plan are routed inside the x quantisation (int8
+ * w8a8, block fp8, MXFP8) or the gate-up GEMM on 16-row tiles (int4 w4a16,
+ * int8 w8a16). */
 int moe_route_forward_int8(const int32_t *topk_ids, const void *x, const float *topk_w,
                            void *routing, size_t routing_bytes,
                            const moe_packed_weights_t *w1, const float *w1_scale,
@@ -373,6 +375,18 @@ int moe_route_forward_mxfp8(const int32_t *topk_ids, const void *x, const float 
                             const moe_packed_weights_t *w2, const uint8_t *w2_scale,
                             int T, int k, int E, int H, int I,
                             void *workspace, size_t workspace_bytes, void *out, void *stream);
+int moe_route_forward_int4(const int32_t *topk_ids, const void *x, const float *topk_w,
+                           void *routing, size_t routing_bytes,
+                           const moe_packed_weights_t *w1, const float *w1_scale,
+                           const moe_packed_weights_t *w2, const float *w2_scale,
+                           int T, int k, int E, int H, int I,
+                           void *workspace, size_t workspace_bytes, void *out, void *stream);
+int moe_route_forward_int8_w8a16(const int32_t *topk_ids, const void *x, const float *topk_w,
+                                 void *routing, size_t routing_bytes,
+                                 const moe_packed_weights_t *w1, const float *w1_scale,
+                                 const moe_packed_weights_t *w2, const float *w2_scale,
+                                 int T, int k, int E, int H, int I,
+                                 void *workspace, size_t workspace_bytes, void *out, void *stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the fp8

@@ -112,7 +112,8 @@ EXPORTS = ("moe_status_string", "moe_pack_weights", "moe_describe_packed_weights
            "moe_build_routing_fp8_block", "moe_forward_fp8_block",
            "moe_build_routing_int8_w8a16", "moe_forward_int8_w8a16", "moe_set_stage_events", "moe_device_cu_count",
            "moe_stream_read", "moe_forward_fp8_noalloc", "moe_route_forward_bf16", "moe_route_forward_fp8",
-           "moe_route_forward_int8", "moe_route_forward_fp8_block", "moe_route_forward_mxfp8")
+           "moe_route_forward_int8", "moe_route_forward_fp8_block", "moe_route_forward_mxfp8",
+           "moe_route_forward_int4", "moe_route_forward_int8_w8a16")
 
 
 def _load():
@@ -173,7 +174,8 @@ def _load():
     L.moe_route_forward_bf16.argtypes = [P, P, P, P, sz, D, D, i, i, i, i, i, P, sz, P, P]
     L.moe_route_forward_fp8.restype = i
     L.moe_route_forward_fp8.argtypes = [P, P, P, P, sz, D, P, D, P, i, i, i, i, i, P, sz, P, P]
-    for f in (L.moe_route_forward_int8, L.moe_route_forward_fp8_block, L.moe_route_forward_mxfp8):
+    for f in (L.moe_route_forward_int8, L.moe_route_forward_fp8_block, L.moe_route_forward_mxfp8,
+              L.moe_route_forward_int4, L.moe_route_forward_int8_w8a16):
         f.restype = i
         f.argtypes = [P, P, P, P, sz, D, P, D, P, i, i, i, i, i, P, sz, P, P]
     return L
@@ -543,13 +545,30 @@ def moe_route_forward_mxfp8(topk_ids, x, topk_w, routing, w1, w1_scale, w2, w2_s
                             lambda E, N, K: (E, N, K // 32))
 
 
+def moe_route_forward_int4(topk_ids, x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, out,
+                           stream=None):
+    """moe_build_routing_int4 + moe_forward_int4 in one call."""
+    return _route_forward_q(_lib.moe_route_forward_int4, "moe_route_forward_int4", topk_ids, x, topk_w, routing,
+                            w1, w1_scale, w2, w2_scale, workspace, out, stream, torch.float32,
+                            lambda E, N, K: (E, N, K // 128))
+
+
+def moe_route_forward_int8_w8a16(topk_ids, x, topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, out,
+                                 stream=None):
+    """moe_build_routing_int8_w8a16 + moe_forward_int8_w8a16 in one call."""
+    return _route_forward_q(_lib.moe_route_forward_int8_w8a16, "moe_route_forward_int8_w8a16", topk_ids, x,
+                            topk_w, routing, w1, w1_scale, w2, w2_scale, workspace, out, stream, torch.float32,
+                            lambda E, N, K: (E, N))
+
+
 def route_forward(topk_ids, x, topk_w, routing, weights, workspace, out, dtype="bf16", stream=None):
-    """Routing build + forward in one library call (bf16, fp8, int8, fp8b, mxfp8)."""
+    """Routing build + forward in one library call, any dtype."""
     W = weights
     if dtype == "bf16":
         return moe_route_forward_bf16(topk_ids, x, topk_w, routing, W["w1"], W["w2"], workspace, out, stream)
     fn = {"fp8": moe_route_forward_fp8, "int8": moe_route_forward_int8, "fp8b": moe_route_forward_fp8_block,
-          "mxfp8": moe_route_forward_mxfp8}[dtype]
+          "mxfp8": moe_route_forward_mxfp8, "int4": moe_route_forward_int4,
+          "int8w": moe_route_forward_int8_w8a16}[dtype]
     return fn(topk_ids, x, topk_w, routing, W["w1"], W["w1_scale"], W["w2"], W["w2_scale"], workspace, out, stream)
 
 

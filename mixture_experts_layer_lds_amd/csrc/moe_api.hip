@@ -1002,7 +1002,8 @@ int forward_fp8b(const void* x, const float* topk_w, const void* routing, const 
 // down (bf16 rows), the top-k reduction.
 int forward_w4(int dtype, const void* x, const float* topk_w, const void* routing, const void* w1,
                const float* w1_scale, const void* w2, const float* w2_scale, int T, int k, int E,
-               int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+               int H, int I, void* workspace, size_t workspace_bytes, void* out, void* stream,
+               const moe_host::DecodeRouteOut* fold = nullptr) {
   int rc = check_shape(T, k, E, H, I, dtype);
   if (rc != MOE_OK) return rc;
   if (T == 0) return MOE_OK;
@@ -1041,6 +1042,8 @@ int forward_w4(int dtype, const void* x, const float* topk_w, const void* routin
     a.w_rows = 2 * I;
     a.topk = k;
     a.max_tasks = p.max_tasks;
+    a.P = P;
+    if (fold) a.route = *fold;
     const int grid = stream_grid((long)p.max_tasks * (I / 16) / (p.nb / 2), p.sw1, cus);
     e = w8 ? moe_host::launch_stream_w8(a, true, p.mb, p.sw1, grid, s, p.nb)
            : moe_host::launch_stream_w4(a, true, p.mb, p.sw1, grid, s, p.nb);
@@ -1504,7 +1507,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
 // pairs on the register-streaming plan is routed inside the forward's first
 // kernel (the x quantisation on the dtypes with quantised activations, the
 // gate-up GEMM on bf16); otherwise the routing build runs as its own launch
-// first.  bf16, per-channel fp8, int8 w8a8, block fp8 and MXFP8.
+// first.  Every dtype of the forward calls.
 int route_forward(int dtype, const int32_t* ids, const void* x, const float* topk_w, void* routing,
                   size_t routing_bytes, const void* w1, const void* w1_scale, const void* w2,
                   const void* w2_scale, int T, int k, int E, int H, int I, void* workspace,
@@ -1531,14 +1534,20 @@ int route_forward(int dtype, const int32_t* ids, const void* x, const float* top
         return forward_mx(x, topk_w, routing, w1, static_cast<const uint8_t*>(w1_scale), w2,
                           static_cast<const uint8_t*>(w2_scale), T, k, E, H, I, workspace, workspace_bytes,
                           out, stream, f);
+      case MOE_DTYPE_INT4_W4A16:
+      case MOE_DTYPE_INT8_W8A16:
+        return forward_w4(dtype, x, topk_w, routing, w1, s1, w2, s2, T, k, E, H, I, workspace, workspace_bytes,
+                          out, stream, f);
       default:
         return forward(dtype, x, topk_w, routing, w1, s1, w2, s2, T, k, E, H, I, workspace,
                        workspace_bytes, out, stream, f);
     }
   };
-  // the x quantisation comes first and takes any plan; bf16: the gate-up
-  // kernels on 16-row tiles
-  const bool first_takes_it = dtype != MOE_DTYPE_BF16 || (p.mb == 1 && (p.half1 || p.nb == 2));
+  // the x quantisation comes first and takes any plan; bf16 activations
+  // (bf16, int4 and int8 weights): the gate-up kernels on 16-row tiles with
+  // two weight blocks per item (bf16 also the half-width items)
+  const bool bf16_act = dtype == MOE_DTYPE_BF16 || dtype == MOE_DTYPE_INT4_W4A16 || dtype == MOE_DTYPE_INT8_W8A16;
+  const bool first_takes_it = !bf16_act || (p.mb == 1 && (p.nb == 2 || (dtype == MOE_DTYPE_BF16 && p.half1)));
   if ((long)T * k <= moe::kDecodeRoutePairs && p.tiling == kStreaming && first_takes_it) {
     char* b = static_cast<char*>(routing);
     moe_host::DecodeRouteOut f;
@@ -1886,6 +1895,29 @@ int moe_route_forward_mxfp8(const int32_t* topk_ids, const void* x, const float*
   const int rc = check_packed(MOE_DTYPE_MXFP8, w1, w2, T, k, E, H, I);
   if (rc != MOE_OK || T == 0) return rc;
   return route_forward(MOE_DTYPE_MXFP8, topk_ids, x, topk_w, routing, routing_bytes, packed_data(w1),
+                       w1_scale, packed_data(w2), w2_scale, T, k, E, H, I, workspace, workspace_bytes, out,
+                       stream);
+}
+
+int moe_route_forward_int4(const int32_t* topk_ids, const void* x, const float* topk_w, void* routing,
+                           size_t routing_bytes, const moe_packed_weights_t* w1, const float* w1_scale,
+                           const moe_packed_weights_t* w2, const float* w2_scale, int T, int k, int E, int H,
+                           int I, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const int rc = check_packed(MOE_DTYPE_INT4_W4A16, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return route_forward(MOE_DTYPE_INT4_W4A16, topk_ids, x, topk_w, routing, routing_bytes, packed_data(w1),
+                       w1_scale, packed_data(w2), w2_scale, T, k, E, H, I, workspace, workspace_bytes, out,
+                       stream);
+}
+
+int moe_route_forward_int8_w8a16(const int32_t* topk_ids, const void* x, const float* topk_w, void* routing,
+                                 size_t routing_bytes, const moe_packed_weights_t* w1, const float* w1_scale,
+                                 const moe_packed_weights_t* w2, const float* w2_scale, int T, int k, int E,
+                                 int H, int I, void* workspace, size_t workspace_bytes, void* out,
+                                 void* stream) {
+  const int rc = check_packed(MOE_DTYPE_INT8_W8A16, w1, w2, T, k, E, H, I);
+  if (rc != MOE_OK || T == 0) return rc;
+  return route_forward(MOE_DTYPE_INT8_W8A16, topk_ids, x, topk_w, routing, routing_bytes, packed_data(w1),
                        w1_scale, packed_data(w2), w2_scale, T, k, E, H, I, workspace, workspace_bytes, out,
                        stream);
 }

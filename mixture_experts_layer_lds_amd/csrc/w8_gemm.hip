@@ -23,6 +23,7 @@
 //    split over the W waves of a workgroup, partial sums added in LDS in
 //    ascending wave order (deterministic).
 #include "lds_dma.h"
+#include "decode_route.h"
 
 namespace moe {
 
@@ -51,16 +52,27 @@ __device__ __forceinline__ void w8_expand(const u32x4& c, u32x4& first, u32x4& l
 // NB weight blocks per item: 2, or 4 on tiles of 32 or more rows (gate-up:
 // two gate and two up blocks, down: 64 columns), halving the re-reads of
 // the tile's token rows.
-template <int MB, int W, bool GATEUP, int NB = kW8NB>
+// ROUTE: gate-up of a decode batch (at most 64 pairs) with the routing build
+// folded in (tasks and row tokens from decode_route).
+template <int MB, int W, bool GATEUP, int NB = kW8NB, bool ROUTE = false>
 __global__ void __launch_bounds__(W * 64)
 stream_w8_kernel(moe_host::StreamArgs g) {
+  static_assert(!ROUTE || GATEUP, "the folded routing build serves the gate-up");
   constexpr int NH = GATEUP ? NB / 2 : NB;   // 16-column output blocks per item
   __shared__ f32x4 red[W][MB][NB][64];
   const int lane = threadIdx.x & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
+  DecodeRoute rt{};
+  int num_tasks;
+  if constexpr (ROUTE) {
+    rt = decode_route(g.route.ids, g.P, g.route.E, g.route.block_m, lane);
+    if (blockIdx.x == 0) decode_route_write(rt, g.route, g.P, threadIdx.x, W * 64, lane, wave);
+    num_tasks = min(rt.ntasks, g.max_tasks);
+  } else {
+    num_tasks = min(g.header[kHdrNumTasks], g.max_tasks);
+  }
   const int n_groups = g.N_out / 16 / NH;
   const int total = num_tasks * n_groups;
   const size_t x_row_bytes = (size_t)g.K * 2;
@@ -78,7 +90,9 @@ stream_w8_kernel(moe_host::StreamArgs g) {
   for (int item = vid; item < total; item += G) {
     const int ti = item / n_groups;
     const int cg = item - ti * n_groups;
-    const moe_task_t task = load_task_scalar(g.tasks + ti);
+    moe_task_t task;
+    if constexpr (ROUTE) task = decode_task(rt, ti, g.route.block_m);
+    else task = load_task_scalar(g.tasks + ti);
     int blk[NB];
     if constexpr (GATEUP) {
 #pragma unroll
@@ -97,7 +111,9 @@ stream_w8_kernel(moe_host::StreamArgs g) {
     for (int b = 0; b < MB; b++) {
       const int rb = b * 16 < task.rows ? b : 0;
       int arow;
-      if constexpr (GATEUP) {
+      if constexpr (ROUTE) {
+        arow = decode_sorted_pair(rt, task.row_begin + (rb * 16 + lrow < task.rows ? rb * 16 + lrow : 0)) / g.topk;
+      } else if constexpr (GATEUP) {
         const i32x16_t sp = load16_scalar(g.sorted_pairs + task.row_begin + rb * 16);
         const int p = rb * 16 + lrow < task.rows ? spread16(sp, lane) : sp[0];
         arow = p / g.topk;
@@ -198,6 +214,15 @@ stream_w8_kernel(moe_host::StreamArgs g) {
 
 template <int MB, int W>
 static hipError_t launch_w8_t(const moe_host::StreamArgs& a, bool gateup, int nb, int grid, hipStream_t s) {
+  if (a.route.ids) {   // the routing build folded in: gate-up on 16-row tiles, two blocks per item
+    if constexpr (MB == 1) {
+      if (gateup && nb == 2) {
+        hipLaunchKernelGGL((stream_w8_kernel<MB, W, true, 2, true>), dim3(grid), dim3(W * 64), 0, s, a);
+        return hipGetLastError();
+      }
+    }
+    return hipErrorInvalidValue;
+  }
   if (nb == 4) {
     if constexpr (MB >= 2 && MB * W <= 16) {   // partial sums within 64 KiB of LDS
       if (gateup)

@@ -1,8 +1,8 @@
 """The routing build and the forward pass in one call (moe_route_forward_bf16
-/ _fp8 / _int8 / _fp8_block / _mxfp8).  For a decode batch of at most 64 token-expert pairs the routing
-build runs inside the forward's first kernel (bf16: the gate-up GEMM, the
-quantised dtypes: the x quantisation), whose workgroup 0 writes the routing
-buffer.
+/ _fp8 / _int8 / _fp8_block / _mxfp8 / _int4 / _int8_w8a16).  For a decode batch of at most 64 token-expert pairs the routing
+build runs inside the forward's first kernel (bf16 activations: the gate-up
+GEMM; quantised activations: the x quantisation), whose workgroup 0 writes
+the routing buffer.
 
 Checked on every case:
 - the routing buffer holds the same bytes as after moe_build_routing_* (both
@@ -42,7 +42,8 @@ def separate(lib, ids, x, w, Wp, dtype, E, H, I, routing, ws, out):
         lib.moe_forward_bf16(x, w, routing, Wp["w1"], Wp["w2"], ws, out)
     else:
         fwd = {"fp8": lib.moe_forward_fp8, "int8": lib.moe_forward_int8, "fp8b": lib.moe_forward_fp8_block,
-               "mxfp8": lib.moe_forward_mxfp8}[dtype]
+               "mxfp8": lib.moe_forward_mxfp8, "int4": lib.moe_forward_int4,
+               "int8w": lib.moe_forward_int8_w8a16}[dtype]
         fwd(x, w, routing, Wp["w1"], Wp["w1_scale"], Wp["w2"], Wp["w2_scale"], ws, out)
 
 
@@ -108,7 +109,7 @@ DECODE_Q = [
     (64, 1024, 512, 8),
     (32, 256, 128, 16),
 ]
-QUANT = ["int8", "fp8b", "mxfp8"]
+QUANT = ["int8", "fp8b", "mxfp8", "int4", "int8w"]
 
 
 @pytest.mark.parametrize("E,H,I,k,dtype", [(*sh, dt) for dt in ("bf16", "fp8") for sh in DECODE] +
@@ -157,7 +158,8 @@ def test_several_tokens(lib, T, k, E, case, dtype):
     check_case(lib, x, ids, w, Wp, Wc, E, H, I, dtype, f"T={T} {case}")
 
 
-FULL_DECODE = [(n, T) for n in ("mixtral", "qwen3", "qwen2", "dsv3", "dsv3i8", "dsv3b", "dsv3mx")
+FULL_DECODE = [(n, T) for n in ("mixtral", "qwen3", "qwen2", "dsv3", "dsv3i8", "dsv3b", "dsv3mx", "mixtral4",
+                                 "mixtral8")
                for T in sorted(set([1] + [t for t in WORKLOADS[n].Ts if t * WORKLOADS[n].k <= 64]))]
 
 
@@ -171,7 +173,7 @@ def test_full_size_decode(lib, name, T):
 
 
 @pytest.mark.parametrize("T,dtype", [(1, "bf16"), (8, "bf16"), (1, "fp8"), (8, "fp8"), (1, "int8"),
-                                     (8, "mxfp8"), (2, "fp8b")])
+                                     (8, "mxfp8"), (2, "fp8b"), (1, "int4"), (4, "int8w")])
 def test_graph_capture_new_ids_between_replays(lib, T, dtype):
     E, H, I, k = 64, 1024, 512, 8
     wl = custom_workload(E, H, I, k, dtype=dtype, seed=70)
