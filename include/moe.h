@@ -155,10 +155,10 @@ typedef struct {
     size_t y;           /* tiling 2 with split_k2 > 1: fp32 [split_k2][P][H]
                            unweighted down partial sums; otherwise bf16
                            [P][H] unweighted down rows (fp8, tilings 0 and 2:
-                           weight scales only); unused (SIZE_MAX) on bf16 and
-                           fp8 at T = 1 with tiling 0 and an even number of
-                           64-byte steps in an I row, where the down launch
-                           adds the token's top-k rows itself */
+                           weight scales only); unused (SIZE_MAX) on bf16,
+                           fp8 and int8 w8a8 at T = 1 with tiling 0 and an
+                           even number of 64-byte steps in an I row, where the
+                           down launch adds the token's top-k rows itself */
     size_t total_bytes; /* minimum size of the workspace */
     int32_t split_k1;   /* slices of the gate-up reduction over H (1 unless tiling 2) */
     int32_t split_k2;   /* slices of the down reduction over I */

@@ -307,6 +307,13 @@ Plan make_plan(int dtype, int T, int k, int E, int H, int I) {
       p.sw1 = nsteps1 % 4 == 0 ? std::min(p.sw1, 2) : 1;
       p.sw2 = nsteps2 % 4 == 0 ? std::min(p.sw2, 2) : 1;
     }
+    if (dtype == MOE_DTYPE_INT8_W8A8 && T == 1 && nsteps2 % 2 == 0) {
+      // one token: the down GEMM adds the top-k rows itself, as on bf16 and
+      // per-channel fp8 (below)
+      p.dr_waves = 8;
+      p.dr_half = k <= 8 && nsteps2 % 4 == 0 && H / 16 < kPlanCUs * 3 / 4;
+      p.dr_u = nsteps2 % (p.dr_half ? 8 : 4) == 0 ? 4 : 2;
+    }
     return p;
   }
   // Few rows per expert (decode): register streaming, tiles of 16 rows.
@@ -504,7 +511,8 @@ void workspace_layout(int dtype, int T, int k, int H, int I, const Plan& p,
     W->g = take(4 * P * I);
     W->h = take(P * I);
     W->h_scale = take(4 * P);
-    W->y = s2 == 1 ? take(2 * P * H) : take(4 * (size_t)s2 * P * H);
+    // one token on streaming: the down launch adds the top-k rows itself
+    W->y = p.tiling == kStreaming && p.dr_waves ? kNone : (s2 == 1 ? take(2 * P * H) : take(4 * (size_t)s2 * P * H));
     W->total_bytes = off;
     W->split_k1 = 1;
     W->split_k2 = s2;
@@ -1213,17 +1221,22 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
     a.sorted_pairs = R.sorted_pairs;
     a.header = R.header;
     a.tasks = R.tasks;
-    a.c = ws + W.y;
+    a.c = p.dr_waves ? nullptr : ws + W.y;
     a.K = I;
     a.N_out = H;
     a.w_rows = H;
     a.topk = k;
     a.max_tasks = p.max_tasks;
-    e = moe_host::launch_stream_gemm(a, false, true, 2, p.mb, p.sw2, p.su2,
-                                     stream_grid((long)p.max_tasks * (H / 16) / p.nb, p.sw2, cus), s, p.nb);
+    a.P = P;
+    if (p.dr_waves)   // one token: the down launch adds the top-k rows itself
+      e = moe_host::launch_stream_down_reduce(a, true, p.dr_waves, p.dr_u, p.dr_half, topk_w, h_scale,
+                                              static_cast<uint16_t*>(out), s, true);
+    else
+      e = moe_host::launch_stream_gemm(a, false, true, 2, p.mb, p.sw2, p.su2,
+                                       stream_grid((long)p.max_tasks * (H / 16) / p.nb, p.sw2, cus), s, p.nb);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
-  {
+  if (!p.dr_waves) {
     StageScope st(s, 4);
     e = moe_host::launch_reduce(ws + W.y, true, 1, P, topk_w, R.pair_pos, R.expert_offsets, h_scale,
                                 E, T, k, H, static_cast<uint16_t*>(out), s);
@@ -1232,8 +1245,8 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
   return MOE_OK;
 }
 
-// Pointer, alignment and workspace-size rules of the bf16 / fp8 forward
-// pass (checked before anything is launched).
+// Pointer, alignment and workspace-size rules of a forward pass of any dtype
+// (checked before anything is launched).
 int check_forward_args(int dtype, const void* x, const float* topk_w, const void* routing, const void* w1,
                        const void* w1_scale, const void* w2, const void* w2_scale, int T, int k, int E,
                        int H, int I, const void* workspace, size_t workspace_bytes, const void* out) {

@@ -340,8 +340,10 @@ hipError_t launch_stream_half_gateup(const StreamArgs& a, int waves, int grid, h
 // [k], h_scale (fp8) per sorted row.  (waves, u) in (4, 2), (8, 2), (16, 2),
 // (8, 4), (16, 4); the K steps (K * element bytes / 64) a multiple of u
 // (`half`: 2u).
+// i8 (with fp8): int8 w8a8 codes on the integer MFMA.
 hipError_t launch_stream_down_reduce(const StreamArgs& a, bool fp8, int waves, int u, bool half,
-                                     const float* topk_w, const float* h_scale, uint16_t* out, hipStream_t s);
+                                     const float* topk_w, const float* h_scale, uint16_t* out, hipStream_t s,
+                                     bool i8 = false);
 // (mb, waves, u) = 16-row blocks per tile, waves per workgroup, K steps per stage.
 bool stream_config_supported(int mb, int waves, int u);
 // kind: 0 per-channel scales (bf16, or fp8 by `fp8`), 1 MXFP8 block scales,

@@ -481,11 +481,15 @@ stream_half_gateup_kernel(moe_host::StreamArgs g) {
 //    column c of the item is the sum of accumulator columns c and c + 8.
 //  * Task records go to LDS first; the per-row weights and scales are loaded
 //    before the weight stream starts and used after it.
-template <int W, int U, bool HALF, bool FP8>
+//  * I8 (int8 w8a8, with FP8 set: the same one-byte layout and scales): one
+//    v_mfma_i32_16x16x64_i8 per 16-byte fragment pair, int32 sums turned to
+//    fp32 where the waves' sums meet.
+template <int W, int U, bool HALF, bool FP8, bool I8 = false>
 __global__ void __launch_bounds__(W * 64)
 stream_down_reduce_kernel(moe_host::StreamArgs g, const float* __restrict__ topk_w,
                           const float* __restrict__ h_scale, uint16_t* __restrict__ out) {
 #pragma clang fp contract(off)
+  static_assert(!I8 || FP8, "int8 uses the one-byte per-channel layout");
   constexpr int KS = HALF ? 2 : 1;   // 64-byte K steps per instruction step
   __shared__ f32x4 red[W][64];
   __shared__ moe_task_t tk[16];
@@ -565,7 +569,16 @@ stream_down_reduce_kernel(moe_host::StreamArgs g, const float* __restrict__ topk
   auto compute = [&](const u32x4 (&fa)[U], const u32x4 (&fb)[U], bool in) __attribute__((always_inline)) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int u = 0; u < U; u++) stream_mfma<FP8>(acc, in ? fa[u] : zero, fb[u]);
+    for (int u = 0; u < U; u++) {
+      if constexpr (I8) {
+        typedef int i32x4 __attribute__((ext_vector_type(4)));
+        acc = __builtin_bit_cast(f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                                            __builtin_bit_cast(i32x4, in ? fa[u] : zero),
+                                            __builtin_bit_cast(i32x4, fb[u]), __builtin_bit_cast(i32x4, acc), 0, 0, 0));
+      } else {
+        stream_mfma<FP8>(acc, in ? fa[u] : zero, fb[u]);
+      }
+    }
   };
   if (ngroups > 0) {
     load(fa0, fb0, in0, 0);
@@ -585,7 +598,12 @@ stream_down_reduce_kernel(moe_host::StreamArgs g, const float* __restrict__ topk
     }
   }
 
-  red[wave][lane] = acc;
+  if constexpr (I8) {   // int32 sums (|sum| <= 127^2 K < 2^31) to fp32
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    red[wave][lane] = __builtin_convertvector(__builtin_bit_cast(i32x4, acc), f32x4);
+  } else {
+    red[wave][lane] = acc;
+  }
   __syncthreads();
   if (wave == 0) {
     f32x4 tot = red[0][lane];
@@ -706,13 +724,18 @@ hipError_t launch_stream_half_gateup(const StreamArgs& a, int waves, int grid, h
 }
 
 hipError_t launch_stream_down_reduce(const StreamArgs& a, bool fp8, int waves, int u, bool half,
-                                     const float* topk_w, const float* h_scale, uint16_t* out, hipStream_t s) {
+                                     const float* topk_w, const float* h_scale, uint16_t* out, hipStream_t s,
+                                     bool i8) {
   const int nsteps = a.K * (fp8 ? 1 : 2) / 64;
-  if (a.P > (half ? 8 : 16) || nsteps % ((half ? 2 : 1) * u) || a.N_out % 16) return hipErrorInvalidValue;
+  if (a.P > (half ? 8 : 16) || nsteps % ((half ? 2 : 1) * u) || a.N_out % 16 || (i8 && !fp8))
+    return hipErrorInvalidValue;
   const dim3 grid(a.N_out / (half ? 8 : 16));
 #define MOE_DR(Wv, Uv, Hv)                                                                              \
   {                                                                                                     \
-    if (fp8)                                                                                            \
+    if (i8)                                                                                             \
+      hipLaunchKernelGGL((moe::stream_down_reduce_kernel<Wv, Uv, Hv, true, true>), grid, dim3(Wv * 64),  \
+                         0, s, a, topk_w, h_scale, out);                                                \
+    else if (fp8)                                                                                       \
       hipLaunchKernelGGL((moe::stream_down_reduce_kernel<Wv, Uv, Hv, true>), grid, dim3(Wv * 64), 0, s, \
                          a, topk_w, h_scale, out);                                                      \
     else                                                                                                \

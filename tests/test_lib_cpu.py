@@ -85,7 +85,8 @@ def test_workspace_layout(m):
         assert D["tiling"] == 0 and D["y"] == 2 ** 64 - 1 and D["h"] < D["total_bytes"]
     # ... but not with an odd number (fp8, I = 576: 9 steps) or another dtype
     assert m.moe_workspace_layout(1, 3, 16, 320, 576, "fp8")["y"] != 2 ** 64 - 1
-    assert m.moe_workspace_layout(1, 8, 256, 7168, 2048, "int8")["y"] != 2 ** 64 - 1
+    assert m.moe_workspace_layout(1, 8, 256, 7168, 2048, "int8")["y"] == 2 ** 64 - 1
+    assert m.moe_workspace_layout(1, 8, 256, 7168, 2048, "mxfp8")["y"] != 2 ** 64 - 1
     assert m.moe_workspace_layout(2, 8, 256, 7168, 2048, "fp8")["y"] != 2 ** 64 - 1
 
 
