@@ -362,6 +362,41 @@ def stream_read_ceiling(moe, gib=4, reps=10):
             "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4)}
 
 
+def tile_copy_rates(moe, row_bytes=8192, reps=4, runs=9):
+    """Per-CU rate of token-tile copies into LDS, apart from any GEMM: the
+    library's tile-copy kernel (one workgroup per CU, groups of 16 on one XCD
+    sharing a 160-row tile, so the copies after the first pass hit L2) for
+    each lane pattern; median of `runs` launches, HIP events around each."""
+    import torch
+    cus = moe.moe_device_cu_count()
+    nbytes = max(1, cus // 128) * 8 * 160 * row_bytes
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(cus, dtype=torch.int32, device="cuda")
+    moved = cus * reps * 160 * row_bytes
+    names = {0: "contiguous 1 KiB (packed weights)", 1: "16 rows x 64 B, MFMA lane order",
+             2: "16 rows x 64 B, a row per lane quad (the GEMMs' token chunks)"}
+    out = {}
+    for pattern in (0, 1, 2):
+        moe.moe_tile_copy_read(pattern, buf, row_bytes, reps, sink)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(runs):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            moe.moe_tile_copy_read(pattern, buf, row_bytes, reps, sink)
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+        t = statistics.median(times)
+        out[names[pattern]] = {"us": round(t * 1e6, 1), "GBs": round(moved / t / 1e9, 1),
+                               "GBs_per_cu": round(moved / t / 1e9 / cus, 1)}
+    del buf
+    torch.cuda.empty_cache()
+    return {"kernel": "moe_tile_copy_read (global->LDS copies of a 160-row tile, 16 workgroups per tile)",
+            "row_bytes": row_bytes, "reps": reps, "cus": cus, "patterns": out}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -431,6 +466,9 @@ def main():
     ap.add_argument("--ceiling", action="store_true",
                     help="measure only the attainable HBM read rate (the library's streaming-read "
                          "kernel over 4 GiB) and print it")
+    ap.add_argument("--copy-rates", action="store_true",
+                    help="measure only the per-CU rate of token-tile copies into LDS in three lane "
+                         "patterns (the library's tile-copy kernel) and print it")
     ap.add_argument("--router", action="store_true",
                     help="measure the router top-k kernel (the step before the routing build) over "
                          "the workload's token grid instead of the layer")
@@ -464,6 +502,9 @@ def main():
     if args.ceiling:
         print(json.dumps({"metric": "attainable HBM read rate, 1 GPU", **stream_read_ceiling(moe)}),
               flush=True)
+        return
+    if args.copy_rates:
+        print(json.dumps({"metric": "token-tile copy rate into LDS, 1 GPU", **tile_copy_rates(moe)}), flush=True)
         return
     wl = WORKLOADS[args.workload]
     if args.router_gemm:

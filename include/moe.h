@@ -519,6 +519,24 @@ int moe_set_stage_events(void *const *events, int n);
  * and carry no other meaning.  bytes == 0 returns MOE_OK with no launch. */
 int moe_stream_read(const void *buf, size_t bytes, uint32_t *sink, size_t sink_words, void *stream);
 
+/* Measurement aid (what a token-tile copy into LDS costs, apart from the
+ * GEMMs around it): one workgroup of 8 waves per compute unit copies, reps
+ * times, every 1 KiB chunk of a 160-row x row_bytes tile (row-major in buf,
+ * device) into LDS with direct global->LDS copies, the workgroups of one XCD
+ * in groups of 16 on the same tile, so that after the first pass the copies
+ * hit L2.  pattern selects the lanes' sources of one chunk: 0 = 1 KiB
+ * contiguous (as the packed weights are copied), 1 = 16 rows x 64 bytes with
+ * lane l on row l % 16 (MFMA lane order), 2 = the same 16 x 64 bytes with
+ * each row's 64 bytes on one quad of lanes (the token-chunk layout of the
+ * LDS-staged GEMMs).  row_bytes: a positive multiple of 2048; bytes: the
+ * size of buf, at least (compute units / 128) x 8 x 160 x row_bytes
+ * (MOE_ERR_BUFFER_TOO_SMALL otherwise); sink (device, 4-byte aligned) takes
+ * one word per workgroup, sink_words >= compute units.  Needs >= 128 compute
+ * units (MOE_ERR_UNSUPPORTED_SHAPE).  Bytes moved = compute units x reps x
+ * 160 x row_bytes.  reps == 0 returns MOE_OK with no launch. */
+int moe_tile_copy_read(int pattern, const void *buf, size_t bytes, int row_bytes, int reps, uint32_t *sink,
+                       size_t sink_words, void *stream);
+
 /* Number of compute units of the current device as cached by the library
  * (queried once per device), or a negative status. */
 int moe_device_cu_count(void);

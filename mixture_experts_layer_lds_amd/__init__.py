@@ -113,7 +113,7 @@ EXPORTS = ("moe_status_string", "moe_pack_weights", "moe_describe_packed_weights
            "moe_build_routing_int8_w8a16", "moe_forward_int8_w8a16", "moe_set_stage_events", "moe_device_cu_count",
            "moe_stream_read", "moe_forward_fp8_noalloc", "moe_route_forward_bf16", "moe_route_forward_fp8",
            "moe_route_forward_int8", "moe_route_forward_fp8_block", "moe_route_forward_mxfp8",
-           "moe_route_forward_int4", "moe_route_forward_int8_w8a16")
+           "moe_route_forward_int4", "moe_route_forward_int8_w8a16", "moe_tile_copy_read")
 
 
 def _load():
@@ -170,6 +170,8 @@ def _load():
     L.moe_forward_fp8_noalloc.argtypes = [P, P, P, D, P, D, P, i, i, i, i, i, P, P]
     L.moe_stream_read.restype = i
     L.moe_stream_read.argtypes = [P, sz, P, sz, P]
+    L.moe_tile_copy_read.restype = i
+    L.moe_tile_copy_read.argtypes = [i, P, sz, i, i, P, sz, P]
     L.moe_route_forward_bf16.restype = i
     L.moe_route_forward_bf16.argtypes = [P, P, P, P, sz, D, D, i, i, i, i, i, P, sz, P, P]
     L.moe_route_forward_fp8.restype = i
@@ -711,6 +713,16 @@ def moe_stream_read(buf, sink, stream=None):
     nbytes = buf.numel() * buf.element_size()
     _check("moe_stream_read", _lib.moe_stream_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(),
                                                    _stream(stream)))
+
+
+def moe_tile_copy_read(pattern, buf, row_bytes, reps, sink, stream=None):
+    """Measurement aid: token-tile copies into LDS in one of three lane
+    patterns (0 contiguous, 1 MFMA lane order, 2 a row per lane quad) from the
+    device tensor `buf` (its whole storage); one word per workgroup into the
+    uint32/int32 tensor `sink`."""
+    nbytes = buf.numel() * buf.element_size()
+    _check("moe_tile_copy_read", _lib.moe_tile_copy_read(pattern, _ptr(buf), nbytes, row_bytes, reps, _ptr(sink),
+                                                         sink.numel(), _stream(stream)))
 
 
 def moe_layer(x, topk_ids, topk_w, weights, dtype="bf16", out=None, stream=None):

@@ -88,6 +88,24 @@ __device__ __forceinline__ int pick16(const i32x16_t& v, int j) {
   return r;
 }
 
+// Token chunks in LDS (16 gathered rows x one 64-byte K step, one wave copy
+// instruction).  The copy gives each quad of lanes one row's 64 contiguous
+// bytes: lane l fetches row l / 4, 16-byte piece (l % 4) ^ tok_swz(row).
+// Copies in MFMA lane order (lane l: row l % 16) touch 16 rows in every
+// quad and move about half as many bytes per CU cycle from L2 (measured on
+// gfx950: 36 against 64-69 GB/s per CU).  Row r thus sits at bytes 64 r of
+// the chunk with its pieces rotated by tok_swz(r), which spreads the 8 rows
+// that one LDS read phase serves over distinct banks.
+__device__ __forceinline__ int tok_swz(int row) { return (row + (row >> 2)) & 3; }
+__device__ __forceinline__ int tok_copy_row(int lane) { return lane >> 2; }
+__device__ __forceinline__ int tok_copy_piece(int lane) { return (lane & 3) ^ tok_swz(lane >> 2); }
+// Byte offset, in such a chunk, of MFMA lane `lane`'s fragment (row
+// lane % 16, piece lane / 16).
+__device__ __forceinline__ int tok_frag_off(int lane) {
+  const int r = lane & 15;
+  return 64 * r + 16 * ((lane >> 4) ^ tok_swz(r));
+}
+
 // Lane l receives v[l % 16].
 __device__ __forceinline__ int spread16(const i32x16_t& v, int lane) {
   const int j = lane & 15;

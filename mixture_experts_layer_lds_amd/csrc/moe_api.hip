@@ -1979,6 +1979,22 @@ int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_w
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+int moe_tile_copy_read(int pattern, const void* buf, size_t bytes, int row_bytes, int reps, uint32_t* sink,
+                       size_t sink_words, void* stream) {
+  if (pattern < 0 || pattern > 2 || !buf || !sink || !aligned(buf, 16) || !aligned(sink, 4) || reps < 0 ||
+      row_bytes <= 0 || row_bytes % 2048)
+    return MOE_ERR_INVALID_ARG;
+  int cus = 0;
+  const int rc = cu_count(&cus);
+  if (rc != MOE_OK) return rc;
+  if (cus < 128) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (bytes < moe_host::tile_copy_bytes(cus, row_bytes) || sink_words < (size_t)cus) return MOE_ERR_BUFFER_TOO_SMALL;
+  if (reps == 0) return MOE_OK;
+  const hipError_t e =
+      moe_host::launch_tile_copy(pattern, buf, row_bytes, reps, sink, cus, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 int moe_device_cu_count(void) {
   int n = 0;
   const int rc = cu_count(&n);

@@ -404,6 +404,11 @@ hipError_t launch_mx_requant(const float* h, int P, int I, const int32_t* expert
 // Streaming read of `bytes` (multiple of 16) of buf by `groups` workgroups,
 // one folded word per workgroup written to sink.
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int groups, hipStream_t s);
+// Token-tile copy measurement (one workgroup per CU, cus >= 128): the bytes
+// its buffer must hold, and the launch.
+size_t tile_copy_bytes(int cus, int row_bytes);
+hipError_t launch_tile_copy(int pattern, const void* buf, int row_bytes, int reps, uint32_t* sink, int cus,
+                            hipStream_t s);
 
 // fp32 rows -> e4m3 codes with the row amax held in h_scale (replaced by the scale).
 hipError_t launch_requant_rows(const float* h32, int P, int I, const int32_t* expert_offsets,

@@ -10,8 +10,10 @@
 //  * One workgroup of 8 waves per CU.  Work item = (task tile of 16*MB
 //    rows, strip of 256 output columns, K slice).
 //  * The tile's token rows go through LDS: a ring of NBUF+1 stages, each
-//    holding KS 64-byte K steps of all 16*MB rows as 1 KiB chunks in MFMA
-//    lane order, filled by direct global->LDS copies spread over the waves.
+//    holding KS 64-byte K steps of all 16*MB rows as 1 KiB chunks (16 rows
+//    of one step, each row's 64 bytes copied by one quad of lanes; the
+//    token-chunk layout of lds_dma.h), filled by direct global->LDS copies
+//    spread over the waves.
 //  * Each wave owns 32 columns of the strip and streams their packed
 //    weights (1 KiB chunks) straight into registers NBUF
 //    stages ahead, so a CU keeps 8 x NBUF x KS x 2 KiB of weights in flight
@@ -105,7 +107,7 @@ __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::St
   it.s = s;
   it.col = g.act ? (nt * W + wave) * 16 : nt * kCols + wave * (NSUB * 16);
   const int step0 = s * nk * KS;
-  const int lrow = lane & 15;
+  const int crow = tok_copy_row(lane);   // this lane's row of each token chunk it copies
 #pragma unroll
   for (int i = 0; i < StripItem<MB, KS, NSUB>::NA; i++) {
     // chunk c = 16-row block c / KS, K step c % KS of every stage
@@ -118,17 +120,18 @@ __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::St
     // A whole block past the tile thus reads one 64-byte line per step
     // (every lane the same row), not 16 rows.
     const bool blk_in = !pad && rb * 16 < task.rows;
-    const bool in_tile = blk_in && rb * 16 + lrow < task.rows;
+    const bool in_tile = blk_in && rb * 16 + crow < task.rows;
     int arow;
     if constexpr (GATHER) {
       const i32x16_t sp = load16_scalar(g.sorted_pairs + task.row_begin + (blk_in ? rb * 16 : 0));
-      const int p = in_tile ? spread16(sp, lane) : sp[0];
+      const int p = in_tile ? pick16(sp, crow) : sp[0];
       arow = p / g.topk;
     } else {
-      arow = task.row_begin + (in_tile ? rb * 16 + lrow : 0);
+      arow = task.row_begin + (in_tile ? rb * 16 + crow : 0);
     }
+    // rows past the tile read the first row's pieces in the same order
     it.a[i] = static_cast<const char*>(g.a) + (size_t)arow * row_bytes + (size_t)(step0 + st) * 64 +
-              16 * (lane >> 4);
+              16 * tok_copy_piece(lane);
   }
   it.b = static_cast<const char*>(g.b) +
          (((size_t)task.expert * (g.N / 16) + it.col / 16) * nsteps + step0) * 1024 + 16 * lane;
@@ -362,6 +365,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
     }
 
     const int lrow = lane & 15, lgrp = lane >> 4;
+    const int aoff = tok_frag_off(lane);   // this lane's token fragment in a chunk
     int f = 0;   // flat stage index over all items of this workgroup
     for (int ii = 0; ii < n_items; ii++) {
       f32x4 acc[MB][NSUB];
@@ -393,8 +397,8 @@ strip_gemm_kernel(moe_host::StripArgs g) {
   #pragma unroll
               for (int m = 0; m < MB; m++) {
                 i32x8 a;
-                a.lo = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st) * 1024 + 16 * lane);
-                a.hi = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st + 1) * 1024 + 16 * lane);
+                a.lo = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st) * 1024 + aoff);
+                a.hi = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st + 1) * 1024 + aoff);
                 const int sa = (int)(rsc[uis * 16 * MB + 16 * m + lrow] >> (8 * lgrp));
   #pragma unroll
                 for (int q = 0; q < NSUB; q++)
@@ -415,8 +419,8 @@ strip_gemm_kernel(moe_host::StripArgs g) {
   #pragma unroll
               for (int m = 0; m < MB; m++) {
                 i32x8 a;
-                a.lo = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st) * 1024 + 16 * lane);
-                a.hi = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st + 1) * 1024 + 16 * lane);
+                a.lo = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st) * 1024 + aoff);
+                a.hi = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st + 1) * 1024 + aoff);
                 const f32x4 sx = *reinterpret_cast<const f32x4*>(scs + uis * MB * 16 + 16 * m + 4 * lgrp);
   #pragma unroll
                 for (int q = 0; q < NSUB; q++) {
@@ -435,8 +439,8 @@ strip_gemm_kernel(moe_host::StripArgs g) {
   #pragma unroll
               for (int m = 0; m < MB; m++) {
                 i32x8 a;
-                a.lo = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st) * 1024 + 16 * lane);
-                a.hi = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st + 1) * 1024 + 16 * lane);
+                a.lo = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st) * 1024 + aoff);
+                a.hi = *reinterpret_cast<const i32x4_t*>(sb + (m * KS + st + 1) * 1024 + aoff);
   #pragma unroll
                 for (int q = 0; q < NSUB; q++) mfma_fp8_unit(acc[m][q], a, bb[u].unit(st >> 1, q));
               }
@@ -446,7 +450,7 @@ strip_gemm_kernel(moe_host::StripArgs g) {
             for (int st = 0; st < KS; st++) {
   #pragma unroll
               for (int m = 0; m < MB; m++) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(sb + (m * KS + st) * 1024 + 16 * lane);
+                const u32x4 a = *reinterpret_cast<const u32x4*>(sb + (m * KS + st) * 1024 + aoff);
   #pragma unroll
                 for (int q = 0; q < NSUB; q++) strip_mfma<FP8, I8>(acc[m][q], a, bb[u].step(st, q));
               }

@@ -288,7 +288,9 @@ static hipError_t launch_tiled_t(const moe_host::TiledArgs& a, int grid, hipStre
 // Operand chunks go from global memory straight into LDS with
 // global_load_lds_dwordx4 (each wave instruction fills one 1 KiB chunk,
 // lane l writing bytes 16*l..16*l+15), through a ring of NST stages of KS
-// 64-byte K steps each.  Stage f+NST-1 is issued while stage f is being
+// 64-byte K steps each.  Weight chunks arrive in MFMA lane order as packed;
+// A chunks in the token-chunk layout of lds_dma.h (a row's 64 bytes per quad
+// of lanes), whose fragment offsets the MFMA reads apply.  Stage f+NST-1 is issued while stage f is being
 // multiplied, so NST-1 compute phases cover the load latency; the ring runs
 // straight across work-item boundaries (the next tile's first stages load
 // while the current tile finishes), which matters for the short-K down
@@ -339,10 +341,10 @@ __device__ __forceinline__ DmaItem<Sh> dma_item(const moe_host::TiledArgs& g, in
   const int st = wave % Sh::KS;
 #pragma unroll
   for (int i = 0; i < Sh::kAPerWave; i++) {
-    int rr = ((wave + Sh::kWaves * i) / Sh::KS) * 16 + (lane & 15);
+    int rr = ((wave + Sh::kWaves * i) / Sh::KS) * 16 + tok_copy_row(lane);
     if (rr >= task.rows) rr = 0;    // a valid row; its products are never stored
     const int arow = GATEUP ? g.sorted_pairs[task.row_begin + rr] / g.topk : task.row_begin + rr;
-    it.a[i] = static_cast<const char*>(g.a) + (size_t)arow * row_bytes + st * 64 + 16 * (lane >> 4);
+    it.a[i] = static_cast<const char*>(g.a) + (size_t)arow * row_bytes + st * 64 + 16 * tok_copy_piece(lane);
   }
   it.b = static_cast<const char*>(g.b) + ((size_t)task.expert * w_blocks * nsteps + st) * 1024 + 16 * lane;
   return it;
@@ -414,6 +416,7 @@ tiled_dma_kernel(moe_host::TiledArgs g) {
   for (int d = 0; d < AHEAD; d++)
     if (d < F) issue_flat(d, 0);   // nk >= AHEAD: all in item 0
 
+  const int aoff = tok_frag_off(lane);   // this lane's fragment in an A chunk
   int f = 0;   // flat stage index over all items of this workgroup
   for (int ii = 0; ii < n_items; ii++) {
     f32x4 acc[MB][NB];
@@ -446,7 +449,7 @@ tiled_dma_kernel(moe_host::TiledArgs g) {
           for (int h = 0; h < 2; h++) {
 #pragma unroll
             for (int m = 0; m < MB; m++)
-              fa[m][h] = *reinterpret_cast<const u32x4*>(base + ((wm * MB + m) * KS + st + h) * 1024 + 16 * lane);
+              fa[m][h] = *reinterpret_cast<const u32x4*>(base + ((wm * MB + m) * KS + st + h) * 1024 + aoff);
 #pragma unroll
             for (int q = 0; q < NB; q++)
               fb[q][h] = *reinterpret_cast<const u32x4*>(base + (Sh::kAChunks + bchunk(q) * KS + st + h) * 1024 + 16 * lane);
@@ -462,7 +465,7 @@ tiled_dma_kernel(moe_host::TiledArgs g) {
           u32x4 fa[MB], fb[NB];
 #pragma unroll
           for (int m = 0; m < MB; m++)
-            fa[m] = *reinterpret_cast<const u32x4*>(base + ((wm * MB + m) * KS + st) * 1024 + 16 * lane);
+            fa[m] = *reinterpret_cast<const u32x4*>(base + ((wm * MB + m) * KS + st) * 1024 + aoff);
 #pragma unroll
           for (int q = 0; q < NB; q++)
             fb[q] = *reinterpret_cast<const u32x4*>(base + (Sh::kAChunks + bchunk(q) * KS + st) * 1024 + 16 * lane);
