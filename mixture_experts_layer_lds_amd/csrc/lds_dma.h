@@ -93,10 +93,13 @@ __device__ __forceinline__ int pick16(const i32x16_t& v, int j) {
 // bytes: lane l fetches row l / 4, 16-byte piece (l % 4) ^ tok_swz(row).
 // Copies in MFMA lane order (lane l: row l % 16) touch 16 rows in every
 // quad and move about half as many bytes per CU cycle from L2 (measured on
-// gfx950: 36 against 64-69 GB/s per CU).  Row r thus sits at bytes 64 r of
-// the chunk with its pieces rotated by tok_swz(r), which spreads the 8 rows
-// that one LDS read phase serves over distinct banks.
-__device__ __forceinline__ int tok_swz(int row) { return (row + (row >> 2)) & 3; }
+// gfx950: 35 against 62 GB/s per CU).  Row r thus sits at bytes 64 r of the
+// chunk with its pieces permuted by tok_swz(r).  With this permutation the
+// MFMA-order fragment reads below (ds_read_b128) run without LDS bank
+// conflicts (SQ_LDS_BANK_CONFLICT = 0, 4 LDS cycles per wave read); the
+// unpermuted layout and several other per-row permutations measured 2-way
+// conflicts.
+__device__ __forceinline__ int tok_swz(int row) { return (row >> 1) & 3; }
 __device__ __forceinline__ int tok_copy_row(int lane) { return lane >> 2; }
 __device__ __forceinline__ int tok_copy_piece(int lane) { return (lane & 3) ^ tok_swz(lane >> 2); }
 // Byte offset, in such a chunk, of MFMA lane `lane`'s fragment (row
