@@ -259,3 +259,21 @@ def test_binding_refuses_unpacked_tensors(m):
     with pytest.raises(TypeError, match="PackedWeight"):
         m.moe_forward_bf16(x, w, torch.zeros(16, dtype=torch.uint8), raw1, raw2,
                            torch.zeros(256, dtype=torch.uint8), torch.zeros(4, 128, dtype=torch.bfloat16))
+
+
+def test_measurement_aids_reject_bad_arguments(m):
+    """moe_stream_read and moe_tile_copy_read check their arguments on the host
+    before anything else (no device query, no launch)."""
+    lib = m._lib
+    fake = ctypes.c_void_p(4096)
+    odd = ctypes.c_void_p(4097)
+    assert lib.moe_stream_read(None, 1024, fake, 8, None) == -1          # null buffer
+    assert lib.moe_stream_read(fake, 1000, fake, 8, None) == -1          # bytes not a multiple of 16
+    assert lib.moe_stream_read(fake, 1024, fake, 0, None) == -1          # no sink words
+    for pattern in (-1, 3):
+        assert lib.moe_tile_copy_read(pattern, fake, 1 << 24, 8192, 1, fake, 256, None) == -1
+    assert lib.moe_tile_copy_read(0, None, 1 << 24, 8192, 1, fake, 256, None) == -1     # null buffer
+    assert lib.moe_tile_copy_read(0, odd, 1 << 24, 8192, 1, fake, 256, None) == -1      # misaligned buffer
+    assert lib.moe_tile_copy_read(1, fake, 1 << 24, 7168, 1, fake, 256, None) == -1     # rows not 2 KiB multiples
+    assert lib.moe_tile_copy_read(2, fake, 1 << 24, 8192, -1, fake, 256, None) == -1    # negative passes
+    assert lib.moe_tile_copy_read(2, fake, 1 << 24, 8192, 1, None, 256, None) == -1     # null sink
