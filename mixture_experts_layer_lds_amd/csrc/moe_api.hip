@@ -154,6 +154,13 @@ bool choose_strip(int nsteps, int mb, bool fp8, long items, int* split, int* ks,
   return best_eff >= 0.0;
 }
 
+// Strips of 160-row tiles run with the K loops of a tile's strips rotated
+// against each other (StripArgs::rotate).
+int rotate_strips(const Plan& p, bool down) {
+  (void)down;
+  return p.mb == 10 ? 1 : 0;
+}
+
 // Tile plan: a fixed function of the shape and dtype, shared by the routing
 // build, the workspace layout and the forward pass.
 // Waves per workgroup for the 128-value-unit streaming kernels (int4,
@@ -1150,6 +1157,7 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
       a.out_bf16 = 0;
       a.act = 1;
       a.x_scale_rows = x_rows;
+      a.rotate = rotate_strips(p, false);
       e = moe_host::launch_strip_gemm(a, true, true, p.mb, p.ks1, p.nbuf1, cus, s, 1);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
@@ -1175,6 +1183,7 @@ int forward_i8(const void* x, const float* topk_w, const void* routing, const vo
       a.max_tasks = p.max_tasks;
       a.split = p.split2;
       a.out_bf16 = y_bf16 ? 1 : 0;
+      a.rotate = rotate_strips(p, true);
       e = moe_host::launch_strip_gemm(a, false, true, p.mb, p.ks2, p.nbuf2, cus, s, 1);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
@@ -1337,6 +1346,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
       a.out_bf16 = 0;
       a.act = fuse_act ? 1 : 0;
       a.x_scale_rows = fuse_act && fp8 ? reinterpret_cast<const float*>(ws + W.x_scale_rows) : nullptr;
+      a.rotate = rotate_strips(p, false);
       e = moe_host::launch_strip_gemm(a, true, fp8, p.mb, p.ks1, p.nbuf1, cus, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }
@@ -1368,6 +1378,7 @@ int forward(int dtype, const void* x, const float* topk_w, const void* routing, 
       a.max_tasks = p.max_tasks;
       a.split = p.split2;
       a.out_bf16 = y_bf16 ? 1 : 0;
+      a.rotate = rotate_strips(p, true);
       e = moe_host::launch_strip_gemm(a, false, fp8, p.mb, p.ks2, p.nbuf2, cus, s);
       if (e != hipSuccess) return MOE_ERR_HIP;
     }

@@ -297,6 +297,10 @@ struct StripArgs {
   // [P][K/32] per sorted row) and of the weights [E][N][K/32]
   const uint8_t* a_mx;
   const uint8_t* b_mx;
+  // 1: strip j of a tile runs its K stages rotated by (j mod 16) x (stages / 16),
+  // so the strips that share the tile's token rows read different rows' lines at
+  // any moment; 0: every strip in K order
+  int rotate;
 };
 
 // (mb, ks, nbuf) = 16-row blocks per tile, 64-byte K steps per stage, stages in flight.

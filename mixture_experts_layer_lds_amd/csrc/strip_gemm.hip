@@ -22,6 +22,10 @@
 //    both of the wave's 16-column blocks.
 //  * The ring runs straight across work items: the next item's first stages
 //    are in flight while the current one finishes and stores its results.
+//  * Optionally (rotate) the strips of one tile start their K loops at
+//    different stages, so that the 16 workgroups sharing its token rows do not
+//    ask L2 for the same lines at the same moment; every stage is still summed
+//    once, in an order fixed by the strip's position.
 //  * Per-item metadata (the task record, the tile's token indices, fp8
 //    column scales) comes from scalar loads, whose waits are on lgkmcnt, so
 //    the vector-memory queue holds only the ring's loads and the epilogue's
@@ -59,6 +63,7 @@ template <int MB, int KS, int NSUB>
 struct StripItem {
   static constexpr int NA = (MB * KS + strip_waves<NSUB>() - 1) / strip_waves<NSUB>();
   int row_begin, rows, s;
+  int rot;                     // K stages the item's loop is rotated by
   int col;                     // first output column of this wave (of h when fusing SiLU-and-mul)
   const char* a[NA];           // this lane's token sources (K step and lane offsets applied)
   const char* b;               // this lane's packed-weight source of column block 0
@@ -105,6 +110,7 @@ __device__ __forceinline__ StripItem<MB, KS, NSUB> strip_item(const moe_host::St
   it.row_begin = task.row_begin;
   it.rows = task.rows;
   it.s = s;
+  it.rot = g.rotate ? (nt % 16) * (nk / 16) : 0;
   it.col = g.act ? (nt * W + wave) * 16 : nt * kCols + wave * (NSUB * 16);
   const int step0 = s * nk * KS;
   const int crow = tok_copy_row(lane);   // this lane's row of each token chunk it copies
@@ -319,6 +325,9 @@ strip_gemm_kernel(moe_host::StripArgs g) {
     auto issue = [&](bool in_cur, int kt, int fslot, WeightStage<KS, NSUB, PAIRS>& b,
                      float (&sw)[NSUB][KS / 2 > 0 ? KS / 2 : 1]) {
       char* sb = lds + fslot * SLOT;
+      // the item's stage kt in its rotated order (every stage exactly once)
+      kt += in_cur ? cur.rot : nxt.rot;
+      if (kt >= nk) kt -= nk;
   #pragma unroll
       for (int i = 0; i < NA; i++)
         dma16((in_cur ? cur.a[i] : nxt.a[i]) + (size_t)kt * KS * 64,
