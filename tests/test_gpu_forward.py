@@ -157,6 +157,7 @@ STRIP = [
     (16, 512, 256, 4, 512, 0.01, 1, 2),     # 128 rows per expert: LDS tiles on bf16, 160-row strips on fp8
     (8, 1024, 512, 2, 500, 0.0, 1, 2),      # 125 rows per expert, 160-row fp8 strips, 2-stage down ring
     (16, 512, 256, 4, 600, 0.0, 1, 2),      # 150 rows per expert: 192-row fp8 strips
+    (16, 2048, 2048, 2, 1000, 0.0, 1, 2),   # 160-row fp8 strips, 16 gate-up strips with rotated K loops
 ]
 
 

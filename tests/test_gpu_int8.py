@@ -76,6 +76,7 @@ STRIP_SHAPES = [
     (32, 256, 2048, 4, 200, 0.05, 64, 8),
     (64, 512, 1024, 8, 960, 0.0, 160, 2),     # 120 rows per expert: 160-row tiles
     (64, 1024, 1024, 8, 960, 0.02, 160, 1),
+    (16, 2048, 2048, 2, 1000, 0.0, 160, 2),   # 16 gate-up strips with rotated K loops
 ]
 
 
